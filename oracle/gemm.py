@@ -1,0 +1,45 @@
+"""Frozen-projection GEMMs of dequantized NVFP4 operands, in float64 (oracle).
+
+PACT runs every frozen projection as an NVFP4 GEMM with FP32 accumulation and
+BF16 output, forward and input-gradient, over cached forward and backward
+NVFP4 weight layouts (Appendix Table 7, row "Frozen projections").  The exact
+result of such a GEMM is the product of the dequantized operands, which is
+what this module computes:
+
+* forward        Y[m, n]  = sum_k deq(X_q)[m, k] * deq(W_fwd)[n, k]
+* input gradient dX[m, k] = sum_n deq(dY_q)[m, n] * deq(W_bwd)[k, n]
+
+with W_fwd = Q(W) (blocks along K) and W_bwd = Q(W^T) (blocks along N), both
+rounded to nearest from the same BF16 W.  Both are "A [M x Kr] times
+B [Nout x Kr]^T", so one function serves both directions.
+"""
+
+from __future__ import annotations
+
+import numpy as np
+
+from .nvfp4 import NVFP4, dequantize, quantize
+
+
+def weight_layouts(w):
+    """(W_fwd, W_bwd) = (Q(W), Q(W^T)) for a BF16 weight W [N x K] given as real values."""
+    w = np.asarray(w, dtype=np.float64)
+    return quantize(w), quantize(w, transpose=True)
+
+
+def gemm_nt(a: NVFP4, b: NVFP4):
+    """(C, |A||B|^T) for C = deq(a) @ deq(b)^T in float64.
+
+    The second result is sum_k |a_k b_k| per output, used by the acceptance bound.
+    """
+    da = dequantize(a)
+    db = dequantize(b)
+    return da @ db.T, np.abs(da) @ np.abs(db).T
+
+
+def gemm_fwd(xq: NVFP4, w_fwd: NVFP4):
+    return gemm_nt(xq, w_fwd)
+
+
+def gemm_dgrad(dyq: NVFP4, w_bwd: NVFP4):
+    return gemm_nt(dyq, w_bwd)

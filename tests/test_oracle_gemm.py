@@ -1,0 +1,157 @@
+"""Pins of the oracle's GEMMs, LoRA branch and tolerance helpers.
+
+Frozen projections are NVFP4 GEMMs with FP32 accumulation and BF16 output
+(PACT, Appendix Table 7, row "Frozen projections"); the LoRA branch is a
+BF16 GEMM on the reconstructed input (row "LoRA branch").  The oracle
+computes both exactly in float64; these tests pin it with exact-rational
+brute force on tiny shapes, an integer special case, finite differences of
+the LoRA gradients, and closed forms of the BF16 rounding helpers.
+"""
+
+from fractions import Fraction
+
+import numpy as np
+
+from oracle import gemm, lora, nvfp4, tolerance
+
+
+def _frac_deq(q):
+    """Dequantize with exact rationals, element by element (independent of nvfp4.dequantize)."""
+    R = q.codes.shape[0]
+    C = q.codes.shape[1] * 2
+    out = [[None] * C for _ in range(R)]
+    for i in range(R):
+        r = Fraction(float(q.rscale[i]))
+        for j in range(C):
+            byte = int(q.codes[i, j // 2])
+            code = (byte >> 4) if j % 2 else (byte & 15)
+            sc = int(q.scales[i, j // 16])
+            e, m = sc >> 3, sc & 7
+            s = Fraction(m, 512) if e == 0 else Fraction(8 + m, 8) * Fraction(2) ** (e - 7)
+            ee, mm = (code >> 1) & 3, code & 1
+            v = Fraction(mm, 2) if ee == 0 else Fraction(2 + mm, 2) * Fraction(2) ** (ee - 1)
+            out[i][j] = (-v if code & 8 else v) * s * r
+    return out
+
+
+def test_gemm_matches_rational_brute_force():
+    rng = np.random.default_rng(5)
+    x = rng.standard_normal((5, 48)) * 3
+    w = rng.standard_normal((7, 48)) * 0.02
+    xq, wf = nvfp4.quantize(x), nvfp4.quantize(w)
+    y, absy = gemm.gemm_fwd(xq, wf)
+    fx, fw = _frac_deq(xq), _frac_deq(wf)
+    for m in range(5):
+        for n in range(7):
+            exact = sum(a * b for a, b in zip(fx[m], fw[n]))
+            abs_exact = sum(abs(a * b) for a, b in zip(fx[m], fw[n]))
+            assert abs(Fraction(y[m, n]) - exact) <= abs_exact * Fraction(1, 2 ** 50)
+            assert abs(Fraction(absy[m, n]) - abs_exact) <= abs_exact * Fraction(1, 2 ** 50)
+
+
+def test_dgrad_uses_backward_layout():
+    """dX = dY_q W_bwd^T with W_bwd = Q(W^T): brute force on a tiny case."""
+    rng = np.random.default_rng(6)
+    w = rng.standard_normal((32, 48)) * 0.02        # [N x K]
+    dy = rng.standard_normal((3, 32)) * 0.01        # [M x N]
+    wf, wb = gemm.weight_layouts(w)
+    assert wf.codes.shape == (32, 24) and wb.codes.shape == (48, 16)
+    dyq = nvfp4.quantize(dy)
+    dx, _ = gemm.gemm_dgrad(dyq, wb)
+    assert dx.shape == (3, 48)
+    fd, fb = _frac_deq(dyq), _frac_deq(wb)
+    for m in range(3):
+        for k in range(48):
+            exact = sum(a * b for a, b in zip(fd[m], fb[k]))
+            assert abs(Fraction(dx[m, k]) - exact) <= Fraction(1, 2 ** 60)
+
+
+def test_integer_special_case_is_exact():
+    """Unit scales: every product is a multiple of 1/4, so the float64 GEMM is exact."""
+    rng = np.random.default_rng(9)
+    M, N, K = 8, 12, 512
+    ca = rng.integers(0, 16, size=(M, K))
+    cb = rng.integers(0, 16, size=(N, K))
+
+    def mk(c):
+        packed = (c[:, 0::2] | (c[:, 1::2] << 4)).astype(np.uint8)
+        return nvfp4.NVFP4(packed, np.full((c.shape[0], c.shape[1] // 16), 0x38, np.uint8),
+                           np.ones(c.shape[0], np.float32))
+
+    y, _ = gemm.gemm_nt(mk(ca), mk(cb))
+    # integer arithmetic: E2M1 value * 2 is an integer
+    ia = np.round(nvfp4.E2M1_ALL[ca] * 2).astype(np.int64)
+    ib = np.round(nvfp4.E2M1_ALL[cb] * 2).astype(np.int64)
+    assert np.array_equal(y * 4, (ia @ ib.T).astype(np.float64))
+
+
+def test_lora_down_and_term():
+    rng = np.random.default_rng(12)
+    x = rng.standard_normal((6, 32))
+    a = rng.standard_normal((4, 32)) * 0.01
+    xq = nvfp4.quantize(x)
+    t, tb, tabs = lora.lora_down(xq, a)
+    fx = _frac_deq(xq)
+    for m in range(6):
+        for j in range(4):
+            exact = sum(p * Fraction(float(q)) for p, q in zip(fx[m], a[j]))
+            abs_exact = sum(abs(p * Fraction(float(q))) for p, q in zip(fx[m], a[j]))
+            assert abs(Fraction(t[m, j]) - exact) <= abs_exact * Fraction(1, 2 ** 50)
+            assert abs(Fraction(tabs[m, j]) - abs_exact) <= abs_exact * Fraction(1, 2 ** 50)
+    assert np.all(np.abs(tb - t) <= tolerance.ulp_bf16(t) / 2)
+    term, _, _ = lora.lora_term(tb, np.zeros((4, 9)), 2.0)
+    assert np.all(term == 0)
+
+
+def test_lora_gradients_by_finite_differences():
+    """dA, dB, dT of L = sum(G * s T B^T), T = X~ A^T, before BF16 rounding."""
+    rng = np.random.default_rng(13)
+    M, K, N, r, s = 5, 32, 7, 3, 0.75
+    xq = nvfp4.quantize(rng.standard_normal((M, K)))
+    xt = nvfp4.dequantize(xq)
+    A = rng.standard_normal((r, K))
+    B = rng.standard_normal((N, r))
+    G = rng.standard_normal((M, N))
+
+    def loss(A_, B_):
+        return float(np.sum(G * (s * (xt @ A_.T) @ B_.T)))
+
+    h = 1e-6
+    num_dA = np.zeros_like(A)
+    for j in range(r):
+        for k in range(K):
+            E = np.zeros_like(A)
+            E[j, k] = h
+            num_dA[j, k] = (loss(A + E, B) - loss(A - E, B)) / (2 * h)
+    num_dB = np.zeros_like(B)
+    for n in range(N):
+        for j in range(r):
+            E = np.zeros_like(B)
+            E[n, j] = h
+            num_dB[n, j] = (loss(A, B + E) - loss(A, B - E)) / (2 * h)
+    out = lora.lora_bwd(xq, A, B, G, s)
+    # the oracle rounds T and dT to BF16 before the next BF16 GEMM; the exact
+    # gradients differ from its results by at most half an ulp of those inputs
+    assert np.all(np.abs(out["dA_exact"] - num_dA) <= out["dA_tslack"] / 2 + 1e-7)
+    assert np.all(np.abs(out["dB_exact"] - num_dB) <= out["dB_tslack"] / 2 + 1e-7)
+    assert np.all(np.abs(out["dT"] - out["dT_exact"]) <= tolerance.ulp_bf16(out["dT_exact"]) / 2)
+    assert np.all(np.abs(out["dA"] - out["dA_exact"]) <= tolerance.ulp_bf16(out["dA_exact"]) / 2)
+
+
+def test_bf16_rne_and_ulp_closed_forms():
+    assert tolerance.ulp_bf16(1.0) == 2.0 ** -7
+    assert tolerance.ulp_bf16(3.0) == 2.0 ** -6
+    assert tolerance.ulp_bf16(-0.75) == 2.0 ** -8
+    assert tolerance.ulp_bf16(0.0) == 2.0 ** -133
+    assert tolerance.ulp_bf16(1e-39) == 2.0 ** -133
+    one = 1.0
+    u = 2.0 ** -7
+    assert tolerance.bf16_rne(one + u / 2) == one                  # tie -> even (1.0)
+    assert tolerance.bf16_rne(one + 1.5 * u) == one + 2 * u        # tie -> even (1 + 2u)
+    assert tolerance.bf16_rne(one + u / 2 + 2.0 ** -40) == one + u # just above the tie
+    assert tolerance.bf16_rne(-(one + u / 2 + 2.0 ** -40)) == -(one + u)
+    assert tolerance.bf16_rne(255.5 * 2.0 ** -7) == 2.0             # carry into next binade
+    # a value that double rounding through float32 would misround
+    v = one + u / 2 + 2.0 ** -30                   # float32 rounds it to the tie point
+    assert tolerance.bf16_rne(v) == one + u
+    assert np.float32(v) == np.float32(one + u / 2)
