@@ -1,0 +1,352 @@
+#!/usr/bin/env python3
+"""Benchmark of the NVFP4 frozen-projection hot path on one MI355X.
+
+One step is one pass of the whole path over a Llama-3B-shaped decoder layer's
+frozen projections at M = 4096 tokens (batch 4 x seq 1024), LoRA rank 16:
+
+  forward   rmsnorm_quant -> q/k/v (lora_down + NVFP4 GEMM with LoRA term)
+            nvfp4_quantize(attention output) -> o
+            rmsnorm_quant -> gate/up -> silu_mul_quant -> down
+  backward  per projection: nvfp4_quantize(dY), lora_bwd, NVFP4 dgrad GEMM
+            (+ LoRA input-gradient term; q/k/v and gate/up accumulate),
+            silu_mul_bwd between down and gate/up, rmsnorm_bwd at both norms
+
+The metric is the NVFP4 fwd + dgrad GEMM throughput of the step:
+  value = (GEMM FLOPs per step) / (wall time per step)   [TFLOP/s]
+with every other kernel of the step inside the timed region.  Inputs are
+synthetic (seeded, BF16, resident in HBM before timing); weights are random
+N(0, 0.02) quantized once to their cached forward and backward layouts
+(offline, untimed).
+
+Prints one JSON line.  --gpus must be 1: this build runs on one GPU.
+"""
+
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK = {"fp16_mfma_tflops": 2500.0, "fp4_mfma_tflops": 10100.0, "hbm_gbs": 8000.0}
+LORA_SCALE = 2.0
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--no-cpu-baseline", action="store_true", help="skip the oracle timing on host cores")
+    ap.add_argument("--cpu-sample-rows", type=int, default=32)
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="also run a 1 GiB read + 1 GiB write elementwise kernel (counter calibration)")
+    return ap.parse_args()
+
+
+class Layer:
+    """Device state of one synthetic Llama-3B decoder layer's frozen-projection path."""
+
+    def __init__(self, fw, torch, synth, wl):
+        self.fw, self.torch = fw, torch
+        M = wl.tokens
+        H, I = 3072, 8192
+        KV = [p.d_out for p in wl.projections if p.name == "k"][0]
+        r = wl.lora_rank
+        self.M, self.H, self.I, self.KV, self.r = M, H, I, KV, r
+        dev = torch.device("cuda:0")
+
+        def up(bits):
+            import numpy as np
+            return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).to(dev)
+
+        act = lambda tid, cols: up(synth.workload_activation(wl, M, cols, tid))
+        self.h1, self.h2, self.attn = act(10, H), act(11, H), act(12, H)
+        self.g1 = up(synth.uniform_bf16((H,), 0.9, 1.1, wl.wid, 13))
+        self.g2 = up(synth.uniform_bf16((H,), 0.9, 1.1, wl.wid, 14))
+        grad = lambda tid, cols: up(synth.normal_bf16((M, cols), wl.dy_std, wl.wid, tid))
+        self.dOut, self.dYo = grad(15, H), grad(16, H)
+        self.dq, self.dk, self.dv = grad(17, H), grad(18, KV), grad(19, KV)
+
+        self.proj = {}
+        for i, p in enumerate(wl.projections):
+            w = up(synth.normal_bf16((p.d_out, p.d_in), wl.w_std, wl.wid, 20 + i))
+            wf, wb = fw.weight_layouts(w)
+            A = up(synth.normal_bf16((r, p.d_in), wl.a_std, wl.wid, 40 + i))
+            B = torch.zeros((p.d_out, r), dtype=torch.bfloat16, device=dev)
+            self.proj[p.name] = dict(p=p, w=w, wf=wf, wb=wb, A=A, B=B,
+                                     T=torch.empty((M, r), dtype=torch.bfloat16, device=dev),
+                                     Y=torch.empty((M, p.d_out), dtype=torch.bfloat16, device=dev),
+                                     dT=torch.empty((M, r), dtype=torch.bfloat16, device=dev),
+                                     dA=torch.empty((r, p.d_in), dtype=torch.bfloat16, device=dev),
+                                     dB=torch.empty((p.d_out, r), dtype=torch.bfloat16, device=dev),
+                                     dyq=fw.empty_nvfp4(M, p.d_out, dev))
+        nv = lambda cols: fw.empty_nvfp4(M, cols, dev)
+        self.y1q, self.y2q, self.aq = nv(H), nv(H), nv(H)
+        self.rstd1 = torch.empty((M,), dtype=torch.float32, device=dev)
+        self.rstd2 = torch.empty((M,), dtype=torch.float32, device=dev)
+        self.hq, self.gq, self.uq = nv(I), nv(I), nv(I)
+        bf = lambda cols: torch.empty((M, cols), dtype=torch.bfloat16, device=dev)
+        self.dh, self.da, self.db = bf(I), bf(I), bf(I)
+        self.dy1, self.dy2, self.dattn, self.dx1, self.dx2 = bf(H), bf(H), bf(H), bf(H), bf(H)
+        self.record = None       # list to append (category, name, start_event, end_event, work) into
+
+    # ---- instrumented launch helper ----
+    def _ev(self, cat, name, work, fn):
+        if self.record is None:
+            return fn()
+        e0 = self.torch.cuda.Event(enable_timing=True)
+        e1 = self.torch.cuda.Event(enable_timing=True)
+        e0.record()
+        out = fn()
+        e1.record()
+        self.record.append((cat, name, e0, e1, work))
+        return out
+
+    def _fwd_proj(self, name, xq):
+        fw, P = self.fw, self.proj[name]
+        p = P["p"]
+        self._ev("lora", "lora_down", None, lambda: fw.lora_down(xq, P["A"], out=P["T"]))
+        work = ("gemm", self.M, p.d_out, p.d_in)
+        self._ev("gemm", f"fwd {name}", work,
+                 lambda: fw.gemm_fwd(xq, P["wf"], lora_t=P["T"], lora_b=P["B"], lora_scale=LORA_SCALE, out=P["Y"]))
+        return P["Y"]
+
+    def _bwd_proj(self, name, xq, dy, dx, accumulate):
+        fw, P = self.fw, self.proj[name]
+        p = P["p"]
+        self._ev("quant", "nvfp4_quantize", ("quant", self.M, p.d_out),
+                 lambda: fw.quantize(dy, out=P["dyq"]))
+        self._ev("lora", "lora_bwd", None,
+                 lambda: fw.lora_bwd(xq, P["A"], P["B"], dy, LORA_SCALE, out=(P["dT"], P["dA"], P["dB"])))
+        work = ("gemm", self.M, p.d_in, p.d_out)
+        self._ev("gemm", f"dgrad {name}", work,
+                 lambda: fw.gemm_dgrad(P["dyq"], P["wb"], out=dx, accumulate=accumulate, lora_dt=P["dT"],
+                                       lora_a=P["A"]))
+
+    def step(self):
+        fw = self.fw
+        M, H, I = self.M, self.H, self.I
+        # ---------------- forward ----------------
+        self._ev("quant", "rmsnorm_quant", ("rmsq", M, H),
+                 lambda: fw.rmsnorm_quant(self.h1, self.g1, 1e-5, out=(self.y1q, self.rstd1)))
+        for n in ("q", "k", "v"):
+            self._fwd_proj(n, self.y1q)
+        self._ev("quant", "nvfp4_quantize", ("quant", M, H), lambda: fw.quantize(self.attn, out=self.aq))
+        self._fwd_proj("o", self.aq)
+        self._ev("quant", "rmsnorm_quant", ("rmsq", M, H),
+                 lambda: fw.rmsnorm_quant(self.h2, self.g2, 1e-5, out=(self.y2q, self.rstd2)))
+        a = self._fwd_proj("gate", self.y2q)
+        b = self._fwd_proj("up", self.y2q)
+        self._ev("quant", "silu_mul_quant", ("silu", M, I),
+                 lambda: fw.silu_mul_quant(a, b, out=(self.hq, self.gq, self.uq)))
+        self._fwd_proj("down", self.hq)
+        # ---------------- backward ----------------
+        self._bwd_proj("down", self.hq, self.dOut, self.dh, False)
+        self._ev("bwd", "silu_mul_bwd", ("silub", M, I),
+                 lambda: fw.silu_mul_bwd(self.gq, self.uq, self.dh, out=(self.da, self.db)))
+        self._bwd_proj("gate", self.y2q, self.da, self.dy2, False)
+        self._bwd_proj("up", self.y2q, self.db, self.dy2, True)
+        self._ev("bwd", "rmsnorm_bwd", ("rmsb", M, H),
+                 lambda: fw.rmsnorm_bwd(self.y2q, self.rstd2, self.g2, self.dy2, out=self.dx2))
+        self._bwd_proj("o", self.aq, self.dYo, self.dattn, False)
+        self._bwd_proj("q", self.y1q, self.dq, self.dy1, False)
+        self._bwd_proj("k", self.y1q, self.dk, self.dy1, True)
+        self._bwd_proj("v", self.y1q, self.dv, self.dy1, True)
+        self._ev("bwd", "rmsnorm_bwd", ("rmsb", M, H),
+                 lambda: fw.rmsnorm_bwd(self.y1q, self.rstd1, self.g1, self.dy1, out=self.dx1))
+
+    def gemm_flops(self):
+        return sum(4 * self.M * P["p"].d_in * P["p"].d_out for P in self.proj.values())
+
+
+# algorithmic bytes per element of each bandwidth-bound kernel (inputs read + outputs written)
+BYTES_PER_ELEM = {"quant": 2.0 + 0.5 + 1 / 16, "rmsq": 2.0 + 0.5 + 1 / 16, "silu": 4.0 + 3 * (0.5 + 1 / 16),
+                  "silub": 2 * (0.5 + 1 / 16) + 2.0 + 4.0, "rmsb": (0.5 + 1 / 16) + 2.0 + 2.0}
+BYTES_PER_ROW = {"quant": 4, "rmsq": 8, "silu": 12, "silub": 8, "rmsb": 8}
+
+
+def kernel_bytes(kind, rows, cols):
+    return BYTES_PER_ELEM[kind] * rows * cols + BYTES_PER_ROW[kind] * rows
+
+
+def src_hash(*names):
+    h = hashlib.sha256()
+    for n in names:
+        h.update(open(os.path.join(ROOT, "frozen_weight_gemms_amd", "csrc", n), "rb").read())
+    return h.hexdigest()[:16]
+
+
+def cpu_baseline(wl, layer_bits, sample_rows):
+    """Time the oracle (as it stands) on a bounded row sample of the same step's GEMMs."""
+    import numpy as np
+    import synth
+    from oracle import gemm as ogemm
+    from oracle import nvfp4 as onv
+
+    vals = lambda b: (np.asarray(b, np.uint16).astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    rng = np.random.default_rng(0)
+    rows = np.sort(rng.choice(wl.tokens, size=sample_rows, replace=False))
+    # offline weight layouts (not timed)
+    wts = {}
+    for i, p in enumerate(wl.projections):
+        w = vals(synth.normal_bf16((p.d_out, p.d_in), wl.w_std, wl.wid, 20 + i))
+        wts[p.name] = ogemm.weight_layouts(w)
+    xs = {n: vals(b[rows]) for n, b in layer_bits.items()}
+    t0 = time.perf_counter()
+    flops = 0
+    for p in wl.projections:
+        wf, wb = wts[p.name]
+        xq = onv.quantize(xs["x_" + p.name])
+        ogemm.gemm_fwd(xq, wf)
+        dyq = onv.quantize(xs["dy_" + p.name])
+        ogemm.gemm_dgrad(dyq, wb)
+        flops += 4 * sample_rows * p.d_in * p.d_out
+    dt = time.perf_counter() - t0
+    try:
+        cores = len(os.sched_getaffinity(0))
+    except AttributeError:
+        cores = os.cpu_count()
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": cores, "kind": "oracle",
+            "sample": f"{sample_rows} of {wl.tokens} token rows of every projection's input and output "
+                      f"gradient: oracle quantize of the rows, then its float64 fwd and dgrad GEMMs against "
+                      f"the full cached weight layouts (dequantized per call); {dt:.1f} s wall, "
+                      f"{flops / 1e9:.1f} GFLOP"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the multi-GPU layout is "
+              f"described in the design notes but not built.", file=sys.stderr)
+        sys.exit(2)
+    import numpy as np
+    import torch
+
+    import frozen_weight_gemms_amd as fw
+    import synth
+    from frozen_weight_gemms_amd import _lib
+
+    wl = synth.WORKLOADS[2]
+    torch.cuda.set_device(0)
+    layer = Layer(fw, torch, synth, wl)
+    torch.cuda.synchronize()
+
+    for _ in range(args.warmup):
+        layer.step()
+    torch.cuda.synchronize()
+
+    # timed region: K steps, wall clock + events on the launch stream
+    layer.record = []
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    ev0.record()
+    for _ in range(args.steps):
+        layer.step()
+    ev1.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    gpu_ms = ev0.elapsed_time(ev1)
+    recs = layer.record
+    layer.record = None
+
+    ms_per_step = wall * 1e3 / args.steps
+    flops = layer.gemm_flops()
+    value = flops / (ms_per_step * 1e-3) / 1e12
+
+    # per-kernel times from the events
+    cat_ms, gemm_by_tile, bw = {}, {}, {}
+    for cat, name, e0, e1, work in recs:
+        t = e0.elapsed_time(e1)
+        cat_ms[cat] = cat_ms.get(cat, 0.0) + t
+        if cat == "gemm":
+            _, M, N, K = work
+            tile = _lib.gemm_tile(M, N, K)
+            g = gemm_by_tile.setdefault(tile, [0.0, 0.0, 0])
+            g[0] += t
+            g[1] += 2.0 * M * N * K
+            g[2] += 1
+        elif work is not None:
+            kind, rows, cols = work
+            b = bw.setdefault(name, [0.0, 0.0, 0])
+            b[0] += t
+            b[1] += kernel_bytes(kind, rows, cols)
+            b[2] += 1
+    steps = args.steps
+    gemm_ms = cat_ms.get("gemm", 0.0) / steps
+    dom_tile = max(gemm_by_tile, key=lambda k: gemm_by_tile[k][0])
+    dt_ms, dflops, dcount = gemm_by_tile[dom_tile]
+    achieved = dflops / (dt_ms * 1e-3) / 1e12
+    kname = f"pact::k_gemm_nvfp4<{dom_tile[0] // 64}, {dom_tile[1] // 64}>"
+
+    traffic = None
+    tfile = os.path.join(ROOT, "profiles", "gemm_traffic.json")
+    if os.path.exists(tfile):
+        try:
+            tj = json.load(open(tfile))
+            if tj.get("src_hash") == src_hash("gemm.hip", "nvfp4_device.h") and tj.get("tile") == list(dom_tile):
+                traffic = tj.get("bytes_per_launch")
+        except (ValueError, OSError):
+            traffic = None
+
+    quant = {n: {"GB/s": round(b[1] / (b[0] * 1e-3) / 1e9, 1), "frac_hbm": round(b[1] / (b[0] * 1e-3) / 8e12, 3),
+                 "us_per_launch": round(b[0] * 1e3 / b[2], 2)} for n, b in bw.items()}
+
+    result = {
+        "metric": "NVFP4 fwd+dgrad GEMM TFLOP/s at Llama-3B shapes; % FP4 MFMA peak",
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "nvfp4 operands, fp16 MFMA (exact products), fp32 accumulation, bf16 output",
+        "data": "synthetic (seeded BF16 activations with 1% outlier channels, N(0,0.02) weights, N(0,0.01) grads)",
+        "config": {"workload": "llama3b-decoder-layer frozen projections fwd+dgrad + fused quantizers + LoRA r16",
+                   "tokens": layer.M, "hidden": layer.H, "intermediate": layer.I, "kv": layer.KV,
+                   "lora_rank": layer.r, "gemm_gflop_per_step": round(flops / 1e9, 1), "parallelism": "single-gpu"},
+        "frac_fp4_peak": round(value / PEAK["fp4_mfma_tflops"], 4),
+        "frac_fp16_peak": round(value / PEAK["fp16_mfma_tflops"], 4),
+        "gemm_only_tflops": round(flops / (gemm_ms * 1e-3) / 1e12, 1),
+        "gpu_ms_per_step_events": round(gpu_ms / steps, 4),
+        "ms_per_step_by_category": {k: round(v / steps, 4) for k, v in sorted(cat_ms.items())},
+        "bandwidth_kernels": quant,
+        "roofline": {"kernel": kname, "bound": "mfma", "achieved": round(achieved, 1),
+                     "peak": PEAK["fp16_mfma_tflops"], "unit": "TFLOP/s",
+                     "frac": round(achieved / PEAK["fp16_mfma_tflops"], 4),
+                     "frac_of_fp4_peak": round(achieved / PEAK["fp4_mfma_tflops"], 4),
+                     "launches_per_step": dcount // steps,
+                     "avg_launch_us": round(dt_ms * 1e3 / dcount, 2),
+                     "traffic": traffic},
+    }
+    if args.copy_calibration:
+        x = torch.empty(1 << 29, dtype=torch.bfloat16, device="cuda")   # 1 GiB
+        y = torch.empty_like(x)
+        torch.neg(x, out=y)
+        torch.cuda.synchronize()
+    if not args.no_cpu_baseline:
+        rows_bits = {}
+        H, KV, I = layer.H, layer.KV, layer.I
+        for name, cols, tid in (("x_q", H, 10), ("x_k", H, 10), ("x_v", H, 10), ("x_o", H, 12),
+                                ("x_gate", H, 11), ("x_up", H, 11)):
+            rows_bits[name] = synth.workload_activation(wl, wl.tokens, cols, tid)
+        # the down projection's input in the step is silu(gate) * up; a fresh activation of that shape
+        rows_bits["x_down"] = synth.workload_activation(wl, wl.tokens, I, 99)
+        for name, cols, tid in (("dy_down", H, 15), ("dy_o", H, 16), ("dy_q", H, 17), ("dy_k", KV, 18),
+                                ("dy_v", KV, 19), ("dy_gate", I, 98), ("dy_up", I, 97)):
+            rows_bits[name] = synth.normal_bf16((wl.tokens, cols), wl.dy_std, wl.wid, tid)
+        result["cpu_baseline"] = cpu_baseline(wl, rows_bits, args.cpu_sample_rows)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,201 @@
+"""NVFP4 frozen-projection path of PACT's LoRA fine-tuning, native on MI355X.
+
+Thin torch-facing wrappers over the C ABI in include/pact_nvfp4.h.  torch
+provides device memory and the current HIP stream; every operation runs in
+the hand-written gfx950 kernels of libpact_nvfp4.so.  The wrappers allocate
+outputs with torch and pass raw pointers; they compute nothing themselves.
+"""
+
+from __future__ import annotations
+
+import dataclasses
+
+import torch
+
+from . import _lib
+from ._lib import PactError, load  # noqa: F401
+
+__all__ = [
+    "NVFP4Tensor", "empty_nvfp4", "quantize", "rmsnorm_quant", "silu_mul_quant", "gemm_fwd", "gemm_dgrad",
+    "lora_down", "lora_bwd", "silu_mul_bwd", "rmsnorm_bwd", "weight_layouts", "PactError",
+]
+
+
+@dataclasses.dataclass
+class NVFP4Tensor:
+    """Canonical NVFP4 tensor [rows x cols]: codes u8 [rows, cols/2], scales u8 [rows, cols/16], rscale f32 [rows]."""
+    codes: torch.Tensor
+    scales: torch.Tensor
+    rscale: torch.Tensor
+
+    @property
+    def rows(self) -> int:
+        return self.codes.shape[0]
+
+    @property
+    def cols(self) -> int:
+        return self.codes.shape[1] * 2
+
+    def ptrs(self):
+        return self.codes.data_ptr(), self.scales.data_ptr(), self.rscale.data_ptr()
+
+
+def _stream():
+    return torch.cuda.current_stream().cuda_stream
+
+
+def _ptr(t):
+    return None if t is None else t.data_ptr()
+
+
+def _bf16(t: torch.Tensor, name: str) -> torch.Tensor:
+    if t.dtype != torch.bfloat16:
+        raise TypeError(f"{name} must be bfloat16 (got {t.dtype})")
+    if not t.is_cuda:
+        raise TypeError(f"{name} must be a device tensor")
+    return t
+
+
+def empty_nvfp4(rows: int, cols: int, device="cuda") -> NVFP4Tensor:
+    if cols % 16:
+        raise ValueError("cols must be a multiple of 16")
+    return NVFP4Tensor(
+        torch.empty((rows, cols // 2), dtype=torch.uint8, device=device),
+        torch.empty((rows, cols // 16), dtype=torch.uint8, device=device),
+        torch.empty((rows,), dtype=torch.float32, device=device),
+    )
+
+
+def quantize(x: torch.Tensor, transpose: bool = False, out: NVFP4Tensor | None = None) -> NVFP4Tensor:
+    """nvfp4_quantize: Q(x) (blocks along the last axis) or, with transpose, Q(x^T)."""
+    _bf16(x, "x")
+    if x.dim() != 2 or x.stride(1) != 1:
+        raise ValueError("x must be a 2-D tensor with unit column stride")
+    if transpose:
+        rows, cols = x.shape[1], x.shape[0]
+    else:
+        rows, cols = x.shape
+    out = out or empty_nvfp4(rows, cols, x.device)
+    _lib.call("nvfp4_quantize", x.data_ptr(), rows, cols, x.stride(0), int(transpose), *out.ptrs(), _stream())
+    return out
+
+
+def weight_layouts(w: torch.Tensor):
+    """Cached forward and backward layouts (Q(W), Q(W^T)) of a frozen BF16 weight W [N x K]."""
+    return quantize(w), quantize(w, transpose=True)
+
+
+def rmsnorm_quant(x: torch.Tensor, gain: torch.Tensor, eps: float = 1e-5, out=None):
+    """(Q(y), rstd) with y = (x * rstd) * gain; ``out`` = (NVFP4Tensor, rstd) to reuse buffers."""
+    _bf16(x, "x"); _bf16(gain, "gain")
+    M, H = x.shape
+    if out is not None:
+        y, rstd = out
+    else:
+        y = empty_nvfp4(M, H, x.device)
+        rstd = torch.empty((M,), dtype=torch.float32, device=x.device)
+    _lib.call("rmsnorm_quant", x.data_ptr(), gain.data_ptr(), float(eps), M, H, x.stride(0), *y.ptrs(),
+              rstd.data_ptr(), _stream())
+    return y, rstd
+
+
+def silu_mul_quant(gate: torch.Tensor, up: torch.Tensor, out=None):
+    """(Q(h), Q(gate), Q(up)) with h = silu(gate) * up; ``out`` = three NVFP4Tensors to reuse."""
+    _bf16(gate, "gate"); _bf16(up, "up")
+    if gate.shape != up.shape or gate.stride() != up.stride():
+        raise ValueError("gate and up must have the same shape and strides")
+    M, I = gate.shape
+    h, gq, uq = out if out is not None else (empty_nvfp4(M, I, gate.device) for _ in range(3))
+    _lib.call("silu_mul_quant", gate.data_ptr(), up.data_ptr(), M, I, gate.stride(0), *h.ptrs(), *gq.ptrs(),
+              *uq.ptrs(), _stream())
+    return h, gq, uq
+
+
+def gemm_fwd(xq: NVFP4Tensor, w_fwd: NVFP4Tensor, lora_t: torch.Tensor | None = None,
+             lora_b: torch.Tensor | None = None, lora_scale: float = 1.0, out: torch.Tensor | None = None):
+    """Y = bf16(deq(X_q) deq(W_fwd)^T [+ lora_scale * T B^T])."""
+    M, K = xq.rows, xq.cols
+    N = w_fwd.rows
+    if w_fwd.cols != K:
+        raise ValueError(f"K mismatch: {K} vs {w_fwd.cols}")
+    out = out if out is not None else torch.empty((M, N), dtype=torch.bfloat16, device=xq.codes.device)
+    r = 0
+    if lora_t is not None:
+        r = lora_t.shape[1]
+        if lora_b is None or lora_b.shape != (N, r) or lora_t.shape[0] != M:
+            raise ValueError("LoRA shapes: T [M x r], B [N x r]")
+    _lib.call("nvfp4_gemm_fwd", *xq.ptrs(), M, K, *w_fwd.ptrs(), N, out.data_ptr(), out.stride(0),
+              _ptr(lora_t), _ptr(lora_b), r, float(lora_scale), _stream())
+    return out
+
+
+def gemm_dgrad(dyq: NVFP4Tensor, w_bwd: NVFP4Tensor, out: torch.Tensor | None = None, accumulate: bool = False,
+               lora_dt: torch.Tensor | None = None, lora_a: torch.Tensor | None = None):
+    """dX = bf16([f32(dX) +] deq(dY_q) deq(W_bwd)^T [+ dT A])."""
+    M, N = dyq.rows, dyq.cols
+    K = w_bwd.rows
+    if w_bwd.cols != N:
+        raise ValueError(f"N mismatch: {N} vs {w_bwd.cols}")
+    if out is None:
+        if accumulate:
+            raise ValueError("accumulate needs an existing output")
+        out = torch.empty((M, K), dtype=torch.bfloat16, device=dyq.codes.device)
+    r = 0
+    if lora_dt is not None:
+        r = lora_dt.shape[1]
+        if lora_a is None or lora_a.shape != (r, K) or lora_dt.shape[0] != M:
+            raise ValueError("LoRA shapes: dT [M x r], A [r x K]")
+    _lib.call("nvfp4_gemm_dgrad", *dyq.ptrs(), M, N, *w_bwd.ptrs(), K, out.data_ptr(), out.stride(0),
+              int(accumulate), _ptr(lora_dt), _ptr(lora_a), r, _stream())
+    return out
+
+
+def lora_down(xq: NVFP4Tensor, A: torch.Tensor, out: torch.Tensor | None = None):
+    _bf16(A, "A")
+    r, K = A.shape
+    if K != xq.cols:
+        raise ValueError("A must be [r x K]")
+    out = out if out is not None else torch.empty((xq.rows, r), dtype=torch.bfloat16, device=A.device)
+    _lib.call("lora_down", *xq.ptrs(), xq.rows, K, A.data_ptr(), r, out.data_ptr(), _stream())
+    return out
+
+
+def lora_bwd(xq: NVFP4Tensor, A: torch.Tensor, B: torch.Tensor, dy: torch.Tensor, scale: float, out=None):
+    """(dT, dA, dB); ``out`` = (dT, dA, dB) tensors to reuse."""
+    _bf16(A, "A"); _bf16(B, "B"); _bf16(dy, "dy")
+    r, K = A.shape
+    N = B.shape[0]
+    M = xq.rows
+    if B.shape != (N, r) or dy.shape != (M, N) or K != xq.cols:
+        raise ValueError("shapes: A [r x K], B [N x r], dy [M x N]")
+    dev = A.device
+    if out is not None:
+        dT, dA, dB = out
+    else:
+        dT = torch.empty((M, r), dtype=torch.bfloat16, device=dev)
+        dA = torch.empty((r, K), dtype=torch.bfloat16, device=dev)
+        dB = torch.empty((N, r), dtype=torch.bfloat16, device=dev)
+    _lib.call("lora_bwd", *xq.ptrs(), M, K, A.data_ptr(), B.data_ptr(), r, float(scale), dy.data_ptr(), N,
+              dT.data_ptr(), dA.data_ptr(), dB.data_ptr(), _stream())
+    return dT, dA, dB
+
+
+def silu_mul_bwd(gq: NVFP4Tensor, uq: NVFP4Tensor, dh: torch.Tensor, out=None):
+    _bf16(dh, "dh")
+    M, I = dh.shape
+    dg, du = out if out is not None else (torch.empty_like(dh), torch.empty_like(dh))
+    _lib.call("silu_mul_bwd", *gq.ptrs(), *uq.ptrs(), dh.data_ptr(), M, I, dg.data_ptr(), du.data_ptr(), _stream())
+    return dg, du
+
+
+def rmsnorm_bwd(yq: NVFP4Tensor, rstd: torch.Tensor, gain: torch.Tensor, dy: torch.Tensor, out=None):
+    _bf16(gain, "gain"); _bf16(dy, "dy")
+    M, H = dy.shape
+    dx = out if out is not None else torch.empty_like(dy)
+    _lib.call("rmsnorm_bwd", *yq.ptrs(), rstd.data_ptr(), gain.data_ptr(), dy.data_ptr(), M, H, dx.data_ptr(),
+              _stream())
+    return dx
+
+
+# fail loudly at import if the native library is missing
+load()

@@ -1,0 +1,277 @@
+// C ABI of the NVFP4 frozen-projection library: argument validation (on the
+// host, before any HIP call) and dispatch to the kernel launchers.  The
+// contract of every entry point is stated in include/pact_nvfp4.h.
+#include <cstdarg>
+#include <cstdio>
+#include <cstdlib>
+#include <cstring>
+
+#include "pact_internal.h"
+#include "pact_nvfp4.h"
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+int fail(int code, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof(g_err), fmt, ap);
+  va_end(ap);
+  return code;
+}
+
+int ok() {
+  g_err[0] = '\0';
+  return PACT_OK;
+}
+
+int hip_status(hipError_t e, const char* what) {
+  if (e == hipSuccess) return ok();
+  return fail(PACT_EHIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+#define REQUIRE(cond, code, ...) \
+  do {                           \
+    if (!(cond)) return fail(code, __VA_ARGS__); \
+  } while (0)
+
+#define REQUIRE_PTR(p, name)                                                   \
+  do {                                                                         \
+    if ((p) == nullptr) return fail(PACT_EINVAL, "%s is NULL", name);          \
+    if (!aligned16(p)) return fail(PACT_EALIGN, "%s is not 16-byte aligned", name); \
+  } while (0)
+
+constexpr int64_t kMaxFusedCols = 16384;
+constexpr int64_t kMaxRank = 128;
+
+int check_nvfp4(const uint8_t* c, const uint8_t* s, const float* r, const char* name) {
+  char buf[64];
+  snprintf(buf, sizeof(buf), "%s codes", name);
+  if (c == nullptr) return fail(PACT_EINVAL, "%s is NULL", buf);
+  if (!aligned16(c)) return fail(PACT_EALIGN, "%s is not 16-byte aligned", buf);
+  snprintf(buf, sizeof(buf), "%s scales", name);
+  if (s == nullptr) return fail(PACT_EINVAL, "%s is NULL", buf);
+  if (!aligned16(s)) return fail(PACT_EALIGN, "%s is not 16-byte aligned", buf);
+  snprintf(buf, sizeof(buf), "%s rscale", name);
+  if (r == nullptr) return fail(PACT_EINVAL, "%s is NULL", buf);
+  if (!aligned16(r)) return fail(PACT_EALIGN, "%s is not 16-byte aligned", buf);
+  return PACT_OK;
+}
+
+hipStream_t as_stream(void* s) { return reinterpret_cast<hipStream_t>(s); }
+
+}  // namespace
+
+extern "C" {
+
+const char* pact_last_error(void) { return g_err; }
+
+int pact_abi_version(void) { return 1; }
+
+int pact_nvfp4_sizes(int64_t rows, int64_t cols, size_t* codes_bytes, size_t* scales_bytes, size_t* rscale_bytes) {
+  REQUIRE(rows >= 0 && cols >= 0, PACT_EINVAL, "negative size (rows=%lld, cols=%lld)", (long long)rows,
+          (long long)cols);
+  REQUIRE(cols % 16 == 0, PACT_ESHAPE, "cols=%lld is not a multiple of 16", (long long)cols);
+  REQUIRE(codes_bytes && scales_bytes && rscale_bytes, PACT_EINVAL, "NULL output pointer");
+  *codes_bytes = (size_t)(rows * (cols / 2));
+  *scales_bytes = (size_t)(rows * (cols / 16));
+  *rscale_bytes = (size_t)rows * sizeof(float);
+  return ok();
+}
+
+int pact_gemm_tile(int64_t M, int64_t Nout, int64_t Kr, int* bm, int* bn) {
+  REQUIRE(M >= 0 && Nout >= 0 && Kr >= 0, PACT_EINVAL, "negative size");
+  REQUIRE(bm != nullptr && bn != nullptr, PACT_EINVAL, "NULL output pointer");
+  pact::gemm_tile(M, Nout, bm, bn);
+  return ok();
+}
+
+int nvfp4_quantize(const uint16_t* x, int64_t rows, int64_t cols, int64_t ldx, int transpose, uint8_t* codes,
+                   uint8_t* scales, float* rscale, void* stream) {
+  REQUIRE(rows >= 0 && cols >= 0, PACT_EINVAL, "negative size (rows=%lld, cols=%lld)", (long long)rows,
+          (long long)cols);
+  REQUIRE(transpose == 0 || transpose == 1, PACT_EINVAL, "transpose must be 0 or 1 (got %d)", transpose);
+  REQUIRE(cols % 16 == 0, PACT_ESHAPE, "cols=%lld is not a multiple of 16", (long long)cols);
+  if (rows == 0) return ok();
+  REQUIRE_PTR(x, "x");
+  int st = check_nvfp4(codes, scales, rscale, "out");
+  if (st != PACT_OK) return st;
+  if (transpose == 0) {
+    REQUIRE(ldx >= cols, PACT_ESHAPE, "ldx=%lld < cols=%lld", (long long)ldx, (long long)cols);
+    REQUIRE(ldx % 8 == 0, PACT_EALIGN, "ldx=%lld is not a multiple of 8 elements", (long long)ldx);
+  } else {
+    REQUIRE(ldx >= rows, PACT_ESHAPE, "ldx=%lld < rows=%lld (transposed input is [cols x rows])", (long long)ldx,
+            (long long)rows);
+  }
+  REQUIRE(rows <= 0x7FFFFFFF, PACT_EUNSUPPORTED, "rows=%lld exceeds the grid limit", (long long)rows);
+  return hip_status(pact::launch_quantize(x, rows, cols, ldx, transpose, codes, scales, rscale, as_stream(stream)),
+                    "nvfp4_quantize launch");
+}
+
+int rmsnorm_quant(const uint16_t* x, const uint16_t* gain, float eps, int64_t M, int64_t H, int64_t ldx,
+                  uint8_t* y_codes, uint8_t* y_scales, float* y_rscale, float* rstd, void* stream) {
+  REQUIRE(M >= 0 && H >= 0, PACT_EINVAL, "negative size (M=%lld, H=%lld)", (long long)M, (long long)H);
+  REQUIRE(H % 16 == 0, PACT_ESHAPE, "H=%lld is not a multiple of 16", (long long)H);
+  REQUIRE(H <= kMaxFusedCols, PACT_EUNSUPPORTED, "H=%lld exceeds %lld", (long long)H, (long long)kMaxFusedCols);
+  REQUIRE(eps >= 0.0f, PACT_EINVAL, "eps must be non-negative");
+  if (M == 0) return ok();
+  REQUIRE(H > 0, PACT_ESHAPE, "H must be positive");
+  REQUIRE_PTR(x, "x");
+  REQUIRE_PTR(gain, "gain");
+  REQUIRE_PTR(rstd, "rstd");
+  int st = check_nvfp4(y_codes, y_scales, y_rscale, "y");
+  if (st != PACT_OK) return st;
+  REQUIRE(ldx >= H && ldx % 8 == 0, PACT_ESHAPE, "ldx=%lld must be >= H and a multiple of 8", (long long)ldx);
+  REQUIRE(M <= 0x7FFFFFFF, PACT_EUNSUPPORTED, "M=%lld exceeds the grid limit", (long long)M);
+  const char* fe = getenv("PACT_RMSNORM_EXACT_SUM");
+  const int force_exact = (fe != nullptr && fe[0] == '1') ? 1 : 0;
+  return hip_status(pact::launch_rmsnorm_quant(x, gain, eps, M, H, ldx, y_codes, y_scales, y_rscale, rstd,
+                                               force_exact, as_stream(stream)),
+                    "rmsnorm_quant launch");
+}
+
+int silu_mul_quant(const uint16_t* gate, const uint16_t* up, int64_t M, int64_t I, int64_t ld, uint8_t* h_codes,
+                   uint8_t* h_scales, float* h_rscale, uint8_t* g_codes, uint8_t* g_scales, float* g_rscale,
+                   uint8_t* u_codes, uint8_t* u_scales, float* u_rscale, void* stream) {
+  REQUIRE(M >= 0 && I >= 0, PACT_EINVAL, "negative size (M=%lld, I=%lld)", (long long)M, (long long)I);
+  REQUIRE(I % 16 == 0, PACT_ESHAPE, "I=%lld is not a multiple of 16", (long long)I);
+  REQUIRE(I <= kMaxFusedCols, PACT_EUNSUPPORTED, "I=%lld exceeds %lld", (long long)I, (long long)kMaxFusedCols);
+  if (M == 0) return ok();
+  REQUIRE_PTR(gate, "gate");
+  REQUIRE_PTR(up, "up");
+  int st = check_nvfp4(h_codes, h_scales, h_rscale, "h");
+  if (st == PACT_OK) st = check_nvfp4(g_codes, g_scales, g_rscale, "gate_q");
+  if (st == PACT_OK) st = check_nvfp4(u_codes, u_scales, u_rscale, "up_q");
+  if (st != PACT_OK) return st;
+  REQUIRE(ld >= I && ld % 8 == 0, PACT_ESHAPE, "ld=%lld must be >= I and a multiple of 8", (long long)ld);
+  REQUIRE(M <= 0x7FFFFFFF, PACT_EUNSUPPORTED, "M=%lld exceeds the grid limit", (long long)M);
+  return hip_status(pact::launch_silu_mul_quant(gate, up, M, I, ld, h_codes, h_scales, h_rscale, g_codes, g_scales,
+                                                g_rscale, u_codes, u_scales, u_rscale, as_stream(stream)),
+                    "silu_mul_quant launch");
+}
+
+static int gemm_common(pact::GemmArgs& a, const char* name, void* stream) {
+  REQUIRE(a.M >= 0 && a.N >= 0 && a.K >= 0, PACT_EINVAL, "%s: negative size", name);
+  REQUIRE(a.K % 16 == 0, PACT_ESHAPE, "%s: contraction length %lld is not a multiple of 16", name,
+          (long long)a.K);
+  if (a.M == 0 || a.N == 0) return ok();
+  int st = check_nvfp4(a.a_codes, a.a_scales, a.a_rscale, "A");
+  if (st == PACT_OK) st = check_nvfp4(a.b_codes, a.b_scales, a.b_rscale, "B");
+  if (st != PACT_OK) return st;
+  REQUIRE(a.out != nullptr, PACT_EINVAL, "%s: output is NULL", name);
+  REQUIRE((reinterpret_cast<uintptr_t>(a.out) & 1u) == 0, PACT_EALIGN, "%s: output is not 2-byte aligned", name);
+  REQUIRE(a.ldo >= a.N, PACT_ESHAPE, "%s: leading dimension %lld < %lld", name, (long long)a.ldo, (long long)a.N);
+  if (a.lora_t != nullptr) {
+    REQUIRE(a.lora_u != nullptr, PACT_EINVAL, "%s: LoRA T given without its second factor", name);
+    REQUIRE(a.lora_r >= 1 && a.lora_r <= kMaxRank, PACT_ESHAPE, "%s: LoRA rank %lld outside [1, %lld]", name,
+            (long long)a.lora_r, (long long)kMaxRank);
+  }
+  REQUIRE((a.M + 127) / 128 * ((a.N + 127) / 128) < 0x7FFFFFFF, PACT_EUNSUPPORTED, "%s: too many tiles", name);
+  return hip_status(pact::launch_gemm(a, as_stream(stream)), name);
+}
+
+int nvfp4_gemm_fwd(const uint8_t* x_codes, const uint8_t* x_scales, const float* x_rscale, int64_t M, int64_t K,
+                   const uint8_t* w_codes, const uint8_t* w_scales, const float* w_rscale, int64_t N, uint16_t* y,
+                   int64_t ldy, const uint16_t* lora_t, const uint16_t* lora_b, int64_t lora_r, float lora_scale,
+                   void* stream) {
+  pact::GemmArgs a{};
+  a.a_codes = x_codes; a.a_scales = x_scales; a.a_rscale = x_rscale;
+  a.b_codes = w_codes; a.b_scales = w_scales; a.b_rscale = w_rscale;
+  a.M = M; a.N = N; a.K = K;
+  a.out = y; a.ldo = ldy; a.accumulate = 0;
+  a.lora_t = lora_t; a.lora_u = lora_b;
+  a.u_stride_j = 1; a.u_stride_n = lora_r;   // U(j, n) = B[n][j], B is [N x r]
+  a.lora_r = lora_r; a.lora_scale = lora_scale;
+  return gemm_common(a, "nvfp4_gemm_fwd", stream);
+}
+
+int nvfp4_gemm_dgrad(const uint8_t* dy_codes, const uint8_t* dy_scales, const float* dy_rscale, int64_t M, int64_t N,
+                     const uint8_t* w_codes, const uint8_t* w_scales, const float* w_rscale, int64_t K, uint16_t* dx,
+                     int64_t lddx, int accumulate, const uint16_t* lora_dt, const uint16_t* lora_a, int64_t lora_r,
+                     void* stream) {
+  REQUIRE(accumulate == 0 || accumulate == 1, PACT_EINVAL, "accumulate must be 0 or 1 (got %d)", accumulate);
+  pact::GemmArgs a{};
+  a.a_codes = dy_codes; a.a_scales = dy_scales; a.a_rscale = dy_rscale;
+  a.b_codes = w_codes; a.b_scales = w_scales; a.b_rscale = w_rscale;
+  a.M = M; a.N = K; a.K = N;                 // output [M x K], contraction over N
+  a.out = dx; a.ldo = lddx; a.accumulate = accumulate;
+  a.lora_t = lora_dt; a.lora_u = lora_a;
+  a.u_stride_j = K; a.u_stride_n = 1;        // U(j, k) = A[j][k], A is [r x K]
+  a.lora_r = lora_r; a.lora_scale = 1.0f;
+  return gemm_common(a, "nvfp4_gemm_dgrad", stream);
+}
+
+int lora_down(const uint8_t* x_codes, const uint8_t* x_scales, const float* x_rscale, int64_t M, int64_t K,
+              const uint16_t* A, int64_t r, uint16_t* T, void* stream) {
+  REQUIRE(M >= 0 && K >= 0, PACT_EINVAL, "negative size");
+  REQUIRE(K % 16 == 0, PACT_ESHAPE, "K=%lld is not a multiple of 16", (long long)K);
+  REQUIRE(r >= 1 && r <= kMaxRank, PACT_ESHAPE, "rank %lld outside [1, %lld]", (long long)r, (long long)kMaxRank);
+  if (M == 0) return ok();
+  int st = check_nvfp4(x_codes, x_scales, x_rscale, "x");
+  if (st != PACT_OK) return st;
+  REQUIRE_PTR(A, "A");
+  REQUIRE_PTR(T, "T");
+  REQUIRE((M + 15) / 16 < 0x7FFFFFFF, PACT_EUNSUPPORTED, "M too large");
+  return hip_status(pact::launch_lora_down(x_codes, x_scales, x_rscale, M, K, A, r, T, as_stream(stream)),
+                    "lora_down launch");
+}
+
+int lora_bwd(const uint8_t* x_codes, const uint8_t* x_scales, const float* x_rscale, int64_t M, int64_t K,
+             const uint16_t* A, const uint16_t* B, int64_t r, float scale, const uint16_t* dy, int64_t N,
+             uint16_t* dT, uint16_t* dA, uint16_t* dB, void* stream) {
+  REQUIRE(M >= 0 && K >= 0 && N >= 0, PACT_EINVAL, "negative size");
+  REQUIRE(K % 16 == 0 && N % 16 == 0, PACT_ESHAPE, "K=%lld and N=%lld must be multiples of 16", (long long)K,
+          (long long)N);
+  REQUIRE(r >= 1 && r <= kMaxRank, PACT_ESHAPE, "rank %lld outside [1, %lld]", (long long)r, (long long)kMaxRank);
+  int st = check_nvfp4(x_codes, x_scales, x_rscale, "x");
+  if (st != PACT_OK && M > 0) return st;
+  REQUIRE_PTR(A, "A");
+  REQUIRE_PTR(B, "B");
+  REQUIRE_PTR(dT, "dT");
+  REQUIRE_PTR(dA, "dA");
+  REQUIRE_PTR(dB, "dB");
+  if (M > 0) REQUIRE_PTR(dy, "dy");
+  return hip_status(pact::launch_lora_bwd(x_codes, x_scales, x_rscale, M, K, A, B, r, scale, dy, N, dT, dA, dB,
+                                          as_stream(stream)),
+                    "lora_bwd launch");
+}
+
+int silu_mul_bwd(const uint8_t* g_codes, const uint8_t* g_scales, const float* g_rscale, const uint8_t* u_codes,
+                 const uint8_t* u_scales, const float* u_rscale, const uint16_t* dh, int64_t M, int64_t I,
+                 uint16_t* dgate, uint16_t* dup, void* stream) {
+  REQUIRE(M >= 0 && I >= 0, PACT_EINVAL, "negative size");
+  REQUIRE(I % 16 == 0, PACT_ESHAPE, "I=%lld is not a multiple of 16", (long long)I);
+  if (M == 0 || I == 0) return ok();
+  int st = check_nvfp4(g_codes, g_scales, g_rscale, "gate_q");
+  if (st == PACT_OK) st = check_nvfp4(u_codes, u_scales, u_rscale, "up_q");
+  if (st != PACT_OK) return st;
+  REQUIRE_PTR(dh, "dh");
+  REQUIRE_PTR(dgate, "dgate");
+  REQUIRE_PTR(dup, "dup");
+  return hip_status(pact::launch_silu_mul_bwd(g_codes, g_scales, g_rscale, u_codes, u_scales, u_rscale, dh, M, I,
+                                              dgate, dup, as_stream(stream)),
+                    "silu_mul_bwd launch");
+}
+
+int rmsnorm_bwd(const uint8_t* y_codes, const uint8_t* y_scales, const float* y_rscale, const float* rstd,
+                const uint16_t* gain, const uint16_t* dy, int64_t M, int64_t H, uint16_t* dx, void* stream) {
+  REQUIRE(M >= 0 && H >= 0, PACT_EINVAL, "negative size");
+  REQUIRE(H % 16 == 0, PACT_ESHAPE, "H=%lld is not a multiple of 16", (long long)H);
+  REQUIRE(H <= kMaxFusedCols, PACT_EUNSUPPORTED, "H=%lld exceeds %lld", (long long)H, (long long)kMaxFusedCols);
+  if (M == 0 || H == 0) return ok();
+  int st = check_nvfp4(y_codes, y_scales, y_rscale, "y");
+  if (st != PACT_OK) return st;
+  REQUIRE_PTR(rstd, "rstd");
+  REQUIRE_PTR(gain, "gain");
+  REQUIRE_PTR(dy, "dy");
+  REQUIRE_PTR(dx, "dx");
+  REQUIRE(M <= 0x7FFFFFFF, PACT_EUNSUPPORTED, "M too large");
+  return hip_status(pact::launch_rmsnorm_bwd(y_codes, y_scales, y_rscale, rstd, gain, dy, M, H, dx,
+                                             as_stream(stream)),
+                    "rmsnorm_bwd launch");
+}
+
+}  // extern "C"

@@ -1,0 +1,148 @@
+// Device-side NVFP4 arithmetic shared by the quantizer, fused and GEMM kernels.
+//
+// Format: 16-element blocks, E2M1 elements, E4M3 block scales (PACT, Appendix
+// Table 6), plus one power-of-two FP32 scale per row.  Every rounding decision
+// here reproduces the format's exact-real definition bit for bit:
+//   * row exponent e: smallest integer with rowmax <= 6*448*2^e, clamped to
+//     [-126, 127], 0 for an all-zero row;
+//   * block scale s = RNE_E4M3(blockmax / (6 r)): blockmax/r is exact (r is a
+//     power of two), its correctly rounded division by 6 can never sit on the
+//     wrong side of an E4M3 midpoint (a midpoint times 6 r has at most 7
+//     significant bits, so an FP32 blockmax is either on it or an ulp away), and
+//     the E4M3 rounding below is integer arithmetic on the FP32 bit pattern;
+//   * element code = RNE(|x| / (s r)) onto E2M1, ties to even, saturating at 6:
+//     the quotient is computed correctly rounded (reciprocal correctly rounded
+//     once per block, then one Markstein correction), and a correctly rounded
+//     quotient equals an E2M1 midpoint exactly when the real quotient does;
+//     v_cvt_scalef32_pk_fp4_f32 with scale 1.0 then performs exactly the RNE,
+//     saturation and sign handling of the format (its scale operand contributes
+//     only its exponent, so the block scale is divided out beforehand).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace pact {
+
+constexpr int kBlock = 16;
+
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
+
+// float -> bf16 bits, round to nearest even (finite inputs).
+__device__ __forceinline__ uint32_t f32_to_bf16_rne(float f) {
+  uint32_t u = __float_as_uint(f);
+  u += 0x7FFFu + ((u >> 16) & 1u);
+  return u >> 16;
+}
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  return f32_to_bf16_rne(lo) | (f32_to_bf16_rne(hi) << 16);
+}
+
+// Smallest e with amax <= 2688 * 2^e (2688 = 1.3125 * 2^11), clamped; 0 for amax == 0.
+__device__ __forceinline__ int row_exponent(float amax) {
+  const uint32_t u = __float_as_uint(amax);
+  if (u == 0u) return 0;
+  const int ef = (int)((u >> 23) & 0xFFu);
+  if (ef == 0) return -126;                       // subnormal rowmax: e would be < -126
+  const int e = ef - 127 - 11 + ((u & 0x7FFFFFu) > 0x280000u ? 1 : 0);
+  return e < -126 ? -126 : (e > 127 ? 127 : e);
+}
+__device__ __forceinline__ float pow2f(int e) {   // e in [-126, 127]
+  return __uint_as_float((uint32_t)(e + 127) << 23);
+}
+
+// RNE of t >= 0 onto the E4M3FN grid, saturating at 448 (code 0x7E).
+__device__ __forceinline__ uint32_t e4m3_encode(float t) {
+  if (t >= 448.0f) return 0x7Eu;
+  if (t < 0.015625f) return (uint32_t)rintf(t * 512.0f);   // subnormal grid m * 2^-9 (m = 8 is 2^-6)
+  uint32_t u = __float_as_uint(t);
+  u += 0x7FFFFu + ((u >> 20) & 1u);                         // keep 3 mantissa bits, ties to even
+  const uint32_t c = (u >> 20) - (120u << 3);                // exponent bias 127 -> 7
+  return c > 0x7Eu ? 0x7Eu : c;
+}
+__device__ __forceinline__ float e4m3_decode(uint32_t c) {
+  return c >= 8u ? __uint_as_float((c + (120u << 3)) << 20) : (float)c * 0.001953125f;
+}
+
+// Per-block constants for quantizing one block.  The quotient |x| / (s r) is
+// formed as (|x| 2^-e) / s: the power-of-two scaling is exact, and s is a
+// normal FP32 number, so the division stays out of the FP32 subnormal range
+// (where the remainder of the correction step would not be exact).
+struct BlockQ {
+  float s;      // block scale (0 if it rounds to 0)
+  float rcp;    // correctly rounded 1/s
+  float inv_r;  // 2^-e
+  uint32_t sc;  // E4M3 code of s
+};
+
+__device__ __forceinline__ BlockQ block_setup(float bmax, float r, float inv_r) {
+  (void)r;
+  BlockQ q;
+  const float t = __fdiv_rn(bmax * inv_r, 6.0f);
+  q.sc = e4m3_encode(t);
+  q.s = e4m3_decode(q.sc);
+  q.rcp = q.s != 0.0f ? __fdiv_rn(1.0f, q.s) : 0.0f;
+  q.inv_r = inv_r;
+  return q;
+}
+
+// Correctly rounded |x| / (s r) with the sign of x (0 with x's sign if s == 0).
+__device__ __forceinline__ float block_quot(float x, const BlockQ& q) {
+  const float ax = fabsf(x) * q.inv_r;
+  const float q0 = __fmul_rn(ax, q.rcp);
+  const float rem = __builtin_fmaf(-q0, q.s, ax);
+  float v = __builtin_fmaf(rem, q.rcp, q0);
+  v = q.s != 0.0f ? v : 0.0f;
+  return __builtin_copysignf(v, x);
+}
+
+// 8 consecutive elements -> 8 packed E2M1 codes (element 0 in the low nibble).
+__device__ __forceinline__ uint32_t encode8(const float* x, const BlockQ& q) {
+  uint32_t w = 0u;
+  w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, block_quot(x[0], q), block_quot(x[1], q), 1.0f, 0);
+  w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, block_quot(x[2], q), block_quot(x[3], q), 1.0f, 1);
+  w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, block_quot(x[4], q), block_quot(x[5], q), 1.0f, 2);
+  w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, block_quot(x[6], q), block_quot(x[7], q), 1.0f, 3);
+  return w;
+}
+
+__device__ __forceinline__ float absmax8(const float* x) {
+  float m = fabsf(x[0]);
+#pragma unroll
+  for (int i = 1; i < 8; ++i) m = fmaxf(m, fabsf(x[i]));
+  return m;
+}
+
+__device__ __forceinline__ void unpack_bf16x8(const uint4& v, float* x) {
+  x[0] = bf16_lo(v.x); x[1] = bf16_hi(v.x);
+  x[2] = bf16_lo(v.y); x[3] = bf16_hi(v.y);
+  x[4] = bf16_lo(v.z); x[5] = bf16_hi(v.z);
+  x[6] = bf16_lo(v.w); x[7] = bf16_hi(v.w);
+}
+
+// Wave and workgroup reductions (wave64).
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
+  return v;
+}
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o, 64);
+  return v;
+}
+
+// Dequantize 8 packed E2M1 codes (one 32-bit word) times a block multiplier m
+// (= s * r, exactly representable in FP32) into 8 floats.
+__device__ __forceinline__ void decode8_f32(uint32_t w, float m, float* out) {
+  typedef float float2_t __attribute__((ext_vector_type(2)));
+  float2_t a = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 0);
+  float2_t b = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 1);
+  float2_t c = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 2);
+  float2_t d = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 3);
+  out[0] = a.x * m; out[1] = a.y * m; out[2] = b.x * m; out[3] = b.y * m;
+  out[4] = c.x * m; out[5] = c.y * m; out[6] = d.x * m; out[7] = d.y * m;
+}
+
+}  // namespace pact

@@ -1,0 +1,61 @@
+// Internal launch interface between the C ABI layer (abi.hip) and the kernels.
+// Every launcher assumes its arguments were validated by the ABI layer.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "nvfp4_device.h"
+
+namespace pact {
+
+hipError_t launch_quantize(const uint16_t* x, int64_t rows, int64_t cols, int64_t ldx, int transpose,
+                           uint8_t* codes, uint8_t* scales, float* rscale, hipStream_t s);
+
+hipError_t launch_rmsnorm_quant(const uint16_t* x, const uint16_t* gain, float eps, int64_t M, int64_t H,
+                                int64_t ldx, uint8_t* codes, uint8_t* scales, float* rscale, float* rstd,
+                                int force_exact, hipStream_t s);
+
+hipError_t launch_silu_mul_quant(const uint16_t* gate, const uint16_t* up, int64_t M, int64_t I, int64_t ld,
+                                 uint8_t* hc, uint8_t* hs, float* hr, uint8_t* gc, uint8_t* gs, float* gr,
+                                 uint8_t* uc, uint8_t* us, float* ur, hipStream_t s);
+
+// C[M x N] = A[M x K] B[N x K]^T for row-blocked NVFP4 A and B, BF16 output.
+struct GemmArgs {
+  const uint8_t* a_codes;
+  const uint8_t* a_scales;
+  const float* a_rscale;
+  const uint8_t* b_codes;
+  const uint8_t* b_scales;
+  const float* b_rscale;
+  int64_t M, N, K;
+  uint16_t* out;
+  int64_t ldo;
+  int accumulate;
+  // optional rank-r term: acc += lora_scale * sum_j T[m][j] * U(j, n)
+  const uint16_t* lora_t;   // [M x r], leading dim lora_r
+  const uint16_t* lora_u;   // U(j, n) = lora_u[j * u_stride_j + n * u_stride_n]
+  int64_t u_stride_j, u_stride_n;
+  int64_t lora_r;
+  float lora_scale;
+};
+
+hipError_t launch_gemm(const GemmArgs& a, hipStream_t s);
+void gemm_tile(int64_t M, int64_t N, int* bm, int* bn);
+
+hipError_t launch_lora_down(const uint8_t* xc, const uint8_t* xs, const float* xr, int64_t M, int64_t K,
+                            const uint16_t* A, int64_t r, uint16_t* T, hipStream_t s);
+
+hipError_t launch_lora_bwd(const uint8_t* xc, const uint8_t* xs, const float* xr, int64_t M, int64_t K,
+                           const uint16_t* A, const uint16_t* B, int64_t r, float scale, const uint16_t* dy,
+                           int64_t N, uint16_t* dT, uint16_t* dA, uint16_t* dB, hipStream_t s);
+
+hipError_t launch_silu_mul_bwd(const uint8_t* gc, const uint8_t* gs, const float* gr, const uint8_t* uc,
+                               const uint8_t* us, const float* ur, const uint16_t* dh, int64_t M, int64_t I,
+                               uint16_t* dgate, uint16_t* dup, hipStream_t s);
+
+hipError_t launch_rmsnorm_bwd(const uint8_t* yc, const uint8_t* ys, const float* yr, const float* rstd,
+                              const uint16_t* gain, const uint16_t* dy, int64_t M, int64_t H, uint16_t* dx,
+                              hipStream_t s);
+
+}  // namespace pact

@@ -1,0 +1,431 @@
+// BF16 -> NVFP4 quantizers and the fused RMSNorm / SiLU-multiply forward kernels.
+//
+// PACT quantizes activations and output gradients to NVFP4 for its native
+// NVFP4 GEMMs and fuses RMSNorm and SiLU-multiply with that quantization,
+// keeping the NVFP4 outputs (plus an FP32 per-token RMSNorm statistic) as the
+// backward state (abstract; Appendix Table 7 rows "RMSNorm", "SiLU-multiply").
+//
+// Mapping on gfx950: one 256-thread workgroup per row.  Thread t owns the
+// 8-element chunks t, t+256, ... of its row, loaded with one 16-byte load each
+// and kept in registers (NCH chunks per thread), so each row is read from HBM
+// exactly once.  A 16-element block is the chunk pair held by lanes 2p and
+// 2p+1; its amax is one cross-lane exchange.  The row amax (needed before any
+// block scale) is a wave64 butterfly plus a 4-entry LDS exchange.  Codes leave
+// as one 32-bit store per chunk (coalesced across the wave), scales as bytes.
+#include "pact_internal.h"
+
+namespace pact {
+
+constexpr int kThreads = 256;
+
+__device__ __forceinline__ float block_max_256(float v, float* red) {
+  v = wave_max(v);
+  const int w = threadIdx.x >> 6;
+  if ((threadIdx.x & 63) == 0) red[w] = v;
+  __syncthreads();
+  const float r = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+  __syncthreads();
+  return r;
+}
+
+__device__ __forceinline__ uint4 load16(const uint16_t* p) { return *reinterpret_cast<const uint4*>(p); }
+
+// Quantize one chunk (8 floats) of a row whose exponent is known.  Both lanes
+// of the pair must call this (it exchanges the chunk amax with lane ^ 1).
+__device__ __forceinline__ void quant_chunk(const float* x, bool valid, float r, float inv_r,
+                                            uint8_t* codes_row, uint8_t* scales_row, int c) {
+  float m = valid ? absmax8(x) : 0.0f;
+  m = fmaxf(m, __shfl_xor(m, 1, 64));
+  if (!valid) return;
+  const BlockQ q = block_setup(m, r, inv_r);
+  const uint32_t w = encode8(x, q);
+  *reinterpret_cast<uint32_t*>(codes_row + 4 * (int64_t)c) = w;
+  if ((c & 1) == 0) scales_row[c >> 1] = (uint8_t)q.sc;
+}
+
+// --------------------------------------------------------------------------
+// nvfp4_quantize, row-wise
+// --------------------------------------------------------------------------
+template <int NCH>
+__global__ __launch_bounds__(kThreads) void k_quantize_rows(const uint16_t* __restrict__ x, int64_t cols,
+                                                            int64_t ldx, uint8_t* __restrict__ codes,
+                                                            uint8_t* __restrict__ scales,
+                                                            float* __restrict__ rscale) {
+  __shared__ float red[4];
+  const int64_t row = blockIdx.x;
+  const int nchunk = (int)(cols >> 3);
+  const uint16_t* xr = x + row * ldx;
+  uint4 v[NCH];
+  float lmax = 0.0f;
+#pragma unroll
+  for (int i = 0; i < NCH; ++i) {
+    const int c = threadIdx.x + kThreads * i;
+    v[i] = c < nchunk ? load16(xr + 8 * c) : make_uint4(0, 0, 0, 0);
+    float f[8];
+    unpack_bf16x8(v[i], f);
+    lmax = fmaxf(lmax, absmax8(f));
+  }
+  const float amax = block_max_256(lmax, red);
+  const int e = row_exponent(amax);
+  const float r = pow2f(e), inv_r = pow2f(-e);
+  uint8_t* crow = codes + row * (cols >> 1);
+  uint8_t* srow = scales + row * (cols >> 4);
+#pragma unroll
+  for (int i = 0; i < NCH; ++i) {
+    const int c = threadIdx.x + kThreads * i;
+    float f[8];
+    unpack_bf16x8(v[i], f);
+    quant_chunk(f, c < nchunk, r, inv_r, crow, srow, c);
+  }
+  if (threadIdx.x == 0) rscale[row] = r;
+}
+
+// Rows longer than 256 * 8 * 8 elements: two passes over the row (the second
+// read is served from L2).
+__global__ __launch_bounds__(kThreads) void k_quantize_rows_long(const uint16_t* __restrict__ x, int64_t cols,
+                                                                 int64_t ldx, uint8_t* __restrict__ codes,
+                                                                 uint8_t* __restrict__ scales,
+                                                                 float* __restrict__ rscale) {
+  __shared__ float red[4];
+  const int64_t row = blockIdx.x;
+  const int nchunk = (int)(cols >> 3);
+  const uint16_t* xr = x + row * ldx;
+  float lmax = 0.0f;
+  for (int c = threadIdx.x; c < nchunk; c += kThreads) {
+    float f[8];
+    unpack_bf16x8(load16(xr + 8 * c), f);
+    lmax = fmaxf(lmax, absmax8(f));
+  }
+  const float amax = block_max_256(lmax, red);
+  const int e = row_exponent(amax);
+  const float r = pow2f(e), inv_r = pow2f(-e);
+  uint8_t* crow = codes + row * (cols >> 1);
+  uint8_t* srow = scales + row * (cols >> 4);
+  const int nround = (nchunk + kThreads - 1) / kThreads;
+  for (int i = 0; i < nround; ++i) {
+    const int c = threadIdx.x + kThreads * i;
+    float f[8];
+    uint4 v = c < nchunk ? load16(xr + 8 * c) : make_uint4(0, 0, 0, 0);
+    unpack_bf16x8(v, f);
+    quant_chunk(f, c < nchunk, r, inv_r, crow, srow, c);
+  }
+  if (threadIdx.x == 0) rscale[row] = r;
+}
+
+// --------------------------------------------------------------------------
+// nvfp4_quantize with transpose: output row i is column i of x [cols x rows].
+// Used offline for the cached backward weight layout W_bwd = Q(W^T).  A
+// workgroup owns 64 consecutive output rows; lane i of each wave reads
+// x[j][i0 + i] so that a wave's loads are 128 contiguous bytes per j.
+// --------------------------------------------------------------------------
+__global__ __launch_bounds__(kThreads) void k_quantize_cols(const uint16_t* __restrict__ x, int64_t rows,
+                                                            int64_t cols, int64_t ldx,
+                                                            uint8_t* __restrict__ codes,
+                                                            uint8_t* __restrict__ scales,
+                                                            float* __restrict__ rscale) {
+  __shared__ float red[4][64];
+  const int li = threadIdx.x & 63, g = threadIdx.x >> 6;
+  const int64_t i = (int64_t)blockIdx.x * 64 + li;
+  const bool ok = i < rows;
+  const int64_t ic = ok ? i : rows - 1;
+  const int64_t nblk = cols >> 4;
+  float lmax = 0.0f;
+  for (int64_t j = g; j < cols; j += 4) lmax = fmaxf(lmax, fabsf(bf16_lo(x[j * ldx + ic])));
+  red[g][li] = lmax;
+  __syncthreads();
+  const float amax = fmaxf(fmaxf(red[0][li], red[1][li]), fmaxf(red[2][li], red[3][li]));
+  const int e = row_exponent(amax);
+  const float r = pow2f(e), inv_r = pow2f(-e);
+  for (int64_t b = g; b < nblk; b += 4) {
+    float f[16];
+    float m = 0.0f;
+#pragma unroll
+    for (int t = 0; t < 16; ++t) {
+      f[t] = bf16_lo(x[(16 * b + t) * ldx + ic]);
+      m = fmaxf(m, fabsf(f[t]));
+    }
+    const BlockQ q = block_setup(m, r, inv_r);
+    const uint32_t w0 = encode8(f, q), w1 = encode8(f + 8, q);
+    if (ok) {
+      uint32_t* dst = reinterpret_cast<uint32_t*>(codes + i * (cols >> 1) + 8 * b);
+      dst[0] = w0;
+      dst[1] = w1;
+      scales[i * nblk + b] = (uint8_t)q.sc;
+    }
+  }
+  if (ok && g == 0) rscale[i] = r;
+}
+
+// --------------------------------------------------------------------------
+// rmsnorm_quant
+// --------------------------------------------------------------------------
+// Error-free sum of two doubles.
+__device__ __forceinline__ void two_sum(double a, double b, double& s, double& e) {
+  s = a + b;
+  const double bb = s - a;
+  e = (a - (s - bb)) + (b - bb);
+}
+
+template <int NCH>
+__global__ __launch_bounds__(kThreads) void k_rmsnorm_quant(const uint16_t* __restrict__ x,
+                                                            const uint16_t* __restrict__ gain, float eps,
+                                                            int64_t H, int64_t ldx, uint8_t* __restrict__ codes,
+                                                            uint8_t* __restrict__ scales,
+                                                            float* __restrict__ rscale,
+                                                            float* __restrict__ rstd_out, int force_exact) {
+  __shared__ double dred[2][4];
+  __shared__ float red[4];
+  const int64_t row = blockIdx.x;
+  const int nchunk = (int)(H >> 3);
+  const uint16_t* xr = x + row * ldx;
+  uint4 v[NCH];
+  double ss = 0.0;
+#pragma unroll
+  for (int i = 0; i < NCH; ++i) {
+    const int c = threadIdx.x + kThreads * i;
+    v[i] = c < nchunk ? load16(xr + 8 * c) : make_uint4(0, 0, 0, 0);
+    float f[8];
+    unpack_bf16x8(v[i], f);
+#pragma unroll
+    for (int t = 0; t < 8; ++t) ss += (double)f[t] * (double)f[t];   // exact square
+  }
+  // workgroup sum (plain float64)
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) ss += __shfl_xor(ss, o, 64);
+  const int w = threadIdx.x >> 6;
+  if ((threadIdx.x & 63) == 0) dred[0][w] = ss;
+  __syncthreads();
+  double S = (dred[0][0] + dred[0][1]) + (dred[0][2] + dred[0][3]);
+  // The FP32 result depends on S only through fp32(S/H).  The float64 sum above
+  // is within (H + 64) * 2^-53 * S of the exactly rounded sum; unless fp32(S/H)
+  // is that close to an FP32 rounding boundary, it is the exactly rounded
+  // value.  Otherwise (rarely), recompute S as an error-free double-double sum.
+  {
+    const double q = S / (double)H;
+    const float f = (float)q;
+    // neighbours of f (f >= 0 and finite): adjacent bit patterns
+    const uint32_t fb = __float_as_uint(f);
+    const double lo = fb > 0u ? (double)__uint_as_float(fb - 1u) : 0.0;
+    const double hi = (double)__uint_as_float(fb + 1u);
+    const double dist = fmin(q - 0.5 * (lo + (double)f), 0.5 * ((double)f + hi) - q);
+    const double margin = ((double)H + 64.0) * 2.220446049250313e-16 * q;   // (H+64) * 2^-52 * q
+    const bool exact = force_exact != 0 || (q > 0.0 && !(dist > margin));
+    __syncthreads();
+    if (exact) {   // uniform across the workgroup
+      double sh = 0.0, sl = 0.0;
+#pragma unroll
+      for (int i = 0; i < NCH; ++i) {
+        float f8[8];
+        unpack_bf16x8(v[i], f8);
+#pragma unroll
+        for (int t = 0; t < 8; ++t) {
+          double s, e;
+          two_sum(sh, (double)f8[t] * (double)f8[t], s, e);
+          sh = s;
+          sl += e;
+        }
+      }
+#pragma unroll
+      for (int o = 32; o >= 1; o >>= 1) {
+        const double oh = __shfl_xor(sh, o, 64), ol = __shfl_xor(sl, o, 64);
+        double s, e;
+        two_sum(sh, oh, s, e);
+        sh = s;
+        sl = sl + ol + e;
+      }
+      if ((threadIdx.x & 63) == 0) { dred[0][w] = sh; dred[1][w] = sl; }
+      __syncthreads();
+      sh = dred[0][0];
+      sl = dred[1][0];
+      for (int k = 1; k < 4; ++k) {
+        double s, e;
+        two_sum(sh, dred[0][k], s, e);
+        sh = s;
+        sl = sl + dred[1][k] + e;
+      }
+      S = sh + sl;   // the double-double value rounded once to float64
+    }
+  }
+  const float ms = (float)(S / (double)H);
+  const float var = __fadd_rn(ms, eps);
+  const float sd = (float)__builtin_sqrt((double)var);        // RN64 then RN32 of sqrt: equals sqrt_rn in FP32
+  const float rstd = __fdiv_rn(1.0f, sd);
+  // y = (x * rstd) * g, kept in registers for the quantization pass
+  float y[NCH][8];
+  float lmax = 0.0f;
+#pragma unroll
+  for (int i = 0; i < NCH; ++i) {
+    const int c = threadIdx.x + kThreads * i;
+    float f[8], g[8];
+    unpack_bf16x8(v[i], f);
+    unpack_bf16x8(c < nchunk ? load16(gain + 8 * c) : make_uint4(0, 0, 0, 0), g);
+#pragma unroll
+    for (int t = 0; t < 8; ++t) y[i][t] = __fmul_rn(__fmul_rn(f[t], rstd), g[t]);
+    lmax = fmaxf(lmax, absmax8(y[i]));
+  }
+  const float amax = block_max_256(lmax, red);
+  const int e = row_exponent(amax);
+  const float r = pow2f(e), inv_r = pow2f(-e);
+  uint8_t* crow = codes + row * (H >> 1);
+  uint8_t* srow = scales + row * (H >> 4);
+#pragma unroll
+  for (int i = 0; i < NCH; ++i) {
+    const int c = threadIdx.x + kThreads * i;
+    quant_chunk(y[i], c < nchunk, r, inv_r, crow, srow, c);
+  }
+  if (threadIdx.x == 0) {
+    rscale[row] = r;
+    rstd_out[row] = rstd;
+  }
+}
+
+// --------------------------------------------------------------------------
+// silu_mul_quant
+// --------------------------------------------------------------------------
+// FP32 exponential: Cody-Waite reduction with ln 2 split in two (the high part
+// has 16 significant bits, so n * LN2_HI is exact for |n| <= 128), then the
+// degree-7 Taylor polynomial of e^r in Horner form, every step an IEEE
+// round-to-nearest operation with no contraction.
+//   L2E    = RN32(1 / ln 2)          = 0x3FB8AA3B
+//   LN2_HI = ln 2 to 16 significant bits = 0x3F317200
+//   LN2_LO = RN32(ln 2 - LN2_HI)     = 0x35BFBE8E
+//   C_k    = RN32(1 / k!)            k = 2..7: 0x3F000000 0x3E2AAAAB 0x3D2AAAAB 0x3C088889 0x3AB60B61 0x39500D01
+__device__ __forceinline__ float exp_pinned(float x) {
+  const float L2E = __uint_as_float(0x3FB8AA3Bu);
+  const float LN2_HI = __uint_as_float(0x3F317200u);
+  const float LN2_LO = __uint_as_float(0x35BFBE8Eu);
+  const float xc = fminf(fmaxf(x, -80.0f), 89.0f);
+  const float n = rintf(__fmul_rn(xc, L2E));
+  const float rr = __fsub_rn(__fsub_rn(xc, __fmul_rn(n, LN2_HI)), __fmul_rn(n, LN2_LO));
+  float p = __uint_as_float(0x39500D01u);                         // 1/7!
+  p = __fadd_rn(__fmul_rn(p, rr), __uint_as_float(0x3AB60B61u));  // 1/6!
+  p = __fadd_rn(__fmul_rn(p, rr), __uint_as_float(0x3C088889u));  // 1/5!
+  p = __fadd_rn(__fmul_rn(p, rr), __uint_as_float(0x3D2AAAABu));  // 1/4!
+  p = __fadd_rn(__fmul_rn(p, rr), __uint_as_float(0x3E2AAAABu));  // 1/3!
+  p = __fadd_rn(__fmul_rn(p, rr), 0.5f);
+  p = __fadd_rn(__fmul_rn(p, rr), 1.0f);
+  p = __fadd_rn(__fmul_rn(p, rr), 1.0f);
+  float e = __builtin_ldexpf(p, (int)n);
+  e = x < -80.0f ? 0.0f : e;
+  e = x > 89.0f ? __builtin_huge_valf() : e;
+  return e;
+}
+
+__device__ __forceinline__ float silu_mul(float a, float b) {
+  const float sig = __fdiv_rn(1.0f, __fadd_rn(1.0f, exp_pinned(-a)));
+  return __fmul_rn(__fmul_rn(a, sig), b);
+}
+
+template <int NCH>
+__global__ __launch_bounds__(kThreads) void k_silu_mul_quant(const uint16_t* __restrict__ gate,
+                                                             const uint16_t* __restrict__ up, int64_t I,
+                                                             int64_t ld, uint8_t* __restrict__ hc,
+                                                             uint8_t* __restrict__ hs, float* __restrict__ hr,
+                                                             uint8_t* __restrict__ gc, uint8_t* __restrict__ gs,
+                                                             float* __restrict__ gr, uint8_t* __restrict__ uc,
+                                                             uint8_t* __restrict__ us, float* __restrict__ ur) {
+  __shared__ float red[3][4];
+  const int64_t row = blockIdx.x;
+  const int nchunk = (int)(I >> 3);
+  uint4 va[NCH], vb[NCH];
+  float h[NCH][8];
+  float ma = 0.0f, mb = 0.0f, mh = 0.0f;
+#pragma unroll
+  for (int i = 0; i < NCH; ++i) {
+    const int c = threadIdx.x + kThreads * i;
+    const bool ok = c < nchunk;
+    va[i] = ok ? load16(gate + row * ld + 8 * c) : make_uint4(0, 0, 0, 0);
+    vb[i] = ok ? load16(up + row * ld + 8 * c) : make_uint4(0, 0, 0, 0);
+    float a[8], b[8];
+    unpack_bf16x8(va[i], a);
+    unpack_bf16x8(vb[i], b);
+#pragma unroll
+    for (int t = 0; t < 8; ++t) h[i][t] = silu_mul(a[t], b[t]);
+    ma = fmaxf(ma, absmax8(a));
+    mb = fmaxf(mb, absmax8(b));
+    mh = fmaxf(mh, absmax8(h[i]));
+  }
+  ma = wave_max(ma);
+  mb = wave_max(mb);
+  mh = wave_max(mh);
+  const int w = threadIdx.x >> 6;
+  if ((threadIdx.x & 63) == 0) { red[0][w] = mh; red[1][w] = ma; red[2][w] = mb; }
+  __syncthreads();
+  float amx[3];
+#pragma unroll
+  for (int k = 0; k < 3; ++k) amx[k] = fmaxf(fmaxf(red[k][0], red[k][1]), fmaxf(red[k][2], red[k][3]));
+  float r[3], ir[3];
+#pragma unroll
+  for (int k = 0; k < 3; ++k) {
+    const int e = row_exponent(amx[k]);
+    r[k] = pow2f(e);
+    ir[k] = pow2f(-e);
+  }
+  const int64_t co = row * (I >> 1), so = row * (I >> 4);
+#pragma unroll
+  for (int i = 0; i < NCH; ++i) {
+    const int c = threadIdx.x + kThreads * i;
+    const bool ok = c < nchunk;
+    float a[8], b[8];
+    unpack_bf16x8(va[i], a);
+    unpack_bf16x8(vb[i], b);
+    quant_chunk(h[i], ok, r[0], ir[0], hc + co, hs + so, c);
+    quant_chunk(a, ok, r[1], ir[1], gc + co, gs + so, c);
+    quant_chunk(b, ok, r[2], ir[2], uc + co, us + so, c);
+  }
+  if (threadIdx.x == 0) { hr[row] = r[0]; gr[row] = r[1]; ur[row] = r[2]; }
+}
+
+// --------------------------------------------------------------------------
+// launchers
+// --------------------------------------------------------------------------
+static int chunks_per_thread(int64_t cols) { return (int)(((cols >> 3) + kThreads - 1) / kThreads); }
+
+hipError_t launch_quantize(const uint16_t* x, int64_t rows, int64_t cols, int64_t ldx, int transpose,
+                           uint8_t* codes, uint8_t* scales, float* rscale, hipStream_t s) {
+  if (transpose) {
+    const unsigned grid = (unsigned)((rows + 63) / 64);
+    k_quantize_cols<<<grid, kThreads, 0, s>>>(x, rows, cols, ldx, codes, scales, rscale);
+    return hipGetLastError();
+  }
+  const int nch = chunks_per_thread(cols);
+  const dim3 grid((unsigned)rows);
+  if (nch <= 1) k_quantize_rows<1><<<grid, kThreads, 0, s>>>(x, cols, ldx, codes, scales, rscale);
+  else if (nch <= 2) k_quantize_rows<2><<<grid, kThreads, 0, s>>>(x, cols, ldx, codes, scales, rscale);
+  else if (nch <= 4) k_quantize_rows<4><<<grid, kThreads, 0, s>>>(x, cols, ldx, codes, scales, rscale);
+  else if (nch <= 8) k_quantize_rows<8><<<grid, kThreads, 0, s>>>(x, cols, ldx, codes, scales, rscale);
+  else k_quantize_rows_long<<<grid, kThreads, 0, s>>>(x, cols, ldx, codes, scales, rscale);
+  return hipGetLastError();
+}
+
+hipError_t launch_rmsnorm_quant(const uint16_t* x, const uint16_t* gain, float eps, int64_t M, int64_t H,
+                                int64_t ldx, uint8_t* codes, uint8_t* scales, float* rscale, float* rstd,
+                                int force_exact, hipStream_t s) {
+  const int nch = chunks_per_thread(H);
+  const dim3 grid((unsigned)M);
+#define PACT_RMS(N) k_rmsnorm_quant<N><<<grid, kThreads, 0, s>>>(x, gain, eps, H, ldx, codes, scales, rscale, rstd, force_exact)
+  if (nch <= 1) PACT_RMS(1);
+  else if (nch <= 2) PACT_RMS(2);
+  else if (nch <= 4) PACT_RMS(4);
+  else if (nch <= 8) PACT_RMS(8);
+  else return hipErrorInvalidValue;
+#undef PACT_RMS
+  return hipGetLastError();
+}
+
+hipError_t launch_silu_mul_quant(const uint16_t* gate, const uint16_t* up, int64_t M, int64_t I, int64_t ld,
+                                 uint8_t* hc, uint8_t* hs, float* hr, uint8_t* gc, uint8_t* gs, float* gr,
+                                 uint8_t* uc, uint8_t* us, float* ur, hipStream_t s) {
+  const int nch = chunks_per_thread(I);
+  const dim3 grid((unsigned)M);
+#define PACT_SILU(N) k_silu_mul_quant<N><<<grid, kThreads, 0, s>>>(gate, up, I, ld, hc, hs, hr, gc, gs, gr, uc, us, ur)
+  if (nch <= 1) PACT_SILU(1);
+  else if (nch <= 2) PACT_SILU(2);
+  else if (nch <= 4) PACT_SILU(4);
+  else if (nch <= 8) PACT_SILU(8);
+  else return hipErrorInvalidValue;
+#undef PACT_SILU
+  return hipGetLastError();
+}
+
+}  // namespace pact

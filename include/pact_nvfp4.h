@@ -1,0 +1,205 @@
+/*
+ * pact_nvfp4.h -- C ABI of the NVFP4 frozen-projection library for MI355X (gfx950).
+ *
+ * The operations are those of PACT's LoRA linear layer and decoder MLP as its
+ * precision-allocation table describes them ("PACT: NVFP4 Data-Flow LoRA
+ * Fine-Tuning on Consumer GPUs", Appendix Table 7): frozen projections as
+ * NVFP4 GEMMs with FP32 accumulation and BF16 output over cached forward and
+ * backward NVFP4 weight layouts; RMSNorm and SiLU-multiply fused with NVFP4
+ * quantization, with FP32 reconstruction in backward; a BF16 LoRA branch on the
+ * reconstructed input.
+ *
+ * NVFP4 tensor (Appendix Table 6: 16-element blocks, E2M1 elements, E4M3
+ * block scales, 4.50 bits/element).  A tensor of logical shape [rows x cols],
+ * cols % 16 == 0, is three buffers, all row-major:
+ *   codes  uint8 [rows][cols/2]   E2M1 codes, element 2j in the low nibble of byte j
+ *   scales uint8 [rows][cols/16]  E4M3FN block scales (bias 7, max 448)
+ *   rscale float [rows]           power-of-two FP32 row scale r = 2^e
+ * Element (i, j) is  E2M1(code) * E4M3(scale[i][j/16]) * rscale[i].
+ * Quantization rules: e is the smallest integer with rowmax <= 6*448*2^e,
+ * clamped to [-126, 127] (0 for an all-zero row); block scale
+ * s = RNE_E4M3(blockmax / (6 r)) saturating at 448; element code =
+ * RNE(|x| / (s r)) onto {0,.5,1,1.5,2,3,4,6}, ties to the even code,
+ * saturating at 6, sign bit of x kept, magnitude 0 when s == 0.
+ *
+ * Conventions for every entry point:
+ *   - All tensor pointers are DEVICE pointers owned by the caller.  The library
+ *     allocates, frees and synchronizes nothing; it launches asynchronously on
+ *     `stream` (a hipStream_t; NULL is the default stream).
+ *   - BF16 tensors are uint16_t bit patterns.
+ *   - Arguments are validated on the host before any HIP call; a negative
+ *     status is returned and pact_last_error() describes it.  Launch failures
+ *     return PACT_EHIP.  Faults inside kernels surface at the caller's next
+ *     synchronization.  No C++ exception crosses this interface.
+ *   - rows == 0 (or M == 0) is a valid no-op.  Column counts that carry NVFP4
+ *     blocks must be multiples of 16.  Every pointer that is dereferenced must
+ *     be non-NULL and 16-byte aligned; leading dimensions are in elements.
+ *   - NaN and Inf inputs are outside the contract.
+ */
+#ifndef PACT_NVFP4_H
+#define PACT_NVFP4_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum {
+  PACT_OK = 0,
+  PACT_EINVAL = -1,      /* NULL pointer, negative size, bad flag */
+  PACT_ESHAPE = -2,      /* cols % 16 != 0, ld < cols, rank out of range */
+  PACT_EALIGN = -3,      /* pointer not 16-byte aligned */
+  PACT_EHIP = -4,        /* a HIP launch failed */
+  PACT_EUNSUPPORTED = -5 /* valid but unsupported by this build */
+};
+
+/* Message for the last non-OK status returned on this thread ("" if none). */
+const char *pact_last_error(void);
+
+/* Interface version (incremented on any change of signature or semantics). */
+int pact_abi_version(void);
+
+/* Host-only size query: bytes of the three buffers of an NVFP4 [rows x cols]. */
+int pact_nvfp4_sizes(int64_t rows, int64_t cols, size_t *codes_bytes, size_t *scales_bytes,
+                     size_t *rscale_bytes);
+
+/*
+ * nvfp4_quantize -- BF16 -> NVFP4 (Appendix Table 6 format; the abstract's
+ * quantization step, Table 11 "Quantization / fused kernels").
+ *   transpose == 0: x is [rows x cols] with leading dimension ldx >= cols; the
+ *                   result is Q(x), blocks along cols.
+ *   transpose == 1: x is [cols x rows] with leading dimension ldx >= rows; the
+ *                   result is Q(x^T) of shape [rows x cols] (row i of the result
+ *                   is column i of x).  This builds the cached backward weight
+ *                   layout W_bwd = Q(W^T) from W [N x K] (rows = K, cols = N).
+ *   Outputs: codes [rows][cols/2], scales [rows][cols/16], rscale [rows].
+ */
+int nvfp4_quantize(const uint16_t *x, int64_t rows, int64_t cols, int64_t ldx, int transpose,
+                   uint8_t *codes, uint8_t *scales, float *rscale, void *stream);
+
+/*
+ * rmsnorm_quant -- RMSNorm forward fused with NVFP4 quantization (Appendix
+ * Table 7 row "RMSNorm": BF16 input, FP32 normalization; NVFP4 output and FP32
+ * per-token statistic kept).  For each row of x [M x H] (leading dim ldx):
+ *   S = sum x^2 (float64), ms = fp32(S/H), v = ms + eps, rstd = 1/sqrt(v),
+ *   y = (x * rstd) * gain  (FP32, round-to-nearest, no contraction),
+ * writes Q(y) (the projection input) and rstd [M].  gain is BF16 [H].
+ * H % 16 == 0.
+ */
+int rmsnorm_quant(const uint16_t *x, const uint16_t *gain, float eps, int64_t M, int64_t H,
+                  int64_t ldx, uint8_t *y_codes, uint8_t *y_scales, float *y_rscale, float *rstd,
+                  void *stream);
+
+/*
+ * silu_mul_quant -- SiLU-multiply forward fused with NVFP4 quantization
+ * (Appendix Table 7 row "SiLU-multiply": BF16 gate/up inputs, FP32 arithmetic,
+ * separate NVFP4 gate/up copies kept).  Elementwise on gate a, up b [M x I]
+ * (shared leading dim ld):
+ *   sigma = 1/(1 + E(-a)), h = (a * sigma) * b   (FP32; E is the library's
+ *   Cody-Waite + degree-7 Taylor exponential),
+ * writes Q(h) (the down-projection input), Q(a) and Q(b).  I % 16 == 0.
+ */
+int silu_mul_quant(const uint16_t *gate, const uint16_t *up, int64_t M, int64_t I, int64_t ld,
+                   uint8_t *h_codes, uint8_t *h_scales, float *h_rscale,
+                   uint8_t *g_codes, uint8_t *g_scales, float *g_rscale,
+                   uint8_t *u_codes, uint8_t *u_scales, float *u_rscale, void *stream);
+
+/*
+ * pact_gemm_tile -- host-only query: the workgroup tile (bm x bn output
+ * elements) that nvfp4_gemm_fwd / nvfp4_gemm_dgrad launch for an output of
+ * M x Nout with contraction length Kr.  Lets callers attribute kernel times.
+ */
+int pact_gemm_tile(int64_t M, int64_t Nout, int64_t Kr, int *bm, int *bn);
+
+/*
+ * nvfp4_gemm_fwd -- frozen-projection forward Y = X W^T (Appendix Table 7 row
+ * "Frozen projections": NVFP4 GEMM, FP32 accumulation, BF16 output).
+ *   X_q: NVFP4 [M x K]; W_fwd: NVFP4 [N x K] (= Q(W), the cached forward layout).
+ *   Y: BF16 [M x N], leading dim ldy >= N.
+ *   Optional LoRA term (Table 7 row "LoRA branch"): if lora_t != NULL,
+ *     Y = bf16( deq(X_q) deq(W_fwd)^T + lora_scale * T B^T )
+ *   with T BF16 [M x r] (row-major, from lora_down) and B BF16 [N x r]
+ *   (row-major), 1 <= r <= 128.  The sum is formed in FP32; one BF16 rounding.
+ * K % 16 == 0.
+ */
+int nvfp4_gemm_fwd(const uint8_t *x_codes, const uint8_t *x_scales, const float *x_rscale,
+                   int64_t M, int64_t K,
+                   const uint8_t *w_codes, const uint8_t *w_scales, const float *w_rscale, int64_t N,
+                   uint16_t *y, int64_t ldy,
+                   const uint16_t *lora_t, const uint16_t *lora_b, int64_t lora_r, float lora_scale,
+                   void *stream);
+
+/*
+ * nvfp4_gemm_dgrad -- frozen-projection input gradient dX = dY W (Appendix
+ * Table 7 row "Frozen projections": NVFP4 input-gradient GEMMs over the cached
+ * backward layout).
+ *   dY_q: NVFP4 [M x N]; W_bwd: NVFP4 [K x N] (= Q(W^T), blocks along N).
+ *   dX: BF16 [M x K], leading dim lddx >= K.
+ *   accumulate != 0: dX = bf16( f32(dX) + result )  (sums several consumers).
+ *   Optional LoRA input-gradient term: if lora_dt != NULL,
+ *     result += dT A  with dT BF16 [M x r] and A BF16 [r x K] (row-major),
+ *   formed in FP32 before the one BF16 rounding.  1 <= r <= 128.
+ * N % 16 == 0.
+ */
+int nvfp4_gemm_dgrad(const uint8_t *dy_codes, const uint8_t *dy_scales, const float *dy_rscale,
+                     int64_t M, int64_t N,
+                     const uint8_t *w_codes, const uint8_t *w_scales, const float *w_rscale, int64_t K,
+                     uint16_t *dx, int64_t lddx, int accumulate,
+                     const uint16_t *lora_dt, const uint16_t *lora_a, int64_t lora_r,
+                     void *stream);
+
+/*
+ * lora_down -- LoRA forward down-projection on the reconstructed input
+ * (Appendix Table 7 row "LoRA branch": BF16 GEMMs on reconstructed inputs).
+ *   T = bf16( deq(X_q) A^T ),  X_q NVFP4 [M x K], A BF16 [r x K] row-major,
+ *   T BF16 [M x r] row-major.  FP32 accumulation.  1 <= r <= 128, K % 16 == 0.
+ */
+int lora_down(const uint8_t *x_codes, const uint8_t *x_scales, const float *x_rscale,
+              int64_t M, int64_t K, const uint16_t *A, int64_t r, uint16_t *T, void *stream);
+
+/*
+ * lora_bwd -- LoRA adapter gradients (Appendix Table 7 row "LoRA branch": BF16
+ * adapter gradients and input gradients; saved state is the shared NVFP4 input
+ * and the BF16 adapters, so T is recomputed).  With X~ = deq(X_q) [M x K],
+ * A [r x K], B [N x r], the BF16 output gradient dY [M x N] (row-major) and
+ * scale s:
+ *   T  = bf16(X~ A^T)          (recomputed)
+ *   dT = bf16(s dY B)          [M x r]   (feeds nvfp4_gemm_dgrad's LoRA term)
+ *   dB = bf16(s dY^T T)        [N x r]
+ *   dA = bf16(dT^T X~)         [r x K]
+ * 1 <= r <= 128; K % 16 == 0.
+ */
+int lora_bwd(const uint8_t *x_codes, const uint8_t *x_scales, const float *x_rscale,
+             int64_t M, int64_t K, const uint16_t *A, const uint16_t *B, int64_t r, float scale,
+             const uint16_t *dy, int64_t N, uint16_t *dT, uint16_t *dA, uint16_t *dB, void *stream);
+
+/*
+ * silu_mul_bwd -- SiLU-multiply backward from the NVFP4 state (Appendix Table 7
+ * row "SiLU-multiply": FP32 reconstruction and derivatives, BF16 gradients).
+ *   a^ = deq(gate_q), b^ = deq(up_q), sigma = 1/(1+exp(-a^)):
+ *   dgate = bf16(dh b^ sigma (1 + a^ (1 - sigma))),  dup = bf16(dh a^ sigma).
+ *   gate_q, up_q NVFP4 [M x I]; dh, dgate, dup BF16 [M x I] (dense rows).
+ */
+int silu_mul_bwd(const uint8_t *g_codes, const uint8_t *g_scales, const float *g_rscale,
+                 const uint8_t *u_codes, const uint8_t *u_scales, const float *u_rscale,
+                 const uint16_t *dh, int64_t M, int64_t I, uint16_t *dgate, uint16_t *dup,
+                 void *stream);
+
+/*
+ * rmsnorm_bwd -- RMSNorm backward from the NVFP4 state (Appendix Table 7 row
+ * "RMSNorm": FP32 reconstruction and reduction, BF16 gradient).
+ *   y^ = deq(y_q) [M x H], rstd f32 [M], gain BF16 [H], dy BF16 [M x H]:
+ *   dx_i = bf16( rstd * (g_i dy_i - (y^_i / g_i) * (1/H) sum_j dy_j y^_j) ).
+ *   dx BF16 [M x H] (dense rows).  The gain is frozen (no gain gradient).
+ */
+int rmsnorm_bwd(const uint8_t *y_codes, const uint8_t *y_scales, const float *y_rscale,
+                const float *rstd, const uint16_t *gain, const uint16_t *dy, int64_t M, int64_t H,
+                uint16_t *dx, void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PACT_NVFP4_H */

@@ -1,0 +1,129 @@
+"""CPU-side checks of the C-ABI library: it loads, exports every function the
+header declares, and rejects invalid arguments on the host before any HIP
+call (so these run without a GPU)."""
+
+import ctypes
+import os
+import subprocess
+
+import pytest
+
+ROOT_ = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+_so = os.path.join(ROOT_, "frozen_weight_gemms_amd", "libpact_nvfp4.so")
+if not os.path.exists(_so):       # build once if nothing is built
+    subprocess.run(["python", os.path.join(ROOT_, "frozen_weight_gemms_amd", "build.py")], check=True)
+
+from frozen_weight_gemms_amd import _lib  # noqa: E402
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return _lib.load()
+
+
+def test_header_symbols_exported(lib):
+    names = _lib.header_functions()
+    assert len(names) == 13, names
+    assert set(names) == set(_lib.SIGNATURES), set(names) ^ set(_lib.SIGNATURES)
+    for n in names:
+        assert hasattr(lib, n), n
+    # the dynamic symbol table has them unmangled (extern "C")
+    out = subprocess.run(["nm", "-D", "--defined-only", _lib.LIB_PATH], capture_output=True, text=True).stdout
+    syms = {line.split()[-1] for line in out.splitlines() if line.strip()}
+    for n in names:
+        assert n in syms, n
+
+
+def test_library_targets_gfx950_only():
+    """The embedded offload bundle holds gfx950 code objects and nothing else."""
+    import re
+    data = open(_lib.LIB_PATH, "rb").read()
+    targets = set(re.findall(rb"amdgcn-amd-amdhsa-[-a-z0-9:+]*", data))
+    assert targets == {b"amdgcn-amd-amdhsa--gfx950"}, targets
+
+
+def test_gemm_tile_query(lib):
+    assert _lib.gemm_tile(4096, 8192, 3072) == (256, 256)
+    assert _lib.gemm_tile(4096, 3072, 3072) == (256, 128)
+    assert _lib.gemm_tile(4096, 1024, 3072) == (128, 128)
+    assert lib.pact_gemm_tile(-1, 1, 1, None, None) == -1
+
+
+def test_abi_version(lib):
+    assert lib.pact_abi_version() == 1
+
+
+def test_sizes(lib):
+    c, s, r = ctypes.c_size_t(), ctypes.c_size_t(), ctypes.c_size_t()
+    assert lib.pact_nvfp4_sizes(4096, 3072, ctypes.byref(c), ctypes.byref(s), ctypes.byref(r)) == 0
+    assert (c.value, s.value, r.value) == (4096 * 1536, 4096 * 192, 4096 * 4)
+    assert (c.value + s.value) * 8 == 4096 * 3072 * 4.5
+    assert lib.pact_nvfp4_sizes(4, 24, ctypes.byref(c), ctypes.byref(s), ctypes.byref(r)) == -2
+    assert b"multiple of 16" in lib.pact_last_error()
+    assert lib.pact_nvfp4_sizes(-1, 16, ctypes.byref(c), ctypes.byref(s), ctypes.byref(r)) == -1
+
+
+ALIGNED = 1 << 20          # fake, 16-byte aligned addresses: never dereferenced on the error paths
+MISALIGNED = ALIGNED + 4
+
+
+def test_quantize_validation(lib):
+    q = lib.nvfp4_quantize
+    assert q(ALIGNED, 4, 24, 24, 0, ALIGNED, ALIGNED, ALIGNED, None) == -2          # cols % 16
+    assert q(ALIGNED, 4, 32, 32, 2, ALIGNED, ALIGNED, ALIGNED, None) == -1          # bad transpose flag
+    assert q(None, 4, 32, 32, 0, ALIGNED, ALIGNED, ALIGNED, None) == -1             # NULL x
+    assert q(MISALIGNED, 4, 32, 32, 0, ALIGNED, ALIGNED, ALIGNED, None) == -3       # misaligned x
+    assert q(ALIGNED, 4, 32, 16, 0, ALIGNED, ALIGNED, ALIGNED, None) == -2          # ldx < cols
+    assert q(ALIGNED, 4, 32, 36, 0, ALIGNED, ALIGNED, ALIGNED, None) == -3          # ldx % 8
+    assert q(ALIGNED, 4, 32, 2, 1, ALIGNED, ALIGNED, ALIGNED, None) == -2           # transposed ldx < rows
+    assert q(ALIGNED, 0, 32, 32, 0, None, None, None, None) == 0                    # empty: no-op
+    assert lib.pact_last_error() == b""
+
+
+def test_fused_validation(lib):
+    assert lib.rmsnorm_quant(ALIGNED, ALIGNED, 1e-5, 4, 20000, 20000, ALIGNED, ALIGNED, ALIGNED, ALIGNED,
+                             None) == -5
+    assert lib.rmsnorm_quant(ALIGNED, None, 1e-5, 4, 32, 32, ALIGNED, ALIGNED, ALIGNED, ALIGNED, None) == -1
+    assert lib.rmsnorm_quant(ALIGNED, ALIGNED, -1.0, 4, 32, 32, ALIGNED, ALIGNED, ALIGNED, ALIGNED, None) == -1
+    args9 = [ALIGNED] * 9
+    assert lib.silu_mul_quant(ALIGNED, ALIGNED, 4, 40, 40, *args9, None) == -2
+    args9[4] = MISALIGNED
+    assert lib.silu_mul_quant(ALIGNED, ALIGNED, 4, 32, 32, *args9, None) == -3
+    assert lib.silu_mul_quant(ALIGNED, ALIGNED, 0, 32, 32, *([None] * 9), None) == 0
+
+
+def test_gemm_validation(lib):
+    A = [ALIGNED] * 3
+    f = lib.nvfp4_gemm_fwd
+    assert f(*A, 64, 40, *A, 64, ALIGNED, 64, None, None, 0, 1.0, None) == -2      # K % 16
+    assert f(*A, 64, 64, *A, 64, ALIGNED, 32, None, None, 0, 1.0, None) == -2      # ldy < N
+    assert f(*A, 64, 64, *A, 64, ALIGNED, 64, ALIGNED, None, 8, 1.0, None) == -1   # T without B
+    assert f(*A, 64, 64, *A, 64, ALIGNED, 64, ALIGNED, ALIGNED, 0, 1.0, None) == -2   # rank 0
+    assert f(*A, 64, 64, *A, 64, ALIGNED, 64, ALIGNED, ALIGNED, 129, 1.0, None) == -2  # rank > 128
+    assert f(None, ALIGNED, ALIGNED, 64, 64, *A, 64, ALIGNED, 64, None, None, 0, 1.0, None) == -1
+    assert f(*A, 0, 64, *A, 64, None, 64, None, None, 0, 1.0, None) == 0              # empty: no-op
+    d = lib.nvfp4_gemm_dgrad
+    assert d(*A, 64, 64, *A, 64, ALIGNED, 64, 2, None, None, 0, None) == -1          # accumulate flag
+    assert d(*A, 64, 72, *A, 64, ALIGNED, 64, 0, None, None, 0, None) == -2          # N % 16
+    assert d(*A, 64, 64, *A, 64, ALIGNED, 64, 0, ALIGNED, None, 8, None) == -1
+
+
+def test_lora_and_backward_validation(lib):
+    A = [ALIGNED] * 3
+    assert lib.lora_down(*A, 64, 64, ALIGNED, 0, ALIGNED, None) == -2
+    assert lib.lora_down(*A, 64, 72, ALIGNED, 8, ALIGNED, None) == -2
+    assert lib.lora_down(*A, 64, 64, None, 8, ALIGNED, None) == -1
+    assert lib.lora_bwd(*A, 64, 64, ALIGNED, ALIGNED, 8, 1.0, ALIGNED, 40, ALIGNED, ALIGNED, ALIGNED, None) == -2
+    assert lib.silu_mul_bwd(*A, *A, ALIGNED, 4, 40, ALIGNED, ALIGNED, None) == -2
+    assert lib.rmsnorm_bwd(*A, ALIGNED, ALIGNED, ALIGNED, 4, 32, None, None) == -1
+    assert lib.rmsnorm_bwd(*A, ALIGNED, ALIGNED, ALIGNED, 0, 32, None, None) == 0
+
+
+def test_package_import_requires_library(tmp_path, monkeypatch):
+    """Without the built library the binding refuses to load (no CPU fallback)."""
+    monkeypatch.setattr(_lib, "_lib", None)
+    monkeypatch.setattr(_lib, "LIB_PATH", str(tmp_path / "missing.so"))
+    with pytest.raises(ImportError):
+        _lib.load()

@@ -1,0 +1,146 @@
+"""GPU parity: nvfp4_gemm_fwd / nvfp4_gemm_dgrad against the oracle's float64 GEMM.
+
+Frozen projections: NVFP4 GEMMs, FP32 accumulation, BF16 output, forward over
+W_fwd = Q(W) and input gradient over W_bwd = Q(W^T) (PACT, Appendix Table 7).
+Bound: |y - y_ref| <= ulp_bf16(y_ref) + 1e-5 * sum_k |a_k b_k| (+ the LoRA
+term's share).  Operands are quantized by the oracle and uploaded, so these
+tests do not depend on the GPU quantizer.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import synth
+from oracle import gemm as ogemm
+from oracle import lora as olora
+from oracle import nvfp4 as onv
+from oracle import tolerance as tol
+
+from gpu_util import assert_within, bf16_values, bits_to_torch, nvfp4_to_gpu, torch_bf16_to_f64
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def fw():
+    import frozen_weight_gemms_amd as fw
+    return fw
+
+
+def _q(bits):
+    return onv.quantize(bf16_values(bits).astype(np.float64))
+
+
+def _qt(bits):
+    return onv.quantize(bf16_values(bits).astype(np.float64), transpose=True)
+
+
+def test_tiny_fwd_dgrad(fw):
+    x = synth.workload_activation(synth.WORKLOADS[0], 64, 256, 1)
+    w = synth.normal_bf16((256, 256), 0.02, 0, 2)
+    dy = synth.normal_bf16((64, 256), 0.01, 0, 3)
+    xq, wf, wb, dyq = _q(x), _q(w), _qt(w), _q(dy)
+    y = fw.gemm_fwd(nvfp4_to_gpu(xq), nvfp4_to_gpu(wf))
+    yref, yabs = ogemm.gemm_fwd(xq, wf)
+    assert_within(torch_bf16_to_f64(y), yref, tol.gemm_bound(yref, yabs), "fwd")
+    dx = fw.gemm_dgrad(nvfp4_to_gpu(dyq), nvfp4_to_gpu(wb))
+    dref, dabs = ogemm.gemm_dgrad(dyq, wb)
+    assert_within(torch_bf16_to_f64(dx), dref, tol.gemm_bound(dref, dabs), "dgrad")
+
+
+def _direct(codes, scale_byte, rows):
+    packed = (codes[:, 0::2] | (codes[:, 1::2] << 4)).astype(np.uint8)
+    sc = np.asarray(scale_byte, dtype=np.uint8)
+    if sc.ndim == 0:
+        sc = np.full((rows, codes.shape[1] // 16), int(sc), np.uint8)
+    return onv.NVFP4(packed, sc, np.ones(rows, np.float32))
+
+
+@pytest.mark.parametrize("M,N,K", [(64, 64, 512), (300, 200, 512), (256, 512, 256)])
+def test_exact_special_case_bit_identical(fw, M, N, K):
+    """Scales in [1, 1.875] and row scale 1: FP32 accumulation is exact, so the
+    BF16 output must equal RNE of the exact result bit for bit."""
+    rng = np.random.default_rng(M * 7 + N)
+    ca, cb = rng.integers(0, 16, size=(M, K)), rng.integers(0, 16, size=(N, K))
+    sa = rng.integers(0x38, 0x40, size=(M, K // 16))       # 1.0 .. 1.875
+    sb = rng.integers(0x38, 0x40, size=(N, K // 16))
+    a, b = _direct(ca, sa, M), _direct(cb, sb, N)
+    y = fw.gemm_fwd(nvfp4_to_gpu(a), nvfp4_to_gpu(b))
+    yref, _ = ogemm.gemm_nt(a, b)
+    got = torch_bf16_to_f64(y)
+    want = tol.bf16_rne(yref)
+    assert np.array_equal(got, want), f"{np.sum(got != want)} outputs differ"
+
+
+@pytest.mark.parametrize("M,N,K", [(1, 16, 16), (7, 33, 48), (130, 257, 272), (300, 100, 1040),
+                                   (513, 640, 4096), (64, 2048, 128)])
+def test_ragged_shapes(fw, M, N, K):
+    a = synth.activations_bf16((M, K), 92, M + 3 * N + 7 * K)
+    b = synth.normal_bf16((N, K), 0.02, 92, M + 3 * N + 7 * K + 1)
+    aq, bq = _q(a), _q(b)
+    y = fw.gemm_fwd(nvfp4_to_gpu(aq), nvfp4_to_gpu(bq))
+    yref, yabs = ogemm.gemm_nt(aq, bq)
+    assert_within(torch_bf16_to_f64(y), yref, tol.gemm_bound(yref, yabs), f"{M}x{N}x{K}")
+
+
+def test_lora_epilogue_fwd(fw):
+    M, K, N, r, s = 96, 256, 320, 8, 2.0
+    x = synth.activations_bf16((M, K), 93, 1)
+    w = synth.normal_bf16((N, K), 0.02, 93, 2)
+    t = synth.normal_bf16((M, r), 0.3, 93, 3)
+    b = synth.normal_bf16((N, r), 0.01, 93, 4)
+    xq, wf = _q(x), _q(w)
+    gx, gw = nvfp4_to_gpu(xq), nvfp4_to_gpu(wf)
+    base = fw.gemm_fwd(gx, gw)
+    zero = fw.gemm_fwd(gx, gw, lora_t=bits_to_torch(t), lora_b=torch.zeros((N, r), dtype=torch.bfloat16,
+                                                                          device="cuda"), lora_scale=s)
+    assert torch.equal(base.view(torch.int16), zero.view(torch.int16)), "B = 0 must not change Y"
+    y = fw.gemm_fwd(gx, gw, lora_t=bits_to_torch(t), lora_b=bits_to_torch(b), lora_scale=s)
+    yref, yabs = ogemm.gemm_fwd(xq, wf)
+    term, tabs, _ = olora.lora_term(bf16_values(t), bf16_values(b).T, s)
+    assert_within(torch_bf16_to_f64(y), yref + term, tol.gemm_bound(yref + term, yabs + tabs), "fwd+lora")
+
+
+def test_dgrad_accumulate_and_lora(fw):
+    M, N, K, r = 80, 192, 272, 16
+    dy = synth.normal_bf16((M, N), 0.01, 94, 1)
+    w = synth.normal_bf16((N, K), 0.02, 94, 2)
+    dt = synth.normal_bf16((M, r), 0.01, 94, 3)
+    A = synth.normal_bf16((r, K), 0.01, 94, 4)
+    prev = synth.normal_bf16((M, K), 0.001, 94, 5)
+    dyq, wb = _q(dy), _qt(w)
+    out = bits_to_torch(prev).clone()
+    fw.gemm_dgrad(nvfp4_to_gpu(dyq), nvfp4_to_gpu(wb), out=out, accumulate=True,
+                  lora_dt=bits_to_torch(dt), lora_a=bits_to_torch(A))
+    dref, dabs = ogemm.gemm_dgrad(dyq, wb)
+    term, tabs, _ = olora.lora_term(bf16_values(dt), bf16_values(A), 1.0)
+    want = bf16_values(prev).astype(np.float64) + dref + term
+    # accumulate rounds once: the previous value enters exactly, so the bound is the same
+    assert_within(torch_bf16_to_f64(out), want, tol.gemm_bound(want, dabs + tabs), "dgrad acc+lora")
+
+
+LLAMA3B = [("q/o", 3072, 3072), ("k/v", 3072, 1024), ("gate/up", 3072, 8192), ("down", 8192, 3072)]
+
+
+@pytest.mark.parametrize("name,d_in,d_out", LLAMA3B)
+def test_llama3b_full_size_sampled(fw, name, d_in, d_out):
+    """Full Llama-3B projection shapes at M = 4096 (the benchmark's launches);
+    64 sampled rows of Y and dX against the oracle."""
+    M = 4096
+    wl = synth.WORKLOADS[2]
+    x = synth.workload_activation(wl, M, d_in, 601)
+    w = synth.normal_bf16((d_out, d_in), 0.02, 2, 602)
+    dy = synth.normal_bf16((M, d_out), 0.01, 2, 603)
+    xq, wf, wb, dyq = _q(x), _q(w), _qt(w), _q(dy)
+    y = fw.gemm_fwd(nvfp4_to_gpu(xq), nvfp4_to_gpu(wf))
+    dx = fw.gemm_dgrad(nvfp4_to_gpu(dyq), nvfp4_to_gpu(wb))
+    rows = np.sort(np.random.default_rng(d_in + d_out).choice(M, size=64, replace=False))
+    rows[-1] = M - 1
+    ysub = torch_bf16_to_f64(y)[rows]
+    dxsub = torch_bf16_to_f64(dx)[rows]
+    sel = lambda q: onv.NVFP4(q.codes[rows], q.scales[rows], q.rscale[rows])
+    yref, yabs = ogemm.gemm_nt(sel(xq), wf)
+    assert_within(ysub, yref, tol.gemm_bound(yref, yabs), f"{name} fwd")
+    dref, dabs = ogemm.gemm_nt(sel(dyq), wb)
+    assert_within(dxsub, dref, tol.gemm_bound(dref, dabs), f"{name} dgrad")

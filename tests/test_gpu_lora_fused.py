@@ -1,0 +1,129 @@
+"""GPU parity: LoRA branch kernels and the fused RMSNorm / SiLU-multiply kernels.
+
+PACT, Appendix Table 7: LoRA branch = BF16 GEMMs on reconstructed inputs and
+BF16 adapter gradients; RMSNorm / SiLU-multiply fused with NVFP4 quantization
+forward (codes bit-exact) and FP32 reconstruction backward (within
+2 ulp_bf16 + 2^-17 * cancelling magnitude).
+"""
+
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import synth
+from oracle import backward as obwd
+from oracle import fused as ofused
+from oracle import lora as olora
+from oracle import nvfp4 as onv
+from oracle import tolerance as tol
+
+from gpu_util import (assert_nvfp4_equal, assert_within, bf16_values, bits_to_torch, nvfp4_to_gpu,
+                      torch_bf16_to_f64)
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def fw():
+    import frozen_weight_gemms_amd as fw
+    return fw
+
+
+def _q(bits):
+    return onv.quantize(bf16_values(bits).astype(np.float64))
+
+
+# ---------------------------------------------------------------- LoRA
+@pytest.mark.parametrize("M,K,N,r", [(64, 256, 256, 8), (37, 48, 80, 5), (4096, 3072, 1024, 16), (300, 512, 272, 64),
+                                     (128, 256, 128, 128)])
+def test_lora_down_and_bwd(fw, M, K, N, r):
+    s = 2.0
+    x = synth.activations_bf16((M, K), 95, M + K)
+    A = synth.normal_bf16((r, K), 0.01, 95, M + K + 1)
+    B = synth.normal_bf16((N, r), 0.01, 95, M + K + 2)
+    dy = synth.normal_bf16((M, N), 0.01, 95, M + K + 3)
+    xq = _q(x)
+    gx = nvfp4_to_gpu(xq)
+    T = fw.lora_down(gx, bits_to_torch(A))
+    t_exact, _, t_abs = olora.lora_down(xq, bf16_values(A))
+    assert_within(torch_bf16_to_f64(T), t_exact, tol.gemm_bound(t_exact, t_abs), "T")
+    dT, dA, dB = fw.lora_bwd(gx, bits_to_torch(A), bits_to_torch(B), bits_to_torch(dy), s)
+    ref = olora.lora_bwd(xq, bf16_values(A), bf16_values(B), bf16_values(dy), s)
+    assert_within(torch_bf16_to_f64(dT), ref["dT_exact"], tol.gemm_bound(ref["dT_exact"], ref["dT_abs"]), "dT")
+    assert_within(torch_bf16_to_f64(dB), ref["dB_exact"],
+                  tol.gemm_bound(ref["dB_exact"], ref["dB_abs"], ref["dB_tslack"]), "dB")
+    assert_within(torch_bf16_to_f64(dA), ref["dA_exact"],
+                  tol.gemm_bound(ref["dA_exact"], ref["dA_abs"], ref["dA_tslack"]), "dA")
+
+
+# ---------------------------------------------------------------- RMSNorm
+def _rms_inputs(M, H, wid=3, tid=700):
+    x = synth.activations_bf16((M, H), wid, tid)
+    g = synth.uniform_bf16((H,), 0.9, 1.1, wid, tid + 1)
+    return x, g
+
+
+@pytest.mark.parametrize("M,H,exact", [(64, 256, "0"), (33, 3072, "0"), (33, 3072, "1"), (8192, 3072, "0"),
+                                       (17, 16384, "0"), (5, 48, "1")])
+def test_rmsnorm_quant(fw, M, H, exact, monkeypatch):
+    monkeypatch.setenv("PACT_RMSNORM_EXACT_SUM", exact)
+    x, g = _rms_inputs(M, H, tid=700 + H)
+    yq, rstd = fw.rmsnorm_quant(bits_to_torch(x), bits_to_torch(g), 1e-5)
+    ref_q, ref_rstd, _ = ofused.rmsnorm_quant(bf16_values(x), bf16_values(g), 1e-5)
+    got_rstd = rstd.cpu().numpy()
+    bad = np.flatnonzero(got_rstd.view(np.uint32) != ref_rstd.view(np.uint32))
+    assert bad.size == 0, f"rstd differs in {bad.size} rows, first {bad[:5]}"
+    assert_nvfp4_equal(yq, ref_q, f"rmsnorm {M}x{H}")
+
+
+def test_rmsnorm_bwd(fw):
+    M, H = 257, 3072
+    x, g = _rms_inputs(M, H, tid=710)
+    dy = synth.normal_bf16((M, H), 0.01, 3, 712)
+    yq, rstd, _ = ofused.rmsnorm_quant(bf16_values(x), bf16_values(g), 1e-5)
+    dx = fw.rmsnorm_bwd(nvfp4_to_gpu(yq), torch.from_numpy(rstd).cuda(), bits_to_torch(g), bits_to_torch(dy))
+    ref, cancel = obwd.rmsnorm_bwd(yq, rstd, bf16_values(g), bf16_values(dy))
+    assert_within(torch_bf16_to_f64(dx), ref, tol.grad_bound(ref, cancel), "rmsnorm_bwd")
+
+
+# ---------------------------------------------------------------- SiLU-multiply
+@pytest.mark.parametrize("M,I", [(64, 256), (19, 8192), (7, 14336), (3, 48)])
+def test_silu_mul_quant(fw, M, I):
+    a = synth.normal_bf16((M, I), 2.0, 96, I + 1)
+    b = synth.normal_bf16((M, I), 1.0, 96, I + 2)
+    if M >= 3:
+        av = bf16_values(a).copy()
+        av[0, :16] = [0, -0.0, 100, -100, 88, -88, 89.5, -89.5, 80.25, -80.25, 1e-30, -1e-30, 3, -3, 1e-3, -1e-3]
+        a = synth.bf16_bits(av)
+    hq, gq, uq = fw.silu_mul_quant(bits_to_torch(a), bits_to_torch(b))
+    rh, ra, rb, _ = ofused.silu_mul_quant(bf16_values(a), bf16_values(b))
+    assert_nvfp4_equal(gq, ra, "gate copy")
+    assert_nvfp4_equal(uq, rb, "up copy")
+    assert_nvfp4_equal(hq, rh, "h")
+
+
+def test_silu_mul_quant_full_size_sampled(fw):
+    """MLP-block shape [8192 x 8192]; rows are independent, 256 sampled rows checked."""
+    M, I = 8192, 8192
+    a = synth.normal_bf16((M, I), 2.0, 3, 720)
+    b = synth.normal_bf16((M, I), 1.0, 3, 721)
+    hq, gq, uq = fw.silu_mul_quant(bits_to_torch(a), bits_to_torch(b))
+    rows = np.sort(np.random.default_rng(5).choice(M, size=256, replace=False))
+    rh, ra, rb, _ = ofused.silu_mul_quant(bf16_values(a[rows]), bf16_values(b[rows]))
+    assert_nvfp4_equal(hq, rh, "h", rows=rows)
+    assert_nvfp4_equal(gq, ra, "gate", rows=rows)
+    assert_nvfp4_equal(uq, rb, "up", rows=rows)
+
+
+@pytest.mark.parametrize("M,I", [(64, 256), (33, 8192)])
+def test_silu_mul_bwd(fw, M, I):
+    a = synth.normal_bf16((M, I), 2.0, 97, I + 1)
+    b = synth.normal_bf16((M, I), 1.0, 97, I + 2)
+    dh = synth.normal_bf16((M, I), 0.01, 97, I + 3)
+    aq, bq = _q(a), _q(b)
+    dg, du = fw.silu_mul_bwd(nvfp4_to_gpu(aq), nvfp4_to_gpu(bq), bits_to_torch(dh))
+    da, db, cda, cdb = obwd.silu_mul_bwd(aq, bq, bf16_values(dh))
+    assert_within(torch_bf16_to_f64(dg), da, tol.grad_bound(da, cda), "dgate")
+    assert_within(torch_bf16_to_f64(du), db, tol.grad_bound(db, cdb), "dup")
