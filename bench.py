@@ -86,6 +86,9 @@ class Layer:
                                      dA=torch.empty((r, p.d_in), dtype=torch.bfloat16, device=dev),
                                      dB=torch.empty((p.d_out, r), dtype=torch.bfloat16, device=dev),
                                      dyq=fw.empty_nvfp4(M, p.d_out, dev))
+        # one LoRA-backward workspace sized for the largest projection (calls are stream-ordered)
+        ws_bytes = max(fw._lib.lora_bwd_workspace_size(M, p.d_in, p.d_out, r) for p in wl.projections)
+        self.lora_ws = torch.empty((ws_bytes,), dtype=torch.uint8, device=dev)
         nv = lambda cols: fw.empty_nvfp4(M, cols, dev)
         self.y1q, self.y2q, self.aq = nv(H), nv(H), nv(H)
         self.rstd1 = torch.empty((M,), dtype=torch.float32, device=dev)
@@ -123,7 +126,8 @@ class Layer:
         self._ev("quant", "nvfp4_quantize", ("quant", self.M, p.d_out),
                  lambda: fw.quantize(dy, out=P["dyq"]))
         self._ev("lora", "lora_bwd", None,
-                 lambda: fw.lora_bwd(xq, P["A"], P["B"], dy, LORA_SCALE, out=(P["dT"], P["dA"], P["dB"])))
+                 lambda: fw.lora_bwd(xq, P["A"], P["B"], dy, LORA_SCALE, out=(P["dT"], P["dA"], P["dB"]),
+                                     workspace=self.lora_ws))
         work = ("gemm", self.M, p.d_in, p.d_out)
         self._ev("gemm", f"dgrad {name}", work,
                  lambda: fw.gemm_dgrad(P["dyq"], P["wb"], out=dx, accumulate=accumulate, lora_dt=P["dT"],
@@ -241,18 +245,49 @@ def main():
         layer.step()
     torch.cuda.synchronize()
 
-    # timed region: K steps, wall clock + events on the launch stream
-    layer.record = []
+    # The step is captured once into a HIP graph (every output buffer and the
+    # LoRA workspace are preallocated, so the step allocates nothing); the timed
+    # region replays it.  If capture is unavailable the timed region runs the
+    # step eagerly.
+    graph = None
+    try:
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            layer.step()
+        torch.cuda.current_stream().wait_stream(side)
+        torch.cuda.synchronize()
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            layer.step()
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+    except Exception as ex:            # capture not supported: time eagerly
+        print(f"graph capture unavailable ({ex}); timing eager steps", file=sys.stderr)
+        graph = None
+    run = graph.replay if graph is not None else layer.step
+
+    # timed region: K steps, wall clock and events on the launch stream
     ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     ev0.record()
     for _ in range(args.steps):
-        layer.step()
+        run()
     ev1.record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     gpu_ms = ev0.elapsed_time(ev1)
+
+    # instrumented pass over the same K steps: events around every launch give
+    # per-kernel durations (events add host and queue overhead between kernels,
+    # so this pass is not the one the step time comes from)
+    layer.record = []
+    torch.cuda.synchronize()
+    for _ in range(args.steps):
+        layer.step()
+    torch.cuda.synchronize()
     recs = layer.record
     layer.record = None
 
@@ -318,7 +353,8 @@ def main():
         "frac_fp16_peak": round(value / PEAK["fp16_mfma_tflops"], 4),
         "gemm_only_tflops": round(flops / (gemm_ms * 1e-3) / 1e12, 1),
         "gpu_ms_per_step_events": round(gpu_ms / steps, 4),
-        "ms_per_step_by_category": {k: round(v / steps, 4) for k, v in sorted(cat_ms.items())},
+        "timed_region": "hip graph replays of the step" if graph is not None else "eager steps",
+        "kernel_ms_per_step_by_category": {k: round(v / steps, 4) for k, v in sorted(cat_ms.items())},
         "bandwidth_kernels": quant,
         "roofline": {"kernel": kname, "bound": "mfma", "achieved": round(achieved, 1),
                      "peak": PEAK["fp16_mfma_tflops"], "unit": "TFLOP/s",

@@ -17,7 +17,7 @@ from ._lib import PactError, load  # noqa: F401
 
 __all__ = [
     "NVFP4Tensor", "empty_nvfp4", "quantize", "rmsnorm_quant", "silu_mul_quant", "gemm_fwd", "gemm_dgrad",
-    "lora_down", "lora_bwd", "silu_mul_bwd", "rmsnorm_bwd", "weight_layouts", "PactError",
+    "lora_down", "lora_bwd", "lora_bwd_workspace", "silu_mul_bwd", "rmsnorm_bwd", "weight_layouts", "PactError",
 ]
 
 
@@ -160,8 +160,15 @@ def lora_down(xq: NVFP4Tensor, A: torch.Tensor, out: torch.Tensor | None = None)
     return out
 
 
-def lora_bwd(xq: NVFP4Tensor, A: torch.Tensor, B: torch.Tensor, dy: torch.Tensor, scale: float, out=None):
-    """(dT, dA, dB); ``out`` = (dT, dA, dB) tensors to reuse."""
+def lora_bwd_workspace(M: int, K: int, N: int, r: int, device="cuda") -> torch.Tensor:
+    """A workspace tensor of the size lora_bwd needs for these shapes (caller-owned, reusable)."""
+    n = _lib.lora_bwd_workspace_size(M, K, N, r)
+    return torch.empty((max(n, 1),), dtype=torch.uint8, device=device)
+
+
+def lora_bwd(xq: NVFP4Tensor, A: torch.Tensor, B: torch.Tensor, dy: torch.Tensor, scale: float, out=None,
+             workspace: torch.Tensor | None = None):
+    """(dT, dA, dB); ``out`` = (dT, dA, dB) tensors to reuse; ``workspace`` from lora_bwd_workspace()."""
     _bf16(A, "A"); _bf16(B, "B"); _bf16(dy, "dy")
     r, K = A.shape
     N = B.shape[0]
@@ -175,8 +182,10 @@ def lora_bwd(xq: NVFP4Tensor, A: torch.Tensor, B: torch.Tensor, dy: torch.Tensor
         dT = torch.empty((M, r), dtype=torch.bfloat16, device=dev)
         dA = torch.empty((r, K), dtype=torch.bfloat16, device=dev)
         dB = torch.empty((N, r), dtype=torch.bfloat16, device=dev)
+    if workspace is None:
+        workspace = lora_bwd_workspace(M, K, N, r, dev)
     _lib.call("lora_bwd", *xq.ptrs(), M, K, A.data_ptr(), B.data_ptr(), r, float(scale), dy.data_ptr(), N,
-              dT.data_ptr(), dA.data_ptr(), dB.data_ptr(), _stream())
+              dT.data_ptr(), dA.data_ptr(), dB.data_ptr(), workspace.data_ptr(), workspace.numel(), _stream())
     return dT, dA, dB
 
 

@@ -38,8 +38,9 @@ SIGNATURES = {
     "nvfp4_gemm_dgrad": ([c_vp, c_vp, c_vp, c_i64, c_i64, c_vp, c_vp, c_vp, c_i64, c_vp, c_i64, c_int,
                           c_vp, c_vp, c_i64, c_vp], c_int),
     "lora_down": ([c_vp, c_vp, c_vp, c_i64, c_i64, c_vp, c_i64, c_vp, c_vp], c_int),
+    "pact_lora_bwd_workspace_size": ([c_i64, c_i64, c_i64, c_i64, c_size_p], c_int),
     "lora_bwd": ([c_vp, c_vp, c_vp, c_i64, c_i64, c_vp, c_vp, c_i64, c_float, c_vp, c_i64,
-                  c_vp, c_vp, c_vp, c_vp], c_int),
+                  c_vp, c_vp, c_vp, c_vp, ctypes.c_size_t, c_vp], c_int),
     "silu_mul_bwd": ([c_vp] * 7 + [c_i64, c_i64, c_vp, c_vp, c_vp], c_int),
     "rmsnorm_bwd": ([c_vp] * 6 + [c_i64, c_i64, c_vp, c_vp], c_int),
 }
@@ -92,6 +93,13 @@ def gemm_tile(M: int, Nout: int, Kr: int):
     bm, bn = c_int(), c_int()
     check(lib.pact_gemm_tile(M, Nout, Kr, ctypes.byref(bm), ctypes.byref(bn)))
     return bm.value, bn.value
+
+
+def lora_bwd_workspace_size(M: int, K: int, N: int, r: int) -> int:
+    lib = load()
+    n = ctypes.c_size_t()
+    check(lib.pact_lora_bwd_workspace_size(M, K, N, r, ctypes.byref(n)))
+    return n.value
 
 
 def call(name: str, *args):

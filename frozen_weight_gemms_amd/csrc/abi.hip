@@ -219,23 +219,38 @@ int lora_down(const uint8_t* x_codes, const uint8_t* x_scales, const float* x_rs
                     "lora_down launch");
 }
 
+int pact_lora_bwd_workspace_size(int64_t M, int64_t K, int64_t N, int64_t r, size_t* bytes) {
+  REQUIRE(M >= 0 && K >= 0 && N >= 0, PACT_EINVAL, "negative size");
+  REQUIRE(r >= 1 && r <= kMaxRank, PACT_ESHAPE, "rank %lld outside [1, %lld]", (long long)r, (long long)kMaxRank);
+  REQUIRE(bytes != nullptr, PACT_EINVAL, "NULL output pointer");
+  *bytes = pact::lora_bwd_workspace(M, K, N, r);
+  return ok();
+}
+
 int lora_bwd(const uint8_t* x_codes, const uint8_t* x_scales, const float* x_rscale, int64_t M, int64_t K,
              const uint16_t* A, const uint16_t* B, int64_t r, float scale, const uint16_t* dy, int64_t N,
-             uint16_t* dT, uint16_t* dA, uint16_t* dB, void* stream) {
+             uint16_t* dT, uint16_t* dA, uint16_t* dB, void* workspace, size_t workspace_bytes, void* stream) {
   REQUIRE(M >= 0 && K >= 0 && N >= 0, PACT_EINVAL, "negative size");
   REQUIRE(K % 16 == 0 && N % 16 == 0, PACT_ESHAPE, "K=%lld and N=%lld must be multiples of 16", (long long)K,
           (long long)N);
   REQUIRE(r >= 1 && r <= kMaxRank, PACT_ESHAPE, "rank %lld outside [1, %lld]", (long long)r, (long long)kMaxRank);
-  int st = check_nvfp4(x_codes, x_scales, x_rscale, "x");
-  if (st != PACT_OK && M > 0) return st;
+  if (M > 0) {
+    int st = check_nvfp4(x_codes, x_scales, x_rscale, "x");
+    if (st != PACT_OK) return st;
+    REQUIRE_PTR(dy, "dy");
+    REQUIRE_PTR(dT, "dT");
+  }
   REQUIRE_PTR(A, "A");
   REQUIRE_PTR(B, "B");
-  REQUIRE_PTR(dT, "dT");
   REQUIRE_PTR(dA, "dA");
   REQUIRE_PTR(dB, "dB");
-  if (M > 0) REQUIRE_PTR(dy, "dy");
+  const size_t need = pact::lora_bwd_workspace(M, K, N, r);
+  REQUIRE(workspace != nullptr, PACT_EINVAL, "workspace is NULL (needs %zu bytes)", need);
+  REQUIRE((reinterpret_cast<uintptr_t>(workspace) & 255u) == 0, PACT_EALIGN, "workspace is not 256-byte aligned");
+  REQUIRE(workspace_bytes >= need, PACT_EINVAL, "workspace has %zu bytes, needs %zu", workspace_bytes, need);
+  REQUIRE((M + 15) / 16 < 0x7FFFFFFF, PACT_EUNSUPPORTED, "M too large");
   return hip_status(pact::launch_lora_bwd(x_codes, x_scales, x_rscale, M, K, A, B, r, scale, dy, N, dT, dA, dB,
-                                          as_stream(stream)),
+                                          workspace, as_stream(stream)),
                     "lora_bwd launch");
 }
 

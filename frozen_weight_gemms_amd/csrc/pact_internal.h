@@ -46,9 +46,11 @@ void gemm_tile(int64_t M, int64_t N, int* bm, int* bn);
 hipError_t launch_lora_down(const uint8_t* xc, const uint8_t* xs, const float* xr, int64_t M, int64_t K,
                             const uint16_t* A, int64_t r, uint16_t* T, hipStream_t s);
 
+size_t lora_bwd_workspace(int64_t M, int64_t K, int64_t N, int64_t r);
+
 hipError_t launch_lora_bwd(const uint8_t* xc, const uint8_t* xs, const float* xr, int64_t M, int64_t K,
                            const uint16_t* A, const uint16_t* B, int64_t r, float scale, const uint16_t* dy,
-                           int64_t N, uint16_t* dT, uint16_t* dA, uint16_t* dB, hipStream_t s);
+                           int64_t N, uint16_t* dT, uint16_t* dA, uint16_t* dB, void* workspace, hipStream_t s);
 
 hipError_t launch_silu_mul_bwd(const uint8_t* gc, const uint8_t* gs, const float* gr, const uint8_t* uc,
                                const uint8_t* us, const float* ur, const uint16_t* dh, int64_t M, int64_t I,

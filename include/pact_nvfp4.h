@@ -165,15 +165,22 @@ int lora_down(const uint8_t *x_codes, const uint8_t *x_scales, const float *x_rs
  * and the BF16 adapters, so T is recomputed).  With X~ = deq(X_q) [M x K],
  * A [r x K], B [N x r], the BF16 output gradient dY [M x N] (row-major) and
  * scale s:
- *   T  = bf16(X~ A^T)          (recomputed)
+ *   T  = bf16(X~ A^T)          (recomputed into the workspace)
  *   dT = bf16(s dY B)          [M x r]   (feeds nvfp4_gemm_dgrad's LoRA term)
  *   dB = bf16(s dY^T T)        [N x r]
  *   dA = bf16(dT^T X~)         [r x K]
- * 1 <= r <= 128; K % 16 == 0.
+ * The reductions over M are split across workgroups into FP32 partials in
+ * `workspace` (device memory owned by the caller, at least
+ * pact_lora_bwd_workspace_size() bytes, 256-byte aligned) and summed in a fixed
+ * order, so results are deterministic.  Calls that share a workspace must not
+ * overlap.  1 <= r <= 128; K % 16 == 0; N % 16 == 0.
  */
+int pact_lora_bwd_workspace_size(int64_t M, int64_t K, int64_t N, int64_t r, size_t *bytes);
+
 int lora_bwd(const uint8_t *x_codes, const uint8_t *x_scales, const float *x_rscale,
              int64_t M, int64_t K, const uint16_t *A, const uint16_t *B, int64_t r, float scale,
-             const uint16_t *dy, int64_t N, uint16_t *dT, uint16_t *dA, uint16_t *dB, void *stream);
+             const uint16_t *dy, int64_t N, uint16_t *dT, uint16_t *dA, uint16_t *dB,
+             void *workspace, size_t workspace_bytes, void *stream);
 
 /*
  * silu_mul_bwd -- SiLU-multiply backward from the NVFP4 state (Appendix Table 7

@@ -25,7 +25,7 @@ def lib():
 
 def test_header_symbols_exported(lib):
     names = _lib.header_functions()
-    assert len(names) == 13, names
+    assert len(names) == 14, names
     assert set(names) == set(_lib.SIGNATURES), set(names) ^ set(_lib.SIGNATURES)
     for n in names:
         assert hasattr(lib, n), n
@@ -46,7 +46,7 @@ def test_library_targets_gfx950_only():
 
 def test_gemm_tile_query(lib):
     assert _lib.gemm_tile(4096, 8192, 3072) == (256, 256)
-    assert _lib.gemm_tile(4096, 3072, 3072) == (256, 128)
+    assert _lib.gemm_tile(4096, 3072, 3072) == (256, 192)
     assert _lib.gemm_tile(4096, 1024, 3072) == (128, 128)
     assert lib.pact_gemm_tile(-1, 1, 1, None, None) == -1
 
@@ -115,7 +115,16 @@ def test_lora_and_backward_validation(lib):
     assert lib.lora_down(*A, 64, 64, ALIGNED, 0, ALIGNED, None) == -2
     assert lib.lora_down(*A, 64, 72, ALIGNED, 8, ALIGNED, None) == -2
     assert lib.lora_down(*A, 64, 64, None, 8, ALIGNED, None) == -1
-    assert lib.lora_bwd(*A, 64, 64, ALIGNED, ALIGNED, 8, 1.0, ALIGNED, 40, ALIGNED, ALIGNED, ALIGNED, None) == -2
+    assert lib.lora_bwd(*A, 64, 64, ALIGNED, ALIGNED, 8, 1.0, ALIGNED, 40, ALIGNED, ALIGNED, ALIGNED, ALIGNED,
+                        1 << 30, None) == -2
+    need = _lib.lora_bwd_workspace_size(4096, 3072, 8192, 16)
+    assert need > 4096 * 16 * 2
+    assert lib.lora_bwd(*A, 64, 64, ALIGNED, ALIGNED, 8, 1.0, ALIGNED, 64, ALIGNED, ALIGNED, ALIGNED, None,
+                        1 << 30, None) == -1                                        # no workspace
+    assert lib.lora_bwd(*A, 64, 64, ALIGNED, ALIGNED, 8, 1.0, ALIGNED, 64, ALIGNED, ALIGNED, ALIGNED, ALIGNED,
+                        16, None) == -1                                             # too small
+    assert lib.lora_bwd(*A, 64, 64, ALIGNED, ALIGNED, 8, 1.0, ALIGNED, 64, ALIGNED, ALIGNED, ALIGNED,
+                        ALIGNED + 16, 1 << 30, None) == -3                          # misaligned
     assert lib.silu_mul_bwd(*A, *A, ALIGNED, 4, 40, ALIGNED, ALIGNED, None) == -2
     assert lib.rmsnorm_bwd(*A, ALIGNED, ALIGNED, ALIGNED, 4, 32, None, None) == -1
     assert lib.rmsnorm_bwd(*A, ALIGNED, ALIGNED, ALIGNED, 0, 32, None, None) == 0
