@@ -354,6 +354,12 @@ struct FastCfg {
   static constexpr int STAGE = PAD + (NS * 4 - NS_TOTAL) * 256;
   static constexpr int NSTAGE = 3;
   static constexpr int LOADS = NC + NS;                 // vmcnt per stage per wave
+  // epilogue: per wave, one 32-row slab of its (BN/2)-column tile as FP32
+  static constexpr int EPI_LD = BN / 2 + 4;             // floats per staged row (pad breaks bank aliasing)
+  static constexpr int EPI_WAVE = 32 * EPI_LD * 4;      // bytes per wave
+  static constexpr int MAIN = NSTAGE * STAGE > 4 * EPI_WAVE ? NSTAGE * STAGE : 4 * EPI_WAVE;
+  static constexpr int RSC = MAIN;                      // row scales of A (BM floats) then B (BN floats)
+  static constexpr int TOTAL = RSC + ROWS * 4;
 };
 
 // Global -> LDS loads of 16 / 4 bytes per lane.  Issued through inline asm so
@@ -380,7 +386,7 @@ template <int WTM, int WTN>
 __global__ __launch_bounds__(256, 1) void k_gemm_nvfp4_fast(GemmArgs p, int tiles_m, int tiles_n) {
   using C = FastCfg<WTM, WTN>;
   constexpr int BM = C::BM, BN = C::BN;
-  __shared__ __attribute__((aligned(1024))) uint8_t smem[C::NSTAGE * C::STAGE];
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[C::TOTAL];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
@@ -402,6 +408,19 @@ __global__ __launch_bounds__(256, 1) void k_gemm_nvfp4_fast(GemmArgs p, int tile
   const int64_t M = p.M, N = p.N, K = p.K;
   const int64_t crow = K >> 1, srow = K >> 4;
   const int nk = (int)(K / KT);
+
+  // row scales of this tile's A rows and B rows, staged once (clamped at the edges)
+  float* rsc = reinterpret_cast<float*>(smem + C::RSC);
+  for (int q = tid; q < C::ROWS; q += 256) {
+    if (q < BM) {
+      const int64_t m = m0 + q;
+      rsc[q] = p.a_rscale[m < M ? m : M - 1];
+    } else {
+      const int64_t n = n0 + (q - BM);
+      rsc[q] = p.b_rscale[n < N ? n : N - 1];
+    }
+  }
+  __syncthreads();
 
   floatx16 acc[WTM][WTN];
 #pragma unroll
@@ -441,20 +460,20 @@ __global__ __launch_bounds__(256, 1) void k_gemm_nvfp4_fast(GemmArgs p, int tile
         for (int j = 0; j < WTN; ++j)
           acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tf[i], uf[j], acc[i][j], 0, 0, 0);
     }
+    // row scales are powers of two: 1/r is exact and computed on the exponent
+    auto inv_pow2 = [](float r) { return __uint_as_float((254u << 23) - __float_as_uint(r)); };
 #pragma unroll
-    for (int j = 0; j < WTN; ++j) {
-      int64_t n = n0 + wn * (BN / 2) + j * 32 + li;
-      n = n < N ? n : N - 1;
-      const float inv_b = 1.0f / p.b_rscale[n];
+    for (int i = 0; i < WTM; ++i)
 #pragma unroll
-      for (int i = 0; i < WTM; ++i)
+      for (int rr = 0; rr < 16; ++rr) {
+        const int row = wm * (BM / 2) + i * 32 + 8 * (rr >> 2) + 4 * h + (rr & 3);
+        const float fa = p.lora_scale * inv_pow2(rsc[row]);
 #pragma unroll
-        for (int rr = 0; rr < 16; ++rr) {
-          int64_t m = m0 + wm * (BM / 2) + i * 32 + 8 * (rr >> 2) + 4 * h + (rr & 3);
-          m = m < M ? m : M - 1;
-          acc[i][j][rr] *= (p.lora_scale * (1.0f / p.a_rscale[m])) * inv_b;
+        for (int j = 0; j < WTN; ++j) {
+          const int col = wn * (BN / 2) + j * 32 + li;
+          acc[i][j][rr] *= fa * inv_pow2(rsc[BM + col]);
         }
-    }
+      }
   }
 
   // ---- per-lane global source addresses for this wave's load instructions ----
@@ -582,23 +601,58 @@ __global__ __launch_bounds__(256, 1) void k_gemm_nvfp4_fast(GemmArgs p, int tile
     }
   }
 
+  // ---- epilogue: row scales, optional accumulate, BF16 rounding ----
+  // Each wave stages one 32-row slab of its tile at a time in LDS as FP32
+  // (MFMA layout in, row-major out), then every lane writes 8 consecutive
+  // columns of a row with one 16-byte store.
+  __syncthreads();                                     // all waves are done reading the stage buffers
+  float* epi = reinterpret_cast<float*>(smem + wave * C::EPI_WAVE);
+  constexpr int WN = BN / 2;                            // columns of this wave's tile
+  constexpr int CHUNKS = WN / 8;                        // 8-column chunks per row
+  const bool vec_ok = (p.ldo % 8) == 0 && ((reinterpret_cast<uintptr_t>(p.out) & 15u) == 0);
 #pragma unroll
-  for (int j = 0; j < WTN; ++j) {
-    const int64_t n = n0 + wn * (BN / 2) + j * 32 + li;
-    if (n >= N) continue;
-    const float rb = p.b_rscale[n];
+  for (int i = 0; i < WTM; ++i) {
 #pragma unroll
-    for (int i = 0; i < WTM; ++i)
+    for (int j = 0; j < WTN; ++j) {
+      const int col = j * 32 + li;
+      const float rb = rsc[BM + wn * WN + col];
 #pragma unroll
       for (int rr = 0; rr < 16; ++rr) {
-        const int64_t m = m0 + wm * (BM / 2) + i * 32 + 8 * (rr >> 2) + 4 * h + (rr & 3);
-        if (m < M) {
-          float v = acc[i][j][rr] * (p.a_rscale[m] * rb);
-          uint16_t* dst = p.out + m * p.ldo + n;
-          if (p.accumulate) v += __uint_as_float((uint32_t)*dst << 16);
-          *dst = (uint16_t)f32_to_bf16_rne(v);
+        const int row = 8 * (rr >> 2) + 4 * h + (rr & 3);
+        epi[row * C::EPI_LD + col] = acc[i][j][rr] * (rsc[wm * (BM / 2) + i * 32 + row] * rb);
+      }
+    }
+    __builtin_amdgcn_s_waitcnt(0xc07f);                 // lgkmcnt(0): this wave's LDS writes done
+    __builtin_amdgcn_wave_barrier();
+    for (int q = lane; q < 32 * CHUNKS; q += 64) {
+      const int row = q / CHUNKS, ch = q % CHUNKS;
+      const int64_t m = m0 + wm * (BM / 2) + i * 32 + row;
+      const int64_t n = n0 + wn * WN + ch * 8;
+      if (m >= M || n >= N) continue;
+      const float* src = epi + row * C::EPI_LD + ch * 8;
+      float v[8];
+#pragma unroll
+      for (int t = 0; t < 8; ++t) v[t] = src[t];
+      uint16_t* dst = p.out + m * p.ldo + n;
+      if (vec_ok && n + 8 <= N) {
+        if (p.accumulate) {
+          const uint4 old = *reinterpret_cast<const uint4*>(dst);
+          v[0] += bf16_lo(old.x); v[1] += bf16_hi(old.x); v[2] += bf16_lo(old.y); v[3] += bf16_hi(old.y);
+          v[4] += bf16_lo(old.z); v[5] += bf16_hi(old.z); v[6] += bf16_lo(old.w); v[7] += bf16_hi(old.w);
+        }
+        uint4 o;
+        o.x = pack_bf16x2(v[0], v[1]); o.y = pack_bf16x2(v[2], v[3]);
+        o.z = pack_bf16x2(v[4], v[5]); o.w = pack_bf16x2(v[6], v[7]);
+        *reinterpret_cast<uint4*>(dst) = o;
+      } else {
+        for (int t = 0; t < 8 && n + t < N; ++t) {
+          float x = v[t];
+          if (p.accumulate) x += __uint_as_float((uint32_t)dst[t] << 16);
+          dst[t] = (uint16_t)f32_to_bf16_rne(x);
         }
       }
+    }
+    __builtin_amdgcn_wave_barrier();                    // slab consumed before the next one is written
   }
 }
 
