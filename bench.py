@@ -44,6 +44,7 @@ def parse():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true", help="skip the oracle timing on host cores")
     ap.add_argument("--cpu-sample-rows", type=int, default=32)
+    ap.add_argument("--eager", action="store_true", help="time eager launches instead of a captured HIP graph")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a 1 GiB read + 1 GiB write elementwise kernel (counter calibration)")
     return ap.parse_args()
@@ -251,6 +252,8 @@ def main():
     # step eagerly.
     graph = None
     try:
+        if args.eager:
+            raise RuntimeError("--eager")
         side = torch.cuda.Stream()
         side.wait_stream(torch.cuda.current_stream())
         with torch.cuda.stream(side):
@@ -264,7 +267,8 @@ def main():
         graph.replay()
         torch.cuda.synchronize()
     except Exception as ex:            # capture not supported: time eagerly
-        print(f"graph capture unavailable ({ex}); timing eager steps", file=sys.stderr)
+        if not args.eager:
+            print(f"graph capture unavailable ({ex}); timing eager steps", file=sys.stderr)
         graph = None
     run = graph.replay if graph is not None else layer.step
 
@@ -302,7 +306,7 @@ def main():
         cat_ms[cat] = cat_ms.get(cat, 0.0) + t
         if cat == "gemm":
             _, M, N, K = work
-            tile = _lib.gemm_tile(M, N, K)
+            tile = _lib.gemm_tile(M, N, K) + (K % 128 == 0,)   # (bm, bn, direct-to-LDS path)
             g = gemm_by_tile.setdefault(tile, [0.0, 0.0, 0])
             g[0] += t
             g[1] += 2.0 * M * N * K
@@ -318,14 +322,15 @@ def main():
     dom_tile = max(gemm_by_tile, key=lambda k: gemm_by_tile[k][0])
     dt_ms, dflops, dcount = gemm_by_tile[dom_tile]
     achieved = dflops / (dt_ms * 1e-3) / 1e12
-    kname = f"pact::k_gemm_nvfp4<{dom_tile[0] // 64}, {dom_tile[1] // 64}>"
+    kname = f"pact::k_gemm_nvfp4{'_fast' if dom_tile[2] else ''}<{dom_tile[0] // 64}, {dom_tile[1] // 64}>"
 
     traffic = None
     tfile = os.path.join(ROOT, "profiles", "gemm_traffic.json")
     if os.path.exists(tfile):
         try:
             tj = json.load(open(tfile))
-            if tj.get("src_hash") == src_hash("gemm.hip", "nvfp4_device.h") and tj.get("tile") == list(dom_tile):
+            if tj.get("src_hash") == src_hash("gemm.hip", "nvfp4_device.h") and tj.get("kernel") == kname \
+                    and tj.get("tile") == list(dom_tile[:2]):
                 traffic = tj.get("bytes_per_launch")
         except (ValueError, OSError):
             traffic = None
