@@ -20,13 +20,15 @@
 //
 // Tiling.  A workgroup of 4 waves (2 x 2) computes a BM x BN tile, each wave
 // (BM/2) x (BN/2) as WTM x WTN MFMA tiles of 32 x 32.  K advances in stages of
-// 128 (8 NVFP4 blocks): packed codes (64 B per row) and the block scales
-// (converted once to FP16 pairs) are staged in LDS, double buffered, with the
-// next stage's global loads issued before the current stage's MFMAs.  Within a
+// 128 (8 NVFP4 blocks): packed codes (64 B per row) and the block scales are
+// staged in LDS (the generic kernel double buffers through registers, the fast
+// one loads three stages ahead straight into LDS).  Within a
 // stage, lane half h of a wave owns K range [64h, 64h+64) of every row it
 // touches, so each fragment is one 32-byte LDS read of codes plus one 16-byte
 // read of scales; MFMA step s takes K = 64h + 8s + t (t = 0..7) from both
 // operands, a consistent permutation of K.
+#include <type_traits>
+
 #include "pact_internal.h"
 
 namespace pact {
@@ -37,6 +39,9 @@ typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float floatx16 __attribute__((ext_vector_type(16)));
 
 constexpr int KT = 128;            // K elements per stage
+#ifndef PACT_VALU_PER_MFMA
+#define PACT_VALU_PER_MFMA 6
+#endif
 constexpr int CODE_STRIDE = 80;    // LDS bytes per row of codes (64 data + 16 pad: conflict-free b128 reads)
 constexpr int SCALE_STRIDE = 48;   // LDS bytes per row of FP16 scale pairs (32 data + 16 pad)
 
@@ -329,51 +334,66 @@ __global__ __launch_bounds__(256, 1) void k_gemm_nvfp4(GemmArgs p, int tiles_m, 
 }
 
 // ===========================================================================
-// Fast path (K % 128 == 0): global -> LDS direct loads, three LDS stages.
+// Fast path (K % 256 == 0): global -> LDS direct loads, two LDS stages of
+// K = 256.
 //
-// Each K stage holds, for the BM + BN rows of the tile, 64 bytes of codes and
-// 8 bytes of raw E4M3 scales per row.  Loads use global_load_lds (16 bytes
-// per lane for codes, 4 for scales), which write 64 consecutive lane slots of
-// LDS per instruction, so no registers stage the data.  Instead of padding, a
-// row's four 16-byte code chunks are stored XOR-swizzled by (row >> 1) & 3,
-// which makes the fragment reads (8 consecutive rows per 128-byte LDS cycle)
-// bank-conflict free.  Scales are converted per fragment with
-// v_cvt_scalef32_pk_f16_fp8 and applied with a broadcast v_pk_mul_f16.
+// Each stage holds, for the BM + BN rows of the tile, 128 bytes of codes and
+// 16 bytes of raw E4M3 scales per row.  The loads are buffer loads with the
+// LDS-direct modifier (16 bytes per lane; each instruction fills 1 KB of LDS at
+// the wave-uniform address in M0), so no registers stage the data and rows
+// past the end of an operand read as zeros through the buffer range check.  A
+// row's eight 16-byte code chunks are stored XOR-swizzled by (row >> 1) & 7,
+// which spreads the 16 rows of every 256-byte LDS access over all banks.
+// Lane half h of a wave owns K range [128h, 128h + 128) of a stage; K step s
+// (0..15) takes K = 128h + 8s + t (t = 0..7) from both operands.
 // ===========================================================================
+constexpr int KT2 = 256;           // K elements per stage of the fast path
+
 template <int WTM, int WTN>
 struct FastCfg {
   static constexpr int BM = 64 * WTM;
   static constexpr int BN = 64 * WTN;
   static constexpr int ROWS = BM + BN;
-  static constexpr int CODES = 0;                       // [ROWS][64] swizzled
-  static constexpr int SCALES = ROWS * 64;              // [ROWS][8]
-  static constexpr int NC = ROWS / 64;                  // 16-byte code load instructions per wave per stage
-  static constexpr int NS_TOTAL = ROWS / 32;            // 4-byte scale load instructions per stage
-  static constexpr int NS = (NS_TOTAL + 3) / 4;         // per wave (the surplus ones fill a pad region)
-  static constexpr int PAD = SCALES + ROWS * 8;         // 256 bytes per surplus instruction
-  static constexpr int STAGE = PAD + (NS * 4 - NS_TOTAL) * 256;
-  static constexpr int NSTAGE = 3;
-  static constexpr int LOADS = NC + NS;                 // vmcnt per stage per wave
+  static constexpr int CODES = 0;                       // [ROWS][128] swizzled
+  static constexpr int SCALES = ROWS * 128;             // [ROWS][16]
+  static constexpr int NC = ROWS / 32;                  // code load instructions per wave per stage (8 rows each)
+  static constexpr int NS_TOTAL = ROWS / 64;            // scale load instructions per stage (64 rows each)
+  static constexpr int NS = (NS_TOTAL + 3) / 4;         // per wave; surplus ones fill a pad region with zeros
+  static constexpr int PAD = SCALES + ROWS * 16;
+  static constexpr int STAGE = PAD + (NS * 4 - NS_TOTAL) * 1024;
+  static constexpr int LOADS = NC + NS;                 // vector-memory instructions per stage per wave
   // epilogue: per wave, one 32-row slab of its (BN/2)-column tile as FP32
   static constexpr int EPI_LD = BN / 2 + 4;             // floats per staged row (pad breaks bank aliasing)
   static constexpr int EPI_WAVE = 32 * EPI_LD * 4;      // bytes per wave
-  static constexpr int MAIN = NSTAGE * STAGE > 4 * EPI_WAVE ? NSTAGE * STAGE : 4 * EPI_WAVE;
+  static constexpr int MAIN = 2 * STAGE > 4 * EPI_WAVE ? 2 * STAGE : 4 * EPI_WAVE;
   static constexpr int RSC = MAIN;                      // row scales of A (BM floats) then B (BN floats)
   static constexpr int TOTAL = RSC + ROWS * 4;
+  static_assert(ROWS % 64 == 0, "tile rows");
 };
 
-// Global -> LDS loads of 16 / 4 bytes per lane.  Issued through inline asm so
-// that the compiler does not treat every later LDS read as a possible alias of
-// the asynchronous write (it would then wait for all outstanding loads, which
-// serializes the stage pipeline); the kernel waits for them explicitly with
-// s_waitcnt vmcnt before the barrier that publishes a stage.  M0 holds the
-// wave-uniform LDS destination; lane i writes bytes [16 i, 16 i + 16) (or
-// [4 i, 4 i + 4)) after it.
-__device__ __forceinline__ void lds_dma16(const void* gptr, uint32_t lds) {
-  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(gptr), "s"(lds) : "memory", "m0");
+typedef int int4v_t __attribute__((ext_vector_type(4)));
+
+// Buffer resource over [base, base + bytes): raw (stride 0), so an access at
+// offset >= bytes returns zeros instead of touching memory.
+__device__ __forceinline__ int4v_t buffer_rsrc(const void* base, uint32_t bytes) {
+  const uint64_t a = reinterpret_cast<uint64_t>(base);
+  int4v_t r;
+  r[0] = (int)(uint32_t)a;
+  r[1] = (int)((a >> 32) & 0xffffu);
+  r[2] = (int)bytes;
+  r[3] = 0x00020000;
+  return r;
 }
-__device__ __forceinline__ void lds_dma4(const void* gptr, uint32_t lds) {
-  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dword %0, off" ::"v"(gptr), "s"(lds) : "memory", "m0");
+
+// 16 bytes per lane from the buffer at voff + soff into LDS at lds + 16 * lane.
+// Issued through inline asm so that the compiler does not treat every later
+// LDS read as a possible alias of the asynchronous write (it would then wait
+// for all outstanding loads and serialize the stage pipeline); the kernel
+// waits for them explicitly with s_waitcnt vmcnt before the barrier that
+// publishes a stage.
+__device__ __forceinline__ void lds_dma_buf16(int4v_t rsrc, uint32_t voff, uint32_t soff, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %2\n\tbuffer_load_dwordx4 %0, %1, %3 offen lds"
+               ::"v"(voff), "s"(rsrc), "s"(lds), "s"(soff) : "memory", "m0");
 }
 __device__ __forceinline__ uint32_t lds_addr(const void* p) {
   return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
@@ -406,8 +426,8 @@ __global__ __launch_bounds__(256, 1) void k_gemm_nvfp4_fast(GemmArgs p, int tile
   const int64_t m0 = (int64_t)tile_m * BM, n0 = (int64_t)tile_n * BN;
 
   const int64_t M = p.M, N = p.N, K = p.K;
-  const int64_t crow = K >> 1, srow = K >> 4;
-  const int nk = (int)(K / KT);
+  const uint32_t crow = (uint32_t)(K >> 1), srow = (uint32_t)(K >> 4);
+  const int nk = (int)(K / KT2);
 
   // row scales of this tile's A rows and B rows, staged once (clamped at the edges)
   float* rsc = reinterpret_cast<float*>(smem + C::RSC);
@@ -476,130 +496,218 @@ __global__ __launch_bounds__(256, 1) void k_gemm_nvfp4_fast(GemmArgs p, int tile
       }
   }
 
-  // ---- per-lane global source addresses for this wave's load instructions ----
-  // code instruction q (q = wave + 4 * c): rows 16q .. 16q+15, lane -> row 16q + lane/4, LDS slot lane%4
-  const uint8_t* csrc[C::NC];
-#pragma unroll
-  for (int c = 0; c < C::NC; ++c) {
-    const int q = wave + 4 * c;
-    const int row = 16 * q + (lane >> 2);
-    const int slot = lane & 3;
-    const int chunk = slot ^ ((row >> 1) & 3);
+  // ---- load addressing ----
+  // Code instruction c of this wave covers tile rows 8 (wave + 4c) .. +7: lane
+  // -> row 8 (wave + 4c) + lane / 8, LDS slot lane % 8, global chunk
+  // slot ^ ((row >> 1) & 7) (independent of c).  Rows below BM are A rows.
+  const int4v_t ra_c = buffer_rsrc(p.a_codes, (uint32_t)(M * crow));
+  const int4v_t rb_c = buffer_rsrc(p.b_codes, (uint32_t)(N * crow));
+  const int4v_t ra_s = buffer_rsrc(p.a_scales, (uint32_t)(M * srow));
+  const int4v_t rb_s = buffer_rsrc(p.b_scales, (uint32_t)(N * srow));
+  const int crow0 = 8 * wave + (lane >> 3);              // tile row of instruction 0
+  const uint32_t cchunk = (uint32_t)(((lane & 7) ^ ((crow0 >> 1) & 7)) << 4);
+  // voffset of code instruction c: the row term must sit in voffset so that
+  // rows past the operand end fail the range check
+  auto code_voff = [&](int c) -> uint32_t {
+    const int row = crow0 + 32 * c;
     if (row < BM) {
-      int64_t m = m0 + row;
-      m = m < M ? m : M - 1;
-      csrc[c] = p.a_codes + m * crow + chunk * 16;
-    } else {
-      int64_t n = n0 + (row - BM);
-      n = n < N ? n : N - 1;
-      csrc[c] = p.b_codes + n * crow + chunk * 16;
+      const int64_t m = m0 + row;
+      return m < M ? (uint32_t)m * crow + cchunk : 0xfffffff0u;
     }
-  }
-  // scale instruction q: rows 32q .. 32q+31, lane -> row 32q + lane/2, dword lane%2
-  const uint8_t* ssrc[C::NS];
+    const int64_t n = n0 + (row - BM);
+    return n < N ? (uint32_t)n * crow + cchunk : 0xfffffff0u;
+  };
+  uint32_t cvo[C::NC];
+#pragma unroll
+  for (int c = 0; c < C::NC; ++c) cvo[c] = code_voff(c);
+  // scale instruction c of this wave: tile rows 64 (wave + 4c) + lane
+  uint32_t svo[C::NS];
 #pragma unroll
   for (int c = 0; c < C::NS; ++c) {
     const int q = wave + 4 * c;
-    int row = 32 * q + (lane >> 1);
-    if (q >= C::NS_TOTAL) row = 0;                    // surplus instruction: any valid address
-    if (row < BM) {
-      int64_t m = m0 + row;
-      m = m < M ? m : M - 1;
-      ssrc[c] = p.a_scales + m * srow + (lane & 1) * 4;
-    } else {
-      int64_t n = n0 + (row - BM);
-      n = n < N ? n : N - 1;
-      ssrc[c] = p.b_scales + n * srow + (lane & 1) * 4;
+    const int row = 64 * q + lane;
+    uint32_t v = 0xfffffff0u;                              // surplus instruction: zeros into the pad
+    if (q < C::NS_TOTAL) {
+      if (row < BM) {
+        const int64_t m = m0 + row;
+        if (m < M) v = (uint32_t)m * srow;
+      } else {
+        const int64_t n = n0 + (row - BM);
+        if (n < N) v = (uint32_t)n * srow;
+      }
     }
+    svo[c] = v;
   }
   const int wave_s = __builtin_amdgcn_readfirstlane(wave);
   const uint32_t lds0 = lds_addr(smem);
-  auto issue_stage = [&](int kt, int buf) {
+  // load instruction q (< LOADS) of stage kt into LDS buffer buf
+  auto issue_one = [&](int kt, int buf, int q) {
     const uint32_t st = lds0 + (uint32_t)(buf * C::STAGE);
-#pragma unroll
-    for (int c = 0; c < C::NC; ++c) {
-      const int q = wave_s + 4 * c;
-      lds_dma16(csrc[c] + (int64_t)kt * 64, st + C::CODES + q * 1024);
-    }
-#pragma unroll
-    for (int c = 0; c < C::NS; ++c) {
-      const int q = wave_s + 4 * c;
-      const uint32_t dst = q < C::NS_TOTAL ? st + C::SCALES + q * 256 : st + C::PAD + (q - C::NS_TOTAL) * 256;
-      lds_dma4(ssrc[c] + (int64_t)kt * 8, dst);
+    if (q < C::NC) {
+      const bool is_a = 8 * (4 * q + 3) + 7 < BM;          // all four waves' rows of instruction q are A rows
+      const bool is_b = 8 * (4 * q) >= BM;
+      static_assert(BM % 32 == 0, "A/B split on an instruction boundary");
+      const uint32_t dst = st + C::CODES + (uint32_t)(wave_s + 4 * q) * 1024u;
+      const uint32_t soff = (uint32_t)kt * 128u;
+      if (is_a) lds_dma_buf16(ra_c, cvo[q], soff, dst);
+      else if (is_b) lds_dma_buf16(rb_c, cvo[q], soff, dst);
+    } else {
+      const int c = q - C::NC;
+      const int qq = wave_s + 4 * c;
+      const uint32_t dst = qq < C::NS_TOTAL ? st + C::SCALES + (uint32_t)qq * 1024u
+                                            : st + C::PAD + (uint32_t)(qq - C::NS_TOTAL) * 1024u;
+      const uint32_t soff = (uint32_t)kt * 16u;
+      // scale instruction c covers rows 64 (wave + 4c) ..: A rows iff 64 (4c + 3) + 63 < BM, B rows iff 256 c >= BM
+      if (64 * (4 * c + 3) + 63 < BM) lds_dma_buf16(ra_s, svo[c], soff, dst);
+      else if (256 * c >= BM) lds_dma_buf16(rb_s, svo[c], soff, dst);
+      else if (qq * 64 < BM) lds_dma_buf16(ra_s, svo[c], soff, dst);   // split by wave: uniform branch
+      else lds_dma_buf16(rb_s, svo[c], soff, dst);
     }
   };
+  auto issue_stage = [&](int kt, int buf) {
+#pragma unroll
+    for (int q = 0; q < C::LOADS; ++q) issue_one(kt, buf, q);
+  };
 
-  issue_stage(0, 0);
-  if (nk > 1) issue_stage(1, 1);
-
-  for (int kt = 0; kt < nk; ++kt) {
-    if (kt + 1 < nk) PACT_WAIT_VMCNT(C::LOADS);
-    else PACT_WAIT_VMCNT(0);
-    __syncthreads();
-    if (kt + 2 < nk) issue_stage(kt + 2, (kt + 2) % 3);
-    const uint8_t* st = smem + (kt % 3) * C::STAGE;
-
-    uint4 ca[WTM][2], cb[WTN][2];
-    half2_t sa[WTM][2], sb[WTN][2];
+  // ---- fragment reads from LDS ----
+  uint4 ca[WTM][2], cb[WTN][2];
+  uint2 sra[WTM], srb[WTN], sra_n[WTM], srb_n[WTN];
+  half2_t sa[WTM][2], sb[WTN][2];
+  // codes chunk c (K steps 4c .. 4c + 3) into register slot c & 1
+  auto read_codes = [&](const uint8_t* st, int c) {
 #pragma unroll
     for (int i = 0; i < WTM; ++i) {
       const int row = wm * (BM / 2) + i * 32 + li;
-      const int sw = (row >> 1) & 3;
-      const uint8_t* rp = st + C::CODES + row * 64;
-      ca[i][0] = *reinterpret_cast<const uint4*>(rp + (((2 * h) ^ sw) << 4));
-      ca[i][1] = *reinterpret_cast<const uint4*>(rp + (((2 * h + 1) ^ sw) << 4));
-      const uint32_t sraw = *reinterpret_cast<const uint32_t*>(st + C::SCALES + row * 8 + 4 * h);
-      sa[i][0] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(sraw, 1.0f, false);
-      sa[i][1] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(sraw, 1.0f, true);
+      ca[i][c & 1] = *reinterpret_cast<const uint4*>(st + C::CODES + row * 128 + (((4 * h + c) ^ ((row >> 1) & 7)) << 4));
     }
 #pragma unroll
     for (int j = 0; j < WTN; ++j) {
       const int row = BM + wn * (BN / 2) + j * 32 + li;
-      const int sw = (row >> 1) & 3;
-      const uint8_t* rp = st + C::CODES + row * 64;
-      cb[j][0] = *reinterpret_cast<const uint4*>(rp + (((2 * h) ^ sw) << 4));
-      cb[j][1] = *reinterpret_cast<const uint4*>(rp + (((2 * h + 1) ^ sw) << 4));
-      const uint32_t sraw = *reinterpret_cast<const uint32_t*>(st + C::SCALES + row * 8 + 4 * h);
-      sb[j][0] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(sraw, 1.0f, false);
-      sb[j][1] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(sraw, 1.0f, true);
+      cb[j][c & 1] = *reinterpret_cast<const uint4*>(st + C::CODES + row * 128 + (((4 * h + c) ^ ((row >> 1) & 7)) << 4));
     }
-    // software pipeline over the 8 K16 steps: dequantize step s+1 while the
-    // MFMAs of step s run, interleaved 1 MFMA : 4 VALU
-    half8_t af[2][WTM], bf[2][WTN];
-    auto deq_step = [&](int s, half8_t* a_out, half8_t* b_out) {
+  };
+  auto read_scales = [&](const uint8_t* st, uint2* a_out, uint2* b_out) {
 #pragma unroll
-      for (int i = 0; i < WTM; ++i) {
-        const uint4& c = ca[i][s >> 2];
-        const uint32_t w = (s & 3) == 0 ? c.x : (s & 3) == 1 ? c.y : (s & 3) == 2 ? c.z : c.w;
-        const half2_t sp = (s >> 1) & 1 ? sa[i][s >> 2].yy : sa[i][s >> 2].xx;
-        a_out[i] = dequant8h(w, sp);
-      }
+    for (int i = 0; i < WTM; ++i)
+      a_out[i] = *reinterpret_cast<const uint2*>(st + C::SCALES + (wm * (BM / 2) + i * 32 + li) * 16 + 8 * h);
 #pragma unroll
-      for (int j = 0; j < WTN; ++j) {
-        const uint4& c = cb[j][s >> 2];
-        const uint32_t w = (s & 3) == 0 ? c.x : (s & 3) == 1 ? c.y : (s & 3) == 2 ? c.z : c.w;
-        const half2_t sp = (s >> 1) & 1 ? sb[j][s >> 2].yy : sb[j][s >> 2].xx;
-        b_out[j] = dequant8h(w, sp);
-      }
-    };
-    deq_step(0, af[0], bf[0]);
+    for (int j = 0; j < WTN; ++j)
+      b_out[j] = *reinterpret_cast<const uint2*>(st + C::SCALES + (BM + wn * (BN / 2) + j * 32 + li) * 16 + 8 * h);
+  };
+  // FP16 scale pair for chunk c (blocks 8h + 2c, 8h + 2c + 1) into slot c & 1
+  auto pair = [](uint32_t w, bool hi) {
+    return hi ? __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w, 1.0f, true)
+              : __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w, 1.0f, false);
+  };
+  auto cvt_chunk_scales = [&](int c) {
 #pragma unroll
-    for (int s = 0; s < 8; ++s) {
-      __builtin_amdgcn_sched_barrier(0);
-      if (s < 7) deq_step(s + 1, af[(s + 1) & 1], bf[(s + 1) & 1]);
+    for (int i = 0; i < WTM; ++i) sa[i][c & 1] = pair((c >> 1) ? sra[i].y : sra[i].x, (c & 1) != 0);
 #pragma unroll
-      for (int i = 0; i < WTM; ++i)
+    for (int j = 0; j < WTN; ++j) sb[j][c & 1] = pair((c >> 1) ? srb[j].y : srb[j].x, (c & 1) != 0);
+  };
+  // K step s of a stage: dequantize the A and B fragments (codes word s % 4 of
+  // chunk s / 4, block scale 8h + s / 2)
+  half8_t af[2][WTM], bf[2][WTN];
+  auto deq_step = [&](int s, half8_t* a_out, half8_t* b_out) {
+    const int c = s >> 2;
 #pragma unroll
-        for (int j = 0; j < WTN; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(af[s & 1][i], bf[s & 1][j], acc[i][j], 0, 0, 0);
-#pragma unroll
-      for (int k = 0; k < WTM * WTN; ++k) {
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // one MFMA
-        __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);   // four VALU
-      }
-      __builtin_amdgcn_sched_barrier(0);
+    for (int i = 0; i < WTM; ++i) {
+      const uint4& q = ca[i][c & 1];
+      const uint32_t w = (s & 3) == 0 ? q.x : (s & 3) == 1 ? q.y : (s & 3) == 2 ? q.z : q.w;
+      a_out[i] = dequant8h(w, (s >> 1) & 1 ? sa[i][c & 1].yy : sa[i][c & 1].xx);
     }
+#pragma unroll
+    for (int j = 0; j < WTN; ++j) {
+      const uint4& q = cb[j][c & 1];
+      const uint32_t w = (s & 3) == 0 ? q.x : (s & 3) == 1 ? q.y : (s & 3) == 2 ? q.z : q.w;
+      b_out[j] = dequant8h(w, (s >> 1) & 1 ? sb[j][c & 1].yy : sb[j][c & 1].xx);
+    }
+  };
+  // MFMAs of K step s.  With dma set, the loads of stage dma_kt into buffer
+  // dma_buf are spread over the MFMAs of steps 12-14 (one instruction every
+  // DMA_SP MFMAs), so the wave's vector-memory issue overlaps the matrix core.
+  constexpr int DMA_SP = (3 * WTM * WTN) / C::LOADS;
+  static_assert(DMA_SP >= 1, "DMA spacing");
+  auto mfma_step = [&](int s, int dma_kt, int dma_buf, bool dma) {
+#pragma unroll
+    for (int k = 0; k < WTM * WTN; ++k) {
+      const int i = k / WTN, j = k % WTN;
+      acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(af[s & 1][i], bf[s & 1][j], acc[i][j], 0, 0, 0);
+      const int g = (s - 12) * WTM * WTN + k;
+      if (dma && s >= 12 && g % DMA_SP == 0 && g / DMA_SP < C::LOADS) issue_one(dma_kt, dma_buf, g / DMA_SP);
+    }
+  };
+  // one MFMA : PACT_VALU_PER_MFMA VALU, front-loading the dequantization of
+  // the next step under the first MFMAs of this one
+  auto interleave = [&]() {
+#pragma unroll
+    for (int k = 0; k < WTM * WTN; ++k) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x002, PACT_VALU_PER_MFMA, 0);
+    }
+  };
+
+  // Stage kt lives in LDS buffer kt % 2.  Its loads are issued during steps
+  // 12-14 of stage kt - 2 (stages 0 and 1 in the prologue) and published by the
+  // barrier at step 12 of stage kt - 1.  Each wave reads codes one chunk ahead:
+  // chunk c + 1 during chunk c, and chunk 0 plus the scales of stage kt + 1
+  // during chunk 3 of stage kt.  By the barrier at step 12 of stage kt every
+  // wave has consumed all of stage kt's LDS data (chunk 3 is dequantized at
+  // step 11), so the loads of stage kt + 2 go into its buffer right after it.
+  auto run_stage = [&](int kt, auto dma_tag) {
+    constexpr bool DMA = decltype(dma_tag)::value;
+    const uint8_t* st = smem + (kt & 1) * C::STAGE;
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      __builtin_amdgcn_sched_barrier(0);
+      if (c < 3) {
+        read_codes(st, c + 1);
+      } else {
+        // publish stage kt + 1 (the only loads in flight); after the last
+        // stage the reads below fetch a stale in-bounds buffer, never used
+        PACT_WAIT_VMCNT(0);
+        __syncthreads();
+        const uint8_t* stn = smem + ((kt + 1) & 1) * C::STAGE;
+        read_codes(stn, 0);
+        read_scales(stn, sra_n, srb_n);
+      }
+#pragma unroll
+      for (int s = 4 * c; s < 4 * c + 4; ++s) {
+        __builtin_amdgcn_sched_barrier(0);
+        if (s == 15) {
+#pragma unroll
+          for (int i = 0; i < WTM; ++i) sra[i] = sra_n[i];
+#pragma unroll
+          for (int j = 0; j < WTN; ++j) srb[j] = srb_n[j];
+          cvt_chunk_scales(0);
+          deq_step(0, af[0], bf[0]);
+        } else {
+          if (((s + 1) & 3) == 0) cvt_chunk_scales((s + 1) >> 2);
+          deq_step(s + 1, af[(s + 1) & 1], bf[(s + 1) & 1]);
+        }
+        mfma_step(s, kt + 2, kt & 1, DMA);
+        interleave();
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    }
+  };
+
+  issue_stage(0, 0);
+  if (nk > 1) {
+    issue_stage(1, 1);
+    PACT_WAIT_VMCNT(C::LOADS);
+  } else {
+    PACT_WAIT_VMCNT(0);
   }
+  __syncthreads();
+  read_codes(smem, 0);
+  read_scales(smem, sra, srb);
+  cvt_chunk_scales(0);
+  deq_step(0, af[0], bf[0]);
+  int kt = 0;
+  for (; kt + 2 < nk; ++kt) run_stage(kt, std::true_type{});
+  for (; kt < nk; ++kt) run_stage(kt, std::false_type{});
+  PACT_WAIT_VMCNT(0);
 
   // ---- epilogue: row scales, optional accumulate, BF16 rounding ----
   // Each wave stages one 32-row slab of its tile at a time in LDS as FP32
@@ -668,7 +776,9 @@ hipError_t launch_gemm(const GemmArgs& a, hipStream_t s) {
   int bm, bn;
   gemm_tile(a.M, a.N, &bm, &bn);
   const int tm = (int)((a.M + bm - 1) / bm), tn = (int)((a.N + bn - 1) / bn);
-  const bool fast = (a.K % KT) == 0;
+  // fast path: K a multiple of the stage length and every operand addressable
+  // with 32-bit buffer offsets
+  const bool fast = (a.K % KT2) == 0 && (uint64_t)(a.M > a.N ? a.M : a.N) * (uint64_t)(a.K / 2) < (1ull << 31);
   if (fast) {
     if (bm == 256 && bn == 256) k_gemm_nvfp4_fast<4, 4><<<tm * tn, 256, 0, s>>>(a, tm, tn);
     else if (bn == 192) k_gemm_nvfp4_fast<4, 3><<<tm * tn, 256, 0, s>>>(a, tm, tn);

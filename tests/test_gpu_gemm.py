@@ -74,7 +74,7 @@ def test_exact_special_case_bit_identical(fw, M, N, K):
 
 
 @pytest.mark.parametrize("M,N,K", [(1, 16, 16), (7, 33, 48), (130, 257, 272), (300, 100, 1040),
-                                   (513, 640, 4096), (64, 2048, 128)])
+                                   (513, 640, 4096), (64, 2048, 128), (2, 300, 768), (1000, 130, 1280)])
 def test_ragged_shapes(fw, M, N, K):
     a = synth.activations_bf16((M, K), 92, M + 3 * N + 7 * K)
     b = synth.normal_bf16((N, K), 0.02, 92, M + 3 * N + 7 * K + 1)
@@ -102,8 +102,10 @@ def test_lora_epilogue_fwd(fw):
     assert_within(torch_bf16_to_f64(y), yref + term, tol.gemm_bound(yref + term, yabs + tabs), "fwd+lora")
 
 
-def test_dgrad_accumulate_and_lora(fw):
-    M, N, K, r = 80, 192, 272, 16
+@pytest.mark.parametrize("M,N,K,r", [(80, 192, 272, 16), (200, 512, 320, 16), (64, 768, 1100, 5)])
+def test_dgrad_accumulate_and_lora(fw, M, N, K, r):
+    """N is the contraction length of the input gradient: 192 and 1100 take the
+    generic kernel, 512 and 768 the direct-to-LDS one (ragged output tiles)."""
     dy = synth.normal_bf16((M, N), 0.01, 94, 1)
     w = synth.normal_bf16((N, K), 0.02, 94, 2)
     dt = synth.normal_bf16((M, r), 0.01, 94, 3)
