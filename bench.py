@@ -1,8 +1,11 @@
 #!/usr/bin/env python3
 """Benchmark of the NVFP4 frozen-projection hot path on one MI355X.
 
-One step is one pass of the whole path over a Llama-3B-shaped decoder layer's
-frozen projections at M = 4096 tokens (batch 4 x seq 1024), LoRA rank 16:
+One step is one pass of the whole path over --layers (default 4) distinct
+Llama-3B-shaped decoder layers' frozen projections at M = 4096 tokens
+(batch 4 x seq 1024), LoRA rank 16 -- distinct weights and buffers per layer,
+about 1 GB each, so operands stream from HBM rather than the 256 MB
+last-level cache.  Per layer:
 
   forward   rmsnorm_quant -> q/k/v (lora_down + NVFP4 GEMM with LoRA term)
             nvfp4_quantize(attention output) -> o
@@ -43,8 +46,11 @@ def parse():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true", help="skip the oracle timing on host cores")
-    ap.add_argument("--cpu-sample-rows", type=int, default=32)
+    ap.add_argument("--cpu-sample-rows", type=int, default=256)
     ap.add_argument("--eager", action="store_true", help="time eager launches instead of a captured HIP graph")
+    ap.add_argument("--layers", type=int, default=4,
+                    help="distinct decoder-layer instances a step runs through (their weights and buffers "
+                         "together exceed the 256 MB last-level cache, so every operand streams from HBM)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a 1 GiB read + 1 GiB write elementwise kernel (counter calibration)")
     return ap.parse_args()
@@ -53,8 +59,9 @@ def parse():
 class Layer:
     """Device state of one synthetic Llama-3B decoder layer's frozen-projection path."""
 
-    def __init__(self, fw, torch, synth, wl):
+    def __init__(self, fw, torch, synth, wl, index=0):
         self.fw, self.torch = fw, torch
+        off = 1000 * index                     # distinct seeded tensors per layer instance
         M = wl.tokens
         H, I = 3072, 8192
         KV = [p.d_out for p in wl.projections if p.name == "k"][0]
@@ -66,21 +73,22 @@ class Layer:
             import numpy as np
             return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).to(dev)
 
-        act = lambda tid, cols: up(synth.workload_activation(wl, M, cols, tid))
+        act = lambda tid, cols: up(synth.workload_activation(wl, M, cols, off + tid))
         self.h1, self.h2, self.attn = act(10, H), act(11, H), act(12, H)
-        self.g1 = up(synth.uniform_bf16((H,), 0.9, 1.1, wl.wid, 13))
-        self.g2 = up(synth.uniform_bf16((H,), 0.9, 1.1, wl.wid, 14))
-        grad = lambda tid, cols: up(synth.normal_bf16((M, cols), wl.dy_std, wl.wid, tid))
+        self.g1 = up(synth.uniform_bf16((H,), 0.9, 1.1, wl.wid, off + 13))
+        self.g2 = up(synth.uniform_bf16((H,), 0.9, 1.1, wl.wid, off + 14))
+        grad = lambda tid, cols: up(synth.normal_bf16((M, cols), wl.dy_std, wl.wid, off + tid))
         self.dOut, self.dYo = grad(15, H), grad(16, H)
         self.dq, self.dk, self.dv = grad(17, H), grad(18, KV), grad(19, KV)
 
         self.proj = {}
         for i, p in enumerate(wl.projections):
-            w = up(synth.normal_bf16((p.d_out, p.d_in), wl.w_std, wl.wid, 20 + i))
+            w = up(synth.normal_bf16((p.d_out, p.d_in), wl.w_std, wl.wid, off + 20 + i))
             wf, wb = fw.weight_layouts(w)
-            A = up(synth.normal_bf16((r, p.d_in), wl.a_std, wl.wid, 40 + i))
+            del w                                # only the cached NVFP4 layouts stay resident
+            A = up(synth.normal_bf16((r, p.d_in), wl.a_std, wl.wid, off + 40 + i))
             B = torch.zeros((p.d_out, r), dtype=torch.bfloat16, device=dev)
-            self.proj[p.name] = dict(p=p, w=w, wf=wf, wb=wb, A=A, B=B,
+            self.proj[p.name] = dict(p=p, wf=wf, wb=wb, A=A, B=B,
                                      T=torch.empty((M, r), dtype=torch.bfloat16, device=dev),
                                      Y=torch.empty((M, p.d_out), dtype=torch.bfloat16, device=dev),
                                      dT=torch.empty((M, r), dtype=torch.bfloat16, device=dev),
@@ -239,11 +247,17 @@ def main():
 
     wl = synth.WORKLOADS[2]
     torch.cuda.set_device(0)
-    layer = Layer(fw, torch, synth, wl)
+    layers = [Layer(fw, torch, synth, wl, li) for li in range(max(1, args.layers))]
+    layer = layers[0]
     torch.cuda.synchronize()
+    resident = torch.cuda.memory_allocated()
+
+    def step():
+        for ly in layers:
+            ly.step()
 
     for _ in range(args.warmup):
-        layer.step()
+        step()
     torch.cuda.synchronize()
 
     # The step is captured once into a HIP graph (every output buffer and the
@@ -257,12 +271,12 @@ def main():
         side = torch.cuda.Stream()
         side.wait_stream(torch.cuda.current_stream())
         with torch.cuda.stream(side):
-            layer.step()
+            step()
         torch.cuda.current_stream().wait_stream(side)
         torch.cuda.synchronize()
         graph = torch.cuda.CUDAGraph()
         with torch.cuda.graph(graph):
-            layer.step()
+            step()
         torch.cuda.synchronize()
         graph.replay()
         torch.cuda.synchronize()
@@ -270,7 +284,7 @@ def main():
         if not args.eager:
             print(f"graph capture unavailable ({ex}); timing eager steps", file=sys.stderr)
         graph = None
-    run = graph.replay if graph is not None else layer.step
+    run = graph.replay if graph is not None else step
 
     # timed region: K steps, wall clock and events on the launch stream
     ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -287,16 +301,18 @@ def main():
     # instrumented pass over the same K steps: events around every launch give
     # per-kernel durations (events add host and queue overhead between kernels,
     # so this pass is not the one the step time comes from)
-    layer.record = []
+    recs = []
+    for ly in layers:
+        ly.record = recs
     torch.cuda.synchronize()
     for _ in range(args.steps):
-        layer.step()
+        step()
     torch.cuda.synchronize()
-    recs = layer.record
-    layer.record = None
+    for ly in layers:
+        ly.record = None
 
     ms_per_step = wall * 1e3 / args.steps
-    flops = layer.gemm_flops()
+    flops = sum(ly.gemm_flops() for ly in layers)
     value = flops / (ms_per_step * 1e-3) / 1e12
 
     # per-kernel times from the events
@@ -351,7 +367,9 @@ def main():
         "vs_baseline": None,
         "dtype": "nvfp4 operands, fp16 MFMA (exact products), fp32 accumulation, bf16 output",
         "data": "synthetic (seeded BF16 activations with 1% outlier channels, N(0,0.02) weights, N(0,0.01) grads)",
-        "config": {"workload": "llama3b-decoder-layer frozen projections fwd+dgrad + fused quantizers + LoRA r16",
+        "config": {"workload": f"llama3b decoder-layer frozen projections fwd+dgrad + fused quantizers + LoRA r16, "
+                               f"{len(layers)} distinct layer instances per step",
+                   "layers": len(layers), "resident_gb": round(resident / 1e9, 2),
                    "tokens": layer.M, "hidden": layer.H, "intermediate": layer.I, "kv": layer.KV,
                    "lora_rank": layer.r, "gemm_gflop_per_step": round(flops / 1e9, 1), "parallelism": "single-gpu"},
         "frac_fp4_peak": round(value / PEAK["fp4_mfma_tflops"], 4),
