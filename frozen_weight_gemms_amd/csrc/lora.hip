@@ -10,224 +10,251 @@
 //               dA = bf16(dT^T X~)
 // (the input-gradient term dT A is added inside the dgrad GEMM's epilogue).
 //
-// All of these are skinny products, Out[P x r] = sum over a long axis R with
-// r <= 128, on v_mfma_f32_16x16x32_bf16 with FP32 accumulation.  lora_bwd is
-// three launches:
-//   * the row kernel reduces along rows (T over K from X_q, dT over N from dY):
-//     a workgroup owns 16 token rows; each of its waves streams 8 consecutive
-//     elements per lane per MFMA step over its share of the long axis, with 8
-//     steps of loads in flight, and the waves reduce through LDS;
-//   * the column kernel contracts over the token axis M (dB from dY and T, dA
-//     from X_q and dT), split over M: a workgroup stages 128-row x 64-column
-//     tiles of the long operand in LDS transposed and writes an FP32 partial
-//     [64 x r]; a third, small launch sums the partials in split order and
-//     writes BF16, so results do not depend on scheduling.
+// All of these are skinny products with r <= 128 on v_mfma_f32_16x16x32_bf16
+// with FP32 accumulation, bound by streaming the long operand (X_q or dY) from
+// HBM.  Two kernel shapes:
+//   * the row kernel reduces along a row of the long operand (T over K from
+//     X_q, dT over N from dY).  A workgroup owns 16 token rows; its 8 waves
+//     take interleaved 128-element chunks of the row, each lane loading 32
+//     consecutive elements of a row per chunk (16 bytes of codes, or four
+//     16-byte BF16 loads) and the matching 32 elements of the rank-major small
+//     operand (A, or B^T transposed once into the workspace);
+//   * the column kernel contracts over the token axis (dB from dY and T, dA
+//     from X_q and dT).  Each lane loads an 8-row x CPL-column block of the
+//     long operand and transposes it in registers, so MFMA instance c takes
+//     columns q0 + CPL i + c (i = lane % 16) with no LDS round trip for the big
+//     operand; T and dT come rank-major from the row kernel.  Each workgroup
+//     writes an FP32 partial for its column strip and token split; a small
+//     reduce launch sums the partials in split order, so results do not depend
+//     on scheduling.
 #include "pact_internal.h"
 
 namespace pact {
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float floatx4 __attribute__((ext_vector_type(4)));
+typedef float float2_t __attribute__((ext_vector_type(2)));
 
-
-__device__ __forceinline__ __bf16 bfbits(uint16_t v) { return __builtin_bit_cast(__bf16, v); }
 __device__ __forceinline__ uint32_t bf16_exact(float f) { return __float_as_uint(f) >> 16; }
+__device__ __forceinline__ uint32_t pack2(float a, float b) { return bf16_exact(a) | (bf16_exact(b) << 16); }
 
-// 8 dequantized NVFP4 elements times m (= s or s * r), packed as BF16 (exact).
-__device__ __forceinline__ uint4 deq8_bf16_packed(uint32_t w, float m) {
-  float f[8];
-  decode8_f32(w, m, f);
-  uint4 v;
-  v.x = bf16_exact(f[0]) | (bf16_exact(f[1]) << 16);
-  v.y = bf16_exact(f[2]) | (bf16_exact(f[3]) << 16);
-  v.z = bf16_exact(f[4]) | (bf16_exact(f[5]) << 16);
-  v.w = bf16_exact(f[6]) | (bf16_exact(f[7]) << 16);
-  return v;
+// 8 NVFP4 elements of one code word times m (= s or s * r), packed as BF16:
+// exact, because e * s has at most 6 significant bits and r is a power of two.
+__device__ __forceinline__ uint4 deq8_bf16(uint32_t w, float m) {
+  const float2_t a = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 0);
+  const float2_t b = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 1);
+  const float2_t c = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 2);
+  const float2_t d = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 3);
+  return make_uint4(pack2(a.x * m, a.y * m), pack2(b.x * m, b.y * m), pack2(c.x * m, c.y * m),
+                    pack2(d.x * m, d.y * m));
 }
 
+__device__ __forceinline__ float e4m3_f32(uint32_t byte) { return __builtin_amdgcn_cvt_f32_fp8((int)byte, 0); }
+
 // ---------------------------------------------------------------------------
-// Row kernel.
-//   part 0 (waves [0, NW/2) or all waves when DO_DT is false):
-//       T[p][j]  = bf16(xr[p] * sum_k (e*s)[p][k] * A[j][k])      (X_q [P x K], A [r x K])
-//   part 1 (waves [NW/2, NW), when DO_DT):
-//       dT[p][j] = bf16(scale * sum_n dY[p][n] * B[n][j])          (dY [P x N], B [N x r])
+// Row kernel.  Block (tile, part) with 16 token rows p0 .. p0 + 15:
+//   part 0:  T[p][j]  = bf16(xr[p] * sum_k (e*s)[p][k] * A[j][k])     X_q [P x K], A [r x K]
+//   part 1:  dT[p][j] = bf16(scale * sum_n dY[p][n] * Bt[j][n])        dY [P x N], Bt = B^T [r x N]
+// Chunk c of the long axis is elements [128c, 128c + 128); waves take chunks
+// wave, wave + 8, ...  The chunk of the long operand (16 rows) is loaded with
+// row-contiguous 16-byte loads (four rows of 256 bytes per BF16 instruction,
+// sixteen rows of 64 bytes of codes per NVFP4 instruction) into a wave-private
+// LDS tile and read back in the MFMA layout: sub-step u (0..3) gives lane
+// (i, g) row i, elements 128c + 32u + 8g + (0..7).  The rank-major small
+// operand is read directly in that layout (it is small and cache-resident).
+// The global loads of CH chunks are issued before any of them is used.
 // ---------------------------------------------------------------------------
 template <int NT>
-struct RowUnroll {
-  static constexpr int value = NT <= 2 ? 8 : (NT <= 4 ? 4 : 2);   // steps of loads in flight
+struct RowCfg {
+  static constexpr int CH = NT <= 1 ? 4 : (NT <= 2 ? 2 : 1);
 };
+constexpr int RL_STRIDE = 272;              // BF16 tile row stride in LDS (256 B + 16: conflict-free b128 reads)
+constexpr int RQ_STRIDE = 80;               // NVFP4 code tile row stride (64 B + 16: conflict-free b32 reads)
+constexpr int RQ_SCALES = 16 * RQ_STRIDE;   // then 16 rows x 8 scale bytes
+constexpr int RSTAGE = 16 * RL_STRIDE;      // bytes of one wave's staging tile
 
-template <int NT, int NWP>
-__device__ __forceinline__ void rowred_part(bool nvfp4, const uint8_t* __restrict__ xc, const uint8_t* __restrict__ xs,
-                                            const uint16_t* __restrict__ lb, int64_t p, int64_t R,
-                                            const uint16_t* __restrict__ w, int64_t wsR, int64_t wsJ, int64_t r,
-                                            int wpart, int i, int g, floatx4* acc) {
-  int64_t jrow[NT];
-  bool jok[NT];
+template <int NT, bool NVFP4>
+__device__ __forceinline__ void row_reduce(const uint8_t* __restrict__ xc, const uint8_t* __restrict__ xs,
+                                           const uint16_t* __restrict__ lb, int64_t p0, int64_t P, int64_t R,
+                                           const uint16_t* __restrict__ S, int64_t r, int wave, int lane,
+                                           uint8_t* stage, floatx4* acc) {
+  constexpr int CH = RowCfg<NT>::CH;
+  const int i = lane & 15, g = lane >> 4;
+  const int64_t nchunk = (R + 127) / 128;
+  for (int64_t cb = wave; cb < nchunk; cb += 8 * CH) {
+    uint4 lv[CH][4];          // BF16: instruction v holds rows 4v + lane/16, elements 8 (lane % 16) + (0..7)
+    uint32_t lsc[CH][2];      // NVFP4: scale bytes of row lane/4, blocks 2 (lane % 4) and + 1
+    uint4 sv[CH][NT][4];
 #pragma unroll
-  for (int t = 0; t < NT; ++t) {
-    const int64_t j = t * 16 + i;
-    jok[t] = j < r;
-    jrow[t] = jok[t] ? j : 0;
-  }
-  const int64_t nsteps = (R + 31) / 32;
-  const int64_t per = (nsteps + NWP - 1) / NWP;
-  const int64_t st0 = wpart * per, st1 = st0 + per < nsteps ? st0 + per : nsteps;
-  constexpr int RR_UNROLL = RowUnroll<NT>::value;
-  for (int64_t sb = st0; sb < st1; sb += RR_UNROLL) {
-    uint4 lv[RR_UNROLL];
-    float ls[RR_UNROLL];
-    bf16x8_t bv[RR_UNROLL][NT];
-#pragma unroll
-    for (int u = 0; u < RR_UNROLL; ++u) {
-      const int64_t k = (sb + u) * 32 + 8 * g;
-      const bool kin = (sb + u) < st1 && k < R;
-      if (nvfp4) {
-        lv[u].x = kin ? *reinterpret_cast<const uint32_t*>(xc + p * (R >> 1) + (k >> 1)) : 0u;
-        ls[u] = kin ? __builtin_amdgcn_cvt_f32_fp8((int)xs[p * (R >> 4) + (k >> 4)], 0) : 0.0f;
+    for (int q = 0; q < CH; ++q) {
+      const int64_t c = cb + 8 * q;
+      const bool cin = c < nchunk;
+      if constexpr (NVFP4) {
+        // lane -> row lane / 4, bytes 16 (lane % 4) .. + 16 of the chunk's 64 code bytes
+        const int64_t row = p0 + (lane >> 2);
+        const int64_t k0 = c * 128 + 32 * (lane & 3);
+        const bool rin = cin && row < P;
+        const bool full = rin && k0 + 32 <= R, half = rin && k0 + 16 <= R;
+        const uint8_t* cp = xc + row * (R >> 1) + (k0 >> 1);
+        const uint2 w01 = half ? *reinterpret_cast<const uint2*>(cp) : make_uint2(0, 0);
+        const uint2 w23 = full ? *reinterpret_cast<const uint2*>(cp + 8) : make_uint2(0, 0);
+        lv[q][0] = make_uint4(w01.x, w01.y, w23.x, w23.y);
+        const uint8_t* sp = xs + row * (R >> 4) + (k0 >> 4);
+        lsc[q][0] = half ? (uint32_t)sp[0] : 0u;
+        lsc[q][1] = full ? (uint32_t)sp[1] : 0u;
       } else {
-        lv[u] = kin ? *reinterpret_cast<const uint4*>(lb + p * R + k) : make_uint4(0, 0, 0, 0);
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+          const int64_t row = p0 + 4 * v + (lane >> 4);
+          const int64_t k = c * 128 + 8 * (lane & 15);
+          const bool ok = cin && row < P && k + 8 <= R;
+          lv[q][v] = ok ? *reinterpret_cast<const uint4*>(lb + row * R + k) : make_uint4(0, 0, 0, 0);
+        }
       }
 #pragma unroll
       for (int t = 0; t < NT; ++t) {
-        if (wsR == 1) {   // small operand K-contiguous (A [r x K])
-          const uint4 v = (kin && jok[t]) ? *reinterpret_cast<const uint4*>(w + jrow[t] * wsJ + k)
-                                          : make_uint4(0, 0, 0, 0);
-          bv[u][t] = __builtin_bit_cast(bf16x8_t, v);
-        } else {          // small operand rank-contiguous (B [N x r]): 8 rows of one column
+        const int64_t j = 16 * t + i;
 #pragma unroll
-          for (int e = 0; e < 8; ++e)
-            bv[u][t][e] = bfbits((kin && jok[t]) ? w[(k + e) * wsR + jrow[t]] : (uint16_t)0);
+        for (int u = 0; u < 4; ++u) {
+          const int64_t k = c * 128 + 32 * u + 8 * g;
+          const bool ok = cin && j < r && k + 8 <= R;
+          sv[q][t][u] = ok ? *reinterpret_cast<const uint4*>(S + j * R + k) : make_uint4(0, 0, 0, 0);
         }
       }
     }
 #pragma unroll
-    for (int u = 0; u < RR_UNROLL; ++u) {
-      const uint4 av = nvfp4 ? deq8_bf16_packed(lv[u].x, ls[u]) : lv[u];
-      const bf16x8_t af = __builtin_bit_cast(bf16x8_t, av);
+    for (int q = 0; q < CH; ++q) {
+      // stage the chunk in this wave's LDS tile, then read it back in the MFMA layout
+      if constexpr (NVFP4) {
+        *reinterpret_cast<uint4*>(stage + (lane >> 2) * RQ_STRIDE + 16 * (lane & 3)) = lv[q][0];
+        stage[RQ_SCALES + (lane >> 2) * 8 + 2 * (lane & 3)] = (uint8_t)lsc[q][0];
+        stage[RQ_SCALES + (lane >> 2) * 8 + 2 * (lane & 3) + 1] = (uint8_t)lsc[q][1];
+      } else {
 #pragma unroll
-      for (int t = 0; t < NT; ++t)
-        acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af, bv[u][t], acc[t], 0, 0, 0);
+        for (int v = 0; v < 4; ++v)
+          *reinterpret_cast<uint4*>(stage + (4 * v + (lane >> 4)) * RL_STRIDE + 16 * (lane & 15)) = lv[q][v];
+      }
+      __builtin_amdgcn_s_waitcnt(0xc07f);             // lgkmcnt(0): this wave's tile is written
+      __builtin_amdgcn_wave_barrier();
+      uint4 av[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        if constexpr (NVFP4) {
+          const uint32_t w = *reinterpret_cast<const uint32_t*>(stage + i * RQ_STRIDE + 16 * u + 4 * g);
+          const uint32_t sb = stage[RQ_SCALES + i * 8 + 2 * u + (g >> 1)];
+          av[u] = deq8_bf16(w, e4m3_f32(sb));
+        } else {
+          av[u] = *reinterpret_cast<const uint4*>(stage + i * RL_STRIDE + 64 * u + 16 * g);
+        }
+      }
+      __builtin_amdgcn_s_waitcnt(0xc07f);             // reads done before the next chunk overwrites the tile
+      __builtin_amdgcn_wave_barrier();
+#pragma unroll
+      for (int u = 0; u < 4; ++u)
+#pragma unroll
+        for (int t = 0; t < NT; ++t)
+          acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, av[u]),
+                                                           __builtin_bit_cast(bf16x8_t, sv[q][t][u]), acc[t], 0, 0, 0);
     }
   }
 }
 
-template <int NT, bool DO_DT>
+// Part 0 writes T (row-major, if T != NULL) and Tt (rank-major with leading
+// dimension ldt, if Tt != NULL); part 1 writes dT and dTt.  The rank-major
+// copies get zeros in their padding columns [P, ldt), which the column kernel
+// reads.
+template <int NT>
 __global__ __launch_bounds__(512) void k_lora_rows(const uint8_t* __restrict__ xc, const uint8_t* __restrict__ xs,
                                                    const float* __restrict__ xr, int64_t P, int64_t K,
                                                    const uint16_t* __restrict__ A, int64_t r,
-                                                   uint16_t* __restrict__ T, const uint16_t* __restrict__ dy,
-                                                   int64_t N, const uint16_t* __restrict__ B, float scale,
-                                                   uint16_t* __restrict__ dT) {
+                                                   uint16_t* __restrict__ T, uint16_t* __restrict__ Tt, int64_t ldt,
+                                                   const uint16_t* __restrict__ dy, int64_t N,
+                                                   const uint16_t* __restrict__ Bt, float scale,
+                                                   uint16_t* __restrict__ dT, uint16_t* __restrict__ dTt) {
   constexpr int NW = 8;
   constexpr int RT = 16 * NT;
   __shared__ float red[NW][16][RT + 1];
+  __shared__ __attribute__((aligned(16))) uint8_t stage[NW][RSTAGE];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int i = lane & 15, g = lane >> 4;
+  const int part = (int)blockIdx.y;
   const int64_t p0 = (int64_t)blockIdx.x * 16;
-  int64_t p = p0 + i;
-  p = p < P ? p : P - 1;
 
   floatx4 acc[NT];
 #pragma unroll
   for (int t = 0; t < NT; ++t) acc[t] = floatx4{0, 0, 0, 0};
-  constexpr int NWP = DO_DT ? NW / 2 : NW;          // waves per part
-  const int part = DO_DT ? wave / NWP : 0;
-  const int wpart = wave - part * NWP;
-  if (part == 0)
-    rowred_part<NT, NWP>(true, xc, xs, nullptr, p, K, A, 1, K, r, wpart, i, g, acc);
-  else
-    rowred_part<NT, NWP>(false, nullptr, nullptr, dy, p, N, B, r, 1, r, wpart, i, g, acc);
-  // accumulator layout: (row, col) at lane col + 16 * (row / 4), reg row % 4
+  if (part == 0) row_reduce<NT, true>(xc, xs, nullptr, p0, P, K, A, r, wave, lane, stage[wave], acc);
+  else row_reduce<NT, false>(nullptr, nullptr, dy, p0, P, N, Bt, r, wave, lane, stage[wave], acc);
+
+  // accumulator layout (16x16): (row, col) at lane col + 16 * (row / 4), register row % 4
 #pragma unroll
   for (int t = 0; t < NT; ++t)
 #pragma unroll
     for (int e = 0; e < 4; ++e) red[wave][4 * g + e][t * 16 + i] = acc[t][e];
   __syncthreads();
-  for (int q = threadIdx.x; q < (DO_DT ? 2 : 1) * 16 * RT; q += 512) {
-    const int prt = q / (16 * RT);
-    const int row = (q / RT) % 16, col = q % RT;
+  uint16_t* out = part == 0 ? T : dT;
+  uint16_t* outt = part == 0 ? Tt : dTt;
+  for (int q = threadIdx.x; q < 16 * RT; q += 512) {
+    const int row = q / RT, col = q % RT;
     const int64_t pp = p0 + row;
     if (pp < P && col < r) {
       float sum = 0.0f;
 #pragma unroll
-      for (int w = 0; w < NWP; ++w) sum += red[prt * NWP + w][row][col];
-      if (prt == 0) T[pp * r + col] = (uint16_t)f32_to_bf16_rne(sum * xr[pp]);
-      else dT[pp * r + col] = (uint16_t)f32_to_bf16_rne(sum * scale);
+      for (int w = 0; w < NW; ++w) sum += red[w][row][col];
+      const uint16_t v = (uint16_t)f32_to_bf16_rne(part == 0 ? sum * xr[pp] : sum * scale);
+      if (out != nullptr) out[pp * r + col] = v;
+      if (outt != nullptr) outt[col * ldt + pp] = v;
     }
+  }
+  if (outt != nullptr && p0 + 16 >= P && ldt > P) {
+    // last row tile: zero the padding columns [P, ldt) of the rank-major copy
+    const int64_t pad = ldt - P;
+    for (int64_t q = threadIdx.x; q < r * pad; q += 512) outt[(q / pad) * ldt + P + q % pad] = 0;
+  }
+}
+
+// B [N x r] -> Bt [r x N]
+__global__ __launch_bounds__(256) void k_transpose_rank(const uint16_t* __restrict__ B, int64_t N, int64_t r,
+                                                        uint16_t* __restrict__ Bt) {
+  for (int64_t q = (int64_t)blockIdx.x * 256 + threadIdx.x; q < N * r; q += (int64_t)gridDim.x * 256) {
+    const int64_t n = q / r, j = q - n * r;
+    Bt[j * N + n] = B[q];
   }
 }
 
 // ---------------------------------------------------------------------------
-// Column kernel: for column strip c (64 columns) and M-split s,
-//   part[s][p][j] = sum_{m in split s} Z[m][p] * W[m][j]
-// with (Z, W, output) = (dY [M x N], T, dB [N x r] scaled by `scale`) for the
-// first nstrip_b strips, and (X~ [M x K], dT, dA [r x K]) for the rest.
+// Column kernel: for column strip x (16 CPL columns of the long operand) and
+// token split y,
+//   part[y][q][j] = sum_{m in split y} Z[m][q] * Wt[j][m]
+// with (Z, Wt) = (dY [M x N], T^T) for the first nstrip_b strips (dB; the
+// reduce applies `scale`) and (X~ [M x K], dT^T) for the rest (dA).  A wave
+// step covers 32 token rows: lane (i, g) loads rows m0 + 8g + (0..7) at
+// columns q0 + CPL i + (0..CPL-1) and transposes the block in registers; MFMA
+// instance c (row i <-> column q0 + CPL i + c) contracts the 32 rows against
+// Wt.  The 4 waves of a workgroup take interleaved steps of the split and are
+// summed through LDS in wave order.
 // ---------------------------------------------------------------------------
-constexpr int CR_ROWS = 128;           // rows of Z staged per iteration
-constexpr int CR_PAD = CR_ROWS + 8;    // LDS row stride (elements) of the transposed tiles
-
 template <int NT>
-__device__ __forceinline__ void colred_strip(bool nvfp4, const uint8_t* __restrict__ xc,
-                                             const uint8_t* __restrict__ xs, const float* __restrict__ xr,
-                                             const uint16_t* __restrict__ zb, int64_t P, int64_t Rb, int64_t Re,
-                                             int64_t p0, const uint16_t* __restrict__ w, int64_t r, uint16_t (*zt)[CR_PAD],
-                                             uint16_t (*wtl)[CR_PAD], floatx4* acc) {
-  constexpr int RT = 16 * NT;
-  const int tid = threadIdx.x;
-  const int lane = tid & 63, wave = tid >> 6;
-  const int i = lane & 15, g = lane >> 4;
-  for (int64_t R0 = Rb; R0 < Re; R0 += CR_ROWS) {
-    uint4 zv[4];
+struct ColCfg {
+  static constexpr int CPL = NT <= 2 ? 8 : (NT <= 4 ? 4 : 2);   // columns per lane
+};
+
+// v_perm_b32 byte selects: (lo16(a), lo16(b)) and (hi16(a), hi16(b)) packed as lo | hi << 16
+__device__ __forceinline__ uint32_t lo_pair(uint32_t a, uint32_t b) { return __builtin_amdgcn_perm(b, a, 0x05040100u); }
+__device__ __forceinline__ uint32_t hi_pair(uint32_t a, uint32_t b) { return __builtin_amdgcn_perm(b, a, 0x07060302u); }
+
+// rows[e] holds CPL consecutive BF16 columns of row e (two per dword);
+// out[c] = the 8 rows of column c (two per dword).
+template <int CPL>
+__device__ __forceinline__ void transpose_rows(const uint32_t (&rows)[8][CPL / 2], uint4 (&out)[CPL]) {
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const int row = (tid >> 3) + 32 * u, ch = tid & 7;
-      const int64_t Rr = R0 + row, pc = p0 + 8 * ch;
-      zv[u] = make_uint4(0, 0, 0, 0);
-      if (Rr < Re && pc < P) {
-        if (nvfp4) {
-          const uint32_t wd = *reinterpret_cast<const uint32_t*>(xc + Rr * (P >> 1) + (pc >> 1));
-          const float m = __builtin_amdgcn_cvt_f32_fp8((int)xs[Rr * (P >> 4) + (pc >> 4)], 0) * xr[Rr];
-          zv[u] = deq8_bf16_packed(wd, m);
-        } else {
-          zv[u] = *reinterpret_cast<const uint4*>(zb + Rr * P + pc);
-        }
-      }
-    }
-    uint16_t wv[CR_ROWS * RT / 256];
+  for (int c = 0; c < CPL; ++c) {
+    const int d = c >> 1;
+    uint32_t v[4];
 #pragma unroll
-    for (int u = 0; u < CR_ROWS * RT / 256; ++u) {
-      const int q = tid + 256 * u;
-      const int row = q / RT, col = q % RT;
-      const int64_t Rr = R0 + row;
-      wv[u] = (Rr < Re && col < r) ? w[Rr * r + col] : (uint16_t)0;
-    }
-#pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const int row = (tid >> 3) + 32 * u, ch = tid & 7;
-      const uint32_t e[4] = {zv[u].x, zv[u].y, zv[u].z, zv[u].w};
-#pragma unroll
-      for (int t = 0; t < 4; ++t) {
-        zt[8 * ch + 2 * t][row] = (uint16_t)(e[t] & 0xFFFFu);
-        zt[8 * ch + 2 * t + 1][row] = (uint16_t)(e[t] >> 16);
-      }
-    }
-#pragma unroll
-    for (int u = 0; u < CR_ROWS * RT / 256; ++u) {
-      const int q = tid + 256 * u;
-      wtl[q % RT][q / RT] = wv[u];
-    }
-    __syncthreads();
-#pragma unroll
-    for (int kk = 0; kk < CR_ROWS / 32; ++kk) {
-      const bf16x8_t af = *reinterpret_cast<const bf16x8_t*>(&zt[16 * wave + i][kk * 32 + 8 * g]);
-#pragma unroll
-      for (int t = 0; t < NT; ++t) {
-        const bf16x8_t bf = *reinterpret_cast<const bf16x8_t*>(&wtl[t * 16 + i][kk * 32 + 8 * g]);
-        acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af, bf, acc[t], 0, 0, 0);
-      }
-    }
-    __syncthreads();
+    for (int t = 0; t < 4; ++t)
+      v[t] = (c & 1) ? hi_pair(rows[2 * t][d], rows[2 * t + 1][d]) : lo_pair(rows[2 * t][d], rows[2 * t + 1][d]);
+    out[c] = make_uint4(v[0], v[1], v[2], v[3]);
   }
 }
 
@@ -235,36 +262,122 @@ template <int NT>
 __global__ __launch_bounds__(256) void k_lora_cols(const uint8_t* __restrict__ xc, const uint8_t* __restrict__ xs,
                                                    const float* __restrict__ xr, int64_t M, int64_t K,
                                                    const uint16_t* __restrict__ dy, int64_t N,
-                                                   const uint16_t* __restrict__ T, const uint16_t* __restrict__ dT,
-                                                   int64_t r, int nstrip_b, int64_t rows_per_split,
+                                                   const uint16_t* __restrict__ Tt, const uint16_t* __restrict__ dTt,
+                                                   int64_t ldt, int64_t r, int nstrip_b, int nsplit_b,
+                                                   int64_t rows_b, int nstrip_a, int64_t rows_a,
                                                    float* __restrict__ part_b, float* __restrict__ part_a) {
-  constexpr int RT = 16 * NT;
-  __shared__ __attribute__((aligned(16))) uint16_t zt[64][CR_PAD];
-  __shared__ __attribute__((aligned(16))) uint16_t wtl[RT][CR_PAD];
+  constexpr int CPL = ColCfg<NT>::CPL;
+  constexpr int SW = 16 * CPL;
+  __shared__ floatx4 red[4][CPL][NT][64];
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
   const int i = lane & 15, g = lane >> 4;
-  const bool is_b = (int)blockIdx.x < nstrip_b;
-  const int strip = is_b ? (int)blockIdx.x : (int)blockIdx.x - nstrip_b;
+  // blocks [0, nstrip_b * nsplit_b) are (strip, split) of dB, the rest of dA.
+  // Consecutive block ids go to different XCDs; the remap gives each XCD a
+  // contiguous run of (strip, split) pairs, i.e. adjacent strips of the same
+  // token rows, so the cache lines of a row (codes, scales, BF16) that
+  // neighbouring strips share are fetched into one L2.
+  const int nb = nstrip_b * nsplit_b;
+  const bool is_b = (int)blockIdx.x < nb;
+  int bid = is_b ? (int)blockIdx.x : (int)blockIdx.x - nb;
+  const int nstrip = is_b ? nstrip_b : nstrip_a;
+  const int npart = is_b ? nb : (int)gridDim.x - nb;
+  if ((npart & 7) == 0 && ((is_b ? 0 : nb) & 7) == 0) bid = (bid & 7) * (npart >> 3) + (bid >> 3);
+  const int strip = bid % nstrip, split = bid / nstrip;
+  const int64_t rows_per_split = is_b ? rows_b : rows_a;
   const int64_t P = is_b ? N : K;
-  const int64_t p0 = (int64_t)strip * 64;
-  const int64_t Rb = (int64_t)blockIdx.y * rows_per_split;
+  const int64_t q0 = (int64_t)strip * SW;
+  const int64_t qc = q0 + CPL * i;                          // this lane's first column
+  const bool qok = qc + CPL <= P;                           // P % 16 == 0: all CPL columns or none
+  const int64_t Rb = (int64_t)split * rows_per_split;
   const int64_t Re = Rb + rows_per_split < M ? Rb + rows_per_split : M;
-  floatx4 acc[NT];
-#pragma unroll
-  for (int t = 0; t < NT; ++t) acc[t] = floatx4{0, 0, 0, 0};
-  if (is_b) colred_strip<NT>(false, nullptr, nullptr, nullptr, dy, P, Rb, Re, p0, T, r, zt, wtl, acc);
-  else colred_strip<NT>(true, xc, xs, xr, nullptr, P, Rb, Re, p0, dT, r, zt, wtl, acc);
+  const uint16_t* Wt = is_b ? Tt : dTt;
 
-  // this split's partial for the strip: part[s][p][j], FP32
-  float* part = (is_b ? part_b : part_a) + (int64_t)blockIdx.y * P * r;
+  floatx4 acc[CPL][NT];
 #pragma unroll
-  for (int t = 0; t < NT; ++t) {
-    const int64_t j = t * 16 + i;
+  for (int c = 0; c < CPL; ++c)
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const int64_t pp = p0 + 16 * wave + 4 * g + e;
-      if (pp < P && j < r) part[pp * r + j] = acc[t][e];
+    for (int t = 0; t < NT; ++t) acc[c][t] = floatx4{0, 0, 0, 0};
+
+  for (int64_t m0 = Rb + 32 * wave; m0 < Re; m0 += 128) {
+    // row scales of the step's 32 rows, one per lane (dA strips only)
+    float xr_step = 0.0f;
+    if (!is_b && m0 + (lane & 31) < Re) xr_step = xr[m0 + (lane & 31)];
+    uint32_t rows[8][CPL / 2];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const int64_t m = m0 + 8 * g + e;
+      const bool ok = qok && m < Re;
+      if (is_b) {
+        const uint16_t* src = dy + m * N + qc;
+        if constexpr (CPL == 8) {
+          const uint4 v = ok ? *reinterpret_cast<const uint4*>(src) : make_uint4(0, 0, 0, 0);
+          rows[e][0] = v.x; rows[e][1] = v.y; rows[e][2] = v.z; rows[e][3] = v.w;
+        } else if constexpr (CPL == 4) {
+          const uint2 v = ok ? *reinterpret_cast<const uint2*>(src) : make_uint2(0, 0);
+          rows[e][0] = v.x; rows[e][1] = v.y;
+        } else {
+          rows[e][0] = ok ? *reinterpret_cast<const uint32_t*>(src) : 0u;
+        }
+      } else {
+        // X~ = e * s * r: CPL codes of row m (within one block), dequantized to BF16;
+        // the row scale of row m0 + 8g + e comes from lane 8g + e
+        const uint8_t* cp = xc + m * (K >> 1) + (qc >> 1);
+        const float rr = __shfl(xr_step, 8 * g + e, 64);
+        const float mlt = ok ? e4m3_f32(xs[m * (K >> 4) + (qc >> 4)]) * rr : 0.0f;
+        if constexpr (CPL == 8) {
+          const uint32_t w = ok ? *reinterpret_cast<const uint32_t*>(cp) : 0u;
+          const uint4 v = deq8_bf16(w, mlt);
+          rows[e][0] = v.x; rows[e][1] = v.y; rows[e][2] = v.z; rows[e][3] = v.w;
+        } else if constexpr (CPL == 4) {
+          const uint32_t w = ok ? (uint32_t)*reinterpret_cast<const uint16_t*>(cp) : 0u;
+          const float2_t a = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 0);
+          const float2_t b = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 1);
+          rows[e][0] = pack2(a.x * mlt, a.y * mlt);
+          rows[e][1] = pack2(b.x * mlt, b.y * mlt);
+        } else {
+          const uint32_t w = ok ? (uint32_t)cp[0] : 0u;
+          const float2_t a = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 0);
+          rows[e][0] = pack2(a.x * mlt, a.y * mlt);
+        }
+      }
+    }
+    uint4 wv[NT];
+#pragma unroll
+    for (int t = 0; t < NT; ++t) {
+      const int64_t j = 16 * t + i;
+      // Wt rows are zero-padded up to ldt (M rounded up to 32), and m0 + 32 <= ldt
+      wv[t] = j < r ? *reinterpret_cast<const uint4*>(Wt + j * ldt + m0 + 8 * g) : make_uint4(0, 0, 0, 0);
+    }
+    uint4 zt[CPL];
+    transpose_rows<CPL>(rows, zt);
+#pragma unroll
+    for (int c = 0; c < CPL; ++c)
+#pragma unroll
+      for (int t = 0; t < NT; ++t)
+        acc[c][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, zt[c]),
+                                                            __builtin_bit_cast(bf16x8_t, wv[t]), acc[c][t], 0, 0, 0);
+  }
+
+#pragma unroll
+  for (int c = 0; c < CPL; ++c)
+#pragma unroll
+    for (int t = 0; t < NT; ++t) red[wave][c][t][lane] = acc[c][t];
+  __syncthreads();
+  // output (q, j): q = q0 + CPL ir + c is C row ir of instance c, j = 16 t + jc its C column;
+  // C (ir, jc) sits at lane jc + 16 (ir / 4), register ir % 4
+  float* part = (is_b ? part_b : part_a) + (int64_t)split * P * r;
+  for (int q = tid; q < SW * NT * 16; q += 256) {
+    const int ql = q / (NT * 16), jr = q % (NT * 16);
+    const int ir = ql / CPL, c = ql % CPL;
+    const int t = jr / 16, jc = jr % 16;
+    const int ln = jc + 16 * (ir / 4), e = ir % 4;
+    const int64_t qq = q0 + ql;
+    if (qq < P && jr < r) {
+      float sum = 0.0f;
+#pragma unroll
+      for (int w = 0; w < 4; ++w) sum += red[w][c][t][ln][e];
+      part[qq * r + jr] = sum;
     }
   }
 }
@@ -273,7 +386,8 @@ __global__ __launch_bounds__(256) void k_lora_cols(const uint8_t* __restrict__ x
 // (times `scale`) for q < N*r, then dA [r x K] (stored transposed from the
 // [K x r] partials).
 __global__ __launch_bounds__(256) void k_lora_reduce(const float* __restrict__ part_b,
-                                                     const float* __restrict__ part_a, int nsplit, int64_t N,
+                                                     const float* __restrict__ part_a, int nsplit_b, int nsplit_a,
+                                                     int64_t N,
                                                      int64_t K, int64_t r, float scale, uint16_t* __restrict__ dB,
                                                      uint16_t* __restrict__ dA) {
   const int64_t nb = N * r, total = nb + K * r;
@@ -282,6 +396,7 @@ __global__ __launch_bounds__(256) void k_lora_reduce(const float* __restrict__ p
     const int64_t qq = is_b ? q : q - nb;
     const int64_t stride = is_b ? nb : K * r;
     const float* base = is_b ? part_b : part_a;
+    const int nsplit = is_b ? nsplit_b : nsplit_a;
     float sum = 0.0f;
     for (int s = 0; s < nsplit; ++s) sum += base[(int64_t)s * stride + qq];
     if (is_b) {
@@ -300,53 +415,72 @@ __global__ __launch_bounds__(256) void k_zero_u16(uint16_t* __restrict__ p, int6
 // ---------------------------------------------------------------------------
 // launchers and workspace layout
 // ---------------------------------------------------------------------------
-static int rank_tiles(int64_t r) { return (int)((r + 15) / 16); }
+static int nt_class(int64_t r) {
+  const int nt = (int)((r + 15) / 16);
+  return nt <= 1 ? 1 : nt <= 2 ? 2 : nt <= 4 ? 4 : 8;
+}
+static int cols_per_lane(int ntc) { return ntc <= 2 ? 8 : (ntc <= 4 ? 4 : 2); }
 
 struct LoraWs {
-  int64_t nsplit, rows_per_split;
+  int64_t ldt, nsplit_b, nsplit_a, rows_b, rows_a;
   int nstrip_b, nstrip_a;
-  size_t off_T, off_pdB, off_pdA, total;
+  size_t off_Bt, off_Tt, off_dTt, off_pdB, off_pdA, total;
 };
 
 static size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
+// token splits for `strips` column strips: about `target` workgroups, at least
+// 128 token rows (one step per wave) per split, split length a multiple of 32
+static void token_splits(int64_t M, int64_t strips, int64_t target, int64_t* nsplit, int64_t* rows) {
+  int64_t ns = strips > 0 ? (target + strips - 1) / strips : 1;
+  const int64_t max_ns = (M + 127) / 128;
+  ns = ns > max_ns ? max_ns : ns;
+  ns = ns < 1 ? 1 : (ns > 64 ? 64 : ns);
+  int64_t rp = ((M + ns - 1) / ns + 31) / 32 * 32;
+  if (rp < 32) rp = 32;
+  *rows = rp;
+  *nsplit = (M + rp - 1) / rp < 1 ? 1 : (M + rp - 1) / rp;
+}
+
 static LoraWs lora_ws(int64_t M, int64_t K, int64_t N, int64_t r) {
   LoraWs w;
-  int64_t ns = (M + 255) / 256;                 // >= 256 token rows per split
-  ns = ns < 1 ? 1 : (ns > 64 ? 64 : ns);
-  w.rows_per_split = (M + ns - 1) / ns;
-  w.rows_per_split = (w.rows_per_split + CR_ROWS - 1) / CR_ROWS * CR_ROWS;
-  if (w.rows_per_split < CR_ROWS) w.rows_per_split = CR_ROWS;
-  w.nsplit = (M + w.rows_per_split - 1) / w.rows_per_split;
-  if (w.nsplit < 1) w.nsplit = 1;
-  w.nstrip_b = (int)((N + 63) / 64);
-  w.nstrip_a = (int)((K + 63) / 64);
+  const int64_t sw = 16 * cols_per_lane(nt_class(r));
+  w.nstrip_b = (int)((N + sw - 1) / sw);
+  w.nstrip_a = (int)((K + sw - 1) / sw);
+  w.ldt = (M + 31) / 32 * 32;
+  // dB strips stream BF16 dY (long steps); dA strips dequantize X_q (shorter splits)
+  token_splits(M, w.nstrip_b, 384, &w.nsplit_b, &w.rows_b);
+  token_splits(M, w.nstrip_a, 384, &w.nsplit_a, &w.rows_a);
   size_t off = 0;
-  w.off_T = off;   off = align256(off + (size_t)M * r * 2);
-  w.off_pdB = off; off = align256(off + (size_t)w.nsplit * N * r * 4);
-  w.off_pdA = off; off = align256(off + (size_t)w.nsplit * K * r * 4);
+  w.off_Bt = off;  off = align256(off + (size_t)r * N * 2);
+  w.off_Tt = off;  off = align256(off + (size_t)r * w.ldt * 2);
+  w.off_dTt = off; off = align256(off + (size_t)r * w.ldt * 2);
+  w.off_pdB = off; off = align256(off + (size_t)w.nsplit_b * N * r * 4);
+  w.off_pdA = off; off = align256(off + (size_t)w.nsplit_a * K * r * 4);
   w.total = off;
   return w;
 }
 
 size_t lora_bwd_workspace(int64_t M, int64_t K, int64_t N, int64_t r) { return lora_ws(M, K, N, r).total; }
 
-template <bool DO_DT>
-static void rows(int nt, unsigned grid, hipStream_t s, const uint8_t* xc, const uint8_t* xs, const float* xr,
-                 int64_t M, int64_t K, const uint16_t* A, int64_t r, uint16_t* T, const uint16_t* dy, int64_t N,
-                 const uint16_t* B, float scale, uint16_t* dT) {
-#define PACT_ROWS(NT) k_lora_rows<NT, DO_DT><<<grid, 512, 0, s>>>(xc, xs, xr, M, K, A, r, T, dy, N, B, scale, dT)
-  if (nt <= 1) PACT_ROWS(1);
-  else if (nt <= 2) PACT_ROWS(2);
-  else if (nt <= 4) PACT_ROWS(4);
+static void rows(int ntc, dim3 grid, hipStream_t s, const uint8_t* xc, const uint8_t* xs, const float* xr,
+                 int64_t M, int64_t K, const uint16_t* A, int64_t r, uint16_t* T, uint16_t* Tt, int64_t ldt,
+                 const uint16_t* dy, int64_t N, const uint16_t* Bt, float scale, uint16_t* dT, uint16_t* dTt) {
+#define PACT_ROWS(NT) \
+  k_lora_rows<NT><<<grid, 512, 0, s>>>(xc, xs, xr, M, K, A, r, T, Tt, ldt, dy, N, Bt, scale, dT, dTt)
+  if (ntc <= 1) PACT_ROWS(1);
+  else if (ntc <= 2) PACT_ROWS(2);
+  else if (ntc <= 4) PACT_ROWS(4);
   else PACT_ROWS(8);
 #undef PACT_ROWS
 }
 
+static unsigned grid_for(int64_t n) { return (unsigned)((n + 255) / 256 < 4096 ? (n + 255) / 256 : 4096); }
+
 hipError_t launch_lora_down(const uint8_t* xc, const uint8_t* xs, const float* xr, int64_t M, int64_t K,
                             const uint16_t* A, int64_t r, uint16_t* T, hipStream_t s) {
-  rows<false>(rank_tiles(r), (unsigned)((M + 15) / 16), s, xc, xs, xr, M, K, A, r, T, nullptr, 0, nullptr, 0.0f,
-              nullptr);
+  rows(nt_class(r), dim3((unsigned)((M + 15) / 16), 1), s, xc, xs, xr, M, K, A, r, T, nullptr, 0, nullptr, 0,
+       nullptr, 0.0f, nullptr, nullptr);
   return hipGetLastError();
 }
 
@@ -355,34 +489,39 @@ hipError_t launch_lora_bwd(const uint8_t* xc, const uint8_t* xs, const float* xr
                            int64_t N, uint16_t* dT, uint16_t* dA, uint16_t* dB, void* workspace, hipStream_t s) {
   const LoraWs w = lora_ws(M, K, N, r);
   uint8_t* ws = static_cast<uint8_t*>(workspace);
-  uint16_t* T = reinterpret_cast<uint16_t*>(ws + w.off_T);
+  uint16_t* Bt = reinterpret_cast<uint16_t*>(ws + w.off_Bt);
+  uint16_t* Tt = reinterpret_cast<uint16_t*>(ws + w.off_Tt);
+  uint16_t* dTt = reinterpret_cast<uint16_t*>(ws + w.off_dTt);
   float* pdB = reinterpret_cast<float*>(ws + w.off_pdB);
   float* pdA = reinterpret_cast<float*>(ws + w.off_pdA);
-  const int nt = rank_tiles(r);
-  const int ncnt = w.nstrip_b + w.nstrip_a;
+  const int ntc = nt_class(r);
   if (M == 0) {
     // empty token axis: every gradient is an empty sum (a fill kernel, not a
     // memset, so the call can be captured in a graph)
-    if (N * r > 0) k_zero_u16<<<(unsigned)((N * r + 255) / 256 < 4096 ? (N * r + 255) / 256 : 4096), 256, 0, s>>>(dB, N * r);
-    if (K * r > 0) k_zero_u16<<<(unsigned)((K * r + 255) / 256 < 4096 ? (K * r + 255) / 256 : 4096), 256, 0, s>>>(dA, K * r);
+    if (N * r > 0) k_zero_u16<<<grid_for(N * r), 256, 0, s>>>(dB, N * r);
+    if (K * r > 0) k_zero_u16<<<grid_for(K * r), 256, 0, s>>>(dA, K * r);
     return hipGetLastError();
   }
-  // T (workspace) and dT
-  rows<true>(nt, (unsigned)((M + 15) / 16), s, xc, xs, xr, M, K, A, r, T, dy, N, B, scale, dT);
+  if (N * r > 0) k_transpose_rank<<<grid_for(N * r), 256, 0, s>>>(B, N, r, Bt);
   hipError_t e = hipGetLastError();
-  if (e != hipSuccess || ncnt == 0) return e;
-  const dim3 grid((unsigned)ncnt, (unsigned)w.nsplit);
-#define PACT_COLS(NT) k_lora_cols<NT><<<grid, 256, 0, s>>>(xc, xs, xr, M, K, dy, N, T, dT, r, w.nstrip_b, \
-                                                           w.rows_per_split, pdB, pdA)
-  if (nt <= 1) PACT_COLS(1);
-  else if (nt <= 2) PACT_COLS(2);
-  else if (nt <= 4) PACT_COLS(4);
+  if (e != hipSuccess) return e;
+  // T^T (workspace), dT and dT^T (workspace)
+  rows(ntc, dim3((unsigned)((M + 15) / 16), 2), s, xc, xs, xr, M, K, A, r, nullptr, Tt, w.ldt, dy, N, Bt, scale, dT,
+       dTt);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  const int64_t nblk = (int64_t)w.nstrip_b * w.nsplit_b + (int64_t)w.nstrip_a * w.nsplit_a;
+  if (nblk == 0) return hipSuccess;
+#define PACT_COLS(NT) k_lora_cols<NT><<<(unsigned)nblk, 256, 0, s>>>(xc, xs, xr, M, K, dy, N, Tt, dTt, w.ldt, r,     \
+                                                                 w.nstrip_b, (int)w.nsplit_b, w.rows_b, w.nstrip_a, \
+                                                                 w.rows_a, pdB, pdA)
+  if (ntc <= 1) PACT_COLS(1);
+  else if (ntc <= 2) PACT_COLS(2);
+  else if (ntc <= 4) PACT_COLS(4);
   else PACT_COLS(8);
 #undef PACT_COLS
   if ((e = hipGetLastError()) != hipSuccess) return e;
   const int64_t tot = (N + K) * r;
-  k_lora_reduce<<<(unsigned)((tot + 255) / 256 < 4096 ? (tot + 255) / 256 : 4096), 256, 0, s>>>(
-      pdB, pdA, (int)w.nsplit, N, K, r, scale, dB, dA);
+  k_lora_reduce<<<grid_for(tot), 256, 0, s>>>(pdB, pdA, (int)w.nsplit_b, (int)w.nsplit_a, N, K, r, scale, dB, dA);
   return hipGetLastError();
 }
 
