@@ -368,7 +368,9 @@ struct FastCfg {
   static constexpr int MAIN = 2 * STAGE > 4 * EPI_WAVE ? 2 * STAGE : 4 * EPI_WAVE;
   static constexpr int RSC = MAIN;                      // row scales of A (BM floats) then B (BN floats)
   static constexpr int TOTAL = RSC + ROWS * 4;
-  static_assert(ROWS % 64 == 0, "tile rows");
+  static constexpr int NR_TOTAL = ROWS / 64;            // row-scale load instructions (64 rows each)
+  static constexpr int NR = (NR_TOTAL + 3) / 4;         // per wave
+  static_assert(ROWS % 64 == 0 && BM % 64 == 0, "tile rows");
 };
 
 typedef int int4v_t __attribute__((ext_vector_type(4)));
@@ -393,6 +395,11 @@ __device__ __forceinline__ int4v_t buffer_rsrc(const void* base, uint32_t bytes)
 // publishes a stage.
 __device__ __forceinline__ void lds_dma_buf16(int4v_t rsrc, uint32_t voff, uint32_t soff, uint32_t lds) {
   asm volatile("s_mov_b32 m0, %2\n\tbuffer_load_dwordx4 %0, %1, %3 offen lds"
+               ::"v"(voff), "s"(rsrc), "s"(lds), "s"(soff) : "memory", "m0");
+}
+// 4 bytes per lane from the buffer at voff + soff into LDS at lds + 4 * lane.
+__device__ __forceinline__ void lds_dma_buf4(int4v_t rsrc, uint32_t voff, uint32_t soff, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %2\n\tbuffer_load_dword %0, %1, %3 offen lds"
                ::"v"(voff), "s"(rsrc), "s"(lds), "s"(soff) : "memory", "m0");
 }
 __device__ __forceinline__ uint32_t lds_addr(const void* p) {
@@ -429,72 +436,7 @@ __global__ __launch_bounds__(256, 1) void k_gemm_nvfp4_fast(GemmArgs p, int tile
   const uint32_t crow = (uint32_t)(K >> 1), srow = (uint32_t)(K >> 4);
   const int nk = (int)(K / KT2);
 
-  // row scales of this tile's A rows and B rows, staged once (clamped at the edges)
-  float* rsc = reinterpret_cast<float*>(smem + C::RSC);
-  for (int q = tid; q < C::ROWS; q += 256) {
-    if (q < BM) {
-      const int64_t m = m0 + q;
-      rsc[q] = p.a_rscale[m < M ? m : M - 1];
-    } else {
-      const int64_t n = n0 + (q - BM);
-      rsc[q] = p.b_rscale[n < N ? n : N - 1];
-    }
-  }
-  __syncthreads();
-
   floatx16 acc[WTM][WTN];
-#pragma unroll
-  for (int i = 0; i < WTM; ++i)
-#pragma unroll
-    for (int j = 0; j < WTN; ++j)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
-
-  if (p.lora_t != nullptr) {
-    const int64_t r = p.lora_r;
-    for (int64_t k0 = 0; k0 < r; k0 += 16) {
-      bf16x8_t tf[WTM], uf[WTN];
-#pragma unroll
-      for (int i = 0; i < WTM; ++i) {
-        int64_t m = m0 + wm * (BM / 2) + i * 32 + li;
-        m = m < M ? m : M - 1;
-#pragma unroll
-        for (int t = 0; t < 8; ++t) {
-          const int64_t j = k0 + 8 * h + t;
-          tf[i][t] = bf16_of(j < r ? p.lora_t[m * r + j] : (uint16_t)0);
-        }
-      }
-#pragma unroll
-      for (int i = 0; i < WTN; ++i) {
-        int64_t n = n0 + wn * (BN / 2) + i * 32 + li;
-        n = n < N ? n : N - 1;
-#pragma unroll
-        for (int t = 0; t < 8; ++t) {
-          const int64_t j = k0 + 8 * h + t;
-          uf[i][t] = bf16_of(j < r ? p.lora_u[j * p.u_stride_j + n * p.u_stride_n] : (uint16_t)0);
-        }
-      }
-#pragma unroll
-      for (int i = 0; i < WTM; ++i)
-#pragma unroll
-        for (int j = 0; j < WTN; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tf[i], uf[j], acc[i][j], 0, 0, 0);
-    }
-    // row scales are powers of two: 1/r is exact and computed on the exponent
-    auto inv_pow2 = [](float r) { return __uint_as_float((254u << 23) - __float_as_uint(r)); };
-#pragma unroll
-    for (int i = 0; i < WTM; ++i)
-#pragma unroll
-      for (int rr = 0; rr < 16; ++rr) {
-        const int row = wm * (BM / 2) + i * 32 + 8 * (rr >> 2) + 4 * h + (rr & 3);
-        const float fa = p.lora_scale * inv_pow2(rsc[row]);
-#pragma unroll
-        for (int j = 0; j < WTN; ++j) {
-          const int col = wn * (BN / 2) + j * 32 + li;
-          acc[i][j][rr] *= fa * inv_pow2(rsc[BM + col]);
-        }
-      }
-  }
 
   // ---- load addressing ----
   // Code instruction c of this wave covers tile rows 8 (wave + 4c) .. +7: lane
@@ -692,13 +634,102 @@ __global__ __launch_bounds__(256, 1) void k_gemm_nvfp4_fast(GemmArgs p, int tile
     }
   };
 
-  issue_stage(0, 0);
-  if (nk > 1) {
-    issue_stage(1, 1);
-    PACT_WAIT_VMCNT(C::LOADS);
-  } else {
-    PACT_WAIT_VMCNT(0);
+  // ---- prologue ----
+  // Row scales of the tile's A rows then B rows go straight into LDS (4 bytes
+  // per lane, 64 rows per instruction; rows past an operand's end read as 0
+  // and are never stored), ahead of the first two stages.
+  float* rsc = reinterpret_cast<float*>(smem + C::RSC);
+  {
+    const int4v_t ra_r = buffer_rsrc(p.a_rscale, (uint32_t)(M * 4));
+    const int4v_t rb_r = buffer_rsrc(p.b_rscale, (uint32_t)(N * 4));
+    const uint32_t rdst = lds0 + (uint32_t)C::RSC;
+#pragma unroll
+    for (int c = 0; c < C::NR; ++c) {
+      const int q = wave_s + 4 * c;                      // instruction q: tile rows 64q .. 64q + 63
+      if (q < C::NR_TOTAL) {
+        if (64 * q < BM) {
+          const int64_t m = m0 + 64 * q + lane;
+          lds_dma_buf4(ra_r, m < M ? (uint32_t)m * 4u : 0xfffffff0u, 0u, rdst + (uint32_t)q * 256u);
+        } else {
+          const int64_t n = n0 + (64 * q - BM) + lane;
+          lds_dma_buf4(rb_r, n < N ? (uint32_t)n * 4u : 0xfffffff0u, 0u, rdst + (uint32_t)q * 256u);
+        }
+      }
+    }
   }
+  issue_stage(0, 0);
+  if (nk > 1) issue_stage(1, 1);
+
+  // The LoRA term is formed while those loads are in flight: acc starts as
+  // (lora_scale / (rA rB)) * T U, so the epilogue's row-scale multiply turns
+  // it into lora_scale * T U.  (The compiler's wait for the T/U loads also
+  // covers the stages issued above.)
+#pragma unroll
+  for (int i = 0; i < WTM; ++i)
+#pragma unroll
+    for (int j = 0; j < WTN; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
+  if (p.lora_t != nullptr) {
+    const int64_t r = p.lora_r;
+    const bool t_vec = (r & 15) == 0;                          // T rows: 16-byte aligned runs of 8 ranks
+    const bool u_vec = t_vec && p.u_stride_j == 1;             // U(j, n) = B[n][j]: same for B rows
+    for (int64_t k0 = 0; k0 < r; k0 += 16) {
+      bf16x8_t tf[WTM], uf[WTN];
+#pragma unroll
+      for (int i = 0; i < WTM; ++i) {
+        int64_t m = m0 + wm * (BM / 2) + i * 32 + li;
+        m = m < M ? m : M - 1;
+        if (t_vec) {
+          tf[i] = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const uint4*>(p.lora_t + m * r + k0 + 8 * h));
+        } else {
+#pragma unroll
+          for (int t = 0; t < 8; ++t) {
+            const int64_t j = k0 + 8 * h + t;
+            tf[i][t] = bf16_of(j < r ? p.lora_t[m * r + j] : (uint16_t)0);
+          }
+        }
+      }
+#pragma unroll
+      for (int i = 0; i < WTN; ++i) {
+        int64_t n = n0 + wn * (BN / 2) + i * 32 + li;
+        n = n < N ? n : N - 1;
+        if (u_vec) {
+          uf[i] = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const uint4*>(p.lora_u + n * p.u_stride_n + k0 + 8 * h));
+        } else {
+#pragma unroll
+          for (int t = 0; t < 8; ++t) {
+            const int64_t j = k0 + 8 * h + t;
+            uf[i][t] = bf16_of(j < r ? p.lora_u[j * p.u_stride_j + n * p.u_stride_n] : (uint16_t)0);
+          }
+        }
+      }
+#pragma unroll
+      for (int i = 0; i < WTM; ++i)
+#pragma unroll
+        for (int j = 0; j < WTN; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tf[i], uf[j], acc[i][j], 0, 0, 0);
+    }
+    PACT_WAIT_VMCNT(0);
+    __syncthreads();                                           // every wave's row-scale loads have landed
+    // row scales are powers of two: 1/r is exact and computed on the exponent
+    auto inv_pow2 = [](float v) { return __uint_as_float((254u << 23) - __float_as_uint(v)); };
+#pragma unroll
+    for (int i = 0; i < WTM; ++i)
+#pragma unroll
+      for (int rr = 0; rr < 16; ++rr) {
+        const int row = wm * (BM / 2) + i * 32 + 8 * (rr >> 2) + 4 * h + (rr & 3);
+        const float fa = p.lora_scale * inv_pow2(rsc[row]);
+#pragma unroll
+        for (int j = 0; j < WTN; ++j) {
+          const int col = wn * (BN / 2) + j * 32 + li;
+          acc[i][j][rr] *= fa * inv_pow2(rsc[BM + col]);
+        }
+      }
+  }
+  // stage 0 (and the row scales) complete and visible
+  if (nk > 1) PACT_WAIT_VMCNT(C::LOADS);
+  else PACT_WAIT_VMCNT(0);
   __syncthreads();
   read_codes(smem, 0);
   read_scales(smem, sra, srb);
