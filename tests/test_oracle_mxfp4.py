@@ -1,0 +1,165 @@
+"""Pins for the MXFP4 oracle (PACT, Appendix Table 6, MXFP4 column).
+
+The oracle's quantizer, dequantizer and GEMM are checked against things other
+than themselves: the E8M0 / E2M1 bit-field definitions, hand-worked vectors
+(tests/golden/mxfp4_vectors.txt), an independent exact-rational brute-force
+quantizer (shared exponent from exact integer arithmetic, nearest E2M1 value
+by enumerating all candidates), power-of-two invariance, sign symmetry,
+idempotence, the error bound, and an exact-rational GEMM on small shapes.
+"""
+
+import os
+from fractions import Fraction
+
+import numpy as np
+import pytest
+
+from oracle import mxfp4 as omx
+from oracle import nvfp4 as onv
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden", "mxfp4_vectors.txt")
+E2M1_MAGS = [Fraction(0), Fraction(1, 2), Fraction(1), Fraction(3, 2), Fraction(2), Fraction(3), Fraction(4),
+             Fraction(6)]
+
+
+def test_e8m0_values_from_bit_field():
+    for b in range(255):
+        assert omx.e8m0_value(b) == 2.0 ** (b - 127)
+    assert np.isnan(omx.e8m0_value(255))
+
+
+def test_storage_is_4_25_bits_per_element():
+    assert omx.storage_bytes(64, 1024) * 8 == 64 * 1024 * 4.25
+
+
+def _load_golden():
+    cases, cur = [], None
+    for line in open(GOLDEN):
+        line = line.strip()
+        if not line or line.startswith("#"):
+            continue
+        key, _, rest = line.partition(" ")
+        if key == "name":
+            cur = {"name": rest}
+        elif key == "input":
+            vals = [float(t) for t in rest.split()]
+            cur["input"] = vals + [0.0] * (32 - len(vals))
+        elif key == "scale":
+            cur["scale"] = int(rest, 16)
+        elif key == "codes":
+            cur["codes"] = [int(t, 16) for t in rest.split()]
+        elif key == "end":
+            cases.append(cur)
+    return cases
+
+
+@pytest.mark.parametrize("case", _load_golden(), ids=lambda c: c["name"])
+def test_golden_vectors(case):
+    x = np.array([case["input"]], dtype=np.float64)
+    q = omx.quantize(x)
+    assert q.scales.tolist() == [[case["scale"]]]
+    assert q.codes.tolist() == [case["codes"]]
+
+
+def _brute_block(vals):
+    """Exact-rational MXFP4 quantization of one block: (scale byte, 32 codes)."""
+    fr = [Fraction(v) for v in vals]
+    amax = max(abs(v) for v in fr)
+    if amax == 0:
+        e = -127
+    else:
+        # floor(log2(amax)) by exact comparison with powers of two
+        fl = 0
+        while Fraction(2) ** fl > amax:
+            fl -= 1
+        while Fraction(2) ** (fl + 1) <= amax:
+            fl += 1
+        e = max(-127, min(127, fl - 2))
+    sc = Fraction(2) ** e
+    codes = []
+    for v, xv in zip(fr, vals):
+        t = abs(v) / sc
+        # nearest magnitude; ties to the even code index; values above 6 take 6
+        best = min(range(8), key=lambda q: (abs(E2M1_MAGS[q] - t), q % 2))
+        if t > 6:
+            best = 7
+        codes.append(best | (8 if np.signbit(xv) else 0))
+    return e + 127, codes
+
+
+def test_matches_exact_rational_brute_force():
+    rng = np.random.default_rng(7)
+    rows = []
+    for i in range(120):
+        kind = i % 4
+        if kind == 0:
+            v = rng.standard_normal(32)
+        elif kind == 1:
+            v = rng.standard_normal(32) * 2.0 ** rng.integers(-60, 60)
+        elif kind == 2:       # values on E2M1 midpoints times a power of two
+            v = rng.choice([0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0, 6.0, 7.0], size=32) * 2.0 ** rng.integers(-8, 8)
+            v *= rng.choice([-1.0, 1.0], size=32)
+        else:
+            v = rng.uniform(-1, 1, 32) * 2.0 ** -125
+        rows.append(v.astype(np.float32).astype(np.float64))
+    x = np.array(rows)
+    q = omx.quantize(x)
+    codes = onv.unpack_codes(q.codes)
+    for i, v in enumerate(rows):
+        sb, cb = _brute_block(v)
+        assert q.scales[i, 0] == sb, i
+        assert codes[i].tolist() == cb, i
+
+
+def test_power_of_two_invariance_and_sign_symmetry():
+    rng = np.random.default_rng(8)
+    x = rng.standard_normal((16, 128))
+    q = omx.quantize(x)
+    for k in (-20, -1, 3, 40):
+        qk = omx.quantize(x * 2.0 ** k)
+        assert np.array_equal(qk.codes, q.codes)
+        assert np.array_equal(qk.scales.astype(int), q.scales.astype(int) + k)
+    qn = omx.quantize(-x)
+    assert np.array_equal(onv.unpack_codes(qn.codes), onv.unpack_codes(q.codes) ^ 8)
+    assert np.array_equal(qn.scales, q.scales)
+
+
+def test_idempotent_and_error_bound():
+    rng = np.random.default_rng(9)
+    x = rng.standard_normal((32, 256)) * np.exp(rng.uniform(-5, 5, (32, 1)))
+    q = omx.quantize(x)
+    d = omx.dequantize(q)
+    q2 = omx.quantize(d)
+    assert np.array_equal(q2.codes, q.codes) and np.array_equal(q2.scales, q.scales)
+    # |x - deq| <= half the E2M1 spacing at the value (<= 1 * 2**e), or < 2 * 2**e when saturated
+    e = q.scales.astype(np.int64) - 127
+    bound = np.repeat(np.ldexp(2.0, e), 32, axis=1)
+    assert np.all(np.abs(x - d) <= bound)
+
+
+def test_transpose_layout():
+    rng = np.random.default_rng(10)
+    w = rng.standard_normal((96, 64))
+    wf, wb = omx.weight_layouts(w)
+    assert wf.codes.shape == (96, 32) and wf.scales.shape == (96, 2)
+    assert wb.codes.shape == (64, 48) and wb.scales.shape == (64, 3)
+    ref = omx.quantize(np.ascontiguousarray(w.T))
+    assert np.array_equal(wb.codes, ref.codes) and np.array_equal(wb.scales, ref.scales)
+
+
+def test_gemm_matches_exact_rational_product():
+    rng = np.random.default_rng(11)
+    a = omx.quantize(rng.standard_normal((5, 64)))
+    b = omx.quantize(rng.standard_normal((3, 64)) * 0.02)
+    c, cabs = omx.gemm_nt(a, b)
+    ca, cb = onv.unpack_codes(a.codes), onv.unpack_codes(b.codes)
+
+    def val(codes, scales, i, k):
+        return E2M1_MAGS[codes[i, k] & 7] * (-1 if codes[i, k] & 8 else 1) * Fraction(2) ** (int(scales[i, k // 32]) - 127)
+
+    for i in range(5):
+        for j in range(3):
+            exact = sum(val(ca, a.scales, i, k) * val(cb, b.scales, j, k) for k in range(64))
+            absum = sum(abs(val(ca, a.scales, i, k) * val(cb, b.scales, j, k)) for k in range(64))
+            assert c[i, j] == float(exact) or abs(c[i, j] - float(exact)) <= 2 ** -50 * float(absum)
+            assert abs(cabs[i, j] - float(absum)) <= 2 ** -50 * float(absum)
