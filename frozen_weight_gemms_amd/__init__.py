@@ -206,5 +206,64 @@ def rmsnorm_bwd(yq: NVFP4Tensor, rstd: torch.Tensor, gain: torch.Tensor, dy: tor
     return dx
 
 
+# ---------------------------------------------------------------------------
+# MXFP4 variant (32-element blocks, E8M0 scales)
+# ---------------------------------------------------------------------------
+class MXFP4Tensor:
+    """MXFP4 tensor [rows x cols]: codes uint8 [rows, cols/2], E8M0 scales uint8 [rows, cols/32]."""
+
+    def __init__(self, codes: torch.Tensor, scales: torch.Tensor):
+        self.codes, self.scales = codes, scales
+
+    @property
+    def rows(self) -> int:
+        return self.codes.shape[0]
+
+    @property
+    def cols(self) -> int:
+        return self.codes.shape[1] * 2
+
+    def ptrs(self):
+        return self.codes.data_ptr(), self.scales.data_ptr()
+
+
+def empty_mxfp4(rows: int, cols: int, device="cuda") -> MXFP4Tensor:
+    if cols % 32:
+        raise ValueError("MXFP4 needs cols % 32 == 0")
+    return MXFP4Tensor(torch.empty((rows, cols // 2), dtype=torch.uint8, device=device),
+                       torch.empty((rows, cols // 32), dtype=torch.uint8, device=device))
+
+
+def mx_quantize(x: torch.Tensor, transpose: bool = False, out: MXFP4Tensor | None = None) -> MXFP4Tensor:
+    """MXFP4 of x [rows x cols] (or of x^T with ``transpose``)."""
+    _bf16(x, "x")
+    if x.dim() != 2 or x.stride(1) != 1:
+        raise ValueError("x must be a 2-D tensor with unit column stride")
+    rows, cols = (x.shape[1], x.shape[0]) if transpose else (x.shape[0], x.shape[1])
+    out = out if out is not None else empty_mxfp4(rows, cols, x.device)
+    _lib.call("mxfp4_quantize", x.data_ptr(), rows, cols, x.stride(0), int(transpose), *out.ptrs(), _stream())
+    return out
+
+
+def mx_weight_layouts(w: torch.Tensor):
+    """(W_fwd, W_bwd) = (Q(W), Q(W^T)) in MXFP4 for a BF16 weight W [N x K]."""
+    return mx_quantize(w), mx_quantize(w, transpose=True)
+
+
+def mx_gemm(a: MXFP4Tensor, b: MXFP4Tensor, out: torch.Tensor | None = None, accumulate: bool = False):
+    """C = bf16([f32(C) +] deq(a) deq(b)^T) for MXFP4 a [M x K], b [N x K]."""
+    M, K = a.rows, a.cols
+    N = b.rows
+    if b.cols != K:
+        raise ValueError(f"K mismatch: {K} vs {b.cols}")
+    if out is None:
+        if accumulate:
+            raise ValueError("accumulate needs an existing output")
+        out = torch.empty((M, N), dtype=torch.bfloat16, device=a.codes.device)
+    _lib.call("mxfp4_gemm", *a.ptrs(), M, K, *b.ptrs(), N, out.data_ptr(), out.stride(0), int(accumulate),
+              _stream())
+    return out
+
+
 # fail loudly at import if the native library is missing
 load()

@@ -69,7 +69,7 @@ extern "C" {
 
 const char* pact_last_error(void) { return g_err; }
 
-int pact_abi_version(void) { return 1; }
+int pact_abi_version(void) { return 2; }
 
 int pact_nvfp4_sizes(int64_t rows, int64_t cols, size_t* codes_bytes, size_t* scales_bytes, size_t* rscale_bytes) {
   REQUIRE(rows >= 0 && cols >= 0, PACT_EINVAL, "negative size (rows=%lld, cols=%lld)", (long long)rows,
@@ -287,6 +287,59 @@ int rmsnorm_bwd(const uint8_t* y_codes, const uint8_t* y_scales, const float* y_
   return hip_status(pact::launch_rmsnorm_bwd(y_codes, y_scales, y_rscale, rstd, gain, dy, M, H, dx,
                                              as_stream(stream)),
                     "rmsnorm_bwd launch");
+}
+
+
+int pact_mxfp4_sizes(int64_t rows, int64_t cols, size_t* codes_bytes, size_t* scales_bytes) {
+  REQUIRE(rows >= 0 && cols >= 0, PACT_EINVAL, "negative size (rows=%lld, cols=%lld)", (long long)rows,
+          (long long)cols);
+  REQUIRE(cols % 32 == 0, PACT_ESHAPE, "cols=%lld is not a multiple of 32", (long long)cols);
+  REQUIRE(codes_bytes && scales_bytes, PACT_EINVAL, "NULL output pointer");
+  *codes_bytes = (size_t)(rows * (cols / 2));
+  *scales_bytes = (size_t)(rows * (cols / 32));
+  return ok();
+}
+
+int mxfp4_quantize(const uint16_t* x, int64_t rows, int64_t cols, int64_t ldx, int transpose, uint8_t* codes,
+                   uint8_t* scales, void* stream) {
+  REQUIRE(rows >= 0 && cols >= 0, PACT_EINVAL, "negative size (rows=%lld, cols=%lld)", (long long)rows,
+          (long long)cols);
+  REQUIRE(transpose == 0 || transpose == 1, PACT_EINVAL, "transpose must be 0 or 1 (got %d)", transpose);
+  REQUIRE(cols % 32 == 0, PACT_ESHAPE, "cols=%lld is not a multiple of 32", (long long)cols);
+  if (rows == 0 || cols == 0) return ok();
+  REQUIRE_PTR(x, "x");
+  REQUIRE_PTR(codes, "out codes");
+  REQUIRE_PTR(scales, "out scales");
+  if (transpose == 0) {
+    REQUIRE(ldx >= cols, PACT_ESHAPE, "ldx=%lld < cols=%lld", (long long)ldx, (long long)cols);
+    REQUIRE(ldx % 8 == 0, PACT_EALIGN, "ldx=%lld is not a multiple of 8 elements", (long long)ldx);
+  } else {
+    REQUIRE(ldx >= rows, PACT_ESHAPE, "ldx=%lld < rows=%lld (transposed input is [cols x rows])", (long long)ldx,
+            (long long)rows);
+  }
+  REQUIRE(rows <= 0x7FFFFFFF, PACT_EUNSUPPORTED, "rows=%lld exceeds the grid limit", (long long)rows);
+  return hip_status(pact::launch_mx_quantize(x, rows, cols, ldx, transpose, codes, scales, as_stream(stream)),
+                    "mxfp4_quantize launch");
+}
+
+int mxfp4_gemm(const uint8_t* a_codes, const uint8_t* a_scales, int64_t M, int64_t K, const uint8_t* b_codes,
+               const uint8_t* b_scales, int64_t N, uint16_t* c, int64_t ldc, int accumulate, void* stream) {
+  REQUIRE(M >= 0 && N >= 0 && K >= 0, PACT_EINVAL, "negative size");
+  REQUIRE(accumulate == 0 || accumulate == 1, PACT_EINVAL, "accumulate must be 0 or 1");
+  REQUIRE(K % 128 == 0, PACT_ESHAPE, "K=%lld is not a multiple of 128", (long long)K);
+  if (M == 0 || N == 0) return ok();
+  REQUIRE(K > 0, PACT_ESHAPE, "K must be positive");
+  REQUIRE_PTR(a_codes, "a codes");
+  REQUIRE_PTR(a_scales, "a scales");
+  REQUIRE_PTR(b_codes, "b codes");
+  REQUIRE_PTR(b_scales, "b scales");
+  REQUIRE_PTR(c, "c");
+  REQUIRE(ldc >= N, PACT_ESHAPE, "ldc=%lld < N=%lld", (long long)ldc, (long long)N);
+  REQUIRE(pact::mx_gemm_supported(M, N, K), PACT_EUNSUPPORTED, "operands exceed 2^31 bytes of codes");
+  REQUIRE((M + 127) / 128 * ((N + 127) / 128) < 0x7FFFFFFF, PACT_EUNSUPPORTED, "grid too large");
+  return hip_status(pact::launch_mx_gemm(a_codes, a_scales, M, K, b_codes, b_scales, N, c, ldc, accumulate,
+                                         as_stream(stream)),
+                    "mxfp4_gemm launch");
 }
 
 }  // extern "C"

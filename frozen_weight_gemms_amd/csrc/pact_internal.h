@@ -60,4 +60,10 @@ hipError_t launch_rmsnorm_bwd(const uint8_t* yc, const uint8_t* ys, const float*
                               const uint16_t* gain, const uint16_t* dy, int64_t M, int64_t H, uint16_t* dx,
                               hipStream_t s);
 
+hipError_t launch_mx_quantize(const uint16_t* x, int64_t rows, int64_t cols, int64_t ldx, int transpose,
+                              uint8_t* codes, uint8_t* scales, hipStream_t s);
+bool mx_gemm_supported(int64_t M, int64_t N, int64_t K);
+hipError_t launch_mx_gemm(const uint8_t* ac, const uint8_t* as, int64_t M, int64_t K, const uint8_t* bc,
+                          const uint8_t* bs, int64_t N, uint16_t* out, int64_t ldo, int accumulate, hipStream_t s);
+
 }  // namespace pact

@@ -205,6 +205,46 @@ int rmsnorm_bwd(const uint8_t *y_codes, const uint8_t *y_scales, const float *y_
                 const float *rstd, const uint16_t *gain, const uint16_t *dy, int64_t M, int64_t H,
                 uint16_t *dx, void *stream);
 
+/* ---------------------------------------------------------------------------
+ * MXFP4 variant (Appendix Table 6, MXFP4 column: 32-element blocks, E2M1
+ * elements, E8M0 block scales, 4.25 bits/element, no other scale).  A tensor
+ * of logical shape [rows x cols], cols % 32 == 0, is two row-major buffers:
+ *   codes  uint8 [rows][cols/2]   E2M1 codes, element 2j in the low nibble of byte j
+ *   scales uint8 [rows][cols/32]  E8M0 block scales: byte b is 2^(b - 127)
+ * Element (i, j) is  E2M1(code) * 2^(scale[i][j/32] - 127).
+ * Block scale (the tables give none; the OCP microscaling rule): shared
+ * exponent e = floor(log2(blockmax)) - 2, clamped to [-127, 127], -127 for an
+ * all-zero block, stored as e + 127; element code = RNE(|x| / 2^e) onto
+ * {0,.5,1,1.5,2,3,4,6}, ties to the even code, saturating at 6, sign kept.
+ * ------------------------------------------------------------------------- */
+
+/* Host-only size query: bytes of the two buffers of an MXFP4 [rows x cols]. */
+int pact_mxfp4_sizes(int64_t rows, int64_t cols, size_t *codes_bytes, size_t *scales_bytes);
+
+/*
+ * mxfp4_quantize -- BF16 -> MXFP4.
+ *   transpose == 0: x is [rows x cols] with leading dimension ldx >= cols
+ *                   (a multiple of 8); the result is Q(x), blocks along cols.
+ *   transpose == 1: x is [cols x rows] with leading dimension ldx >= rows; the
+ *                   result is Q(x^T) [rows x cols] (the backward weight layout
+ *                   W_bwd = Q(W^T) from W [N x K] with rows = K, cols = N).
+ *   cols % 32 == 0.  Outputs: codes [rows][cols/2], scales [rows][cols/32].
+ */
+int mxfp4_quantize(const uint16_t *x, int64_t rows, int64_t cols, int64_t ldx, int transpose,
+                   uint8_t *codes, uint8_t *scales, void *stream);
+
+/*
+ * mxfp4_gemm -- C = A B^T for MXFP4 A [M x K] and B [N x K] (forward: X_q and
+ * W_fwd = Q(W); input gradient: dY_q [M x N] and W_bwd = Q(W^T) [K x N]), on
+ * the scaled FP4 matrix instructions with FP32 accumulation (Appendix Table 7
+ * row "Frozen projections", with the Table 6 MXFP4 format in place of NVFP4).
+ *   C BF16 [M x N], leading dim ldc >= N; accumulate != 0: C = bf16(f32(C) + A B^T).
+ *   K % 128 == 0; A and B hold fewer than 2^31 bytes of codes each.
+ */
+int mxfp4_gemm(const uint8_t *a_codes, const uint8_t *a_scales, int64_t M, int64_t K,
+               const uint8_t *b_codes, const uint8_t *b_scales, int64_t N, uint16_t *c, int64_t ldc,
+               int accumulate, void *stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -25,7 +25,7 @@ def lib():
 
 def test_header_symbols_exported(lib):
     names = _lib.header_functions()
-    assert len(names) == 14, names
+    assert len(names) == 17, names
     assert set(names) == set(_lib.SIGNATURES), set(names) ^ set(_lib.SIGNATURES)
     for n in names:
         assert hasattr(lib, n), n
@@ -52,7 +52,7 @@ def test_gemm_tile_query(lib):
 
 
 def test_abi_version(lib):
-    assert lib.pact_abi_version() == 1
+    assert lib.pact_abi_version() == 2
 
 
 def test_sizes(lib):
@@ -136,3 +136,23 @@ def test_package_import_requires_library(tmp_path, monkeypatch):
     monkeypatch.setattr(_lib, "LIB_PATH", str(tmp_path / "missing.so"))
     with pytest.raises(ImportError):
         _lib.load()
+
+
+def test_mxfp4_sizes_and_validation(lib):
+    c, s = ctypes.c_size_t(), ctypes.c_size_t()
+    assert lib.pact_mxfp4_sizes(4096, 3072, ctypes.byref(c), ctypes.byref(s)) == 0
+    assert (c.value, s.value) == (4096 * 1536, 4096 * 96)
+    assert (c.value + s.value) * 8 == 4096 * 3072 * 4.25
+    assert lib.pact_mxfp4_sizes(4, 48, ctypes.byref(c), ctypes.byref(s)) == -2      # cols % 32
+    q = lib.mxfp4_quantize
+    assert q(ALIGNED, 4, 48, 48, 0, ALIGNED, ALIGNED, None) == -2                  # cols % 32
+    assert q(ALIGNED, 4, 64, 64, 3, ALIGNED, ALIGNED, None) == -1                  # bad transpose flag
+    assert q(None, 4, 64, 64, 0, ALIGNED, ALIGNED, None) == -1                     # NULL x
+    assert q(ALIGNED, 4, 64, 64, 0, MISALIGNED, ALIGNED, None) == -3               # misaligned codes
+    assert q(ALIGNED, 4, 64, 32, 0, ALIGNED, ALIGNED, None) == -2                  # ldx < cols
+    g = lib.mxfp4_gemm
+    assert g(ALIGNED, ALIGNED, 64, 96, ALIGNED, ALIGNED, 64, ALIGNED, 64, 0, None) == -2   # K % 128
+    assert g(ALIGNED, ALIGNED, 64, 128, ALIGNED, ALIGNED, 64, ALIGNED, 32, 0, None) == -2  # ldc < N
+    assert g(ALIGNED, ALIGNED, 64, 128, None, ALIGNED, 64, ALIGNED, 64, 0, None) == -1     # NULL b
+    assert g(ALIGNED, ALIGNED, 64, 128, ALIGNED, ALIGNED, 64, ALIGNED, 64, 2, None) == -1  # accumulate flag
+    assert g(ALIGNED, ALIGNED, 0, 128, ALIGNED, ALIGNED, 64, ALIGNED, 64, 0, None) == 0    # empty: no-op
