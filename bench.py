@@ -21,6 +21,11 @@ synthetic (seeded, BF16, resident in HBM before timing); weights are random
 N(0, 0.02) quantized once to their cached forward and backward layouts
 (offline, untimed).
 
+A second leg times the MXFP4 variant (32-element blocks, E8M0 scales) on the
+same shapes: the 7 forward and 7 input-gradient GEMMs of each layer instance,
+with MXFP4 operands quantized beforehand, as HIP-graph replays; it is reported
+under "mxfp4_variant" and is not part of "value".
+
 Prints one JSON line.  --gpus must be 1: this build runs on one GPU.
 """
 
@@ -38,6 +43,7 @@ sys.path.insert(0, ROOT)
 
 PEAK = {"fp16_mfma_tflops": 2500.0, "fp4_mfma_tflops": 10100.0, "hbm_gbs": 8000.0}
 LORA_SCALE = 2.0
+HEAD_START_CYCLES = 40_000_000      # spin ahead of each instrumented step (about 20 ms)
 
 
 def parse():
@@ -51,6 +57,7 @@ def parse():
     ap.add_argument("--layers", type=int, default=4,
                     help="distinct decoder-layer instances a step runs through (their weights and buffers "
                          "together exceed the 256 MB last-level cache, so every operand streams from HBM)")
+    ap.add_argument("--no-mxfp4", action="store_true", help="skip the MXFP4-variant GEMM leg")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a 1 GiB read + 1 GiB write elementwise kernel (counter calibration)")
     return ap.parse_args()
@@ -178,6 +185,109 @@ class Layer:
         return sum(4 * self.M * P["p"].d_in * P["p"].d_out for P in self.proj.values())
 
 
+class MxLayer:
+    """The same layer's projections in the MXFP4 variant: cached W_fwd / W_bwd in
+    MXFP4 (quantized once, untimed) and MXFP4 GEMM inputs; a step is the 7
+    forward and 7 input-gradient GEMMs."""
+
+    def __init__(self, fw, torch, synth, wl, index=0):
+        import numpy as np
+        self.fw, self.torch = fw, torch
+        off = 5000 + 1000 * index
+        M = wl.tokens
+        dev = torch.device("cuda:0")
+        up = lambda bits: torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).to(dev)
+        self.M, self.items = M, []
+        for i, p in enumerate(wl.projections):
+            w = up(synth.normal_bf16((p.d_out, p.d_in), wl.w_std, wl.wid, off + 20 + i))
+            wf, wb = fw.mx_weight_layouts(w)
+            del w
+            xq = fw.mx_quantize(up(synth.workload_activation(wl, M, p.d_in, off + 60 + i)))
+            dyq = fw.mx_quantize(up(synth.normal_bf16((M, p.d_out), wl.dy_std, wl.wid, off + 80 + i)))
+            self.items.append(dict(p=p, wf=wf, wb=wb, xq=xq, dyq=dyq,
+                                   Y=torch.empty((M, p.d_out), dtype=torch.bfloat16, device=dev),
+                                   dX=torch.empty((M, p.d_in), dtype=torch.bfloat16, device=dev)))
+        self.record = None
+
+    def step(self):
+        fw, torch = self.fw, self.torch
+        for it in self.items:
+            p = it["p"]
+            for what, a, b, out, n, k in (("fwd", it["xq"], it["wf"], it["Y"], p.d_out, p.d_in),
+                                          ("dgrad", it["dyq"], it["wb"], it["dX"], p.d_in, p.d_out)):
+                if self.record is None:
+                    fw.mx_gemm(a, b, out=out)
+                else:
+                    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                    e0.record()
+                    fw.mx_gemm(a, b, out=out)
+                    e1.record()
+                    self.record.append((e0, e1, (self.M, n, k)))
+
+    def gemm_flops(self):
+        return sum(4 * self.M * it["p"].d_in * it["p"].d_out for it in self.items)
+
+
+def mxfp4_leg(fw, torch, synth, wl, nlayers, steps, warmup):
+    """Throughput of the MXFP4 variant's GEMMs (same shapes, same rotation over
+    distinct layer instances, HIP-graph replays) and its dominant kernel."""
+    from frozen_weight_gemms_amd import _lib
+    layers = [MxLayer(fw, torch, synth, wl, li) for li in range(nlayers)]
+
+    def step():
+        for ly in layers:
+            ly.step()
+
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        step()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        step()
+    graph.replay()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        graph.replay()
+    torch.cuda.synchronize()
+    ms = (time.perf_counter() - t0) * 1e3 / steps
+    recs = []
+    for ly in layers:
+        ly.record = recs
+    for _ in range(steps):
+        torch.cuda._sleep(HEAD_START_CYCLES)
+        step()
+    torch.cuda.synchronize()
+    by_tile = {}
+    for e0, e1, (M, N, K) in recs:
+        t = by_tile.setdefault(_lib.gemm_tile(M, N, K), [0.0, 0.0, 0])
+        t[0] += e0.elapsed_time(e1)
+        t[1] += 2.0 * M * N * K
+        t[2] += 1
+    dom = max(by_tile, key=lambda k: by_tile[k][0])
+    dt, dfl, dn = by_tile[dom]
+    ach = dfl / (dt * 1e-3) / 1e12
+    flops = sum(ly.gemm_flops() for ly in layers)
+    gemm_ms = sum(v[0] for v in by_tile.values()) / steps
+    value = flops / (ms * 1e-3) / 1e12
+    del layers, graph
+    torch.cuda.synchronize()
+    return {"gemm_tflops": round(value, 1), "frac_fp4_peak": round(value / PEAK["fp4_mfma_tflops"], 4),
+            "ms_per_step": round(ms, 4), "layers": nlayers,
+            "gemm_only_tflops_events": round(flops / (gemm_ms * 1e-3) / 1e12, 1),
+            "timed_region": "hip graph replays of 14 MXFP4 GEMMs per layer",
+            "roofline": {"kernel": f"pact::k_gemm_mxfp4<{dom[0] // 64}, {dom[1] // 64}>", "bound": "mfma",
+                         "achieved": round(ach, 1), "peak": PEAK["fp4_mfma_tflops"], "unit": "TFLOP/s",
+                         "frac": round(ach / PEAK["fp4_mfma_tflops"], 4), "launches_per_step": dn // steps,
+                         "avg_launch_us": round(dt * 1e3 / dn, 2)}}
+
+
 # algorithmic bytes per element of each bandwidth-bound kernel (inputs read + outputs written)
 BYTES_PER_ELEM = {"quant": 2.0 + 0.5 + 1 / 16, "rmsq": 2.0 + 0.5 + 1 / 16, "silu": 4.0 + 3 * (0.5 + 1 / 16),
                   "silub": 2 * (0.5 + 1 / 16) + 2.0 + 4.0, "rmsb": (0.5 + 1 / 16) + 2.0 + 2.0}
@@ -299,13 +409,16 @@ def main():
     gpu_ms = ev0.elapsed_time(ev1)
 
     # instrumented pass over the same K steps: events around every launch give
-    # per-kernel durations (events add host and queue overhead between kernels,
-    # so this pass is not the one the step time comes from)
+    # per-kernel durations (events add queue overhead between kernels, so this
+    # pass is not the one the step time comes from).  A spin kernel ahead of each
+    # step lets the host enqueue the step's launches before the GPU reaches
+    # them, so an event pair brackets the kernel and not the host's launch time.
     recs = []
     for ly in layers:
         ly.record = recs
     torch.cuda.synchronize()
     for _ in range(args.steps):
+        torch.cuda._sleep(HEAD_START_CYCLES)
         step()
     torch.cuda.synchronize()
     for ly in layers:
@@ -345,7 +458,7 @@ def main():
     if os.path.exists(tfile):
         try:
             tj = json.load(open(tfile))
-            if tj.get("src_hash") == src_hash("gemm.hip", "nvfp4_device.h") and tj.get("kernel") == kname \
+            if tj.get("src_hash") == src_hash("gemm.hip", "nvfp4_device.h", "lds_dma.h") and tj.get("kernel") == kname \
                     and tj.get("tile") == list(dom_tile[:2]):
                 traffic = tj.get("bytes_per_launch")
         except (ValueError, OSError):
@@ -387,6 +500,9 @@ def main():
                      "avg_launch_us": round(dt_ms * 1e3 / dcount, 2),
                      "traffic": traffic},
     }
+    if not args.no_mxfp4:
+        del graph
+        result["mxfp4_variant"] = mxfp4_leg(fw, torch, synth, wl, max(1, args.layers), args.steps, args.warmup)
     if args.copy_calibration:
         x = torch.empty(1 << 29, dtype=torch.bfloat16, device="cuda")   # 1 GiB
         y = torch.empty_like(x)
