@@ -32,7 +32,7 @@ def hipcc() -> str:
 
 def common_flags():
     return [
-        f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC",
+        f"--offload-arch={ARCH}", "-O3", "-std=c++20", "-fPIC",
         "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
         "-ffp-contract=off", "-fno-fast-math",
         "-I", INCLUDE, "-I", CSRC,

@@ -21,6 +21,7 @@
 // fill), with K stages of 128 and four LDS buffers: a stage takes a quarter of
 // the MFMA time of an NVFP4 stage, so loads are issued three stages ahead.
 #include <type_traits>
+#include <utility>
 
 #include "lds_dma.h"
 #include "pact_internal.h"
@@ -114,6 +115,18 @@ __global__ __launch_bounds__(256) void k_mx_quantize_cols(const uint16_t* __rest
 // ---------------------------------------------------------------------------
 // GEMM: C = A B^T, A = MXFP4 [M x K], B = MXFP4 [N x K], FP32 accumulation,
 // BF16 output (optionally C = bf16(f32(C) + A B^T)).
+//
+// K is processed in stages of 128 (64 code bytes per row) held in a ring of
+// four LDS buffers; the loads of stage kt + 4 are issued while stage kt is
+// multiplied.  Scales travel in groups of G = 4 stages (16 bytes per row: one
+// memory request per row per group instead of one per stage; 8 stages measured
+// no faster): the group for stages Gg .. Gg + G - 1 is loaded together with
+// the codes of stage Gg into one of two scale buffers.
+// Fragments are double-buffered in registers: after the barrier that
+// publishes stage kt + 1, a wave reads stage kt + 1's fragments and scales
+// while it multiplies stage kt, one LDS read after each MFMA (a burst of reads
+// stalls the wave's in-order issue behind a full LDS queue and starves the
+// matrix core), so LDS latency is hidden behind a whole stage of MFMAs.
 // ---------------------------------------------------------------------------
 template <int WTM, int WTN>
 struct MxCfg {
@@ -121,20 +134,28 @@ struct MxCfg {
   static constexpr int BN = 64 * WTN;
   static constexpr int ROWS = BM + BN;
   static constexpr int KS = 128;                        // K elements per stage
-  static constexpr int CODES = 0;                       // [ROWS][64] swizzled by (row >> 2) & 3
-  static constexpr int SCALES = ROWS * 64;              // [ROWS][4] (4 blocks of 32 per stage)
-  static constexpr int NC = ROWS / 64;                  // code load instructions per wave per stage (16 rows each)
-  static constexpr int NS_TOTAL = ROWS / 64;            // scale load instructions per stage (64 rows each)
-  static constexpr int NS = (NS_TOTAL + 3) / 4;         // per wave; surplus ones fill a pad region with zeros
-  static constexpr int PAD = SCALES + ROWS * 4;
-  static constexpr int STAGE = PAD + (NS * 4 - NS_TOTAL) * 256;
-  static constexpr int NSTAGE = 4;
-  static constexpr int LOADS = NC + NS;
+  static constexpr int NCODE = 4;                       // code stage buffers
+  static constexpr int CODE_STAGE = ROWS * 64;          // [ROWS][64] swizzled by (row >> 2) & 3
+#ifndef PACT_MX_SCALE_GROUP
+#define PACT_MX_SCALE_GROUP 4
+#endif
+  static constexpr int G = PACT_MX_SCALE_GROUP;         // stages per scale group
+  static constexpr int SC_ROW = 4 * G;                  // scale bytes per row and group
+  static constexpr int SC_BYTES = ROWS * SC_ROW;        // [ROWS][SC_ROW]: G stages x 4 blocks
+  static constexpr int SC_OFF = NCODE * CODE_STAGE;
+  static constexpr int NC = ROWS / 64;                  // code loads per wave per stage (16 rows each)
+  static constexpr int SC_LANES = SC_ROW / 16;          // lanes per row in a scale load
+  static constexpr int NSG_TOTAL = SC_BYTES / 1024;     // scale loads per group (1 KB each)
+  static constexpr int NSG = (NSG_TOTAL + 3) / 4;       // per wave; surplus ones fill a pad region
+  static constexpr int PAD_OFF = SC_OFF + 2 * SC_BYTES;
+  static constexpr int MAIN = PAD_OFF + (NSG * 4 - NSG_TOTAL) * 1024;
   static constexpr int EPI_LD = BN / 2 + 4;
   static constexpr int EPI_WAVE = 32 * EPI_LD * 4;
-  static constexpr int TOTAL = NSTAGE * STAGE > 4 * EPI_WAVE ? NSTAGE * STAGE : 4 * EPI_WAVE;
+  static constexpr int TOTAL = MAIN > 4 * EPI_WAVE ? MAIN : 4 * EPI_WAVE;
   static_assert(ROWS % 64 == 0 && BM % 64 == 0, "tile rows");
-  static_assert(2 * LOADS <= 63 && 3 * LOADS <= 63, "vmcnt range");
+  static_assert(2 * NC + NSG <= 63 && 3 * NC + NSG <= 63, "vmcnt range");
+  static_assert(NC + NSG <= 2 * WTM * WTN, "one load per MFMA");
+  static_assert(TOTAL <= 160 * 1024, "LDS");
 };
 
 struct MxGemmArgs {
@@ -153,7 +174,7 @@ __device__ __forceinline__ uint32_t bf16_pack2(float lo, float hi) { return pack
 template <int WTM, int WTN>
 __global__ __launch_bounds__(256, 1) void k_gemm_mxfp4(MxGemmArgs p, int tiles_m, int tiles_n) {
   using C = MxCfg<WTM, WTN>;
-  constexpr int BM = C::BM, BN = C::BN;
+  constexpr int BM = C::BM, BN = C::BN, NC = C::NC, NSG = C::NSG;
   __shared__ __attribute__((aligned(1024))) uint8_t smem[C::TOTAL];
 
   const int tid = threadIdx.x;
@@ -178,17 +199,21 @@ __global__ __launch_bounds__(256, 1) void k_gemm_mxfp4(MxGemmArgs p, int tiles_m
   const int nk = (int)(K / C::KS);
 
   // ---- load addressing ----
-  // Code instruction c of this wave covers tile rows 16 (wave + 4c) .. +15:
-  // lane -> row 16 (wave + 4c) + lane / 4, LDS slot lane % 4, global chunk
-  // slot ^ ((row >> 2) & 3) = slot ^ ((lane >> 4) & 3).
+  // Code load c of this wave covers tile rows 16 (wave + 4c) .. +15: lane ->
+  // row 16 (wave + 4c) + lane / 4, LDS slot lane % 4, global chunk
+  // slot ^ ((row >> 2) & 3) = slot ^ ((lane >> 4) & 3).  Scale load c covers
+  // 1 KB of the [ROWS][SC_ROW] group buffer: lane -> row
+  // (64 / SC_LANES) (wave + 4c) + lane / SC_LANES, 16-byte part lane % SC_LANES.
+  // Rows outside the operands get an offset past the buffer end: the range
+  // check returns zeros.
   const int4v_t ra_c = buffer_rsrc(p.a_codes, (uint32_t)(M * crow));
   const int4v_t rb_c = buffer_rsrc(p.b_codes, (uint32_t)(N * crow));
   const int4v_t ra_s = buffer_rsrc(p.a_scales, (uint32_t)(M * srow));
   const int4v_t rb_s = buffer_rsrc(p.b_scales, (uint32_t)(N * srow));
   const uint32_t cchunk = (uint32_t)(((lane & 3) ^ ((lane >> 4) & 3)) << 4);
-  uint32_t cvo[C::NC];
+  uint32_t cvo[NC];
 #pragma unroll
-  for (int c = 0; c < C::NC; ++c) {
+  for (int c = 0; c < NC; ++c) {
     const int row = 16 * (wave + 4 * c) + (lane >> 2);
     uint32_t v = 0xfffffff0u;
     if (row < BM) {
@@ -200,81 +225,91 @@ __global__ __launch_bounds__(256, 1) void k_gemm_mxfp4(MxGemmArgs p, int tiles_m
     }
     cvo[c] = v;
   }
-  uint32_t svo[C::NS];
+  uint32_t svo[NSG];
 #pragma unroll
-  for (int c = 0; c < C::NS; ++c) {
+  for (int c = 0; c < NSG; ++c) {
     const int q = wave + 4 * c;
-    const int row = 64 * q + lane;
+    const int row = (64 / C::SC_LANES) * q + lane / C::SC_LANES;
+    const uint32_t part = (uint32_t)(lane % C::SC_LANES) * 16u;
     uint32_t v = 0xfffffff0u;
-    if (q < C::NS_TOTAL) {
+    if (q < C::NSG_TOTAL) {
       if (row < BM) {
         const int64_t m = m0 + row;
-        if (m < M) v = (uint32_t)m * srow;
+        if (m < M) v = (uint32_t)m * srow + part;
       } else {
         const int64_t n = n0 + (row - BM);
-        if (n < N) v = (uint32_t)n * srow;
+        if (n < N) v = (uint32_t)n * srow + part;
       }
     }
     svo[c] = v;
   }
   const int wave_s = __builtin_amdgcn_readfirstlane(wave);
   const uint32_t lds0 = lds_addr(smem);
-  auto issue_one = [&](int kt, int buf, int q) {
-    const uint32_t st = lds0 + (uint32_t)(buf * C::STAGE);
-    if (q < C::NC) {
-      static_assert(BM % 64 == 0, "A/B split on an instruction boundary");
-      const uint32_t dst = st + C::CODES + (uint32_t)(wave_s + 4 * q) * 1024u;
-      const uint32_t soff = (uint32_t)kt * 64u;
+  // load q of stage s: codes for q < NC, then (first stage of a group only) scales
+  auto issue_one = [&](int s, int q) {
+    if (q < NC) {
+      const uint32_t dst = lds0 + (uint32_t)((s & 3) * C::CODE_STAGE) + (uint32_t)(wave_s + 4 * q) * 1024u;
+      const uint32_t soff = (uint32_t)s * 64u;
       if (16 * (4 * q + 3) + 15 < BM) lds_dma_buf16(ra_c, cvo[q], soff, dst);
       else lds_dma_buf16(rb_c, cvo[q], soff, dst);
     } else {
-      const int c = q - C::NC;
+      const int c = q - NC;
       const int qq = wave_s + 4 * c;
-      const uint32_t dst = qq < C::NS_TOTAL ? st + C::SCALES + (uint32_t)qq * 256u
-                                            : st + C::PAD + (uint32_t)(qq - C::NS_TOTAL) * 256u;
-      const uint32_t soff = (uint32_t)kt * 4u;
-      if (64 * (4 * c + 3) + 63 < BM) lds_dma_buf4(ra_s, svo[c], soff, dst);
-      else if (256 * c >= BM) lds_dma_buf4(rb_s, svo[c], soff, dst);
-      else if (qq * 64 < BM) lds_dma_buf4(ra_s, svo[c], soff, dst);   // split by wave: uniform branch
-      else lds_dma_buf4(rb_s, svo[c], soff, dst);
+      const int g = s / C::G;
+      const uint32_t dst = qq < C::NSG_TOTAL
+                               ? lds0 + (uint32_t)(C::SC_OFF + (g & 1) * C::SC_BYTES) + (uint32_t)qq * 1024u
+                               : lds0 + (uint32_t)C::PAD_OFF + (uint32_t)(qq - C::NSG_TOTAL) * 1024u;
+      const uint32_t soff = (uint32_t)g * (uint32_t)C::SC_ROW;
+      constexpr int RPL = 64 / C::SC_LANES;                    // rows per scale load
+      if (RPL * (4 * c + 3) + RPL - 1 < BM) lds_dma_buf16(ra_s, svo[c], soff, dst);
+      else if (RPL * 4 * c >= BM) lds_dma_buf16(rb_s, svo[c], soff, dst);
+      else if (qq * RPL < BM) lds_dma_buf16(ra_s, svo[c], soff, dst);   // split by wave: uniform branch
+      else lds_dma_buf16(rb_s, svo[c], soff, dst);
     }
   };
-  auto issue_stage = [&](int kt, int buf) {
-#pragma unroll
-    for (int q = 0; q < C::LOADS; ++q) issue_one(kt, buf, q);
+  // number of loads issued for stage s (0 past the end)
+  auto loads_of = [&](int s) { return (s >= 0 && s < nk) ? NC + ((s % C::G) == 0 ? NSG : 0) : 0; };
+  // wait until at most n loads are outstanding (n is one of a few per-tile constants)
+  auto wait_outstanding = [&](int n) {
+    if (n >= 2 * NC + NSG) PACT_WAIT_VMCNT(2 * NC + NSG);
+    else if (n >= 2 * NC) PACT_WAIT_VMCNT(2 * NC);
+    else if (n >= NC + NSG) PACT_WAIT_VMCNT(NC + NSG);
+    else if (n >= NC) PACT_WAIT_VMCNT(NC);
+    else PACT_WAIT_VMCNT(0);
   };
 
-  // ---- fragments ----
+  // ---- fragments (two register sets) ----
   // step s (0, 1) of a stage: lane (i, h) holds row i's K = 64 s + 32 h .. + 32
-  // (16 bytes, chunk 2s + h of the row) and the scale of that block.
-  uint4 fa[2][WTM], fb[2][WTN];
-  uint32_t sa[WTM], sb[WTN], sa_n[WTM], sb_n[WTN];
-  auto read_frags = [&](const uint8_t* st, int s, int slot) {
-#pragma unroll
-    for (int i = 0; i < WTM; ++i) {
-      const int row = wm * (BM / 2) + i * 32 + li;
-      fa[slot][i] = *reinterpret_cast<const uint4*>(st + C::CODES + row * 64 + (((2 * s + h) ^ ((row >> 2) & 3)) << 4));
-    }
-#pragma unroll
-    for (int j = 0; j < WTN; ++j) {
-      const int row = BM + wn * (BN / 2) + j * 32 + li;
-      fb[slot][j] = *reinterpret_cast<const uint4*>(st + C::CODES + row * 64 + (((2 * s + h) ^ ((row >> 2) & 3)) << 4));
+  // (16 bytes, chunk 2s + h of the row) and the scale of that block; the scale
+  // dword of a row holds blocks 0..3 of the stage and is permuted so that
+  // byte 0 / 1 are the blocks of steps 0 / 1 (op_sel picks the byte).
+  uint4 fa[2][2][WTM], fb[2][2][WTN];
+  uint32_t wa[2][WTM], wb[2][WTN];          // raw scale dwords (permuted when used)
+  const uint32_t ssel = h ? 0x0c0c0301u : 0x0c0c0200u;
+  // read item q (0 .. NREAD-1) of stage s into register set R: per A row tile
+  // i the two code fragments and the scale dword, then the same per B tile j
+  constexpr int NREAD = 3 * (WTM + WTN);
+  auto read_item = [&](int s, auto set_tag, auto item_tag) {
+    constexpr int R = decltype(set_tag)::value;
+    constexpr int Q = decltype(item_tag)::value;
+    constexpr bool IS_A = Q < 3 * WTM;
+    constexpr int T = IS_A ? Q / 3 : (Q - 3 * WTM) / 3;       // tile index i or j
+    constexpr int PART = Q % 3;                                 // 0, 1: code fragment of step PART; 2: scale
+    const int row = IS_A ? wm * (BM / 2) + T * 32 + li : BM + wn * (BN / 2) + T * 32 + li;
+    if constexpr (PART < 2) {
+      const uint8_t* st = smem + (s & 3) * C::CODE_STAGE;
+      const uint4 v = *reinterpret_cast<const uint4*>(st + row * 64 + (((2 * PART + h) ^ ((row >> 2) & 3)) << 4));
+      if constexpr (IS_A) fa[R][PART][T] = v; else fb[R][PART][T] = v;
+    } else {
+      const uint8_t* sc = smem + C::SC_OFF + ((s / C::G) & 1) * C::SC_BYTES + (s % C::G) * 4;
+      const uint32_t v = *reinterpret_cast<const uint32_t*>(sc + row * C::SC_ROW);
+      if constexpr (IS_A) wa[R][T] = v; else wb[R][T] = v;
     }
   };
-  // scale dword of a row holds blocks 0..3 of the stage; lane half h needs
-  // blocks h (step 0) and 2 + h (step 1): moved to bytes 0 and 1
-  const uint32_t ssel = h ? 0x0c0c0301u : 0x0c0c0200u;
-  auto read_scales = [&](const uint8_t* st, uint32_t* a_out, uint32_t* b_out) {
-#pragma unroll
-    for (int i = 0; i < WTM; ++i) {
-      const uint32_t w = *reinterpret_cast<const uint32_t*>(st + C::SCALES + (wm * (BM / 2) + i * 32 + li) * 4);
-      a_out[i] = __builtin_amdgcn_perm(w, w, ssel);
-    }
-#pragma unroll
-    for (int j = 0; j < WTN; ++j) {
-      const uint32_t w = *reinterpret_cast<const uint32_t*>(st + C::SCALES + (BM + wn * (BN / 2) + j * 32 + li) * 4);
-      b_out[j] = __builtin_amdgcn_perm(w, w, ssel);
-    }
+  auto read_stage = [&](int s, auto set_tag) {
+    [&]<int... Q>(std::integer_sequence<int, Q...>) {
+      (read_item(s, set_tag, std::integral_constant<int, Q>{}), ...);
+    }(std::make_integer_sequence<int, NREAD>{});
   };
 
   floatx16 acc[WTM][WTN];
@@ -289,70 +324,84 @@ __global__ __launch_bounds__(256, 1) void k_gemm_mxfp4(MxGemmArgs p, int tiles_m
     v8i_t r = {(int)q.x, (int)q.y, (int)q.z, (int)q.w, 0, 0, 0, 0};
     return r;
   };
-  // MFMAs of step s (scale byte s), optionally with the loads of stage dma_kt
-  // into buffer dma_buf spread one per MFMA
-  auto mfma_step = [&](int s, int slot, bool dma, int dma_kt, int dma_buf) {
-#pragma unroll
-    for (int k = 0; k < WTM * WTN; ++k) {
-      const int i = k / WTN, j = k % WTN;
-      if (s == 0)
-        acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(v8(fa[slot][i]), v8(fb[slot][j]), acc[i][j], 4, 4,
-                                                                    0, (int)sa[i], 0, (int)sb[j]);
-      else
-        acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(v8(fa[slot][i]), v8(fb[slot][j]), acc[i][j], 4, 4,
-                                                                    1, (int)sa[i], 1, (int)sb[j]);
-      if (dma && k < C::LOADS) issue_one(dma_kt, dma_buf, k);
-    }
-    if (dma) {
-#pragma unroll
-      for (int q = WTM * WTN; q < C::LOADS; ++q) issue_one(dma_kt, dma_buf, q);   // small tiles: the rest
-    }
-  };
 
-  // Stage kt lives in buffer kt % 4; its loads are issued during step 1 of
-  // stage kt - 4 (stages 0..3 in the prologue) and published by the barrier
-  // at step 1 of stage kt - 1, after which every wave has read stage kt - 1
-  // completely (its step-1 fragments were read during step 0).
-  auto wait_for_next = [&](int kt) {
-    // loads in flight: stages kt+1 .. min(kt+3, nk-1); keep all but the oldest
-    const int inflight = min(nk - 1, kt + 3) - kt;
-    if (inflight >= 3) PACT_WAIT_VMCNT(2 * C::LOADS);
-    else if (inflight == 2) PACT_WAIT_VMCNT(C::LOADS);
-    else PACT_WAIT_VMCNT(0);
-  };
-  auto run_stage = [&](int kt, auto dma_tag) {
-    constexpr bool DMA = decltype(dma_tag)::value;
-    const uint8_t* st = smem + (kt & 3) * C::STAGE;
-    // step 0
-    read_frags(st, 1, 1);
-    mfma_step(0, 0, false, 0, 0);
-    // step 1: publish stage kt + 1, refill buffer kt % 4 with stage kt + 4
-    __builtin_amdgcn_s_waitcnt(0xc07f);                    // lgkmcnt(0): this wave's reads of stage kt done
-    wait_for_next(kt);
+  // Stage kt: wait for stage kt + 1's loads (issued three stages earlier) and
+  // for this wave's reads of stage kt, barrier (stage kt + 1 published, buffer
+  // kt % 4 free), read stage kt + 1 into the other register set, multiply
+  // stage kt, and issue stage kt + 4's loads into buffer kt % 4, one per MFMA.
+  // MODE 0 .. G-1: steady state with kt % G == MODE (every count is a
+  // constant); MODE G: the last stages, with counts from kt.
+  auto run_stage = [&](int kt, auto set_tag, auto mode_tag) {
+    constexpr int R = decltype(set_tag)::value;
+    constexpr int MODE = decltype(mode_tag)::value;
+    if constexpr (MODE < C::G) {
+      constexpr int W = 2 * NC + (((MODE + 2) % C::G == 0 || (MODE + 3) % C::G == 0) ? NSG : 0);
+      PACT_WAIT_VMCNT(W);
+    } else {
+      wait_outstanding(loads_of(kt + 2) + loads_of(kt + 3));
+    }
+    __builtin_amdgcn_s_waitcnt(0xc07f);                    // lgkmcnt(0)
     __syncthreads();
-    const uint8_t* stn = smem + ((kt + 1) & 3) * C::STAGE;   // stale (in-bounds) after the last stage
-    read_frags(stn, 0, 0);
-    read_scales(stn, sa_n, sb_n);
-    mfma_step(1, 1, DMA, kt + 4, kt & 3);
+    uint32_t sa[WTM], sb[WTN];
 #pragma unroll
-    for (int i = 0; i < WTM; ++i) sa[i] = sa_n[i];
+    for (int i = 0; i < WTM; ++i) sa[i] = __builtin_amdgcn_perm(wa[R][i], wa[R][i], ssel);
 #pragma unroll
-    for (int j = 0; j < WTN; ++j) sb[j] = sb_n[j];
+    for (int j = 0; j < WTN; ++j) sb[j] = __builtin_amdgcn_perm(wb[R][j], wb[R][j], ssel);
+    // Stage kt's MFMAs with stage kt + 1's reads (past the last stage: stale,
+    // in-bounds, unused) and stage kt + 4's loads spread between them: a burst
+    // of LDS reads would stall the wave's in-order issue and starve the MFMAs.
+    const int nload = MODE < C::G ? NC + ((MODE + 4) % C::G == 0 ? NSG : 0) : (kt + 4 < nk ? loads_of(kt + 4) : 0);
+    constexpr int NMFMA = 2 * WTM * WTN;
+    [&]<int... K>(std::integer_sequence<int, K...>) {
+      ([&] {
+        constexpr int k = K % (WTM * WTN), st = K / (WTM * WTN);
+        constexpr int i = k / WTN, j = k % WTN;
+        acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(v8(fa[R][st][i]), v8(fb[R][st][j]), acc[i][j], 4, 4,
+                                                                    st, (int)sa[i], st, (int)sb[j]);
+        // read items r with r * NMFMA / NREAD == K follow MFMA K
+        constexpr int r0 = (K * NREAD + NMFMA - 1) / NMFMA, r1 = ((K + 1) * NREAD + NMFMA - 1) / NMFMA;
+        [&]<int... Rr>(std::integer_sequence<int, Rr...>) {
+          (read_item(kt + 1, std::integral_constant<int, R ^ 1>{}, std::integral_constant<int, r0 + Rr>{}), ...);
+        }(std::make_integer_sequence<int, r1 - r0>{});
+        // loads spread evenly: load q follows MFMA q * NMFMA / (NC + NSG)
+        constexpr int NL = NC + NSG;
+        constexpr int l0 = (K * NL + NMFMA - 1) / NMFMA, l1 = ((K + 1) * NL + NMFMA - 1) / NMFMA;
+        [&]<int... Ll>(std::integer_sequence<int, Ll...>) {
+          ((l0 + Ll < nload ? issue_one(kt + 4, l0 + Ll) : void()), ...);
+        }(std::make_integer_sequence<int, l1 - l0>{});
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);      // this MFMA
+        __builtin_amdgcn_sched_group_barrier(0x100, r1 - r0, 0);  // then its reads
+      }(), ...);
+    }(std::make_integer_sequence<int, NMFMA>{});
+    __builtin_amdgcn_sched_barrier(0);
   };
+  using I0 = std::integral_constant<int, 0>;
+  using I1 = std::integral_constant<int, 1>;
 
-  // prologue: stages 0..3 in flight, wait for stage 0
+  // prologue: stages 0..3 (and scale group 0) in flight; wait for stage 0
   const int pre = nk < 4 ? nk : 4;
-  for (int q = 0; q < pre; ++q) issue_stage(q, q);
-  if (pre >= 4) PACT_WAIT_VMCNT(3 * C::LOADS);
-  else if (pre == 3) PACT_WAIT_VMCNT(2 * C::LOADS);
-  else if (pre == 2) PACT_WAIT_VMCNT(C::LOADS);
+  for (int s = 0; s < pre; ++s) {
+    const int nl = loads_of(s);
+#pragma unroll
+    for (int q = 0; q < NC + NSG; ++q)
+      if (q < nl) issue_one(s, q);
+  }
+  if (pre >= 4) PACT_WAIT_VMCNT(3 * NC);      // stages 1..3 carry no scale group
+  else if (pre == 3) PACT_WAIT_VMCNT(2 * NC);
+  else if (pre == 2) PACT_WAIT_VMCNT(NC);
   else PACT_WAIT_VMCNT(0);
   __syncthreads();
-  read_frags(smem, 0, 0);
-  read_scales(smem, sa, sb);
+  read_stage(0, I0{});
   int kt = 0;
-  for (; kt + 4 < nk; ++kt) run_stage(kt, std::true_type{});
-  for (; kt < nk; ++kt) run_stage(kt, std::false_type{});
+  for (; kt + C::G + 4 <= nk; kt += C::G) {  // stages kt .. kt + G - 1 all issue loads
+    [&]<int... U>(std::integer_sequence<int, U...>) {
+      (run_stage(kt + U, std::integral_constant<int, U & 1>{}, std::integral_constant<int, U>{}), ...);
+    }(std::make_integer_sequence<int, C::G>{});
+  }
+  for (; kt < nk; kt += 2) {                 // kt is even here
+    run_stage(kt, I0{}, std::integral_constant<int, C::G>{});
+    if (kt + 1 < nk) run_stage(kt + 1, I1{}, std::integral_constant<int, C::G>{});
+  }
   PACT_WAIT_VMCNT(0);
 
   // ---- epilogue: optional accumulate, BF16 rounding, staged through LDS ----
