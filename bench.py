@@ -228,9 +228,10 @@ class MxLayer:
         return sum(4 * self.M * it["p"].d_in * it["p"].d_out for it in self.items)
 
 
-def mxfp4_leg(fw, torch, synth, wl, nlayers, steps, warmup):
+def mxfp4_leg(fw, torch, synth, wl, nlayers, steps, warmup, eager=False):
     """Throughput of the MXFP4 variant's GEMMs (same shapes, same rotation over
-    distinct layer instances, HIP-graph replays) and its dominant kernel."""
+    distinct layer instances, HIP-graph replays unless ``eager``) and its
+    dominant kernel."""
     from frozen_weight_gemms_amd import _lib
     layers = [MxLayer(fw, torch, synth, wl, li) for li in range(nlayers)]
 
@@ -241,20 +242,23 @@ def mxfp4_leg(fw, torch, synth, wl, nlayers, steps, warmup):
     for _ in range(warmup):
         step()
     torch.cuda.synchronize()
-    side = torch.cuda.Stream()
-    side.wait_stream(torch.cuda.current_stream())
-    with torch.cuda.stream(side):
-        step()
-    torch.cuda.current_stream().wait_stream(side)
-    torch.cuda.synchronize()
-    graph = torch.cuda.CUDAGraph()
-    with torch.cuda.graph(graph):
-        step()
-    graph.replay()
-    torch.cuda.synchronize()
+    run = step
+    if not eager:
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            step()
+        torch.cuda.current_stream().wait_stream(side)
+        torch.cuda.synchronize()
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            step()
+        graph.replay()
+        torch.cuda.synchronize()
+        run = graph.replay
     t0 = time.perf_counter()
     for _ in range(steps):
-        graph.replay()
+        run()
     torch.cuda.synchronize()
     ms = (time.perf_counter() - t0) * 1e3 / steps
     recs = []
@@ -276,16 +280,26 @@ def mxfp4_leg(fw, torch, synth, wl, nlayers, steps, warmup):
     flops = sum(ly.gemm_flops() for ly in layers)
     gemm_ms = sum(v[0] for v in by_tile.values()) / steps
     value = flops / (ms * 1e-3) / 1e12
-    del layers, graph
+    del layers, run
     torch.cuda.synchronize()
+    kname = f"pact::k_gemm_mxfp4<{dom[0] // 64}, {dom[1] // 64}>"
+    traffic = None
+    tfile = os.path.join(ROOT, "profiles", "mxfp4_gemm_traffic.json")
+    if os.path.exists(tfile):
+        try:
+            tj = json.load(open(tfile))
+            if tj.get("src_hash") == src_hash("mxfp4.hip", "lds_dma.h") and tj.get("kernel") == kname:
+                traffic = tj.get("bytes_per_launch")
+        except (ValueError, OSError):
+            traffic = None
     return {"gemm_tflops": round(value, 1), "frac_fp4_peak": round(value / PEAK["fp4_mfma_tflops"], 4),
             "ms_per_step": round(ms, 4), "layers": nlayers,
             "gemm_only_tflops_events": round(flops / (gemm_ms * 1e-3) / 1e12, 1),
-            "timed_region": "hip graph replays of 14 MXFP4 GEMMs per layer",
-            "roofline": {"kernel": f"pact::k_gemm_mxfp4<{dom[0] // 64}, {dom[1] // 64}>", "bound": "mfma",
+            "timed_region": ("eager" if eager else "hip graph replays") + " of 14 MXFP4 GEMMs per layer",
+            "roofline": {"kernel": kname, "bound": "mfma",
                          "achieved": round(ach, 1), "peak": PEAK["fp4_mfma_tflops"], "unit": "TFLOP/s",
                          "frac": round(ach / PEAK["fp4_mfma_tflops"], 4), "launches_per_step": dn // steps,
-                         "avg_launch_us": round(dt * 1e3 / dn, 2)}}
+                         "avg_launch_us": round(dt * 1e3 / dn, 2), "traffic": traffic}}
 
 
 # algorithmic bytes per element of each bandwidth-bound kernel (inputs read + outputs written)
@@ -502,7 +516,8 @@ def main():
     }
     if not args.no_mxfp4:
         del graph
-        result["mxfp4_variant"] = mxfp4_leg(fw, torch, synth, wl, max(1, args.layers), args.steps, args.warmup)
+        result["mxfp4_variant"] = mxfp4_leg(fw, torch, synth, wl, max(1, args.layers), args.steps, args.warmup,
+                                            eager=args.eager)
     if args.copy_calibration:
         x = torch.empty(1 << 29, dtype=torch.bfloat16, device="cuda")   # 1 GiB
         y = torch.empty_like(x)
