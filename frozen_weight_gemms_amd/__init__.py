@@ -56,6 +56,12 @@ def _bf16(t: torch.Tensor, name: str) -> torch.Tensor:
     return t
 
 
+def _dense(t: torch.Tensor, name: str) -> torch.Tensor:
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous (dense rows)")
+    return t
+
+
 def empty_nvfp4(rows: int, cols: int, device="cuda") -> NVFP4Tensor:
     if cols % 16:
         raise ValueError("cols must be a multiple of 16")
@@ -190,7 +196,7 @@ def lora_bwd(xq: NVFP4Tensor, A: torch.Tensor, B: torch.Tensor, dy: torch.Tensor
 
 
 def silu_mul_bwd(gq: NVFP4Tensor, uq: NVFP4Tensor, dh: torch.Tensor, out=None):
-    _bf16(dh, "dh")
+    _dense(_bf16(dh, "dh"), "dh")
     M, I = dh.shape
     dg, du = out if out is not None else (torch.empty_like(dh), torch.empty_like(dh))
     _lib.call("silu_mul_bwd", *gq.ptrs(), *uq.ptrs(), dh.data_ptr(), M, I, dg.data_ptr(), du.data_ptr(), _stream())
@@ -198,12 +204,42 @@ def silu_mul_bwd(gq: NVFP4Tensor, uq: NVFP4Tensor, dh: torch.Tensor, out=None):
 
 
 def rmsnorm_bwd(yq: NVFP4Tensor, rstd: torch.Tensor, gain: torch.Tensor, dy: torch.Tensor, out=None):
-    _bf16(gain, "gain"); _bf16(dy, "dy")
+    _bf16(gain, "gain"); _dense(_bf16(dy, "dy"), "dy")
     M, H = dy.shape
     dx = out if out is not None else torch.empty_like(dy)
     _lib.call("rmsnorm_bwd", *yq.ptrs(), rstd.data_ptr(), gain.data_ptr(), dy.data_ptr(), M, H, dx.data_ptr(),
               _stream())
     return dx
+
+
+def silu_mul_bwd_quant(gq: NVFP4Tensor, uq: NVFP4Tensor, dh: torch.Tensor, out=None):
+    """(dgate, dup, Q(dgate), Q(dup)): silu_mul_bwd plus the NVFP4 copies of its outputs."""
+    _dense(_bf16(dh, "dh"), "dh")
+    M, I = dh.shape
+    if out is None:
+        out = (torch.empty_like(dh), torch.empty_like(dh), empty_nvfp4(M, I, dh.device), empty_nvfp4(M, I, dh.device))
+    dg, du, dgq, duq = out
+    _lib.call("silu_mul_bwd_quant", *gq.ptrs(), *uq.ptrs(), dh.data_ptr(), M, I, dg.data_ptr(), du.data_ptr(),
+              *dgq.ptrs(), *duq.ptrs(), _stream())
+    return dg, du, dgq, duq
+
+
+def rmsnorm_bwd_residual(yq: NVFP4Tensor, rstd: torch.Tensor, gain: torch.Tensor, dy: torch.Tensor,
+                         resid: torch.Tensor | None = None, quantize_out: bool = True, out=None):
+    """(out, Q(out) or None) with out = bf16(bf16(rmsnorm_bwd) + resid)."""
+    _bf16(gain, "gain"); _dense(_bf16(dy, "dy"), "dy")
+    if resid is not None:
+        _dense(_bf16(resid, "resid"), "resid")
+        if resid.shape != dy.shape:
+            raise ValueError("resid must have dy's shape")
+    M, H = dy.shape
+    if out is None:
+        out = (torch.empty_like(dy), empty_nvfp4(M, H, dy.device) if quantize_out else None)
+    dx, q = out
+    qp = q.ptrs() if q is not None else (0, 0, 0)
+    _lib.call("rmsnorm_bwd_residual", *yq.ptrs(), rstd.data_ptr(), gain.data_ptr(), dy.data_ptr(),
+              resid.data_ptr() if resid is not None else 0, M, H, dx.data_ptr(), *qp, _stream())
+    return dx, q
 
 
 # ---------------------------------------------------------------------------

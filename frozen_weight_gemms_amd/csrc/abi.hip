@@ -69,7 +69,7 @@ extern "C" {
 
 const char* pact_last_error(void) { return g_err; }
 
-int pact_abi_version(void) { return 2; }
+int pact_abi_version(void) { return 3; }
 
 int pact_nvfp4_sizes(int64_t rows, int64_t cols, size_t* codes_bytes, size_t* scales_bytes, size_t* rscale_bytes) {
   REQUIRE(rows >= 0 && cols >= 0, PACT_EINVAL, "negative size (rows=%lld, cols=%lld)", (long long)rows,
@@ -284,9 +284,54 @@ int rmsnorm_bwd(const uint8_t* y_codes, const uint8_t* y_scales, const float* y_
   REQUIRE_PTR(dy, "dy");
   REQUIRE_PTR(dx, "dx");
   REQUIRE(M <= 0x7FFFFFFF, PACT_EUNSUPPORTED, "M too large");
-  return hip_status(pact::launch_rmsnorm_bwd(y_codes, y_scales, y_rscale, rstd, gain, dy, M, H, dx,
-                                             as_stream(stream)),
+  return hip_status(pact::launch_rmsnorm_bwd(y_codes, y_scales, y_rscale, rstd, gain, dy, M, H, nullptr, dx,
+                                             nullptr, nullptr, nullptr, as_stream(stream)),
                     "rmsnorm_bwd launch");
+}
+
+int silu_mul_bwd_quant(const uint8_t* g_codes, const uint8_t* g_scales, const float* g_rscale,
+                       const uint8_t* u_codes, const uint8_t* u_scales, const float* u_rscale, const uint16_t* dh,
+                       int64_t M, int64_t I, uint16_t* dgate, uint16_t* dup, uint8_t* dg_codes, uint8_t* dg_scales,
+                       float* dg_rscale, uint8_t* du_codes, uint8_t* du_scales, float* du_rscale, void* stream) {
+  REQUIRE(M >= 0 && I >= 0, PACT_EINVAL, "negative size");
+  REQUIRE(I % 16 == 0, PACT_ESHAPE, "I=%lld is not a multiple of 16", (long long)I);
+  REQUIRE(I <= kMaxFusedCols, PACT_EUNSUPPORTED, "I=%lld exceeds %lld", (long long)I, (long long)kMaxFusedCols);
+  if (M == 0 || I == 0) return ok();
+  int st = check_nvfp4(g_codes, g_scales, g_rscale, "gate_q");
+  if (st == PACT_OK) st = check_nvfp4(u_codes, u_scales, u_rscale, "up_q");
+  if (st == PACT_OK) st = check_nvfp4(dg_codes, dg_scales, dg_rscale, "dgate_q");
+  if (st == PACT_OK) st = check_nvfp4(du_codes, du_scales, du_rscale, "dup_q");
+  if (st != PACT_OK) return st;
+  REQUIRE_PTR(dh, "dh");
+  REQUIRE_PTR(dgate, "dgate");
+  REQUIRE_PTR(dup, "dup");
+  REQUIRE(M <= 0x7FFFFFFF, PACT_EUNSUPPORTED, "M too large");
+  return hip_status(pact::launch_silu_mul_bwd_quant(g_codes, g_scales, g_rscale, u_codes, u_scales, u_rscale, dh, M,
+                                                    I, dgate, dup, dg_codes, dg_scales, dg_rscale, du_codes,
+                                                    du_scales, du_rscale, as_stream(stream)),
+                    "silu_mul_bwd_quant launch");
+}
+
+int rmsnorm_bwd_residual(const uint8_t* y_codes, const uint8_t* y_scales, const float* y_rscale, const float* rstd,
+                         const uint16_t* gain, const uint16_t* dy, const uint16_t* resid, int64_t M, int64_t H,
+                         uint16_t* dx, uint8_t* q_codes, uint8_t* q_scales, float* q_rscale, void* stream) {
+  REQUIRE(M >= 0 && H >= 0, PACT_EINVAL, "negative size");
+  REQUIRE(H % 16 == 0, PACT_ESHAPE, "H=%lld is not a multiple of 16", (long long)H);
+  REQUIRE(H <= kMaxFusedCols, PACT_EUNSUPPORTED, "H=%lld exceeds %lld", (long long)H, (long long)kMaxFusedCols);
+  const bool want_q = q_codes != nullptr || q_scales != nullptr || q_rscale != nullptr;
+  if (M == 0 || H == 0) return ok();
+  int st = check_nvfp4(y_codes, y_scales, y_rscale, "y");
+  if (st == PACT_OK && want_q) st = check_nvfp4(q_codes, q_scales, q_rscale, "out_q");
+  if (st != PACT_OK) return st;
+  REQUIRE_PTR(rstd, "rstd");
+  REQUIRE_PTR(gain, "gain");
+  REQUIRE_PTR(dy, "dy");
+  REQUIRE_PTR(dx, "dx");
+  if (resid != nullptr) REQUIRE_PTR(resid, "resid");
+  REQUIRE(M <= 0x7FFFFFFF, PACT_EUNSUPPORTED, "M too large");
+  return hip_status(pact::launch_rmsnorm_bwd(y_codes, y_scales, y_rscale, rstd, gain, dy, M, H, resid, dx,
+                                             want_q ? q_codes : nullptr, q_scales, q_rscale, as_stream(stream)),
+                    "rmsnorm_bwd_residual launch");
 }
 
 

@@ -1,15 +1,56 @@
 // SiLU-multiply and RMSNorm backward from the saved NVFP4 state (PACT,
 // Appendix Table 7: "FP32 reconstruction and derivatives, BF16 gradients" for
 // SiLU-multiply; "FP32 reconstruction and reduction, BF16 gradient" for
-// RMSNorm).  Both are HBM-bound elementwise / row-reduction kernels.
+// RMSNorm; residuals: "BF16 gradient accumulation").  HBM-bound elementwise /
+// row-reduction kernels.
 //
-//   silu_mul_bwd: a^ = deq(gate_q), b^ = deq(up_q), sigma = 1/(1+e^-a^)
-//                 dgate = dh b^ sigma (1 + a^ (1 - sigma)),  dup = dh a^ sigma
-//   rmsnorm_bwd:  y^ = deq(y_q)
-//                 dx = rstd (g dy - (y^ / g) (1/H) sum_j dy_j y^_j)
+//   silu_mul_bwd: a^ = deq(gate_q), b^ = deq(up_q), sigma = 1/(1+E(-a^))
+//                 dgate = ((dh b^) sigma) (1 + a^ (1 - sigma)),  dup = (dh a^) sigma
+//   rmsnorm_bwd:  y^ = deq(y_q), S = sum_j dy_j y^_j (exact, rounded once to
+//                 float64), mean = fp32(S / H)
+//                 dx = rstd ((g dy) - ((y^ / g) mean))
+// Every FP32 step is one IEEE round-to-nearest operation in the order written
+// (no contraction), and E is the pinned exponential of the forward SiLU, so the
+// BF16 gradients are reproducible bit for bit.
+//
+// The quantize-on-emit variants also write the NVFP4 copy of what they store
+// (the input of the next input-gradient GEMM): silu_mul_bwd_quant emits
+// Q(dgate), Q(dup) next to the BF16 gradients the LoRA backward needs, and
+// rmsnorm_bwd_residual adds the incoming residual gradient in BF16
+// (out = bf16(bf16(dx) + resid)) and can emit Q(out).
 #include "pact_internal.h"
+#include "row_ops.h"
 
 namespace pact {
+
+__device__ __forceinline__ void silu_bwd_elem(float a, float b, float d, float& da, float& db) {
+  const float sig = sigmoid_pinned(a);
+  const float t = __fmul_rn(__fmul_rn(d, b), sig);
+  const float w = __fadd_rn(1.0f, __fmul_rn(a, __fsub_rn(1.0f, sig)));
+  da = __fmul_rn(t, w);
+  db = __fmul_rn(__fmul_rn(d, a), sig);
+}
+
+// Decode one chunk of a and b, load dh, and form the BF16 gradients (packed).
+__device__ __forceinline__ void silu_bwd_chunk(uint32_t wa, float ma, uint32_t wb, float mb, const uint4& vd,
+                                               uint4& oa, uint4& ob) {
+  float a[8], b[8], d[8], da[8], db[8];
+  decode8_f32(wa, ma, a);
+  decode8_f32(wb, mb, b);
+  unpack_bf16x8(vd, d);
+#pragma unroll
+  for (int t = 0; t < 8; ++t) silu_bwd_elem(a[t], b[t], d[t], da[t], db[t]);
+  oa.x = pack_bf16x2(da[0], da[1]); oa.y = pack_bf16x2(da[2], da[3]);
+  oa.z = pack_bf16x2(da[4], da[5]); oa.w = pack_bf16x2(da[6], da[7]);
+  ob.x = pack_bf16x2(db[0], db[1]); ob.y = pack_bf16x2(db[2], db[3]);
+  ob.z = pack_bf16x2(db[4], db[5]); ob.w = pack_bf16x2(db[6], db[7]);
+}
+
+__device__ __forceinline__ float absmax_bf16x8(const uint4& v) {
+  float f[8];
+  unpack_bf16x8(v, f);
+  return absmax8(f);
+}
 
 // One thread per 8-element chunk (one 32-bit word of codes).
 __global__ __launch_bounds__(256) void k_silu_mul_bwd(const uint8_t* __restrict__ gc, const uint8_t* __restrict__ gs,
@@ -22,78 +63,144 @@ __global__ __launch_bounds__(256) void k_silu_mul_bwd(const uint8_t* __restrict_
   for (int64_t q = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; q < total; q += (int64_t)gridDim.x * blockDim.x) {
     const int64_t row = q / nchunk_row, c = q - row * nchunk_row;
     const int64_t e0 = row * I + 8 * c;
-    const uint32_t wa = reinterpret_cast<const uint32_t*>(gc)[q];
-    const uint32_t wb = reinterpret_cast<const uint32_t*>(uc)[q];
-    const float ma = __builtin_amdgcn_cvt_f32_fp8((int)gs[row * (I >> 4) + (c >> 1)], 0) * gr[row];
-    const float mb = __builtin_amdgcn_cvt_f32_fp8((int)us[row * (I >> 4) + (c >> 1)], 0) * ur[row];
-    float a[8], b[8], d[8];
-    decode8_f32(wa, ma, a);
-    decode8_f32(wb, mb, b);
-    unpack_bf16x8(*reinterpret_cast<const uint4*>(dh + e0), d);
-    float da[8], db[8];
-#pragma unroll
-    for (int t = 0; t < 8; ++t) {
-      const float en = expf(-fabsf(a[t]));                 // no overflow for either sign
-      const float sig = a[t] >= 0.0f ? 1.0f / (1.0f + en) : en / (1.0f + en);
-      const float tt = 1.0f + a[t] * (1.0f - sig);
-      da[t] = ((d[t] * b[t]) * sig) * tt;
-      db[t] = (d[t] * a[t]) * sig;
-    }
+    const float ma = e4m3_decode(gs[row * (I >> 4) + (c >> 1)]) * gr[row];
+    const float mb = e4m3_decode(us[row * (I >> 4) + (c >> 1)]) * ur[row];
     uint4 oa, ob;
-    oa.x = pack_bf16x2(da[0], da[1]); oa.y = pack_bf16x2(da[2], da[3]);
-    oa.z = pack_bf16x2(da[4], da[5]); oa.w = pack_bf16x2(da[6], da[7]);
-    ob.x = pack_bf16x2(db[0], db[1]); ob.y = pack_bf16x2(db[2], db[3]);
-    ob.z = pack_bf16x2(db[4], db[5]); ob.w = pack_bf16x2(db[6], db[7]);
+    silu_bwd_chunk(reinterpret_cast<const uint32_t*>(gc)[q], ma, reinterpret_cast<const uint32_t*>(uc)[q], mb,
+                   load16(dh + e0), oa, ob);
     *reinterpret_cast<uint4*>(dgate + e0) = oa;
     *reinterpret_cast<uint4*>(dup + e0) = ob;
   }
 }
 
-// One 256-thread workgroup per row; NCH 8-element chunks per thread in registers.
+// silu_mul_bwd with NVFP4 copies of both gradients: one 256-thread workgroup
+// per row, NCH chunks per thread kept (as BF16) in registers until the row
+// maxima are known.
+template <int NCH>
+__global__ __launch_bounds__(256) void k_silu_mul_bwd_quant(
+    const uint8_t* __restrict__ gc, const uint8_t* __restrict__ gs, const float* __restrict__ gr,
+    const uint8_t* __restrict__ uc, const uint8_t* __restrict__ us, const float* __restrict__ ur,
+    const uint16_t* __restrict__ dh, int64_t I, uint16_t* __restrict__ dgate, uint16_t* __restrict__ dup,
+    uint8_t* __restrict__ qgc, uint8_t* __restrict__ qgs, float* __restrict__ qgr, uint8_t* __restrict__ quc,
+    uint8_t* __restrict__ qus, float* __restrict__ qur) {
+  __shared__ float red[4];
+  const int64_t row = blockIdx.x;
+  const int nchunk = (int)(I >> 3);
+  const float rg = gr[row], ru = ur[row];
+  uint4 oa[NCH], ob[NCH];
+  float la = 0.0f, lb = 0.0f;
+#pragma unroll
+  for (int i = 0; i < NCH; ++i) {
+    const int c = threadIdx.x + 256 * i;
+    if (c < nchunk) {
+      const int64_t q = row * nchunk + c;
+      const float ma = e4m3_decode(gs[row * (I >> 4) + (c >> 1)]) * rg;
+      const float mb = e4m3_decode(us[row * (I >> 4) + (c >> 1)]) * ru;
+      silu_bwd_chunk(reinterpret_cast<const uint32_t*>(gc)[q], ma, reinterpret_cast<const uint32_t*>(uc)[q], mb,
+                     load16(dh + row * I + 8 * c), oa[i], ob[i]);
+      *reinterpret_cast<uint4*>(dgate + row * I + 8 * c) = oa[i];
+      *reinterpret_cast<uint4*>(dup + row * I + 8 * c) = ob[i];
+      la = fmaxf(la, absmax_bf16x8(oa[i]));
+      lb = fmaxf(lb, absmax_bf16x8(ob[i]));
+    } else {
+      oa[i] = make_uint4(0, 0, 0, 0);
+      ob[i] = make_uint4(0, 0, 0, 0);
+    }
+  }
+  const float amax_a = block_max_256(la, red);
+  const float amax_b = block_max_256(lb, red);
+  const int ea = row_exponent(amax_a), eb = row_exponent(amax_b);
+  const float ra = pow2f(ea), ira = pow2f(-ea), rb = pow2f(eb), irb = pow2f(-eb);
+#pragma unroll
+  for (int i = 0; i < NCH; ++i) {
+    const int c = threadIdx.x + 256 * i;
+    float f[8];
+    unpack_bf16x8(oa[i], f);
+    quant_chunk(f, c < nchunk, ra, ira, qgc + row * (I >> 1), qgs + row * (I >> 4), c);
+    unpack_bf16x8(ob[i], f);
+    quant_chunk(f, c < nchunk, rb, irb, quc + row * (I >> 1), qus + row * (I >> 4), c);
+  }
+  if (threadIdx.x == 0) {
+    qgr[row] = ra;
+    qur[row] = rb;
+  }
+}
+
+// RMSNorm backward, optionally + residual gradient and + NVFP4 copy of the
+// result.  One 256-thread workgroup per row; NCH 8-element chunks per thread.
 template <int NCH>
 __global__ __launch_bounds__(256) void k_rmsnorm_bwd(const uint8_t* __restrict__ yc, const uint8_t* __restrict__ ys,
                                                      const float* __restrict__ yr, const float* __restrict__ rstd,
                                                      const uint16_t* __restrict__ gain, const uint16_t* __restrict__ dy,
-                                                     int64_t H, uint16_t* __restrict__ dx) {
-  __shared__ double red[4];
+                                                     int64_t H, const uint16_t* __restrict__ resid,
+                                                     uint16_t* __restrict__ dx, uint8_t* __restrict__ qc,
+                                                     uint8_t* __restrict__ qs, float* __restrict__ qr) {
+  __shared__ double dred[2][4];
+  __shared__ float red[4];
   const int64_t row = blockIdx.x;
   const int nchunk = (int)(H >> 3);
   float y[NCH][8], d[NCH][8];
-  double dot = 0.0;
+  double sh = 0.0, sl = 0.0;                   // double-double partial of sum dy y^ (each product exact)
   const float rr = yr[row];
 #pragma unroll
   for (int i = 0; i < NCH; ++i) {
     const int c = threadIdx.x + 256 * i;
     if (c < nchunk) {
       const uint32_t w = *reinterpret_cast<const uint32_t*>(yc + row * (H >> 1) + 4 * c);
-      const float m = __builtin_amdgcn_cvt_f32_fp8((int)ys[row * (H >> 4) + (c >> 1)], 0) * rr;
-      decode8_f32(w, m, y[i]);
-      unpack_bf16x8(*reinterpret_cast<const uint4*>(dy + row * H + 8 * c), d[i]);
+      decode8_f32(w, e4m3_decode(ys[row * (H >> 4) + (c >> 1)]) * rr, y[i]);
+      unpack_bf16x8(load16(dy + row * H + 8 * c), d[i]);
     } else {
 #pragma unroll
       for (int t = 0; t < 8; ++t) { y[i][t] = 0.0f; d[i][t] = 0.0f; }
     }
 #pragma unroll
-    for (int t = 0; t < 8; ++t) dot += (double)d[i][t] * (double)y[i][t];
+    for (int t = 0; t < 8; ++t) {
+      double s, e;
+      two_sum(sh, (double)d[i][t] * (double)y[i][t], s, e);
+      sh = s;
+      sl += e;
+    }
   }
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) dot += __shfl_xor(dot, o, 64);
-  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = dot;
-  __syncthreads();
-  const float mean = (float)(((red[0] + red[1]) + (red[2] + red[3])) / (double)H);
+  const double S = block_sum_dd(sh, sl, dred);
+  const float mean = (float)(S / (double)H);
   const float rs = rstd[row];
+  uint4 out[NCH];
+  float lmax = 0.0f;
 #pragma unroll
   for (int i = 0; i < NCH; ++i) {
     const int c = threadIdx.x + 256 * i;
+    out[i] = make_uint4(0, 0, 0, 0);
     if (c >= nchunk) continue;
     float g[8], o[8];
-    unpack_bf16x8(*reinterpret_cast<const uint4*>(gain + 8 * c), g);
+    unpack_bf16x8(load16(gain + 8 * c), g);
 #pragma unroll
-    for (int t = 0; t < 8; ++t) o[t] = rs * (g[t] * d[i][t] - (y[i][t] / g[t]) * mean);
+    for (int t = 0; t < 8; ++t)
+      o[t] = __fmul_rn(rs, __fsub_rn(__fmul_rn(g[t], d[i][t]), __fmul_rn(__fdiv_rn(y[i][t], g[t]), mean)));
+    if (resid != nullptr) {
+      float rv[8];
+      unpack_bf16x8(load16(resid + row * H + 8 * c), rv);
+#pragma unroll
+      for (int t = 0; t < 8; ++t) o[t] = __fadd_rn(__uint_as_float(f32_to_bf16_rne(o[t]) << 16), rv[t]);
+    }
     uint4 v;
     v.x = pack_bf16x2(o[0], o[1]); v.y = pack_bf16x2(o[2], o[3]);
     v.z = pack_bf16x2(o[4], o[5]); v.w = pack_bf16x2(o[6], o[7]);
     *reinterpret_cast<uint4*>(dx + row * H + 8 * c) = v;
+    out[i] = v;
+    lmax = fmaxf(lmax, absmax_bf16x8(v));
+  }
+  if (qc != nullptr) {                         // uniform: a kernel argument
+    const float amax = block_max_256(lmax, red);
+    const int e = row_exponent(amax);
+    const float r = pow2f(e), ir = pow2f(-e);
+#pragma unroll
+    for (int i = 0; i < NCH; ++i) {
+      const int c = threadIdx.x + 256 * i;
+      float f[8];
+      unpack_bf16x8(out[i], f);
+      quant_chunk(f, c < nchunk, r, ir, qc + row * (H >> 1), qs + row * (H >> 4), c);
+    }
+    if (threadIdx.x == 0) qr[row] = r;
   }
 }
 
@@ -107,16 +214,35 @@ hipError_t launch_silu_mul_bwd(const uint8_t* gc, const uint8_t* gs, const float
   return hipGetLastError();
 }
 
+hipError_t launch_silu_mul_bwd_quant(const uint8_t* gc, const uint8_t* gs, const float* gr, const uint8_t* uc,
+                                     const uint8_t* us, const float* ur, const uint16_t* dh, int64_t M, int64_t I,
+                                     uint16_t* dgate, uint16_t* dup, uint8_t* qgc, uint8_t* qgs, float* qgr,
+                                     uint8_t* quc, uint8_t* qus, float* qur, hipStream_t s) {
+  const int nch = (int)(((I >> 3) + 255) / 256);
+  const dim3 grid((unsigned)M);
+#define PACT_SMBQ(n) k_silu_mul_bwd_quant<n><<<grid, 256, 0, s>>>(gc, gs, gr, uc, us, ur, dh, I, dgate, dup, qgc, qgs, qgr, quc, qus, qur)
+  if (nch <= 1) PACT_SMBQ(1);
+  else if (nch <= 2) PACT_SMBQ(2);
+  else if (nch <= 4) PACT_SMBQ(4);
+  else if (nch <= 8) PACT_SMBQ(8);
+  else return hipErrorInvalidValue;
+#undef PACT_SMBQ
+  return hipGetLastError();
+}
+
 hipError_t launch_rmsnorm_bwd(const uint8_t* yc, const uint8_t* ys, const float* yr, const float* rstd,
-                              const uint16_t* gain, const uint16_t* dy, int64_t M, int64_t H, uint16_t* dx,
+                              const uint16_t* gain, const uint16_t* dy, int64_t M, int64_t H,
+                              const uint16_t* resid, uint16_t* dx, uint8_t* qc, uint8_t* qs, float* qr,
                               hipStream_t s) {
   const int nch = (int)(((H >> 3) + 255) / 256);
   const dim3 grid((unsigned)M);
-  if (nch <= 1) k_rmsnorm_bwd<1><<<grid, 256, 0, s>>>(yc, ys, yr, rstd, gain, dy, H, dx);
-  else if (nch <= 2) k_rmsnorm_bwd<2><<<grid, 256, 0, s>>>(yc, ys, yr, rstd, gain, dy, H, dx);
-  else if (nch <= 4) k_rmsnorm_bwd<4><<<grid, 256, 0, s>>>(yc, ys, yr, rstd, gain, dy, H, dx);
-  else if (nch <= 8) k_rmsnorm_bwd<8><<<grid, 256, 0, s>>>(yc, ys, yr, rstd, gain, dy, H, dx);
+#define PACT_RMSB(n) k_rmsnorm_bwd<n><<<grid, 256, 0, s>>>(yc, ys, yr, rstd, gain, dy, H, resid, dx, qc, qs, qr)
+  if (nch <= 1) PACT_RMSB(1);
+  else if (nch <= 2) PACT_RMSB(2);
+  else if (nch <= 4) PACT_RMSB(4);
+  else if (nch <= 8) PACT_RMSB(8);
   else return hipErrorInvalidValue;
+#undef PACT_RMSB
   return hipGetLastError();
 }
 

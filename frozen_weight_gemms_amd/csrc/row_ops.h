@@ -1,0 +1,109 @@
+// Device helpers for the row-per-workgroup kernels (quantizers, fused forward
+// and backward kernels): workgroup reductions, the per-chunk NVFP4 encoder,
+// an error-free float64 sum and the pinned FP32 exponential.
+#pragma once
+
+#include "nvfp4_device.h"
+
+namespace pact {
+
+constexpr int kThreads = 256;
+
+__device__ __forceinline__ float block_max_256(float v, float* red) {
+  v = wave_max(v);
+  const int w = threadIdx.x >> 6;
+  if ((threadIdx.x & 63) == 0) red[w] = v;
+  __syncthreads();
+  const float r = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+  __syncthreads();
+  return r;
+}
+
+__device__ __forceinline__ uint4 load16(const uint16_t* p) { return *reinterpret_cast<const uint4*>(p); }
+
+// Quantize one chunk (8 floats) of a row whose exponent is known.  Both lanes
+// of the pair must call this (it exchanges the chunk amax with lane ^ 1).
+__device__ __forceinline__ void quant_chunk(const float* x, bool valid, float r, float inv_r,
+                                            uint8_t* codes_row, uint8_t* scales_row, int c) {
+  float m = valid ? absmax8(x) : 0.0f;
+  m = fmaxf(m, __shfl_xor(m, 1, 64));
+  if (!valid) return;
+  const BlockQ q = block_setup(m, r, inv_r);
+  const uint32_t w = encode8(x, q);
+  *reinterpret_cast<uint32_t*>(codes_row + 4 * (int64_t)c) = w;
+  if ((c & 1) == 0) scales_row[c >> 1] = (uint8_t)q.sc;
+}
+
+// Error-free sum of two doubles.
+__device__ __forceinline__ void two_sum(double a, double b, double& s, double& e) {
+  s = a + b;
+  const double bb = s - a;
+  e = (a - (s - bb)) + (b - bb);
+}
+
+// FP32 exponential: Cody-Waite reduction with ln 2 split in two (the high part
+// has 16 significant bits, so n * LN2_HI is exact for |n| <= 128), then the
+// degree-7 Taylor polynomial of e^r in Horner form, every step an IEEE
+// round-to-nearest operation with no contraction.
+//   L2E    = RN32(1 / ln 2)          = 0x3FB8AA3B
+//   LN2_HI = ln 2 to 16 significant bits = 0x3F317200
+//   LN2_LO = RN32(ln 2 - LN2_HI)     = 0x35BFBE8E
+//   C_k    = RN32(1 / k!)            k = 2..7: 0x3F000000 0x3E2AAAAB 0x3D2AAAAB 0x3C088889 0x3AB60B61 0x39500D01
+__device__ __forceinline__ float exp_pinned(float x) {
+  const float L2E = __uint_as_float(0x3FB8AA3Bu);
+  const float LN2_HI = __uint_as_float(0x3F317200u);
+  const float LN2_LO = __uint_as_float(0x35BFBE8Eu);
+  const float xc = fminf(fmaxf(x, -80.0f), 89.0f);
+  const float n = rintf(__fmul_rn(xc, L2E));
+  const float rr = __fsub_rn(__fsub_rn(xc, __fmul_rn(n, LN2_HI)), __fmul_rn(n, LN2_LO));
+  float p = __uint_as_float(0x39500D01u);                         // 1/7!
+  p = __fadd_rn(__fmul_rn(p, rr), __uint_as_float(0x3AB60B61u));  // 1/6!
+  p = __fadd_rn(__fmul_rn(p, rr), __uint_as_float(0x3C088889u));  // 1/5!
+  p = __fadd_rn(__fmul_rn(p, rr), __uint_as_float(0x3D2AAAABu));  // 1/4!
+  p = __fadd_rn(__fmul_rn(p, rr), __uint_as_float(0x3E2AAAABu));  // 1/3!
+  p = __fadd_rn(__fmul_rn(p, rr), 0.5f);
+  p = __fadd_rn(__fmul_rn(p, rr), 1.0f);
+  p = __fadd_rn(__fmul_rn(p, rr), 1.0f);
+  float e = __builtin_ldexpf(p, (int)n);
+  e = x < -80.0f ? 0.0f : e;
+  e = x > 89.0f ? __builtin_huge_valf() : e;
+  return e;
+}
+
+// sigma(a) = 1 / (1 + E(-a)) in the pinned FP32 sequence (0 when E overflows).
+__device__ __forceinline__ float sigmoid_pinned(float a) {
+  return __fdiv_rn(1.0f, __fadd_rn(1.0f, exp_pinned(-a)));
+}
+
+__device__ __forceinline__ float silu_mul(float a, float b) {
+  const float sig = sigmoid_pinned(a);
+  return __fmul_rn(__fmul_rn(a, sig), b);
+}
+
+// Workgroup (256 threads) sum of per-thread double-double partials (sh, sl),
+// returned rounded once to float64.  dred: __shared__ double[2][4].
+__device__ __forceinline__ double block_sum_dd(double sh, double sl, double (*dred)[4]) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) {
+    const double oh = __shfl_xor(sh, o, 64), ol = __shfl_xor(sl, o, 64);
+    double s, e;
+    two_sum(sh, oh, s, e);
+    sh = s;
+    sl = sl + ol + e;
+  }
+  const int w = threadIdx.x >> 6;
+  if ((threadIdx.x & 63) == 0) { dred[0][w] = sh; dred[1][w] = sl; }
+  __syncthreads();
+  sh = dred[0][0];
+  sl = dred[1][0];
+  for (int k = 1; k < 4; ++k) {
+    double s, e;
+    two_sum(sh, dred[0][k], s, e);
+    sh = s;
+    sl = sl + dred[1][k] + e;
+  }
+  __syncthreads();
+  return sh + sl;
+}
+
+}  // namespace pact

@@ -185,8 +185,11 @@ int lora_bwd(const uint8_t *x_codes, const uint8_t *x_scales, const float *x_rsc
 /*
  * silu_mul_bwd -- SiLU-multiply backward from the NVFP4 state (Appendix Table 7
  * row "SiLU-multiply": FP32 reconstruction and derivatives, BF16 gradients).
- *   a^ = deq(gate_q), b^ = deq(up_q), sigma = 1/(1+exp(-a^)):
- *   dgate = bf16(dh b^ sigma (1 + a^ (1 - sigma))),  dup = bf16(dh a^ sigma).
+ *   a^ = deq(gate_q), b^ = deq(up_q), sigma = 1/(1 + E(-a^)) with E the
+ *   pinned FP32 exponential of silu_mul_quant:
+ *   dgate = bf16( ((dh b^) sigma) (1 + a^ (1 - sigma)) ),  dup = bf16( (dh a^) sigma ),
+ *   every FP32 operation rounded to nearest in the order written (so the
+ *   result is reproducible bit for bit).
  *   gate_q, up_q NVFP4 [M x I]; dh, dgate, dup BF16 [M x I] (dense rows).
  */
 int silu_mul_bwd(const uint8_t *g_codes, const uint8_t *g_scales, const float *g_rscale,
@@ -195,15 +198,49 @@ int silu_mul_bwd(const uint8_t *g_codes, const uint8_t *g_scales, const float *g
                  void *stream);
 
 /*
+ * silu_mul_bwd_quant -- silu_mul_bwd that also emits the NVFP4 copies
+ * dgate_q = Q(dgate), dup_q = Q(dup) of the BF16 gradients it stores (the
+ * inputs of the gate and up input-gradient GEMMs; the BF16 gradients still
+ * feed the LoRA backward).  Same results as silu_mul_bwd followed by two
+ * nvfp4_quantize calls, with one pass over the data (quantize-on-emit).
+ * dgate_q, dup_q NVFP4 [M x I] (caller buffers).  I % 16 == 0, I <= 16384.
+ */
+int silu_mul_bwd_quant(const uint8_t *g_codes, const uint8_t *g_scales, const float *g_rscale,
+                       const uint8_t *u_codes, const uint8_t *u_scales, const float *u_rscale,
+                       const uint16_t *dh, int64_t M, int64_t I, uint16_t *dgate, uint16_t *dup,
+                       uint8_t *dg_codes, uint8_t *dg_scales, float *dg_rscale,
+                       uint8_t *du_codes, uint8_t *du_scales, float *du_rscale, void *stream);
+
+/*
  * rmsnorm_bwd -- RMSNorm backward from the NVFP4 state (Appendix Table 7 row
  * "RMSNorm": FP32 reconstruction and reduction, BF16 gradient).
  *   y^ = deq(y_q) [M x H], rstd f32 [M], gain BF16 [H], dy BF16 [M x H]:
- *   dx_i = bf16( rstd * (g_i dy_i - (y^_i / g_i) * (1/H) sum_j dy_j y^_j) ).
+ *   S = sum_j dy_j y^_j exactly, rounded once to float64; mean = fp32(S / H)
+ *   (float64 division);
+ *   dx_i = bf16( rstd ((g_i dy_i) - ((y^_i / g_i) mean)) ), each FP32 operation
+ *   rounded to nearest in the order written.
  *   dx BF16 [M x H] (dense rows).  The gain is frozen (no gain gradient).
+ *   H % 16 == 0, H <= 16384.
  */
 int rmsnorm_bwd(const uint8_t *y_codes, const uint8_t *y_scales, const float *y_rscale,
                 const float *rstd, const uint16_t *gain, const uint16_t *dy, int64_t M, int64_t H,
                 uint16_t *dx, void *stream);
+
+/*
+ * rmsnorm_bwd_residual -- rmsnorm_bwd fused with the residual-gradient
+ * accumulation (Appendix Table 7 row "Residuals": BF16 gradient accumulation)
+ * and, optionally, the NVFP4 quantization of the sum (quantize-on-emit: the
+ * result is the output gradient of the projection that produced the residual
+ * stream's previous value).
+ *   out = bf16( fp32(bf16(dx)) + resid )   with dx as in rmsnorm_bwd;
+ *   resid BF16 [M x H] or NULL (then out = bf16(dx));
+ *   out_q = Q(out) NVFP4 [M x H] when q_codes, q_scales, q_rscale are all given
+ *   (all NULL: no NVFP4 output).  out BF16 [M x H] must not alias dy or resid.
+ */
+int rmsnorm_bwd_residual(const uint8_t *y_codes, const uint8_t *y_scales, const float *y_rscale,
+                         const float *rstd, const uint16_t *gain, const uint16_t *dy,
+                         const uint16_t *resid, int64_t M, int64_t H, uint16_t *dx,
+                         uint8_t *q_codes, uint8_t *q_scales, float *q_rscale, void *stream);
 
 /* ---------------------------------------------------------------------------
  * MXFP4 variant (Appendix Table 6, MXFP4 column: 32-element blocks, E2M1

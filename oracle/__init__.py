@@ -12,7 +12,7 @@ It is deliberately slow and plain: numpy in float64 for every real-valued
 result, exact comparisons (products of short-mantissa values are exact in
 float64) for every rounding decision, and numpy float32 only where a reading
 pins an FP32 operation sequence (the fused RMSNorm and SiLU-multiply
-forward).
+forward and backward).
 
 Modules
   nvfp4     E2M1 / E4M3 value sets, quantize, dequantize, packing
@@ -20,7 +20,9 @@ Modules
   gemm      float64 forward and input-gradient GEMMs of dequantized operands
   lora      the BF16 rank-r branch on the dequantized input
   fused     RMSNorm -> quantize and SiLU-multiply -> quantize forward
-  backward  RMSNorm and SiLU-multiply backward from the saved NVFP4 state
+  backward  RMSNorm and SiLU-multiply backward from the saved NVFP4 state,
+            their pinned FP32 sequences, the BF16 residual accumulation and the
+            quantize-on-emit compositions
   tolerance the acceptance bounds for floating-point results
 
 Parity status: every function here is pinned by tests in

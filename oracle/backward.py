@@ -18,13 +18,30 @@ a^ = deq(a_q), b^ = deq(b_q) and sigma = 1 / (1 + e^(-a^)):
 
 Each function also returns the summed magnitude of the terms that cancel,
 which the acceptance bound uses.
+
+Pinned FP32 sequences (reading D14).  So that the BF16 gradients, and the
+NVFP4 copies the quantize-on-emit kernels make of them, are reproducible bit
+for bit, the kernels evaluate these formulas in a fixed FP32 sequence, every
+operation rounded to nearest:
+    sigma = 1 / (1 + E(-a^))            (E: the pinned exponential of fused.py)
+    dgate = ((dh * b^) * sigma) * (1 + a^ * (1 - sigma)),  dup = (dh * a^) * sigma
+    S = sum_j dy_j y^_j exactly, rounded once to float64;  mean = fp32(S / H)
+    dx = rstd * ((g * dy) - ((y^ / g) * mean))
+each rounded to BF16 (RNE).  ``*_f32`` below are those sequences in numpy
+float32; the float64 functions above are the exact values they approximate.
+Residual gradients accumulate in BF16 (Table 7 row "Residuals"):
+out = bf16(fp32(dx) + resid) with dx already BF16.
 """
 
 from __future__ import annotations
 
+import math
+
 import numpy as np
 
-from .nvfp4 import NVFP4, dequantize
+from .fused import exp_f32
+from .nvfp4 import NVFP4, dequantize, quantize
+from .tolerance import bf16_rne
 
 
 def rmsnorm_bwd(yq: NVFP4, rstd, g, dy):
@@ -56,3 +73,59 @@ def silu_mul_bwd(aq: NVFP4, bq: NVFP4, dh):
     cancel_da = np.abs(dh * bh * sig) * (1.0 + np.abs(ah) * (1.0 - sig))
     cancel_db = np.abs(db)
     return da, db, cancel_da, cancel_db
+
+
+def to_bf16_f32(x) -> np.ndarray:
+    """float32 values rounded to the nearest BF16 value (ties to even), as float32."""
+    return bf16_rne(np.asarray(x, dtype=np.float32).astype(np.float64)).astype(np.float32)
+
+
+def silu_mul_bwd_f32(aq: NVFP4, bq: NVFP4, dh):
+    """(dgate, dup) as BF16 values (float32) from the pinned FP32 sequence."""
+    a = dequantize(aq).astype(np.float32)      # exact: short-mantissa values
+    b = dequantize(bq).astype(np.float32)
+    d = np.asarray(dh, dtype=np.float32)
+    one = np.float32(1.0)
+    with np.errstate(over="ignore"):
+        sig = one / (one + exp_f32(-a))
+    da = ((d * b) * sig) * (one + a * (one - sig))
+    db = (d * a) * sig
+    return to_bf16_f32(da), to_bf16_f32(db)
+
+
+def silu_mul_bwd_quant(aq: NVFP4, bq: NVFP4, dh):
+    """(dgate, dup, Q(dgate), Q(dup)): the BF16 gradients and their NVFP4 copies."""
+    da, db = silu_mul_bwd_f32(aq, bq, dh)
+    return da, db, quantize(da.astype(np.float64)), quantize(db.astype(np.float64))
+
+
+def rmsnorm_mean_f32(yq: NVFP4, dy) -> np.ndarray:
+    """Per-row fp32(S / H) with S = sum_j dy_j y^_j rounded once to float64."""
+    y = dequantize(yq)
+    d = np.asarray(dy, dtype=np.float32).astype(np.float64)
+    prod = d * y                               # exact: 8 + 6 significant bits
+    S = np.array([math.fsum(row) for row in prod], dtype=np.float64)
+    return (S / np.float64(y.shape[1])).astype(np.float32)
+
+
+def rmsnorm_bwd_f32(yq: NVFP4, rstd, g, dy) -> np.ndarray:
+    """dx as BF16 values (float32) from the pinned FP32 sequence."""
+    y = dequantize(yq).astype(np.float32)
+    d = np.asarray(dy, dtype=np.float32)
+    gg = np.asarray(g, dtype=np.float32)[None, :]
+    rs = np.asarray(rstd, dtype=np.float32)[:, None]
+    mean = rmsnorm_mean_f32(yq, dy)[:, None]
+    dx = rs * ((gg * d) - ((y / gg) * mean))
+    return to_bf16_f32(dx)
+
+
+def residual_add_bf16(dx_bf16, resid) -> np.ndarray:
+    """bf16(fp32(dx) + resid) for BF16 operands given as float32 values."""
+    return to_bf16_f32(np.asarray(dx_bf16, dtype=np.float32) + np.asarray(resid, dtype=np.float32))
+
+
+def rmsnorm_bwd_residual(yq: NVFP4, rstd, g, dy, resid=None):
+    """(out, Q(out)) with out = bf16(rmsnorm_bwd) [+ resid in BF16]."""
+    dx = rmsnorm_bwd_f32(yq, rstd, g, dy)
+    out = dx if resid is None else residual_add_bf16(dx, resid)
+    return out, quantize(out.astype(np.float64))

@@ -25,7 +25,7 @@ def lib():
 
 def test_header_symbols_exported(lib):
     names = _lib.header_functions()
-    assert len(names) == 17, names
+    assert len(names) == 19, names
     assert set(names) == set(_lib.SIGNATURES), set(names) ^ set(_lib.SIGNATURES)
     for n in names:
         assert hasattr(lib, n), n
@@ -52,7 +52,7 @@ def test_gemm_tile_query(lib):
 
 
 def test_abi_version(lib):
-    assert lib.pact_abi_version() == 2
+    assert lib.pact_abi_version() == 3
 
 
 def test_sizes(lib):
@@ -156,3 +156,19 @@ def test_mxfp4_sizes_and_validation(lib):
     assert g(ALIGNED, ALIGNED, 64, 128, None, ALIGNED, 64, ALIGNED, 64, 0, None) == -1     # NULL b
     assert g(ALIGNED, ALIGNED, 64, 128, ALIGNED, ALIGNED, 64, ALIGNED, 64, 2, None) == -1  # accumulate flag
     assert g(ALIGNED, ALIGNED, 0, 128, ALIGNED, ALIGNED, 64, ALIGNED, 64, 0, None) == 0    # empty: no-op
+
+
+def test_fused_backward_validation(lib):
+    A, X = ALIGNED, MISALIGNED
+    f = lib.silu_mul_bwd_quant
+    assert f(A, A, A, A, A, A, A, 4, 40, A, A, A, A, A, A, A, A, None) == -2        # I % 16
+    assert f(A, A, A, A, A, A, A, 4, 32768, A, A, A, A, A, A, A, A, None) == -5     # I > 16384
+    assert f(A, A, A, A, A, A, A, 4, 64, A, A, None, A, A, A, A, A, None) == -1     # NULL dgate_q codes
+    assert f(A, A, A, A, A, A, A, 4, 64, A, A, A, A, A, A, A, X, None) == -3        # misaligned dup_q rscale
+    assert f(A, A, A, A, A, A, A, 0, 64, A, A, A, A, A, A, A, A, None) == 0         # empty
+    g = lib.rmsnorm_bwd_residual
+    assert g(A, A, A, A, A, A, None, 4, 40, A, None, None, None, None) == -2       # H % 16
+    assert g(A, A, A, A, A, A, None, 4, 64, None, None, None, None, None) == -1    # NULL dx
+    assert g(A, A, A, A, A, A, X, 4, 64, A, None, None, None, None) == -3          # misaligned resid
+    assert g(A, A, A, A, A, A, None, 4, 64, A, A, None, A, None) == -1             # partial NVFP4 output
+    assert g(A, A, A, A, A, A, None, 0, 64, A, None, None, None, None) == 0        # empty
