@@ -5,14 +5,20 @@ One step is one pass of the whole path over --layers (default 4) distinct
 Llama-3B-shaped decoder layers' frozen projections at M = 4096 tokens
 (batch 4 x seq 1024), LoRA rank 16 -- distinct weights and buffers per layer,
 about 1 GB each, so operands stream from HBM rather than the 256 MB
-last-level cache.  Per layer:
+last-level cache.  Forward through every layer, then backward from the top
+layer down, each layer's input gradient (the residual stream) being the
+output gradient of the layer below:
 
   forward   rmsnorm_quant -> q/k/v (lora_down + NVFP4 GEMM with LoRA term)
             nvfp4_quantize(attention output) -> o
             rmsnorm_quant -> gate/up -> silu_mul_quant -> down
-  backward  per projection: nvfp4_quantize(dY), lora_bwd, NVFP4 dgrad GEMM
-            (+ LoRA input-gradient term; q/k/v and gate/up accumulate),
-            silu_mul_bwd between down and gate/up, rmsnorm_bwd at both norms
+  backward  down (its dY = the layer's output gradient, already NVFP4)
+            silu_mul_bwd_quant (BF16 da, db and their NVFP4 copies) -> gate, up
+            rmsnorm_bwd_residual (+ the output gradient; NVFP4 copy) -> o
+            q/k/v (nvfp4_quantize of the attention-backward gradients)
+            rmsnorm_bwd_residual (+ the MLP-block residual gradient; NVFP4 copy)
+  per projection: lora_bwd and the NVFP4 dgrad GEMM with the LoRA
+  input-gradient term (q/k/v and gate/up accumulate into one dX)
 
 The metric is the NVFP4 fwd + dgrad GEMM throughput of the step:
   value = (GEMM FLOPs per step) / (wall time per step)   [TFLOP/s]
@@ -85,7 +91,8 @@ class Layer:
         self.g1 = up(synth.uniform_bf16((H,), 0.9, 1.1, wl.wid, off + 13))
         self.g2 = up(synth.uniform_bf16((H,), 0.9, 1.1, wl.wid, off + 14))
         grad = lambda tid, cols: up(synth.normal_bf16((M, cols), wl.dy_std, wl.wid, off + tid))
-        self.dOut, self.dYo = grad(15, H), grad(16, H)
+        self.dOut = grad(15, H)                    # output gradient entering the stack (top layer)
+        self.dOut_q = fw.empty_nvfp4(M, H, dev)
         self.dq, self.dk, self.dv = grad(17, H), grad(18, KV), grad(19, KV)
 
         self.proj = {}
@@ -112,7 +119,10 @@ class Layer:
         self.hq, self.gq, self.uq = nv(I), nv(I), nv(I)
         bf = lambda cols: torch.empty((M, cols), dtype=torch.bfloat16, device=dev)
         self.dh, self.da, self.db = bf(I), bf(I), bf(I)
-        self.dy1, self.dy2, self.dattn, self.dx1, self.dx2 = bf(H), bf(H), bf(H), bf(H), bf(H)
+        self.daq, self.dbq = nv(I), nv(I)
+        self.dy1, self.dy2, self.dattn = bf(H), bf(H), bf(H)
+        self.dh2, self.dh1 = bf(H), bf(H)                   # residual-stream gradients (BF16)
+        self.dh2q, self.dh1q = nv(H), nv(H)                 # their NVFP4 copies
         self.record = None       # list to append (category, name, start_event, end_event, work) into
 
     # ---- instrumented launch helper ----
@@ -136,23 +146,25 @@ class Layer:
                  lambda: fw.gemm_fwd(xq, P["wf"], lora_t=P["T"], lora_b=P["B"], lora_scale=LORA_SCALE, out=P["Y"]))
         return P["Y"]
 
-    def _bwd_proj(self, name, xq, dy, dx, accumulate):
+    def _bwd_proj(self, name, xq, dy, dx, accumulate, dyq=None):
+        """LoRA backward and input-gradient GEMM of one projection; dY is
+        quantized here unless its NVFP4 copy comes from a fused kernel."""
         fw, P = self.fw, self.proj[name]
         p = P["p"]
-        self._ev("quant", "nvfp4_quantize", ("quant", self.M, p.d_out),
-                 lambda: fw.quantize(dy, out=P["dyq"]))
+        if dyq is None:
+            dyq = P["dyq"]
+            self._ev("quant", "nvfp4_quantize", ("quant", self.M, p.d_out), lambda: fw.quantize(dy, out=dyq))
         self._ev("lora", "lora_bwd", None,
                  lambda: fw.lora_bwd(xq, P["A"], P["B"], dy, LORA_SCALE, out=(P["dT"], P["dA"], P["dB"]),
                                      workspace=self.lora_ws))
         work = ("gemm", self.M, p.d_in, p.d_out)
         self._ev("gemm", f"dgrad {name}", work,
-                 lambda: fw.gemm_dgrad(P["dyq"], P["wb"], out=dx, accumulate=accumulate, lora_dt=P["dT"],
+                 lambda: fw.gemm_dgrad(dyq, P["wb"], out=dx, accumulate=accumulate, lora_dt=P["dT"],
                                        lora_a=P["A"]))
 
-    def step(self):
+    def forward(self):
         fw = self.fw
         M, H, I = self.M, self.H, self.I
-        # ---------------- forward ----------------
         self._ev("quant", "rmsnorm_quant", ("rmsq", M, H),
                  lambda: fw.rmsnorm_quant(self.h1, self.g1, 1e-5, out=(self.y1q, self.rstd1)))
         for n in ("q", "k", "v"):
@@ -166,20 +178,32 @@ class Layer:
         self._ev("quant", "silu_mul_quant", ("silu", M, I),
                  lambda: fw.silu_mul_quant(a, b, out=(self.hq, self.gq, self.uq)))
         self._fwd_proj("down", self.hq)
-        # ---------------- backward ----------------
-        self._bwd_proj("down", self.hq, self.dOut, self.dh, False)
-        self._ev("bwd", "silu_mul_bwd", ("silub", M, I),
-                 lambda: fw.silu_mul_bwd(self.gq, self.uq, self.dh, out=(self.da, self.db)))
-        self._bwd_proj("gate", self.y2q, self.da, self.dy2, False)
-        self._bwd_proj("up", self.y2q, self.db, self.dy2, True)
-        self._ev("bwd", "rmsnorm_bwd", ("rmsb", M, H),
-                 lambda: fw.rmsnorm_bwd(self.y2q, self.rstd2, self.g2, self.dy2, out=self.dx2))
-        self._bwd_proj("o", self.aq, self.dYo, self.dattn, False)
+
+    def backward(self, dout, dout_q):
+        """Backward of the layer given the gradient of its output (BF16 and its
+        NVFP4 copy); returns the gradient of its input, the residual stream
+        (Table 7 row "Residuals": BF16 gradient accumulation)."""
+        fw = self.fw
+        M, H, I = self.M, self.H, self.I
+        # MLP block: out = h2 + down(silu(gate(n2)) * up(n2)),  n2 = rmsnorm(h2)
+        self._bwd_proj("down", self.hq, dout, self.dh, False, dyq=dout_q)
+        self._ev("bwd", "silu_mul_bwd_quant", ("silubq", M, I),
+                 lambda: fw.silu_mul_bwd_quant(self.gq, self.uq, self.dh, out=(self.da, self.db, self.daq, self.dbq)))
+        self._bwd_proj("gate", self.y2q, self.da, self.dy2, False, dyq=self.daq)
+        self._bwd_proj("up", self.y2q, self.db, self.dy2, True, dyq=self.dbq)
+        self._ev("bwd", "rmsnorm_bwd_residual", ("rmsbr", M, H),
+                 lambda: fw.rmsnorm_bwd_residual(self.y2q, self.rstd2, self.g2, self.dy2, resid=dout,
+                                                 out=(self.dh2, self.dh2q)))
+        # attention block: h2 = h1 + o(attn(q, k, v of n1)),  n1 = rmsnorm(h1); the
+        # attention backward itself is not part of the path (dq, dk, dv are inputs)
+        self._bwd_proj("o", self.aq, self.dh2, self.dattn, False, dyq=self.dh2q)
         self._bwd_proj("q", self.y1q, self.dq, self.dy1, False)
         self._bwd_proj("k", self.y1q, self.dk, self.dy1, True)
         self._bwd_proj("v", self.y1q, self.dv, self.dy1, True)
-        self._ev("bwd", "rmsnorm_bwd", ("rmsb", M, H),
-                 lambda: fw.rmsnorm_bwd(self.y1q, self.rstd1, self.g1, self.dy1, out=self.dx1))
+        self._ev("bwd", "rmsnorm_bwd_residual", ("rmsbr", M, H),
+                 lambda: fw.rmsnorm_bwd_residual(self.y1q, self.rstd1, self.g1, self.dy1, resid=self.dh2,
+                                                 out=(self.dh1, self.dh1q)))
+        return self.dh1, self.dh1q
 
     def gemm_flops(self):
         return sum(4 * self.M * P["p"].d_in * P["p"].d_out for P in self.proj.values())
@@ -304,8 +328,9 @@ def mxfp4_leg(fw, torch, synth, wl, nlayers, steps, warmup, eager=False):
 
 # algorithmic bytes per element of each bandwidth-bound kernel (inputs read + outputs written)
 BYTES_PER_ELEM = {"quant": 2.0 + 0.5 + 1 / 16, "rmsq": 2.0 + 0.5 + 1 / 16, "silu": 4.0 + 3 * (0.5 + 1 / 16),
-                  "silub": 2 * (0.5 + 1 / 16) + 2.0 + 4.0, "rmsb": (0.5 + 1 / 16) + 2.0 + 2.0}
-BYTES_PER_ROW = {"quant": 4, "rmsq": 8, "silu": 12, "silub": 8, "rmsb": 8}
+                  "silubq": 2 * (0.5 + 1 / 16) + 2.0 + 4.0 + 2 * (0.5 + 1 / 16),
+                  "rmsbr": (0.5 + 1 / 16) + 2.0 + 2.0 + 2.0 + (0.5 + 1 / 16)}
+BYTES_PER_ROW = {"quant": 4, "rmsq": 8, "silu": 12, "silubq": 16, "rmsbr": 12}
 
 
 def kernel_bytes(kind, rows, cols):
@@ -377,8 +402,15 @@ def main():
     resident = torch.cuda.memory_allocated()
 
     def step():
+        # forward through every layer, then backward from the top: each layer's
+        # input gradient (and its NVFP4 copy) is the output gradient of the one below
         for ly in layers:
-            ly.step()
+            ly.forward()
+        top = layers[-1]
+        top._ev("quant", "nvfp4_quantize", ("quant", top.M, top.H), lambda: fw.quantize(top.dOut, out=top.dOut_q))
+        d, dq = top.dOut, top.dOut_q
+        for ly in reversed(layers):
+            d, dq = ly.backward(d, dq)
 
     for _ in range(args.warmup):
         step()
@@ -495,7 +527,8 @@ def main():
         "dtype": "nvfp4 operands, fp16 MFMA (exact products), fp32 accumulation, bf16 output",
         "data": "synthetic (seeded BF16 activations with 1% outlier channels, N(0,0.02) weights, N(0,0.01) grads)",
         "config": {"workload": f"llama3b decoder-layer frozen projections fwd+dgrad + fused quantizers + LoRA r16, "
-                               f"{len(layers)} distinct layer instances per step",
+                               f"{len(layers)} distinct layer instances per step, backward chained through "
+                               f"BF16 residual gradients",
                    "layers": len(layers), "resident_gb": round(resident / 1e9, 2),
                    "tokens": layer.M, "hidden": layer.H, "intermediate": layer.I, "kv": layer.KV,
                    "lora_rank": layer.r, "gemm_gflop_per_step": round(flops / 1e9, 1), "parallelism": "single-gpu"},
