@@ -86,6 +86,35 @@ def quantize(x: torch.Tensor, transpose: bool = False, out: NVFP4Tensor | None =
     return out
 
 
+QUANT_ROUND_UP_SCALES = 1
+QUANT_TENSOR_SCALE = 2
+QUANT_COMPUTE_AMAX = 4
+
+
+def quantize_ex(x: torch.Tensor, transpose: bool = False, round_up: bool = False, tensor_scale: bool = False,
+                amax: torch.Tensor | None = None, compute_amax: bool = True, out: NVFP4Tensor | None = None):
+    """NVFP4 of x (or x^T) with the recipe variants: round-up block scales and/or one
+    power-of-two scale for the whole tensor from amax (a float32 device scalar,
+    computed here by a first pass when compute_amax, else supplied)."""
+    _bf16(x, "x")
+    if x.dim() != 2 or x.stride(1) != 1:
+        raise ValueError("x must be a 2-D tensor with unit column stride")
+    rows, cols = (x.shape[1], x.shape[0]) if transpose else (x.shape[0], x.shape[1])
+    out = out if out is not None else empty_nvfp4(rows, cols, x.device)
+    flags = (QUANT_ROUND_UP_SCALES if round_up else 0)
+    if tensor_scale:
+        flags |= QUANT_TENSOR_SCALE | (QUANT_COMPUTE_AMAX if compute_amax else 0)
+        if amax is None:
+            if not compute_amax:
+                raise ValueError("a supplied amax is needed when compute_amax is False")
+            amax = torch.empty((), dtype=torch.float32, device=x.device)
+        if amax.dtype != torch.float32 or amax.numel() != 1:
+            raise TypeError("amax must be a float32 device scalar")
+    _lib.call("nvfp4_quantize_ex", x.data_ptr(), rows, cols, x.stride(0), int(transpose), flags,
+              amax.data_ptr() if tensor_scale else 0, *out.ptrs(), _stream())
+    return out
+
+
 def weight_layouts(w: torch.Tensor):
     """Cached forward and backward layouts (Q(W), Q(W^T)) of a frozen BF16 weight W [N x K]."""
     return quantize(w), quantize(w, transpose=True)

@@ -69,7 +69,7 @@ extern "C" {
 
 const char* pact_last_error(void) { return g_err; }
 
-int pact_abi_version(void) { return 3; }
+int pact_abi_version(void) { return 4; }
 
 int pact_nvfp4_sizes(int64_t rows, int64_t cols, size_t* codes_bytes, size_t* scales_bytes, size_t* rscale_bytes) {
   REQUIRE(rows >= 0 && cols >= 0, PACT_EINVAL, "negative size (rows=%lld, cols=%lld)", (long long)rows,
@@ -109,6 +109,46 @@ int nvfp4_quantize(const uint16_t* x, int64_t rows, int64_t cols, int64_t ldx, i
   REQUIRE(rows <= 0x7FFFFFFF, PACT_EUNSUPPORTED, "rows=%lld exceeds the grid limit", (long long)rows);
   return hip_status(pact::launch_quantize(x, rows, cols, ldx, transpose, codes, scales, rscale, as_stream(stream)),
                     "nvfp4_quantize launch");
+}
+
+int nvfp4_quantize_ex(const uint16_t* x, int64_t rows, int64_t cols, int64_t ldx, int transpose, int flags,
+                      float* amax, uint8_t* codes, uint8_t* scales, float* rscale, void* stream) {
+  REQUIRE(rows >= 0 && cols >= 0, PACT_EINVAL, "negative size (rows=%lld, cols=%lld)", (long long)rows,
+          (long long)cols);
+  REQUIRE(transpose == 0 || transpose == 1, PACT_EINVAL, "transpose must be 0 or 1 (got %d)", transpose);
+  REQUIRE((flags & ~(PACT_QUANT_ROUND_UP_SCALES | PACT_QUANT_TENSOR_SCALE | PACT_QUANT_COMPUTE_AMAX)) == 0,
+          PACT_EINVAL, "unknown flags 0x%x", flags);
+  REQUIRE(!(flags & PACT_QUANT_COMPUTE_AMAX) || (flags & PACT_QUANT_TENSOR_SCALE), PACT_EINVAL,
+          "PACT_QUANT_COMPUTE_AMAX needs PACT_QUANT_TENSOR_SCALE");
+  REQUIRE(cols % 16 == 0, PACT_ESHAPE, "cols=%lld is not a multiple of 16", (long long)cols);
+  const bool tensor = (flags & PACT_QUANT_TENSOR_SCALE) != 0;
+  if (tensor) {
+    REQUIRE(amax != nullptr, PACT_EINVAL, "amax is NULL (required by PACT_QUANT_TENSOR_SCALE)");
+    REQUIRE((reinterpret_cast<uintptr_t>(amax) & 3u) == 0, PACT_EALIGN, "amax is not 4-byte aligned");
+  }
+  if (rows == 0 || cols == 0) return ok();
+  REQUIRE_PTR(x, "x");
+  int st = check_nvfp4(codes, scales, rscale, "out");
+  if (st != PACT_OK) return st;
+  if (transpose == 0) {
+    REQUIRE(ldx >= cols, PACT_ESHAPE, "ldx=%lld < cols=%lld", (long long)ldx, (long long)cols);
+    REQUIRE(ldx % 8 == 0, PACT_EALIGN, "ldx=%lld is not a multiple of 8 elements", (long long)ldx);
+  } else {
+    REQUIRE(ldx >= rows, PACT_ESHAPE, "ldx=%lld < rows=%lld (transposed input is [cols x rows])", (long long)ldx,
+            (long long)rows);
+  }
+  REQUIRE(rows <= 0x7FFFFFFF, PACT_EUNSUPPORTED, "rows=%lld exceeds the grid limit", (long long)rows);
+  hipStream_t s = as_stream(stream);
+  if (flags & PACT_QUANT_COMPUTE_AMAX) {
+    // the input buffer is [rows x cols] (transpose 0) or [cols x rows] (transpose 1)
+    const int64_t xr = transpose ? cols : rows, xc = transpose ? rows : cols;
+    st = hip_status(pact::launch_tensor_absmax(x, xr, xc, ldx, amax, s), "tensor amax launch");
+    if (st != PACT_OK) return st;
+  }
+  return hip_status(pact::launch_quantize_ex(x, rows, cols, ldx, transpose,
+                                             (flags & PACT_QUANT_ROUND_UP_SCALES) ? 1 : 0, tensor ? amax : nullptr,
+                                             codes, scales, rscale, s),
+                    "nvfp4_quantize_ex launch");
 }
 
 int rmsnorm_quant(const uint16_t* x, const uint16_t* gain, float eps, int64_t M, int64_t H, int64_t ldx,

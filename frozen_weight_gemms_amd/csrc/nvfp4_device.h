@@ -76,11 +76,22 @@ struct BlockQ {
   uint32_t sc;  // E4M3 code of s
 };
 
-__device__ __forceinline__ BlockQ block_setup(float bmax, float r, float inv_r) {
+// Smallest E4M3FN code whose value is >= X / 6 (X = blockmax / r <= 2688, so
+// no saturation): round t = RN32(X / 6) up on the grid, then correct by one
+// step with exact comparisons (6 * value has at most 6 significant bits).
+__device__ __forceinline__ uint32_t e4m3_encode_up(float X) {
+  const float t = __fdiv_rn(X, 6.0f);
+  uint32_t c = e4m3_encode(t);                         // nearest, then step to the ceiling
+  if (c < 0x7Eu && 6.0f * e4m3_decode(c) < X) ++c;
+  if (c > 0u && 6.0f * e4m3_decode(c - 1u) >= X) --c;
+  return c;
+}
+
+__device__ __forceinline__ BlockQ block_setup(float bmax, float r, float inv_r, bool round_up = false) {
   (void)r;
   BlockQ q;
-  const float t = __fdiv_rn(bmax * inv_r, 6.0f);
-  q.sc = e4m3_encode(t);
+  const float X = bmax * inv_r;                        // exact: r is a power of two
+  q.sc = round_up ? e4m3_encode_up(X) : e4m3_encode(__fdiv_rn(X, 6.0f));
   q.s = e4m3_decode(q.sc);
   q.rcp = q.s != 0.0f ? __fdiv_rn(1.0f, q.s) : 0.0f;
   q.inv_r = inv_r;

@@ -12,6 +12,15 @@ namespace pact {
 hipError_t launch_quantize(const uint16_t* x, int64_t rows, int64_t cols, int64_t ldx, int transpose,
                            uint8_t* codes, uint8_t* scales, float* rscale, hipStream_t s);
 
+// round_up: block scales rounded up (non-saturating); tensor_amax (device, may be
+// null): one power-of-two scale for the whole tensor from that maximum
+hipError_t launch_quantize_ex(const uint16_t* x, int64_t rows, int64_t cols, int64_t ldx, int transpose,
+                              int round_up, const float* tensor_amax, uint8_t* codes, uint8_t* scales,
+                              float* rscale, hipStream_t s);
+// *amax = max |x| over x [rows x cols] (row stride ldx)
+hipError_t launch_tensor_absmax(const uint16_t* x, int64_t rows, int64_t cols, int64_t ldx, float* amax,
+                                hipStream_t s);
+
 hipError_t launch_rmsnorm_quant(const uint16_t* x, const uint16_t* gain, float eps, int64_t M, int64_t H,
                                 int64_t ldx, uint8_t* codes, uint8_t* scales, float* rscale, float* rstd,
                                 int force_exact, hipStream_t s);

@@ -24,7 +24,8 @@ template <int NCH>
 __global__ __launch_bounds__(kThreads) void k_quantize_rows(const uint16_t* __restrict__ x, int64_t cols,
                                                             int64_t ldx, uint8_t* __restrict__ codes,
                                                             uint8_t* __restrict__ scales,
-                                                            float* __restrict__ rscale) {
+                                                            float* __restrict__ rscale, int round_up,
+                                                            const float* __restrict__ tensor_amax) {
   __shared__ float red[4];
   const int64_t row = blockIdx.x;
   const int nchunk = (int)(cols >> 3);
@@ -39,7 +40,8 @@ __global__ __launch_bounds__(kThreads) void k_quantize_rows(const uint16_t* __re
     unpack_bf16x8(v[i], f);
     lmax = fmaxf(lmax, absmax8(f));
   }
-  const float amax = block_max_256(lmax, red);
+  // tensor_amax (a kernel argument, uniform): one scale for every row
+  const float amax = tensor_amax != nullptr ? *tensor_amax : block_max_256(lmax, red);
   const int e = row_exponent(amax);
   const float r = pow2f(e), inv_r = pow2f(-e);
   uint8_t* crow = codes + row * (cols >> 1);
@@ -49,7 +51,7 @@ __global__ __launch_bounds__(kThreads) void k_quantize_rows(const uint16_t* __re
     const int c = threadIdx.x + kThreads * i;
     float f[8];
     unpack_bf16x8(v[i], f);
-    quant_chunk(f, c < nchunk, r, inv_r, crow, srow, c);
+    quant_chunk(f, c < nchunk, r, inv_r, crow, srow, c, round_up != 0);
   }
   if (threadIdx.x == 0) rscale[row] = r;
 }
@@ -59,7 +61,8 @@ __global__ __launch_bounds__(kThreads) void k_quantize_rows(const uint16_t* __re
 __global__ __launch_bounds__(kThreads) void k_quantize_rows_long(const uint16_t* __restrict__ x, int64_t cols,
                                                                  int64_t ldx, uint8_t* __restrict__ codes,
                                                                  uint8_t* __restrict__ scales,
-                                                                 float* __restrict__ rscale) {
+                                                                 float* __restrict__ rscale, int round_up,
+                                                                 const float* __restrict__ tensor_amax) {
   __shared__ float red[4];
   const int64_t row = blockIdx.x;
   const int nchunk = (int)(cols >> 3);
@@ -70,7 +73,7 @@ __global__ __launch_bounds__(kThreads) void k_quantize_rows_long(const uint16_t*
     unpack_bf16x8(load16(xr + 8 * c), f);
     lmax = fmaxf(lmax, absmax8(f));
   }
-  const float amax = block_max_256(lmax, red);
+  const float amax = tensor_amax != nullptr ? *tensor_amax : block_max_256(lmax, red);
   const int e = row_exponent(amax);
   const float r = pow2f(e), inv_r = pow2f(-e);
   uint8_t* crow = codes + row * (cols >> 1);
@@ -81,7 +84,7 @@ __global__ __launch_bounds__(kThreads) void k_quantize_rows_long(const uint16_t*
     float f[8];
     uint4 v = c < nchunk ? load16(xr + 8 * c) : make_uint4(0, 0, 0, 0);
     unpack_bf16x8(v, f);
-    quant_chunk(f, c < nchunk, r, inv_r, crow, srow, c);
+    quant_chunk(f, c < nchunk, r, inv_r, crow, srow, c, round_up != 0);
   }
   if (threadIdx.x == 0) rscale[row] = r;
 }
@@ -96,7 +99,8 @@ __global__ __launch_bounds__(kThreads) void k_quantize_cols(const uint16_t* __re
                                                             int64_t cols, int64_t ldx,
                                                             uint8_t* __restrict__ codes,
                                                             uint8_t* __restrict__ scales,
-                                                            float* __restrict__ rscale) {
+                                                            float* __restrict__ rscale, int round_up,
+                                                            const float* __restrict__ tensor_amax) {
   __shared__ float red[4][64];
   const int li = threadIdx.x & 63, g = threadIdx.x >> 6;
   const int64_t i = (int64_t)blockIdx.x * 64 + li;
@@ -107,7 +111,8 @@ __global__ __launch_bounds__(kThreads) void k_quantize_cols(const uint16_t* __re
   for (int64_t j = g; j < cols; j += 4) lmax = fmaxf(lmax, fabsf(bf16_lo(x[j * ldx + ic])));
   red[g][li] = lmax;
   __syncthreads();
-  const float amax = fmaxf(fmaxf(red[0][li], red[1][li]), fmaxf(red[2][li], red[3][li]));
+  const float amax = tensor_amax != nullptr ? *tensor_amax
+                                            : fmaxf(fmaxf(red[0][li], red[1][li]), fmaxf(red[2][li], red[3][li]));
   const int e = row_exponent(amax);
   const float r = pow2f(e), inv_r = pow2f(-e);
   for (int64_t b = g; b < nblk; b += 4) {
@@ -118,7 +123,7 @@ __global__ __launch_bounds__(kThreads) void k_quantize_cols(const uint16_t* __re
       f[t] = bf16_lo(x[(16 * b + t) * ldx + ic]);
       m = fmaxf(m, fabsf(f[t]));
     }
-    const BlockQ q = block_setup(m, r, inv_r);
+    const BlockQ q = block_setup(m, r, inv_r, round_up != 0);
     const uint32_t w0 = encode8(f, q), w1 = encode8(f + 8, q);
     if (ok) {
       uint32_t* dst = reinterpret_cast<uint32_t*>(codes + i * (cols >> 1) + 8 * b);
@@ -314,21 +319,75 @@ __global__ __launch_bounds__(kThreads) void k_silu_mul_quant(const uint16_t* __r
 // --------------------------------------------------------------------------
 static int chunks_per_thread(int64_t cols) { return (int)(((cols >> 3) + kThreads - 1) / kThreads); }
 
-hipError_t launch_quantize(const uint16_t* x, int64_t rows, int64_t cols, int64_t ldx, int transpose,
-                           uint8_t* codes, uint8_t* scales, float* rscale, hipStream_t s) {
+// Tensor amax for the per-tensor scale recipe: max |x| over the logical
+// matrix [rows x cols] (row stride ldx), written to *amax (non-negative, so the
+// float's bit pattern orders like an unsigned integer and an unsigned atomic
+// max combines the workgroups in any order with the same result).
+__global__ void k_zero_f32(float* p) {
+  if (blockIdx.x == 0 && threadIdx.x == 0) *p = 0.0f;
+}
+__global__ __launch_bounds__(kThreads) void k_absmax_vec(const uint16_t* __restrict__ x, int64_t rows, int64_t cols,
+                                                         int64_t ldx, unsigned* __restrict__ amax) {
+  const int64_t cpr = cols >> 3, total = rows * cpr;
+  float m = 0.0f;
+  for (int64_t q = (int64_t)blockIdx.x * kThreads + threadIdx.x; q < total; q += (int64_t)gridDim.x * kThreads) {
+    const int64_t row = q / cpr, c = q - row * cpr;
+    float f[8];
+    unpack_bf16x8(load16(x + row * ldx + 8 * c), f);
+    m = fmaxf(m, absmax8(f));
+  }
+  m = wave_max(m);
+  if ((threadIdx.x & 63) == 0) atomicMax(amax, __float_as_uint(m));
+}
+__global__ __launch_bounds__(kThreads) void k_absmax_scalar(const uint16_t* __restrict__ x, int64_t rows,
+                                                            int64_t cols, int64_t ldx, unsigned* __restrict__ amax) {
+  const int64_t total = rows * cols;
+  float m = 0.0f;
+  for (int64_t q = (int64_t)blockIdx.x * kThreads + threadIdx.x; q < total; q += (int64_t)gridDim.x * kThreads) {
+    const int64_t row = q / cols, c = q - row * cols;
+    m = fmaxf(m, fabsf(bf16_lo(x[row * ldx + c])));
+  }
+  m = wave_max(m);
+  if ((threadIdx.x & 63) == 0) atomicMax(amax, __float_as_uint(m));
+}
+
+hipError_t launch_tensor_absmax(const uint16_t* x, int64_t rows, int64_t cols, int64_t ldx, float* amax,
+                                hipStream_t s) {
+  k_zero_f32<<<1, 64, 0, s>>>(amax);
+  const bool vec = (cols % 8) == 0 && (ldx % 8) == 0 && (reinterpret_cast<uintptr_t>(x) & 15u) == 0;
+  const int64_t work = vec ? rows * (cols >> 3) : rows * cols;
+  int64_t blocks = (work + kThreads - 1) / kThreads;
+  if (blocks > 4096) blocks = 4096;
+  if (blocks < 1) blocks = 1;
+  unsigned* a = reinterpret_cast<unsigned*>(amax);
+  if (vec) k_absmax_vec<<<(unsigned)blocks, kThreads, 0, s>>>(x, rows, cols, ldx, a);
+  else k_absmax_scalar<<<(unsigned)blocks, kThreads, 0, s>>>(x, rows, cols, ldx, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_quantize_ex(const uint16_t* x, int64_t rows, int64_t cols, int64_t ldx, int transpose,
+                              int round_up, const float* tensor_amax, uint8_t* codes, uint8_t* scales,
+                              float* rscale, hipStream_t s) {
   if (transpose) {
     const unsigned grid = (unsigned)((rows + 63) / 64);
-    k_quantize_cols<<<grid, kThreads, 0, s>>>(x, rows, cols, ldx, codes, scales, rscale);
+    k_quantize_cols<<<grid, kThreads, 0, s>>>(x, rows, cols, ldx, codes, scales, rscale, round_up, tensor_amax);
     return hipGetLastError();
   }
   const int nch = chunks_per_thread(cols);
   const dim3 grid((unsigned)rows);
-  if (nch <= 1) k_quantize_rows<1><<<grid, kThreads, 0, s>>>(x, cols, ldx, codes, scales, rscale);
-  else if (nch <= 2) k_quantize_rows<2><<<grid, kThreads, 0, s>>>(x, cols, ldx, codes, scales, rscale);
-  else if (nch <= 4) k_quantize_rows<4><<<grid, kThreads, 0, s>>>(x, cols, ldx, codes, scales, rscale);
-  else if (nch <= 8) k_quantize_rows<8><<<grid, kThreads, 0, s>>>(x, cols, ldx, codes, scales, rscale);
-  else k_quantize_rows_long<<<grid, kThreads, 0, s>>>(x, cols, ldx, codes, scales, rscale);
+#define PACT_QR(N) k_quantize_rows<N><<<grid, kThreads, 0, s>>>(x, cols, ldx, codes, scales, rscale, round_up, tensor_amax)
+  if (nch <= 1) PACT_QR(1);
+  else if (nch <= 2) PACT_QR(2);
+  else if (nch <= 4) PACT_QR(4);
+  else if (nch <= 8) PACT_QR(8);
+  else k_quantize_rows_long<<<grid, kThreads, 0, s>>>(x, cols, ldx, codes, scales, rscale, round_up, tensor_amax);
+#undef PACT_QR
   return hipGetLastError();
+}
+
+hipError_t launch_quantize(const uint16_t* x, int64_t rows, int64_t cols, int64_t ldx, int transpose,
+                           uint8_t* codes, uint8_t* scales, float* rscale, hipStream_t s) {
+  return launch_quantize_ex(x, rows, cols, ldx, transpose, 0, nullptr, codes, scales, rscale, s);
 }
 
 hipError_t launch_rmsnorm_quant(const uint16_t* x, const uint16_t* gain, float eps, int64_t M, int64_t H,

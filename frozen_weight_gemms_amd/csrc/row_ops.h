@@ -24,11 +24,11 @@ __device__ __forceinline__ uint4 load16(const uint16_t* p) { return *reinterpret
 // Quantize one chunk (8 floats) of a row whose exponent is known.  Both lanes
 // of the pair must call this (it exchanges the chunk amax with lane ^ 1).
 __device__ __forceinline__ void quant_chunk(const float* x, bool valid, float r, float inv_r,
-                                            uint8_t* codes_row, uint8_t* scales_row, int c) {
+                                            uint8_t* codes_row, uint8_t* scales_row, int c, bool round_up = false) {
   float m = valid ? absmax8(x) : 0.0f;
   m = fmaxf(m, __shfl_xor(m, 1, 64));
   if (!valid) return;
-  const BlockQ q = block_setup(m, r, inv_r);
+  const BlockQ q = block_setup(m, r, inv_r, round_up);
   const uint32_t w = encode8(x, q);
   *reinterpret_cast<uint32_t*>(codes_row + 4 * (int64_t)c) = w;
   if ((c & 1) == 0) scales_row[c >> 1] = (uint8_t)q.sc;

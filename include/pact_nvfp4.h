@@ -80,6 +80,28 @@ int nvfp4_quantize(const uint16_t *x, int64_t rows, int64_t cols, int64_t ldx, i
                    uint8_t *codes, uint8_t *scales, float *rscale, void *stream);
 
 /*
+ * nvfp4_quantize_ex -- nvfp4_quantize with the recipe variants (what the
+ * tables leave open; the default, flags == 0, is nvfp4_quantize exactly):
+ *   PACT_QUANT_ROUND_UP_SCALES: each block scale is the smallest E4M3 value
+ *       >= blockmax / (6 r) instead of the nearest, so no element saturates
+ *       (every |x| / (s r) <= 6).
+ *   PACT_QUANT_TENSOR_SCALE: one power-of-two scale for the whole tensor, the
+ *       row-scale rule applied to the tensor maximum *amax (every row's rscale
+ *       is that value; rows with smaller maxima keep it).  amax: device float,
+ *       4-byte aligned.  Without PACT_QUANT_COMPUTE_AMAX the caller supplies
+ *       *amax (for example from the epilogue of the kernel that produced x); it
+ *       must be >= max |x| or elements saturate.
+ *   PACT_QUANT_COMPUTE_AMAX (with PACT_QUANT_TENSOR_SCALE): a first pass over x
+ *       writes max |x| to *amax (two passes over x in all).
+ * Other arguments and layouts as nvfp4_quantize.  Unknown flags: PACT_EINVAL.
+ */
+#define PACT_QUANT_ROUND_UP_SCALES 1
+#define PACT_QUANT_TENSOR_SCALE 2
+#define PACT_QUANT_COMPUTE_AMAX 4
+int nvfp4_quantize_ex(const uint16_t *x, int64_t rows, int64_t cols, int64_t ldx, int transpose, int flags,
+                      float *amax, uint8_t *codes, uint8_t *scales, float *rscale, void *stream);
+
+/*
  * rmsnorm_quant -- RMSNorm forward fused with NVFP4 quantization (Appendix
  * Table 7 row "RMSNorm": BF16 input, FP32 normalization; NVFP4 output and FP32
  * per-token statistic kept).  For each row of x [M x H] (leading dim ldx):

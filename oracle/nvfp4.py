@@ -147,11 +147,22 @@ def e2m1_round_mag(v_num: np.ndarray, scale: np.ndarray) -> np.ndarray:
     return mu
 
 
-def quantize(x, transpose: bool = False) -> NVFP4:
+def e4m3_round_up_code(t_times6: np.ndarray) -> np.ndarray:
+    """E4M3FN code of the smallest E4M3 value >= t, given 6*t exactly (t <= 448)."""
+    return np.searchsorted(6.0 * E4M3_POS, t_times6, side="left").astype(np.uint8)
+
+
+def quantize(x, transpose: bool = False, round_up: bool = False, tensor_amax=None) -> NVFP4:
     """Quantize a real matrix X [R x C] (C % 16 == 0) to canonical NVFP4.
 
     With ``transpose`` the input is X^T of the given matrix: rows of the result
     are columns of ``x``, blocked along the other axis.
+
+    Recipe variants (reading D15): ``round_up`` takes each block scale as the
+    smallest E4M3 value >= blockmax / (6 r) instead of the nearest (then no
+    element saturates); ``tensor_amax`` (a real >= max |x|, or "auto" for
+    max |x|) gives every row the one power-of-two scale the row rule assigns to
+    that maximum.
     """
     x = np.asarray(x, dtype=np.float64)
     if transpose:
@@ -160,12 +171,17 @@ def quantize(x, transpose: bool = False) -> NVFP4:
         raise ValueError("quantize expects [rows x cols] with cols % 16 == 0")
     R, C = x.shape
     ax = np.abs(x)
-    e = row_exponent(ax.max(axis=1) if C else np.zeros(R))
+    if tensor_amax is None:
+        e = row_exponent(ax.max(axis=1) if C else np.zeros(R))
+    else:
+        ta = (ax.max() if ax.size else 0.0) if isinstance(tensor_amax, str) else float(tensor_amax)
+        e = np.full(R, int(row_exponent(np.array(ta))), dtype=np.int64)
     inv_r = np.ldexp(1.0, -e)[:, None]
     xr = ax * inv_r                                           # |x| / r, exact
     blk = xr.reshape(R, C // BLOCK, BLOCK)
     bmax = blk.max(axis=2) if C else np.zeros((R, 0))
-    scode = e4m3_round_code(bmax)                             # compare against 6*mid exactly
+    # compare against 6*mid (or 6*value) exactly
+    scode = e4m3_round_up_code(bmax) if round_up else e4m3_round_code(bmax)
     s = E4M3_POS[scode]                                       # [R, C/16]
     mu = e2m1_round_mag(blk, s[:, :, None])
     mu = np.where(s[:, :, None] == 0, 0, mu)
