@@ -32,6 +32,9 @@ same shapes: the 7 forward and 7 input-gradient GEMMs of each layer instance,
 with MXFP4 operands quantized beforehand, as HIP-graph replays; it is reported
 under "mxfp4_variant" and is not part of "value".
 
+A third leg ("recipe_variants") times the Q/K/V and gate/up GEMMs with
+stacked weights against separate ones, and the quantizer's variants.
+
 Prints one JSON line.  --gpus must be 1: this build runs on one GPU.
 """
 
@@ -64,6 +67,7 @@ def parse():
                     help="distinct decoder-layer instances a step runs through (their weights and buffers "
                          "together exceed the 256 MB last-level cache, so every operand streams from HBM)")
     ap.add_argument("--no-mxfp4", action="store_true", help="skip the MXFP4-variant GEMM leg")
+    ap.add_argument("--no-recipes", action="store_true", help="skip the recipe-variant leg")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a 1 GiB read + 1 GiB write elementwise kernel (counter calibration)")
     return ap.parse_args()
@@ -326,6 +330,104 @@ def mxfp4_leg(fw, torch, synth, wl, nlayers, steps, warmup, eager=False):
                          "avg_launch_us": round(dt * 1e3 / dn, 2), "traffic": traffic}}
 
 
+def recipe_leg(fw, torch, synth, wl, n_inst=4, reps=5):
+    """The recipe variants at the Llama-3B shapes (M = 4096), over n_inst
+    rotating instances: the Q/K/V and gate/up forward and input-gradient GEMMs
+    with separate weights versus stacked weights (one GEMM per group, the
+    stacked dgrad summing every consumer), and the quantizer's variants on a
+    [4096 x 3072] output gradient."""
+    import numpy as np
+    M, H, I, KV = wl.tokens, 3072, 8192, 1024
+    dev = torch.device("cuda:0")
+    up = lambda bits: torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).to(dev)
+    bf = lambda r, c: torch.empty((r, c), dtype=torch.bfloat16, device=dev)
+    inst = []
+    for i in range(n_inst):
+        off = 9000 + 100 * i
+        d = {"x": fw.quantize(up(synth.workload_activation(wl, M, H, off)))}
+        w = {n: up(synth.normal_bf16((rows, H), wl.w_std, wl.wid, off + k))
+             for k, (n, rows) in enumerate((("q", H), ("k", KV), ("v", KV), ("gate", I), ("up", I)))}
+        d["sep"] = {n: fw.weight_layouts(t) for n, t in w.items()}
+        d["qkv"] = fw.weight_layouts(torch.cat([w["q"], w["k"], w["v"]], 0).contiguous())
+        d["gu"] = fw.weight_layouts(torch.cat([w["gate"], w["up"]], 0).contiguous())
+        del w
+        dy = {n: up(synth.normal_bf16((M, c), wl.dy_std, wl.wid, off + 10 + k))
+              for k, (n, c) in enumerate((("q", H), ("k", KV), ("v", KV), ("gate", I), ("up", I)))}
+        d["dyq"] = {n: fw.quantize(t) for n, t in dy.items()}
+        d["dy_qkv"] = fw.quantize(torch.cat([dy["q"], dy["k"], dy["v"]], 1).contiguous())
+        d["dy_gu"] = fw.quantize(torch.cat([dy["gate"], dy["up"]], 1).contiguous())
+        del dy
+        d["y"] = {n: bf(M, c) for n, c in (("q", H), ("k", KV), ("v", KV), ("gate", I), ("up", I))}
+        d["y_qkv"], d["y_gu"], d["dx1"], d["dx2"] = bf(M, H + 2 * KV), bf(M, 2 * I), bf(M, H), bf(M, H)
+        inst.append(d)
+
+    def separate(d):
+        for n in ("q", "k", "v", "gate", "up"):
+            fw.gemm_fwd(d["x"], d["sep"][n][0], out=d["y"][n])
+        for k, n in enumerate(("q", "k", "v")):
+            fw.gemm_dgrad(d["dyq"][n], d["sep"][n][1], out=d["dx1"], accumulate=k > 0)
+        for k, n in enumerate(("gate", "up")):
+            fw.gemm_dgrad(d["dyq"][n], d["sep"][n][1], out=d["dx2"], accumulate=k > 0)
+
+    def stacked(d):
+        fw.gemm_fwd(d["x"], d["qkv"][0], out=d["y_qkv"])
+        fw.gemm_fwd(d["x"], d["gu"][0], out=d["y_gu"])
+        fw.gemm_dgrad(d["dy_qkv"], d["qkv"][1], out=d["dx1"])
+        fw.gemm_dgrad(d["dy_gu"], d["gu"][1], out=d["dx2"])
+
+    def timed(fn):
+        best = 1e30
+        for _ in range(reps):
+            torch.cuda._sleep(HEAD_START_CYCLES)
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            for d in inst:
+                fn(d)
+            e1.record()
+            torch.cuda.synchronize()
+            best = min(best, e0.elapsed_time(e1) / len(inst))
+        return best
+
+    for fn in (separate, stacked):
+        for d in inst:
+            fn(d)
+    torch.cuda.synchronize()
+    flops = 2.0 * M * H * (H + 2 * KV + 2 * I) * 2          # forward + input gradient
+    t_sep, t_cat = timed(separate), timed(stacked)
+    out = {"stacked_qkv_gate_up": {"separate_tflops": round(flops / (t_sep * 1e-3) / 1e12, 1),
+                                   "stacked_tflops": round(flops / (t_cat * 1e-3) / 1e12, 1),
+                                   "separate_ms": round(t_sep, 4), "stacked_ms": round(t_cat, 4),
+                                   "launches": {"separate": 10, "stacked": 4}}}
+    # quantizer variants on [M x H]
+    xs = [up(synth.normal_bf16((M, H), wl.dy_std, wl.wid, 9900 + i)) for i in range(n_inst)]
+    qs = [fw.empty_nvfp4(M, H, dev) for _ in range(n_inst)]
+    amax = torch.empty((), dtype=torch.float32, device=dev)
+    variants = {"default": lambda x, q: fw.quantize(x, out=q),
+                "round_up_scales": lambda x, q: fw.quantize_ex(x, round_up=True, out=q),
+                "tensor_scale_two_pass": lambda x, q: fw.quantize_ex(x, tensor_scale=True, amax=amax, out=q)}
+    qb = {}
+    for name, f in variants.items():
+        for x, q in zip(xs, qs):
+            f(x, q)
+        torch.cuda.synchronize()
+        best = 1e30
+        for _ in range(reps):
+            torch.cuda._sleep(HEAD_START_CYCLES)
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            for x, q in zip(xs, qs):
+                f(x, q)
+            e1.record()
+            torch.cuda.synchronize()
+            best = min(best, e0.elapsed_time(e1) / len(xs))
+        qb[name] = {"us": round(best * 1e3, 2),
+                    "GB/s": round(kernel_bytes("quant", M, H) / (best * 1e-3) / 1e9, 1)}
+    out["quantizer_4096x3072"] = qb
+    del inst, xs, qs
+    torch.cuda.synchronize()
+    return out
+
+
 # algorithmic bytes per element of each bandwidth-bound kernel (inputs read + outputs written)
 BYTES_PER_ELEM = {"quant": 2.0 + 0.5 + 1 / 16, "rmsq": 2.0 + 0.5 + 1 / 16, "silu": 4.0 + 3 * (0.5 + 1 / 16),
                   "silubq": 2 * (0.5 + 1 / 16) + 2.0 + 4.0 + 2 * (0.5 + 1 / 16),
@@ -547,6 +649,8 @@ def main():
                      "avg_launch_us": round(dt_ms * 1e3 / dcount, 2),
                      "traffic": traffic},
     }
+    if not args.no_recipes:
+        result["recipe_variants"] = recipe_leg(fw, torch, synth, wl)
     if not args.no_mxfp4:
         del graph
         result["mxfp4_variant"] = mxfp4_leg(fw, torch, synth, wl, max(1, args.layers), args.steps, args.warmup,

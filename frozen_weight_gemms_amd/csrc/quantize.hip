@@ -336,8 +336,9 @@ __global__ __launch_bounds__(kThreads) void k_absmax_vec(const uint16_t* __restr
     unpack_bf16x8(load16(x + row * ldx + 8 * c), f);
     m = fmaxf(m, absmax8(f));
   }
-  m = wave_max(m);
-  if ((threadIdx.x & 63) == 0) atomicMax(amax, __float_as_uint(m));
+  __shared__ float red[4];
+  m = block_max_256(m, red);                   // one atomic per workgroup
+  if (threadIdx.x == 0) atomicMax(amax, __float_as_uint(m));
 }
 __global__ __launch_bounds__(kThreads) void k_absmax_scalar(const uint16_t* __restrict__ x, int64_t rows,
                                                             int64_t cols, int64_t ldx, unsigned* __restrict__ amax) {
@@ -347,8 +348,9 @@ __global__ __launch_bounds__(kThreads) void k_absmax_scalar(const uint16_t* __re
     const int64_t row = q / cols, c = q - row * cols;
     m = fmaxf(m, fabsf(bf16_lo(x[row * ldx + c])));
   }
-  m = wave_max(m);
-  if ((threadIdx.x & 63) == 0) atomicMax(amax, __float_as_uint(m));
+  __shared__ float red[4];
+  m = block_max_256(m, red);
+  if (threadIdx.x == 0) atomicMax(amax, __float_as_uint(m));
 }
 
 hipError_t launch_tensor_absmax(const uint16_t* x, int64_t rows, int64_t cols, int64_t ldx, float* amax,
@@ -357,7 +359,7 @@ hipError_t launch_tensor_absmax(const uint16_t* x, int64_t rows, int64_t cols, i
   const bool vec = (cols % 8) == 0 && (ldx % 8) == 0 && (reinterpret_cast<uintptr_t>(x) & 15u) == 0;
   const int64_t work = vec ? rows * (cols >> 3) : rows * cols;
   int64_t blocks = (work + kThreads - 1) / kThreads;
-  if (blocks > 4096) blocks = 4096;
+  if (blocks > 1024) blocks = 1024;                 // 4 per CU; one atomic each
   if (blocks < 1) blocks = 1;
   unsigned* a = reinterpret_cast<unsigned*>(amax);
   if (vec) k_absmax_vec<<<(unsigned)blocks, kThreads, 0, s>>>(x, rows, cols, ldx, a);
