@@ -185,6 +185,40 @@ def gemm_dgrad(dyq: NVFP4Tensor, w_bwd: NVFP4Tensor, out: torch.Tensor | None = 
     return out
 
 
+class SingleLayoutWeight:
+    """A frozen weight kept only as W_fwd = Q(W) [N x K], plus the largest
+    row-scale exponent over its nonzero rows (device int32), for the
+    single-layout dgrad."""
+
+    def __init__(self, w_fwd: NVFP4Tensor):
+        self.w_fwd = w_fwd
+        self.exp_max = torch.empty((1,), dtype=torch.int32, device=w_fwd.codes.device)
+        _lib.call("pact_nvfp4_row_exp_max", *w_fwd.ptrs(), w_fwd.rows, w_fwd.cols, self.exp_max.data_ptr(),
+                  _stream())
+
+
+def gemm_dgrad_fwd_layout(dyq: NVFP4Tensor, w: SingleLayoutWeight, out: torch.Tensor | None = None,
+                          accumulate: bool = False, lora_dt: torch.Tensor | None = None,
+                          lora_a: torch.Tensor | None = None):
+    """dX = bf16([dX +] deq(dY_q) deq(W_fwd) [+ dT A]) over the forward layout only."""
+    M, N = dyq.rows, dyq.cols
+    K = w.w_fwd.cols
+    if w.w_fwd.rows != N:
+        raise ValueError(f"contraction mismatch: dY has {N} columns, W_fwd {w.w_fwd.rows} rows")
+    if out is None:
+        if accumulate:
+            raise ValueError("accumulate needs an existing output")
+        out = torch.empty((M, K), dtype=torch.bfloat16, device=dyq.codes.device)
+    r = 0
+    if lora_dt is not None:
+        r = lora_dt.shape[1]
+        if lora_a is None or lora_a.shape != (r, K) or lora_dt.shape[0] != M:
+            raise ValueError("LoRA shapes: dT [M x r], A [r x K]")
+    _lib.call("nvfp4_gemm_dgrad_fwd_layout", *dyq.ptrs(), M, N, *w.w_fwd.ptrs(), w.exp_max.data_ptr(), K,
+              out.data_ptr(), out.stride(0), int(accumulate), _ptr(lora_dt), _ptr(lora_a), r, _stream())
+    return out
+
+
 def lora_down(xq: NVFP4Tensor, A: torch.Tensor, out: torch.Tensor | None = None):
     _bf16(A, "A")
     r, K = A.shape

@@ -44,6 +44,9 @@ SIGNATURES = {
     "silu_mul_bwd": ([c_vp] * 7 + [c_i64, c_i64, c_vp, c_vp, c_vp], c_int),
     "rmsnorm_bwd": ([c_vp] * 6 + [c_i64, c_i64, c_vp, c_vp], c_int),
     "nvfp4_quantize_ex": ([c_vp, c_i64, c_i64, c_i64, c_int, c_int, c_vp, c_vp, c_vp, c_vp, c_vp], c_int),
+    "nvfp4_gemm_dgrad_fwd_layout": ([c_vp, c_vp, c_vp, c_i64, c_i64, c_vp, c_vp, c_vp, c_vp, c_i64, c_vp, c_i64,
+                                     c_int, c_vp, c_vp, c_i64, c_vp], c_int),
+    "pact_nvfp4_row_exp_max": ([c_vp, c_vp, c_vp, c_i64, c_i64, c_vp, c_vp], c_int),
     "silu_mul_bwd_quant": ([c_vp] * 7 + [c_i64, c_i64] + [c_vp] * 9, c_int),
     "rmsnorm_bwd_residual": ([c_vp] * 7 + [c_i64, c_i64] + [c_vp] * 5, c_int),
     "pact_mxfp4_sizes": ([c_i64, c_i64, c_size_p, c_size_p], c_int),

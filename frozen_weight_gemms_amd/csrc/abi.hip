@@ -69,7 +69,7 @@ extern "C" {
 
 const char* pact_last_error(void) { return g_err; }
 
-int pact_abi_version(void) { return 4; }
+int pact_abi_version(void) { return 5; }
 
 int pact_nvfp4_sizes(int64_t rows, int64_t cols, size_t* codes_bytes, size_t* scales_bytes, size_t* rscale_bytes) {
   REQUIRE(rows >= 0 && cols >= 0, PACT_EINVAL, "negative size (rows=%lld, cols=%lld)", (long long)rows,
@@ -327,6 +327,47 @@ int rmsnorm_bwd(const uint8_t* y_codes, const uint8_t* y_scales, const float* y_
   return hip_status(pact::launch_rmsnorm_bwd(y_codes, y_scales, y_rscale, rstd, gain, dy, M, H, nullptr, dx,
                                              nullptr, nullptr, nullptr, as_stream(stream)),
                     "rmsnorm_bwd launch");
+}
+
+int pact_nvfp4_row_exp_max(const uint8_t* codes, const uint8_t* scales, const float* rscale, int64_t rows,
+                           int64_t cols, int* out, void* stream) {
+  REQUIRE(rows > 0 && cols > 0, PACT_EINVAL, "rows=%lld and cols=%lld must be positive", (long long)rows,
+          (long long)cols);
+  REQUIRE(cols % 16 == 0, PACT_ESHAPE, "cols=%lld is not a multiple of 16", (long long)cols);
+  int st = check_nvfp4(codes, scales, rscale, "x");
+  if (st != PACT_OK) return st;
+  REQUIRE(out != nullptr, PACT_EINVAL, "out is NULL");
+  REQUIRE((reinterpret_cast<uintptr_t>(out) & 3u) == 0, PACT_EALIGN, "out is not 4-byte aligned");
+  return hip_status(pact::launch_row_exp_max(rscale, scales, rows, cols, out, as_stream(stream)),
+                    "row exponent max launch");
+}
+
+int nvfp4_gemm_dgrad_fwd_layout(const uint8_t* dy_codes, const uint8_t* dy_scales, const float* dy_rscale, int64_t M,
+                                int64_t N, const uint8_t* w_codes, const uint8_t* w_scales, const float* w_rscale,
+                                const int* w_exp_max, int64_t K, uint16_t* dx, int64_t ldx, int accumulate,
+                                const uint16_t* lora_dt, const uint16_t* lora_a, int64_t r, void* stream) {
+  REQUIRE(M >= 0 && N >= 0 && K >= 0, PACT_EINVAL, "negative size");
+  REQUIRE(accumulate == 0 || accumulate == 1, PACT_EINVAL, "accumulate must be 0 or 1");
+  REQUIRE(N % 16 == 0 && K % 16 == 0, PACT_ESHAPE, "N=%lld and K=%lld must be multiples of 16", (long long)N,
+          (long long)K);
+  if (M == 0 || K == 0) return ok();
+  REQUIRE(N > 0, PACT_ESHAPE, "N must be positive");
+  int st = check_nvfp4(dy_codes, dy_scales, dy_rscale, "dy_q");
+  if (st == PACT_OK) st = check_nvfp4(w_codes, w_scales, w_rscale, "w_fwd");
+  if (st != PACT_OK) return st;
+  REQUIRE(w_exp_max != nullptr, PACT_EINVAL, "w_exp_max is NULL");
+  REQUIRE((reinterpret_cast<uintptr_t>(w_exp_max) & 3u) == 0, PACT_EALIGN, "w_exp_max is not 4-byte aligned");
+  REQUIRE_PTR(dx, "dx");
+  REQUIRE(ldx >= K, PACT_ESHAPE, "ldx=%lld < K=%lld", (long long)ldx, (long long)K);
+  REQUIRE(lora_dt == nullptr || (lora_a != nullptr && r >= 1 && r <= 128), PACT_EINVAL,
+          "LoRA term needs lora_a and 1 <= r <= 128");
+  REQUIRE(pact::dgrad_fwdlayout_supported(M, N, K), PACT_EUNSUPPORTED,
+          "single-layout dgrad needs N %% 256 == 0, K %% 64 == 0 and operands below 2^31 bytes (N=%lld, K=%lld)",
+          (long long)N, (long long)K);
+  return hip_status(pact::launch_dgrad_fwdlayout(dy_codes, dy_scales, dy_rscale, M, N, w_codes, w_scales, w_rscale,
+                                                 w_exp_max, K, dx, ldx, accumulate, lora_dt, lora_a,
+                                                 lora_dt != nullptr ? r : 0, as_stream(stream)),
+                    "nvfp4_gemm_dgrad_fwd_layout launch");
 }
 
 int silu_mul_bwd_quant(const uint8_t* g_codes, const uint8_t* g_scales, const float* g_rscale,

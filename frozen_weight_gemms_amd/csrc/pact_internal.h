@@ -52,6 +52,16 @@ struct GemmArgs {
 hipError_t launch_gemm(const GemmArgs& a, hipStream_t s);
 void gemm_tile(int64_t M, int64_t N, int* bm, int* bn);
 
+// Single-layout input gradient: dX [M x K] = deq(dY_q [M x N]) deq(W_fwd [N x K]);
+// bexp = largest row exponent over W_fwd's nonzero rows (device int, from launch_row_exp_max)
+bool dgrad_fwdlayout_supported(int64_t M, int64_t N, int64_t K);
+hipError_t launch_dgrad_fwdlayout(const uint8_t* ac, const uint8_t* as, const float* ar, int64_t M, int64_t N,
+                                  const uint8_t* bc, const uint8_t* bs, const float* br, const int* bexp, int64_t K,
+                                  uint16_t* out, int64_t ldo, int accumulate, const uint16_t* lora_dt,
+                                  const uint16_t* lora_a, int64_t r, hipStream_t s);
+hipError_t launch_row_exp_max(const float* rscale, const uint8_t* scales, int64_t rows, int64_t cols, int* out,
+                              hipStream_t s);
+
 hipError_t launch_lora_down(const uint8_t* xc, const uint8_t* xs, const float* xr, int64_t M, int64_t K,
                             const uint16_t* A, int64_t r, uint16_t* T, hipStream_t s);
 

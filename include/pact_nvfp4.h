@@ -173,6 +173,36 @@ int nvfp4_gemm_dgrad(const uint8_t *dy_codes, const uint8_t *dy_scales, const fl
                      void *stream);
 
 /*
+ * nvfp4_gemm_dgrad_fwd_layout -- single-layout input gradient: dX = dY W over
+ * the forward layout W_fwd = Q(W) [N x K] only (blocks along K), so a frozen
+ * weight keeps one cached NVFP4 layout instead of two and the forward and
+ * input-gradient products use identical effective weights.  (The pages keep
+ * both layouts, Appendix Table 7 row "Frozen projections"; this is the
+ * alternative that reuses W_fwd tiles through a transposed read.)
+ *   dX = bf16( [f32(dX) +] deq(dY_q) deq(W_fwd) [+ dT A] ),
+ *   dY_q NVFP4 [M x N]; W_fwd NVFP4 [N x K]; dX BF16 [M x K], ldx >= K;
+ *   LoRA term and accumulate as nvfp4_gemm_dgrad.
+ *   w_exp_max: device int, the largest row-scale exponent over W_fwd's
+ *   nonzero rows (pact_nvfp4_row_exp_max, once per weight).  Each B element is formed
+ *   in FP16 as code * block scale * 2^(e_row - w_exp_max): exact while no row's
+ *   exponent is more than 14 below w_exp_max, rounded in FP16 below that.
+ *   N % 256 == 0 and K % 64 == 0 (else PACT_EUNSUPPORTED), operands below
+ *   2^31 bytes of codes.
+ */
+int nvfp4_gemm_dgrad_fwd_layout(const uint8_t *dy_codes, const uint8_t *dy_scales, const float *dy_rscale,
+                                int64_t M, int64_t N,
+                                const uint8_t *w_codes, const uint8_t *w_scales, const float *w_rscale,
+                                const int *w_exp_max, int64_t K, uint16_t *dx, int64_t ldx, int accumulate,
+                                const uint16_t *lora_dt, const uint16_t *lora_a, int64_t lora_r, void *stream);
+
+/* Largest exponent e of the power-of-two row scales 2^e over the rows of an
+ * NVFP4 tensor [rows x cols] that are not all zero (device int *out; -126 if
+ * every row is zero), for nvfp4_gemm_dgrad_fwd_layout.  codes is validated
+ * but not read.  rows > 0, cols % 16 == 0. */
+int pact_nvfp4_row_exp_max(const uint8_t *codes, const uint8_t *scales, const float *rscale, int64_t rows,
+                           int64_t cols, int *out, void *stream);
+
+/*
  * lora_down -- LoRA forward down-projection on the reconstructed input
  * (Appendix Table 7 row "LoRA branch": BF16 GEMMs on reconstructed inputs).
  *   T = bf16( deq(X_q) A^T ),  X_q NVFP4 [M x K], A BF16 [r x K] row-major,

@@ -8,6 +8,8 @@ what this module computes:
 
 * forward        Y[m, n]  = sum_k deq(X_q)[m, k] * deq(W_fwd)[n, k]
 * input gradient dX[m, k] = sum_n deq(dY_q)[m, n] * deq(W_bwd)[k, n]
+* single-layout input gradient (the variant that keeps W_fwd only)
+                 dX[m, k] = sum_n deq(dY_q)[m, n] * deq(W_fwd)[n, k]
 
 with W_fwd = Q(W) (blocks along K) and W_bwd = Q(W^T) (blocks along N), both
 rounded to nearest from the same BF16 W.  Both are "A [M x Kr] times
@@ -43,3 +45,15 @@ def gemm_fwd(xq: NVFP4, w_fwd: NVFP4):
 
 def gemm_dgrad(dyq: NVFP4, w_bwd: NVFP4):
     return gemm_nt(dyq, w_bwd)
+
+
+def gemm_dgrad_fwd_layout(dyq: NVFP4, w_fwd: NVFP4):
+    """Single-layout input gradient: (dX, |dY||W|) for dX = deq(dY_q) @ deq(W_fwd).
+
+    W_fwd = Q(W) [N x K] is the forward layout (blocks along K); the input
+    gradient contracts over its rows, so forward and input gradient use the
+    same effective weight deq(W_fwd) instead of deq(W_fwd) and deq(W_bwd)^T.
+    """
+    da = dequantize(dyq)
+    dw = dequantize(w_fwd)
+    return da @ dw, np.abs(da) @ np.abs(dw)
