@@ -33,7 +33,9 @@ with MXFP4 operands quantized beforehand, as HIP-graph replays; it is reported
 under "mxfp4_variant" and is not part of "value".
 
 A third leg ("recipe_variants") times the Q/K/V and gate/up GEMMs with
-stacked weights against separate ones, and the quantizer's variants.
+stacked weights against separate ones, and the quantizer's variants; a fourth
+("single_layout_dgrad") the input-gradient GEMMs over the forward weight
+layout only against the dual-layout ones.
 
 Prints one JSON line.  --gpus must be 1: this build runs on one GPU.
 """
@@ -428,6 +430,89 @@ def recipe_leg(fw, torch, synth, wl, n_inst=4, reps=5):
     return out
 
 
+def single_layout_leg(fw, torch, synth, wl, n_inst=4, reps=5):
+    """Input-gradient GEMMs of the 7 projections per layer over the forward
+    layout only (single-layout dgrad) versus over the cached backward layout,
+    same shapes and rotation over n_inst layer instances; cached weight bytes
+    per layer for both."""
+    import numpy as np
+    M = wl.tokens
+    dev = torch.device("cuda:0")
+    up = lambda bits: torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).to(dev)
+    inst = []
+    for i in range(n_inst):
+        off = 12000 + 100 * i
+        items = []
+        for k, p in enumerate(wl.projections):
+            w = up(synth.normal_bf16((p.d_out, p.d_in), wl.w_std, wl.wid, off + k))
+            wf, wb = fw.weight_layouts(w)
+            del w
+            items.append(dict(p=p, wf=wf, wb=wb, sl=fw.SingleLayoutWeight(wf),
+                              dyq=fw.quantize(up(synth.normal_bf16((M, p.d_out), wl.dy_std, wl.wid, off + 20 + k))),
+                              dx=torch.empty((M, p.d_in), dtype=torch.bfloat16, device=dev)))
+        inst.append(items)
+
+    def dual(items):
+        for it in items:
+            fw.gemm_dgrad(it["dyq"], it["wb"], out=it["dx"])
+
+    def single(items):
+        for it in items:
+            fw.gemm_dgrad_fwd_layout(it["dyq"], it["sl"], out=it["dx"])
+
+    for fn in (dual, single):
+        for items in inst:
+            fn(items)
+    torch.cuda.synchronize()
+
+    def timed(fn):
+        best = 1e30
+        for _ in range(reps):
+            torch.cuda._sleep(HEAD_START_CYCLES)
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            for items in inst:
+                fn(items)
+            e1.record()
+            torch.cuda.synchronize()
+            best = min(best, e0.elapsed_time(e1) / len(inst))
+        return best
+
+    # dominant launch of the single-layout kernel: per-launch times of the largest shapes
+    per = {}
+    for it in inst[0]:
+        p = it["p"]
+        best = 1e30
+        for _ in range(reps):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            for items in inst:
+                fw.gemm_dgrad_fwd_layout(items[[q["p"].name for q in items].index(p.name)]["dyq"],
+                                         items[[q["p"].name for q in items].index(p.name)]["sl"],
+                                         out=items[[q["p"].name for q in items].index(p.name)]["dx"])
+            e1.record()
+            torch.cuda.synchronize()
+            best = min(best, e0.elapsed_time(e1) / len(inst))
+        per[p.name] = (best, 2.0 * M * p.d_in * p.d_out)
+    flops = sum(2.0 * M * it["p"].d_in * it["p"].d_out for it in inst[0])
+    t_dual, t_single = timed(dual), timed(single)
+    nv = lambda r, c: r * c * 9 // 16 + 4 * r
+    bytes_dual = sum(nv(it["p"].d_out, it["p"].d_in) + nv(it["p"].d_in, it["p"].d_out) for it in inst[0])
+    bytes_single = sum(nv(it["p"].d_out, it["p"].d_in) + 4 for it in inst[0])
+    name = max(per, key=lambda k: per[k][0])
+    t, f = per[name]
+    del inst
+    torch.cuda.synchronize()
+    return {"dual_layout_tflops": round(flops / (t_dual * 1e-3) / 1e12, 1),
+            "single_layout_tflops": round(flops / (t_single * 1e-3) / 1e12, 1),
+            "dual_ms_per_layer": round(t_dual, 4), "single_ms_per_layer": round(t_single, 4),
+            "cached_weight_mb_per_layer": {"dual": round(bytes_dual / 1e6, 2), "single": round(bytes_single / 1e6, 2)},
+            "roofline": {"kernel": "pact::k_gemm_dgrad_fwdlayout<4>", "projection": name, "bound": "mfma",
+                         "achieved": round(f / (t * 1e-3) / 1e12, 1), "peak": PEAK["fp16_mfma_tflops"],
+                         "unit": "TFLOP/s", "frac": round(f / (t * 1e-3) / 1e12 / PEAK["fp16_mfma_tflops"], 4),
+                         "avg_launch_us": round(t * 1e3, 2)}}
+
+
 # algorithmic bytes per element of each bandwidth-bound kernel (inputs read + outputs written)
 BYTES_PER_ELEM = {"quant": 2.0 + 0.5 + 1 / 16, "rmsq": 2.0 + 0.5 + 1 / 16, "silu": 4.0 + 3 * (0.5 + 1 / 16),
                   "silubq": 2 * (0.5 + 1 / 16) + 2.0 + 4.0 + 2 * (0.5 + 1 / 16),
@@ -651,6 +736,7 @@ def main():
     }
     if not args.no_recipes:
         result["recipe_variants"] = recipe_leg(fw, torch, synth, wl)
+        result["single_layout_dgrad"] = single_layout_leg(fw, torch, synth, wl)
     if not args.no_mxfp4:
         del graph
         result["mxfp4_variant"] = mxfp4_leg(fw, torch, synth, wl, max(1, args.layers), args.steps, args.warmup,
