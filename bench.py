@@ -691,7 +691,7 @@ def main():
     if os.path.exists(tfile):
         try:
             tj = json.load(open(tfile))
-            if tj.get("src_hash") == src_hash("gemm.hip", "nvfp4_device.h", "lds_dma.h") and tj.get("kernel") == kname \
+            if tj.get("src_hash") == src_hash("gemm.hip", "nvfp4_device.h", "lds_dma.h", "mfma_fp16.h") and tj.get("kernel") == kname \
                     and tj.get("tile") == list(dom_tile[:2]):
                 traffic = tj.get("bytes_per_launch")
         except (ValueError, OSError):
