@@ -17,8 +17,8 @@
 //     X_q, dT over N from dY).  A workgroup owns 16 token rows; its 8 waves
 //     take interleaved 128-element chunks of the row, each lane loading 32
 //     consecutive elements of a row per chunk (16 bytes of codes, or four
-//     16-byte BF16 loads) and the matching 32 elements of the rank-major small
-//     operand (A, or B^T transposed once into the workspace);
+//     16-byte BF16 loads) and the matching 32 elements of the small operand
+//     (A read rank-major; B transposed through LDS);
 //   * the column kernel contracts over the token axis (dB from dY and T, dA
 //     from X_q and dT).  Each lane loads an 8-row x CPL-column block of the
 //     long operand and transposes it in registers, so MFMA instance c takes
@@ -28,6 +28,8 @@
 //     reduce launch sums the partials in split order, so results do not depend
 //     on scheduling.
 #include "pact_internal.h"
+
+#include <type_traits>
 
 namespace pact {
 
@@ -54,24 +56,53 @@ __device__ __forceinline__ float e4m3_f32(uint32_t byte) { return __builtin_amdg
 // ---------------------------------------------------------------------------
 // Row kernel.  Block (tile, part) with 16 token rows p0 .. p0 + 15:
 //   part 0:  T[p][j]  = bf16(xr[p] * sum_k (e*s)[p][k] * A[j][k])     X_q [P x K], A [r x K]
-//   part 1:  dT[p][j] = bf16(scale * sum_n dY[p][n] * Bt[j][n])        dY [P x N], Bt = B^T [r x N]
+//   part 1:  dT[p][j] = bf16(scale * sum_n dY[p][n] * B[n][j])         dY [P x N], B [N x r]
 // Chunk c of the long axis is elements [128c, 128c + 128); waves take chunks
 // wave, wave + 8, ...  The chunk of the long operand (16 rows) is loaded with
 // row-contiguous 16-byte loads (four rows of 256 bytes per BF16 instruction,
 // sixteen rows of 64 bytes of codes per NVFP4 instruction) into a wave-private
 // LDS tile and read back in the MFMA layout: sub-step u (0..3) gives lane
-// (i, g) row i, elements 128c + 32u + 8g + (0..7).  The rank-major small
-// operand is read directly in that layout (it is small and cache-resident).
+// (i, g) row i, elements 128c + 32u + 8g + (0..7).  The small operand must
+// reach lane (i, g) as rank 16t + i at those same 8 elements:
+//   * A [r x K] is rank-major, so it is read directly in that layout (it is
+//     small and cache-resident);
+//   * B [N x r] is element-major: its 128 x 16 slice for the chunk and rank
+//     tile t is copied as loaded (32 bytes a row) into the wave's tile once the
+//     long operand has been read out of it, and read back with
+//     ds_read_b64_tr_b16.  That instruction transposes within each 16-lane
+//     group: output lane i, element a, is element i % 4 of source lane
+//     4a + i / 4, so source lane 4a + c (group g, half h) addresses row
+//     32u + 8g + 4h + a, columns 4c .. 4c + 3, and output lane i receives
+//     column i of the four rows 32u + 8g + 4h + (0..3).
 // The global loads of CH chunks are issued before any of them is used.
 // ---------------------------------------------------------------------------
 template <int NT>
 struct RowCfg {
-  static constexpr int CH = NT <= 1 ? 4 : (NT <= 2 ? 2 : 1);
+  static constexpr int CH = NT <= 2 ? 2 : 1;
 };
 constexpr int RL_STRIDE = 272;              // BF16 tile row stride in LDS (256 B + 16: conflict-free b128 reads)
 constexpr int RQ_STRIDE = 80;               // NVFP4 code tile row stride (64 B + 16: conflict-free b32 reads)
 constexpr int RQ_SCALES = 16 * RQ_STRIDE;   // then 16 rows x 8 scale bytes
-constexpr int RSTAGE = 16 * RL_STRIDE;      // bytes of one wave's staging tile
+constexpr int RSTAGE = 16 * RL_STRIDE;      // bytes of one wave's staging tile (>= 128 rows x 32 bytes of B)
+
+typedef short short4_t __attribute__((ext_vector_type(4)));
+
+// Row n, columns col .. col + 7 of B [N x r] (zeros outside the matrix);
+// 16-byte loads when rows are 16-byte aligned (r % 8 == 0).
+__device__ __forceinline__ uint4 load_b8(const uint16_t* __restrict__ B, int64_t n, int64_t col, int64_t N,
+                                         int64_t r, bool ok) {
+  if (!ok || n >= N || col >= r) return make_uint4(0, 0, 0, 0);
+  const uint16_t* p = B + n * r + col;
+  if ((r & 7) == 0) return *reinterpret_cast<const uint4*>(p);
+  uint32_t w[4];
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const uint32_t lo = col + 2 * k < r ? (uint32_t)p[2 * k] : 0u;
+    const uint32_t hi = col + 2 * k + 1 < r ? (uint32_t)p[2 * k + 1] : 0u;
+    w[k] = lo | (hi << 16);
+  }
+  return make_uint4(w[0], w[1], w[2], w[3]);
+}
 
 template <int NT, bool NVFP4>
 __device__ __forceinline__ void row_reduce(const uint8_t* __restrict__ xc, const uint8_t* __restrict__ xs,
@@ -84,7 +115,7 @@ __device__ __forceinline__ void row_reduce(const uint8_t* __restrict__ xc, const
   for (int64_t cb = wave; cb < nchunk; cb += 8 * CH) {
     uint4 lv[CH][4];          // BF16: instruction v holds rows 4v + lane/16, elements 8 (lane % 16) + (0..7)
     uint32_t lsc[CH][2];      // NVFP4: scale bytes of row lane/4, blocks 2 (lane % 4) and + 1
-    uint4 sv[CH][NT][4];
+    uint4 sv[CH][NT][4];      // A: MFMA operand of sub-step u; B: rows 32v + lane/2, columns 16t + 8 (lane % 2) + (0..7)
 #pragma unroll
     for (int q = 0; q < CH; ++q) {
       const int64_t c = cb + 8 * q;
@@ -113,12 +144,18 @@ __device__ __forceinline__ void row_reduce(const uint8_t* __restrict__ xc, const
       }
 #pragma unroll
       for (int t = 0; t < NT; ++t) {
-        const int64_t j = 16 * t + i;
+        if constexpr (NVFP4) {
+          const int64_t j = 16 * t + i;
 #pragma unroll
-        for (int u = 0; u < 4; ++u) {
-          const int64_t k = c * 128 + 32 * u + 8 * g;
-          const bool ok = cin && j < r && k + 8 <= R;
-          sv[q][t][u] = ok ? *reinterpret_cast<const uint4*>(S + j * R + k) : make_uint4(0, 0, 0, 0);
+          for (int u = 0; u < 4; ++u) {
+            const int64_t k = c * 128 + 32 * u + 8 * g;
+            const bool ok = cin && j < r && k + 8 <= R;
+            sv[q][t][u] = ok ? *reinterpret_cast<const uint4*>(S + j * R + k) : make_uint4(0, 0, 0, 0);
+          }
+        } else {
+#pragma unroll
+          for (int v = 0; v < 4; ++v)
+            sv[q][t][v] = load_b8(S, c * 128 + 32 * v + (lane >> 1), 16 * t + 8 * (lane & 1), R, r, cin);
         }
       }
     }
@@ -147,14 +184,41 @@ __device__ __forceinline__ void row_reduce(const uint8_t* __restrict__ xc, const
           av[u] = *reinterpret_cast<const uint4*>(stage + i * RL_STRIDE + 64 * u + 16 * g);
         }
       }
-      __builtin_amdgcn_s_waitcnt(0xc07f);             // reads done before the next chunk overwrites the tile
+      __builtin_amdgcn_s_waitcnt(0xc07f);             // reads done before the tile is overwritten
       __builtin_amdgcn_wave_barrier();
 #pragma unroll
-      for (int u = 0; u < 4; ++u)
+      for (int t = 0; t < NT; ++t) {
+        uint4 bv[4];
+        if constexpr (NVFP4) {
 #pragma unroll
-        for (int t = 0; t < NT; ++t)
+          for (int u = 0; u < 4; ++u) bv[u] = sv[q][t][u];
+        } else {
+          // B slice (128 rows x 32 bytes) into the tile as loaded, read back transposed
+#pragma unroll
+          for (int v = 0; v < 4; ++v)
+            *reinterpret_cast<uint4*>(stage + (32 * v + (lane >> 1)) * 32 + 16 * (lane & 1)) = sv[q][t][v];
+          __builtin_amdgcn_s_waitcnt(0xc07f);
+          __builtin_amdgcn_wave_barrier();
+          const int l16 = lane & 15;
+#pragma unroll
+          for (int u = 0; u < 4; ++u) {
+            short4_t h2[2];
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+              uint8_t* a = stage + (32 * u + 8 * g + 4 * h + (l16 >> 2)) * 32 + 8 * (l16 & 3);
+              h2[h] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) short4_t*)a);
+            }
+            const uint2 lo = __builtin_bit_cast(uint2, h2[0]), hi = __builtin_bit_cast(uint2, h2[1]);
+            bv[u] = make_uint4(lo.x, lo.y, hi.x, hi.y);
+          }
+          __builtin_amdgcn_s_waitcnt(0xc07f);         // reads done before the tile is overwritten
+          __builtin_amdgcn_wave_barrier();
+        }
+#pragma unroll
+        for (int u = 0; u < 4; ++u)
           acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, av[u]),
-                                                           __builtin_bit_cast(bf16x8_t, sv[q][t][u]), acc[t], 0, 0, 0);
+                                                           __builtin_bit_cast(bf16x8_t, bv[u]), acc[t], 0, 0, 0);
+      }
     }
   }
 }
@@ -169,7 +233,7 @@ __global__ __launch_bounds__(512) void k_lora_rows(const uint8_t* __restrict__ x
                                                    const uint16_t* __restrict__ A, int64_t r,
                                                    uint16_t* __restrict__ T, uint16_t* __restrict__ Tt, int64_t ldt,
                                                    const uint16_t* __restrict__ dy, int64_t N,
-                                                   const uint16_t* __restrict__ Bt, float scale,
+                                                   const uint16_t* __restrict__ B, float scale,
                                                    uint16_t* __restrict__ dT, uint16_t* __restrict__ dTt) {
   constexpr int NW = 8;
   constexpr int RT = 16 * NT;
@@ -184,7 +248,7 @@ __global__ __launch_bounds__(512) void k_lora_rows(const uint8_t* __restrict__ x
 #pragma unroll
   for (int t = 0; t < NT; ++t) acc[t] = floatx4{0, 0, 0, 0};
   if (part == 0) row_reduce<NT, true>(xc, xs, nullptr, p0, P, K, A, r, wave, lane, stage[wave], acc);
-  else row_reduce<NT, false>(nullptr, nullptr, dy, p0, P, N, Bt, r, wave, lane, stage[wave], acc);
+  else row_reduce<NT, false>(nullptr, nullptr, dy, p0, P, N, B, r, wave, lane, stage[wave], acc);
 
   // accumulator layout (16x16): (row, col) at lane col + 16 * (row / 4), register row % 4
 #pragma unroll
@@ -210,15 +274,6 @@ __global__ __launch_bounds__(512) void k_lora_rows(const uint8_t* __restrict__ x
     // last row tile: zero the padding columns [P, ldt) of the rank-major copy
     const int64_t pad = ldt - P;
     for (int64_t q = threadIdx.x; q < r * pad; q += 512) outt[(q / pad) * ldt + P + q % pad] = 0;
-  }
-}
-
-// B [N x r] -> Bt [r x N]
-__global__ __launch_bounds__(256) void k_transpose_rank(const uint16_t* __restrict__ B, int64_t N, int64_t r,
-                                                        uint16_t* __restrict__ Bt) {
-  for (int64_t q = (int64_t)blockIdx.x * 256 + threadIdx.x; q < N * r; q += (int64_t)gridDim.x * 256) {
-    const int64_t n = q / r, j = q - n * r;
-    Bt[j * N + n] = B[q];
   }
 }
 
@@ -258,6 +313,85 @@ __device__ __forceinline__ void transpose_rows(const uint32_t (&rows)[8][CPL / 2
   }
 }
 
+// One wave step's long-operand block (8 rows x CPL columns per lane, as BF16
+// pairs) and its rank-major small operand.
+template <int NT, int CPL>
+struct ColStep {
+  uint32_t rows[8][CPL / 2];
+  uint4 wv[NT];
+};
+
+template <int NT, int CPL, bool is_b>
+__device__ __forceinline__ void col_load(ColStep<NT, CPL>& st, const uint8_t* __restrict__ xc,
+                                         const uint8_t* __restrict__ xs, const float* __restrict__ xr, int64_t K,
+                                         const uint16_t* __restrict__ dy, int64_t N, const uint16_t* __restrict__ Wt,
+                                         int64_t ldt, int64_t r, int64_t m0, int64_t Re, int64_t qc, bool qok,
+                                         int lane) {
+  const int i = lane & 15, g = lane >> 4;
+  // row scales of the step's 32 rows, one per lane (dA strips only)
+  float xr_step = 0.0f;
+  if constexpr (!is_b)
+    if (m0 + (lane & 31) < Re) xr_step = xr[m0 + (lane & 31)];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    const int64_t m = m0 + 8 * g + e;
+    const bool ok = qok && m < Re;
+    if constexpr (is_b) {
+      const uint16_t* src = dy + m * N + qc;
+      if constexpr (CPL == 8) {
+        const uint4 v = ok ? *reinterpret_cast<const uint4*>(src) : make_uint4(0, 0, 0, 0);
+        st.rows[e][0] = v.x; st.rows[e][1] = v.y; st.rows[e][2] = v.z; st.rows[e][3] = v.w;
+      } else if constexpr (CPL == 4) {
+        const uint2 v = ok ? *reinterpret_cast<const uint2*>(src) : make_uint2(0, 0);
+        st.rows[e][0] = v.x; st.rows[e][1] = v.y;
+      } else {
+        st.rows[e][0] = ok ? *reinterpret_cast<const uint32_t*>(src) : 0u;
+      }
+    } else {
+      // X~ = e * s * r: CPL codes of row m (within one block), dequantized to BF16;
+      // the row scale of row m0 + 8g + e comes from lane 8g + e
+      const uint8_t* cp = xc + m * (K >> 1) + (qc >> 1);
+      const float rr = __shfl(xr_step, 8 * g + e, 64);
+      const float mlt = ok ? e4m3_f32(xs[m * (K >> 4) + (qc >> 4)]) * rr : 0.0f;
+      if constexpr (CPL == 8) {
+        const uint32_t w = ok ? *reinterpret_cast<const uint32_t*>(cp) : 0u;
+        const uint4 v = deq8_bf16(w, mlt);
+        st.rows[e][0] = v.x; st.rows[e][1] = v.y; st.rows[e][2] = v.z; st.rows[e][3] = v.w;
+      } else if constexpr (CPL == 4) {
+        const uint32_t w = ok ? (uint32_t)*reinterpret_cast<const uint16_t*>(cp) : 0u;
+        const float2_t a = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 0);
+        const float2_t b = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 1);
+        st.rows[e][0] = pack2(a.x * mlt, a.y * mlt);
+        st.rows[e][1] = pack2(b.x * mlt, b.y * mlt);
+      } else {
+        const uint32_t w = ok ? (uint32_t)cp[0] : 0u;
+        const float2_t a = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 0);
+        st.rows[e][0] = pack2(a.x * mlt, a.y * mlt);
+      }
+    }
+  }
+#pragma unroll
+  for (int t = 0; t < NT; ++t) {
+    const int64_t j = 16 * t + i;
+    // Wt rows are zero-padded up to ldt (M rounded up to 32), and m0 + 32 <= ldt
+    st.wv[t] = j < r ? *reinterpret_cast<const uint4*>(Wt + j * ldt + m0 + 8 * g) : make_uint4(0, 0, 0, 0);
+  }
+}
+
+template <int NT, int CPL>
+__device__ __forceinline__ void col_mma(const ColStep<NT, CPL>& st, floatx4 (&acc)[CPL][NT]) {
+  uint4 zt[CPL];
+  transpose_rows<CPL>(st.rows, zt);
+#pragma unroll
+  for (int c = 0; c < CPL; ++c)
+#pragma unroll
+    for (int t = 0; t < NT; ++t)
+      acc[c][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, zt[c]),
+                                                          __builtin_bit_cast(bf16x8_t, st.wv[t]), acc[c][t], 0, 0, 0);
+}
+
+// Column kernel.  Blocks [0, nstrip_b * nsplit_b) are (strip, split) pairs of
+// dB, the rest of dA; each writes the FP32 partial of its strip and split.
 template <int NT>
 __global__ __launch_bounds__(256) void k_lora_cols(const uint8_t* __restrict__ xc, const uint8_t* __restrict__ xs,
                                                    const float* __restrict__ xr, int64_t M, int64_t K,
@@ -271,8 +405,7 @@ __global__ __launch_bounds__(256) void k_lora_cols(const uint8_t* __restrict__ x
   __shared__ floatx4 red[4][CPL][NT][64];
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
-  const int i = lane & 15, g = lane >> 4;
-  // blocks [0, nstrip_b * nsplit_b) are (strip, split) of dB, the rest of dA.
+  const int i = lane & 15;
   // Consecutive block ids go to different XCDs; the remap gives each XCD a
   // contiguous run of (strip, split) pairs, i.e. adjacent strips of the same
   // token rows, so the cache lines of a row (codes, scales, BF16) that
@@ -299,65 +432,17 @@ __global__ __launch_bounds__(256) void k_lora_cols(const uint8_t* __restrict__ x
 #pragma unroll
     for (int t = 0; t < NT; ++t) acc[c][t] = floatx4{0, 0, 0, 0};
 
-  for (int64_t m0 = Rb + 32 * wave; m0 < Re; m0 += 128) {
-    // row scales of the step's 32 rows, one per lane (dA strips only)
-    float xr_step = 0.0f;
-    if (!is_b && m0 + (lane & 31) < Re) xr_step = xr[m0 + (lane & 31)];
-    uint32_t rows[8][CPL / 2];
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const int64_t m = m0 + 8 * g + e;
-      const bool ok = qok && m < Re;
-      if (is_b) {
-        const uint16_t* src = dy + m * N + qc;
-        if constexpr (CPL == 8) {
-          const uint4 v = ok ? *reinterpret_cast<const uint4*>(src) : make_uint4(0, 0, 0, 0);
-          rows[e][0] = v.x; rows[e][1] = v.y; rows[e][2] = v.z; rows[e][3] = v.w;
-        } else if constexpr (CPL == 4) {
-          const uint2 v = ok ? *reinterpret_cast<const uint2*>(src) : make_uint2(0, 0);
-          rows[e][0] = v.x; rows[e][1] = v.y;
-        } else {
-          rows[e][0] = ok ? *reinterpret_cast<const uint32_t*>(src) : 0u;
-        }
-      } else {
-        // X~ = e * s * r: CPL codes of row m (within one block), dequantized to BF16;
-        // the row scale of row m0 + 8g + e comes from lane 8g + e
-        const uint8_t* cp = xc + m * (K >> 1) + (qc >> 1);
-        const float rr = __shfl(xr_step, 8 * g + e, 64);
-        const float mlt = ok ? e4m3_f32(xs[m * (K >> 4) + (qc >> 4)]) * rr : 0.0f;
-        if constexpr (CPL == 8) {
-          const uint32_t w = ok ? *reinterpret_cast<const uint32_t*>(cp) : 0u;
-          const uint4 v = deq8_bf16(w, mlt);
-          rows[e][0] = v.x; rows[e][1] = v.y; rows[e][2] = v.z; rows[e][3] = v.w;
-        } else if constexpr (CPL == 4) {
-          const uint32_t w = ok ? (uint32_t)*reinterpret_cast<const uint16_t*>(cp) : 0u;
-          const float2_t a = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 0);
-          const float2_t b = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 1);
-          rows[e][0] = pack2(a.x * mlt, a.y * mlt);
-          rows[e][1] = pack2(b.x * mlt, b.y * mlt);
-        } else {
-          const uint32_t w = ok ? (uint32_t)cp[0] : 0u;
-          const float2_t a = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 0);
-          rows[e][0] = pack2(a.x * mlt, a.y * mlt);
-        }
-      }
+  // a wave step covers 32 token rows; the 4 waves interleave steps
+  auto run = [&](auto tag) {
+    constexpr bool B_PART = decltype(tag)::value;
+    for (int64_t m0 = Rb + 32 * wave; m0 < Re; m0 += 128) {
+      ColStep<NT, CPL> st;
+      col_load<NT, CPL, B_PART>(st, xc, xs, xr, K, dy, N, Wt, ldt, r, m0, Re, qc, qok, lane);
+      col_mma<NT, CPL>(st, acc);
     }
-    uint4 wv[NT];
-#pragma unroll
-    for (int t = 0; t < NT; ++t) {
-      const int64_t j = 16 * t + i;
-      // Wt rows are zero-padded up to ldt (M rounded up to 32), and m0 + 32 <= ldt
-      wv[t] = j < r ? *reinterpret_cast<const uint4*>(Wt + j * ldt + m0 + 8 * g) : make_uint4(0, 0, 0, 0);
-    }
-    uint4 zt[CPL];
-    transpose_rows<CPL>(rows, zt);
-#pragma unroll
-    for (int c = 0; c < CPL; ++c)
-#pragma unroll
-      for (int t = 0; t < NT; ++t)
-        acc[c][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, zt[c]),
-                                                            __builtin_bit_cast(bf16x8_t, wv[t]), acc[c][t], 0, 0, 0);
-  }
+  };
+  if (is_b) run(std::true_type{});
+  else run(std::false_type{});
 
 #pragma unroll
   for (int c = 0; c < CPL; ++c)
@@ -380,30 +465,47 @@ __global__ __launch_bounds__(256) void k_lora_cols(const uint8_t* __restrict__ x
       part[qq * r + jr] = sum;
     }
   }
+
 }
 
 // Sum of the split partials in split order, rounded to BF16: dB [N x r]
-// (times `scale`) for q < N*r, then dA [r x K] (stored transposed from the
-// [K x r] partials).
+// (times `scale`) for the first N*r elements, then dA [r x K] (stored
+// transposed from the [K x r] partials).  A thread owns 4 consecutive elements
+// and issues the loads of 8 splits before adding them, in split order.
 __global__ __launch_bounds__(256) void k_lora_reduce(const float* __restrict__ part_b,
                                                      const float* __restrict__ part_a, int nsplit_b, int nsplit_a,
-                                                     int64_t N,
-                                                     int64_t K, int64_t r, float scale, uint16_t* __restrict__ dB,
-                                                     uint16_t* __restrict__ dA) {
-  const int64_t nb = N * r, total = nb + K * r;
-  for (int64_t q = (int64_t)blockIdx.x * 256 + threadIdx.x; q < total; q += (int64_t)gridDim.x * 256) {
-    const bool is_b = q < nb;
-    const int64_t qq = is_b ? q : q - nb;
-    const int64_t stride = is_b ? nb : K * r;
-    const float* base = is_b ? part_b : part_a;
+                                                     int64_t N, int64_t K, int64_t r, float scale,
+                                                     uint16_t* __restrict__ dB, uint16_t* __restrict__ dA) {
+  const int64_t nb4 = N * r / 4, total4 = nb4 + K * r / 4;       // N * r and K * r are multiples of 16
+  for (int64_t q = (int64_t)blockIdx.x * 256 + threadIdx.x; q < total4; q += (int64_t)gridDim.x * 256) {
+    const bool is_b = q < nb4;
+    const int64_t qq = is_b ? q : q - nb4;
+    const int64_t stride = is_b ? N * r : K * r;
+    const float* base = (is_b ? part_b : part_a) + 4 * qq;
     const int nsplit = is_b ? nsplit_b : nsplit_a;
-    float sum = 0.0f;
-    for (int s = 0; s < nsplit; ++s) sum += base[(int64_t)s * stride + qq];
-    if (is_b) {
-      dB[qq] = (uint16_t)f32_to_bf16_rne(sum * scale);
-    } else {
-      const int64_t k = qq / r, j = qq - k * r;
-      dA[j * K + k] = (uint16_t)f32_to_bf16_rne(sum);
+    float4 sum = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+    for (int sb = 0; sb < nsplit; sb += 8) {
+      float4 pv[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u)
+        pv[u] = sb + u < nsplit ? *reinterpret_cast<const float4*>(base + (int64_t)(sb + u) * stride)
+                                : make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+#pragma unroll
+      for (int u = 0; u < 8; ++u)
+        if (sb + u < nsplit) {
+          sum.x += pv[u].x; sum.y += pv[u].y; sum.z += pv[u].z; sum.w += pv[u].w;
+        }
+    }
+    const float sv[4] = {sum.x, sum.y, sum.z, sum.w};
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int64_t e = 4 * qq + u;
+      if (is_b) {
+        dB[e] = (uint16_t)f32_to_bf16_rne(sv[u] * scale);
+      } else {
+        const int64_t k = e / r, j = e - k * r;
+        dA[j * K + k] = (uint16_t)f32_to_bf16_rne(sv[u]);
+      }
     }
   }
 }
@@ -424,7 +526,7 @@ static int cols_per_lane(int ntc) { return ntc <= 2 ? 8 : (ntc <= 4 ? 4 : 2); }
 struct LoraWs {
   int64_t ldt, nsplit_b, nsplit_a, rows_b, rows_a;
   int nstrip_b, nstrip_a;
-  size_t off_Bt, off_Tt, off_dTt, off_pdB, off_pdA, total;
+  size_t off_Tt, off_dTt, off_pdB, off_pdA, total;
 };
 
 static size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
@@ -452,7 +554,6 @@ static LoraWs lora_ws(int64_t M, int64_t K, int64_t N, int64_t r) {
   token_splits(M, w.nstrip_b, 384, &w.nsplit_b, &w.rows_b);
   token_splits(M, w.nstrip_a, 384, &w.nsplit_a, &w.rows_a);
   size_t off = 0;
-  w.off_Bt = off;  off = align256(off + (size_t)r * N * 2);
   w.off_Tt = off;  off = align256(off + (size_t)r * w.ldt * 2);
   w.off_dTt = off; off = align256(off + (size_t)r * w.ldt * 2);
   w.off_pdB = off; off = align256(off + (size_t)w.nsplit_b * N * r * 4);
@@ -465,9 +566,9 @@ size_t lora_bwd_workspace(int64_t M, int64_t K, int64_t N, int64_t r) { return l
 
 static void rows(int ntc, dim3 grid, hipStream_t s, const uint8_t* xc, const uint8_t* xs, const float* xr,
                  int64_t M, int64_t K, const uint16_t* A, int64_t r, uint16_t* T, uint16_t* Tt, int64_t ldt,
-                 const uint16_t* dy, int64_t N, const uint16_t* Bt, float scale, uint16_t* dT, uint16_t* dTt) {
+                 const uint16_t* dy, int64_t N, const uint16_t* B, float scale, uint16_t* dT, uint16_t* dTt) {
 #define PACT_ROWS(NT) \
-  k_lora_rows<NT><<<grid, 512, 0, s>>>(xc, xs, xr, M, K, A, r, T, Tt, ldt, dy, N, Bt, scale, dT, dTt)
+  k_lora_rows<NT><<<grid, 512, 0, s>>>(xc, xs, xr, M, K, A, r, T, Tt, ldt, dy, N, B, scale, dT, dTt)
   if (ntc <= 1) PACT_ROWS(1);
   else if (ntc <= 2) PACT_ROWS(2);
   else if (ntc <= 4) PACT_ROWS(4);
@@ -489,7 +590,6 @@ hipError_t launch_lora_bwd(const uint8_t* xc, const uint8_t* xs, const float* xr
                            int64_t N, uint16_t* dT, uint16_t* dA, uint16_t* dB, void* workspace, hipStream_t s) {
   const LoraWs w = lora_ws(M, K, N, r);
   uint8_t* ws = static_cast<uint8_t*>(workspace);
-  uint16_t* Bt = reinterpret_cast<uint16_t*>(ws + w.off_Bt);
   uint16_t* Tt = reinterpret_cast<uint16_t*>(ws + w.off_Tt);
   uint16_t* dTt = reinterpret_cast<uint16_t*>(ws + w.off_dTt);
   float* pdB = reinterpret_cast<float*>(ws + w.off_pdB);
@@ -502,26 +602,25 @@ hipError_t launch_lora_bwd(const uint8_t* xc, const uint8_t* xs, const float* xr
     if (K * r > 0) k_zero_u16<<<grid_for(K * r), 256, 0, s>>>(dA, K * r);
     return hipGetLastError();
   }
-  if (N * r > 0) k_transpose_rank<<<grid_for(N * r), 256, 0, s>>>(B, N, r, Bt);
+  // T^T (workspace), dT and dT^T (workspace)
+  rows(ntc, dim3((unsigned)((M + 15) / 16), 2), s, xc, xs, xr, M, K, A, r, nullptr, Tt, w.ldt, dy, N, B, scale, dT,
+       dTt);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  // T^T (workspace), dT and dT^T (workspace)
-  rows(ntc, dim3((unsigned)((M + 15) / 16), 2), s, xc, xs, xr, M, K, A, r, nullptr, Tt, w.ldt, dy, N, Bt, scale, dT,
-       dTt);
-  if ((e = hipGetLastError()) != hipSuccess) return e;
   const int64_t nblk = (int64_t)w.nstrip_b * w.nsplit_b + (int64_t)w.nstrip_a * w.nsplit_a;
   if (nblk == 0) return hipSuccess;
-#define PACT_COLS(NT) k_lora_cols<NT><<<(unsigned)nblk, 256, 0, s>>>(xc, xs, xr, M, K, dy, N, Tt, dTt, w.ldt, r,     \
-                                                                 w.nstrip_b, (int)w.nsplit_b, w.rows_b, w.nstrip_a, \
-                                                                 w.rows_a, pdB, pdA)
+#define PACT_COLS(NT)                                                                                          \
+  k_lora_cols<NT><<<(unsigned)nblk, 256, 0, s>>>(xc, xs, xr, M, K, dy, N, Tt, dTt, w.ldt, r, w.nstrip_b,           \
+                                                 (int)w.nsplit_b, w.rows_b, w.nstrip_a, w.rows_a,                  \
+                                                 pdB, pdA)
   if (ntc <= 1) PACT_COLS(1);
   else if (ntc <= 2) PACT_COLS(2);
   else if (ntc <= 4) PACT_COLS(4);
   else PACT_COLS(8);
 #undef PACT_COLS
   if ((e = hipGetLastError()) != hipSuccess) return e;
-  const int64_t tot = (N + K) * r;
-  k_lora_reduce<<<grid_for(tot), 256, 0, s>>>(pdB, pdA, (int)w.nsplit_b, (int)w.nsplit_a, N, K, r, scale, dB, dA);
+  const int64_t tot4 = (N + K) * r / 4;
+  k_lora_reduce<<<grid_for(tot4), 256, 0, s>>>(pdB, pdA, (int)w.nsplit_b, (int)w.nsplit_a, N, K, r, scale, dB, dA);
   return hipGetLastError();
 }
 
