@@ -115,6 +115,15 @@ def quantize_ex(x: torch.Tensor, transpose: bool = False, round_up: bool = False
     return out
 
 
+def selftest_arith(device="cuda") -> list:
+    """Disagreement counts of the device's arithmetic shortcuts against IEEE
+    operations over their whole input ranges (pact_selftest_arith); all 0 on a
+    conforming device."""
+    counts = torch.zeros((4,), dtype=torch.int64, device=device)
+    _lib.call("pact_selftest_arith", counts.data_ptr(), _stream())
+    return [int(v) for v in counts.cpu().tolist()]
+
+
 def weight_layouts(w: torch.Tensor):
     """Cached forward and backward layouts (Q(W), Q(W^T)) of a frozen BF16 weight W [N x K]."""
     return quantize(w), quantize(w, transpose=True)

@@ -69,7 +69,7 @@ extern "C" {
 
 const char* pact_last_error(void) { return g_err; }
 
-int pact_abi_version(void) { return 5; }
+int pact_abi_version(void) { return 6; }
 
 int pact_nvfp4_sizes(int64_t rows, int64_t cols, size_t* codes_bytes, size_t* scales_bytes, size_t* rscale_bytes) {
   REQUIRE(rows >= 0 && cols >= 0, PACT_EINVAL, "negative size (rows=%lld, cols=%lld)", (long long)rows,
@@ -327,6 +327,11 @@ int rmsnorm_bwd(const uint8_t* y_codes, const uint8_t* y_scales, const float* y_
   return hip_status(pact::launch_rmsnorm_bwd(y_codes, y_scales, y_rscale, rstd, gain, dy, M, H, nullptr, dx,
                                              nullptr, nullptr, nullptr, as_stream(stream)),
                     "rmsnorm_bwd launch");
+}
+
+int pact_selftest_arith(unsigned long long* counts, void* stream) {
+  REQUIRE(counts != nullptr, PACT_EINVAL, "NULL counts");
+  return hip_status(pact::launch_selftest_arith(counts, as_stream(stream)), "selftest launch");
 }
 
 int pact_nvfp4_row_exp_max(const uint8_t* codes, const uint8_t* scales, const float* rscale, int64_t rows,

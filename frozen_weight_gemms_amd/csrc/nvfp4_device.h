@@ -29,14 +29,40 @@ constexpr int kBlock = 16;
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
 
-// float -> bf16 bits, round to nearest even (finite inputs).
+// float -> bf16 bits, round to nearest even: the hardware conversion
+// (v_cvt_pk_bf16_f32), which equals integer RNE on the bit pattern,
+// u + 0x7FFF + ((u >> 16) & 1) >> 16, for every non-NaN input (the device
+// self-test checks all 2^32 patterns).
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 __device__ __forceinline__ uint32_t f32_to_bf16_rne(float f) {
-  uint32_t u = __float_as_uint(f);
-  u += 0x7FFFu + ((u >> 16) & 1u);
-  return u >> 16;
+  return (uint32_t)__builtin_bit_cast(uint16_t, (__bf16)f);
 }
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
-  return f32_to_bf16_rne(lo) | (f32_to_bf16_rne(hi) << 16);
+  const bf16x2_t v = {(__bf16)lo, (__bf16)hi};
+  return __builtin_bit_cast(uint32_t, v);
+}
+
+// Correctly rounded 1/d for d in [2^-126, 2^126) (normal d with a normal
+// reciprocal): the hardware estimate y, the exact residual e = 1 - d*y (one
+// FMA), then y + e*y rounded once.  Equal to IEEE division for every such d
+// (the device self-test checks them all).
+__device__ __forceinline__ float recip_rn(float d) {
+  const float y = __builtin_amdgcn_rcpf(d);
+  const float e = __builtin_fmaf(-d, y, 1.0f);
+  return __builtin_fmaf(e, y, y);
+}
+
+// Correctly rounded x / 6: q = x * RN(1/6), then one correction with the
+// exact remainder x - 6q (Markstein's division step).  Equal to IEEE division
+// for every x >= 6 * 2^-126 (a normal quotient; the device self-test checks
+// them all).  Below that both quotients are under 2^-126, far beneath the
+// smallest E4M3 step 2^-9, so the block-scale code is 0 either way (and the
+// round-up recipe decides with exact comparisons on x, not on the quotient).
+__device__ __forceinline__ float div6_rn(float x) {
+  const float c = __uint_as_float(0x3E2AAAABu);        // RN(1/6)
+  const float q = __fmul_rn(x, c);
+  const float r = __builtin_fmaf(-q, 6.0f, x);
+  return __builtin_fmaf(r, c, q);
 }
 
 // Smallest e with amax <= 2688 * 2^e (2688 = 1.3125 * 2^11), clamped; 0 for amax == 0.
@@ -80,7 +106,7 @@ struct BlockQ {
 // no saturation): round t = RN32(X / 6) up on the grid, then correct by one
 // step with exact comparisons (6 * value has at most 6 significant bits).
 __device__ __forceinline__ uint32_t e4m3_encode_up(float X) {
-  const float t = __fdiv_rn(X, 6.0f);
+  const float t = div6_rn(X);
   uint32_t c = e4m3_encode(t);                         // nearest, then step to the ceiling
   if (c < 0x7Eu && 6.0f * e4m3_decode(c) < X) ++c;
   if (c > 0u && 6.0f * e4m3_decode(c - 1u) >= X) --c;
@@ -91,9 +117,9 @@ __device__ __forceinline__ BlockQ block_setup(float bmax, float r, float inv_r, 
   (void)r;
   BlockQ q;
   const float X = bmax * inv_r;                        // exact: r is a power of two
-  q.sc = round_up ? e4m3_encode_up(X) : e4m3_encode(__fdiv_rn(X, 6.0f));
+  q.sc = round_up ? e4m3_encode_up(X) : e4m3_encode(div6_rn(X));
   q.s = e4m3_decode(q.sc);
-  q.rcp = q.s != 0.0f ? __fdiv_rn(1.0f, q.s) : 0.0f;
+  q.rcp = q.s != 0.0f ? recip_rn(q.s) : 0.0f;          // s >= 2^-9: normal, with a normal reciprocal
   q.inv_r = inv_r;
   return q;
 }
@@ -136,6 +162,11 @@ __device__ __forceinline__ void unpack_bf16x8(const uint4& v, float* x) {
 __device__ __forceinline__ float wave_max(float v) {
 #pragma unroll
   for (int o = 32; o >= 1; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
+  return v;
+}
+__device__ __forceinline__ uint64_t wave_sum_u64(uint64_t v) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o, 64);
   return v;
 }
 __device__ __forceinline__ float wave_sum(float v) {

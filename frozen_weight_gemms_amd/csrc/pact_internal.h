@@ -18,6 +18,7 @@ hipError_t launch_quantize_ex(const uint16_t* x, int64_t rows, int64_t cols, int
                               int round_up, const float* tensor_amax, uint8_t* codes, uint8_t* scales,
                               float* rscale, hipStream_t s);
 // *amax = max |x| over x [rows x cols] (row stride ldx)
+hipError_t launch_selftest_arith(unsigned long long* counts, hipStream_t s);
 hipError_t launch_tensor_absmax(const uint16_t* x, int64_t rows, int64_t cols, int64_t ldx, float* amax,
                                 hipStream_t s);
 

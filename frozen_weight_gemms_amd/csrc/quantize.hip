@@ -315,6 +315,52 @@ __global__ __launch_bounds__(kThreads) void k_silu_mul_quant(const uint16_t* __r
 }
 
 // --------------------------------------------------------------------------
+// Device self-test of the arithmetic shortcuts the kernels rely on, checked
+// exhaustively over every input bit pattern in the stated range against the
+// IEEE operation they replace (counts of disagreements, one per check):
+//   0: recip_rn(d) == 1/d               d in [2^-126, 2^126)
+//   1: div6_rn(x) == x/6                x in [6 * 2^-126, FLT_MAX] (normal quotient)
+//   2: sigmoid_pinned(a) == 1/(1 + E(-a)), IEEE division   every non-NaN a
+//   3: f32_to_bf16_rne(x) == integer RNE of the bit pattern  every non-NaN x
+// --------------------------------------------------------------------------
+__global__ __launch_bounds__(kThreads) void k_selftest_arith(int which, uint64_t lo, uint64_t hi,
+                                                             unsigned long long* __restrict__ count) {
+  const uint64_t step = (uint64_t)gridDim.x * kThreads;
+  unsigned long long bad = 0;
+  for (uint64_t u = lo + (uint64_t)blockIdx.x * kThreads + threadIdx.x; u <= hi; u += step) {
+    const float x = __uint_as_float((uint32_t)u);
+    if (x != x) continue;
+    bool ok;
+    if (which == 0) {
+      ok = __float_as_uint(recip_rn(x)) == __float_as_uint(__fdiv_rn(1.0f, x));
+    } else if (which == 1) {
+      ok = __float_as_uint(div6_rn(x)) == __float_as_uint(__fdiv_rn(x, 6.0f));
+    } else if (which == 2) {
+      const float ref = __fdiv_rn(1.0f, __fadd_rn(1.0f, exp_pinned(-x)));
+      ok = __float_as_uint(sigmoid_pinned(x)) == __float_as_uint(ref);
+    } else {
+      const uint32_t b = __float_as_uint(x);
+      ok = f32_to_bf16_rne(x) == ((b + 0x7FFFu + ((b >> 16) & 1u)) >> 16);
+    }
+    bad += ok ? 0ull : 1ull;
+  }
+  bad = (unsigned long long)wave_sum_u64(bad);
+  if ((threadIdx.x & 63) == 0 && bad != 0) atomicAdd(count + which, bad);
+}
+
+__global__ void k_zero_u64x4(unsigned long long* p) {
+  if (threadIdx.x < 4) p[threadIdx.x] = 0ull;
+}
+
+hipError_t launch_selftest_arith(unsigned long long* counts, hipStream_t s) {
+  k_zero_u64x4<<<1, 64, 0, s>>>(counts);
+  const uint64_t lo[4] = {0x00800000ull, 0x01C00000ull, 0ull, 0ull};
+  const uint64_t hi[4] = {0x7E7FFFFFull, 0x7F7FFFFFull, 0xFFFFFFFFull, 0xFFFFFFFFull};
+  for (int w = 0; w < 4; ++w) k_selftest_arith<<<8192, kThreads, 0, s>>>(w, lo[w], hi[w], counts);
+  return hipGetLastError();
+}
+
+// --------------------------------------------------------------------------
 // launchers
 // --------------------------------------------------------------------------
 static int chunks_per_thread(int64_t cols) { return (int)(((cols >> 3) + kThreads - 1) / kThreads); }

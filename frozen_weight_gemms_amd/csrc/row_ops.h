@@ -70,9 +70,15 @@ __device__ __forceinline__ float exp_pinned(float x) {
   return e;
 }
 
-// sigma(a) = 1 / (1 + E(-a)) in the pinned FP32 sequence (0 when E overflows).
+// sigma(a) = 1 / (1 + E(-a)) in the pinned FP32 sequence (0 when E overflows),
+// the division correctly rounded: recip_rn while 1 + E < 2^126, IEEE division
+// beyond (a < -87, where the reciprocal is subnormal or 0).
 __device__ __forceinline__ float sigmoid_pinned(float a) {
-  return __fdiv_rn(1.0f, __fadd_rn(1.0f, exp_pinned(-a)));
+  const float d = __fadd_rn(1.0f, exp_pinned(-a));
+  float sig;
+  if (d < 0x1p126f) sig = recip_rn(d);
+  else sig = __fdiv_rn(1.0f, d);
+  return sig;
 }
 
 __device__ __forceinline__ float silu_mul(float a, float b) {

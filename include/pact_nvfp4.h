@@ -61,6 +61,25 @@ const char *pact_last_error(void);
 /* Interface version (incremented on any change of signature or semantics). */
 int pact_abi_version(void);
 
+/*
+ * pact_selftest_arith -- device self-test of the arithmetic shortcuts inside
+ * the kernels, each checked against the IEEE operation it stands for over
+ * every input bit pattern of its range.  counts: device array of 4 unsigned
+ * 64-bit integers (caller-owned), set to the number of disagreements of
+ *   [0] the correctly rounded reciprocal (hardware estimate + one FMA
+ *       correction), d in [2^-126, 2^126);
+ *   [1] the correctly rounded division by 6 (reciprocal product + one FMA
+ *       correction), every x in [6 * 2^-126, FLT_MAX] (a normal quotient;
+ *       below it the block-scale code is 0 whatever the quotient's low bits);
+ *   [2] the SiLU sigmoid 1/(1 + E(-a)) with that reciprocal (IEEE division
+ *       past 1 + E >= 2^126), every non-NaN a;
+ *   [3] the hardware float -> BF16 conversion against integer round to
+ *       nearest even on the bit pattern, every non-NaN x.
+ * All four are 0 on a conforming device.  Asynchronous on `stream`; about
+ * 1.3e10 evaluations (well under a second on one GPU).
+ */
+int pact_selftest_arith(unsigned long long *counts, void *stream);
+
 /* Host-only size query: bytes of the three buffers of an NVFP4 [rows x cols]. */
 int pact_nvfp4_sizes(int64_t rows, int64_t cols, size_t *codes_bytes, size_t *scales_bytes,
                      size_t *rscale_bytes);
