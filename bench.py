@@ -65,6 +65,8 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true", help="skip the oracle timing on host cores")
     ap.add_argument("--cpu-sample-rows", type=int, default=256)
     ap.add_argument("--eager", action="store_true", help="time eager launches instead of a captured HIP graph")
+    ap.add_argument("--sequential", action="store_true",
+                    help="one stream: no concurrent branches (q/k/v and gate/up forward, their LoRA backwards)")
     ap.add_argument("--layers", type=int, default=4,
                     help="distinct decoder-layer instances a step runs through (their weights and buffers "
                          "together exceed the 256 MB last-level cache, so every operand streams from HBM)")
@@ -115,9 +117,12 @@ class Layer:
                                      dA=torch.empty((r, p.d_in), dtype=torch.bfloat16, device=dev),
                                      dB=torch.empty((p.d_out, r), dtype=torch.bfloat16, device=dev),
                                      dyq=fw.empty_nvfp4(M, p.d_out, dev))
-        # one LoRA-backward workspace sized for the largest projection (calls are stream-ordered)
-        ws_bytes = max(fw._lib.lora_bwd_workspace_size(M, p.d_in, p.d_out, r) for p in wl.projections)
-        self.lora_ws = torch.empty((ws_bytes,), dtype=torch.uint8, device=dev)
+        # a LoRA-backward workspace per projection (the gate/up and q/k/v LoRA
+        # backwards may run concurrently on side streams)
+        for P in self.proj.values():
+            p = P["p"]
+            P["ws"] = torch.empty((fw._lib.lora_bwd_workspace_size(M, p.d_in, p.d_out, r),), dtype=torch.uint8,
+                                  device=dev)
         nv = lambda cols: fw.empty_nvfp4(M, cols, dev)
         self.y1q, self.y2q, self.aq = nv(H), nv(H), nv(H)
         self.rstd1 = torch.empty((M,), dtype=torch.float32, device=dev)
@@ -130,6 +135,7 @@ class Layer:
         self.dh2, self.dh1 = bf(H), bf(H)                   # residual-stream gradients (BF16)
         self.dh2q, self.dh1q = nv(H), nv(H)                 # their NVFP4 copies
         self.record = None       # list to append (category, name, start_event, end_event, work) into
+        self.streams = None      # two side streams: independent branches of the step run concurrently
 
     # ---- instrumented launch helper ----
     def _ev(self, cat, name, work, fn):
@@ -152,9 +158,9 @@ class Layer:
                  lambda: fw.gemm_fwd(xq, P["wf"], lora_t=P["T"], lora_b=P["B"], lora_scale=LORA_SCALE, out=P["Y"]))
         return P["Y"]
 
-    def _bwd_proj(self, name, xq, dy, dx, accumulate, dyq=None):
-        """LoRA backward and input-gradient GEMM of one projection; dY is
-        quantized here unless its NVFP4 copy comes from a fused kernel."""
+    def _bwd_lora(self, name, xq, dy, dyq=None):
+        """dY's NVFP4 copy (unless a fused kernel made it) and the LoRA
+        backward of one projection; returns the NVFP4 dY."""
         fw, P = self.fw, self.proj[name]
         p = P["p"]
         if dyq is None:
@@ -162,25 +168,63 @@ class Layer:
             self._ev("quant", "nvfp4_quantize", ("quant", self.M, p.d_out), lambda: fw.quantize(dy, out=dyq))
         self._ev("lora", "lora_bwd", None,
                  lambda: fw.lora_bwd(xq, P["A"], P["B"], dy, LORA_SCALE, out=(P["dT"], P["dA"], P["dB"]),
-                                     workspace=self.lora_ws))
+                                     workspace=P["ws"]))
+        return dyq
+
+    def _bwd_dgrad(self, name, dyq, dx, accumulate):
+        """Input-gradient GEMM of one projection with its LoRA term dT A."""
+        fw, P = self.fw, self.proj[name]
+        p = P["p"]
         work = ("gemm", self.M, p.d_in, p.d_out)
         self._ev("gemm", f"dgrad {name}", work,
                  lambda: fw.gemm_dgrad(dyq, P["wb"], out=dx, accumulate=accumulate, lora_dt=P["dT"],
                                        lora_a=P["A"]))
+
+    def _bwd_proj(self, name, xq, dy, dx, accumulate, dyq=None):
+        self._bwd_dgrad(name, self._bwd_lora(name, xq, dy, dyq), dx, accumulate)
+
+    def _fork(self, fns):
+        """Launch fns on the side streams, each after the current stream's
+        work so far; returns a join function that makes the current stream wait
+        for side branch i (or all of them).  Without side streams (or while the
+        step is instrumented) the branches run in place, in order."""
+        if self.streams is None or self.record is not None:
+            for f in fns:
+                f()
+            return lambda i=None: None
+        torch = self.torch
+        cur = torch.cuda.current_stream()
+        side = self.streams[:len(fns)]
+        for st, f in zip(side, fns):
+            st.wait_stream(cur)
+            with torch.cuda.stream(st):
+                f()
+
+        def join(i=None):
+            for st in (side if i is None else [side[i]]):
+                cur.wait_stream(st)
+        return join
+
+    def _branches(self, fns):
+        """fns[0] on the current stream, fns[1:] concurrently on side streams;
+        the current stream then waits for all of them."""
+        join = self._fork(fns[1:])
+        fns[0]()
+        join()
 
     def forward(self):
         fw = self.fw
         M, H, I = self.M, self.H, self.I
         self._ev("quant", "rmsnorm_quant", ("rmsq", M, H),
                  lambda: fw.rmsnorm_quant(self.h1, self.g1, 1e-5, out=(self.y1q, self.rstd1)))
-        for n in ("q", "k", "v"):
-            self._fwd_proj(n, self.y1q)
+        # q, k and v read the same NVFP4 input and are independent
+        self._branches([lambda n=n: self._fwd_proj(n, self.y1q) for n in ("q", "k", "v")])
         self._ev("quant", "nvfp4_quantize", ("quant", M, H), lambda: fw.quantize(self.attn, out=self.aq))
         self._fwd_proj("o", self.aq)
         self._ev("quant", "rmsnorm_quant", ("rmsq", M, H),
                  lambda: fw.rmsnorm_quant(self.h2, self.g2, 1e-5, out=(self.y2q, self.rstd2)))
-        a = self._fwd_proj("gate", self.y2q)
-        b = self._fwd_proj("up", self.y2q)
+        self._branches([lambda: self._fwd_proj("gate", self.y2q), lambda: self._fwd_proj("up", self.y2q)])
+        a, b = self.proj["gate"]["Y"], self.proj["up"]["Y"]
         self._ev("quant", "silu_mul_quant", ("silu", M, I),
                  lambda: fw.silu_mul_quant(a, b, out=(self.hq, self.gq, self.uq)))
         self._fwd_proj("down", self.hq)
@@ -195,17 +239,26 @@ class Layer:
         self._bwd_proj("down", self.hq, dout, self.dh, False, dyq=dout_q)
         self._ev("bwd", "silu_mul_bwd_quant", ("silubq", M, I),
                  lambda: fw.silu_mul_bwd_quant(self.gq, self.uq, self.dh, out=(self.da, self.db, self.daq, self.dbq)))
+        # the up projection's LoRA backward runs beside the gate projection's
+        # LoRA backward and input-gradient GEMM; the two input-gradient GEMMs
+        # accumulate into one dX in order
+        join = self._fork([lambda: self._bwd_lora("up", self.y2q, self.db, self.dbq)])
         self._bwd_proj("gate", self.y2q, self.da, self.dy2, False, dyq=self.daq)
-        self._bwd_proj("up", self.y2q, self.db, self.dy2, True, dyq=self.dbq)
+        join()
+        self._bwd_dgrad("up", self.dbq, self.dy2, True)
         self._ev("bwd", "rmsnorm_bwd_residual", ("rmsbr", M, H),
                  lambda: fw.rmsnorm_bwd_residual(self.y2q, self.rstd2, self.g2, self.dy2, resid=dout,
                                                  out=(self.dh2, self.dh2q)))
         # attention block: h2 = h1 + o(attn(q, k, v of n1)),  n1 = rmsnorm(h1); the
         # attention backward itself is not part of the path (dq, dk, dv are inputs)
         self._bwd_proj("o", self.aq, self.dh2, self.dattn, False, dyq=self.dh2q)
+        join = self._fork([lambda: self._bwd_lora("k", self.y1q, self.dk),
+                           lambda: self._bwd_lora("v", self.y1q, self.dv)])
         self._bwd_proj("q", self.y1q, self.dq, self.dy1, False)
-        self._bwd_proj("k", self.y1q, self.dk, self.dy1, True)
-        self._bwd_proj("v", self.y1q, self.dv, self.dy1, True)
+        join(0)
+        self._bwd_dgrad("k", self.proj["k"]["dyq"], self.dy1, True)
+        join(1)
+        self._bwd_dgrad("v", self.proj["v"]["dyq"], self.dy1, True)
         self._ev("bwd", "rmsnorm_bwd_residual", ("rmsbr", M, H),
                  lambda: fw.rmsnorm_bwd_residual(self.y1q, self.rstd1, self.g1, self.dy1, resid=self.dh2,
                                                  out=(self.dh1, self.dh1q)))
@@ -585,6 +638,13 @@ def main():
     torch.cuda.set_device(0)
     layers = [Layer(fw, torch, synth, wl, li) for li in range(max(1, args.layers))]
     layer = layers[0]
+    # independent branches of the step (the q/k/v and gate/up forward
+    # projections, the LoRA backwards beside the input-gradient GEMMs) go to
+    # two side streams at default priority, forked from and joined back into
+    # the launch stream
+    side_streams = None if args.sequential else [torch.cuda.Stream(), torch.cuda.Stream()]
+    for ly in layers:
+        ly.streams = side_streams
     torch.cuda.synchronize()
     resident = torch.cuda.memory_allocated()
 
@@ -640,6 +700,26 @@ def main():
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     gpu_ms = ev0.elapsed_time(ev1)
+
+    # the concurrent schedule computes what the one-stream order does, bit for
+    # bit (same kernels, same inputs; only their overlap differs)
+    def snapshot():
+        return [t.clone() for t in (layers[0].dh1, layers[0].dy1, layers[-1].proj["v"]["Y"],
+                                    layers[0].proj["up"]["dB"], layers[-1].proj["k"]["dB"],
+                                    layers[0].proj["q"]["dT"])]
+    run()
+    torch.cuda.synchronize()
+    conc = snapshot()
+    for ly in layers:
+        ly.streams = None
+    step()
+    torch.cuda.synchronize()
+    seq = snapshot()
+    for ly in layers:
+        ly.streams = side_streams
+    schedule_matches = all(torch.equal(a.view(torch.int16), b.view(torch.int16)) for a, b in zip(conc, seq))
+    if not schedule_matches:
+        print("concurrent schedule differs from the one-stream order", file=sys.stderr)
 
     # instrumented pass over the same K steps: events around every launch give
     # per-kernel durations (events add queue overhead between kernels, so this
@@ -724,6 +804,10 @@ def main():
         "gemm_only_tflops": round(flops / (gemm_ms * 1e-3) / 1e12, 1),
         "gpu_ms_per_step_events": round(gpu_ms / steps, 4),
         "timed_region": "hip graph replays of the step" if graph is not None else "eager steps",
+        "schedule": ("one stream" if side_streams is None else
+                     "independent branches on 2 side streams (q/k/v and gate/up forward; LoRA backwards beside "
+                     "the input-gradient GEMMs)"),
+        "schedule_matches_one_stream": schedule_matches,
         "kernel_ms_per_step_by_category": {k: round(v / steps, 4) for k, v in sorted(cat_ms.items())},
         "bandwidth_kernels": quant,
         "roofline": {"kernel": kname, "bound": "mfma", "achieved": round(achieved, 1),
