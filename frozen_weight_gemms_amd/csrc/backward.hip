@@ -128,79 +128,132 @@ __global__ __launch_bounds__(256) void k_silu_mul_bwd_quant(
 
 // RMSNorm backward, optionally + residual gradient and + NVFP4 copy of the
 // result.  One 256-thread workgroup per row; NCH 8-element chunks per thread.
-template <int NCH>
+// One row per WPR waves (the quantizer's row layout): lane l of the row's
+// wave p owns the 16-element blocks l + 64 p + 64 WPR i.  Between passes it
+// keeps the raw codes, scale byte and BF16 bits of its blocks and decodes them
+// again where needed (the same operations, so the same values).
+template <int NB, int WPR>
 __global__ __launch_bounds__(256) void k_rmsnorm_bwd(const uint8_t* __restrict__ yc, const uint8_t* __restrict__ ys,
                                                      const float* __restrict__ yr, const float* __restrict__ rstd,
                                                      const uint16_t* __restrict__ gain, const uint16_t* __restrict__ dy,
-                                                     int64_t H, const uint16_t* __restrict__ resid,
+                                                     int64_t M, int64_t H, const uint16_t* __restrict__ resid,
                                                      uint16_t* __restrict__ dx, uint8_t* __restrict__ qc,
                                                      uint8_t* __restrict__ qs, float* __restrict__ qr) {
   __shared__ double dred[2][4];
   __shared__ float red[4];
-  const int64_t row = blockIdx.x;
-  const int nchunk = (int)(H >> 3);
-  float y[NCH][8], d[NCH][8];
-  double sh = 0.0, sl = 0.0;                   // double-double partial of sum dy y^ (each product exact)
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int part = wave % WPR;
+  const int64_t row0 = (int64_t)blockIdx.x * (4 / WPR) + wave / WPR;
+  const bool row_ok = row0 < M;                        // uniform per wave (no early exit: barriers below)
+  const int64_t row = row_ok ? row0 : 0;
+  const int nblk = (int)(H >> 4);
   const float rr = yr[row];
+  uint2 cw[NB];                                        // 16 codes
+  float sm[NB];                                        // block scale * row scale
+  uint4 dv[NB][2];                                     // 16 BF16 dy
+  double sh = 0.0, sl = 0.0;                           // double-double partial of sum dy y^ (each product exact)
 #pragma unroll
-  for (int i = 0; i < NCH; ++i) {
-    const int c = threadIdx.x + 256 * i;
-    if (c < nchunk) {
-      const uint32_t w = *reinterpret_cast<const uint32_t*>(yc + row * (H >> 1) + 4 * c);
-      decode8_f32(w, e4m3_decode(ys[row * (H >> 4) + (c >> 1)]) * rr, y[i]);
-      unpack_bf16x8(load16(dy + row * H + 8 * c), d[i]);
-    } else {
+  for (int i = 0; i < NB; ++i) {
+    const int blk = lane + 64 * part + 64 * WPR * i;
+    const bool ok = row_ok && blk < nblk;
+    cw[i] = ok ? *reinterpret_cast<const uint2*>(yc + row * (H >> 1) + 8 * blk) : make_uint2(0, 0);
+    sm[i] = ok ? e4m3_decode(ys[row * (H >> 4) + blk]) * rr : 0.0f;
+    dv[i][0] = ok ? load16(dy + row * H + 16 * blk) : make_uint4(0, 0, 0, 0);
+    dv[i][1] = ok ? load16(dy + row * H + 16 * blk + 8) : make_uint4(0, 0, 0, 0);
+  }
 #pragma unroll
-      for (int t = 0; t < 8; ++t) { y[i][t] = 0.0f; d[i][t] = 0.0f; }
-    }
+  for (int i = 0; i < NB; ++i) {
 #pragma unroll
-    for (int t = 0; t < 8; ++t) {
-      double s, e;
-      two_sum(sh, (double)d[i][t] * (double)y[i][t], s, e);
-      sh = s;
-      sl += e;
+    for (int h = 0; h < 2; ++h) {
+      float y[8], d[8];
+      decode8_f32(h ? cw[i].y : cw[i].x, sm[i], y);
+      unpack_bf16x8(dv[i][h], d);
+#pragma unroll
+      for (int t = 0; t < 8; ++t) {
+        double s2, e2;
+        two_sum(sh, (double)d[t] * (double)y[t], s2, e2);
+        sh = s2;
+        sl += e2;
+      }
     }
   }
-  const double S = block_sum_dd(sh, sl, dred);
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) {
+    const double oh = __shfl_xor(sh, o, 64), ol = __shfl_xor(sl, o, 64);
+    double s2, e2;
+    two_sum(sh, oh, s2, e2);
+    sh = s2;
+    sl = sl + ol + e2;
+  }
+  if constexpr (WPR > 1) {
+    if (lane == 0) { dred[0][wave] = sh; dred[1][wave] = sl; }
+    __syncthreads();
+    const int w0 = wave - part;
+    sh = dred[0][w0];
+    sl = dred[1][w0];
+    for (int k = 1; k < WPR; ++k) {
+      double s2, e2;
+      two_sum(sh, dred[0][w0 + k], s2, e2);
+      sh = s2;
+      sl = sl + dred[1][w0 + k] + e2;
+    }
+  }
+  const double S = sh + sl;                            // the double-double value rounded once to float64
   const float mean = (float)(S / (double)H);
   const float rs = rstd[row];
-  uint4 out[NCH];
+  uint4 out[NB][2];
   float lmax = 0.0f;
 #pragma unroll
-  for (int i = 0; i < NCH; ++i) {
-    const int c = threadIdx.x + 256 * i;
-    out[i] = make_uint4(0, 0, 0, 0);
-    if (c >= nchunk) continue;
-    float g[8], o[8];
-    unpack_bf16x8(load16(gain + 8 * c), g);
+  for (int i = 0; i < NB; ++i) {
+    const int blk = lane + 64 * part + 64 * WPR * i;
+    out[i][0] = out[i][1] = make_uint4(0, 0, 0, 0);
+    if (!row_ok || blk >= nblk) continue;
 #pragma unroll
-    for (int t = 0; t < 8; ++t)
-      o[t] = __fmul_rn(rs, __fsub_rn(__fmul_rn(g[t], d[i][t]), __fmul_rn(__fdiv_rn(y[i][t], g[t]), mean)));
-    if (resid != nullptr) {
-      float rv[8];
-      unpack_bf16x8(load16(resid + row * H + 8 * c), rv);
+    for (int h = 0; h < 2; ++h) {
+      float y[8], d[8], g[8], o[8];
+      decode8_f32(h ? cw[i].y : cw[i].x, sm[i], y);
+      unpack_bf16x8(dv[i][h], d);
+      unpack_bf16x8(load16(gain + 16 * blk + 8 * h), g);
 #pragma unroll
-      for (int t = 0; t < 8; ++t) o[t] = __fadd_rn(__uint_as_float(f32_to_bf16_rne(o[t]) << 16), rv[t]);
+      for (int t = 0; t < 8; ++t)
+        o[t] = __fmul_rn(rs, __fsub_rn(__fmul_rn(g[t], d[t]), __fmul_rn(__fdiv_rn(y[t], g[t]), mean)));
+      if (resid != nullptr) {
+        float rv[8];
+        unpack_bf16x8(load16(resid + row * H + 16 * blk + 8 * h), rv);
+#pragma unroll
+        for (int t = 0; t < 8; ++t) o[t] = __fadd_rn(__uint_as_float(f32_to_bf16_rne(o[t]) << 16), rv[t]);
+      }
+      uint4 v;
+      v.x = pack_bf16x2(o[0], o[1]); v.y = pack_bf16x2(o[2], o[3]);
+      v.z = pack_bf16x2(o[4], o[5]); v.w = pack_bf16x2(o[6], o[7]);
+      *reinterpret_cast<uint4*>(dx + row * H + 16 * blk + 8 * h) = v;
+      out[i][h] = v;
+      lmax = fmaxf(lmax, absmax_bf16x8(v));
     }
-    uint4 v;
-    v.x = pack_bf16x2(o[0], o[1]); v.y = pack_bf16x2(o[2], o[3]);
-    v.z = pack_bf16x2(o[4], o[5]); v.w = pack_bf16x2(o[6], o[7]);
-    *reinterpret_cast<uint4*>(dx + row * H + 8 * c) = v;
-    out[i] = v;
-    lmax = fmaxf(lmax, absmax_bf16x8(v));
   }
-  if (qc != nullptr) {                         // uniform: a kernel argument
-    const float amax = block_max_256(lmax, red);
+  if (qc != nullptr) {                                 // uniform: a kernel argument
+    float amax = wave_max(lmax);
+    if constexpr (WPR > 1) {
+      if (lane == 0) red[wave] = amax;
+      __syncthreads();
+      const int w0 = wave - part;
+#pragma unroll
+      for (int k = 0; k < WPR; ++k) amax = fmaxf(amax, red[w0 + k]);
+    }
+    if (!row_ok) return;
     const int e = row_exponent(amax);
     const float r = pow2f(e), ir = pow2f(-e);
 #pragma unroll
-    for (int i = 0; i < NCH; ++i) {
-      const int c = threadIdx.x + 256 * i;
-      float f[8];
-      unpack_bf16x8(out[i], f);
-      quant_chunk(f, c < nchunk, r, ir, qc + row * (H >> 1), qs + row * (H >> 4), c);
+    for (int i = 0; i < NB; ++i) {
+      const int blk = lane + 64 * part + 64 * WPR * i;
+      if (blk < nblk) {
+        float f[16];
+        unpack_bf16x8(out[i][0], f);
+        unpack_bf16x8(out[i][1], f + 8);
+        quant_block16(f, fmaxf(absmax8(f), absmax8(f + 8)), r, ir, qc + row * (H >> 1), qs + row * (H >> 4), blk);
+      }
     }
-    if (threadIdx.x == 0) qr[row] = r;
+    if (lane == 0 && part == 0) qr[row] = r;
   }
 }
 
@@ -234,14 +287,23 @@ hipError_t launch_rmsnorm_bwd(const uint8_t* yc, const uint8_t* ys, const float*
                               const uint16_t* gain, const uint16_t* dy, int64_t M, int64_t H,
                               const uint16_t* resid, uint16_t* dx, uint8_t* qc, uint8_t* qs, float* qr,
                               hipStream_t s) {
-  const int nch = (int)(((H >> 3) + 255) / 256);
-  const dim3 grid((unsigned)M);
-#define PACT_RMSB(n) k_rmsnorm_bwd<n><<<grid, 256, 0, s>>>(yc, ys, yr, rstd, gain, dy, H, resid, dx, qc, qs, qr)
-  if (nch <= 1) PACT_RMSB(1);
-  else if (nch <= 2) PACT_RMSB(2);
-  else if (nch <= 4) PACT_RMSB(4);
-  else if (nch <= 8) PACT_RMSB(8);
-  else return hipErrorInvalidValue;
+  // the quantizer's row layout: blocks per lane <= 4 (one wave per row up to
+  // 4096 columns, two up to 8192, four up to 16384)
+  const int64_t nblk = H >> 4;
+  if (nblk > 1024) return hipErrorInvalidValue;
+  const int wpr = nblk <= 256 ? 1 : (nblk <= 512 ? 2 : 4);
+  const int64_t nb = (nblk + 64 * wpr - 1) / (64 * wpr);
+  const dim3 grid((unsigned)((M + 4 / wpr - 1) / (4 / wpr)));
+#define PACT_RMSB(N, W) \
+  k_rmsnorm_bwd<N, W><<<grid, 256, 0, s>>>(yc, ys, yr, rstd, gain, dy, M, H, resid, dx, qc, qs, qr)
+  if (wpr == 1 && nb <= 1) PACT_RMSB(1, 1);
+  else if (wpr == 1 && nb <= 2) PACT_RMSB(2, 1);
+  else if (wpr == 1 && nb <= 3) PACT_RMSB(3, 1);
+  else if (wpr == 1) PACT_RMSB(4, 1);
+  else if (wpr == 2 && nb <= 3) PACT_RMSB(3, 2);
+  else if (wpr == 2) PACT_RMSB(4, 2);
+  else if (nb <= 3) PACT_RMSB(3, 4);
+  else PACT_RMSB(4, 4);
 #undef PACT_RMSB
   return hipGetLastError();
 }

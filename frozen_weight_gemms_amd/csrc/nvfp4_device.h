@@ -124,13 +124,13 @@ __device__ __forceinline__ BlockQ block_setup(float bmax, float r, float inv_r, 
   return q;
 }
 
-// Correctly rounded |x| / (s r) with the sign of x (0 with x's sign if s == 0).
+// Correctly rounded |x| / (s r) with the sign of x (0 with x's sign if s == 0:
+// then rcp == 0, so q0 == 0, rem == ax and the correction adds ax * 0).
 __device__ __forceinline__ float block_quot(float x, const BlockQ& q) {
   const float ax = fabsf(x) * q.inv_r;
   const float q0 = __fmul_rn(ax, q.rcp);
   const float rem = __builtin_fmaf(-q0, q.s, ax);
-  float v = __builtin_fmaf(rem, q.rcp, q0);
-  v = q.s != 0.0f ? v : 0.0f;
+  const float v = __builtin_fmaf(rem, q.rcp, q0);
   return __builtin_copysignf(v, x);
 }
 

@@ -20,44 +20,70 @@ namespace pact {
 // --------------------------------------------------------------------------
 // nvfp4_quantize, row-wise
 // --------------------------------------------------------------------------
-template <int NCH>
-__global__ __launch_bounds__(kThreads) void k_quantize_rows(const uint16_t* __restrict__ x, int64_t cols,
-                                                            int64_t ldx, uint8_t* __restrict__ codes,
+// Row-wise quantizer: WPR waves per row (1, 2 or 4), 4 / WPR rows per
+// workgroup.  Lane l of the row's wave p owns the 16-element blocks
+// l + 64 p + 64 WPR i (two 16-byte loads each), so every block's scale is set
+// up once by the lane that holds it; the row maximum is a wave reduction,
+// exchanged through LDS when a row spans several waves.  NB = blocks per lane.
+template <int NB, int WPR>
+__global__ __launch_bounds__(kThreads) void k_quantize_rows(const uint16_t* __restrict__ x, int64_t rows,
+                                                            int64_t cols, int64_t ldx, uint8_t* __restrict__ codes,
                                                             uint8_t* __restrict__ scales,
                                                             float* __restrict__ rscale, int round_up,
                                                             const float* __restrict__ tensor_amax) {
   __shared__ float red[4];
-  const int64_t row = blockIdx.x;
-  const int nchunk = (int)(cols >> 3);
-  const uint16_t* xr = x + row * ldx;
-  uint4 v[NCH];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int part = wave % WPR;
+  const int64_t row = (int64_t)blockIdx.x * (4 / WPR) + wave / WPR;
+  const bool row_ok = row < rows;                      // uniform per wave (no early exit: barrier below)
+  const int nblk = (int)(cols >> 4);
+  const uint16_t* xr = x + (row_ok ? row : 0) * ldx;
+  uint4 v[NB][2];
+  float bm[NB];
   float lmax = 0.0f;
 #pragma unroll
-  for (int i = 0; i < NCH; ++i) {
-    const int c = threadIdx.x + kThreads * i;
-    v[i] = c < nchunk ? load16(xr + 8 * c) : make_uint4(0, 0, 0, 0);
-    float f[8];
-    unpack_bf16x8(v[i], f);
-    lmax = fmaxf(lmax, absmax8(f));
+  for (int i = 0; i < NB; ++i) {
+    const int blk = lane + 64 * part + 64 * WPR * i;
+    const bool ok = row_ok && blk < nblk;
+    v[i][0] = ok ? load16(xr + 16 * blk) : make_uint4(0, 0, 0, 0);
+    v[i][1] = ok ? load16(xr + 16 * blk + 8) : make_uint4(0, 0, 0, 0);
+    float f[16];
+    unpack_bf16x8(v[i][0], f);
+    unpack_bf16x8(v[i][1], f + 8);
+    bm[i] = fmaxf(absmax8(f), absmax8(f + 8));
+    lmax = fmaxf(lmax, bm[i]);
   }
-  // tensor_amax (a kernel argument, uniform): one scale for every row
-  const float amax = tensor_amax != nullptr ? *tensor_amax : block_max_256(lmax, red);
+  float amax;
+  if (tensor_amax != nullptr) {                        // a kernel argument, uniform: one scale for every row
+    amax = *tensor_amax;
+  } else {
+    amax = wave_max(lmax);
+    if constexpr (WPR > 1) {
+      if (lane == 0) red[wave] = amax;
+      __syncthreads();
+      const int w0 = wave - part;
+#pragma unroll
+      for (int k = 0; k < WPR; ++k) amax = fmaxf(amax, red[w0 + k]);
+    }
+  }
+  if (!row_ok) return;
   const int e = row_exponent(amax);
   const float r = pow2f(e), inv_r = pow2f(-e);
   uint8_t* crow = codes + row * (cols >> 1);
   uint8_t* srow = scales + row * (cols >> 4);
 #pragma unroll
-  for (int i = 0; i < NCH; ++i) {
-    const int c = threadIdx.x + kThreads * i;
-    float f[8];
-    unpack_bf16x8(v[i], f);
-    quant_chunk(f, c < nchunk, r, inv_r, crow, srow, c, round_up != 0);
+  for (int i = 0; i < NB; ++i) {
+    const int blk = lane + 64 * part + 64 * WPR * i;
+    if (blk < nblk) {
+      float f[16];
+      unpack_bf16x8(v[i][0], f);
+      unpack_bf16x8(v[i][1], f + 8);
+      quant_block16(f, bm[i], r, inv_r, crow, srow, blk, round_up != 0);
+    }
   }
-  if (threadIdx.x == 0) rscale[row] = r;
+  if (lane == 0 && part == 0) rscale[row] = r;
 }
 
-// Rows longer than 256 * 8 * 8 elements: two passes over the row (the second
-// read is served from L2).
 __global__ __launch_bounds__(kThreads) void k_quantize_rows_long(const uint16_t* __restrict__ x, int64_t cols,
                                                                  int64_t ldx, uint8_t* __restrict__ codes,
                                                                  uint8_t* __restrict__ scales,
@@ -138,36 +164,57 @@ __global__ __launch_bounds__(kThreads) void k_quantize_cols(const uint16_t* __re
 // --------------------------------------------------------------------------
 // rmsnorm_quant
 // --------------------------------------------------------------------------
-template <int NCH>
+// RMSNorm -> NVFP4 in the row layout of the quantizer: WPR waves per row,
+// lane l of the row's wave p owns the 16-element blocks l + 64 p + 64 WPR i.
+// Sums over the row are wave reductions, exchanged through LDS (in wave
+// order) when a row spans several waves.
+template <int NB, int WPR>
+__device__ __forceinline__ double row_sum_f64(double v, double* dred, int wave, int part) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o, 64);
+  if constexpr (WPR > 1) {
+    if ((threadIdx.x & 63) == 0) dred[wave] = v;
+    __syncthreads();
+    v = dred[wave - part];
+#pragma unroll
+    for (int k = 1; k < WPR; ++k) v += dred[wave - part + k];
+    __syncthreads();
+  }
+  return v;
+}
+
+template <int NB, int WPR>
 __global__ __launch_bounds__(kThreads) void k_rmsnorm_quant(const uint16_t* __restrict__ x,
                                                             const uint16_t* __restrict__ gain, float eps,
-                                                            int64_t H, int64_t ldx, uint8_t* __restrict__ codes,
+                                                            int64_t M, int64_t H, int64_t ldx,
+                                                            uint8_t* __restrict__ codes,
                                                             uint8_t* __restrict__ scales,
                                                             float* __restrict__ rscale,
                                                             float* __restrict__ rstd_out, int force_exact) {
   __shared__ double dred[2][4];
   __shared__ float red[4];
-  const int64_t row = blockIdx.x;
-  const int nchunk = (int)(H >> 3);
-  const uint16_t* xr = x + row * ldx;
-  uint4 v[NCH];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int part = wave % WPR;
+  const int64_t row = (int64_t)blockIdx.x * (4 / WPR) + wave / WPR;
+  const bool row_ok = row < M;                         // uniform per wave (no early exit: barriers below)
+  const int nblk = (int)(H >> 4);
+  const uint16_t* xr = x + (row_ok ? row : 0) * ldx;
+  uint4 v[NB][2];
   double ss = 0.0;
 #pragma unroll
-  for (int i = 0; i < NCH; ++i) {
-    const int c = threadIdx.x + kThreads * i;
-    v[i] = c < nchunk ? load16(xr + 8 * c) : make_uint4(0, 0, 0, 0);
-    float f[8];
-    unpack_bf16x8(v[i], f);
+  for (int i = 0; i < NB; ++i) {
+    const int blk = lane + 64 * part + 64 * WPR * i;
+    const bool ok = row_ok && blk < nblk;
+    v[i][0] = ok ? load16(xr + 16 * blk) : make_uint4(0, 0, 0, 0);
+    v[i][1] = ok ? load16(xr + 16 * blk + 8) : make_uint4(0, 0, 0, 0);
+    float f[16];
+    unpack_bf16x8(v[i][0], f);
+    unpack_bf16x8(v[i][1], f + 8);
+    // the square is exact in float64, so fma(d, d, ss) rounds exactly as ss + d*d
 #pragma unroll
-    for (int t = 0; t < 8; ++t) ss += (double)f[t] * (double)f[t];   // exact square
+    for (int t = 0; t < 16; ++t) ss = __builtin_fma((double)f[t], (double)f[t], ss);
   }
-  // workgroup sum (plain float64)
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) ss += __shfl_xor(ss, o, 64);
-  const int w = threadIdx.x >> 6;
-  if ((threadIdx.x & 63) == 0) dred[0][w] = ss;
-  __syncthreads();
-  double S = (dred[0][0] + dred[0][1]) + (dred[0][2] + dred[0][3]);
+  double S = row_sum_f64<NB, WPR>(ss, dred[0], wave, part);
   // The FP32 result depends on S only through fp32(S/H).  The float64 sum above
   // is within (H + 64) * 2^-53 * S of the exactly rounded sum; unless fp32(S/H)
   // is that close to an FP32 rounding boundary, it is the exactly rounded
@@ -181,39 +228,57 @@ __global__ __launch_bounds__(kThreads) void k_rmsnorm_quant(const uint16_t* __re
     const double hi = (double)__uint_as_float(fb + 1u);
     const double dist = fmin(q - 0.5 * (lo + (double)f), 0.5 * ((double)f + hi) - q);
     const double margin = ((double)H + 64.0) * 2.220446049250313e-16 * q;   // (H+64) * 2^-52 * q
-    const bool exact = force_exact != 0 || (q > 0.0 && !(dist > margin));
-    __syncthreads();
-    if (exact) {   // uniform across the workgroup
+    bool exact = force_exact != 0 || (q > 0.0 && !(dist > margin));
+    // uniform per wave; with several waves per row every wave of the
+    // workgroup takes the exact path if any row needs it (barriers inside)
+    if constexpr (WPR > 1) exact = __syncthreads_or(exact) != 0;
+    if (exact) {
       double sh = 0.0, sl = 0.0;
 #pragma unroll
-      for (int i = 0; i < NCH; ++i) {
-        float f8[8];
-        unpack_bf16x8(v[i], f8);
+      for (int i = 0; i < NB; ++i) {
 #pragma unroll
-        for (int t = 0; t < 8; ++t) {
-          double s, e;
-          two_sum(sh, (double)f8[t] * (double)f8[t], s, e);
-          sh = s;
-          sl += e;
+        for (int h = 0; h < 2; ++h) {
+          // scheduling fences keep this rarely taken path from raising the
+          // kernel's register count (it would otherwise widen every element to
+          // float64 at once)
+          __builtin_amdgcn_sched_barrier(0);
+          // an opaque copy of the raw bits: stops the compiler from sharing the
+          // unpacked values with the passes below and keeping them all live
+          uint4 w = v[i][h];
+          asm volatile("" : "+v"(w.x), "+v"(w.y), "+v"(w.z), "+v"(w.w));
+          float f8[8];
+          unpack_bf16x8(w, f8);
+#pragma unroll
+          for (int t = 0; t < 8; ++t) {
+            double s2, e2;
+            two_sum(sh, (double)f8[t] * (double)f8[t], s2, e2);
+            sh = s2;
+            sl += e2;
+          }
         }
       }
+      __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
       for (int o = 32; o >= 1; o >>= 1) {
         const double oh = __shfl_xor(sh, o, 64), ol = __shfl_xor(sl, o, 64);
-        double s, e;
-        two_sum(sh, oh, s, e);
-        sh = s;
-        sl = sl + ol + e;
+        double s2, e2;
+        two_sum(sh, oh, s2, e2);
+        sh = s2;
+        sl = sl + ol + e2;
       }
-      if ((threadIdx.x & 63) == 0) { dred[0][w] = sh; dred[1][w] = sl; }
-      __syncthreads();
-      sh = dred[0][0];
-      sl = dred[1][0];
-      for (int k = 1; k < 4; ++k) {
-        double s, e;
-        two_sum(sh, dred[0][k], s, e);
-        sh = s;
-        sl = sl + dred[1][k] + e;
+      if constexpr (WPR > 1) {
+        if (lane == 0) { dred[0][wave] = sh; dred[1][wave] = sl; }
+        __syncthreads();
+        const int w0 = wave - part;
+        sh = dred[0][w0];
+        sl = dred[1][w0];
+        for (int k = 1; k < WPR; ++k) {
+          double s2, e2;
+          two_sum(sh, dred[0][w0 + k], s2, e2);
+          sh = s2;
+          sl = sl + dred[1][w0 + k] + e2;
+        }
+        __syncthreads();
       }
       S = sh + sl;   // the double-double value rounded once to float64
     }
@@ -222,30 +287,55 @@ __global__ __launch_bounds__(kThreads) void k_rmsnorm_quant(const uint16_t* __re
   const float var = __fadd_rn(ms, eps);
   const float sd = (float)__builtin_sqrt((double)var);        // RN64 then RN32 of sqrt: equals sqrt_rn in FP32
   const float rstd = __fdiv_rn(1.0f, sd);
-  // y = (x * rstd) * g, kept in registers for the quantization pass
-  float y[NCH][8];
+  // y = (x * rstd) * g: formed once for the block maxima and again, by the same
+  // operations, in the quantization pass (cheaper than holding it in registers)
+  uint4 gv[NB][2];
+  float bm[NB];
   float lmax = 0.0f;
 #pragma unroll
-  for (int i = 0; i < NCH; ++i) {
-    const int c = threadIdx.x + kThreads * i;
-    float f[8], g[8];
-    unpack_bf16x8(v[i], f);
-    unpack_bf16x8(c < nchunk ? load16(gain + 8 * c) : make_uint4(0, 0, 0, 0), g);
+  for (int i = 0; i < NB; ++i) {
+    const int blk = lane + 64 * part + 64 * WPR * i;
+    const bool ok = blk < nblk;
+    gv[i][0] = ok ? load16(gain + 16 * blk) : make_uint4(0, 0, 0, 0);
+    gv[i][1] = ok ? load16(gain + 16 * blk + 8) : make_uint4(0, 0, 0, 0);
+    float f[16], g[16], y[16];
+    unpack_bf16x8(v[i][0], f);
+    unpack_bf16x8(v[i][1], f + 8);
+    unpack_bf16x8(gv[i][0], g);
+    unpack_bf16x8(gv[i][1], g + 8);
 #pragma unroll
-    for (int t = 0; t < 8; ++t) y[i][t] = __fmul_rn(__fmul_rn(f[t], rstd), g[t]);
-    lmax = fmaxf(lmax, absmax8(y[i]));
+    for (int t = 0; t < 16; ++t) y[t] = __fmul_rn(__fmul_rn(f[t], rstd), g[t]);
+    bm[i] = fmaxf(absmax8(y), absmax8(y + 8));
+    lmax = fmaxf(lmax, bm[i]);
   }
-  const float amax = block_max_256(lmax, red);
+  float amax = wave_max(lmax);
+  if constexpr (WPR > 1) {
+    if (lane == 0) red[wave] = amax;
+    __syncthreads();
+    const int w0 = wave - part;
+#pragma unroll
+    for (int k = 0; k < WPR; ++k) amax = fmaxf(amax, red[w0 + k]);
+  }
+  if (!row_ok) return;
   const int e = row_exponent(amax);
   const float r = pow2f(e), inv_r = pow2f(-e);
   uint8_t* crow = codes + row * (H >> 1);
   uint8_t* srow = scales + row * (H >> 4);
 #pragma unroll
-  for (int i = 0; i < NCH; ++i) {
-    const int c = threadIdx.x + kThreads * i;
-    quant_chunk(y[i], c < nchunk, r, inv_r, crow, srow, c);
+  for (int i = 0; i < NB; ++i) {
+    const int blk = lane + 64 * part + 64 * WPR * i;
+    if (blk < nblk) {
+      float f[16], g[16], y[16];
+      unpack_bf16x8(v[i][0], f);
+      unpack_bf16x8(v[i][1], f + 8);
+      unpack_bf16x8(gv[i][0], g);
+      unpack_bf16x8(gv[i][1], g + 8);
+#pragma unroll
+      for (int t = 0; t < 16; ++t) y[t] = __fmul_rn(__fmul_rn(f[t], rstd), g[t]);
+      quant_block16(y, bm[i], r, inv_r, crow, srow, blk);
+    }
   }
-  if (threadIdx.x == 0) {
+  if (lane == 0 && part == 0) {
     rscale[row] = r;
     rstd_out[row] = rstd;
   }
@@ -421,14 +511,23 @@ hipError_t launch_quantize_ex(const uint16_t* x, int64_t rows, int64_t cols, int
     k_quantize_cols<<<grid, kThreads, 0, s>>>(x, rows, cols, ldx, codes, scales, rscale, round_up, tensor_amax);
     return hipGetLastError();
   }
-  const int nch = chunks_per_thread(cols);
-  const dim3 grid((unsigned)rows);
-#define PACT_QR(N) k_quantize_rows<N><<<grid, kThreads, 0, s>>>(x, cols, ldx, codes, scales, rscale, round_up, tensor_amax)
-  if (nch <= 1) PACT_QR(1);
-  else if (nch <= 2) PACT_QR(2);
-  else if (nch <= 4) PACT_QR(4);
-  else if (nch <= 8) PACT_QR(8);
-  else k_quantize_rows_long<<<grid, kThreads, 0, s>>>(x, cols, ldx, codes, scales, rscale, round_up, tensor_amax);
+  // blocks per lane <= 4: one wave per row up to 4096 columns, two up to 8192, four up to 16384
+  const int64_t nblk = cols >> 4;
+  const int wpr = nblk <= 256 ? 1 : (nblk <= 512 ? 2 : 4);
+  const int64_t nb = (nblk + 64 * wpr - 1) / (64 * wpr);
+  const dim3 grid((unsigned)((rows + 4 / wpr - 1) / (4 / wpr)));
+#define PACT_QR(N, W) \
+  k_quantize_rows<N, W><<<grid, kThreads, 0, s>>>(x, rows, cols, ldx, codes, scales, rscale, round_up, tensor_amax)
+  if (nblk > 1024) k_quantize_rows_long<<<dim3((unsigned)rows), kThreads, 0, s>>>(x, cols, ldx, codes, scales, rscale,
+                                                                                  round_up, tensor_amax);
+  else if (wpr == 1 && nb <= 1) PACT_QR(1, 1);
+  else if (wpr == 1 && nb <= 2) PACT_QR(2, 1);
+  else if (wpr == 1 && nb <= 3) PACT_QR(3, 1);
+  else if (wpr == 1) PACT_QR(4, 1);
+  else if (wpr == 2 && nb <= 3) PACT_QR(3, 2);
+  else if (wpr == 2) PACT_QR(4, 2);
+  else if (nb <= 3) PACT_QR(3, 4);
+  else PACT_QR(4, 4);
 #undef PACT_QR
   return hipGetLastError();
 }
@@ -441,14 +540,23 @@ hipError_t launch_quantize(const uint16_t* x, int64_t rows, int64_t cols, int64_
 hipError_t launch_rmsnorm_quant(const uint16_t* x, const uint16_t* gain, float eps, int64_t M, int64_t H,
                                 int64_t ldx, uint8_t* codes, uint8_t* scales, float* rscale, float* rstd,
                                 int force_exact, hipStream_t s) {
-  const int nch = chunks_per_thread(H);
-  const dim3 grid((unsigned)M);
-#define PACT_RMS(N) k_rmsnorm_quant<N><<<grid, kThreads, 0, s>>>(x, gain, eps, H, ldx, codes, scales, rscale, rstd, force_exact)
-  if (nch <= 1) PACT_RMS(1);
-  else if (nch <= 2) PACT_RMS(2);
-  else if (nch <= 4) PACT_RMS(4);
-  else if (nch <= 8) PACT_RMS(8);
-  else return hipErrorInvalidValue;
+  // the quantizer's row layout: blocks per lane <= 4 (one wave per row up to
+  // 4096 columns, two up to 8192, four up to 16384)
+  const int64_t nblk = H >> 4;
+  if (nblk > 1024) return hipErrorInvalidValue;
+  const int wpr = nblk <= 256 ? 1 : (nblk <= 512 ? 2 : 4);
+  const int64_t nb = (nblk + 64 * wpr - 1) / (64 * wpr);
+  const dim3 grid((unsigned)((M + 4 / wpr - 1) / (4 / wpr)));
+#define PACT_RMS(N, W) \
+  k_rmsnorm_quant<N, W><<<grid, kThreads, 0, s>>>(x, gain, eps, M, H, ldx, codes, scales, rscale, rstd, force_exact)
+  if (wpr == 1 && nb <= 1) PACT_RMS(1, 1);
+  else if (wpr == 1 && nb <= 2) PACT_RMS(2, 1);
+  else if (wpr == 1 && nb <= 3) PACT_RMS(3, 1);
+  else if (wpr == 1) PACT_RMS(4, 1);
+  else if (wpr == 2 && nb <= 3) PACT_RMS(3, 2);
+  else if (wpr == 2) PACT_RMS(4, 2);
+  else if (nb <= 3) PACT_RMS(3, 4);
+  else PACT_RMS(4, 4);
 #undef PACT_RMS
   return hipGetLastError();
 }

@@ -34,6 +34,17 @@ __device__ __forceinline__ void quant_chunk(const float* x, bool valid, float r,
   if ((c & 1) == 0) scales_row[c >> 1] = (uint8_t)q.sc;
 }
 
+// Quantize one whole 16-element block held by one lane (block maximum bmax
+// already known): 8 code bytes and the scale byte of block `blk` of the row.
+__device__ __forceinline__ void quant_block16(const float* x, float bmax, float r, float inv_r, uint8_t* codes_row,
+                                              uint8_t* scales_row, int blk, bool round_up = false) {
+  const BlockQ q = block_setup(bmax, r, inv_r, round_up);
+  const uint32_t w0 = encode8(x, q);
+  const uint32_t w1 = encode8(x + 8, q);
+  *reinterpret_cast<uint2*>(codes_row + 8 * (int64_t)blk) = make_uint2(w0, w1);
+  scales_row[blk] = (uint8_t)q.sc;
+}
+
 // Error-free sum of two doubles.
 __device__ __forceinline__ void two_sum(double a, double b, double& s, double& e) {
   s = a + b;

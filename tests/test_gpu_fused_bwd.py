@@ -83,7 +83,7 @@ def _rms_state(M, H, seed):
     return yq, rstd, g, dy, resid
 
 
-@pytest.mark.parametrize("M,H", [(257, 3072), (64, 2048), (9, 16384), (4, 48)])
+@pytest.mark.parametrize("M,H", [(257, 3072), (64, 2048), (9, 16384), (4, 48), (5, 8192), (7, 5120)])
 def test_rmsnorm_bwd_bit_exact_and_residual(fw, M, H):
     yq, rstd, g, dy, resid = _rms_state(M, H, H + 11)
     gy, grs, gg, gdy, gres = (nvfp4_to_gpu(yq), torch.from_numpy(rstd).cuda(), bits_to_torch(g),

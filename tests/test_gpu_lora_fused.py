@@ -66,7 +66,8 @@ def _rms_inputs(M, H, wid=3, tid=700):
 
 
 @pytest.mark.parametrize("M,H,exact", [(64, 256, "0"), (33, 3072, "0"), (33, 3072, "1"), (8192, 3072, "0"),
-                                       (17, 16384, "0"), (5, 48, "1")])
+                                       (17, 16384, "0"), (5, 48, "1"), (9, 8192, "1"), (9, 6144, "0"),
+                                       (6, 12288, "1")])
 def test_rmsnorm_quant(fw, M, H, exact, monkeypatch):
     monkeypatch.setenv("PACT_RMSNORM_EXACT_SUM", exact)
     x, g = _rms_inputs(M, H, tid=700 + H)
