@@ -57,3 +57,18 @@ def gemm_dgrad_fwd_layout(dyq: NVFP4, w_fwd: NVFP4):
     da = dequantize(dyq)
     dw = dequantize(w_fwd)
     return da @ dw, np.abs(da) @ np.abs(dw)
+
+
+def gemm_dgrad_multi(segments):
+    """Input gradient summed over projections that read one input (PACT,
+    Appendix Table 7 row "Frozen projections"; every consumer's dY_i W_i adds
+    into the same dX): sum_i deq(dY_i) deq(W_bwd,i)^T in float64, with the sum
+    of |a||b| products for the acceptance bound.  ``segments``: list of
+    (dY_i NVFP4 [M x N_i], W_bwd,i NVFP4 [K x N_i])."""
+    ref, rabs = None, None
+    for dyq, wb in segments:
+        r, a = gemm_dgrad(dyq, wb)
+        ref = r if ref is None else ref + r
+        rabs = a if rabs is None else rabs + a
+    return ref, rabs
+

@@ -155,3 +155,35 @@ def test_bf16_rne_and_ulp_closed_forms():
     v = one + u / 2 + 2.0 ** -30                   # float32 rounds it to the tie point
     assert tolerance.bf16_rne(v) == one + u
     assert np.float32(v) == np.float32(one + u / 2)
+
+
+def test_dgrad_multi_matches_rational_sum_over_segments():
+    """Summed input gradient over segments of different widths and row-scale
+    ranges equals the exact rational sum of every segment's products (rows of
+    dY_i against rows of W_bwd,i = columns of W_i)."""
+    rng = np.random.default_rng(140)
+    M, K, widths = 3, 2, (16, 48, 32)
+    segs = []
+    for i, n in enumerate(widths):
+        dy = rng.standard_normal((M, n)) * 2.0 ** (6 * i - 6)
+        w = rng.standard_normal((n, K)) * 2.0 ** (-3 * i)
+        segs.append((nvfp4.quantize(dy), nvfp4.quantize(w, transpose=True)))
+    ref, rabs = gemm.gemm_dgrad_multi(segs)
+    assert ref.shape == (M, K)
+    exact = [[Fraction(0)] * K for _ in range(M)]
+    absum = [[Fraction(0)] * K for _ in range(M)]
+    for dyq, wb in segs:
+        a, b = _frac_deq(dyq), _frac_deq(wb)
+        for m in range(M):
+            for k in range(K):
+                for j in range(dyq.cols):
+                    exact[m][k] += a[m][j] * b[k][j]
+                    absum[m][k] += abs(a[m][j] * b[k][j])
+    for m in range(M):
+        for k in range(K):
+            assert abs(Fraction(float(ref[m, k])) - exact[m][k]) <= Fraction(2) ** -50 * absum[m][k]
+            assert abs(Fraction(float(rabs[m, k])) - absum[m][k]) <= Fraction(2) ** -50 * absum[m][k]
+    # one segment is the plain input gradient
+    r1, a1 = gemm.gemm_dgrad_multi(segs[:1])
+    r0, a0 = gemm.gemm_dgrad(*segs[0])
+    assert np.array_equal(r1, r0) and np.array_equal(a1, a0)
