@@ -194,6 +194,48 @@ def gemm_dgrad(dyq: NVFP4Tensor, w_bwd: NVFP4Tensor, out: torch.Tensor | None = 
     return out
 
 
+def gemm_dgrad_multi(segments, out: torch.Tensor | None = None, accumulate: bool = False, lora=None):
+    """dX = bf16([f32(dX) +] sum_i (deq(dY_i) deq(W_bwd,i)^T [+ dT_i A_i])) in one launch.
+
+    ``segments``: list of (dY_i NVFP4 [M x N_i], W_bwd,i NVFP4 [K x N_i]), 1..4 of them,
+    N_i multiples of 256; ``lora``: None or a list of (dT_i, A_i) or None per segment."""
+    import ctypes
+    n = len(segments)
+    M = segments[0][0].rows
+    K = segments[0][1].rows
+    for dyq, wb in segments:
+        if dyq.rows != M or wb.rows != K or wb.cols != dyq.cols:
+            raise ValueError("segments: dY_i [M x N_i] and W_bwd,i [K x N_i] with one M and one K")
+    if out is None:
+        if accumulate:
+            raise ValueError("accumulate needs an existing output")
+        out = torch.empty((M, K), dtype=torch.bfloat16, device=segments[0][0].codes.device)
+    P = ctypes.c_void_p * n
+    arr = lambda vals: P(*[ctypes.c_void_p(v) for v in vals])
+    i64 = ctypes.c_int64 * n
+    dts = as_ = rs = None
+    if lora is not None:
+        if len(lora) != n:
+            raise ValueError("one LoRA entry (or None) per segment")
+        dtp, ap, rv = [], [], []
+        for entry in lora:
+            if entry is None:
+                dtp.append(0); ap.append(0); rv.append(0)
+                continue
+            dT, A = entry
+            r = dT.shape[1]
+            if dT.shape[0] != M or A.shape != (r, K):
+                raise ValueError("LoRA shapes: dT [M x r], A [r x K]")
+            dtp.append(dT.data_ptr()); ap.append(A.data_ptr()); rv.append(r)
+        dts, as_, rs = arr(dtp), arr(ap), i64(*rv)
+    _lib.call("nvfp4_gemm_dgrad_multi", n, arr([d.codes.data_ptr() for d, _ in segments]),
+              arr([d.scales.data_ptr() for d, _ in segments]), arr([d.rscale.data_ptr() for d, _ in segments]),
+              i64(*[d.cols for d, _ in segments]), arr([w.codes.data_ptr() for _, w in segments]),
+              arr([w.scales.data_ptr() for _, w in segments]), arr([w.rscale.data_ptr() for _, w in segments]),
+              M, K, out.data_ptr(), out.stride(0), int(accumulate), dts, as_, rs, _stream())
+    return out
+
+
 class SingleLayoutWeight:
     """A frozen weight kept only as W_fwd = Q(W) [N x K], plus the largest
     row-scale exponent over its nonzero rows (device int32), for the

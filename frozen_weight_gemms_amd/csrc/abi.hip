@@ -69,7 +69,7 @@ extern "C" {
 
 const char* pact_last_error(void) { return g_err; }
 
-int pact_abi_version(void) { return 6; }
+int pact_abi_version(void) { return 7; }
 
 int pact_nvfp4_sizes(int64_t rows, int64_t cols, size_t* codes_bytes, size_t* scales_bytes, size_t* rscale_bytes) {
   REQUIRE(rows >= 0 && cols >= 0, PACT_EINVAL, "negative size (rows=%lld, cols=%lld)", (long long)rows,
@@ -242,6 +242,57 @@ int nvfp4_gemm_dgrad(const uint8_t* dy_codes, const uint8_t* dy_scales, const fl
   a.u_stride_j = K; a.u_stride_n = 1;        // U(j, k) = A[j][k], A is [r x K]
   a.lora_r = lora_r; a.lora_scale = 1.0f;
   return gemm_common(a, "nvfp4_gemm_dgrad", stream);
+}
+
+int nvfp4_gemm_dgrad_multi(int nseg, const uint8_t* const* dy_codes, const uint8_t* const* dy_scales,
+                           const float* const* dy_rscale, const int64_t* seg_n, const uint8_t* const* w_codes,
+                           const uint8_t* const* w_scales, const float* const* w_rscale, int64_t M, int64_t K,
+                           uint16_t* dx, int64_t lddx, int accumulate, const uint16_t* const* lora_dt,
+                           const uint16_t* const* lora_a, const int64_t* lora_r, void* stream) {
+  REQUIRE(nseg >= 1 && nseg <= pact::kMaxSeg, PACT_EINVAL, "nseg=%d outside [1, %d]", nseg, pact::kMaxSeg);
+  REQUIRE(dy_codes && dy_scales && dy_rscale && seg_n && w_codes && w_scales && w_rscale, PACT_EINVAL,
+          "NULL segment array");
+  REQUIRE(accumulate == 0 || accumulate == 1, PACT_EINVAL, "accumulate must be 0 or 1 (got %d)", accumulate);
+  REQUIRE(M >= 0 && K >= 0, PACT_EINVAL, "negative size");
+  REQUIRE(lora_dt == nullptr || (lora_a != nullptr && lora_r != nullptr), PACT_EINVAL,
+          "LoRA dT array given without the A and rank arrays");
+  pact::GemmArgs a{};
+  pact::SegArgs sg{};
+  sg.nseg = nseg;
+  for (int i = 0; i < nseg; ++i) {
+    REQUIRE(seg_n[i] > 0 && seg_n[i] % 256 == 0, PACT_EUNSUPPORTED,
+            "segment %d: contraction length %lld is not a positive multiple of 256", i, (long long)seg_n[i]);
+    pact::SegOperand& o = sg.s[i];
+    o.a_codes = dy_codes[i]; o.a_scales = dy_scales[i]; o.a_rscale = dy_rscale[i];
+    o.b_codes = w_codes[i]; o.b_scales = w_scales[i]; o.b_rscale = w_rscale[i];
+    o.K = seg_n[i];
+    if (M > 0 && K > 0) {
+      int st = check_nvfp4(o.a_codes, o.a_scales, o.a_rscale, "dY segment");
+      if (st == PACT_OK) st = check_nvfp4(o.b_codes, o.b_scales, o.b_rscale, "W_bwd segment");
+      if (st != PACT_OK) return st;
+    }
+    if (lora_dt != nullptr && lora_dt[i] != nullptr) {
+      REQUIRE(lora_a[i] != nullptr, PACT_EINVAL, "segment %d: LoRA dT given without A", i);
+      REQUIRE(lora_r[i] >= 1 && lora_r[i] <= kMaxRank, PACT_ESHAPE, "segment %d: LoRA rank %lld outside [1, %lld]",
+              i, (long long)lora_r[i], (long long)kMaxRank);
+      o.lora_t = lora_dt[i]; o.lora_u = lora_a[i]; o.lora_r = lora_r[i];
+    }
+  }
+  if (M == 0 || K == 0) return ok();
+  REQUIRE(dx != nullptr, PACT_EINVAL, "dx is NULL");
+  REQUIRE((reinterpret_cast<uintptr_t>(dx) & 1u) == 0, PACT_EALIGN, "dx is not 2-byte aligned");
+  REQUIRE(lddx >= K, PACT_ESHAPE, "leading dimension %lld < %lld", (long long)lddx, (long long)K);
+  // segment 0 fills the plain fields (the kernel's first descriptors)
+  a.a_codes = sg.s[0].a_codes; a.a_scales = sg.s[0].a_scales; a.a_rscale = sg.s[0].a_rscale;
+  a.b_codes = sg.s[0].b_codes; a.b_scales = sg.s[0].b_scales; a.b_rscale = sg.s[0].b_rscale;
+  a.M = M; a.N = K; a.K = sg.s[0].K;
+  a.out = dx; a.ldo = lddx; a.accumulate = accumulate;
+  a.u_stride_j = K; a.u_stride_n = 1;        // U(j, k) = A[j][k], A is [r x K]
+  a.lora_scale = 1.0f;
+  REQUIRE(pact::gemm_multi_supported(a, sg), PACT_EUNSUPPORTED,
+          "operands too large for 32-bit buffer offsets (M=%lld, K=%lld)", (long long)M, (long long)K);
+  REQUIRE((M + 127) / 128 * ((K + 127) / 128) < 0x7FFFFFFF, PACT_EUNSUPPORTED, "too many tiles");
+  return hip_status(pact::launch_gemm_multi(a, sg, as_stream(stream)), "nvfp4_gemm_dgrad_multi launch");
 }
 
 int lora_down(const uint8_t* x_codes, const uint8_t* x_scales, const float* x_rscale, int64_t M, int64_t K,

@@ -344,11 +344,20 @@ struct FastCfg {
   static_assert(ROWS % 64 == 0 && BM % 64 == 0, "tile rows");
 };
 
-template <int WTM, int WTN>
-__global__ __launch_bounds__(256, 1) void k_gemm_nvfp4_fast(GemmArgs p, int tiles_m, int tiles_n) {
+// With SEG, the contraction runs over up to kMaxSeg segments (sg), each with
+// its own A and B operands, contraction length (a multiple of the stage) and
+// row scales: the input gradient summed over several projections that read
+// the same X.  The accumulator holds each segment's partial sum in units of
+// the current segment's row scales; at a segment boundary it is rescaled by
+// the power of two r_A,old r_B,old / (r_A,new r_B,new) (v_ldexp: exact in the
+// FP32 range), so the epilogue applies the last segment's scales.  Without SEG
+// every segment branch compiles away.
+template <int WTM, int WTN, bool SEG = false>
+__global__ __launch_bounds__(256, 1) void k_gemm_nvfp4_fast(GemmArgs p, int tiles_m, int tiles_n, SegArgs sg) {
   using C = FastCfg<WTM, WTN>;
   constexpr int BM = C::BM, BN = C::BN;
-  __shared__ __attribute__((aligned(1024))) uint8_t smem[C::TOTAL];
+  constexpr int NSEG_LDS = SEG ? kMaxSeg : 1;            // row-scale areas (one per segment)
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[C::TOTAL + (NSEG_LDS - 1) * C::ROWS * 4];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
@@ -368,7 +377,7 @@ __global__ __launch_bounds__(256, 1) void k_gemm_nvfp4_fast(GemmArgs p, int tile
   const int64_t m0 = (int64_t)tile_m * BM, n0 = (int64_t)tile_n * BN;
 
   const int64_t M = p.M, N = p.N, K = p.K;
-  const uint32_t crow = (uint32_t)(K >> 1), srow = (uint32_t)(K >> 4);
+  uint32_t crow = (uint32_t)(K >> 1), srow = (uint32_t)(K >> 4);
   const int nk = (int)(K / KT2);
 
   floatx16 acc[WTM][WTN];
@@ -377,10 +386,10 @@ __global__ __launch_bounds__(256, 1) void k_gemm_nvfp4_fast(GemmArgs p, int tile
   // Code instruction c of this wave covers tile rows 8 (wave + 4c) .. +7: lane
   // -> row 8 (wave + 4c) + lane / 8, LDS slot lane % 8, global chunk
   // slot ^ ((row >> 1) & 7) (independent of c).  Rows below BM are A rows.
-  const int4v_t ra_c = buffer_rsrc(p.a_codes, (uint32_t)(M * crow));
-  const int4v_t rb_c = buffer_rsrc(p.b_codes, (uint32_t)(N * crow));
-  const int4v_t ra_s = buffer_rsrc(p.a_scales, (uint32_t)(M * srow));
-  const int4v_t rb_s = buffer_rsrc(p.b_scales, (uint32_t)(N * srow));
+  int4v_t ra_c = buffer_rsrc(p.a_codes, (uint32_t)(M * crow));
+  int4v_t rb_c = buffer_rsrc(p.b_codes, (uint32_t)(N * crow));
+  int4v_t ra_s = buffer_rsrc(p.a_scales, (uint32_t)(M * srow));
+  int4v_t rb_s = buffer_rsrc(p.b_scales, (uint32_t)(N * srow));
   const int crow0 = 8 * wave + (lane >> 3);              // tile row of instruction 0
   const uint32_t cchunk = (uint32_t)(((lane & 7) ^ ((crow0 >> 1) & 7)) << 4);
   // voffset of code instruction c: the row term must sit in voffset so that
@@ -395,10 +404,11 @@ __global__ __launch_bounds__(256, 1) void k_gemm_nvfp4_fast(GemmArgs p, int tile
     return n < N ? (uint32_t)n * crow + cchunk : 0xfffffff0u;
   };
   uint32_t cvo[C::NC];
+  uint32_t svo[C::NS];
+  // scale instruction c of this wave: tile rows 64 (wave + 4c) + lane
+  auto set_voffsets = [&]() __attribute__((always_inline)) {
 #pragma unroll
   for (int c = 0; c < C::NC; ++c) cvo[c] = code_voff(c);
-  // scale instruction c of this wave: tile rows 64 (wave + 4c) + lane
-  uint32_t svo[C::NS];
 #pragma unroll
   for (int c = 0; c < C::NS; ++c) {
     const int q = wave + 4 * c;
@@ -415,6 +425,21 @@ __global__ __launch_bounds__(256, 1) void k_gemm_nvfp4_fast(GemmArgs p, int tile
     }
     svo[c] = v;
   }
+  };
+  set_voffsets();
+  // load descriptors and voffsets of segment sgi's operands
+  auto set_segment = [&](int sgi) __attribute__((always_inline)) {
+    if constexpr (SEG) {
+      const int64_t Ks = sg.s[sgi].K;
+      crow = (uint32_t)(Ks >> 1);
+      srow = (uint32_t)(Ks >> 4);
+      ra_c = buffer_rsrc(sg.s[sgi].a_codes, (uint32_t)(M * crow));
+      rb_c = buffer_rsrc(sg.s[sgi].b_codes, (uint32_t)(N * crow));
+      ra_s = buffer_rsrc(sg.s[sgi].a_scales, (uint32_t)(M * srow));
+      rb_s = buffer_rsrc(sg.s[sgi].b_scales, (uint32_t)(N * srow));
+      set_voffsets();
+    }
+  };
   const int wave_s = __builtin_amdgcn_readfirstlane(wave);
   const uint32_t lds0 = lds_addr(smem);
   // load instruction q (< LOADS) of stage kt into LDS buffer buf
@@ -531,6 +556,33 @@ __global__ __launch_bounds__(256, 1) void k_gemm_nvfp4_fast(GemmArgs p, int tile
   // during chunk 3 of stage kt.  By the barrier at step 12 of stage kt every
   // wave has consumed all of stage kt's LDS data (chunk 3 is dequantized at
   // step 11), so the loads of stage kt + 2 go into its buffer right after it.
+  const float* const rsc0 = reinterpret_cast<const float*>(smem + C::RSC);
+  // accumulator from units of segment cseg's row scales to those of cseg + 1
+  auto rescale_acc = [&](int cseg) __attribute__((always_inline)) {
+    if constexpr (SEG) {
+      const float* ro = rsc0 + cseg * C::ROWS;
+      const float* rn = ro + C::ROWS;
+      auto ex = [](float v) { return (int)((__float_as_uint(v) >> 23) & 255u); };
+      int dcol[WTN];
+#pragma unroll
+      for (int j = 0; j < WTN; ++j) {
+        const int col = BM + wn * (BN / 2) + j * 32 + li;
+        dcol[j] = ex(ro[col]) - ex(rn[col]);
+      }
+#pragma unroll
+      for (int i = 0; i < WTM; ++i)
+#pragma unroll
+        for (int rr = 0; rr < 16; ++rr) {
+          __builtin_amdgcn_sched_barrier(0);               // a few live exponents at a time
+          const int row = wm * (BM / 2) + i * 32 + 8 * (rr >> 2) + 4 * h + (rr & 3);
+          const int drow = ex(ro[row]) - ex(rn[row]);
+#pragma unroll
+          for (int j = 0; j < WTN; ++j) acc[i][j][rr] = __builtin_ldexpf(acc[i][j][rr], drow + dcol[j]);
+        }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  };
+
   auto run_stage = [&](int kt, auto dma_tag) {
     constexpr bool DMA = decltype(dma_tag)::value;
     const uint8_t* st = smem + (kt & 1) * C::STAGE;
@@ -574,10 +626,10 @@ __global__ __launch_bounds__(256, 1) void k_gemm_nvfp4_fast(GemmArgs p, int tile
   // per lane, 64 rows per instruction; rows past an operand's end read as 0
   // and are never stored), ahead of the first two stages.
   float* rsc = reinterpret_cast<float*>(smem + C::RSC);
-  {
-    const int4v_t ra_r = buffer_rsrc(p.a_rscale, (uint32_t)(M * 4));
-    const int4v_t rb_r = buffer_rsrc(p.b_rscale, (uint32_t)(N * 4));
-    const uint32_t rdst = lds0 + (uint32_t)C::RSC;
+  for (int sgi = 0; sgi < (SEG ? sg.nseg : 1); ++sgi) {
+    const int4v_t ra_r = buffer_rsrc(SEG ? sg.s[sgi].a_rscale : p.a_rscale, (uint32_t)(M * 4));
+    const int4v_t rb_r = buffer_rsrc(SEG ? sg.s[sgi].b_rscale : p.b_rscale, (uint32_t)(N * 4));
+    const uint32_t rdst = lds0 + (uint32_t)C::RSC + (uint32_t)(sgi * C::ROWS * 4);
 #pragma unroll
     for (int c = 0; c < C::NR; ++c) {
       const int q = wave_s + 4 * c;                      // instruction q: tile rows 64q .. 64q + 63
@@ -592,8 +644,9 @@ __global__ __launch_bounds__(256, 1) void k_gemm_nvfp4_fast(GemmArgs p, int tile
       }
     }
   }
+  const int nk0 = SEG ? (int)(sg.s[0].K / KT2) : nk;   // stages of the first (or only) segment
   issue_stage(0, 0);
-  if (nk > 1) issue_stage(1, 1);
+  if (nk0 > 1) issue_stage(1, 1);
 
   // The LoRA term is formed while those loads are in flight: acc starts as
   // (lora_scale / (rA rB)) * T U, so the epilogue's row-scale multiply turns
@@ -605,8 +658,14 @@ __global__ __launch_bounds__(256, 1) void k_gemm_nvfp4_fast(GemmArgs p, int tile
     for (int j = 0; j < WTN; ++j)
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
-  if (p.lora_t != nullptr) {
-    const int64_t r = p.lora_r;
+  bool any_lora = false;
+  // one rank-r term (T, U) per segment with SEG, else p's
+  for (int lp = 0; lp < (SEG ? sg.nseg : 1); ++lp) {
+    const uint16_t* lt = SEG ? sg.s[lp].lora_t : p.lora_t;
+    const uint16_t* lu = SEG ? sg.s[lp].lora_u : p.lora_u;
+    if (lt == nullptr) continue;
+    any_lora = true;
+    const int64_t r = SEG ? sg.s[lp].lora_r : p.lora_r;
     const bool t_vec = (r & 15) == 0;                          // T rows: 16-byte aligned runs of 8 ranks
     const bool u_vec = t_vec && p.u_stride_j == 1;             // U(j, n) = B[n][j]: same for B rows
     for (int64_t k0 = 0; k0 < r; k0 += 16) {
@@ -616,12 +675,12 @@ __global__ __launch_bounds__(256, 1) void k_gemm_nvfp4_fast(GemmArgs p, int tile
         int64_t m = m0 + wm * (BM / 2) + i * 32 + li;
         m = m < M ? m : M - 1;
         if (t_vec) {
-          tf[i] = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const uint4*>(p.lora_t + m * r + k0 + 8 * h));
+          tf[i] = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const uint4*>(lt + m * r + k0 + 8 * h));
         } else {
 #pragma unroll
           for (int t = 0; t < 8; ++t) {
             const int64_t j = k0 + 8 * h + t;
-            tf[i][t] = bf16_of(j < r ? p.lora_t[m * r + j] : (uint16_t)0);
+            tf[i][t] = bf16_of(j < r ? lt[m * r + j] : (uint16_t)0);
           }
         }
       }
@@ -630,12 +689,12 @@ __global__ __launch_bounds__(256, 1) void k_gemm_nvfp4_fast(GemmArgs p, int tile
         int64_t n = n0 + wn * (BN / 2) + i * 32 + li;
         n = n < N ? n : N - 1;
         if (u_vec) {
-          uf[i] = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const uint4*>(p.lora_u + n * p.u_stride_n + k0 + 8 * h));
+          uf[i] = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const uint4*>(lu + n * p.u_stride_n + k0 + 8 * h));
         } else {
 #pragma unroll
           for (int t = 0; t < 8; ++t) {
             const int64_t j = k0 + 8 * h + t;
-            uf[i][t] = bf16_of(j < r ? p.lora_u[j * p.u_stride_j + n * p.u_stride_n] : (uint16_t)0);
+            uf[i][t] = bf16_of(j < r ? lu[j * p.u_stride_j + n * p.u_stride_n] : (uint16_t)0);
           }
         }
       }
@@ -645,6 +704,8 @@ __global__ __launch_bounds__(256, 1) void k_gemm_nvfp4_fast(GemmArgs p, int tile
         for (int j = 0; j < WTN; ++j)
           acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tf[i], uf[j], acc[i][j], 0, 0, 0);
     }
+  }
+  if (any_lora) {
     PACT_WAIT_VMCNT(0);
     __syncthreads();                                           // every wave's row-scale loads have landed
     // row scales are powers of two: 1/r is exact and computed on the exponent
@@ -662,17 +723,39 @@ __global__ __launch_bounds__(256, 1) void k_gemm_nvfp4_fast(GemmArgs p, int tile
         }
       }
   }
-  // stage 0 (and the row scales) complete and visible
-  if (nk > 1) PACT_WAIT_VMCNT(C::LOADS);
-  else PACT_WAIT_VMCNT(0);
-  __syncthreads();
-  read_codes(smem, 0);
-  read_scales(smem, sra, srb);
-  cvt_chunk_scales(0);
-  deq_step(0, af[0], bf[0]);
-  int kt = 0;
-  for (; kt + 2 < nk; ++kt) run_stage(kt, std::true_type{});
-  for (; kt < nk; ++kt) run_stage(kt, std::false_type{});
+  // One pass of the stage pipeline over nks stages whose first two stages'
+  // loads are in flight.
+  auto run_segment = [&](int nks) __attribute__((always_inline)) {
+    // stage 0 (and the row scales) complete and visible
+    if (nks > 1) PACT_WAIT_VMCNT(C::LOADS);
+    else PACT_WAIT_VMCNT(0);
+    __syncthreads();
+    read_codes(smem, 0);
+    read_scales(smem, sra, srb);
+    cvt_chunk_scales(0);
+    deq_step(0, af[0], bf[0]);
+    int kt = 0;
+    for (; kt + 2 < nks; ++kt) run_stage(kt, std::true_type{});
+    for (; kt < nks; ++kt) run_stage(kt, std::false_type{});
+  };
+  // segments after the first: every wave is past its reads of the stage
+  // buffers before they refill, and the accumulator changes to the segment's
+  // row-scale units (one copy of the pipeline serves every segment)
+  for (int sgi = 0; sgi < (SEG ? sg.nseg : 1); ++sgi) {
+    int nks = nk0;
+    if constexpr (SEG) {
+      if (sgi > 0) {
+        PACT_WAIT_VMCNT(0);
+        __syncthreads();
+        rescale_acc(sgi - 1);
+        set_segment(sgi);
+        nks = (int)(sg.s[sgi].K / KT2);
+        issue_stage(0, 0);
+        if (nks > 1) issue_stage(1, 1);
+      }
+    }
+    run_segment(nks);
+  }
   PACT_WAIT_VMCNT(0);
 
   // ---- epilogue: row scales, optional accumulate, BF16 rounding ----
@@ -681,6 +764,7 @@ __global__ __launch_bounds__(256, 1) void k_gemm_nvfp4_fast(GemmArgs p, int tile
   // columns of a row with one 16-byte store.
   __syncthreads();                                     // all waves are done reading the stage buffers
   float* epi = reinterpret_cast<float*>(smem + wave * C::EPI_WAVE);
+  const float* rse = rsc + (SEG ? (sg.nseg - 1) * C::ROWS : 0);   // the last segment's row scales
   constexpr int WN = BN / 2;                            // columns of this wave's tile
   constexpr int CHUNKS = WN / 8;                        // 8-column chunks per row
   const bool vec_ok = (p.ldo % 8) == 0 && ((reinterpret_cast<uintptr_t>(p.out) & 15u) == 0);
@@ -689,11 +773,11 @@ __global__ __launch_bounds__(256, 1) void k_gemm_nvfp4_fast(GemmArgs p, int tile
 #pragma unroll
     for (int j = 0; j < WTN; ++j) {
       const int col = j * 32 + li;
-      const float rb = rsc[BM + wn * WN + col];
+      const float rb = rse[BM + wn * WN + col];
 #pragma unroll
       for (int rr = 0; rr < 16; ++rr) {
         const int row = 8 * (rr >> 2) + 4 * h + (rr & 3);
-        epi[row * C::EPI_LD + col] = acc[i][j][rr] * (rsc[wm * (BM / 2) + i * 32 + row] * rb);
+        epi[row * C::EPI_LD + col] = acc[i][j][rr] * (rse[wm * (BM / 2) + i * 32 + row] * rb);
       }
     }
     __builtin_amdgcn_s_waitcnt(0xc07f);                 // lgkmcnt(0): this wave's LDS writes done
@@ -746,10 +830,11 @@ hipError_t launch_gemm(const GemmArgs& a, hipStream_t s) {
   // with 32-bit buffer offsets
   const bool fast = (a.K % KT2) == 0 && (uint64_t)(a.M > a.N ? a.M : a.N) * (uint64_t)(a.K / 2) < (1ull << 31);
   if (fast) {
-    if (bm == 256 && bn == 256) k_gemm_nvfp4_fast<4, 4><<<tm * tn, 256, 0, s>>>(a, tm, tn);
-    else if (bn == 192) k_gemm_nvfp4_fast<4, 3><<<tm * tn, 256, 0, s>>>(a, tm, tn);
-    else if (bm == 256) k_gemm_nvfp4_fast<4, 2><<<tm * tn, 256, 0, s>>>(a, tm, tn);
-    else k_gemm_nvfp4_fast<2, 2><<<tm * tn, 256, 0, s>>>(a, tm, tn);
+    const SegArgs none{};
+    if (bm == 256 && bn == 256) k_gemm_nvfp4_fast<4, 4><<<tm * tn, 256, 0, s>>>(a, tm, tn, none);
+    else if (bn == 192) k_gemm_nvfp4_fast<4, 3><<<tm * tn, 256, 0, s>>>(a, tm, tn, none);
+    else if (bm == 256) k_gemm_nvfp4_fast<4, 2><<<tm * tn, 256, 0, s>>>(a, tm, tn, none);
+    else k_gemm_nvfp4_fast<2, 2><<<tm * tn, 256, 0, s>>>(a, tm, tn, none);
   } else {
     // generic contraction lengths: register-staged kernel (tile shapes 256x256, 256x128, 128x128)
     if (bm == 256 && bn == 256) k_gemm_nvfp4<4, 4><<<tm * tn, 256, 0, s>>>(a, tm, tn);
@@ -758,6 +843,30 @@ hipError_t launch_gemm(const GemmArgs& a, hipStream_t s) {
       k_gemm_nvfp4<4, 2><<<tm * tn2, 256, 0, s>>>(a, tm, tn2);
     } else k_gemm_nvfp4<2, 2><<<tm * tn, 256, 0, s>>>(a, tm, tn);
   }
+  return hipGetLastError();
+}
+
+// Input gradient summed over segments (sg): a.M x a.N output, every segment's
+// contraction a multiple of the stage and addressable with 32-bit buffer
+// offsets (checked by the caller, gemm_multi_supported).
+bool gemm_multi_supported(const GemmArgs& a, const SegArgs& sg) {
+  if (sg.nseg < 1 || sg.nseg > kMaxSeg) return false;
+  for (int i = 0; i < sg.nseg; ++i) {
+    const int64_t Ks = sg.s[i].K;
+    if (Ks <= 0 || Ks % KT2 != 0) return false;
+    if ((uint64_t)(a.M > a.N ? a.M : a.N) * (uint64_t)(Ks / 2) >= (1ull << 31)) return false;
+  }
+  return true;
+}
+
+hipError_t launch_gemm_multi(const GemmArgs& a, const SegArgs& sg, hipStream_t s) {
+  int bm, bn;
+  gemm_tile(a.M, a.N, &bm, &bn);
+  const int tm = (int)((a.M + bm - 1) / bm), tn = (int)((a.N + bn - 1) / bn);
+  if (bm == 256 && bn == 256) k_gemm_nvfp4_fast<4, 4, true><<<tm * tn, 256, 0, s>>>(a, tm, tn, sg);
+  else if (bn == 192) k_gemm_nvfp4_fast<4, 3, true><<<tm * tn, 256, 0, s>>>(a, tm, tn, sg);
+  else if (bm == 256) k_gemm_nvfp4_fast<4, 2, true><<<tm * tn, 256, 0, s>>>(a, tm, tn, sg);
+  else k_gemm_nvfp4_fast<2, 2, true><<<tm * tn, 256, 0, s>>>(a, tm, tn, sg);
   return hipGetLastError();
 }
 

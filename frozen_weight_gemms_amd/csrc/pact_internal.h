@@ -51,6 +51,29 @@ struct GemmArgs {
 };
 
 hipError_t launch_gemm(const GemmArgs& a, hipStream_t s);
+
+// Contraction over up to kMaxSeg segments (see launch_gemm_multi): segment i
+// has its own operands [M x K_i] and [N x K_i] with row scales and its own
+// optional rank-r term (lora_t [M x lora_r], lora_u with GemmArgs' strides).
+constexpr int kMaxSeg = 4;
+struct SegOperand {
+  const uint8_t* a_codes;
+  const uint8_t* a_scales;
+  const float* a_rscale;
+  const uint8_t* b_codes;
+  const uint8_t* b_scales;
+  const float* b_rscale;
+  int64_t K;
+  const uint16_t* lora_t;
+  const uint16_t* lora_u;
+  int64_t lora_r;
+};
+struct SegArgs {
+  int nseg;
+  SegOperand s[kMaxSeg];
+};
+bool gemm_multi_supported(const GemmArgs& a, const SegArgs& sg);
+hipError_t launch_gemm_multi(const GemmArgs& a, const SegArgs& sg, hipStream_t s);
 void gemm_tile(int64_t M, int64_t N, int* bm, int* bn);
 
 // Single-layout input gradient: dX [M x K] = deq(dY_q [M x N]) deq(W_fwd [N x K]);

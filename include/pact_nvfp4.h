@@ -214,6 +214,31 @@ int nvfp4_gemm_dgrad_fwd_layout(const uint8_t *dy_codes, const uint8_t *dy_scale
                                 const int *w_exp_max, int64_t K, uint16_t *dx, int64_t ldx, int accumulate,
                                 const uint16_t *lora_dt, const uint16_t *lora_a, int64_t lora_r, void *stream);
 
+/*
+ * nvfp4_gemm_dgrad_multi -- input gradient summed over the projections that
+ * read one input (Appendix Table 7 row "Frozen projections": q, k and v, or
+ * gate and up, each contribute dY_i W_i to the same dX): one launch whose
+ * contraction runs over nseg (1..4) segments,
+ *   dX = bf16( [f32(dX) +] sum_i ( deq(dY_i) deq(W_bwd,i) + dT_i A_i ) ),
+ * formed in FP32 with one BF16 rounding.  Segment i: dY_i NVFP4 [M x N_i]
+ * (dy_codes[i], dy_scales[i], dy_rscale[i]), W_bwd,i NVFP4 [K x N_i], N_i =
+ * seg_n[i] a positive multiple of 256 (else PACT_EUNSUPPORTED); optional LoRA
+ * term dT_i BF16 [M x r_i] and A_i BF16 [r_i x K] (lora_dt may be NULL, or
+ * lora_dt[i] NULL for a segment without one; 1 <= r_i <= 128).  The segment
+ * arrays are host arrays of device pointers.  dX BF16 [M x K], lddx >= K.
+ * Each segment keeps its own row scales: the partial sum is carried from one
+ * segment's row-scale units to the next by an exact power-of-two rescale
+ * (exact unless two segments' row exponents differ by more than about 90,
+ * where the smaller contribution can leave the FP32 range).  With nseg == 1
+ * the result equals nvfp4_gemm_dgrad's bit for bit.
+ */
+int nvfp4_gemm_dgrad_multi(int nseg, const uint8_t *const *dy_codes, const uint8_t *const *dy_scales,
+                           const float *const *dy_rscale, const int64_t *seg_n,
+                           const uint8_t *const *w_codes, const uint8_t *const *w_scales,
+                           const float *const *w_rscale, int64_t M, int64_t K, uint16_t *dx, int64_t lddx,
+                           int accumulate, const uint16_t *const *lora_dt, const uint16_t *const *lora_a,
+                           const int64_t *lora_r, void *stream);
+
 /* Largest exponent e of the power-of-two row scales 2^e over the rows of an
  * NVFP4 tensor [rows x cols] that are not all zero (device int *out; -126 if
  * every row is zero), for nvfp4_gemm_dgrad_fwd_layout.  codes is validated

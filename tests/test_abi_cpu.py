@@ -25,7 +25,7 @@ def lib():
 
 def test_header_symbols_exported(lib):
     names = _lib.header_functions()
-    assert len(names) == 23, names
+    assert len(names) == 24, names
     assert set(names) == set(_lib.SIGNATURES), set(names) ^ set(_lib.SIGNATURES)
     for n in names:
         assert hasattr(lib, n), n
@@ -52,7 +52,7 @@ def test_gemm_tile_query(lib):
 
 
 def test_abi_version(lib):
-    assert lib.pact_abi_version() == 6
+    assert lib.pact_abi_version() == 7
 
 
 def test_sizes(lib):
@@ -172,3 +172,19 @@ def test_fused_backward_validation(lib):
     assert g(A, A, A, A, A, A, X, 4, 64, A, None, None, None, None) == -3          # misaligned resid
     assert g(A, A, A, A, A, A, None, 4, 64, A, A, None, A, None) == -1             # partial NVFP4 output
     assert g(A, A, A, A, A, A, None, 0, 64, A, None, None, None, None) == 0        # empty
+
+
+def test_dgrad_multi_validation(lib):
+    """Argument checks of nvfp4_gemm_dgrad_multi run before any device call."""
+    import ctypes
+    P = ctypes.c_void_p * 2
+    fake = P(ctypes.c_void_p(256), ctypes.c_void_p(512))
+    widths = (ctypes.c_int64 * 2)(512, 272)
+    st = lib.nvfp4_gemm_dgrad_multi(0, fake, fake, fake, widths, fake, fake, fake, 64, 64, ctypes.c_void_p(256), 64,
+                                    0, None, None, None, None)
+    assert st == -1                                      # nseg outside [1, 4]
+    st = lib.nvfp4_gemm_dgrad_multi(2, fake, fake, fake, widths, fake, fake, fake, 64, 64, ctypes.c_void_p(256), 64,
+                                    0, None, None, None, None)
+    assert st == -5                                      # 272 is not a multiple of 256
+    assert b"multiple of 256" in lib.pact_last_error()
+
