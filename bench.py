@@ -17,8 +17,9 @@ output gradient of the layer below:
             rmsnorm_bwd_residual (+ the output gradient; NVFP4 copy) -> o
             q/k/v (nvfp4_quantize of the attention-backward gradients)
             rmsnorm_bwd_residual (+ the MLP-block residual gradient; NVFP4 copy)
-  per projection: lora_bwd and the NVFP4 dgrad GEMM with the LoRA
-  input-gradient term (q/k/v and gate/up accumulate into one dX)
+  per projection: lora_bwd; per input: one NVFP4 dgrad launch with the LoRA
+  input-gradient terms (q/k/v and gate/up each sum into one dX in a single
+  nvfp4_gemm_dgrad_multi launch; down and o alone)
 
 The metric is the NVFP4 fwd + dgrad GEMM throughput of the step:
   value = (GEMM FLOPs per step) / (wall time per step)   [TFLOP/s]
@@ -153,7 +154,7 @@ class Layer:
         fw, P = self.fw, self.proj[name]
         p = P["p"]
         self._ev("lora", "lora_down", None, lambda: fw.lora_down(xq, P["A"], out=P["T"]))
-        work = ("gemm", self.M, p.d_out, p.d_in)
+        work = ("gemm", self.M, p.d_out, (p.d_in,), False)      # M, Nout, contraction segments, accumulate
         self._ev("gemm", f"fwd {name}", work,
                  lambda: fw.gemm_fwd(xq, P["wf"], lora_t=P["T"], lora_b=P["B"], lora_scale=LORA_SCALE, out=P["Y"]))
         return P["Y"]
@@ -175,13 +176,23 @@ class Layer:
         """Input-gradient GEMM of one projection with its LoRA term dT A."""
         fw, P = self.fw, self.proj[name]
         p = P["p"]
-        work = ("gemm", self.M, p.d_in, p.d_out)
+        work = ("gemm", self.M, p.d_in, (p.d_out,), bool(accumulate))
         self._ev("gemm", f"dgrad {name}", work,
                  lambda: fw.gemm_dgrad(dyq, P["wb"], out=dx, accumulate=accumulate, lora_dt=P["dT"],
                                        lora_a=P["A"]))
 
     def _bwd_proj(self, name, xq, dy, dx, accumulate, dyq=None):
         self._bwd_dgrad(name, self._bwd_lora(name, xq, dy, dyq), dx, accumulate)
+
+    def _bwd_dgrad_multi(self, names, dx):
+        """One input-gradient launch summing the projections that read one
+        input (each with its LoRA term dT A)."""
+        fw = self.fw
+        Ps = [self.proj[n] for n in names]
+        work = ("gemm", self.M, Ps[0]["p"].d_in, tuple(P["p"].d_out for P in Ps), False)
+        self._ev("gemm", "dgrad " + "/".join(names), work,
+                 lambda: fw.gemm_dgrad_multi([(P["dyq"], P["wb"]) for P in Ps], out=dx,
+                                             lora=[(P["dT"], P["A"]) for P in Ps]))
 
     def _fork(self, fns):
         """Launch fns on the side streams, each after the current stream's
@@ -239,26 +250,21 @@ class Layer:
         self._bwd_proj("down", self.hq, dout, self.dh, False, dyq=dout_q)
         self._ev("bwd", "silu_mul_bwd_quant", ("silubq", M, I),
                  lambda: fw.silu_mul_bwd_quant(self.gq, self.uq, self.dh, out=(self.da, self.db, self.daq, self.dbq)))
-        # the up projection's LoRA backward runs beside the gate projection's
-        # LoRA backward and input-gradient GEMM; the two input-gradient GEMMs
-        # accumulate into one dX in order
-        join = self._fork([lambda: self._bwd_lora("up", self.y2q, self.db, self.dbq)])
-        self._bwd_proj("gate", self.y2q, self.da, self.dy2, False, dyq=self.daq)
-        join()
-        self._bwd_dgrad("up", self.dbq, self.dy2, True)
+        # the gate and up LoRA backwards run side by side; one input-gradient
+        # launch sums both projections into dX
+        self.proj["gate"]["dyq"], self.proj["up"]["dyq"] = self.daq, self.dbq
+        self._branches([lambda: self._bwd_lora("gate", self.y2q, self.da, self.daq),
+                        lambda: self._bwd_lora("up", self.y2q, self.db, self.dbq)])
+        self._bwd_dgrad_multi(("gate", "up"), self.dy2)
         self._ev("bwd", "rmsnorm_bwd_residual", ("rmsbr", M, H),
                  lambda: fw.rmsnorm_bwd_residual(self.y2q, self.rstd2, self.g2, self.dy2, resid=dout,
                                                  out=(self.dh2, self.dh2q)))
         # attention block: h2 = h1 + o(attn(q, k, v of n1)),  n1 = rmsnorm(h1); the
         # attention backward itself is not part of the path (dq, dk, dv are inputs)
         self._bwd_proj("o", self.aq, self.dh2, self.dattn, False, dyq=self.dh2q)
-        join = self._fork([lambda: self._bwd_lora("k", self.y1q, self.dk),
-                           lambda: self._bwd_lora("v", self.y1q, self.dv)])
-        self._bwd_proj("q", self.y1q, self.dq, self.dy1, False)
-        join(0)
-        self._bwd_dgrad("k", self.proj["k"]["dyq"], self.dy1, True)
-        join(1)
-        self._bwd_dgrad("v", self.proj["v"]["dyq"], self.dy1, True)
+        self._branches([lambda n=n, d=d: self._bwd_lora(n, self.y1q, d)
+                        for n, d in (("q", self.dq), ("k", self.dk), ("v", self.dv))])
+        self._bwd_dgrad_multi(("q", "k", "v"), self.dy1)
         self._ev("bwd", "rmsnorm_bwd_residual", ("rmsbr", M, H),
                  lambda: fw.rmsnorm_bwd_residual(self.y1q, self.rstd1, self.g1, self.dy1, resid=self.dh2,
                                                  out=(self.dh1, self.dh1q)))
@@ -573,6 +579,21 @@ BYTES_PER_ELEM = {"quant": 2.0 + 0.5 + 1 / 16, "rmsq": 2.0 + 0.5 + 1 / 16, "silu
 BYTES_PER_ROW = {"quant": 4, "rmsq": 8, "silu": 12, "silubq": 16, "rmsbr": 12}
 
 
+def gemm_bytes(M, N, segs, accumulate):
+    """Algorithmic HBM bytes of one GEMM launch: every segment's NVFP4 A
+    [M x K_i] and B [N x K_i] (codes, block scales, row scales), the BF16
+    output, and the output read back when accumulating."""
+    nv = lambda rows, cols: rows * cols * 9 // 16 + 4 * rows
+    return sum(nv(M, k) + nv(N, k) for k in segs) + 2 * M * N * (2 if accumulate else 1)
+
+
+def gemm_kernel_name(bm, bn, staged, segmented):
+    """The kernel a launch of this group runs, as the profiler names it."""
+    if staged:
+        return f"pact::k_gemm_nvfp4_fast<{bm // 64}, {bn // 64}, {'true' if segmented else 'false'}>"
+    return f"pact::k_gemm_nvfp4<{bm // 64}, {bn // 64}>"
+
+
 def kernel_bytes(kind, rows, cols):
     return BYTES_PER_ELEM[kind] * rows * cols + BYTES_PER_ROW[kind] * rows
 
@@ -747,12 +768,15 @@ def main():
         t = e0.elapsed_time(e1)
         cat_ms[cat] = cat_ms.get(cat, 0.0) + t
         if cat == "gemm":
-            _, M, N, K = work
-            tile = _lib.gemm_tile(M, N, K) + (K % 128 == 0,)   # (bm, bn, direct-to-LDS path)
-            g = gemm_by_tile.setdefault(tile, [0.0, 0.0, 0])
+            _, M, N, segs, acc = work
+            K = sum(segs)
+            # kernel group: (bm, bn, stage-pipelined path, segmented)
+            tile = _lib.gemm_tile(M, N, K) + (all(k % 256 == 0 for k in segs), len(segs) > 1)
+            g = gemm_by_tile.setdefault(tile, [0.0, 0.0, 0, 0.0])
             g[0] += t
             g[1] += 2.0 * M * N * K
             g[2] += 1
+            g[3] += gemm_bytes(M, N, segs, acc)
         elif work is not None:
             kind, rows, cols = work
             b = bw.setdefault(name, [0.0, 0.0, 0])
@@ -762,9 +786,9 @@ def main():
     steps = args.steps
     gemm_ms = cat_ms.get("gemm", 0.0) / steps
     dom_tile = max(gemm_by_tile, key=lambda k: gemm_by_tile[k][0])
-    dt_ms, dflops, dcount = gemm_by_tile[dom_tile]
+    dt_ms, dflops, dcount, dbytes = gemm_by_tile[dom_tile]
     achieved = dflops / (dt_ms * 1e-3) / 1e12
-    kname = f"pact::k_gemm_nvfp4{'_fast' if dom_tile[2] else ''}<{dom_tile[0] // 64}, {dom_tile[1] // 64}>"
+    kname = gemm_kernel_name(*dom_tile)
 
     traffic = None
     tfile = os.path.join(ROOT, "profiles", "gemm_traffic.json")
@@ -805,8 +829,8 @@ def main():
         "gpu_ms_per_step_events": round(gpu_ms / steps, 4),
         "timed_region": "hip graph replays of the step" if graph is not None else "eager steps",
         "schedule": ("one stream" if side_streams is None else
-                     "independent branches on 2 side streams (q/k/v and gate/up forward; LoRA backwards beside "
-                     "the input-gradient GEMMs)"),
+                     "independent branches on 2 side streams (q/k/v and gate/up forward, their LoRA "
+                     "backwards); one input-gradient launch each for q/k/v and gate/up"),
         "schedule_matches_one_stream": schedule_matches,
         "kernel_ms_per_step_by_category": {k: round(v / steps, 4) for k, v in sorted(cat_ms.items())},
         "bandwidth_kernels": quant,
@@ -816,6 +840,7 @@ def main():
                      "frac_of_fp4_peak": round(achieved / PEAK["fp4_mfma_tflops"], 4),
                      "launches_per_step": dcount // steps,
                      "avg_launch_us": round(dt_ms * 1e3 / dcount, 2),
+                     "algorithmic_bytes_per_launch": round(dbytes / dcount),
                      "traffic": traffic},
     }
     if not args.no_recipes:

@@ -660,12 +660,7 @@ __global__ __launch_bounds__(256, 1) void k_gemm_nvfp4_fast(GemmArgs p, int tile
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
   bool any_lora = false;
   // one rank-r term (T, U) per segment with SEG, else p's
-  for (int lp = 0; lp < (SEG ? sg.nseg : 1); ++lp) {
-    const uint16_t* lt = SEG ? sg.s[lp].lora_t : p.lora_t;
-    const uint16_t* lu = SEG ? sg.s[lp].lora_u : p.lora_u;
-    if (lt == nullptr) continue;
-    any_lora = true;
-    const int64_t r = SEG ? sg.s[lp].lora_r : p.lora_r;
+  auto lora_term = [&](const uint16_t* lt, const uint16_t* lu, int64_t r) __attribute__((always_inline)) {
     const bool t_vec = (r & 15) == 0;                          // T rows: 16-byte aligned runs of 8 ranks
     const bool u_vec = t_vec && p.u_stride_j == 1;             // U(j, n) = B[n][j]: same for B rows
     for (int64_t k0 = 0; k0 < r; k0 += 16) {
@@ -704,6 +699,16 @@ __global__ __launch_bounds__(256, 1) void k_gemm_nvfp4_fast(GemmArgs p, int tile
         for (int j = 0; j < WTN; ++j)
           acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tf[i], uf[j], acc[i][j], 0, 0, 0);
     }
+  };
+  if constexpr (SEG) {
+    for (int lp = 0; lp < sg.nseg; ++lp)
+      if (sg.s[lp].lora_t != nullptr) {
+        any_lora = true;
+        lora_term(sg.s[lp].lora_t, sg.s[lp].lora_u, sg.s[lp].lora_r);
+      }
+  } else if (p.lora_t != nullptr) {
+    any_lora = true;
+    lora_term(p.lora_t, p.lora_u, p.lora_r);
   }
   if (any_lora) {
     PACT_WAIT_VMCNT(0);
@@ -723,11 +728,9 @@ __global__ __launch_bounds__(256, 1) void k_gemm_nvfp4_fast(GemmArgs p, int tile
         }
       }
   }
-  // One pass of the stage pipeline over nks stages whose first two stages'
-  // loads are in flight.
-  auto run_segment = [&](int nks) __attribute__((always_inline)) {
+  if constexpr (!SEG) {
     // stage 0 (and the row scales) complete and visible
-    if (nks > 1) PACT_WAIT_VMCNT(C::LOADS);
+    if (nk > 1) PACT_WAIT_VMCNT(C::LOADS);
     else PACT_WAIT_VMCNT(0);
     __syncthreads();
     read_codes(smem, 0);
@@ -735,15 +738,15 @@ __global__ __launch_bounds__(256, 1) void k_gemm_nvfp4_fast(GemmArgs p, int tile
     cvt_chunk_scales(0);
     deq_step(0, af[0], bf[0]);
     int kt = 0;
-    for (; kt + 2 < nks; ++kt) run_stage(kt, std::true_type{});
-    for (; kt < nks; ++kt) run_stage(kt, std::false_type{});
-  };
-  // segments after the first: every wave is past its reads of the stage
-  // buffers before they refill, and the accumulator changes to the segment's
-  // row-scale units (one copy of the pipeline serves every segment)
-  for (int sgi = 0; sgi < (SEG ? sg.nseg : 1); ++sgi) {
-    int nks = nk0;
-    if constexpr (SEG) {
+    for (; kt + 2 < nk; ++kt) run_stage(kt, std::true_type{});
+    for (; kt < nk; ++kt) run_stage(kt, std::false_type{});
+  } else {
+    // one pass of the stage pipeline per segment (its first two stages'
+    // loads in flight); before a later segment every wave is past its reads
+    // of the stage buffers, and the accumulator changes to the segment's
+    // row-scale units (one copy of the pipeline serves every segment)
+    for (int sgi = 0; sgi < sg.nseg; ++sgi) {
+      int nks = nk0;
       if (sgi > 0) {
         PACT_WAIT_VMCNT(0);
         __syncthreads();
@@ -753,8 +756,17 @@ __global__ __launch_bounds__(256, 1) void k_gemm_nvfp4_fast(GemmArgs p, int tile
         issue_stage(0, 0);
         if (nks > 1) issue_stage(1, 1);
       }
+      if (nks > 1) PACT_WAIT_VMCNT(C::LOADS);
+      else PACT_WAIT_VMCNT(0);
+      __syncthreads();
+      read_codes(smem, 0);
+      read_scales(smem, sra, srb);
+      cvt_chunk_scales(0);
+      deq_step(0, af[0], bf[0]);
+      int kt = 0;
+      for (; kt + 2 < nks; ++kt) run_stage(kt, std::true_type{});
+      for (; kt < nks; ++kt) run_stage(kt, std::false_type{});
     }
-    run_segment(nks);
   }
   PACT_WAIT_VMCNT(0);
 
