@@ -790,14 +790,20 @@ def main():
     achieved = dflops / (dt_ms * 1e-3) / 1e12
     kname = gemm_kernel_name(*dom_tile)
 
+    # every GEMM kernel of the step: launches, time and algorithmic bytes
+    gemm_kernels = {gemm_kernel_name(*k): {"launches_per_step": g[2] // steps,
+                                           "avg_launch_us": round(g[0] * 1e3 / g[2], 2),
+                                           "tflops": round(g[1] / (g[0] * 1e-3) / 1e12, 1),
+                                           "algorithmic_bytes_per_launch": round(g[3] / g[2])}
+                    for k, g in sorted(gemm_by_tile.items(), key=lambda kv: -kv[1][0])}
+
     traffic = None
     tfile = os.path.join(ROOT, "profiles", "gemm_traffic.json")
     if os.path.exists(tfile):
         try:
             tj = json.load(open(tfile))
-            if tj.get("src_hash") == src_hash("gemm.hip", "nvfp4_device.h", "lds_dma.h", "mfma_fp16.h") and tj.get("kernel") == kname \
-                    and tj.get("tile") == list(dom_tile[:2]):
-                traffic = tj.get("bytes_per_launch")
+            if tj.get("src_hash") == src_hash("gemm.hip", "nvfp4_device.h", "lds_dma.h", "mfma_fp16.h"):
+                traffic = tj.get("kernels", {}).get(kname, {}).get("bytes_per_launch")
         except (ValueError, OSError):
             traffic = None
 
@@ -834,6 +840,7 @@ def main():
         "schedule_matches_one_stream": schedule_matches,
         "kernel_ms_per_step_by_category": {k: round(v / steps, 4) for k, v in sorted(cat_ms.items())},
         "bandwidth_kernels": quant,
+        "gemm_kernels": gemm_kernels,
         "roofline": {"kernel": kname, "bound": "mfma", "achieved": round(achieved, 1),
                      "peak": PEAK["fp16_mfma_tflops"], "unit": "TFLOP/s",
                      "frac": round(achieved / PEAK["fp16_mfma_tflops"], 4),
