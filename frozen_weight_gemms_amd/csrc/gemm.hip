@@ -560,22 +560,24 @@ __global__ __launch_bounds__(256, 1) void k_gemm_nvfp4_fast(GemmArgs p, int tile
   // accumulator from units of segment cseg's row scales to those of cseg + 1
   auto rescale_acc = [&](int cseg) __attribute__((always_inline)) {
     if constexpr (SEG) {
-      const float* ro = rsc0 + cseg * C::ROWS;
+      // this lane's rows are wm (BM / 2) + 4h + (a compile-time offset), its
+      // columns BM + wn (BN / 2) + li + 32 j: one base address each, so every
+      // read takes an immediate offset
+      const float* ro = rsc0 + cseg * C::ROWS + wm * (BM / 2) + 4 * h;
       const float* rn = ro + C::ROWS;
+      const float* co = rsc0 + cseg * C::ROWS + BM + wn * (BN / 2) + li;
+      const float* cn = co + C::ROWS;
       auto ex = [](float v) { return (int)((__float_as_uint(v) >> 23) & 255u); };
       int dcol[WTN];
 #pragma unroll
-      for (int j = 0; j < WTN; ++j) {
-        const int col = BM + wn * (BN / 2) + j * 32 + li;
-        dcol[j] = ex(ro[col]) - ex(rn[col]);
-      }
+      for (int j = 0; j < WTN; ++j) dcol[j] = ex(co[j * 32]) - ex(cn[j * 32]);
 #pragma unroll
       for (int i = 0; i < WTM; ++i)
 #pragma unroll
         for (int rr = 0; rr < 16; ++rr) {
           __builtin_amdgcn_sched_barrier(0);               // a few live exponents at a time
-          const int row = wm * (BM / 2) + i * 32 + 8 * (rr >> 2) + 4 * h + (rr & 3);
-          const int drow = ex(ro[row]) - ex(rn[row]);
+          const int off = i * 32 + 8 * (rr >> 2) + (rr & 3);
+          const int drow = ex(ro[off]) - ex(rn[off]);
 #pragma unroll
           for (int j = 0; j < WTN; ++j) acc[i][j][rr] = __builtin_ldexpf(acc[i][j][rr], drow + dcol[j]);
         }
@@ -650,83 +652,126 @@ __global__ __launch_bounds__(256, 1) void k_gemm_nvfp4_fast(GemmArgs p, int tile
 
   // The LoRA term is formed while those loads are in flight: acc starts as
   // (lora_scale / (rA rB)) * T U, so the epilogue's row-scale multiply turns
-  // it into lora_scale * T U.  (The compiler's wait for the T/U loads also
-  // covers the stages issued above.)
+  // it into lora_scale * T U.  The T rows are scaled by f_m = lora_scale / rA
+  // and the U columns by 1/rB as they are loaded (1/rA and 1/rB are powers of
+  // two), so the MFMAs produce the term directly and the accumulator is never
+  // rescaled.  With a power-of-two lora_scale, T f_m is exact in BF16 (which
+  // has FP32's exponent range).  Otherwise x = fl32(T f_m) is split into three
+  // BF16 values hi + mid + lo = x exactly (each residual is exact in FP32 and
+  // the last has at most 8 significant bits), and the term runs three MFMA
+  // passes, one per piece.  (The compiler's wait for the T/U loads also covers
+  // the stages issued above.)
 #pragma unroll
   for (int i = 0; i < WTM; ++i)
 #pragma unroll
     for (int j = 0; j < WTN; ++j)
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
-  bool any_lora = false;
+  // row scales are powers of two: 1/r is exact and computed on the exponent
+  auto inv_pow2 = [](float v) { return __uint_as_float((254u << 23) - __float_as_uint(v)); };
+  const uint32_t s_bits = __float_as_uint(p.lora_scale);
+  const uint32_t s_exp = (s_bits >> 23) & 255u;
+  const int npieces = ((s_bits & 0x7FFFFFu) == 0 && s_exp >= 1u && s_exp <= 254u) ? 1 : 3;
+  // row scales the accumulator's units refer to (the first segment's with SEG)
+  const float* const lra = SEG ? sg.s[0].a_rscale : p.a_rscale;
+  const float* const lrb = SEG ? sg.s[0].b_rscale : p.b_rscale;
+  // eight BF16 values times f; piece 0, 1, 2 of the exact three-way split
+  auto scaled = [](uint4 v, float f, int piece) __attribute__((always_inline)) {
+    auto one = [&](float x) {
+      const float hi = __uint_as_float(f32_to_bf16_rne(x) << 16);
+      if (piece == 0) return hi;
+      const float r1 = x - hi;
+      const float mid = __uint_as_float(f32_to_bf16_rne(r1) << 16);
+      return piece == 1 ? mid : r1 - mid;
+    };
+    uint4 o;
+    o.x = pack_bf16x2(one(bf16_lo(v.x) * f), one(bf16_hi(v.x) * f));
+    o.y = pack_bf16x2(one(bf16_lo(v.y) * f), one(bf16_hi(v.y) * f));
+    o.z = pack_bf16x2(one(bf16_lo(v.z) * f), one(bf16_hi(v.z) * f));
+    o.w = pack_bf16x2(one(bf16_lo(v.w) * f), one(bf16_hi(v.w) * f));
+    return __builtin_bit_cast(bf16x8_t, o);
+  };
+  // T row and U column factors of this lane's fragments
+  float fa[WTM], fb[WTN];
+  auto lora_factors = [&]() __attribute__((always_inline)) {
+#pragma unroll
+    for (int i = 0; i < WTM; ++i) {
+      int64_t m = m0 + wm * (BM / 2) + i * 32 + li;
+      m = m < M ? m : M - 1;
+      fa[i] = p.lora_scale * inv_pow2(lra[m]);
+    }
+#pragma unroll
+    for (int i = 0; i < WTN; ++i) {
+      int64_t n = n0 + wn * (BN / 2) + i * 32 + li;
+      n = n < N ? n : N - 1;
+      fb[i] = inv_pow2(lrb[n]);
+    }
+  };
   // one rank-r term (T, U) per segment with SEG, else p's
   auto lora_term = [&](const uint16_t* lt, const uint16_t* lu, int64_t r) __attribute__((always_inline)) {
     const bool t_vec = (r & 15) == 0;                          // T rows: 16-byte aligned runs of 8 ranks
     const bool u_vec = t_vec && p.u_stride_j == 1;             // U(j, n) = B[n][j]: same for B rows
     for (int64_t k0 = 0; k0 < r; k0 += 16) {
-      bf16x8_t tf[WTM], uf[WTN];
+      uint4 tv[WTM];
+      bf16x8_t uf[WTN];
 #pragma unroll
       for (int i = 0; i < WTM; ++i) {
         int64_t m = m0 + wm * (BM / 2) + i * 32 + li;
         m = m < M ? m : M - 1;
+        uint4& v = tv[i];
         if (t_vec) {
-          tf[i] = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const uint4*>(lt + m * r + k0 + 8 * h));
+          v = *reinterpret_cast<const uint4*>(lt + m * r + k0 + 8 * h);
         } else {
+          uint32_t e[8];
 #pragma unroll
           for (int t = 0; t < 8; ++t) {
             const int64_t j = k0 + 8 * h + t;
-            tf[i][t] = bf16_of(j < r ? lt[m * r + j] : (uint16_t)0);
+            e[t] = j < r ? lt[m * r + j] : 0u;
           }
+          v = make_uint4(e[0] | (e[1] << 16), e[2] | (e[3] << 16), e[4] | (e[5] << 16), e[6] | (e[7] << 16));
         }
       }
 #pragma unroll
       for (int i = 0; i < WTN; ++i) {
         int64_t n = n0 + wn * (BN / 2) + i * 32 + li;
         n = n < N ? n : N - 1;
+        uint4 v;
         if (u_vec) {
-          uf[i] = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const uint4*>(lu + n * p.u_stride_n + k0 + 8 * h));
+          v = *reinterpret_cast<const uint4*>(lu + n * p.u_stride_n + k0 + 8 * h);
         } else {
+          uint32_t e[8];
 #pragma unroll
           for (int t = 0; t < 8; ++t) {
             const int64_t j = k0 + 8 * h + t;
-            uf[i][t] = bf16_of(j < r ? lu[j * p.u_stride_j + n * p.u_stride_n] : (uint16_t)0);
+            e[t] = j < r ? lu[j * p.u_stride_j + n * p.u_stride_n] : 0u;
           }
+          v = make_uint4(e[0] | (e[1] << 16), e[2] | (e[3] << 16), e[4] | (e[5] << 16), e[6] | (e[7] << 16));
         }
+        uf[i] = scaled(v, fb[i], 0);
       }
+      for (int piece = 0; piece < npieces; ++piece) {
+        bf16x8_t tf[WTM];
 #pragma unroll
-      for (int i = 0; i < WTM; ++i)
+        for (int i = 0; i < WTM; ++i) tf[i] = scaled(tv[i], fa[i], piece);
 #pragma unroll
-        for (int j = 0; j < WTN; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tf[i], uf[j], acc[i][j], 0, 0, 0);
+        for (int i = 0; i < WTM; ++i)
+#pragma unroll
+          for (int j = 0; j < WTN; ++j)
+            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tf[i], uf[j], acc[i][j], 0, 0, 0);
+      }
     }
   };
   if constexpr (SEG) {
-    for (int lp = 0; lp < sg.nseg; ++lp)
-      if (sg.s[lp].lora_t != nullptr) {
-        any_lora = true;
-        lora_term(sg.s[lp].lora_t, sg.s[lp].lora_u, sg.s[lp].lora_r);
-      }
+    bool any = false;
+    for (int lp = 0; lp < sg.nseg; ++lp) any = any || sg.s[lp].lora_t != nullptr;
+    if (any) {
+      lora_factors();
+      for (int lp = 0; lp < sg.nseg; ++lp)
+        if (sg.s[lp].lora_t != nullptr) lora_term(sg.s[lp].lora_t, sg.s[lp].lora_u, sg.s[lp].lora_r);
+    }
   } else if (p.lora_t != nullptr) {
-    any_lora = true;
+    lora_factors();
     lora_term(p.lora_t, p.lora_u, p.lora_r);
-  }
-  if (any_lora) {
-    PACT_WAIT_VMCNT(0);
-    __syncthreads();                                           // every wave's row-scale loads have landed
-    // row scales are powers of two: 1/r is exact and computed on the exponent
-    auto inv_pow2 = [](float v) { return __uint_as_float((254u << 23) - __float_as_uint(v)); };
-#pragma unroll
-    for (int i = 0; i < WTM; ++i)
-#pragma unroll
-      for (int rr = 0; rr < 16; ++rr) {
-        const int row = wm * (BM / 2) + i * 32 + 8 * (rr >> 2) + 4 * h + (rr & 3);
-        const float fa = p.lora_scale * inv_pow2(rsc[row]);
-#pragma unroll
-        for (int j = 0; j < WTN; ++j) {
-          const int col = wn * (BN / 2) + j * 32 + li;
-          acc[i][j][rr] *= fa * inv_pow2(rsc[BM + col]);
-        }
-      }
   }
   if constexpr (!SEG) {
     // stage 0 (and the row scales) complete and visible

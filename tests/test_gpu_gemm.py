@@ -102,6 +102,43 @@ def test_lora_epilogue_fwd(fw):
     assert_within(torch_bf16_to_f64(y), yref + term, tol.gemm_bound(yref + term, yabs + tabs), "fwd+lora")
 
 
+
+@pytest.mark.parametrize("M,N,K", [(96, 320, 256), (200, 1536, 512), (4096, 2048, 256), (1024, 12288, 256),
+                                   (2048, 12288, 256)])
+@pytest.mark.parametrize("s", [2.0, 0.75, -1.0 / 3.0])
+def test_lora_term_scale_under_cancellation(fw, M, N, K, s):
+    """lora_scale * T B^T alone (W = 0), with rank pairs that nearly cancel:
+    T = [T1, T2] with T2 = bf16(T1 (1 + 2^-6)) and B = [B1, -B1], so the term is
+    about 2^-6 of sum |T||B| and the bound (1e-5 of that sum plus one BF16 ulp)
+    exposes any rounding of s T before the products.  Fast-path tiles:
+    128 x 128 (the first two, one with a ragged row tile), 256 x 128,
+    256 x 192 and 256 x 256.  A power-of-two s scales T exactly; any other s
+    must keep FP32 accuracy of s T (a single BF16 rounding of s T / r_A is
+    shown below to violate the bound)."""
+    x = synth.activations_bf16((M, K), 95, 1)
+    w = np.zeros((N, K), dtype=np.uint16)
+    t1 = synth.normal_bf16((M, 16), 0.3, 95, 3)
+    t2 = synth.bf16_bits(synth.bf16_from_bits(t1) * np.float32(1 + 2.0 ** -6))
+    b1 = synth.normal_bf16((N, 16), 0.01, 95, 4)
+    t = np.ascontiguousarray(np.hstack([t1, t2]))
+    b = np.ascontiguousarray(np.hstack([b1, b1 ^ np.uint16(0x8000)]))
+    xq, wf = _q(x), _q(w)
+    y = fw.gemm_fwd(nvfp4_to_gpu(xq), nvfp4_to_gpu(wf), lora_t=bits_to_torch(t), lora_b=bits_to_torch(b),
+                    lora_scale=s)
+    rows = np.arange(M) if M <= 256 else np.sort(np.random.default_rng(M + N).choice(M, size=64, replace=False))
+    rows[-1] = M - 1
+    tv, bv = bf16_values(t)[rows], bf16_values(b)
+    term, tabs, _ = olora.lora_term(tv, bv.T, s)
+    bound = tol.gemm_bound(term, tabs)
+    assert_within(torch_bf16_to_f64(y)[rows], term, bound, f"lora s={s} {M}x{N}x{K}")
+    if s != 2.0:
+        # the planted mistake: s T / r_A rounded once to BF16, then exact products
+        f = (np.float32(s) * (np.float32(1.0) / xq.rscale[rows])).astype(np.float32)
+        hi = synth.bf16_round((tv * f[:, None]).astype(np.float32)).astype(np.float64)
+        wrong = synth.bf16_round(((hi * xq.rscale[rows].astype(np.float64)[:, None]) @ bv.T.astype(np.float64))
+                                 .astype(np.float32)).astype(np.float64)
+        assert tol.violations(wrong, term, bound)[0] > 0, "the case does not separate FP32 from BF16 scaling"
+
 @pytest.mark.parametrize("M,N,K,r", [(80, 192, 272, 16), (200, 512, 320, 16), (64, 768, 1100, 5)])
 def test_dgrad_accumulate_and_lora(fw, M, N, K, r):
     """N is the contraction length of the input gradient: 192 and 1100 take the
