@@ -526,8 +526,9 @@ __global__ __launch_bounds__(256, 1) void k_gemm_nvfp4_fast(GemmArgs p, int tile
     }
   };
   // MFMAs of K step s.  With dma set, the loads of stage dma_kt into buffer
-  // dma_buf are spread over the MFMAs of steps 12-14 (one instruction every
-  // DMA_SP MFMAs), so the wave's vector-memory issue overlaps the matrix core.
+  // dma_buf are spread over the MFMAs of steps 13-15 (one instruction every
+  // DMA_SP MFMAs), so the wave's vector-memory issue overlaps the matrix core
+  // (step 12 carries the LDS reads that follow the stage's barrier).
   constexpr int DMA_SP = (3 * WTM * WTN) / C::LOADS;
   static_assert(DMA_SP >= 1, "DMA spacing");
   auto mfma_step = [&](int s, int dma_kt, int dma_buf, bool dma) {
@@ -535,22 +536,27 @@ __global__ __launch_bounds__(256, 1) void k_gemm_nvfp4_fast(GemmArgs p, int tile
     for (int k = 0; k < WTM * WTN; ++k) {
       const int i = k / WTN, j = k % WTN;
       acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(af[s & 1][i], bf[s & 1][j], acc[i][j], 0, 0, 0);
-      const int g = (s - 12) * WTM * WTN + k;
-      if (dma && s >= 12 && g % DMA_SP == 0 && g / DMA_SP < C::LOADS) issue_one(dma_kt, dma_buf, g / DMA_SP);
+      const int g = (s - 13) * WTM * WTN + k;
+      if (dma && s >= 13 && g % DMA_SP == 0 && g / DMA_SP < C::LOADS) issue_one(dma_kt, dma_buf, g / DMA_SP);
     }
   };
   // one MFMA : PACT_VALU_PER_MFMA VALU, front-loading the dequantization of
-  // the next step under the first MFMAs of this one
-  auto interleave = [&]() {
+  // the next step under the first MFMAs of this one; nr LDS reads of the step
+  // go one (or two) after each of its first MFMAs, so the wave's in-order
+  // issue never waits behind a burst of reads
+  auto interleave = [&](int nr) __attribute__((always_inline)) {
+    constexpr int NM = WTM * WTN;
 #pragma unroll
-    for (int k = 0; k < WTM * WTN; ++k) {
+    for (int k = 0; k < NM; ++k) {
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      if (k < nr - NM) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+      else if (k < nr) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
       __builtin_amdgcn_sched_group_barrier(0x002, PACT_VALU_PER_MFMA, 0);
     }
   };
 
   // Stage kt lives in LDS buffer kt % 2.  Its loads are issued during steps
-  // 12-14 of stage kt - 2 (stages 0 and 1 in the prologue) and published by the
+  // 13-15 of stage kt - 2 (stages 0 and 1 in the prologue) and published by the
   // barrier at step 12 of stage kt - 1.  Each wave reads codes one chunk ahead:
   // chunk c + 1 during chunk c, and chunk 0 plus the scales of stage kt + 1
   // during chunk 3 of stage kt.  By the barrier at step 12 of stage kt every
@@ -590,21 +596,27 @@ __global__ __launch_bounds__(256, 1) void k_gemm_nvfp4_fast(GemmArgs p, int tile
     const uint8_t* st = smem + (kt & 1) * C::STAGE;
 #pragma unroll
     for (int c = 0; c < 4; ++c) {
-      __builtin_amdgcn_sched_barrier(0);
-      if (c < 3) {
-        read_codes(st, c + 1);
-      } else {
-        // publish stage kt + 1 (the only loads in flight); after the last
-        // stage the reads below fetch a stale in-bounds buffer, never used
-        PACT_WAIT_VMCNT(0);
-        __syncthreads();
-        const uint8_t* stn = smem + ((kt + 1) & 1) * C::STAGE;
-        read_codes(stn, 0);
-        read_scales(stn, sra_n, srb_n);
-      }
 #pragma unroll
       for (int s = 4 * c; s < 4 * c + 4; ++s) {
         __builtin_amdgcn_sched_barrier(0);
+        // the first step of chunk c reads chunk c + 1 (at chunk 3: the next
+        // stage's chunk 0 and scales), spread over its MFMAs
+        int nr = 0;
+        if (s == 4 * c) {
+          if (c < 3) {
+            read_codes(st, c + 1);
+            nr = WTM + WTN;
+          } else {
+            // publish stage kt + 1 (the only loads in flight); after the last
+            // stage the reads below fetch a stale in-bounds buffer, never used
+            PACT_WAIT_VMCNT(0);
+            __syncthreads();
+            const uint8_t* stn = smem + ((kt + 1) & 1) * C::STAGE;
+            read_codes(stn, 0);
+            read_scales(stn, sra_n, srb_n);
+            nr = 2 * (WTM + WTN);
+          }
+        }
         if (s == 15) {
 #pragma unroll
           for (int i = 0; i < WTM; ++i) sra[i] = sra_n[i];
@@ -617,7 +629,7 @@ __global__ __launch_bounds__(256, 1) void k_gemm_nvfp4_fast(GemmArgs p, int tile
           deq_step(s + 1, af[(s + 1) & 1], bf[(s + 1) & 1]);
         }
         mfma_step(s, kt + 2, kt & 1, DMA);
-        interleave();
+        interleave(nr);
         __builtin_amdgcn_sched_barrier(0);
       }
     }
