@@ -771,7 +771,9 @@ def main():
             _, M, N, segs, acc = work
             K = sum(segs)
             # kernel group: (bm, bn, stage-pipelined path, segmented)
-            tile = _lib.gemm_tile(M, N, K) + (all(k % 256 == 0 for k in segs), len(segs) > 1)
+            seg = len(segs) > 1
+            tile = (_lib.gemm_multi_tile(M, N) if seg else _lib.gemm_tile(M, N, K)) + \
+                (all(k % 256 == 0 for k in segs), seg)
             g = gemm_by_tile.setdefault(tile, [0.0, 0.0, 0, 0.0])
             g[0] += t
             g[1] += 2.0 * M * N * K

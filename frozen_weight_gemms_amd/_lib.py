@@ -30,6 +30,7 @@ SIGNATURES = {
     "pact_abi_version": ([], c_int),
     "pact_nvfp4_sizes": ([c_i64, c_i64, c_size_p, c_size_p, c_size_p], c_int),
     "pact_gemm_tile": ([c_i64, c_i64, c_i64, ctypes.POINTER(c_int), ctypes.POINTER(c_int)], c_int),
+    "pact_gemm_multi_tile": ([c_i64, c_i64, ctypes.POINTER(c_int), ctypes.POINTER(c_int)], c_int),
     "nvfp4_quantize": ([c_vp, c_i64, c_i64, c_i64, c_int, c_vp, c_vp, c_vp, c_vp], c_int),
     "rmsnorm_quant": ([c_vp, c_vp, c_float, c_i64, c_i64, c_i64, c_vp, c_vp, c_vp, c_vp, c_vp], c_int),
     "silu_mul_quant": ([c_vp, c_vp, c_i64, c_i64, c_i64] + [c_vp] * 9 + [c_vp], c_int),
@@ -104,6 +105,14 @@ def gemm_tile(M: int, Nout: int, Kr: int):
     lib = load()
     bm, bn = c_int(), c_int()
     check(lib.pact_gemm_tile(M, Nout, Kr, ctypes.byref(bm), ctypes.byref(bn)))
+    return bm.value, bn.value
+
+
+def gemm_multi_tile(M: int, Nout: int):
+    """(bm, bn) workgroup tile the segmented input-gradient GEMM launches for this output shape."""
+    lib = load()
+    bm, bn = c_int(), c_int()
+    check(lib.pact_gemm_multi_tile(M, Nout, ctypes.byref(bm), ctypes.byref(bn)))
     return bm.value, bn.value
 
 

@@ -69,7 +69,7 @@ extern "C" {
 
 const char* pact_last_error(void) { return g_err; }
 
-int pact_abi_version(void) { return 7; }
+int pact_abi_version(void) { return 8; }
 
 int pact_nvfp4_sizes(int64_t rows, int64_t cols, size_t* codes_bytes, size_t* scales_bytes, size_t* rscale_bytes) {
   REQUIRE(rows >= 0 && cols >= 0, PACT_EINVAL, "negative size (rows=%lld, cols=%lld)", (long long)rows,
@@ -86,6 +86,13 @@ int pact_gemm_tile(int64_t M, int64_t Nout, int64_t Kr, int* bm, int* bn) {
   REQUIRE(M >= 0 && Nout >= 0 && Kr >= 0, PACT_EINVAL, "negative size");
   REQUIRE(bm != nullptr && bn != nullptr, PACT_EINVAL, "NULL output pointer");
   pact::gemm_tile(M, Nout, bm, bn);
+  return ok();
+}
+
+int pact_gemm_multi_tile(int64_t M, int64_t Nout, int* bm, int* bn) {
+  REQUIRE(M >= 0 && Nout >= 0, PACT_EINVAL, "negative size");
+  REQUIRE(bm != nullptr && bn != nullptr, PACT_EINVAL, "NULL output pointer");
+  pact::gemm_multi_tile(M, Nout, bm, bn);
   return ok();
 }
 

@@ -928,12 +928,21 @@ bool gemm_multi_supported(const GemmArgs& a, const SegArgs& sg) {
   return true;
 }
 
+// The segmented kernel has no 256 x 256 instantiation: with the segment loop
+// around the pipeline that tile's per-lane load offsets no longer fit in
+// registers (hundreds of spilled values, reloaded before every segment's first
+// loads), while 256 x 192 tiles stay spill-free at the same MFMA rate per tile
+// column.
+void gemm_multi_tile(int64_t M, int64_t N, int* bm, int* bn) {
+  gemm_tile(M, N, bm, bn);
+  if (*bm == 256 && *bn == 256) *bn = 192;
+}
+
 hipError_t launch_gemm_multi(const GemmArgs& a, const SegArgs& sg, hipStream_t s) {
   int bm, bn;
-  gemm_tile(a.M, a.N, &bm, &bn);
+  gemm_multi_tile(a.M, a.N, &bm, &bn);
   const int tm = (int)((a.M + bm - 1) / bm), tn = (int)((a.N + bn - 1) / bn);
-  if (bm == 256 && bn == 256) k_gemm_nvfp4_fast<4, 4, true><<<tm * tn, 256, 0, s>>>(a, tm, tn, sg);
-  else if (bn == 192) k_gemm_nvfp4_fast<4, 3, true><<<tm * tn, 256, 0, s>>>(a, tm, tn, sg);
+  if (bn == 192) k_gemm_nvfp4_fast<4, 3, true><<<tm * tn, 256, 0, s>>>(a, tm, tn, sg);
   else if (bm == 256) k_gemm_nvfp4_fast<4, 2, true><<<tm * tn, 256, 0, s>>>(a, tm, tn, sg);
   else k_gemm_nvfp4_fast<2, 2, true><<<tm * tn, 256, 0, s>>>(a, tm, tn, sg);
   return hipGetLastError();

@@ -75,6 +75,7 @@ struct SegArgs {
 bool gemm_multi_supported(const GemmArgs& a, const SegArgs& sg);
 hipError_t launch_gemm_multi(const GemmArgs& a, const SegArgs& sg, hipStream_t s);
 void gemm_tile(int64_t M, int64_t N, int* bm, int* bn);
+void gemm_multi_tile(int64_t M, int64_t N, int* bm, int* bn);
 
 // Single-layout input gradient: dX [M x K] = deq(dY_q [M x N]) deq(W_fwd [N x K]);
 // bexp = largest row exponent over W_fwd's nonzero rows (device int, from launch_row_exp_max)

@@ -155,6 +155,14 @@ int silu_mul_quant(const uint16_t *gate, const uint16_t *up, int64_t M, int64_t 
 int pact_gemm_tile(int64_t M, int64_t Nout, int64_t Kr, int *bm, int *bn);
 
 /*
+ * pact_gemm_multi_tile -- host-only query: the workgroup tile that
+ * nvfp4_gemm_dgrad_multi launches for an output of M x Nout (the tile of
+ * pact_gemm_tile, except that a 256 x 256 tile becomes 256 x 192: the
+ * segmented kernel has no 256 x 256 instantiation).
+ */
+int pact_gemm_multi_tile(int64_t M, int64_t Nout, int *bm, int *bn);
+
+/*
  * nvfp4_gemm_fwd -- frozen-projection forward Y = X W^T (Appendix Table 7 row
  * "Frozen projections": NVFP4 GEMM, FP32 accumulation, BF16 output).
  *   X_q: NVFP4 [M x K]; W_fwd: NVFP4 [N x K] (= Q(W), the cached forward layout).

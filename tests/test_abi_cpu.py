@@ -25,7 +25,7 @@ def lib():
 
 def test_header_symbols_exported(lib):
     names = _lib.header_functions()
-    assert len(names) == 24, names
+    assert len(names) == 25, names
     assert set(names) == set(_lib.SIGNATURES), set(names) ^ set(_lib.SIGNATURES)
     for n in names:
         assert hasattr(lib, n), n
@@ -49,10 +49,15 @@ def test_gemm_tile_query(lib):
     assert _lib.gemm_tile(4096, 3072, 3072) == (256, 192)
     assert _lib.gemm_tile(4096, 1024, 3072) == (128, 128)
     assert lib.pact_gemm_tile(-1, 1, 1, None, None) == -1
+    assert _lib.gemm_multi_tile(2048, 12288) == (256, 192)      # 256 x 256 for the plain GEMM
+    assert _lib.gemm_multi_tile(4096, 3072) == (256, 192)
+    assert _lib.gemm_multi_tile(4096, 2048) == (256, 128)
+    assert _lib.gemm_multi_tile(160, 640) == (128, 128)
+    assert lib.pact_gemm_multi_tile(-1, 1, None, None) == -1
 
 
 def test_abi_version(lib):
-    assert lib.pact_abi_version() == 7
+    assert lib.pact_abi_version() == 8
 
 
 def test_sizes(lib):

@@ -105,6 +105,47 @@ def test_llama3b_sampled(fw, name, widths, K):
     assert_within(torch_bf16_to_f64(dx)[np.ix_(rows, kcols)], ref, tol.gemm_bound(ref, rabs), name)
 
 
+
+@pytest.mark.parametrize("M,K,widths", [(2048, 12288, (512, 256, 256)), (4096, 2048, (256, 768)),
+                                        (1024, 12288, (256, 256, 256, 256)), (4096, 3072, (256, 512))])
+def test_segmented_tiles_sampled(fw, M, K, widths):
+    """Every tile of the segmented kernel (256 x 192 in place of 256 x 256,
+    256 x 128, 256 x 192), with row scales spread over 2^20 between segments,
+    LoRA terms on some segments and accumulate; 48 rows x 160 columns against
+    an exact sub-problem (quantization is per row of dY_i and of W_bwd,i)."""
+    assert fw._lib.gemm_multi_tile(M, K) in ((256, 192), (256, 128))
+    r = 16
+    rng = np.random.default_rng(M + K + len(widths))
+    rows = np.sort(rng.choice(M, size=48, replace=False))
+    rows[-1] = M - 1
+    kcols = np.sort(rng.choice(K, size=160, replace=False))
+    kcols[-1] = K - 1
+    spread = (1.0, 2.0 ** -12, 2.0 ** 8, 2.0 ** -4)
+    segs, lora, ref, rabs = [], [], 0.0, 0.0
+    for i, n in enumerate(widths):
+        dyv = bf16_values(synth.normal_bf16((M, n), 0.01, 97, 10 * i + 1)).astype(np.float64) * spread[i]
+        dy = synth.bf16_bits(dyv.astype(np.float32))
+        w = synth.normal_bf16((n, K), 0.02, 97, 10 * i + 2)
+        segs.append((fw.quantize(bits_to_torch(dy)), fw.quantize(bits_to_torch(w), transpose=True)))
+        a = onv.dequantize(onv.quantize(bf16_values(dy[rows]).astype(np.float64)))
+        b = _wbwd_rows(bf16_values(w).astype(np.float64), kcols)
+        ref = ref + a @ b.T
+        rabs = rabs + np.abs(a) @ np.abs(b).T
+        if i % 2 == 0:
+            dT = synth.normal_bf16((M, r), 0.01, 97, 10 * i + 3)
+            A = synth.normal_bf16((r, K), 0.01, 97, 10 * i + 4)
+            lora.append((bits_to_torch(dT), bits_to_torch(A)))
+            t, tabs, _ = olora.lora_term(bf16_values(dT)[rows], bf16_values(A)[:, kcols], 1.0)
+            ref, rabs = ref + t, rabs + tabs
+        else:
+            lora.append(None)
+    prev = synth.normal_bf16((M, K), 0.001, 97, 99)
+    out = bits_to_torch(prev).clone()
+    fw.gemm_dgrad_multi(segs, out=out, accumulate=True, lora=lora)
+    want = bf16_values(prev[np.ix_(rows, kcols)]).astype(np.float64) + ref
+    assert_within(torch_bf16_to_f64(out)[np.ix_(rows, kcols)], want, tol.gemm_bound(want, rabs),
+                  f"{M}x{K} widths {widths}")
+
 def test_unsupported_width_is_rejected(fw):
     dyq, wb = _seg(64, 272, 256, 7)
     with pytest.raises(fw.PactError, match="multiple of 256"):
