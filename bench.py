@@ -36,7 +36,8 @@ under "mxfp4_variant" and is not part of "value".
 A third leg ("recipe_variants") times the Q/K/V and gate/up GEMMs with
 stacked weights against separate ones, and the quantizer's variants; a fourth
 ("single_layout_dgrad") the input-gradient GEMMs over the forward weight
-layout only against the dual-layout ones.
+layout only against the dual-layout ones.  "quantizer_bandwidth" times nvfp4_quantize
+alone at the workloads' activation shapes (up to the 8B-scale 16384 x 14336).
 
 Prints one JSON line.  --gpus must be 1: this build runs on one GPU.
 """
@@ -489,6 +490,40 @@ def recipe_leg(fw, torch, synth, wl, n_inst=4, reps=5):
     return out
 
 
+def quantizer_leg(fw, torch, reps=5):
+    """nvfp4_quantize alone on the activation shapes of the workloads: the
+    Llama-3B hidden and intermediate widths at M = 4096 and the 8B-scale ones
+    at M = 16384.  Four distinct seeded inputs per shape (the same rotation
+    rule as the step, so small shapes are not served from the Infinity Cache),
+    back-to-back launches after a spin-kernel head start, best of `reps`."""
+    dev = "cuda"
+    gen = torch.Generator(device=dev)
+    out = {}
+    for M, K in ((4096, 3072), (4096, 8192), (16384, 4096), (16384, 14336)):
+        gen.manual_seed(M * 7 + K)
+        xs = [(torch.randn((M, K), generator=gen, device=dev) * 0.01).to(torch.bfloat16) for _ in range(4)]
+        qs = [fw.empty_nvfp4(M, K, dev) for _ in range(4)]
+        for x, q in zip(xs, qs):
+            fw.quantize(x, out=q)
+        torch.cuda.synchronize()
+        best = 1e30
+        for _ in range(reps):
+            torch.cuda._sleep(HEAD_START_CYCLES)
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            for x, q in zip(xs, qs):
+                fw.quantize(x, out=q)
+            e1.record()
+            torch.cuda.synchronize()
+            best = min(best, e0.elapsed_time(e1) / len(xs))
+        gbs = kernel_bytes("quant", M, K) / (best * 1e-3) / 1e9
+        out[f"{M}x{K}"] = {"us": round(best * 1e3, 2), "GB/s": round(gbs, 1),
+                           "frac_hbm": round(gbs / PEAK["hbm_gbs"], 3)}
+        del xs, qs
+        torch.cuda.synchronize()
+    return out
+
+
 def single_layout_leg(fw, torch, synth, wl, n_inst=4, reps=5):
     """Input-gradient GEMMs of the 7 projections per layer over the forward
     layout only (single-layout dgrad) versus over the cached backward layout,
@@ -855,6 +890,7 @@ def main():
     if not args.no_recipes:
         result["recipe_variants"] = recipe_leg(fw, torch, synth, wl)
         result["single_layout_dgrad"] = single_layout_leg(fw, torch, synth, wl)
+        result["quantizer_bandwidth"] = quantizer_leg(fw, torch)
     if not args.no_mxfp4:
         del graph
         result["mxfp4_variant"] = mxfp4_leg(fw, torch, synth, wl, max(1, args.layers), args.steps, args.warmup,
