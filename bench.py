@@ -37,7 +37,10 @@ A third leg ("recipe_variants") times the Q/K/V and gate/up GEMMs with
 stacked weights against separate ones, and the quantizer's variants; a fourth
 ("single_layout_dgrad") the input-gradient GEMMs over the forward weight
 layout only against the dual-layout ones.  "quantizer_bandwidth" times nvfp4_quantize
-alone at the workloads' activation shapes (up to the 8B-scale 16384 x 14336).
+alone at the workloads' activation shapes (up to the 8B-scale 16384 x 14336).  "lora_term" times each
+projection's GEMMs with and without the fused LoRA term; "mfma_loop_peak" is
+the measured back-to-back MFMA rate (FP16 and scaled FP4) and the clock held
+under it, reported beside the published peaks.
 
 Prints one JSON line.  --gpus must be 1: this build runs on one GPU.
 """
@@ -524,6 +527,60 @@ def quantizer_leg(fw, torch, reps=5):
     return out
 
 
+def lora_term_leg(fw, torch, synth, wl, reps=3, n=10):
+    """Cost of the LoRA term inside the frozen GEMMs: each projection's forward
+    (s T B^T) and input-gradient (dT A) GEMM timed with and without the term,
+    back-to-back launches after a spin-kernel head start, best of `reps`.
+    Reported per projection and as the sum over one decoder layer's seven
+    projections (each with its own launch; the step merges q/k/v and gate/up
+    input gradients, so this is an upper bound for those)."""
+    dev = "cuda"
+    M, r = wl.tokens, wl.lora_rank
+    up = lambda b: torch.from_numpy(b.view("int16")).view(torch.bfloat16).to(dev)
+
+    def best_us(fn):
+        fn()
+        torch.cuda.synchronize()
+        best = 1e30
+        for _ in range(reps):
+            torch.cuda._sleep(HEAD_START_CYCLES)
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            for _ in range(n):
+                fn()
+            e1.record()
+            torch.cuda.synchronize()
+            best = min(best, e0.elapsed_time(e1) * 1e3 / n)
+        return best
+
+    out, tot = {}, 0.0
+    seen = {}
+    for i, p in enumerate(wl.projections):
+        key = (p.d_in, p.d_out)
+        if key not in seen:
+            x = up(synth.activations_bf16((M, p.d_in), wl.wid, 9800 + i))
+            w = up(synth.normal_bf16((p.d_out, p.d_in), wl.w_std, wl.wid, 9810 + i))
+            dy = up(synth.normal_bf16((M, p.d_out), wl.dy_std, wl.wid, 9820 + i))
+            T = up(synth.normal_bf16((M, r), 0.3, wl.wid, 9830 + i))
+            B = up(synth.normal_bf16((p.d_out, r), wl.a_std, wl.wid, 9840 + i))
+            A = up(synth.normal_bf16((r, p.d_in), wl.a_std, wl.wid, 9850 + i))
+            dT = up(synth.normal_bf16((M, r), 0.01, wl.wid, 9860 + i))
+            xq, wf, wb, dyq = fw.quantize(x), fw.quantize(w), fw.quantize(w, transpose=True), fw.quantize(dy)
+            y = torch.empty((M, p.d_out), dtype=torch.bfloat16, device=dev)
+            dx = torch.empty((M, p.d_in), dtype=torch.bfloat16, device=dev)
+            f0 = best_us(lambda: fw.gemm_fwd(xq, wf, out=y))
+            f1 = best_us(lambda: fw.gemm_fwd(xq, wf, lora_t=T, lora_b=B, lora_scale=LORA_SCALE, out=y))
+            d0 = best_us(lambda: fw.gemm_dgrad(dyq, wb, out=dx))
+            d1 = best_us(lambda: fw.gemm_dgrad(dyq, wb, out=dx, lora_dt=dT, lora_a=A))
+            seen[key] = {"fwd_us": round(f0, 2), "fwd_lora_us": round(f1, 2),
+                         "dgrad_us": round(d0, 2), "dgrad_lora_us": round(d1, 2)}
+            del x, w, dy, xq, wf, wb, dyq, y, dx
+        out[p.name] = seen[key]
+        tot += (seen[key]["fwd_lora_us"] - seen[key]["fwd_us"]) + (seen[key]["dgrad_lora_us"] - seen[key]["dgrad_us"])
+    torch.cuda.synchronize()
+    return {"per_projection": out, "lora_term_us_per_layer": round(tot, 1)}
+
+
 def single_layout_leg(fw, torch, synth, wl, n_inst=4, reps=5):
     """Input-gradient GEMMs of the 7 projections per layer over the forward
     layout only (single-layout dgrad) versus over the cached backward layout,
@@ -891,10 +948,26 @@ def main():
         result["recipe_variants"] = recipe_leg(fw, torch, synth, wl)
         result["single_layout_dgrad"] = single_layout_leg(fw, torch, synth, wl)
         result["quantizer_bandwidth"] = quantizer_leg(fw, torch)
+        result["lora_term"] = lora_term_leg(fw, torch, synth, wl)
     if not args.no_mxfp4:
         del graph
         result["mxfp4_variant"] = mxfp4_leg(fw, torch, synth, wl, max(1, args.layers), args.steps, args.warmup,
                                             eager=args.eager)
+    # measured MFMA-loop peak beside the published dense peaks (no memory traffic in the loop)
+    p16, c16 = fw.mfma_probe(0)
+    p4, c4 = fw.mfma_probe(1)
+    result["mfma_loop_peak"] = {"fp16_tflops": round(p16, 1), "fp16_clock_ghz": round(c16, 3),
+                                "fp4_tflops": round(p4, 1), "fp4_clock_ghz": round(c4, 3),
+                                "probe": "pact_mfma_probe: 512 workgroups x 4 waves, 16 independent MFMA chains "
+                                         "per wave, 4000 iterations; clock from s_memtime / s_memrealtime"}
+    result["roofline"]["measured_peak"] = round(p16, 1)
+    result["roofline"]["frac_of_measured_peak"] = round(result["roofline"]["achieved"] / p16, 4)
+    if "mxfp4_variant" in result and "roofline" in result["mxfp4_variant"]:
+        mr = result["mxfp4_variant"]["roofline"]
+        mr["measured_peak"] = round(p4, 1)
+        mr["frac_of_measured_peak"] = round(mr["achieved"] / p4, 4)
+    result["device"] = {"name": torch.cuda.get_device_name(0), "hip": torch.version.hip,
+                        "torch": torch.__version__}
     if args.copy_calibration:
         x = torch.empty(1 << 29, dtype=torch.bfloat16, device="cuda")   # 1 GiB
         y = torch.empty_like(x)

@@ -124,6 +124,28 @@ def selftest_arith(device="cuda") -> list:
     return [int(v) for v in counts.cpu().tolist()]
 
 
+def mfma_probe(kind: int, iters: int = 4000, device="cuda"):
+    """Measured MFMA-loop peak (pact_mfma_probe): kind 0 FP16 32x32x16, kind 1
+    scaled FP4 32x32x64.  Returns (TFLOP/s from events around one launch on the
+    current stream, mean shader clock in GHz over the workgroups)."""
+    groups = 512
+    sink = torch.empty((groups * 256,), dtype=torch.float32, device=device)
+    clocks = torch.zeros((2 * groups,), dtype=torch.int64, device=device)
+    args = lambda: (kind, iters, sink.data_ptr(), sink.numel(), clocks.data_ptr(), clocks.numel(), _stream())
+    _lib.call("pact_mfma_probe", *args())                  # warm-up
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    _lib.call("pact_mfma_probe", *args())
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1)
+    flops = groups * 4 * iters * 16 * (32768 if kind == 0 else 131072)
+    c = clocks.view(groups, 2).cpu().double()
+    ghz = float((c[:, 0] / (c[:, 1] / 100e6)).mean() / 1e9)
+    return flops / (ms * 1e-3) / 1e12, ghz
+
+
 def weight_layouts(w: torch.Tensor):
     """Cached forward and backward layouts (Q(W), Q(W^T)) of a frozen BF16 weight W [N x K]."""
     return quantize(w), quantize(w, transpose=True)

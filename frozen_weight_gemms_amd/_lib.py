@@ -49,6 +49,7 @@ SIGNATURES = {
                                      c_int, c_vp, c_vp, c_i64, c_vp], c_int),
     "pact_nvfp4_row_exp_max": ([c_vp, c_vp, c_vp, c_i64, c_i64, c_vp, c_vp], c_int),
     "pact_selftest_arith": ([c_vp, c_vp], c_int),
+    "pact_mfma_probe": ([c_int, c_int, c_vp, c_i64, c_vp, c_i64, c_vp], c_int),
     "nvfp4_gemm_dgrad_multi": ([c_int] + [c_vp] * 7 + [c_i64, c_i64, c_vp, c_i64, c_int] + [c_vp] * 3 + [c_vp],
                                c_int),
     "silu_mul_bwd_quant": ([c_vp] * 7 + [c_i64, c_i64] + [c_vp] * 9, c_int),

@@ -19,7 +19,8 @@ CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(os.path.dirname(HERE), "include")
 BUILD = os.path.join(os.path.dirname(HERE), "_build")
 LIB = os.path.join(HERE, "libpact_nvfp4.so")
-SOURCES = ["abi.hip", "quantize.hip", "gemm.hip", "gemm_fwdlayout.hip", "lora.hip", "backward.hip", "mxfp4.hip"]
+SOURCES = ["abi.hip", "quantize.hip", "gemm.hip", "gemm_fwdlayout.hip", "lora.hip", "backward.hip", "mxfp4.hip",
+           "probe.hip"]
 ARCH = "gfx950"
 
 

@@ -69,7 +69,7 @@ extern "C" {
 
 const char* pact_last_error(void) { return g_err; }
 
-int pact_abi_version(void) { return 8; }
+int pact_abi_version(void) { return 9; }
 
 int pact_nvfp4_sizes(int64_t rows, int64_t cols, size_t* codes_bytes, size_t* scales_bytes, size_t* rscale_bytes) {
   REQUIRE(rows >= 0 && cols >= 0, PACT_EINVAL, "negative size (rows=%lld, cols=%lld)", (long long)rows,
@@ -390,6 +390,18 @@ int rmsnorm_bwd(const uint8_t* y_codes, const uint8_t* y_scales, const float* y_
 int pact_selftest_arith(unsigned long long* counts, void* stream) {
   REQUIRE(counts != nullptr, PACT_EINVAL, "NULL counts");
   return hip_status(pact::launch_selftest_arith(counts, as_stream(stream)), "selftest launch");
+}
+
+int pact_mfma_probe(int kind, int iters, float* sink, int64_t sink_len, unsigned long long* clocks,
+                    int64_t clocks_len, void* stream) {
+  REQUIRE(kind == 0 || kind == 1, PACT_EINVAL, "kind must be 0 (FP16) or 1 (scaled FP4), got %d", kind);
+  REQUIRE(iters >= 1 && iters <= (1 << 20), PACT_EINVAL, "iters=%d outside 1 .. 2^20", iters);
+  REQUIRE(sink != nullptr && clocks != nullptr, PACT_EINVAL, "NULL sink or clocks");
+  REQUIRE(sink_len >= (int64_t)pact::kMfmaProbeGroups * 256, PACT_ESHAPE, "sink holds %lld floats, needs %d",
+          (long long)sink_len, pact::kMfmaProbeGroups * 256);
+  REQUIRE(clocks_len >= (int64_t)pact::kMfmaProbeGroups * 2, PACT_ESHAPE, "clocks holds %lld values, needs %d",
+          (long long)clocks_len, pact::kMfmaProbeGroups * 2);
+  return hip_status(pact::launch_mfma_probe(kind, iters, sink, clocks, as_stream(stream)), "mfma probe launch");
 }
 
 int pact_nvfp4_row_exp_max(const uint8_t* codes, const uint8_t* scales, const float* rscale, int64_t rows,

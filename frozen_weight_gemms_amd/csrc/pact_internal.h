@@ -19,6 +19,8 @@ hipError_t launch_quantize_ex(const uint16_t* x, int64_t rows, int64_t cols, int
                               float* rscale, hipStream_t s);
 // *amax = max |x| over x [rows x cols] (row stride ldx)
 hipError_t launch_selftest_arith(unsigned long long* counts, hipStream_t s);
+constexpr int kMfmaProbeGroups = 512;      // workgroups of the MFMA-rate probe
+hipError_t launch_mfma_probe(int kind, int iters, float* sink, unsigned long long* clocks, hipStream_t s);
 hipError_t launch_tensor_absmax(const uint16_t* x, int64_t rows, int64_t cols, int64_t ldx, float* amax,
                                 hipStream_t s);
 

@@ -80,6 +80,25 @@ int pact_abi_version(void);
  */
 int pact_selftest_arith(unsigned long long *counts, void *stream);
 
+/*
+ * pact_mfma_probe -- measured MFMA-loop peak (a diagnostic beside the
+ * published dense peaks; no part of the method).  Launches 512 workgroups of
+ * 256 threads; every wave runs `iters` (1 .. 2^20) iterations of 16
+ * independent accumulation chains of
+ *   kind 0: v_mfma_f32_32x32x16_f16           (32768 FLOP each), or
+ *   kind 1: v_mfma_scale_f32_32x32x64_f8f6f4 with FP4 operands and unit
+ *           scales (131072 FLOP each),
+ * so one launch performs 512 * 4 * iters * 16 MFMAs.  sink: device float
+ * array of at least 512 * 256 (written, to keep the work); clocks: device
+ * array of at least 2 * 512 unsigned 64-bit values, set per workgroup to the
+ * shader-clock cycles (s_memtime) and the 100 MHz constant-clock ticks
+ * (s_memrealtime) between its start and end.  The caller times the launch
+ * (e.g. with events on `stream`).  Errors: PACT_EINVAL for a bad kind, iters or
+ * NULL pointer, PACT_ESHAPE for short buffers.
+ */
+int pact_mfma_probe(int kind, int iters, float *sink, int64_t sink_len, unsigned long long *clocks,
+                    int64_t clocks_len, void *stream);
+
 /* Host-only size query: bytes of the three buffers of an NVFP4 [rows x cols]. */
 int pact_nvfp4_sizes(int64_t rows, int64_t cols, size_t *codes_bytes, size_t *scales_bytes,
                      size_t *rscale_bytes);

@@ -25,7 +25,7 @@ def lib():
 
 def test_header_symbols_exported(lib):
     names = _lib.header_functions()
-    assert len(names) == 25, names
+    assert len(names) == 26, names
     assert set(names) == set(_lib.SIGNATURES), set(names) ^ set(_lib.SIGNATURES)
     for n in names:
         assert hasattr(lib, n), n
@@ -57,7 +57,7 @@ def test_gemm_tile_query(lib):
 
 
 def test_abi_version(lib):
-    assert lib.pact_abi_version() == 8
+    assert lib.pact_abi_version() == 9
 
 
 def test_sizes(lib):
@@ -193,3 +193,13 @@ def test_dgrad_multi_validation(lib):
     assert st == -5                                      # 272 is not a multiple of 256
     assert b"multiple of 256" in lib.pact_last_error()
 
+
+
+def test_mfma_probe_validation(lib):
+    """Argument checks of pact_mfma_probe run before any device call."""
+    A = ALIGNED
+    assert lib.pact_mfma_probe(2, 10, A, 512 * 256, A, 1024, None) == -1        # kind
+    assert lib.pact_mfma_probe(0, 0, A, 512 * 256, A, 1024, None) == -1         # iters
+    assert lib.pact_mfma_probe(0, 10, None, 512 * 256, A, 1024, None) == -1     # NULL sink
+    assert lib.pact_mfma_probe(1, 10, A, 512 * 256 - 1, A, 1024, None) == -2    # short sink
+    assert lib.pact_mfma_probe(1, 10, A, 512 * 256, A, 1023, None) == -2        # short clocks

@@ -16,3 +16,14 @@ def test_arith_shortcuts_exhaustive():
     counts = fw.selftest_arith()
     names = ["reciprocal", "division by 6", "sigmoid", "bf16 conversion"]
     assert counts == [0, 0, 0, 0], dict(zip(names, counts))
+
+
+def test_mfma_probe_rates():
+    """The MFMA-loop probe runs both instruction kinds and reports a rate and a
+    clock inside physical limits (it is a measurement aid for the GEMM
+    rooflines, so only plausibility is checked)."""
+    import frozen_weight_gemms_amd as fw
+    for kind, peak in ((0, 2500.0), (1, 10100.0)):
+        tflops, ghz = fw.mfma_probe(kind, iters=500)
+        assert 0.1 * peak < tflops < 1.05 * peak, (kind, tflops)
+        assert 0.5 < ghz < 3.0, (kind, ghz)
