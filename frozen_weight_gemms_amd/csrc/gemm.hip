@@ -660,7 +660,6 @@ __global__ __launch_bounds__(256, 1) void k_gemm_nvfp4_fast(GemmArgs p, int tile
   }
   const int nk0 = SEG ? (int)(sg.s[0].K / KT2) : nk;   // stages of the first (or only) segment
   issue_stage(0, 0);
-  if (nk0 > 1) issue_stage(1, 1);
 
   // The LoRA term is formed while those loads are in flight: acc starts as
   // (lora_scale / (rA rB)) * T U, so the epilogue's row-scale multiply turns
@@ -672,7 +671,8 @@ __global__ __launch_bounds__(256, 1) void k_gemm_nvfp4_fast(GemmArgs p, int tile
   // BF16 values hi + mid + lo = x exactly (each residual is exact in FP32 and
   // the last has at most 8 significant bits), and the term runs three MFMA
   // passes, one per piece.  (The compiler's wait for the T/U loads also covers
-  // the stages issued above.)
+  // stage 0's loads issued above; stage 1's are issued after the term, so the
+  // prologue never waits for them: they are needed from step 12 of stage 0.)
 #pragma unroll
   for (int i = 0; i < WTM; ++i)
 #pragma unroll
@@ -724,43 +724,69 @@ __global__ __launch_bounds__(256, 1) void k_gemm_nvfp4_fast(GemmArgs p, int tile
     const bool t_vec = (r & 15) == 0;                          // T rows: 16-byte aligned runs of 8 ranks
     const bool u_vec = t_vec && p.u_stride_j == 1;             // U(j, n) = B[n][j]: same for B rows
     for (int64_t k0 = 0; k0 < r; k0 += 16) {
+      // Fragments of T (rows) and U (columns).  Where a fragment is not one
+      // aligned 16-byte run, its 8 elements are gathered with clamped indices
+      // and selected afterwards (no branches), and every fragment's loads are
+      // issued before any is used, so they are in flight together.
       uint4 tv[WTM];
       bf16x8_t uf[WTN];
+      if (t_vec) {
 #pragma unroll
-      for (int i = 0; i < WTM; ++i) {
-        int64_t m = m0 + wm * (BM / 2) + i * 32 + li;
-        m = m < M ? m : M - 1;
-        uint4& v = tv[i];
-        if (t_vec) {
-          v = *reinterpret_cast<const uint4*>(lt + m * r + k0 + 8 * h);
-        } else {
-          uint32_t e[8];
+        for (int i = 0; i < WTM; ++i) {
+          int64_t m = m0 + wm * (BM / 2) + i * 32 + li;
+          m = m < M ? m : M - 1;
+          tv[i] = *reinterpret_cast<const uint4*>(lt + m * r + k0 + 8 * h);
+        }
+      } else {
+        uint32_t e[WTM][8];
+#pragma unroll
+        for (int i = 0; i < WTM; ++i) {
+          int64_t m = m0 + wm * (BM / 2) + i * 32 + li;
+          m = m < M ? m : M - 1;
 #pragma unroll
           for (int t = 0; t < 8; ++t) {
             const int64_t j = k0 + 8 * h + t;
-            e[t] = j < r ? lt[m * r + j] : 0u;
+            e[i][t] = lt[m * r + (j < r ? j : r - 1)];
           }
-          v = make_uint4(e[0] | (e[1] << 16), e[2] | (e[3] << 16), e[4] | (e[5] << 16), e[6] | (e[7] << 16));
+        }
+#pragma unroll
+        for (int i = 0; i < WTM; ++i) {
+          uint32_t w[8];
+#pragma unroll
+          for (int t = 0; t < 8; ++t) w[t] = k0 + 8 * h + t < r ? e[i][t] : 0u;
+          tv[i] = make_uint4(w[0] | (w[1] << 16), w[2] | (w[3] << 16), w[4] | (w[5] << 16), w[6] | (w[7] << 16));
         }
       }
+      uint4 uv[WTN];
+      if (u_vec) {
 #pragma unroll
-      for (int i = 0; i < WTN; ++i) {
-        int64_t n = n0 + wn * (BN / 2) + i * 32 + li;
-        n = n < N ? n : N - 1;
-        uint4 v;
-        if (u_vec) {
-          v = *reinterpret_cast<const uint4*>(lu + n * p.u_stride_n + k0 + 8 * h);
-        } else {
-          uint32_t e[8];
+        for (int i = 0; i < WTN; ++i) {
+          int64_t n = n0 + wn * (BN / 2) + i * 32 + li;
+          n = n < N ? n : N - 1;
+          uv[i] = *reinterpret_cast<const uint4*>(lu + n * p.u_stride_n + k0 + 8 * h);
+        }
+      } else {
+        uint32_t e[WTN][8];
+#pragma unroll
+        for (int i = 0; i < WTN; ++i) {
+          int64_t n = n0 + wn * (BN / 2) + i * 32 + li;
+          n = n < N ? n : N - 1;
 #pragma unroll
           for (int t = 0; t < 8; ++t) {
             const int64_t j = k0 + 8 * h + t;
-            e[t] = j < r ? lu[j * p.u_stride_j + n * p.u_stride_n] : 0u;
+            e[i][t] = lu[(j < r ? j : r - 1) * p.u_stride_j + n * p.u_stride_n];
           }
-          v = make_uint4(e[0] | (e[1] << 16), e[2] | (e[3] << 16), e[4] | (e[5] << 16), e[6] | (e[7] << 16));
         }
-        uf[i] = scaled(v, fb[i], 0);
+#pragma unroll
+        for (int i = 0; i < WTN; ++i) {
+          uint32_t w[8];
+#pragma unroll
+          for (int t = 0; t < 8; ++t) w[t] = k0 + 8 * h + t < r ? e[i][t] : 0u;
+          uv[i] = make_uint4(w[0] | (w[1] << 16), w[2] | (w[3] << 16), w[4] | (w[5] << 16), w[6] | (w[7] << 16));
+        }
       }
+#pragma unroll
+      for (int i = 0; i < WTN; ++i) uf[i] = scaled(uv[i], fb[i], 0);
       for (int piece = 0; piece < npieces; ++piece) {
         bf16x8_t tf[WTM];
 #pragma unroll
@@ -785,6 +811,7 @@ __global__ __launch_bounds__(256, 1) void k_gemm_nvfp4_fast(GemmArgs p, int tile
     lora_factors();
     lora_term(p.lora_t, p.lora_u, p.lora_r);
   }
+  if (nk0 > 1) issue_stage(1, 1);
   if constexpr (!SEG) {
     // stage 0 (and the row scales) complete and visible
     if (nk > 1) PACT_WAIT_VMCNT(C::LOADS);
