@@ -76,7 +76,8 @@ def parse():
                     help="distinct decoder-layer instances a step runs through (their weights and buffers "
                          "together exceed the 256 MB last-level cache, so every operand streams from HBM)")
     ap.add_argument("--no-mxfp4", action="store_true", help="skip the MXFP4-variant GEMM leg")
-    ap.add_argument("--no-recipes", action="store_true", help="skip the recipe-variant leg")
+    ap.add_argument("--no-recipes", action="store_true",
+                    help="skip the recipe, single-layout, quantizer-bandwidth and LoRA-term legs")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a 1 GiB read + 1 GiB write elementwise kernel (counter calibration)")
     return ap.parse_args()
