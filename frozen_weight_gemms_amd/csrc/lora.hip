@@ -53,6 +53,17 @@ __device__ __forceinline__ uint4 deq8_bf16(uint32_t w, float m) {
 
 __device__ __forceinline__ float e4m3_f32(uint32_t byte) { return __builtin_amdgcn_cvt_f32_fp8((int)byte, 0); }
 
+// *p where ok, else zero, without a branch: the load always reads a valid
+// address (p, or `safe` where !ok) and the value is selected afterwards.  A
+// conditional load compiles to a branch around it, and the compiler then waits
+// for each such load before the next one: the loads of a step would be
+// serialized instead of in flight together.
+template <typename T>
+__device__ __forceinline__ T load_or_zero(const T* p, const T* safe, bool ok) {
+  const T v = *(ok ? p : safe);
+  return ok ? v : T{};
+}
+
 // ---------------------------------------------------------------------------
 // Row kernel.  Block (tile, part) with 16 token rows p0 .. p0 + 15:
 //   part 0:  T[p][j]  = bf16(xr[p] * sum_k (e*s)[p][k] * A[j][k])     X_q [P x K], A [r x K]
@@ -91,14 +102,15 @@ typedef short short4_t __attribute__((ext_vector_type(4)));
 // 16-byte loads when rows are 16-byte aligned (r % 8 == 0).
 __device__ __forceinline__ uint4 load_b8(const uint16_t* __restrict__ B, int64_t n, int64_t col, int64_t N,
                                          int64_t r, bool ok) {
-  if (!ok || n >= N || col >= r) return make_uint4(0, 0, 0, 0);
+  const bool in = ok && n < N && col < r;
   const uint16_t* p = B + n * r + col;
-  if ((r & 7) == 0) return *reinterpret_cast<const uint4*>(p);
+  if ((r & 7) == 0)
+    return load_or_zero(reinterpret_cast<const uint4*>(p), reinterpret_cast<const uint4*>(B), in);
   uint32_t w[4];
 #pragma unroll
   for (int k = 0; k < 4; ++k) {
-    const uint32_t lo = col + 2 * k < r ? (uint32_t)p[2 * k] : 0u;
-    const uint32_t hi = col + 2 * k + 1 < r ? (uint32_t)p[2 * k + 1] : 0u;
+    const uint32_t lo = load_or_zero(p + 2 * k, B, in && col + 2 * k < r);
+    const uint32_t hi = load_or_zero(p + 2 * k + 1, B, in && col + 2 * k + 1 < r);
     w[k] = lo | (hi << 16);
   }
   return make_uint4(w[0], w[1], w[2], w[3]);
@@ -127,19 +139,21 @@ __device__ __forceinline__ void row_reduce(const uint8_t* __restrict__ xc, const
         const bool rin = cin && row < P;
         const bool full = rin && k0 + 32 <= R, half = rin && k0 + 16 <= R;
         const uint8_t* cp = xc + row * (R >> 1) + (k0 >> 1);
-        const uint2 w01 = half ? *reinterpret_cast<const uint2*>(cp) : make_uint2(0, 0);
-        const uint2 w23 = full ? *reinterpret_cast<const uint2*>(cp + 8) : make_uint2(0, 0);
+        const uint2* c2 = reinterpret_cast<const uint2*>(xc);
+        const uint2 w01 = load_or_zero(reinterpret_cast<const uint2*>(cp), c2, half);
+        const uint2 w23 = load_or_zero(reinterpret_cast<const uint2*>(cp + 8), c2, full);
         lv[q][0] = make_uint4(w01.x, w01.y, w23.x, w23.y);
         const uint8_t* sp = xs + row * (R >> 4) + (k0 >> 4);
-        lsc[q][0] = half ? (uint32_t)sp[0] : 0u;
-        lsc[q][1] = full ? (uint32_t)sp[1] : 0u;
+        lsc[q][0] = load_or_zero(sp, xs, half);
+        lsc[q][1] = load_or_zero(sp + 1, xs, full);
       } else {
 #pragma unroll
         for (int v = 0; v < 4; ++v) {
           const int64_t row = p0 + 4 * v + (lane >> 4);
           const int64_t k = c * 128 + 8 * (lane & 15);
           const bool ok = cin && row < P && k + 8 <= R;
-          lv[q][v] = ok ? *reinterpret_cast<const uint4*>(lb + row * R + k) : make_uint4(0, 0, 0, 0);
+          lv[q][v] = load_or_zero(reinterpret_cast<const uint4*>(lb + row * R + k),
+                                  reinterpret_cast<const uint4*>(lb), ok);
         }
       }
 #pragma unroll
@@ -150,7 +164,8 @@ __device__ __forceinline__ void row_reduce(const uint8_t* __restrict__ xc, const
           for (int u = 0; u < 4; ++u) {
             const int64_t k = c * 128 + 32 * u + 8 * g;
             const bool ok = cin && j < r && k + 8 <= R;
-            sv[q][t][u] = ok ? *reinterpret_cast<const uint4*>(S + j * R + k) : make_uint4(0, 0, 0, 0);
+            sv[q][t][u] = load_or_zero(reinterpret_cast<const uint4*>(S + j * R + k),
+                                       reinterpret_cast<const uint4*>(S), ok);
           }
         } else {
 #pragma unroll
@@ -330,41 +345,54 @@ __device__ __forceinline__ void col_load(ColStep<NT, CPL>& st, const uint8_t* __
   const int i = lane & 15, g = lane >> 4;
   // row scales of the step's 32 rows, one per lane (dA strips only)
   float xr_step = 0.0f;
-  if constexpr (!is_b)
-    if (m0 + (lane & 31) < Re) xr_step = xr[m0 + (lane & 31)];
+  if constexpr (!is_b) xr_step = load_or_zero(xr + m0 + (lane & 31), xr, m0 + (lane & 31) < Re);
+  if constexpr (is_b) {
 #pragma unroll
-  for (int e = 0; e < 8; ++e) {
-    const int64_t m = m0 + 8 * g + e;
-    const bool ok = qok && m < Re;
-    if constexpr (is_b) {
+    for (int e = 0; e < 8; ++e) {
+      const int64_t m = m0 + 8 * g + e;
+      const bool ok = qok && m < Re;
       const uint16_t* src = dy + m * N + qc;
       if constexpr (CPL == 8) {
-        const uint4 v = ok ? *reinterpret_cast<const uint4*>(src) : make_uint4(0, 0, 0, 0);
+        const uint4 v = load_or_zero(reinterpret_cast<const uint4*>(src), reinterpret_cast<const uint4*>(dy), ok);
         st.rows[e][0] = v.x; st.rows[e][1] = v.y; st.rows[e][2] = v.z; st.rows[e][3] = v.w;
       } else if constexpr (CPL == 4) {
-        const uint2 v = ok ? *reinterpret_cast<const uint2*>(src) : make_uint2(0, 0);
+        const uint2 v = load_or_zero(reinterpret_cast<const uint2*>(src), reinterpret_cast<const uint2*>(dy), ok);
         st.rows[e][0] = v.x; st.rows[e][1] = v.y;
       } else {
-        st.rows[e][0] = ok ? *reinterpret_cast<const uint32_t*>(src) : 0u;
+        st.rows[e][0] = load_or_zero(reinterpret_cast<const uint32_t*>(src), reinterpret_cast<const uint32_t*>(dy), ok);
       }
-    } else {
-      // X~ = e * s * r: CPL codes of row m (within one block), dequantized to BF16;
-      // the row scale of row m0 + 8g + e comes from lane 8g + e
+    }
+  } else {
+    // X~ = e * s * r: CPL codes of row m (within one block), dequantized to
+    // BF16; the row scale of row m0 + 8g + e comes from lane 8g + e.  All 8
+    // rows' codes and scale bytes are loaded before any is used.
+    uint32_t cw[8], sc[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const int64_t m = m0 + 8 * g + e;
+      const bool ok = qok && m < Re;
       const uint8_t* cp = xc + m * (K >> 1) + (qc >> 1);
+      sc[e] = load_or_zero(xs + m * (K >> 4) + (qc >> 4), xs, ok);
+      if constexpr (CPL == 8) cw[e] = load_or_zero(reinterpret_cast<const uint32_t*>(cp), reinterpret_cast<const uint32_t*>(xc), ok);
+      else if constexpr (CPL == 4) cw[e] = load_or_zero(reinterpret_cast<const uint16_t*>(cp), reinterpret_cast<const uint16_t*>(xc), ok);
+      else cw[e] = load_or_zero(cp, xc, ok);
+    }
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const int64_t m = m0 + 8 * g + e;
+      const bool ok = qok && m < Re;
       const float rr = __shfl(xr_step, 8 * g + e, 64);
-      const float mlt = ok ? e4m3_f32(xs[m * (K >> 4) + (qc >> 4)]) * rr : 0.0f;
+      const float mlt = ok ? e4m3_f32(sc[e]) * rr : 0.0f;
+      const uint32_t w = cw[e];
       if constexpr (CPL == 8) {
-        const uint32_t w = ok ? *reinterpret_cast<const uint32_t*>(cp) : 0u;
         const uint4 v = deq8_bf16(w, mlt);
         st.rows[e][0] = v.x; st.rows[e][1] = v.y; st.rows[e][2] = v.z; st.rows[e][3] = v.w;
       } else if constexpr (CPL == 4) {
-        const uint32_t w = ok ? (uint32_t)*reinterpret_cast<const uint16_t*>(cp) : 0u;
         const float2_t a = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 0);
         const float2_t b = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 1);
         st.rows[e][0] = pack2(a.x * mlt, a.y * mlt);
         st.rows[e][1] = pack2(b.x * mlt, b.y * mlt);
       } else {
-        const uint32_t w = ok ? (uint32_t)cp[0] : 0u;
         const float2_t a = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 0);
         st.rows[e][0] = pack2(a.x * mlt, a.y * mlt);
       }
@@ -374,7 +402,8 @@ __device__ __forceinline__ void col_load(ColStep<NT, CPL>& st, const uint8_t* __
   for (int t = 0; t < NT; ++t) {
     const int64_t j = 16 * t + i;
     // Wt rows are zero-padded up to ldt (M rounded up to 32), and m0 + 32 <= ldt
-    st.wv[t] = j < r ? *reinterpret_cast<const uint4*>(Wt + j * ldt + m0 + 8 * g) : make_uint4(0, 0, 0, 0);
+    st.wv[t] = load_or_zero(reinterpret_cast<const uint4*>(Wt + j * ldt + m0 + 8 * g), reinterpret_cast<const uint4*>(Wt),
+                            j < r);
   }
 }
 
@@ -488,8 +517,8 @@ __global__ __launch_bounds__(256) void k_lora_reduce(const float* __restrict__ p
       float4 pv[8];
 #pragma unroll
       for (int u = 0; u < 8; ++u)
-        pv[u] = sb + u < nsplit ? *reinterpret_cast<const float4*>(base + (int64_t)(sb + u) * stride)
-                                : make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+        pv[u] = load_or_zero(reinterpret_cast<const float4*>(base + (int64_t)(sb + u) * stride),
+                             reinterpret_cast<const float4*>(base), sb + u < nsplit);
 #pragma unroll
       for (int u = 0; u < 8; ++u)
         if (sb + u < nsplit) {
