@@ -89,15 +89,27 @@ __global__ __launch_bounds__(256) void k_silu_mul_bwd_quant(
   const float rg = gr[row], ru = ur[row];
   uint4 oa[NCH], ob[NCH];
   float la = 0.0f, lb = 0.0f;
+  // every chunk's inputs are loaded (branch-free) before any is used
+  uint32_t wg[NCH], wu[NCH], sg[NCH], su[NCH];
+  uint4 vdh[NCH];
+#pragma unroll
+  for (int i = 0; i < NCH; ++i) {
+    const int c = threadIdx.x + 256 * i;
+    const bool ok = c < nchunk;
+    const int64_t q = row * nchunk + c;
+    wg[i] = load_or_zero(reinterpret_cast<const uint32_t*>(gc) + q, reinterpret_cast<const uint32_t*>(gc), ok);
+    wu[i] = load_or_zero(reinterpret_cast<const uint32_t*>(uc) + q, reinterpret_cast<const uint32_t*>(uc), ok);
+    sg[i] = load_or_zero(gs + row * (I >> 4) + (c >> 1), gs, ok);
+    su[i] = load_or_zero(us + row * (I >> 4) + (c >> 1), us, ok);
+    vdh[i] = load_or_zero(reinterpret_cast<const uint4*>(dh + row * I + 8 * c), reinterpret_cast<const uint4*>(dh), ok);
+  }
 #pragma unroll
   for (int i = 0; i < NCH; ++i) {
     const int c = threadIdx.x + 256 * i;
     if (c < nchunk) {
-      const int64_t q = row * nchunk + c;
-      const float ma = e4m3_decode(gs[row * (I >> 4) + (c >> 1)]) * rg;
-      const float mb = e4m3_decode(us[row * (I >> 4) + (c >> 1)]) * ru;
-      silu_bwd_chunk(reinterpret_cast<const uint32_t*>(gc)[q], ma, reinterpret_cast<const uint32_t*>(uc)[q], mb,
-                     load16(dh + row * I + 8 * c), oa[i], ob[i]);
+      const float ma = e4m3_decode(sg[i]) * rg;
+      const float mb = e4m3_decode(su[i]) * ru;
+      silu_bwd_chunk(wg[i], ma, wu[i], mb, vdh[i], oa[i], ob[i]);
       *reinterpret_cast<uint4*>(dgate + row * I + 8 * c) = oa[i];
       *reinterpret_cast<uint4*>(dup + row * I + 8 * c) = ob[i];
       la = fmaxf(la, absmax_bf16x8(oa[i]));

@@ -53,16 +53,6 @@ __device__ __forceinline__ uint4 deq8_bf16(uint32_t w, float m) {
 
 __device__ __forceinline__ float e4m3_f32(uint32_t byte) { return __builtin_amdgcn_cvt_f32_fp8((int)byte, 0); }
 
-// *p where ok, else zero, without a branch: the load always reads a valid
-// address (p, or `safe` where !ok) and the value is selected afterwards.  A
-// conditional load compiles to a branch around it, and the compiler then waits
-// for each such load before the next one: the loads of a step would be
-// serialized instead of in flight together.
-template <typename T>
-__device__ __forceinline__ T load_or_zero(const T* p, const T* safe, bool ok) {
-  const T v = *(ok ? p : safe);
-  return ok ? v : T{};
-}
 
 // ---------------------------------------------------------------------------
 // Row kernel.  Block (tile, part) with 16 token rows p0 .. p0 + 15:

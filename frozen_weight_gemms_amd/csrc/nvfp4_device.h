@@ -26,6 +26,17 @@ namespace pact {
 
 constexpr int kBlock = 16;
 
+// *p where ok, else zero, without a branch: the load always reads a valid
+// address (p, or `safe` where !ok) and the value is selected afterwards.  A
+// conditional load compiles to a branch around it, and the compiler then waits
+// for each such load before the next one: the loads of a step would be
+// serialized instead of in flight together.
+template <typename T>
+__device__ __forceinline__ T load_or_zero(const T* p, const T* safe, bool ok) {
+  const T v = *(ok ? p : safe);
+  return ok ? v : T{};
+}
+
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
 

@@ -358,12 +358,16 @@ __global__ __launch_bounds__(kThreads) void k_silu_mul_quant(const uint16_t* __r
   uint4 va[NCH], vb[NCH];
   float h[NCH][8];
   float ma = 0.0f, mb = 0.0f, mh = 0.0f;
+  // every chunk's loads are issued (branch-free) before any is used
 #pragma unroll
   for (int i = 0; i < NCH; ++i) {
     const int c = threadIdx.x + kThreads * i;
     const bool ok = c < nchunk;
-    va[i] = ok ? load16(gate + row * ld + 8 * c) : make_uint4(0, 0, 0, 0);
-    vb[i] = ok ? load16(up + row * ld + 8 * c) : make_uint4(0, 0, 0, 0);
+    va[i] = load_or_zero(reinterpret_cast<const uint4*>(gate + row * ld + 8 * c), reinterpret_cast<const uint4*>(gate), ok);
+    vb[i] = load_or_zero(reinterpret_cast<const uint4*>(up + row * ld + 8 * c), reinterpret_cast<const uint4*>(up), ok);
+  }
+#pragma unroll
+  for (int i = 0; i < NCH; ++i) {
     float a[8], b[8];
     unpack_bf16x8(va[i], a);
     unpack_bf16x8(vb[i], b);
