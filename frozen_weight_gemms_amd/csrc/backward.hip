@@ -163,16 +163,19 @@ __global__ __launch_bounds__(256) void k_rmsnorm_bwd(const uint8_t* __restrict__
   uint2 cw[NB];                                        // 16 codes
   float sm[NB];                                        // block scale * row scale
   uint4 dv[NB][2];                                     // 16 BF16 dy
+  uint32_t sb[NB];                                     // raw E4M3 block scales
   double sh = 0.0, sl = 0.0;                           // double-double partial of sum dy y^ (each product exact)
 #pragma unroll
   for (int i = 0; i < NB; ++i) {
     const int blk = lane + 64 * part + 64 * WPR * i;
     const bool ok = row_ok && blk < nblk;
     cw[i] = ok ? *reinterpret_cast<const uint2*>(yc + row * (H >> 1) + 8 * blk) : make_uint2(0, 0);
-    sm[i] = ok ? e4m3_decode(ys[row * (H >> 4) + blk]) * rr : 0.0f;
+    sb[i] = load_or_zero(ys + row * (H >> 4) + blk, ys, ok);      // decoded once every load is issued
     dv[i][0] = ok ? load16(dy + row * H + 16 * blk) : make_uint4(0, 0, 0, 0);
     dv[i][1] = ok ? load16(dy + row * H + 16 * blk + 8) : make_uint4(0, 0, 0, 0);
   }
+#pragma unroll
+  for (int i = 0; i < NB; ++i) sm[i] = row_ok && lane + 64 * part + 64 * WPR * i < nblk ? e4m3_decode(sb[i]) * rr : 0.0f;
 #pragma unroll
   for (int i = 0; i < NB; ++i) {
 #pragma unroll
