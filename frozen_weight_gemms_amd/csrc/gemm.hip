@@ -19,14 +19,15 @@
 // contraction runs at the FP16 matrix rate.
 //
 // Tiling.  A workgroup of 4 waves (2 x 2) computes a BM x BN tile, each wave
-// (BM/2) x (BN/2) as WTM x WTN MFMA tiles of 32 x 32.  K advances in stages of
-// 128 (8 NVFP4 blocks): packed codes (64 B per row) and the block scales are
-// staged in LDS (the generic kernel double buffers through registers, the fast
-// one loads three stages ahead straight into LDS).  Within a
-// stage, lane half h of a wave owns K range [64h, 64h+64) of every row it
-// touches, so each fragment is one 32-byte LDS read of codes plus one 16-byte
-// read of scales; MFMA step s takes K = 64h + 8s + t (t = 0..7) from both
-// operands, a consistent permutation of K.
+// (BM/2) x (BN/2) as WTM x WTN MFMA tiles of 32 x 32.  Two kernels:
+//   * the generic one (any K % 16 == 0) advances K in stages of 128 (8 NVFP4
+//     blocks, 64 code bytes per row), double-buffered through registers into
+//     LDS; lane half h owns K range [64h, 64h + 64) of a stage and MFMA step s
+//     takes K = 64h + 8s + t (t = 0..7) from both operands;
+//   * the fast one (K % 256 == 0, below) advances K in stages of 256 loaded
+//     straight into two LDS buffers with LDS-direct buffer loads; lane half h
+//     owns K range [128h, 128h + 128) and step s takes K = 128h + 8s + t.
+// Both take the same consistent permutation of K for the two operands.
 #include <type_traits>
 
 #include "lds_dma.h"
