@@ -42,7 +42,7 @@ projection's GEMMs with and without the fused LoRA term; "mfma_loop_peak" is
 the measured back-to-back MFMA rate (FP16 and scaled FP4) and the clock held
 under it, reported beside the published peaks.
 
-Prints one JSON line.  --gpus must be 1: this build runs on one GPU.
+Prints one JSON line.  --gpus must be 1: the path runs on one GPU.
 """
 
 from __future__ import annotations

@@ -3,8 +3,8 @@
 // frozen weight needs one cached NVFP4 layout instead of two and the forward
 // and input-gradient products use identical effective weights.  (The pages'
 // method keeps cached forward and backward layouts, PACT Appendix Table 7 row
-// "Frozen projections"; this is the alternative the survey of the pages ranks
-// next, reusing W_fwd tiles with a transposed read.)
+// "Frozen projections"; this variant instead reuses the W_fwd tiles through a
+// transposed read, so each weight keeps one layout.)
 //
 // The contraction runs over N, the row axis of W_fwd.  Per stage of 256
 // contraction rows the workgroup stages, for its 128 output columns, the

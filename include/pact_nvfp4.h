@@ -52,7 +52,7 @@ enum {
   PACT_ESHAPE = -2,      /* cols % 16 != 0, ld < cols, rank out of range */
   PACT_EALIGN = -3,      /* pointer not 16-byte aligned */
   PACT_EHIP = -4,        /* a HIP launch failed */
-  PACT_EUNSUPPORTED = -5 /* valid but unsupported by this build */
+  PACT_EUNSUPPORTED = -5 /* valid but unsupported by this library */
 };
 
 /* Message for the last non-OK status returned on this thread ("" if none). */
