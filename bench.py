@@ -25,7 +25,7 @@ The metric is the NVFP4 fwd + dgrad GEMM throughput of the step:
   value = (GEMM FLOPs per step) / (wall time per step)   [TFLOP/s]
 with every other kernel of the step inside the timed region.  Inputs are
 synthetic (seeded, BF16, resident in HBM before timing); weights are random
-N(0, 0.02) quantized once to their cached forward and backward layouts
+N(0, 0.02) quantized once to their two cached NVFP4 layouts (one per direction)
 (offline, untimed).
 
 A second leg times the MXFP4 variant (32-element blocks, E8M0 scales) on the
@@ -248,7 +248,7 @@ class Layer:
     def backward(self, dout, dout_q):
         """Backward of the layer given the gradient of its output (BF16 and its
         NVFP4 copy); returns the gradient of its input, the residual stream
-        (Table 7 row "Residuals": BF16 gradient accumulation)."""
+        (Table 7 row "Residuals": the residual gradients are summed in BF16)."""
         fw = self.fw
         M, H, I = self.M, self.H, self.I
         # MLP block: out = h2 + down(silu(gate(n2)) * up(n2)),  n2 = rmsnorm(h2)

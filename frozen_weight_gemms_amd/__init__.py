@@ -147,12 +147,13 @@ def mfma_probe(kind: int, iters: int = 4000, device="cuda"):
 
 
 def weight_layouts(w: torch.Tensor):
-    """Cached forward and backward layouts (Q(W), Q(W^T)) of a frozen BF16 weight W [N x K]."""
+    """The two cached NVFP4 layouts Q(W) (forward) and Q(W^T) (input gradient) of a frozen BF16 weight W [N x K]."""
     return quantize(w), quantize(w, transpose=True)
 
 
-def rmsnorm_quant(x: torch.Tensor, gain: torch.Tensor, eps: float = 1e-5, out=None):
-    """(Q(y), rstd) with y = (x * rstd) * gain; ``out`` = (NVFP4Tensor, rstd) to reuse buffers."""
+def rmsnorm_quant(x: torch.Tensor, gain: torch.Tensor, eps: float = 1e-5, out=None, exact_sum: bool = False):
+    """(Q(y), rstd) with y = (x * rstd) * gain; ``out`` = (NVFP4Tensor, rstd) to reuse buffers.
+    ``exact_sum``: every row's sum of squares on the double-double path (same results)."""
     _bf16(x, "x"); _bf16(gain, "gain")
     M, H = x.shape
     if out is not None:
@@ -160,8 +161,12 @@ def rmsnorm_quant(x: torch.Tensor, gain: torch.Tensor, eps: float = 1e-5, out=No
     else:
         y = empty_nvfp4(M, H, x.device)
         rstd = torch.empty((M,), dtype=torch.float32, device=x.device)
-    _lib.call("rmsnorm_quant", x.data_ptr(), gain.data_ptr(), float(eps), M, H, x.stride(0), *y.ptrs(),
-              rstd.data_ptr(), _stream())
+    if exact_sum:
+        _lib.call("rmsnorm_quant_ex", x.data_ptr(), gain.data_ptr(), float(eps), M, H, x.stride(0), 1, *y.ptrs(),
+                  rstd.data_ptr(), _stream())
+    else:
+        _lib.call("rmsnorm_quant", x.data_ptr(), gain.data_ptr(), float(eps), M, H, x.stride(0), *y.ptrs(),
+                  rstd.data_ptr(), _stream())
     return y, rstd
 
 
@@ -259,14 +264,17 @@ def gemm_dgrad_multi(segments, out: torch.Tensor | None = None, accumulate: bool
 
 
 class SingleLayoutWeight:
-    """A frozen weight kept only as W_fwd = Q(W) [N x K], plus the largest
-    row-scale exponent over its nonzero rows (device int32), for the
-    single-layout dgrad."""
+    """A frozen weight kept only as W_fwd = Q(W) [N x K], plus the largest and
+    smallest row-scale exponents over its nonzero rows (device int32 [2]), for
+    the single-layout dgrad.  Raises PactError (PACT_EUNSUPPORTED) for a weight
+    whose nonzero rows span more than 2^14 in row scale (the dgrad would not
+    be exact); the set-up synchronizes the current stream."""
 
     def __init__(self, w_fwd: NVFP4Tensor):
         self.w_fwd = w_fwd
-        self.exp_max = torch.empty((1,), dtype=torch.int32, device=w_fwd.codes.device)
-        _lib.call("pact_nvfp4_row_exp_max", *w_fwd.ptrs(), w_fwd.rows, w_fwd.cols, self.exp_max.data_ptr(),
+        self.exp_range = torch.empty((2,), dtype=torch.int32, device=w_fwd.codes.device)
+        self.exp_max = self.exp_range[:1]
+        _lib.call("pact_nvfp4_row_exp_max", *w_fwd.ptrs(), w_fwd.rows, w_fwd.cols, self.exp_range.data_ptr(),
                   _stream())
 
 
@@ -328,6 +336,21 @@ def lora_bwd(xq: NVFP4Tensor, A: torch.Tensor, B: torch.Tensor, dy: torch.Tensor
         workspace = lora_bwd_workspace(M, K, N, r, dev)
     _lib.call("lora_bwd", *xq.ptrs(), M, K, A.data_ptr(), B.data_ptr(), r, float(scale), dy.data_ptr(), N,
               dT.data_ptr(), dA.data_ptr(), dB.data_ptr(), workspace.data_ptr(), workspace.numel(), _stream())
+    return dT, dA, dB
+
+
+def lora_bwd_noalloc(xq: NVFP4Tensor, A: torch.Tensor, B: torch.Tensor, dy: torch.Tensor, scale: float, out):
+    """lora_bwd into caller tensors ``out`` = (dT, dA, dB) with the library's fixed
+    per-device scratch instead of a workspace (allocates nothing)."""
+    _bf16(A, "A"); _bf16(B, "B"); _bf16(dy, "dy")
+    r, K = A.shape
+    N = B.shape[0]
+    M = xq.rows
+    if B.shape != (N, r) or dy.shape != (M, N) or K != xq.cols:
+        raise ValueError("shapes: A [r x K], B [N x r], dy [M x N]")
+    dT, dA, dB = out
+    _lib.call("lora_bwd_noalloc", *xq.ptrs(), M, K, A.data_ptr(), B.data_ptr(), r, float(scale), dy.data_ptr(), N,
+              dT.data_ptr(), dA.data_ptr(), dB.data_ptr(), _stream())
     return dT, dA, dB
 
 

@@ -33,6 +33,7 @@ SIGNATURES = {
     "pact_gemm_multi_tile": ([c_i64, c_i64, ctypes.POINTER(c_int), ctypes.POINTER(c_int)], c_int),
     "nvfp4_quantize": ([c_vp, c_i64, c_i64, c_i64, c_int, c_vp, c_vp, c_vp, c_vp], c_int),
     "rmsnorm_quant": ([c_vp, c_vp, c_float, c_i64, c_i64, c_i64, c_vp, c_vp, c_vp, c_vp, c_vp], c_int),
+    "rmsnorm_quant_ex": ([c_vp, c_vp, c_float, c_i64, c_i64, c_i64, c_int, c_vp, c_vp, c_vp, c_vp, c_vp], c_int),
     "silu_mul_quant": ([c_vp, c_vp, c_i64, c_i64, c_i64] + [c_vp] * 9 + [c_vp], c_int),
     "nvfp4_gemm_fwd": ([c_vp, c_vp, c_vp, c_i64, c_i64, c_vp, c_vp, c_vp, c_i64, c_vp, c_i64,
                         c_vp, c_vp, c_i64, c_float, c_vp], c_int),
@@ -42,6 +43,8 @@ SIGNATURES = {
     "pact_lora_bwd_workspace_size": ([c_i64, c_i64, c_i64, c_i64, c_size_p], c_int),
     "lora_bwd": ([c_vp, c_vp, c_vp, c_i64, c_i64, c_vp, c_vp, c_i64, c_float, c_vp, c_i64,
                   c_vp, c_vp, c_vp, c_vp, ctypes.c_size_t, c_vp], c_int),
+    "lora_bwd_noalloc": ([c_vp, c_vp, c_vp, c_i64, c_i64, c_vp, c_vp, c_i64, c_float, c_vp, c_i64,
+                          c_vp, c_vp, c_vp, c_vp], c_int),
     "silu_mul_bwd": ([c_vp] * 7 + [c_i64, c_i64, c_vp, c_vp, c_vp], c_int),
     "rmsnorm_bwd": ([c_vp] * 6 + [c_i64, c_i64, c_vp, c_vp], c_int),
     "nvfp4_quantize_ex": ([c_vp, c_i64, c_i64, c_i64, c_int, c_int, c_vp, c_vp, c_vp, c_vp, c_vp], c_int),

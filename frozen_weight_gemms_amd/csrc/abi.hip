@@ -69,7 +69,7 @@ extern "C" {
 
 const char* pact_last_error(void) { return g_err; }
 
-int pact_abi_version(void) { return 9; }
+int pact_abi_version(void) { return 10; }
 
 int pact_nvfp4_sizes(int64_t rows, int64_t cols, size_t* codes_bytes, size_t* scales_bytes, size_t* rscale_bytes) {
   REQUIRE(rows >= 0 && cols >= 0, PACT_EINVAL, "negative size (rows=%lld, cols=%lld)", (long long)rows,
@@ -158,8 +158,9 @@ int nvfp4_quantize_ex(const uint16_t* x, int64_t rows, int64_t cols, int64_t ldx
                     "nvfp4_quantize_ex launch");
 }
 
-int rmsnorm_quant(const uint16_t* x, const uint16_t* gain, float eps, int64_t M, int64_t H, int64_t ldx,
-                  uint8_t* y_codes, uint8_t* y_scales, float* y_rscale, float* rstd, void* stream) {
+int rmsnorm_quant_ex(const uint16_t* x, const uint16_t* gain, float eps, int64_t M, int64_t H, int64_t ldx,
+                     int flags, uint8_t* y_codes, uint8_t* y_scales, float* y_rscale, float* rstd, void* stream) {
+  REQUIRE((flags & ~PACT_RMSNORM_EXACT_SUM) == 0, PACT_EINVAL, "unknown flags 0x%x", flags);
   REQUIRE(M >= 0 && H >= 0, PACT_EINVAL, "negative size (M=%lld, H=%lld)", (long long)M, (long long)H);
   REQUIRE(H % 16 == 0, PACT_ESHAPE, "H=%lld is not a multiple of 16", (long long)H);
   REQUIRE(H <= kMaxFusedCols, PACT_EUNSUPPORTED, "H=%lld exceeds %lld", (long long)H, (long long)kMaxFusedCols);
@@ -173,11 +174,15 @@ int rmsnorm_quant(const uint16_t* x, const uint16_t* gain, float eps, int64_t M,
   if (st != PACT_OK) return st;
   REQUIRE(ldx >= H && ldx % 8 == 0, PACT_ESHAPE, "ldx=%lld must be >= H and a multiple of 8", (long long)ldx);
   REQUIRE(M <= 0x7FFFFFFF, PACT_EUNSUPPORTED, "M=%lld exceeds the grid limit", (long long)M);
-  const char* fe = getenv("PACT_RMSNORM_EXACT_SUM");
-  const int force_exact = (fe != nullptr && fe[0] == '1') ? 1 : 0;
+  const int force_exact = (flags & PACT_RMSNORM_EXACT_SUM) ? 1 : 0;
   return hip_status(pact::launch_rmsnorm_quant(x, gain, eps, M, H, ldx, y_codes, y_scales, y_rscale, rstd,
                                                force_exact, as_stream(stream)),
                     "rmsnorm_quant launch");
+}
+
+int rmsnorm_quant(const uint16_t* x, const uint16_t* gain, float eps, int64_t M, int64_t H, int64_t ldx,
+                  uint8_t* y_codes, uint8_t* y_scales, float* y_rscale, float* rstd, void* stream) {
+  return rmsnorm_quant_ex(x, gain, eps, M, H, ldx, 0, y_codes, y_scales, y_rscale, rstd, stream);
 }
 
 int silu_mul_quant(const uint16_t* gate, const uint16_t* up, int64_t M, int64_t I, int64_t ld, uint8_t* h_codes,
@@ -352,6 +357,37 @@ int lora_bwd(const uint8_t* x_codes, const uint8_t* x_scales, const float* x_rsc
                     "lora_bwd launch");
 }
 
+int lora_bwd_noalloc(const uint8_t* x_codes, const uint8_t* x_scales, const float* x_rscale, int64_t M, int64_t K,
+                     const uint16_t* A, const uint16_t* B, int64_t r, float scale, const uint16_t* dy, int64_t N,
+                     uint16_t* dT, uint16_t* dA, uint16_t* dB, void* stream) {
+  REQUIRE(M >= 0 && K >= 0 && N >= 0, PACT_EINVAL, "negative size");
+  REQUIRE(K % 16 == 0 && N % 16 == 0, PACT_ESHAPE, "K=%lld and N=%lld must be multiples of 16", (long long)K,
+          (long long)N);
+  REQUIRE(r >= 1 && r <= kMaxRank, PACT_ESHAPE, "rank %lld outside [1, %lld]", (long long)r, (long long)kMaxRank);
+  if (M > 0) {
+    int st = check_nvfp4(x_codes, x_scales, x_rscale, "x");
+    if (st != PACT_OK) return st;
+    REQUIRE_PTR(dy, "dy");
+    REQUIRE_PTR(dT, "dT");
+  }
+  REQUIRE_PTR(A, "A");
+  REQUIRE_PTR(B, "B");
+  REQUIRE_PTR(dA, "dA");
+  REQUIRE_PTR(dB, "dB");
+  const size_t need = pact::lora_bwd_workspace(M, K, N, r);
+  REQUIRE(need <= pact::kLoraScratchBytes, PACT_EUNSUPPORTED,
+          "lora_bwd_noalloc: M=%lld K=%lld N=%lld r=%lld needs %zu bytes of scratch, more than the fixed %zu "
+          "(use lora_bwd with a workspace)",
+          (long long)M, (long long)K, (long long)N, (long long)r, need, pact::kLoraScratchBytes);
+  REQUIRE((M + 15) / 16 < 0x7FFFFFFF, PACT_EUNSUPPORTED, "M too large");
+  void* ws = nullptr;
+  int st = hip_status(pact::lora_scratch_address(&ws), "lora_bwd_noalloc scratch lookup");
+  if (st != PACT_OK) return st;
+  return hip_status(pact::launch_lora_bwd(x_codes, x_scales, x_rscale, M, K, A, B, r, scale, dy, N, dT, dA, dB, ws,
+                                          as_stream(stream)),
+                    "lora_bwd_noalloc launch");
+}
+
 int silu_mul_bwd(const uint8_t* g_codes, const uint8_t* g_scales, const float* g_rscale, const uint8_t* u_codes,
                  const uint8_t* u_scales, const float* u_rscale, const uint16_t* dh, int64_t M, int64_t I,
                  uint16_t* dgate, uint16_t* dup, void* stream) {
@@ -413,8 +449,21 @@ int pact_nvfp4_row_exp_max(const uint8_t* codes, const uint8_t* scales, const fl
   if (st != PACT_OK) return st;
   REQUIRE(out != nullptr, PACT_EINVAL, "out is NULL");
   REQUIRE((reinterpret_cast<uintptr_t>(out) & 3u) == 0, PACT_EALIGN, "out is not 4-byte aligned");
-  return hip_status(pact::launch_row_exp_max(rscale, scales, rows, cols, out, as_stream(stream)),
-                    "row exponent max launch");
+  hipStream_t s = as_stream(stream);
+  st = hip_status(pact::launch_row_exp_max(rscale, scales, rows, cols, out, s), "row exponent range launch");
+  if (st != PACT_OK) return st;
+  // a once-per-weight set-up call: wait for the two exponents and check the
+  // window in which the single-layout dgrad's FP16 operand is exact
+  int host[2] = {0, 0};
+  st = hip_status(hipMemcpyAsync(host, out, sizeof(host), hipMemcpyDeviceToHost, s), "row exponent read-back");
+  if (st != PACT_OK) return st;
+  st = hip_status(hipStreamSynchronize(s), "row exponent read-back");
+  if (st != PACT_OK) return st;
+  REQUIRE(host[0] - host[1] <= 14, PACT_EUNSUPPORTED,
+          "nonzero rows span row exponents %d .. %d (more than 14 apart): the single-layout dgrad would not be "
+          "exact for this weight",
+          host[1], host[0]);
+  return ok();
 }
 
 int nvfp4_gemm_dgrad_fwd_layout(const uint8_t* dy_codes, const uint8_t* dy_scales, const float* dy_rscale, int64_t M,

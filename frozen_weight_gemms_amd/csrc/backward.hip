@@ -1,7 +1,8 @@
 // SiLU-multiply and RMSNorm backward from the saved NVFP4 state (PACT,
-// Appendix Table 7: "FP32 reconstruction and derivatives, BF16 gradients" for
-// SiLU-multiply; "FP32 reconstruction and reduction, BF16 gradient" for
-// RMSNorm; residuals: "BF16 gradient accumulation").  HBM-bound elementwise /
+// Appendix Table 7, rows "SiLU-multiply", "RMSNorm" and "Residuals", backward
+// column: both operators rebuild their inputs from the NVFP4 copies and work
+// in FP32, RMSNorm adding a row reduction; gradients leave as BF16, and the
+// residual gradients are summed in BF16).  HBM-bound elementwise /
 // row-reduction kernels.
 //
 //   silu_mul_bwd: a^ = deq(gate_q), b^ = deq(up_q), sigma = 1/(1+E(-a^))

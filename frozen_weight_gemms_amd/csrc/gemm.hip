@@ -1,7 +1,7 @@
 // NVFP4 x NVFP4 -> BF16 GEMM for the frozen projections: C = A B^T with both
 // operands row-blocked NVFP4 (PACT, Appendix Table 7 row "Frozen projections":
-// NVFP4 GEMMs with FP32 accumulation and BF16 output, forward and input
-// gradient over cached forward and backward weight layouts).  With
+// both the forward product and the input gradient are NVFP4 GEMMs that sum in
+// FP32 and write BF16, each over its own cached NVFP4 copy of the weight).  With
 // W_fwd = Q(W) and W_bwd = Q(W^T) both directions are this one product:
 //   forward  Y  = X_q  W_fwd^T   (A = X_q  [M x K],  B = W_fwd [N x K])
 //   dgrad    dX = dY_q W_bwd^T   (A = dY_q [M x N],  B = W_bwd [K x N])

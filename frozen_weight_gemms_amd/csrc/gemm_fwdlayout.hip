@@ -1,10 +1,10 @@
 // Input-gradient GEMM over the forward weight layout only (single-layout
 // dgrad): dX = dY_q . deq(W_fwd), W_fwd = Q(W) [N x K] blocked along K, so the
 // frozen weight needs one cached NVFP4 layout instead of two and the forward
-// and input-gradient products use identical effective weights.  (The pages'
-// method keeps cached forward and backward layouts, PACT Appendix Table 7 row
-// "Frozen projections"; this variant instead reuses the W_fwd tiles through a
-// transposed read, so each weight keeps one layout.)
+// and input-gradient products use identical effective weights.  (PACT keeps
+// two cached NVFP4 copies of each weight, one per direction, Appendix Table 7
+// row "Frozen projections"; this variant instead reuses the W_fwd tiles
+// through a transposed read, so each weight keeps one layout.)
 //
 // The contraction runs over N, the row axis of W_fwd.  Per stage of 256
 // contraction rows the workgroup stages, for its 128 output columns, the
@@ -20,7 +20,11 @@
 // exponent over W_fwd's nonzero rows (a per-weight constant computed once);
 // the epilogue multiplies by 2^e_ref.  A B element c * s * 2^(e_n - e_ref) is exact
 // in FP16 while e_ref - e_n <= 14 (c s is a multiple of 2^-10 with at most 6
-// significant bits); rows more than 2^14 below the largest one round in FP16.
+// significant bits).  A row with nonzero block scales outside that window
+// (more than 2^14 below e_ref, or above it: an e_ref that is not this
+// weight's) would round or vanish in FP16; the table build flags it and the
+// workgroup then writes NaN to every output it owns instead of a silently
+// wrong gradient (pact_nvfp4_row_exp_max rejects such a weight up front).
 //
 // The A side (dY_q, blocked along N), the stage pipeline (two LDS stages of
 // 256, loads issued one stage ahead, one barrier per stage plus one after the
@@ -176,6 +180,7 @@ __global__ __launch_bounds__(256, 1) void k_gemm_dgrad_fwdlayout(FlArgs p, int t
   };
 
   // ---- FP16 scale table of a stage: thread t handles contraction row t ----
+  uint32_t inexact_row = 0;                              // a nonzero row outside the exact FP16 window
   auto build_table = [&](int buf) {
     const uint8_t* st = smem + buf * C::STAGE;
     const uint2 raw = *reinterpret_cast<const uint2*>(st + C::B_SC + tid * 8);
@@ -183,7 +188,9 @@ __global__ __launch_bounds__(256, 1) void k_gemm_dgrad_fwdlayout(FlArgs p, int t
     const int e_n = (int)((rb >> 23) & 0xFFu) - 127;     // r is a power of two (0 for rows past N)
     const int d = e_ref - e_n;
     // 2^-d in FP16, exact for 0 <= d <= 24; d > 24: below FP16 (0); d < 0 only
-    // for all-zero rows (excluded from e_ref), whose block scales are 0 anyway
+    // for all-zero rows (excluded from e_ref), whose block scales are 0 anyway.
+    // Exactness of every c s 2^-d needs 0 <= d <= 14 on rows with a nonzero scale.
+    inexact_row |= ((d > 14 || d < 0) && (raw.x | raw.y) != 0u) ? 1u : 0u;
     const _Float16 mult = (d >= 0 && d <= 24) ? (_Float16)__uint_as_float((uint32_t)(127 - d) << 23)
                                                : (_Float16)0.0f;
     const half2_t m2 = {mult, mult};
@@ -430,8 +437,9 @@ __global__ __launch_bounds__(256, 1) void k_gemm_dgrad_fwdlayout(FlArgs p, int t
   PACT_WAIT_VMCNT(0);
 
   // ---- epilogue: r_A[m] 2^e_ref, optional accumulate, BF16 rounding ----
-  __syncthreads();
-  const float ref = __uint_as_float((uint32_t)(e_ref + 127) << 23);
+  // every thread saw every stage's table rows, so the flag is per workgroup
+  const bool poison = __syncthreads_or((int)inexact_row) != 0;
+  const float ref = poison ? __uint_as_float(0x7FC00000u) : __uint_as_float((uint32_t)(e_ref + 127) << 23);
   float* epi = reinterpret_cast<float*>(smem + wave * C::EPI_WAVE);
   constexpr int WN = BN / 2;
   constexpr int CHUNKS = WN / 8;
@@ -488,19 +496,23 @@ __global__ __launch_bounds__(256, 1) void k_gemm_dgrad_fwdlayout(FlArgs p, int t
   }
 }
 
-// Largest row exponent over the rows of an NVFP4 tensor that are not all zero
-// (an all-zero row has row scale 1 by the row rule, which must not set the
-// reference).  Each wave tests one row at a time (any nonzero block scale);
-// one atomic per workgroup combines the maxima (the initial value is -126).
+// Largest and smallest row exponent over the rows of an NVFP4 tensor that are
+// not all zero (an all-zero row has row scale 1 by the row rule, which must
+// not set the reference).  Each wave tests one row at a time (any nonzero block
+// scale); one atomic pair per workgroup combines the extremes (initial values
+// -126 and 127).
 __global__ void k_init_exp(int* out) {
-  if (blockIdx.x == 0 && threadIdx.x == 0) *out = -126;
+  if (blockIdx.x == 0 && threadIdx.x == 0) {
+    out[0] = -126;
+    out[1] = 127;
+  }
 }
-__global__ __launch_bounds__(256) void k_row_exp_max(const float* __restrict__ rscale,
-                                                     const uint8_t* __restrict__ scales, int64_t rows,
-                                                     int64_t nblk, int* __restrict__ out) {
-  __shared__ int red[4];
+__global__ __launch_bounds__(256) void k_row_exp_range(const float* __restrict__ rscale,
+                                                       const uint8_t* __restrict__ scales, int64_t rows,
+                                                       int64_t nblk, int* __restrict__ out) {
+  __shared__ int red[2][4];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  int m = -126;
+  int hi = -126, lo = 127;
   for (int64_t i = (int64_t)blockIdx.x * 4 + wave; i < rows; i += (int64_t)gridDim.x * 4) {
     uint32_t any = 0;
     for (int64_t b = lane; b < nblk; b += 64) any |= scales[i * nblk + b];
@@ -508,15 +520,23 @@ __global__ __launch_bounds__(256) void k_row_exp_max(const float* __restrict__ r
     for (int o = 32; o >= 1; o >>= 1) any |= (uint32_t)__shfl_xor((int)any, o, 64);
     if (any != 0) {
       const int e = (int)((__float_as_uint(rscale[i]) >> 23) & 0xFFu) - 127;
-      m = e > m ? e : m;
+      hi = e > hi ? e : hi;
+      lo = e < lo ? e : lo;
     }
   }
-  if (lane == 0) red[wave] = m;
+  if (lane == 0) {
+    red[0][wave] = hi;
+    red[1][wave] = lo;
+  }
   __syncthreads();
   if (threadIdx.x == 0) {
-    int r = red[0];
-    for (int k = 1; k < 4; ++k) r = red[k] > r ? red[k] : r;
-    atomicMax(out, r);
+    int h = red[0][0], l = red[1][0];
+    for (int k = 1; k < 4; ++k) {
+      h = red[0][k] > h ? red[0][k] : h;
+      l = red[1][k] < l ? red[1][k] : l;
+    }
+    atomicMax(out, h);
+    atomicMin(out + 1, l);
   }
 }
 
@@ -525,7 +545,7 @@ hipError_t launch_row_exp_max(const float* rscale, const uint8_t* scales, int64_
   k_init_exp<<<1, 64, 0, s>>>(out);
   int64_t grid = (rows + 3) / 4;
   if (grid > 256) grid = 256;
-  k_row_exp_max<<<(unsigned)grid, 256, 0, s>>>(rscale, scales, rows, cols / 16, out);
+  k_row_exp_range<<<(unsigned)grid, 256, 0, s>>>(rscale, scales, rows, cols / 16, out);
   return hipGetLastError();
 }
 

@@ -1,7 +1,7 @@
 // BF16 rank-r LoRA branch on the reconstructed input (PACT, Appendix Table 7
-// row "LoRA branch": BF16 GEMMs on reconstructed inputs forward; BF16 adapter
-// gradients and input gradients backward; saved state is the shared NVFP4
-// input and the BF16 adapters; Figure 3's caption describes the same split).
+// row "LoRA branch": the adapter products run in BF16 on the dequantized
+// NVFP4 input in both directions, and backward keeps only that NVFP4 input
+// and the BF16 adapters; Figure 3's caption draws the same split).
 //
 //   lora_down : T  = bf16(X~ A^T)             X~ = deq(X_q), exact in BF16
 //   lora_bwd  : T  = bf16(X~ A^T)             (recomputed, kept in the workspace)
@@ -29,6 +29,7 @@
 //     on scheduling.
 #include "pact_internal.h"
 
+#include <mutex>
 #include <type_traits>
 
 namespace pact {
@@ -641,6 +642,38 @@ hipError_t launch_lora_bwd(const uint8_t* xc, const uint8_t* xs, const float* xr
   const int64_t tot4 = (N + K) * r / 4;
   k_lora_reduce<<<grid_for(tot4), 256, 0, s>>>(pdB, pdA, (int)w.nsplit_b, (int)w.nsplit_a, N, K, r, scale, dB, dA);
   return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// lora_bwd without a caller workspace: the same launches, with the workspace
+// in a fixed device array.  Every byte of the workspace that a launch reads is
+// written earlier in the same call (T^T and dT^T by the row kernel for rows
+// < M, each split's partials by the column kernel), so nothing is cleared
+// between calls.  One array per device, shared by every call on that device:
+// calls that overlap on one GPU race.
+// ---------------------------------------------------------------------------
+static __device__ __align__(256) uint8_t scratch[kLoraScratchBytes];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_dev[kMaxDevices] = {};     // device address of `scratch` on each device, once looked up
+}  // namespace
+
+hipError_t lora_scratch_address(void** out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_dev[dev] == nullptr) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));      // with `dev` current: this device's copy
+    if (e != hipSuccess) return e;
+    g_scratch_dev[dev] = p;
+  }
+  *out = g_scratch_dev[dev];
+  return hipSuccess;
 }
 
 }  // namespace pact

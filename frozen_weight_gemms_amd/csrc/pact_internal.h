@@ -94,6 +94,11 @@ hipError_t launch_lora_down(const uint8_t* xc, const uint8_t* xs, const float* x
 
 size_t lora_bwd_workspace(int64_t M, int64_t K, int64_t N, int64_t r);
 
+// fixed per-device scratch of lora_bwd_noalloc (a device array; its address on
+// the current device is looked up once per device)
+constexpr size_t kLoraScratchBytes = (size_t)32 << 20;
+hipError_t lora_scratch_address(void** out);
+
 hipError_t launch_lora_bwd(const uint8_t* xc, const uint8_t* xs, const float* xr, int64_t M, int64_t K,
                            const uint16_t* A, const uint16_t* B, int64_t r, float scale, const uint16_t* dy,
                            int64_t N, uint16_t* dT, uint16_t* dA, uint16_t* dB, void* workspace, hipStream_t s);

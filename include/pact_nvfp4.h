@@ -3,11 +3,11 @@
  *
  * The operations are those of PACT's LoRA linear layer and decoder MLP as its
  * precision-allocation table describes them ("PACT: NVFP4 Data-Flow LoRA
- * Fine-Tuning on Consumer GPUs", Appendix Table 7): frozen projections as
- * NVFP4 GEMMs with FP32 accumulation and BF16 output over cached forward and
- * backward NVFP4 weight layouts; RMSNorm and SiLU-multiply fused with NVFP4
- * quantization, with FP32 reconstruction in backward; a BF16 LoRA branch on the
- * reconstructed input.
+ * Fine-Tuning on Consumer GPUs", Appendix Table 7): frozen projections run as
+ * NVFP4 GEMMs that sum in FP32 and write BF16, each direction over its own
+ * cached NVFP4 copy of the weight; RMSNorm and SiLU-multiply are fused with
+ * NVFP4 quantization and rebuild their inputs in FP32 for backward; the LoRA
+ * branch runs in BF16 on the dequantized input.
  *
  * NVFP4 tensor (Appendix Table 6: 16-element blocks, E2M1 elements, E4M3
  * block scales, 4.50 bits/element).  A tensor of logical shape [rows x cols],
@@ -141,8 +141,8 @@ int nvfp4_quantize_ex(const uint16_t *x, int64_t rows, int64_t cols, int64_t ldx
 
 /*
  * rmsnorm_quant -- RMSNorm forward fused with NVFP4 quantization (Appendix
- * Table 7 row "RMSNorm": BF16 input, FP32 normalization; NVFP4 output and FP32
- * per-token statistic kept).  For each row of x [M x H] (leading dim ldx):
+ * Table 7 row "RMSNorm": a BF16 row normalized in FP32; the NVFP4 result and
+ * one FP32 statistic per token are saved for backward).  For each row of x [M x H] (leading dim ldx):
  *   S = sum x^2 (float64), ms = fp32(S/H), v = ms + eps, rstd = 1/sqrt(v),
  *   y = (x * rstd) * gain  (FP32, round-to-nearest, no contraction),
  * writes Q(y) (the projection input) and rstd [M].  gain is BF16 [H].
@@ -153,9 +153,22 @@ int rmsnorm_quant(const uint16_t *x, const uint16_t *gain, float eps, int64_t M,
                   void *stream);
 
 /*
+ * rmsnorm_quant_ex -- rmsnorm_quant with flags (0: rmsnorm_quant exactly).
+ *   PACT_RMSNORM_EXACT_SUM: every row's sum of squares takes the double-double
+ *   path.  rmsnorm_quant already switches a row to that path whenever its
+ *   float64 sum lies within the sum's error bound of a float32 rounding
+ *   boundary, so the results are identical; the flag exists so that tests can
+ *   check the double-double path on every row.  Unknown flags: PACT_EINVAL.
+ */
+#define PACT_RMSNORM_EXACT_SUM 1
+int rmsnorm_quant_ex(const uint16_t *x, const uint16_t *gain, float eps, int64_t M, int64_t H,
+                     int64_t ldx, int flags, uint8_t *y_codes, uint8_t *y_scales, float *y_rscale,
+                     float *rstd, void *stream);
+
+/*
  * silu_mul_quant -- SiLU-multiply forward fused with NVFP4 quantization
- * (Appendix Table 7 row "SiLU-multiply": BF16 gate/up inputs, FP32 arithmetic,
- * separate NVFP4 gate/up copies kept).  Elementwise on gate a, up b [M x I]
+ * (Appendix Table 7 row "SiLU-multiply": FP32 arithmetic on the BF16 gate and
+ * up values; an NVFP4 copy of each of the two is saved for backward).  Elementwise on gate a, up b [M x I]
  * (shared leading dim ld):
  *   sigma = 1/(1 + E(-a)), h = (a * sigma) * b   (FP32; E is the library's
  *   Cody-Waite + degree-7 Taylor exponential),
@@ -201,8 +214,8 @@ int nvfp4_gemm_fwd(const uint8_t *x_codes, const uint8_t *x_scales, const float 
 
 /*
  * nvfp4_gemm_dgrad -- frozen-projection input gradient dX = dY W (Appendix
- * Table 7 row "Frozen projections": NVFP4 input-gradient GEMMs over the cached
- * backward layout).
+ * Table 7 row "Frozen projections": the input gradient is an NVFP4 GEMM over
+ * the weight's cached backward copy).
  *   dY_q: NVFP4 [M x N]; W_bwd: NVFP4 [K x N] (= Q(W^T), blocks along N).
  *   dX: BF16 [M x K], leading dim lddx >= K.
  *   accumulate != 0: dX = bf16( f32(dX) + result )  (sums several consumers).
@@ -229,9 +242,13 @@ int nvfp4_gemm_dgrad(const uint8_t *dy_codes, const uint8_t *dy_scales, const fl
  *   dY_q NVFP4 [M x N]; W_fwd NVFP4 [N x K]; dX BF16 [M x K], ldx >= K;
  *   LoRA term and accumulate as nvfp4_gemm_dgrad.
  *   w_exp_max: device int, the largest row-scale exponent over W_fwd's
- *   nonzero rows (pact_nvfp4_row_exp_max, once per weight).  Each B element is formed
- *   in FP16 as code * block scale * 2^(e_row - w_exp_max): exact while no row's
- *   exponent is more than 14 below w_exp_max, rounded in FP16 below that.
+ *   nonzero rows (out[0] of pact_nvfp4_row_exp_max, once per weight).  Each B
+ *   element is formed in FP16 as code * block scale * 2^(e_row - w_exp_max),
+ *   exact while every nonzero row's exponent lies in [w_exp_max - 14,
+ *   w_exp_max] (the weights pact_nvfp4_row_exp_max accepts).  If a nonzero row
+ *   falls outside that window the launch cannot be exact: every output the
+ *   affected workgroups own is written as NaN (in practice all of dX, since
+ *   every workgroup contracts over all rows) rather than a rounded gradient.
  *   N % 256 == 0 and K % 64 == 0 (else PACT_EUNSUPPORTED), operands below
  *   2^31 bytes of codes.
  */
@@ -266,16 +283,24 @@ int nvfp4_gemm_dgrad_multi(int nseg, const uint8_t *const *dy_codes, const uint8
                            int accumulate, const uint16_t *const *lora_dt, const uint16_t *const *lora_a,
                            const int64_t *lora_r, void *stream);
 
-/* Largest exponent e of the power-of-two row scales 2^e over the rows of an
- * NVFP4 tensor [rows x cols] that are not all zero (device int *out; -126 if
- * every row is zero), for nvfp4_gemm_dgrad_fwd_layout.  codes is validated
- * but not read.  rows > 0, cols % 16 == 0. */
+/*
+ * pact_nvfp4_row_exp_max -- set-up of a weight for nvfp4_gemm_dgrad_fwd_layout,
+ * once per weight.  Over the rows of an NVFP4 tensor [rows x cols] that are not
+ * all zero, writes the largest exponent e of the power-of-two row scales 2^e to
+ * out[0] and the smallest to out[1] (out: device array of 2 ints; -126 and 127
+ * if every row is zero).  codes is validated but not read.  rows > 0,
+ * cols % 16 == 0.  Unlike the other entry points this call synchronizes
+ * `stream` (it reads the two exponents back) and returns PACT_EUNSUPPORTED when
+ * out[0] - out[1] > 14: the single-layout dgrad forms each weight element in
+ * FP16 relative to 2^out[0], which is exact only within that window (the
+ * exponents are still written).
+ */
 int pact_nvfp4_row_exp_max(const uint8_t *codes, const uint8_t *scales, const float *rscale, int64_t rows,
                            int64_t cols, int *out, void *stream);
 
 /*
  * lora_down -- LoRA forward down-projection on the reconstructed input
- * (Appendix Table 7 row "LoRA branch": BF16 GEMMs on reconstructed inputs).
+ * (Appendix Table 7 row "LoRA branch": a BF16 product on the dequantized input).
  *   T = bf16( deq(X_q) A^T ),  X_q NVFP4 [M x K], A BF16 [r x K] row-major,
  *   T BF16 [M x r] row-major.  FP32 accumulation.  1 <= r <= 128, K % 16 == 0.
  */
@@ -306,8 +331,25 @@ int lora_bwd(const uint8_t *x_codes, const uint8_t *x_scales, const float *x_rsc
              void *workspace, size_t workspace_bytes, void *stream);
 
 /*
+ * lora_bwd_noalloc -- lora_bwd for callers that cannot allocate device memory
+ * (code under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc): the same operation, arguments and results as lora_bwd (bit for
+ * bit), without the workspace.  The library's own fixed scratch array of
+ * 32 MiB per device (allocated when the library is loaded onto that device,
+ * held until the process ends) takes its place; no call allocates or frees
+ * memory.  PACT_EUNSUPPORTED when pact_lora_bwd_workspace_size(M, K, N, r)
+ * exceeds 32 MiB (never for r <= 128 with M <= 16384 and K, N <= 16384).
+ * Every call on a device shares that device's array: calls that overlap on one
+ * GPU (other streams, other threads) race and must be serialized by the caller.
+ */
+int lora_bwd_noalloc(const uint8_t *x_codes, const uint8_t *x_scales, const float *x_rscale,
+                     int64_t M, int64_t K, const uint16_t *A, const uint16_t *B, int64_t r, float scale,
+                     const uint16_t *dy, int64_t N, uint16_t *dT, uint16_t *dA, uint16_t *dB, void *stream);
+
+/*
  * silu_mul_bwd -- SiLU-multiply backward from the NVFP4 state (Appendix Table 7
- * row "SiLU-multiply": FP32 reconstruction and derivatives, BF16 gradients).
+ * row "SiLU-multiply", backward column: inputs rebuilt from the NVFP4 copies,
+ * derivatives in FP32, BF16 results).
  *   a^ = deq(gate_q), b^ = deq(up_q), sigma = 1/(1 + E(-a^)) with E the
  *   pinned FP32 exponential of silu_mul_quant:
  *   dgate = bf16( ((dh b^) sigma) (1 + a^ (1 - sigma)) ),  dup = bf16( (dh a^) sigma ),
@@ -336,7 +378,8 @@ int silu_mul_bwd_quant(const uint8_t *g_codes, const uint8_t *g_scales, const fl
 
 /*
  * rmsnorm_bwd -- RMSNorm backward from the NVFP4 state (Appendix Table 7 row
- * "RMSNorm": FP32 reconstruction and reduction, BF16 gradient).
+ * "RMSNorm", backward column: input rebuilt from the NVFP4 copy, FP32 row
+ * reduction, BF16 result).
  *   y^ = deq(y_q) [M x H], rstd f32 [M], gain BF16 [H], dy BF16 [M x H]:
  *   S = sum_j dy_j y^_j exactly, rounded once to float64; mean = fp32(S / H)
  *   (float64 division);
@@ -351,7 +394,7 @@ int rmsnorm_bwd(const uint8_t *y_codes, const uint8_t *y_scales, const float *y_
 
 /*
  * rmsnorm_bwd_residual -- rmsnorm_bwd fused with the residual-gradient
- * accumulation (Appendix Table 7 row "Residuals": BF16 gradient accumulation)
+ * accumulation (Appendix Table 7 row "Residuals": residual gradients summed in BF16)
  * and, optionally, the NVFP4 quantization of the sum (quantize-on-emit: the
  * result is the output gradient of the projection that produced the residual
  * stream's previous value).

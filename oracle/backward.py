@@ -1,9 +1,9 @@
 """RMSNorm and SiLU-multiply backward from the saved NVFP4 state (oracle).
 
-PACT's backward for these operators reconstructs in FP32 from the NVFP4
-state kept in forward and emits BF16 gradients (Appendix Table 7, rows
-"RMSNorm": FP32 reconstruction and reduction, BF16 gradient; "SiLU-multiply":
-FP32 reconstruction and derivatives, BF16 gradients).  The exact value of
+PACT's backward for these operators rebuilds its inputs in FP32 from the
+NVFP4 copies saved in forward and writes BF16 gradients (Appendix Table 7,
+rows "RMSNorm" and "SiLU-multiply", backward column; RMSNorm's also reduces
+over the row).  The exact value of
 such a gradient is the textbook derivative evaluated at the reconstructed
 inputs, which is what these functions return, in float64.
 

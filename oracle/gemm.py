@@ -1,8 +1,8 @@
 """Frozen-projection GEMMs of dequantized NVFP4 operands, in float64 (oracle).
 
-PACT runs every frozen projection as an NVFP4 GEMM with FP32 accumulation and
-BF16 output, forward and input-gradient, over cached forward and backward
-NVFP4 weight layouts (Appendix Table 7, row "Frozen projections").  The exact
+PACT runs every frozen projection as an NVFP4 GEMM that sums in FP32 and
+writes BF16, in both directions, each direction over its own cached NVFP4
+copy of the weight (Appendix Table 7, row "Frozen projections").  The exact
 result of such a GEMM is the product of the dequantized operands, which is
 what this module computes:
 

@@ -1,9 +1,9 @@
 """The BF16 rank-r LoRA branch on the dequantized input (oracle).
 
-PACT keeps the adapter path in BF16: "BF16 GEMMs on reconstructed inputs"
-forward, "BF16 adapter gradients and input gradients" backward, with the
-shared NVFP4 input and the BF16 adapters as the saved state (Appendix
-Table 7, row "LoRA branch"; Figure 3's caption describes the same split).
+PACT keeps the adapter path in BF16: its products run in BF16 on the
+dequantized NVFP4 input, forward and backward, and backward keeps only that
+NVFP4 input and the BF16 adapters (Appendix Table 7, row "LoRA branch";
+Figure 3's caption draws the same split).
 
 Readings (the pages give no formulas, rank or scale):
 * X~ = deq(X_q) is the reconstructed input; it is exact in BF16.

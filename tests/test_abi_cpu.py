@@ -25,7 +25,7 @@ def lib():
 
 def test_header_symbols_exported(lib):
     names = _lib.header_functions()
-    assert len(names) == 26, names
+    assert len(names) == len(set(names)) and len(names) >= 27, names
     assert set(names) == set(_lib.SIGNATURES), set(names) ^ set(_lib.SIGNATURES)
     for n in names:
         assert hasattr(lib, n), n
@@ -57,7 +57,7 @@ def test_gemm_tile_query(lib):
 
 
 def test_abi_version(lib):
-    assert lib.pact_abi_version() == 9
+    assert lib.pact_abi_version() == 10
 
 
 def test_sizes(lib):

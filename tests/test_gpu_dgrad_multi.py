@@ -150,3 +150,25 @@ def test_unsupported_width_is_rejected(fw):
     dyq, wb = _seg(64, 272, 256, 7)
     with pytest.raises(fw.PactError, match="multiple of 256"):
         fw.gemm_dgrad_multi([(nvfp4_to_gpu(dyq), nvfp4_to_gpu(wb))])
+
+
+@pytest.mark.parametrize("r", [64, 128])
+def test_segments_high_rank_lora(fw, r):
+    """Segmented input gradient with rank-64 and rank-128 LoRA terms on every
+    segment (and one segment without), against the oracle's sum."""
+    M, K, widths = 192, 768, (512, 256, 256)
+    segs = [_seg(M, n, K, 70 + 3 * i + r) for i, n in enumerate(widths)]
+    lora, terms = [], []
+    for i in range(len(widths)):
+        if i == 1:
+            lora.append(None)
+            continue
+        dT = synth.normal_bf16((M, r), 0.01, 96, 80 + i + r)
+        A = synth.normal_bf16((r, K), 0.01, 96, 90 + i + r)
+        lora.append((bits_to_torch(dT), bits_to_torch(A)))
+        terms.append(olora.lora_term(bf16_values(dT), bf16_values(A), 1.0))
+    out = fw.gemm_dgrad_multi([(nvfp4_to_gpu(a), nvfp4_to_gpu(b)) for a, b in segs], lora=lora)
+    ref, rabs = ogemm.gemm_dgrad_multi(segs)
+    for term, tabs, _ in terms:
+        ref, rabs = ref + term, rabs + tabs
+    assert_within(torch_bf16_to_f64(out), ref, tol.gemm_bound(ref, rabs), f"segments r={r}")

@@ -183,3 +183,40 @@ def test_llama3b_full_size_sampled(fw, name, d_in, d_out):
     assert_within(ysub, yref, tol.gemm_bound(yref, yabs), f"{name} fwd")
     dref, dabs = ogemm.gemm_nt(sel(dyq), wb)
     assert_within(dxsub, dref, tol.gemm_bound(dref, dabs), f"{name} dgrad")
+
+
+@pytest.mark.parametrize("r", [64, 128])
+@pytest.mark.parametrize("s", [2.0, 0.75])
+@pytest.mark.parametrize("M,N,K", [(320, 640, 512), (200, 384, 272), (4096, 3072, 3072)])
+def test_lora_epilogue_high_rank(fw, M, N, K, r, s):
+    """The fused LoRA term at rank 64 (the 8B-scale workload's rank) and 128
+    (the largest the library accepts), forward (s T B^T) and input gradient
+    (dT A, accumulating), with a power-of-two and another scale.  K = 512 and
+    3072 take the direct-to-LDS kernel (the 3072 case is a step shape, rows
+    sampled), K = 272 the generic one (contraction not a multiple of 256)."""
+    x = synth.activations_bf16((M, K), 97, M + K + r)
+    w = synth.normal_bf16((N, K), 0.02, 97, M + K + r + 1)
+    t = synth.normal_bf16((M, r), 0.3, 97, M + K + r + 2)
+    b = synth.normal_bf16((N, r), 0.01, 97, M + K + r + 3)
+    dy = synth.normal_bf16((M, N), 0.01, 97, M + K + r + 4)
+    dt = synth.normal_bf16((M, r), 0.01, 97, M + K + r + 5)
+    A = synth.normal_bf16((r, K), 0.01, 97, M + K + r + 6)
+    prev = synth.normal_bf16((M, K), 0.001, 97, M + K + r + 7)
+    xq, wf, wb, dyq = _q(x), _q(w), _qt(w), _q(dy)
+    rows = np.arange(M) if M <= 512 else np.sort(np.random.default_rng(M + r).choice(M, size=48, replace=False))
+    rows[-1] = M - 1
+    sel = lambda q: onv.NVFP4(q.codes[rows], q.scales[rows], q.rscale[rows])
+    y = fw.gemm_fwd(nvfp4_to_gpu(xq), nvfp4_to_gpu(wf), lora_t=bits_to_torch(t), lora_b=bits_to_torch(b),
+                    lora_scale=s)
+    yref, yabs = ogemm.gemm_nt(sel(xq), wf)
+    term, tabs, _ = olora.lora_term(bf16_values(t)[rows], bf16_values(b).T, s)
+    assert np.abs(term).max() > 0
+    assert_within(torch_bf16_to_f64(y)[rows], yref + term, tol.gemm_bound(yref + term, yabs + tabs),
+                  f"fwd r={r} s={s}")
+    out = bits_to_torch(prev).clone()
+    fw.gemm_dgrad(nvfp4_to_gpu(dyq), nvfp4_to_gpu(wb), out=out, accumulate=True,
+                  lora_dt=bits_to_torch(dt), lora_a=bits_to_torch(A))
+    dref, dabs = ogemm.gemm_nt(sel(dyq), wb)
+    dterm, dtabs, _ = olora.lora_term(bf16_values(dt)[rows], bf16_values(A), 1.0)
+    want = bf16_values(prev)[rows].astype(np.float64) + dref + dterm
+    assert_within(torch_bf16_to_f64(out)[rows], want, tol.gemm_bound(want, dabs + dtabs), f"dgrad r={r}")

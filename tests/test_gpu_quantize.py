@@ -55,7 +55,9 @@ def test_golden_vectors_on_gpu(fw):
 
 
 @pytest.mark.parametrize("rows,cols", [(1, 16), (7, 48), (33, 272), (5, 2048), (3, 4096 + 16), (2, 16384),
-                                       (3, 20480), (300, 1024)])
+                                       (3, 20480), (300, 1024),
+                                       # 513..768 blocks per row: four waves per row, three blocks per lane
+                                       (3, 8208), (5, 10240), (4, 12288), (2, 12304)])
 def test_ragged_and_long_shapes(fw, rows, cols):
     bits = synth.activations_bf16((rows, cols), 90, rows * 100003 + cols)
     _check(fw, bits, what=f"{rows}x{cols}")

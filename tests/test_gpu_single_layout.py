@@ -70,6 +70,36 @@ def test_row_scale_spread_and_zero_rows(fw):
     assert torch.count_nonzero(dx[7]).item() == 0
 
 
+def test_exponent_window_is_enforced(fw):
+    """Nonzero rows 2^20 apart in row scale (beyond the 2^14 window in which
+    the FP16 weight operand is exact): the set-up call refuses the weight,
+    and the kernel, launched anyway with that weight's largest exponent,
+    writes NaN rather than a rounded gradient.  The oracle's exact product is
+    finite and nonzero there."""
+    M, N, K = 64, 512, 128
+    w = bf16_values(synth.normal_bf16((N, K), 0.02, 88, 21)).astype(np.float64)
+    w[N // 2:] *= 2.0 ** -20
+    dyv = bf16_values(synth.normal_bf16((M, N), 0.01, 88, 22)).astype(np.float64)
+    wf, dyq = onv.quantize(w), onv.quantize(dyv)
+    gw = nvfp4_to_gpu(wf)
+    with pytest.raises(fw._lib.PactError) as ei:
+        fw.SingleLayoutWeight(gw)
+    assert ei.value.status == -5
+    sw = fw.SingleLayoutWeight.__new__(fw.SingleLayoutWeight)
+    sw.w_fwd = gw
+    sw.exp_range = torch.empty((2,), dtype=torch.int32, device="cuda")
+    sw.exp_max = sw.exp_range[:1]
+    lib = fw._lib.load()
+    st = lib.pact_nvfp4_row_exp_max(*gw.ptrs(), N, K, sw.exp_range.data_ptr(), None)
+    assert st == -5
+    lo, hi = np.frexp(wf.rscale.astype(np.float64))[1].min() - 1, np.frexp(wf.rscale.astype(np.float64))[1].max() - 1
+    assert sw.exp_range.cpu().tolist() == [hi, lo] and hi - lo >= 20
+    dx = fw.gemm_dgrad_fwd_layout(nvfp4_to_gpu(dyq), sw)
+    assert torch.isnan(dx.float()).all(), "an inexact launch must not return numbers"
+    ref, _ = ogemm.gemm_dgrad_fwd_layout(dyq, wf)
+    assert np.all(np.isfinite(ref)) and np.abs(ref).max() > 0
+
+
 def test_accumulate_and_lora(fw):
     M, N, K, r = 160, 512, 384, 16
     dy = synth.normal_bf16((M, N), 0.01, 88, 10)

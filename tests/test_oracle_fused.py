@@ -1,9 +1,10 @@
 """Pins of the oracle's fused RMSNorm / SiLU-multiply forward and backward.
 
-PACT, Appendix Table 7: RMSNorm takes BF16 input with FP32 normalization and
-keeps NVFP4 output plus an FP32 per-token statistic; SiLU-multiply takes BF16
-gate/up with FP32 arithmetic and keeps separate NVFP4 gate/up copies;
-backward reconstructs in FP32 from that state.  The tests check the pinned
+PACT, Appendix Table 7, rows "RMSNorm" and "SiLU-multiply": RMSNorm
+normalizes a BF16 row in FP32 and saves its NVFP4 result with one FP32
+statistic per token; SiLU-multiply computes in FP32 from the BF16 gate and up
+and saves an NVFP4 copy of each; backward rebuilds its inputs in FP32 from
+those copies.  The tests check the pinned
 FP32 exponential against math.exp, closed forms (constant rows, silu(0),
 sigmoid(0)), invariances of the exact sum of squares, and the backward
 formulas against finite differences of the float64 forward.

@@ -1,7 +1,7 @@
 """Pins of the oracle's GEMMs, LoRA branch and tolerance helpers.
 
-Frozen projections are NVFP4 GEMMs with FP32 accumulation and BF16 output
-(PACT, Appendix Table 7, row "Frozen projections"); the LoRA branch is a
+Frozen projections are NVFP4 GEMMs that sum in FP32 and write BF16 (PACT,
+Appendix Table 7, row "Frozen projections"); the LoRA branch is a
 BF16 GEMM on the reconstructed input (row "LoRA branch").  The oracle
 computes both exactly in float64; these tests pin it with exact-rational
 brute force on tiny shapes, an integer special case, finite differences of
@@ -187,3 +187,105 @@ def test_dgrad_multi_matches_rational_sum_over_segments():
     r1, a1 = gemm.gemm_dgrad_multi(segs[:1])
     r0, a0 = gemm.gemm_dgrad(*segs[0])
     assert np.array_equal(r1, r0) and np.array_equal(a1, a0)
+
+
+def _frac_bf16(x: Fraction) -> Fraction:
+    """Round an exact rational to the nearest BF16 value, ties to the even
+    significand (8 significant bits; subnormal spacing 2^-133), written with
+    integer arithmetic only (independent of tolerance.bf16_rne)."""
+    if x == 0:
+        return Fraction(0)
+    a = abs(x)
+    e = a.numerator.bit_length() - a.denominator.bit_length()
+    if Fraction(2) ** e > a:
+        e -= 1
+    elif Fraction(2) ** (e + 1) <= a:
+        e += 1
+    q = Fraction(2) ** max(e - 7, -133)
+    n = a / q
+    fl = n.numerator // n.denominator
+    rem = n - fl
+    if rem > Fraction(1, 2) or (rem == Fraction(1, 2) and fl % 2 == 1):
+        fl += 1
+    return (fl * q) if x > 0 else -(fl * q)
+
+
+def _frac_ulp_bf16(x: Fraction) -> Fraction:
+    """BF16 unit in the last place at |x| by its definition: 2^(max(floor(log2|x|), -126) - 7)."""
+    if x == 0:
+        return Fraction(2) ** -133
+    a = abs(x)
+    e = a.numerator.bit_length() - a.denominator.bit_length()
+    if Fraction(2) ** e > a:
+        e -= 1
+    elif Fraction(2) ** (e + 1) <= a:
+        e += 1
+    return Fraction(2) ** (max(e, -126) - 7)
+
+
+def test_lora_term_nonzero_against_rationals():
+    """lora_term(T, U, s) = s T U with its two bound sums, checked against
+    exact rationals on a non-square case (r = 3, Nout = 5) with nonzero U and
+    scales that are not 1 or 2 (one not a power of two, one negative and not
+    a binary fraction).  A dropped or doubled s, a sign error or a transposed
+    U changes the term by far more than the 2^-50 relative slack."""
+    rng = np.random.default_rng(141)
+    M, r, N = 4, 3, 5
+    t = tolerance.bf16_rne(rng.standard_normal((M, r)) * 0.3)
+    u = tolerance.bf16_rne(rng.standard_normal((r, N)) * 0.01)
+    for s in (0.75, -1.0 / 3.0):
+        term, tabs, tslack = lora.lora_term(t, u, s)
+        assert term.shape == (M, N) and tabs.shape == (M, N) and tslack.shape == (M, N)
+        fs = Fraction(s)                       # the float the oracle was given
+        for m in range(M):
+            for n in range(N):
+                prods = [Fraction(float(t[m, j])) * Fraction(float(u[j, n])) for j in range(r)]
+                exact = fs * sum(prods)
+                absum = abs(fs) * sum(abs(p) for p in prods)
+                slack = abs(fs) * sum(_frac_ulp_bf16(Fraction(float(t[m, j]))) * abs(Fraction(float(u[j, n])))
+                                      for j in range(r))
+                assert absum > 0
+                assert abs(Fraction(float(term[m, n])) - exact) <= absum * Fraction(1, 2 ** 50)
+                assert abs(Fraction(float(tabs[m, n])) - absum) <= absum * Fraction(1, 2 ** 50)
+                assert abs(Fraction(float(tslack[m, n])) - slack) <= slack * Fraction(1, 2 ** 50)
+        # the transposed product is a different matrix here (and a different shape)
+        with np.testing.assert_raises(ValueError):
+            lora.lora_term(t, u.T, s)
+
+
+def test_forward_with_lora_composed_against_rationals():
+    """Y = X~ W~^T + s bf16(X~ A^T) B^T, composed from the oracle's pieces
+    (gemm_fwd, lora_down, lora_term) exactly as the GPU tests compose their
+    expected value, against an exact-rational evaluation of the same formula
+    with its own BF16 rounding of T.  s = 0.75 and s = -1/3."""
+    rng = np.random.default_rng(142)
+    M, K, N, r = 3, 32, 5, 4
+    x = rng.standard_normal((M, K))
+    w = rng.standard_normal((N, K)) * 0.02
+    a = tolerance.bf16_rne(rng.standard_normal((r, K)) * 0.05)
+    b = tolerance.bf16_rne(rng.standard_normal((N, r)) * 0.05)
+    xq, wf = nvfp4.quantize(x), nvfp4.quantize(w)
+    fx, fw = _frac_deq(xq), _frac_deq(wf)
+    ft = [[_frac_bf16(sum(fx[m][k] * Fraction(float(a[j, k])) for k in range(K))) for j in range(r)]
+          for m in range(M)]
+    y, yabs = gemm.gemm_fwd(xq, wf)
+    _, t_bf16, _ = lora.lora_down(xq, a)
+    for m in range(M):
+        for j in range(r):
+            assert Fraction(float(t_bf16[m, j])) == ft[m][j], "T must be the BF16 rounding of the exact X~ A^T"
+    for s in (0.75, -1.0 / 3.0):
+        term, tabs, _ = lora.lora_term(t_bf16, b.T, s)
+        got = y + term
+        fs = Fraction(s)
+        for m in range(M):
+            for n in range(N):
+                base = [fx[m][k] * fw[n][k] for k in range(K)]
+                lr = [ft[m][j] * Fraction(float(b[n, j])) for j in range(r)]
+                exact = sum(base) + fs * sum(lr)
+                absum = sum(abs(v) for v in base) + abs(fs) * sum(abs(v) for v in lr)
+                assert abs(Fraction(float(got[m, n])) - exact) <= absum * Fraction(1, 2 ** 49)
+                assert abs(Fraction(float(yabs[m, n] + tabs[m, n])) - absum) <= absum * Fraction(1, 2 ** 49)
+        # the LoRA term is not negligible in this case: dropping it moves Y by
+        # much more than the GPU acceptance bound
+        bound = tolerance.gemm_bound(got, yabs + tabs)
+        assert np.any(np.abs(term) > bound)
