@@ -445,6 +445,32 @@ def mx_weight_layouts(w: torch.Tensor):
     return mx_quantize(w), mx_quantize(w, transpose=True)
 
 
+def mx_rmsnorm_quant(x: torch.Tensor, gain: torch.Tensor, eps: float = 1e-5, out=None):
+    """(MXFP4(y), rstd) with y = (x * rstd) * gain; ``out`` = (MXFP4Tensor, rstd) to reuse buffers."""
+    _bf16(x, "x"); _bf16(gain, "gain")
+    M, H = x.shape
+    if out is not None:
+        y, rstd = out
+    else:
+        y = empty_mxfp4(M, H, x.device)
+        rstd = torch.empty((M,), dtype=torch.float32, device=x.device)
+    _lib.call("mxfp4_rmsnorm_quant", x.data_ptr(), gain.data_ptr(), float(eps), M, H, x.stride(0), *y.ptrs(),
+              rstd.data_ptr(), _stream())
+    return y, rstd
+
+
+def mx_silu_mul_quant(gate: torch.Tensor, up: torch.Tensor, out=None):
+    """(MXFP4(h), MXFP4(gate), MXFP4(up)) with h = silu(gate) * up; ``out`` = three MXFP4Tensors."""
+    _bf16(gate, "gate"); _bf16(up, "up")
+    if gate.shape != up.shape or gate.stride() != up.stride():
+        raise ValueError("gate and up must have the same shape and strides")
+    M, I = gate.shape
+    h, gq, uq = out if out is not None else (empty_mxfp4(M, I, gate.device) for _ in range(3))
+    _lib.call("mxfp4_silu_mul_quant", gate.data_ptr(), up.data_ptr(), M, I, gate.stride(0), *h.ptrs(), *gq.ptrs(),
+              *uq.ptrs(), _stream())
+    return h, gq, uq
+
+
 def mx_gemm(a: MXFP4Tensor, b: MXFP4Tensor, out: torch.Tensor | None = None, accumulate: bool = False):
     """C = bf16([f32(C) +] deq(a) deq(b)^T) for MXFP4 a [M x K], b [N x K]."""
     M, K = a.rows, a.cols

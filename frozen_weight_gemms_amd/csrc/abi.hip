@@ -176,7 +176,7 @@ int rmsnorm_quant_ex(const uint16_t* x, const uint16_t* gain, float eps, int64_t
   REQUIRE(M <= 0x7FFFFFFF, PACT_EUNSUPPORTED, "M=%lld exceeds the grid limit", (long long)M);
   const int force_exact = (flags & PACT_RMSNORM_EXACT_SUM) ? 1 : 0;
   return hip_status(pact::launch_rmsnorm_quant(x, gain, eps, M, H, ldx, y_codes, y_scales, y_rscale, rstd,
-                                               force_exact, as_stream(stream)),
+                                               force_exact, 0, as_stream(stream)),
                     "rmsnorm_quant launch");
 }
 
@@ -201,7 +201,7 @@ int silu_mul_quant(const uint16_t* gate, const uint16_t* up, int64_t M, int64_t 
   REQUIRE(ld >= I && ld % 8 == 0, PACT_ESHAPE, "ld=%lld must be >= I and a multiple of 8", (long long)ld);
   REQUIRE(M <= 0x7FFFFFFF, PACT_EUNSUPPORTED, "M=%lld exceeds the grid limit", (long long)M);
   return hip_status(pact::launch_silu_mul_quant(gate, up, M, I, ld, h_codes, h_scales, h_rscale, g_codes, g_scales,
-                                                g_rscale, u_codes, u_scales, u_rscale, as_stream(stream)),
+                                                g_rscale, u_codes, u_scales, u_rscale, 0, as_stream(stream)),
                     "silu_mul_quant launch");
 }
 
@@ -570,6 +570,48 @@ int mxfp4_quantize(const uint16_t* x, int64_t rows, int64_t cols, int64_t ldx, i
   REQUIRE(rows <= 0x7FFFFFFF, PACT_EUNSUPPORTED, "rows=%lld exceeds the grid limit", (long long)rows);
   return hip_status(pact::launch_mx_quantize(x, rows, cols, ldx, transpose, codes, scales, as_stream(stream)),
                     "mxfp4_quantize launch");
+}
+
+int mxfp4_rmsnorm_quant(const uint16_t* x, const uint16_t* gain, float eps, int64_t M, int64_t H, int64_t ldx,
+                        uint8_t* y_codes, uint8_t* y_scales, float* rstd, void* stream) {
+  REQUIRE(M >= 0 && H >= 0, PACT_EINVAL, "negative size (M=%lld, H=%lld)", (long long)M, (long long)H);
+  REQUIRE(H % 32 == 0, PACT_ESHAPE, "H=%lld is not a multiple of 32", (long long)H);
+  REQUIRE(H <= kMaxFusedCols, PACT_EUNSUPPORTED, "H=%lld exceeds %lld", (long long)H, (long long)kMaxFusedCols);
+  REQUIRE(eps >= 0.0f, PACT_EINVAL, "eps must be non-negative");
+  if (M == 0) return ok();
+  REQUIRE(H > 0, PACT_ESHAPE, "H must be positive");
+  REQUIRE_PTR(x, "x");
+  REQUIRE_PTR(gain, "gain");
+  REQUIRE_PTR(rstd, "rstd");
+  REQUIRE_PTR(y_codes, "y codes");
+  REQUIRE_PTR(y_scales, "y scales");
+  REQUIRE(ldx >= H && ldx % 8 == 0, PACT_ESHAPE, "ldx=%lld must be >= H and a multiple of 8", (long long)ldx);
+  REQUIRE(M <= 0x7FFFFFFF, PACT_EUNSUPPORTED, "M=%lld exceeds the grid limit", (long long)M);
+  return hip_status(pact::launch_rmsnorm_quant(x, gain, eps, M, H, ldx, y_codes, y_scales, nullptr, rstd, 0, 1,
+                                               as_stream(stream)),
+                    "mxfp4_rmsnorm_quant launch");
+}
+
+int mxfp4_silu_mul_quant(const uint16_t* gate, const uint16_t* up, int64_t M, int64_t I, int64_t ld,
+                         uint8_t* h_codes, uint8_t* h_scales, uint8_t* g_codes, uint8_t* g_scales, uint8_t* u_codes,
+                         uint8_t* u_scales, void* stream) {
+  REQUIRE(M >= 0 && I >= 0, PACT_EINVAL, "negative size (M=%lld, I=%lld)", (long long)M, (long long)I);
+  REQUIRE(I % 32 == 0, PACT_ESHAPE, "I=%lld is not a multiple of 32", (long long)I);
+  REQUIRE(I <= kMaxFusedCols, PACT_EUNSUPPORTED, "I=%lld exceeds %lld", (long long)I, (long long)kMaxFusedCols);
+  if (M == 0 || I == 0) return ok();
+  REQUIRE_PTR(gate, "gate");
+  REQUIRE_PTR(up, "up");
+  REQUIRE_PTR(h_codes, "h codes");
+  REQUIRE_PTR(h_scales, "h scales");
+  REQUIRE_PTR(g_codes, "gate_q codes");
+  REQUIRE_PTR(g_scales, "gate_q scales");
+  REQUIRE_PTR(u_codes, "up_q codes");
+  REQUIRE_PTR(u_scales, "up_q scales");
+  REQUIRE(ld >= I && ld % 8 == 0, PACT_ESHAPE, "ld=%lld must be >= I and a multiple of 8", (long long)ld);
+  REQUIRE(M <= 0x7FFFFFFF, PACT_EUNSUPPORTED, "M=%lld exceeds the grid limit", (long long)M);
+  return hip_status(pact::launch_silu_mul_quant(gate, up, M, I, ld, h_codes, h_scales, nullptr, g_codes, g_scales,
+                                                nullptr, u_codes, u_scales, nullptr, 1, as_stream(stream)),
+                    "mxfp4_silu_mul_quant launch");
 }
 
 int mxfp4_gemm(const uint8_t* a_codes, const uint8_t* a_scales, int64_t M, int64_t K, const uint8_t* b_codes,

@@ -181,7 +181,7 @@ __global__ __launch_bounds__(256, 1) void k_gemm_dgrad_fwdlayout(FlArgs p, int t
 
   // ---- FP16 scale table of a stage: thread t handles contraction row t ----
   uint32_t inexact_row = 0;                              // a nonzero row outside the exact FP16 window
-  auto build_table = [&](int buf) {
+  auto build_table = [&](int buf, bool real_stage) {
     const uint8_t* st = smem + buf * C::STAGE;
     const uint2 raw = *reinterpret_cast<const uint2*>(st + C::B_SC + tid * 8);
     const uint32_t rb = __float_as_uint(*reinterpret_cast<const float*>(st + C::B_R + tid * 4));
@@ -190,7 +190,8 @@ __global__ __launch_bounds__(256, 1) void k_gemm_dgrad_fwdlayout(FlArgs p, int t
     // 2^-d in FP16, exact for 0 <= d <= 24; d > 24: below FP16 (0); d < 0 only
     // for all-zero rows (excluded from e_ref), whose block scales are 0 anyway.
     // Exactness of every c s 2^-d needs 0 <= d <= 14 on rows with a nonzero scale.
-    inexact_row |= ((d > 14 || d < 0) && (raw.x | raw.y) != 0u) ? 1u : 0u;
+    // (only for a real stage: past the last one the buffer holds stale bytes)
+    inexact_row |= (real_stage && (d > 14 || d < 0) && (raw.x | raw.y) != 0u) ? 1u : 0u;
     const _Float16 mult = (d >= 0 && d <= 24) ? (_Float16)__uint_as_float((uint32_t)(127 - d) << 23)
                                                : (_Float16)0.0f;
     const half2_t m2 = {mult, mult};
@@ -334,7 +335,7 @@ __global__ __launch_bounds__(256, 1) void k_gemm_dgrad_fwdlayout(FlArgs p, int t
         PACT_WAIT_VMCNT(0);
         __syncthreads();                                // stage kt + 1 published (stale past the end)
         const uint8_t* stn = smem + ((kt + 1) & 1) * C::STAGE;
-        build_table((kt + 1) & 1);
+        build_table((kt + 1) & 1, kt + 1 < nk);
         read_a(stn, 0);
         read_b(stn, 0);
         read_a_scales(stn, sra_n);
@@ -423,7 +424,7 @@ __global__ __launch_bounds__(256, 1) void k_gemm_dgrad_fwdlayout(FlArgs p, int t
         for (int j = 0; j < WTN; ++j) acc[i][j][rr] *= fa;
       }
   }
-  build_table(0);
+  build_table(0, true);
   read_a(smem, 0);
   read_b(smem, 0);
   read_a_scales(smem, sra);
@@ -437,8 +438,13 @@ __global__ __launch_bounds__(256, 1) void k_gemm_dgrad_fwdlayout(FlArgs p, int t
   PACT_WAIT_VMCNT(0);
 
   // ---- epilogue: r_A[m] 2^e_ref, optional accumulate, BF16 rounding ----
-  // every thread saw every stage's table rows, so the flag is per workgroup
-  const bool poison = __syncthreads_or((int)inexact_row) != 0;
+  // the threads together saw every stage's table rows: OR the flag over the
+  // workgroup (a ballot per wave, one LDS word per wave)
+  __shared__ uint32_t inexact_wave[4];
+  const bool wave_inexact = __ballot(inexact_row != 0u) != 0ull;
+  if (lane == 0) inexact_wave[wave] = wave_inexact ? 1u : 0u;
+  __syncthreads();
+  const bool poison = (inexact_wave[0] | inexact_wave[1] | inexact_wave[2] | inexact_wave[3]) != 0u;
   const float ref = poison ? __uint_as_float(0x7FC00000u) : __uint_as_float((uint32_t)(e_ref + 127) << 23);
   float* epi = reinterpret_cast<float*>(smem + wave * C::EPI_WAVE);
   constexpr int WN = BN / 2;

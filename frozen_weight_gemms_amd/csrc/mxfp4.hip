@@ -1,15 +1,7 @@
 // MXFP4 variant of the frozen-projection path: quantizers and the GEMM on
 // gfx950's scaled FP4 matrix instructions.
 //
-// Format (PACT, Appendix Table 6, MXFP4 column): 32-element blocks, E2M1
-// elements, one E8M0 scale per block, 4.25 bits per element, no other scale.
-// Block scale (the OCP microscaling rule): shared exponent
-// e = floor(log2(blockmax)) - 2 clamped to [-127, 127] (-127 for an all-zero
-// block), stored as the byte e + 127; element code = RNE(|x| / 2^e) onto E2M1,
-// ties to even, saturating at 6, sign kept.  |x| / 2^e is an exact power-of-
-// two scaling (2^-e is a normal FP32 number for every e a finite FP32 block
-// maximum can produce), and v_cvt_scalef32_pk_fp4_f32 with scale 1.0 performs
-// the RNE, saturation and sign handling.
+// Format and block rule: mxfp4_device.h (Appendix Table 6, MXFP4 column).
 //
 // GEMM.  v_mfma_scale_f32_32x32x64_f8f6f4 with both operands in FP4 takes, per
 // lane (i = lane % 32, h = lane / 32), row i's 32 elements K = 32h .. 32h + 31
@@ -24,37 +16,13 @@
 #include <utility>
 
 #include "lds_dma.h"
+#include "mxfp4_device.h"
 #include "pact_internal.h"
 
 namespace pact {
 
 typedef float floatx16 __attribute__((ext_vector_type(16)));
 typedef int v8i_t __attribute__((ext_vector_type(8)));
-
-constexpr int kMxBlock = 32;
-
-// floor(log2(amax)) - 2, clamped to [-127, 127]; -127 for amax == 0 (amax >= 0 finite).
-__device__ __forceinline__ int mx_shared_exp(float amax) {
-  const uint32_t u = __float_as_uint(amax);
-  if (u == 0u) return -127;
-  const int ef = (int)(u >> 23);
-  const int fl = ef != 0 ? ef - 127 : (31 - __builtin_clz(u & 0x7FFFFFu)) - 149;   // subnormal amax
-  const int e = fl - 2;
-  return e < -127 ? -127 : (e > 127 ? 127 : e);
-}
-
-// 8 elements times 2^-e -> 8 packed E2M1 codes (element 0 in the low nibble).
-__device__ __forceinline__ uint32_t mx_encode8(const float* x, float inv) {
-  uint32_t w = 0u;
-  w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, x[0] * inv, x[1] * inv, 1.0f, 0);
-  w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, x[2] * inv, x[3] * inv, 1.0f, 1);
-  w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, x[4] * inv, x[5] * inv, 1.0f, 2);
-  w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, x[6] * inv, x[7] * inv, 1.0f, 3);
-  return w;
-}
-
-// 2^-e as FP32 for e in [-127, 125] (a normal number)
-__device__ __forceinline__ float mx_inv_scale(int e) { return __uint_as_float((uint32_t)(127 - e) << 23); }
 
 // ---------------------------------------------------------------------------
 // Row quantizer: thread q handles chunk q (8 elements) of the [rows x cols]

@@ -26,11 +26,11 @@ hipError_t launch_tensor_absmax(const uint16_t* x, int64_t rows, int64_t cols, i
 
 hipError_t launch_rmsnorm_quant(const uint16_t* x, const uint16_t* gain, float eps, int64_t M, int64_t H,
                                 int64_t ldx, uint8_t* codes, uint8_t* scales, float* rscale, float* rstd,
-                                int force_exact, hipStream_t s);
+                                int force_exact, int mx, hipStream_t s);   // mx: MXFP4 output (rscale unused)
 
 hipError_t launch_silu_mul_quant(const uint16_t* gate, const uint16_t* up, int64_t M, int64_t I, int64_t ld,
                                  uint8_t* hc, uint8_t* hs, float* hr, uint8_t* gc, uint8_t* gs, float* gr,
-                                 uint8_t* uc, uint8_t* us, float* ur, hipStream_t s);
+                                 uint8_t* uc, uint8_t* us, float* ur, int mx, hipStream_t s);
 
 // C[M x N] = A[M x K] B[N x K]^T for row-blocked NVFP4 A and B, BF16 output.
 struct GemmArgs {

@@ -12,6 +12,7 @@
 // 2p+1; its amax is one cross-lane exchange.  The row amax (needed before any
 // block scale) is a wave64 butterfly plus a 4-entry LDS exchange.  Codes leave
 // as one 32-bit store per chunk (coalesced across the wave), scales as bytes.
+#include "mxfp4_device.h"
 #include "pact_internal.h"
 #include "row_ops.h"
 
@@ -183,7 +184,9 @@ __device__ __forceinline__ double row_sum_f64(double v, double* dred, int wave, 
   return v;
 }
 
-template <int NB, int WPR>
+// MX: the output is MXFP4 (32-element blocks, E8M0 scales, no row scale;
+// rscale unused) instead of NVFP4; the FP32 sequence is the same.
+template <int NB, int WPR, bool MX>
 __global__ __launch_bounds__(kThreads) void k_rmsnorm_quant(const uint16_t* __restrict__ x,
                                                             const uint16_t* __restrict__ gain, float eps,
                                                             int64_t M, int64_t H, int64_t ldx,
@@ -308,6 +311,27 @@ __global__ __launch_bounds__(kThreads) void k_rmsnorm_quant(const uint16_t* __re
     bm[i] = fmaxf(absmax8(y), absmax8(y + 8));
     lmax = fmaxf(lmax, bm[i]);
   }
+  if constexpr (MX) {
+    // MXFP4: a 32-element block is the 16-element blocks of lanes 2p, 2p + 1
+    // (H % 32 == 0, so both halves are in the row or neither); no row scale
+    if (!row_ok) return;
+    uint8_t* crow = codes + row * (H >> 1);
+    uint8_t* srow = scales + row * (H >> 5);
+#pragma unroll
+    for (int i = 0; i < NB; ++i) {
+      const int blk = lane + 64 * part + 64 * WPR * i;
+      float f[16], g[16], y[16];
+      unpack_bf16x8(v[i][0], f);
+      unpack_bf16x8(v[i][1], f + 8);
+      unpack_bf16x8(gv[i][0], g);
+      unpack_bf16x8(gv[i][1], g + 8);
+#pragma unroll
+      for (int t = 0; t < 16; ++t) y[t] = __fmul_rn(__fmul_rn(f[t], rstd), g[t]);
+      mx_quant_half(y, bm[i], blk < nblk, crow, srow, blk);
+    }
+    if (lane == 0 && part == 0) rstd_out[row] = rstd;
+    return;
+  }
   float amax = wave_max(lmax);
   if constexpr (WPR > 1) {
     if (lane == 0) red[wave] = amax;
@@ -344,7 +368,9 @@ __global__ __launch_bounds__(kThreads) void k_rmsnorm_quant(const uint16_t* __re
 // --------------------------------------------------------------------------
 // silu_mul_quant
 // --------------------------------------------------------------------------
-template <int NCH>
+// MX: MXFP4 outputs (32-element blocks on lanes 4p .. 4p + 3, E8M0 scales, no
+// row scales or row maxima; the r* arguments are unused).
+template <int NCH, bool MX>
 __global__ __launch_bounds__(kThreads) void k_silu_mul_quant(const uint16_t* __restrict__ gate,
                                                              const uint16_t* __restrict__ up, int64_t I,
                                                              int64_t ld, uint8_t* __restrict__ hc,
@@ -376,6 +402,21 @@ __global__ __launch_bounds__(kThreads) void k_silu_mul_quant(const uint16_t* __r
     ma = fmaxf(ma, absmax8(a));
     mb = fmaxf(mb, absmax8(b));
     mh = fmaxf(mh, absmax8(h[i]));
+  }
+  if constexpr (MX) {
+    const int64_t co = row * (I >> 1), so = row * (I >> 5);
+#pragma unroll
+    for (int i = 0; i < NCH; ++i) {
+      const int c = threadIdx.x + kThreads * i;
+      const bool ok = c < nchunk;                  // I % 32 == 0: uniform over a block's four lanes
+      float a[8], b[8];
+      unpack_bf16x8(va[i], a);
+      unpack_bf16x8(vb[i], b);
+      mx_quant_chunk(h[i], ok, hc + co, hs + so, c);
+      mx_quant_chunk(a, ok, gc + co, gs + so, c);
+      mx_quant_chunk(b, ok, uc + co, us + so, c);
+    }
+    return;
   }
   ma = wave_max(ma);
   mb = wave_max(mb);
@@ -543,7 +584,7 @@ hipError_t launch_quantize(const uint16_t* x, int64_t rows, int64_t cols, int64_
 
 hipError_t launch_rmsnorm_quant(const uint16_t* x, const uint16_t* gain, float eps, int64_t M, int64_t H,
                                 int64_t ldx, uint8_t* codes, uint8_t* scales, float* rscale, float* rstd,
-                                int force_exact, hipStream_t s) {
+                                int force_exact, int mx, hipStream_t s) {
   // the quantizer's row layout: blocks per lane <= 4 (one wave per row up to
   // 4096 columns, two up to 8192, four up to 16384)
   const int64_t nblk = H >> 4;
@@ -551,8 +592,13 @@ hipError_t launch_rmsnorm_quant(const uint16_t* x, const uint16_t* gain, float e
   const int wpr = nblk <= 256 ? 1 : (nblk <= 512 ? 2 : 4);
   const int64_t nb = (nblk + 64 * wpr - 1) / (64 * wpr);
   const dim3 grid((unsigned)((M + 4 / wpr - 1) / (4 / wpr)));
-#define PACT_RMS(N, W) \
-  k_rmsnorm_quant<N, W><<<grid, kThreads, 0, s>>>(x, gain, eps, M, H, ldx, codes, scales, rscale, rstd, force_exact)
+#define PACT_RMS(N, W)                                                                                          \
+  do {                                                                                                         \
+    if (mx) k_rmsnorm_quant<N, W, true><<<grid, kThreads, 0, s>>>(x, gain, eps, M, H, ldx, codes, scales, rscale,   \
+                                                               rstd, force_exact);                             \
+    else k_rmsnorm_quant<N, W, false><<<grid, kThreads, 0, s>>>(x, gain, eps, M, H, ldx, codes, scales, rscale,     \
+                                                                rstd, force_exact);                            \
+  } while (0)
   if (wpr == 1 && nb <= 1) PACT_RMS(1, 1);
   else if (wpr == 1 && nb <= 2) PACT_RMS(2, 1);
   else if (wpr == 1 && nb <= 3) PACT_RMS(3, 1);
@@ -567,10 +613,14 @@ hipError_t launch_rmsnorm_quant(const uint16_t* x, const uint16_t* gain, float e
 
 hipError_t launch_silu_mul_quant(const uint16_t* gate, const uint16_t* up, int64_t M, int64_t I, int64_t ld,
                                  uint8_t* hc, uint8_t* hs, float* hr, uint8_t* gc, uint8_t* gs, float* gr,
-                                 uint8_t* uc, uint8_t* us, float* ur, hipStream_t s) {
+                                 uint8_t* uc, uint8_t* us, float* ur, int mx, hipStream_t s) {
   const int nch = chunks_per_thread(I);
   const dim3 grid((unsigned)M);
-#define PACT_SILU(N) k_silu_mul_quant<N><<<grid, kThreads, 0, s>>>(gate, up, I, ld, hc, hs, hr, gc, gs, gr, uc, us, ur)
+#define PACT_SILU(N)                                                                                         \
+  do {                                                                                                      \
+    if (mx) k_silu_mul_quant<N, true><<<grid, kThreads, 0, s>>>(gate, up, I, ld, hc, hs, hr, gc, gs, gr, uc, us, ur); \
+    else k_silu_mul_quant<N, false><<<grid, kThreads, 0, s>>>(gate, up, I, ld, hc, hs, hr, gc, gs, gr, uc, us, ur);  \
+  } while (0)
   if (nch <= 1) PACT_SILU(1);
   else if (nch <= 2) PACT_SILU(2);
   else if (nch <= 4) PACT_SILU(4);

@@ -437,6 +437,27 @@ int mxfp4_quantize(const uint16_t *x, int64_t rows, int64_t cols, int64_t ldx, i
                    uint8_t *codes, uint8_t *scales, void *stream);
 
 /*
+ * mxfp4_rmsnorm_quant -- rmsnorm_quant with an MXFP4 output (Appendix Table 7
+ * row "RMSNorm" with the Table 6 MXFP4 format): the same FP32 sequence
+ *   S = sum x^2 (float64), ms = fp32(S/H), v = ms + eps, rstd = 1/sqrt(v),
+ *   y = (x * rstd) * gain,
+ * then y_q = MXFP4(y) [M x H] (codes, E8M0 scales) and rstd [M].  H % 32 == 0,
+ * H <= 16384; ldx >= H, a multiple of 8.
+ */
+int mxfp4_rmsnorm_quant(const uint16_t *x, const uint16_t *gain, float eps, int64_t M, int64_t H, int64_t ldx,
+                        uint8_t *y_codes, uint8_t *y_scales, float *rstd, void *stream);
+
+/*
+ * mxfp4_silu_mul_quant -- silu_mul_quant with MXFP4 outputs (Appendix Table 7
+ * row "SiLU-multiply" with the Table 6 MXFP4 format): h = (a * sigma) * b in
+ * the same FP32 sequence, outputs MXFP4(h), MXFP4(a), MXFP4(b) [M x I].
+ * I % 32 == 0, I <= 16384; gate and up share the leading dimension ld.
+ */
+int mxfp4_silu_mul_quant(const uint16_t *gate, const uint16_t *up, int64_t M, int64_t I, int64_t ld,
+                         uint8_t *h_codes, uint8_t *h_scales, uint8_t *g_codes, uint8_t *g_scales,
+                         uint8_t *u_codes, uint8_t *u_scales, void *stream);
+
+/*
  * mxfp4_gemm -- C = A B^T for MXFP4 A [M x K] and B [N x K] (forward: X_q and
  * W_fwd = Q(W); input gradient: dY_q [M x N] and W_bwd = Q(W^T) [K x N]), on
  * the scaled FP4 matrix instructions with FP32 accumulation (Appendix Table 7

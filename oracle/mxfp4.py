@@ -109,3 +109,30 @@ def gemm_nt(a: MXFP4, b: MXFP4):
     da = dequantize(a)
     db = dequantize(b)
     return da @ db.T, np.abs(da) @ np.abs(db).T
+
+
+def rmsnorm_quant(x, g, eps: float):
+    """RMSNorm fused with MXFP4 quantization: (Q_mx(y), rstd, y) with y the
+    RMSNorm output in the same pinned FP32 sequence as the NVFP4 path's
+    (fused.rmsnorm_stats: exact sum of squares rounded once to float64,
+    ms = fp32(S / K), v = ms + eps, rstd = 1 / sqrt(v), y = (x * rstd) * g),
+    then the MXFP4 quantizer above.  Appendix Table 7 row "RMSNorm" with the
+    Table 6 MXFP4 format in place of NVFP4."""
+    from .fused import rmsnorm_stats
+    x = np.asarray(x, dtype=np.float32)
+    g = np.asarray(g, dtype=np.float32)
+    rstd = rmsnorm_stats(x, eps)
+    y = ((x * rstd[:, None]) * g[None, :]).astype(np.float32)
+    return quantize(y.astype(np.float64)), rstd, y
+
+
+def silu_mul_quant(a, b):
+    """SiLU-multiply fused with MXFP4 quantization: (Q_mx(h), Q_mx(a), Q_mx(b), h)
+    with h = (a * sigma(a)) * b in the pinned FP32 sequence of the NVFP4 path
+    (fused.silu_f32).  Appendix Table 7 row "SiLU-multiply" with the Table 6
+    MXFP4 format."""
+    from .fused import silu_f32
+    a = np.asarray(a, dtype=np.float32)
+    b = np.asarray(b, dtype=np.float32)
+    h = (silu_f32(a) * b).astype(np.float32)
+    return (quantize(h.astype(np.float64)), quantize(a.astype(np.float64)), quantize(b.astype(np.float64)), h)

@@ -162,3 +162,55 @@ def workload_activation(wl: Workload, rows: int, cols: int, tensor_id: int) -> n
     if wl.act == "student_t3":
         return student_t_bf16((rows, cols), 3.0, wl.wid, tensor_id)
     raise ValueError(wl.act)
+
+
+# ---------------------------------------------------------------------------
+# Device-side draws (benchmark inputs): the same distributions drawn by torch's
+# seeded generator on the GPU, so multi-GB workloads need no host sampling.
+# Parity checks of benchmark outputs read these tensors back from the device.
+# ---------------------------------------------------------------------------
+
+def torch_generator(workload_id: int, tensor_id: int, device="cuda"):
+    import torch
+    g = torch.Generator(device=device)
+    g.manual_seed((int(workload_id) << 40) + int(tensor_id))
+    return g
+
+
+def normal_torch(shape, std: float, workload_id: int, tensor_id: int, device="cuda"):
+    """bfloat16 device tensor of N(0, std) samples (float32 draws, RNE to BF16)."""
+    import torch
+    g = torch_generator(workload_id, tensor_id, device)
+    x = torch.randn(shape, generator=g, device=device, dtype=torch.float32)
+    if std != 1.0:
+        x.mul_(std)
+    return x.to(torch.bfloat16)
+
+
+def uniform_torch(shape, lo: float, hi: float, workload_id: int, tensor_id: int, device="cuda"):
+    import torch
+    g = torch_generator(workload_id, tensor_id, device)
+    x = torch.rand(shape, generator=g, device=device, dtype=torch.float32)
+    return (x * (hi - lo) + lo).to(torch.bfloat16)
+
+
+def activation_torch(wl: Workload, rows: int, cols: int, tensor_id: int, device="cuda"):
+    """bfloat16 device activations [rows x cols] with the workload's distribution:
+    N(0,1); N(0,1) with ceil(1%) of the columns x20; or standard Student-t(3),
+    drawn as Z / sqrt((Z1^2 + Z2^2 + Z3^2) / 3) from independent normals."""
+    import torch
+    g = torch_generator(wl.wid, tensor_id, device)
+    x = torch.randn((rows, cols), generator=g, device=device, dtype=torch.float32)
+    if wl.act == "normal_outliers":
+        n_out = int(np.ceil(0.01 * cols))
+        idx = torch.randperm(cols, generator=g, device=device)[:n_out]
+        x[:, idx] *= 20.0
+    elif wl.act == "student_t3":
+        chi = torch.zeros_like(x)
+        for _ in range(3):
+            z = torch.randn((rows, cols), generator=g, device=device, dtype=torch.float32)
+            chi.addcmul_(z, z)
+        x.div_(torch.sqrt(chi / 3.0))
+    elif wl.act != "normal":
+        raise ValueError(wl.act)
+    return x.to(torch.bfloat16)

@@ -211,3 +211,57 @@ def test_llama3b_full_size_sampled(fw, name, d_in, d_out):
     assert_within(torch_bf16_to_f64(y)[np.ix_(rows, ncols)], yref, tol.gemm_bound(yref, yabs), name + " fwd")
     dref, dabs = omx.gemm_nt(odyq, owb)
     assert_within(torch_bf16_to_f64(dx)[np.ix_(rows, kcols)], dref, tol.gemm_bound(dref, dabs), name + " dgrad")
+
+
+# ---------------------------------------------------------------- fused forward operators, MXFP4 outputs
+@pytest.mark.parametrize("M,H", [(64, 256), (33, 3072), (9, 8192), (17, 16384), (5, 96), (8192, 3072), (3, 12288)])
+def test_mx_rmsnorm_quant(fw, M, H):
+    """RMSNorm -> MXFP4: rstd, codes and E8M0 scales bit-exact (every row layout:
+    one, two and four waves per row, ragged blocks per lane); the MLP-block
+    shape [8192 x 3072] checked on sampled rows."""
+    x = synth.activations_bf16((M, H), 3, 760 + H)
+    g = synth.uniform_bf16((H,), 0.9, 1.1, 3, 761 + H)
+    yq, rstd = fw.mx_rmsnorm_quant(bits_to_torch(x), bits_to_torch(g), 1e-5)
+    rows = np.arange(M) if M <= 64 else np.sort(np.random.default_rng(M).choice(M, size=128, replace=False))
+    ref_q, ref_rstd, _ = omx.rmsnorm_quant(bf16_values(x[rows]), bf16_values(g), 1e-5)
+    got = rstd.cpu().numpy()[rows]
+    assert np.array_equal(got.view(np.uint32), ref_rstd.view(np.uint32)), "rstd"
+    _assert_equal(yq, ref_q, f"mx rmsnorm {M}x{H}", rows=rows)
+
+
+@pytest.mark.parametrize("M,I", [(64, 256), (19, 8192), (7, 14336), (3, 96), (4096, 8192)])
+def test_mx_silu_mul_quant(fw, M, I):
+    """SiLU-multiply -> MXFP4 h, gate and up copies bit-exact, including
+    sigmoid edge values (0, -0, saturating and overflowing exponent inputs)."""
+    a = synth.normal_bf16((M, I), 2.0, 98, I + 1)
+    b = synth.normal_bf16((M, I), 1.0, 98, I + 2)
+    av = bf16_values(a).copy()
+    av[0, :16] = [0, -0.0, 100, -100, 88, -88, 89.5, -89.5, 80.25, -80.25, 1e-30, -1e-30, 3, -3, 1e-3, -1e-3]
+    av[-1, :32] = 0.0                                       # a zero block of h and of the gate copy
+    a = synth.bf16_bits(av)
+    hq, gq, uq = fw.mx_silu_mul_quant(bits_to_torch(a), bits_to_torch(b))
+    rows = np.arange(M) if M <= 64 else np.sort(np.append(
+        np.random.default_rng(I).choice(M - 1, size=127, replace=False), M - 1))
+    rows[0] = 0
+    rows = np.unique(rows)
+    rh, ra, rb, _ = omx.silu_mul_quant(bf16_values(a[rows]), bf16_values(b[rows]))
+    _assert_equal(gq, ra, "gate copy", rows=rows)
+    _assert_equal(uq, rb, "up copy", rows=rows)
+    _assert_equal(hq, rh, "h", rows=rows)
+
+
+def test_mx_fused_strided_and_validation(fw):
+    """Gate and up as column halves of one [M x 2I] buffer (the stacked
+    gate/up GEMM output), and host-side rejection of widths not a multiple of 32."""
+    M, I = 16, 512
+    y = synth.normal_bf16((M, 2 * I), 1.5, 98, 901)
+    t = bits_to_torch(y)
+    hq, gq, uq = fw.mx_silu_mul_quant(t[:, :I], t[:, I:])
+    rh, ra, rb, _ = omx.silu_mul_quant(bf16_values(y[:, :I]), bf16_values(y[:, I:]))
+    _assert_equal(hq, rh, "h (strided)")
+    _assert_equal(gq, ra, "gate (strided)")
+    _assert_equal(uq, rb, "up (strided)")
+    lib = fw._lib.load()
+    p = t.data_ptr()
+    assert lib.mxfp4_silu_mul_quant(p, p, 4, 48, 48, p, p, p, p, p, p, None) == -2
+    assert lib.mxfp4_rmsnorm_quant(p, p, 1e-5, 4, 48, 48, p, p, p, None) == -2

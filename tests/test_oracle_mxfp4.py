@@ -183,3 +183,81 @@ def test_nvfp4_scales_are_more_precise_on_workload_tensors():
         e_mx = rel(omx.dequantize(omx.quantize(x)))
         assert e_nv < e_mx, f"{name}: NVFP4 {e_nv:.4f} vs MXFP4 {e_mx:.4f}"
         assert e_mx / e_nv > 1.1, name
+
+
+# ---------------------------------------------------------------------------
+# fused forward operators in the MXFP4 format (RMSNorm and SiLU-multiply with
+# MXFP4 outputs): the FP32 sequences are the NVFP4 path's (pinned in
+# test_oracle_fused.py); here the MXFP4 outputs are pinned against the
+# independent exact-rational quantizer above and against closed forms
+# ---------------------------------------------------------------------------
+def _brute_rows(y):
+    """Exact-rational MXFP4 of every 32-element block of the rows of y."""
+    R, C = y.shape
+    scales = np.zeros((R, C // 32), np.uint8)
+    codes = np.zeros((R, C), np.int64)
+    for i in range(R):
+        for b in range(C // 32):
+            sb, cb = _brute_block([float(v) for v in y[i, 32 * b:32 * b + 32]])
+            scales[i, b] = sb
+            codes[i, 32 * b:32 * b + 32] = cb
+    return scales, codes
+
+
+def test_mx_rmsnorm_quant_against_brute_force():
+    from oracle import fused as ofused
+    rng = np.random.default_rng(151)
+    x = rng.standard_normal((6, 96)).astype(np.float32)
+    x[1] *= 2.0 ** -30
+    x[2, 5] = 300.0                                      # one outlier column
+    x = (x.astype(np.float32).view(np.uint32) & 0xFFFF0000).view(np.float32)     # BF16 values
+    g = rng.uniform(0.9, 1.1, 96).astype(np.float32)
+    g = (g.view(np.uint32) & 0xFFFF0000).view(np.float32)
+    q, rstd, y = omx.rmsnorm_quant(x, g, 1e-5)
+    # rstd and y are the NVFP4 path's pinned FP32 values, bit for bit
+    _, rstd_nv, y_nv = ofused.rmsnorm_quant(x, g, 1e-5)
+    assert np.array_equal(rstd.view(np.uint32), rstd_nv.view(np.uint32))
+    assert np.array_equal(y.view(np.uint32), y_nv.view(np.uint32))
+    sb, cb = _brute_rows(y.astype(np.float64))
+    assert np.array_equal(q.scales, sb)
+    assert np.array_equal(onv.unpack_codes(q.codes), cb)
+
+
+def test_mx_rmsnorm_quant_constant_row_closed_form():
+    """x = c everywhere and g = 1: y = fl32(c * rstd) in every element, so each
+    block's exponent is floor(log2 y) - 2 and every code is RNE(y / 2^e) with
+    y / 2^e in [4, 8): 4 (code 6) up to the tie at 5, 6 (code 7) above it."""
+    for c in (0.5, 1.0, 3.0, 7.25, 1e-3, 117.0):
+        x = np.full((1, 64), c, np.float32)
+        q, rstd, y = omx.rmsnorm_quant(x, np.ones(64, np.float32), 1e-5)
+        yv = Fraction(float(y[0, 0]))
+        fl = 0
+        while Fraction(2) ** fl > yv:
+            fl -= 1
+        while Fraction(2) ** (fl + 1) <= yv:
+            fl += 1
+        t = yv / Fraction(2) ** (fl - 2)
+        assert Fraction(4) <= t < Fraction(8)
+        want = 6 if t <= 5 else 7
+        assert q.scales.tolist() == [[fl - 2 + 127] * 2]
+        assert set(onv.unpack_codes(q.codes)[0].tolist()) == {want}
+
+
+def test_mx_silu_mul_quant_against_brute_force_and_closed_forms():
+    from oracle import fused as ofused
+    rng = np.random.default_rng(152)
+    a = (rng.standard_normal((4, 64)) * 3).astype(np.float32)
+    b = rng.standard_normal((4, 64)).astype(np.float32)
+    a = (a.view(np.uint32) & 0xFFFF0000).view(np.float32)
+    b = (b.view(np.uint32) & 0xFFFF0000).view(np.float32)
+    a[3, :32] = 0.0                                      # silu(0) = 0: a zero block of h
+    b[3, :32] = -1.0                                     # with h = (0 * sigma) * -1 = -0
+    hq, aq, bq, h = omx.silu_mul_quant(a, b)
+    assert np.array_equal(h.view(np.uint32), (ofused.silu_f32(a) * b).astype(np.float32).view(np.uint32))
+    for q, v in ((hq, h), (aq, a), (bq, b)):
+        sb, cb = _brute_rows(v.astype(np.float64))
+        assert np.array_equal(q.scales, sb)
+        assert np.array_equal(onv.unpack_codes(q.codes), cb)
+    # the zero block: scale byte 0 (e = -127), every code the sign bit alone
+    assert hq.scales[3, 0] == 0
+    assert set(onv.unpack_codes(hq.codes)[3, :32].tolist()) == {8}
