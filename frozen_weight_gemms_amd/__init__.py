@@ -471,6 +471,36 @@ def mx_silu_mul_quant(gate: torch.Tensor, up: torch.Tensor, out=None):
     return h, gq, uq
 
 
+def mx_silu_mul_bwd_quant(gq: MXFP4Tensor, uq: MXFP4Tensor, dh: torch.Tensor, out=None):
+    """(dgate, dup, MXFP4(dgate), MXFP4(dup)) from the MXFP4 state of silu_mul."""
+    _dense(_bf16(dh, "dh"), "dh")
+    M, I = dh.shape
+    if out is None:
+        out = (torch.empty_like(dh), torch.empty_like(dh), empty_mxfp4(M, I, dh.device), empty_mxfp4(M, I, dh.device))
+    dg, du, dgq, duq = out
+    _lib.call("mxfp4_silu_mul_bwd_quant", *gq.ptrs(), *uq.ptrs(), dh.data_ptr(), M, I, dg.data_ptr(), du.data_ptr(),
+              *dgq.ptrs(), *duq.ptrs(), _stream())
+    return dg, du, dgq, duq
+
+
+def mx_rmsnorm_bwd_residual(yq: MXFP4Tensor, rstd: torch.Tensor, gain: torch.Tensor, dy: torch.Tensor,
+                            resid: torch.Tensor | None = None, quantize_out: bool = True, out=None):
+    """(out, MXFP4(out) or None) with out = bf16(bf16(rmsnorm_bwd) + resid) from an MXFP4 state."""
+    _bf16(gain, "gain"); _dense(_bf16(dy, "dy"), "dy")
+    if resid is not None:
+        _dense(_bf16(resid, "resid"), "resid")
+        if resid.shape != dy.shape:
+            raise ValueError("resid must have dy's shape")
+    M, H = dy.shape
+    if out is None:
+        out = (torch.empty_like(dy), empty_mxfp4(M, H, dy.device) if quantize_out else None)
+    dx, q = out
+    qp = q.ptrs() if q is not None else (0, 0)
+    _lib.call("mxfp4_rmsnorm_bwd_residual", *yq.ptrs(), rstd.data_ptr(), gain.data_ptr(), dy.data_ptr(),
+              resid.data_ptr() if resid is not None else 0, M, H, dx.data_ptr(), *qp, _stream())
+    return dx, q
+
+
 def mx_gemm(a: MXFP4Tensor, b: MXFP4Tensor, out: torch.Tensor | None = None, accumulate: bool = False):
     """C = bf16([f32(C) +] deq(a) deq(b)^T) for MXFP4 a [M x K], b [N x K]."""
     M, K = a.rows, a.cols

@@ -61,6 +61,8 @@ SIGNATURES = {
     "mxfp4_quantize": ([c_vp, c_i64, c_i64, c_i64, c_int, c_vp, c_vp, c_vp], c_int),
     "mxfp4_rmsnorm_quant": ([c_vp, c_vp, c_float, c_i64, c_i64, c_i64, c_vp, c_vp, c_vp, c_vp], c_int),
     "mxfp4_silu_mul_quant": ([c_vp, c_vp, c_i64, c_i64, c_i64] + [c_vp] * 6 + [c_vp], c_int),
+    "mxfp4_silu_mul_bwd_quant": ([c_vp] * 5 + [c_i64, c_i64] + [c_vp] * 6 + [c_vp], c_int),
+    "mxfp4_rmsnorm_bwd_residual": ([c_vp] * 6 + [c_i64, c_i64] + [c_vp] * 3 + [c_vp], c_int),
     "mxfp4_gemm": ([c_vp, c_vp, c_i64, c_i64, c_vp, c_vp, c_i64, c_vp, c_i64, c_int, c_vp], c_int),
 }
 

@@ -419,7 +419,7 @@ int rmsnorm_bwd(const uint8_t* y_codes, const uint8_t* y_scales, const float* y_
   REQUIRE_PTR(dx, "dx");
   REQUIRE(M <= 0x7FFFFFFF, PACT_EUNSUPPORTED, "M too large");
   return hip_status(pact::launch_rmsnorm_bwd(y_codes, y_scales, y_rscale, rstd, gain, dy, M, H, nullptr, dx,
-                                             nullptr, nullptr, nullptr, as_stream(stream)),
+                                             nullptr, nullptr, nullptr, 0, as_stream(stream)),
                     "rmsnorm_bwd launch");
 }
 
@@ -513,7 +513,7 @@ int silu_mul_bwd_quant(const uint8_t* g_codes, const uint8_t* g_scales, const fl
   REQUIRE(M <= 0x7FFFFFFF, PACT_EUNSUPPORTED, "M too large");
   return hip_status(pact::launch_silu_mul_bwd_quant(g_codes, g_scales, g_rscale, u_codes, u_scales, u_rscale, dh, M,
                                                     I, dgate, dup, dg_codes, dg_scales, dg_rscale, du_codes,
-                                                    du_scales, du_rscale, as_stream(stream)),
+                                                    du_scales, du_rscale, 0, as_stream(stream)),
                     "silu_mul_bwd_quant launch");
 }
 
@@ -535,8 +535,59 @@ int rmsnorm_bwd_residual(const uint8_t* y_codes, const uint8_t* y_scales, const 
   if (resid != nullptr) REQUIRE_PTR(resid, "resid");
   REQUIRE(M <= 0x7FFFFFFF, PACT_EUNSUPPORTED, "M too large");
   return hip_status(pact::launch_rmsnorm_bwd(y_codes, y_scales, y_rscale, rstd, gain, dy, M, H, resid, dx,
-                                             want_q ? q_codes : nullptr, q_scales, q_rscale, as_stream(stream)),
+                                             want_q ? q_codes : nullptr, q_scales, q_rscale, 0, as_stream(stream)),
                     "rmsnorm_bwd_residual launch");
+}
+
+int mxfp4_silu_mul_bwd_quant(const uint8_t* g_codes, const uint8_t* g_scales, const uint8_t* u_codes,
+                             const uint8_t* u_scales, const uint16_t* dh, int64_t M, int64_t I, uint16_t* dgate,
+                             uint16_t* dup, uint8_t* dg_codes, uint8_t* dg_scales, uint8_t* du_codes,
+                             uint8_t* du_scales, void* stream) {
+  REQUIRE(M >= 0 && I >= 0, PACT_EINVAL, "negative size");
+  REQUIRE(I % 32 == 0, PACT_ESHAPE, "I=%lld is not a multiple of 32", (long long)I);
+  REQUIRE(I <= kMaxFusedCols, PACT_EUNSUPPORTED, "I=%lld exceeds %lld", (long long)I, (long long)kMaxFusedCols);
+  if (M == 0 || I == 0) return ok();
+  REQUIRE_PTR(g_codes, "gate_q codes");
+  REQUIRE_PTR(g_scales, "gate_q scales");
+  REQUIRE_PTR(u_codes, "up_q codes");
+  REQUIRE_PTR(u_scales, "up_q scales");
+  REQUIRE_PTR(dg_codes, "dgate_q codes");
+  REQUIRE_PTR(dg_scales, "dgate_q scales");
+  REQUIRE_PTR(du_codes, "dup_q codes");
+  REQUIRE_PTR(du_scales, "dup_q scales");
+  REQUIRE_PTR(dh, "dh");
+  REQUIRE_PTR(dgate, "dgate");
+  REQUIRE_PTR(dup, "dup");
+  REQUIRE(M <= 0x7FFFFFFF, PACT_EUNSUPPORTED, "M too large");
+  return hip_status(pact::launch_silu_mul_bwd_quant(g_codes, g_scales, nullptr, u_codes, u_scales, nullptr, dh, M, I,
+                                                    dgate, dup, dg_codes, dg_scales, nullptr, du_codes, du_scales,
+                                                    nullptr, 1, as_stream(stream)),
+                    "mxfp4_silu_mul_bwd_quant launch");
+}
+
+int mxfp4_rmsnorm_bwd_residual(const uint8_t* y_codes, const uint8_t* y_scales, const float* rstd,
+                               const uint16_t* gain, const uint16_t* dy, const uint16_t* resid, int64_t M, int64_t H,
+                               uint16_t* dx, uint8_t* q_codes, uint8_t* q_scales, void* stream) {
+  REQUIRE(M >= 0 && H >= 0, PACT_EINVAL, "negative size");
+  REQUIRE(H % 32 == 0, PACT_ESHAPE, "H=%lld is not a multiple of 32", (long long)H);
+  REQUIRE(H <= kMaxFusedCols, PACT_EUNSUPPORTED, "H=%lld exceeds %lld", (long long)H, (long long)kMaxFusedCols);
+  REQUIRE((q_codes == nullptr) == (q_scales == nullptr), PACT_EINVAL, "q_codes and q_scales: both or neither");
+  if (M == 0 || H == 0) return ok();
+  REQUIRE_PTR(y_codes, "y codes");
+  REQUIRE_PTR(y_scales, "y scales");
+  if (q_codes != nullptr) {
+    REQUIRE_PTR(q_codes, "out_q codes");
+    REQUIRE_PTR(q_scales, "out_q scales");
+  }
+  REQUIRE_PTR(rstd, "rstd");
+  REQUIRE_PTR(gain, "gain");
+  REQUIRE_PTR(dy, "dy");
+  REQUIRE_PTR(dx, "dx");
+  if (resid != nullptr) REQUIRE_PTR(resid, "resid");
+  REQUIRE(M <= 0x7FFFFFFF, PACT_EUNSUPPORTED, "M too large");
+  return hip_status(pact::launch_rmsnorm_bwd(y_codes, y_scales, nullptr, rstd, gain, dy, M, H, resid, dx, q_codes,
+                                             q_scales, nullptr, 1, as_stream(stream)),
+                    "mxfp4_rmsnorm_bwd_residual launch");
 }
 
 

@@ -19,6 +19,7 @@
 // Q(dgate), Q(dup) next to the BF16 gradients the LoRA backward needs, and
 // rmsnorm_bwd_residual adds the incoming residual gradient in BF16
 // (out = bf16(bf16(dx) + resid)) and can emit Q(out).
+#include "mxfp4_device.h"
 #include "pact_internal.h"
 #include "row_ops.h"
 
@@ -76,8 +77,9 @@ __global__ __launch_bounds__(256) void k_silu_mul_bwd(const uint8_t* __restrict_
 
 // silu_mul_bwd with NVFP4 copies of both gradients: one 256-thread workgroup
 // per row, NCH chunks per thread kept (as BF16) in registers until the row
-// maxima are known.
-template <int NCH>
+// maxima are known.  MX: the saved state and the copies are MXFP4 (32-element
+// blocks, E8M0 scales, no row scales: gr, ur, qgr, qur unused, no row maxima).
+template <int NCH, bool MX>
 __global__ __launch_bounds__(256) void k_silu_mul_bwd_quant(
     const uint8_t* __restrict__ gc, const uint8_t* __restrict__ gs, const float* __restrict__ gr,
     const uint8_t* __restrict__ uc, const uint8_t* __restrict__ us, const float* __restrict__ ur,
@@ -87,7 +89,8 @@ __global__ __launch_bounds__(256) void k_silu_mul_bwd_quant(
   __shared__ float red[4];
   const int64_t row = blockIdx.x;
   const int nchunk = (int)(I >> 3);
-  const float rg = gr[row], ru = ur[row];
+  const float rg = MX ? 1.0f : gr[row], ru = MX ? 1.0f : ur[row];
+  constexpr int SSH = MX ? 5 : 4;                      // log2 of the block length
   uint4 oa[NCH], ob[NCH];
   float la = 0.0f, lb = 0.0f;
   // every chunk's inputs are loaded (branch-free) before any is used
@@ -100,16 +103,16 @@ __global__ __launch_bounds__(256) void k_silu_mul_bwd_quant(
     const int64_t q = row * nchunk + c;
     wg[i] = load_or_zero(reinterpret_cast<const uint32_t*>(gc) + q, reinterpret_cast<const uint32_t*>(gc), ok);
     wu[i] = load_or_zero(reinterpret_cast<const uint32_t*>(uc) + q, reinterpret_cast<const uint32_t*>(uc), ok);
-    sg[i] = load_or_zero(gs + row * (I >> 4) + (c >> 1), gs, ok);
-    su[i] = load_or_zero(us + row * (I >> 4) + (c >> 1), us, ok);
+    sg[i] = load_or_zero(gs + row * (I >> SSH) + (c >> (SSH - 3)), gs, ok);
+    su[i] = load_or_zero(us + row * (I >> SSH) + (c >> (SSH - 3)), us, ok);
     vdh[i] = load_or_zero(reinterpret_cast<const uint4*>(dh + row * I + 8 * c), reinterpret_cast<const uint4*>(dh), ok);
   }
 #pragma unroll
   for (int i = 0; i < NCH; ++i) {
     const int c = threadIdx.x + 256 * i;
     if (c < nchunk) {
-      const float ma = e4m3_decode(sg[i]) * rg;
-      const float mb = e4m3_decode(su[i]) * ru;
+      const float ma = MX ? e8m0_decode(sg[i]) : e4m3_decode(sg[i]) * rg;
+      const float mb = MX ? e8m0_decode(su[i]) : e4m3_decode(su[i]) * ru;
       silu_bwd_chunk(wg[i], ma, wu[i], mb, vdh[i], oa[i], ob[i]);
       *reinterpret_cast<uint4*>(dgate + row * I + 8 * c) = oa[i];
       *reinterpret_cast<uint4*>(dup + row * I + 8 * c) = ob[i];
@@ -119,6 +122,18 @@ __global__ __launch_bounds__(256) void k_silu_mul_bwd_quant(
       oa[i] = make_uint4(0, 0, 0, 0);
       ob[i] = make_uint4(0, 0, 0, 0);
     }
+  }
+  if constexpr (MX) {
+#pragma unroll
+    for (int i = 0; i < NCH; ++i) {
+      const int c = threadIdx.x + 256 * i;
+      float f[8];
+      unpack_bf16x8(oa[i], f);
+      mx_quant_chunk(f, c < nchunk, qgc + row * (I >> 1), qgs + row * (I >> 5), c);
+      unpack_bf16x8(ob[i], f);
+      mx_quant_chunk(f, c < nchunk, quc + row * (I >> 1), qus + row * (I >> 5), c);
+    }
+    return;
   }
   const float amax_a = block_max_256(la, red);
   const float amax_b = block_max_256(lb, red);
@@ -145,7 +160,9 @@ __global__ __launch_bounds__(256) void k_silu_mul_bwd_quant(
 // wave p owns the 16-element blocks l + 64 p + 64 WPR i.  Between passes it
 // keeps the raw codes, scale byte and BF16 bits of its blocks and decodes them
 // again where needed (the same operations, so the same values).
-template <int NB, int WPR>
+// MX: y_q and the copy are MXFP4 (32-element blocks on lanes 2p, 2p + 1, E8M0
+// scales; yr and qr unused).
+template <int NB, int WPR, bool MX>
 __global__ __launch_bounds__(256) void k_rmsnorm_bwd(const uint8_t* __restrict__ yc, const uint8_t* __restrict__ ys,
                                                      const float* __restrict__ yr, const float* __restrict__ rstd,
                                                      const uint16_t* __restrict__ gain, const uint16_t* __restrict__ dy,
@@ -160,7 +177,7 @@ __global__ __launch_bounds__(256) void k_rmsnorm_bwd(const uint8_t* __restrict__
   const bool row_ok = row0 < M;                        // uniform per wave (no early exit: barriers below)
   const int64_t row = row_ok ? row0 : 0;
   const int nblk = (int)(H >> 4);
-  const float rr = yr[row];
+  const float rr = MX ? 1.0f : yr[row];
   uint2 cw[NB];                                        // 16 codes
   float sm[NB];                                        // block scale * row scale
   uint4 dv[NB][2];                                     // 16 BF16 dy
@@ -171,12 +188,15 @@ __global__ __launch_bounds__(256) void k_rmsnorm_bwd(const uint8_t* __restrict__
     const int blk = lane + 64 * part + 64 * WPR * i;
     const bool ok = row_ok && blk < nblk;
     cw[i] = ok ? *reinterpret_cast<const uint2*>(yc + row * (H >> 1) + 8 * blk) : make_uint2(0, 0);
-    sb[i] = load_or_zero(ys + row * (H >> 4) + blk, ys, ok);      // decoded once every load is issued
+    sb[i] = MX ? load_or_zero(ys + row * (H >> 5) + (blk >> 1), ys, ok)
+               : load_or_zero(ys + row * (H >> 4) + blk, ys, ok);      // decoded once every load is issued
     dv[i][0] = ok ? load16(dy + row * H + 16 * blk) : make_uint4(0, 0, 0, 0);
     dv[i][1] = ok ? load16(dy + row * H + 16 * blk + 8) : make_uint4(0, 0, 0, 0);
   }
 #pragma unroll
-  for (int i = 0; i < NB; ++i) sm[i] = row_ok && lane + 64 * part + 64 * WPR * i < nblk ? e4m3_decode(sb[i]) * rr : 0.0f;
+  for (int i = 0; i < NB; ++i)
+    sm[i] = row_ok && lane + 64 * part + 64 * WPR * i < nblk ? (MX ? e8m0_decode(sb[i]) : e4m3_decode(sb[i]) * rr)
+                                                             : 0.0f;
 #pragma unroll
   for (int i = 0; i < NB; ++i) {
 #pragma unroll
@@ -247,7 +267,19 @@ __global__ __launch_bounds__(256) void k_rmsnorm_bwd(const uint8_t* __restrict__
       lmax = fmaxf(lmax, absmax_bf16x8(v));
     }
   }
-  if (qc != nullptr) {                                 // uniform: a kernel argument
+  if (MX && qc != nullptr) {
+    if (!row_ok) return;
+#pragma unroll
+    for (int i = 0; i < NB; ++i) {
+      const int blk = lane + 64 * part + 64 * WPR * i;
+      float f[16];
+      unpack_bf16x8(out[i][0], f);
+      unpack_bf16x8(out[i][1], f + 8);
+      mx_quant_half(f, fmaxf(absmax8(f), absmax8(f + 8)), blk < nblk, qc + row * (H >> 1), qs + row * (H >> 5), blk);
+    }
+    return;
+  }
+  if (!MX && qc != nullptr) {                          // uniform: a kernel argument
     float amax = wave_max(lmax);
     if constexpr (WPR > 1) {
       if (lane == 0) red[wave] = amax;
@@ -286,10 +318,16 @@ hipError_t launch_silu_mul_bwd(const uint8_t* gc, const uint8_t* gs, const float
 hipError_t launch_silu_mul_bwd_quant(const uint8_t* gc, const uint8_t* gs, const float* gr, const uint8_t* uc,
                                      const uint8_t* us, const float* ur, const uint16_t* dh, int64_t M, int64_t I,
                                      uint16_t* dgate, uint16_t* dup, uint8_t* qgc, uint8_t* qgs, float* qgr,
-                                     uint8_t* quc, uint8_t* qus, float* qur, hipStream_t s) {
+                                     uint8_t* quc, uint8_t* qus, float* qur, int mx, hipStream_t s) {
   const int nch = (int)(((I >> 3) + 255) / 256);
   const dim3 grid((unsigned)M);
-#define PACT_SMBQ(n) k_silu_mul_bwd_quant<n><<<grid, 256, 0, s>>>(gc, gs, gr, uc, us, ur, dh, I, dgate, dup, qgc, qgs, qgr, quc, qus, qur)
+#define PACT_SMBQ(n)                                                                                         \
+  do {                                                                                                      \
+    if (mx) k_silu_mul_bwd_quant<n, true><<<grid, 256, 0, s>>>(gc, gs, gr, uc, us, ur, dh, I, dgate, dup, qgc, qgs,  \
+                                                              qgr, quc, qus, qur);                          \
+    else k_silu_mul_bwd_quant<n, false><<<grid, 256, 0, s>>>(gc, gs, gr, uc, us, ur, dh, I, dgate, dup, qgc, qgs,    \
+                                                             qgr, quc, qus, qur);                           \
+  } while (0)
   if (nch <= 1) PACT_SMBQ(1);
   else if (nch <= 2) PACT_SMBQ(2);
   else if (nch <= 4) PACT_SMBQ(4);
@@ -301,7 +339,7 @@ hipError_t launch_silu_mul_bwd_quant(const uint8_t* gc, const uint8_t* gs, const
 
 hipError_t launch_rmsnorm_bwd(const uint8_t* yc, const uint8_t* ys, const float* yr, const float* rstd,
                               const uint16_t* gain, const uint16_t* dy, int64_t M, int64_t H,
-                              const uint16_t* resid, uint16_t* dx, uint8_t* qc, uint8_t* qs, float* qr,
+                              const uint16_t* resid, uint16_t* dx, uint8_t* qc, uint8_t* qs, float* qr, int mx,
                               hipStream_t s) {
   // the quantizer's row layout: blocks per lane <= 4 (one wave per row up to
   // 4096 columns, two up to 8192, four up to 16384)
@@ -310,8 +348,11 @@ hipError_t launch_rmsnorm_bwd(const uint8_t* yc, const uint8_t* ys, const float*
   const int wpr = nblk <= 256 ? 1 : (nblk <= 512 ? 2 : 4);
   const int64_t nb = (nblk + 64 * wpr - 1) / (64 * wpr);
   const dim3 grid((unsigned)((M + 4 / wpr - 1) / (4 / wpr)));
-#define PACT_RMSB(N, W) \
-  k_rmsnorm_bwd<N, W><<<grid, 256, 0, s>>>(yc, ys, yr, rstd, gain, dy, M, H, resid, dx, qc, qs, qr)
+#define PACT_RMSB(N, W)                                                                                     \
+  do {                                                                                                     \
+    if (mx) k_rmsnorm_bwd<N, W, true><<<grid, 256, 0, s>>>(yc, ys, yr, rstd, gain, dy, M, H, resid, dx, qc, qs, qr); \
+    else k_rmsnorm_bwd<N, W, false><<<grid, 256, 0, s>>>(yc, ys, yr, rstd, gain, dy, M, H, resid, dx, qc, qs, qr);  \
+  } while (0)
   if (wpr == 1 && nb <= 1) PACT_RMSB(1, 1);
   else if (wpr == 1 && nb <= 2) PACT_RMSB(2, 1);
   else if (wpr == 1 && nb <= 3) PACT_RMSB(3, 1);

@@ -36,6 +36,12 @@ __device__ __forceinline__ uint32_t mx_encode8(const float* x, float inv) {
   return w;
 }
 
+// Value of an E8M0 scale byte b (0..254): 2^(b - 127), exact in FP32 (b = 0 is
+// the subnormal 2^-127).
+__device__ __forceinline__ float e8m0_decode(uint32_t b) {
+  return b != 0u ? __uint_as_float(b << 23) : __uint_as_float(0x00400000u);
+}
+
 // 2^-e as FP32 for e in [-127, 125] (a normal number)
 __device__ __forceinline__ float mx_inv_scale(int e) { return __uint_as_float((uint32_t)(127 - e) << 23); }
 

@@ -110,12 +110,13 @@ hipError_t launch_silu_mul_bwd(const uint8_t* gc, const uint8_t* gs, const float
 hipError_t launch_silu_mul_bwd_quant(const uint8_t* gc, const uint8_t* gs, const float* gr, const uint8_t* uc,
                                      const uint8_t* us, const float* ur, const uint16_t* dh, int64_t M, int64_t I,
                                      uint16_t* dgate, uint16_t* dup, uint8_t* qgc, uint8_t* qgs, float* qgr,
-                                     uint8_t* quc, uint8_t* qus, float* qur, hipStream_t s);
+                                     uint8_t* quc, uint8_t* qus, float* qur, int mx, hipStream_t s);
 
-// dx = bf16(rmsnorm backward) [+ resid, rounded again to BF16]; qc == nullptr: no NVFP4 copy
+// dx = bf16(rmsnorm backward) [+ resid, rounded again to BF16]; qc == nullptr: no copy.
+// mx: y_q and the copy are MXFP4 (yr, qr unused)
 hipError_t launch_rmsnorm_bwd(const uint8_t* yc, const uint8_t* ys, const float* yr, const float* rstd,
                               const uint16_t* gain, const uint16_t* dy, int64_t M, int64_t H,
-                              const uint16_t* resid, uint16_t* dx, uint8_t* qc, uint8_t* qs, float* qr,
+                              const uint16_t* resid, uint16_t* dx, uint8_t* qc, uint8_t* qs, float* qr, int mx,
                               hipStream_t s);
 
 hipError_t launch_mx_quantize(const uint16_t* x, int64_t rows, int64_t cols, int64_t ldx, int transpose,

@@ -458,6 +458,31 @@ int mxfp4_silu_mul_quant(const uint16_t *gate, const uint16_t *up, int64_t M, in
                          uint8_t *u_codes, uint8_t *u_scales, void *stream);
 
 /*
+ * mxfp4_silu_mul_bwd_quant -- silu_mul_bwd_quant from an MXFP4 state with
+ * MXFP4 copies (Appendix Table 7 row "SiLU-multiply", backward column, with
+ * the Table 6 MXFP4 format): a^ = deq(gate_q), b^ = deq(up_q) (MXFP4
+ * [M x I]), the same pinned FP32 sequence as silu_mul_bwd for the BF16 dgate,
+ * dup [M x I] (dense rows), and dgate_q = MXFP4(dgate), dup_q = MXFP4(dup).
+ * I % 32 == 0, I <= 16384.
+ */
+int mxfp4_silu_mul_bwd_quant(const uint8_t *g_codes, const uint8_t *g_scales, const uint8_t *u_codes,
+                             const uint8_t *u_scales, const uint16_t *dh, int64_t M, int64_t I, uint16_t *dgate,
+                             uint16_t *dup, uint8_t *dg_codes, uint8_t *dg_scales, uint8_t *du_codes,
+                             uint8_t *du_scales, void *stream);
+
+/*
+ * mxfp4_rmsnorm_bwd_residual -- rmsnorm_bwd_residual from an MXFP4 state
+ * (Appendix Table 7 rows "RMSNorm" and "Residuals", backward column, with the
+ * Table 6 MXFP4 format): y^ = deq(y_q) (MXFP4 [M x H]), the same FP32 sequence
+ * as rmsnorm_bwd, out = bf16(fp32(bf16(dx)) + resid) (resid may be NULL),
+ * and, when q_codes and q_scales are given, out_q = MXFP4(out).
+ * H % 32 == 0, H <= 16384.
+ */
+int mxfp4_rmsnorm_bwd_residual(const uint8_t *y_codes, const uint8_t *y_scales, const float *rstd,
+                               const uint16_t *gain, const uint16_t *dy, const uint16_t *resid, int64_t M, int64_t H,
+                               uint16_t *dx, uint8_t *q_codes, uint8_t *q_scales, void *stream);
+
+/*
  * mxfp4_gemm -- C = A B^T for MXFP4 A [M x K] and B [N x K] (forward: X_q and
  * W_fwd = Q(W); input gradient: dY_q [M x N] and W_bwd = Q(W^T) [K x N]), on
  * the scaled FP4 matrix instructions with FP32 accumulation (Appendix Table 7

@@ -45,7 +45,13 @@ from .tolerance import bf16_rne
 
 
 def rmsnorm_bwd(yq: NVFP4, rstd, g, dy):
-    yh = dequantize(yq)
+    return rmsnorm_bwd_values(dequantize(yq), rstd, g, dy)
+
+
+def rmsnorm_bwd_values(yh, rstd, g, dy):
+    """float64 RMSNorm input gradient and its cancellation magnitude from the
+    reconstructed output values yh (any format's dequantization)."""
+    yh = np.asarray(yh, dtype=np.float64)
     rstd = np.asarray(rstd, dtype=np.float64)[:, None]
     g = np.asarray(g, dtype=np.float64)[None, :]
     dy = np.asarray(dy, dtype=np.float64)
@@ -64,8 +70,14 @@ def _sigmoid(x):
 
 
 def silu_mul_bwd(aq: NVFP4, bq: NVFP4, dh):
-    ah = dequantize(aq)
-    bh = dequantize(bq)
+    return silu_mul_bwd_values(dequantize(aq), dequantize(bq), dh)
+
+
+def silu_mul_bwd_values(ah, bh, dh):
+    """float64 SiLU-multiply gradients and cancellation magnitudes from the
+    reconstructed gate and up values (any format's dequantization)."""
+    ah = np.asarray(ah, dtype=np.float64)
+    bh = np.asarray(bh, dtype=np.float64)
     dh = np.asarray(dh, dtype=np.float64)
     sig = _sigmoid(ah)
     da = dh * bh * sig * (1.0 + ah * (1.0 - sig))
@@ -82,8 +94,13 @@ def to_bf16_f32(x) -> np.ndarray:
 
 def silu_mul_bwd_f32(aq: NVFP4, bq: NVFP4, dh):
     """(dgate, dup) as BF16 values (float32) from the pinned FP32 sequence."""
-    a = dequantize(aq).astype(np.float32)      # exact: short-mantissa values
-    b = dequantize(bq).astype(np.float32)
+    return silu_mul_bwd_f32_values(dequantize(aq), dequantize(bq), dh)
+
+
+def silu_mul_bwd_f32_values(ah, bh, dh):
+    """The pinned FP32 sequence on reconstructed gate/up values (exact in FP32)."""
+    a = np.asarray(ah, dtype=np.float64).astype(np.float32)      # exact: short-mantissa values
+    b = np.asarray(bh, dtype=np.float64).astype(np.float32)
     d = np.asarray(dh, dtype=np.float32)
     one = np.float32(1.0)
     with np.errstate(over="ignore"):
@@ -101,7 +118,11 @@ def silu_mul_bwd_quant(aq: NVFP4, bq: NVFP4, dh):
 
 def rmsnorm_mean_f32(yq: NVFP4, dy) -> np.ndarray:
     """Per-row fp32(S / H) with S = sum_j dy_j y^_j rounded once to float64."""
-    y = dequantize(yq)
+    return rmsnorm_mean_f32_values(dequantize(yq), dy)
+
+
+def rmsnorm_mean_f32_values(yh, dy) -> np.ndarray:
+    y = np.asarray(yh, dtype=np.float64)
     d = np.asarray(dy, dtype=np.float32).astype(np.float64)
     prod = d * y                               # exact: 8 + 6 significant bits
     S = np.array([math.fsum(row) for row in prod], dtype=np.float64)
@@ -110,11 +131,15 @@ def rmsnorm_mean_f32(yq: NVFP4, dy) -> np.ndarray:
 
 def rmsnorm_bwd_f32(yq: NVFP4, rstd, g, dy) -> np.ndarray:
     """dx as BF16 values (float32) from the pinned FP32 sequence."""
-    y = dequantize(yq).astype(np.float32)
+    return rmsnorm_bwd_f32_values(dequantize(yq), rstd, g, dy)
+
+
+def rmsnorm_bwd_f32_values(yh, rstd, g, dy) -> np.ndarray:
+    y = np.asarray(yh, dtype=np.float64).astype(np.float32)
     d = np.asarray(dy, dtype=np.float32)
     gg = np.asarray(g, dtype=np.float32)[None, :]
     rs = np.asarray(rstd, dtype=np.float32)[:, None]
-    mean = rmsnorm_mean_f32(yq, dy)[:, None]
+    mean = rmsnorm_mean_f32_values(yh, dy)[:, None]
     dx = rs * ((gg * d) - ((y / gg) * mean))
     return to_bf16_f32(dx)
 

@@ -136,3 +136,26 @@ def silu_mul_quant(a, b):
     b = np.asarray(b, dtype=np.float32)
     h = (silu_f32(a) * b).astype(np.float32)
     return (quantize(h.astype(np.float64)), quantize(a.astype(np.float64)), quantize(b.astype(np.float64)), h)
+
+
+def silu_mul_bwd_quant(aq: MXFP4, bq: MXFP4, dh):
+    """SiLU-multiply backward from an MXFP4 state with MXFP4 copies:
+    (dgate, dup, Q_mx(dgate), Q_mx(dup)).  The BF16 gradients follow the NVFP4
+    path's pinned FP32 sequence (backward.silu_mul_bwd_f32_values) on the
+    dequantized MXFP4 gate and up values.  Appendix Table 7 row
+    "SiLU-multiply" with the Table 6 MXFP4 format."""
+    from .backward import silu_mul_bwd_f32_values
+    da, db = silu_mul_bwd_f32_values(dequantize(aq), dequantize(bq), dh)
+    return da, db, quantize(da.astype(np.float64)), quantize(db.astype(np.float64))
+
+
+def rmsnorm_bwd_residual(yq: MXFP4, rstd, g, dy, resid=None):
+    """RMSNorm backward from an MXFP4 state (+ BF16 residual gradient) with an
+    MXFP4 copy: (out, Q_mx(out)), out = bf16(bf16(dx) + resid), dx in the
+    NVFP4 path's pinned FP32 sequence (backward.rmsnorm_bwd_f32_values) on the
+    dequantized MXFP4 values.  Appendix Table 7 rows "RMSNorm" and "Residuals"
+    with the Table 6 MXFP4 format."""
+    from .backward import residual_add_bf16, rmsnorm_bwd_f32_values
+    dx = rmsnorm_bwd_f32_values(dequantize(yq), rstd, g, dy)
+    out = dx if resid is None else residual_add_bf16(dx, resid)
+    return out, quantize(out.astype(np.float64))

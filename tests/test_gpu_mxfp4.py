@@ -265,3 +265,51 @@ def test_mx_fused_strided_and_validation(fw):
     p = t.data_ptr()
     assert lib.mxfp4_silu_mul_quant(p, p, 4, 48, 48, p, p, p, p, p, p, None) == -2
     assert lib.mxfp4_rmsnorm_quant(p, p, 1e-5, 4, 48, 48, p, p, p, None) == -2
+
+
+# ---------------------------------------------------------------- backward from an MXFP4 state
+def _as_values_f32(bits):
+    return bf16_values(bits).astype(np.float32)
+
+
+@pytest.mark.parametrize("M,I", [(64, 256), (33, 8192), (5, 14336), (2, 96), (2048, 8192)])
+def test_mx_silu_mul_bwd_quant(fw, M, I):
+    """BF16 gradients and their MXFP4 copies bit-exact against the oracle's
+    pinned sequence on the dequantized MXFP4 gate/up state (sampled rows at
+    the MLP-block width)."""
+    a = synth.normal_bf16((M, I), 2.0, 99, I + 11)
+    b = synth.normal_bf16((M, I), 1.0, 99, I + 12)
+    dh = synth.normal_bf16((M, I), 0.01, 99, I + 13)
+    aq, bq = _ox(a), _ox(b)
+    dg, du, dgq, duq = fw.mx_silu_mul_bwd_quant(_to_gpu(aq), _to_gpu(bq), bits_to_torch(dh))
+    rows = np.arange(M) if M <= 64 else np.sort(np.random.default_rng(I).choice(M, size=64, replace=False))
+    sel = lambda q: omx.MXFP4(q.codes[rows], q.scales[rows])
+    da, db, daq, dbq = omx.silu_mul_bwd_quant(sel(aq), sel(bq), _as_values_f32(dh[rows]))
+    got_a = dg.contiguous().view(torch.int16).cpu().numpy().view(np.uint16)[rows]
+    got_b = du.contiguous().view(torch.int16).cpu().numpy().view(np.uint16)[rows]
+    assert np.array_equal(bf16_values(got_a).view(np.uint32), da.view(np.uint32)), "dgate"
+    assert np.array_equal(bf16_values(got_b).view(np.uint32), db.view(np.uint32)), "dup"
+    _assert_equal(dgq, daq, "dgate copy", rows=rows)
+    _assert_equal(duq, dbq, "dup copy", rows=rows)
+
+
+@pytest.mark.parametrize("M,H,resid,copy", [(64, 256, True, True), (33, 3072, True, True), (9, 8192, False, True),
+                                             (17, 16384, True, False), (3, 96, True, True), (4096, 3072, True, True)])
+def test_mx_rmsnorm_bwd_residual(fw, M, H, resid, copy):
+    x = synth.activations_bf16((M, H), 99, 900 + H)
+    g = synth.uniform_bf16((H,), 0.9, 1.1, 99, 901 + H)
+    yq, rstd = omx.rmsnorm_quant(bf16_values(x), bf16_values(g), 1e-5)[:2]
+    dy = synth.normal_bf16((M, H), 0.01, 99, 902 + H)
+    rs = synth.normal_bf16((M, H), 0.01, 99, 903 + H) if resid else None
+    out, q = fw.mx_rmsnorm_bwd_residual(_to_gpu(yq), torch.from_numpy(rstd).to(dev()), bits_to_torch(g),
+                                        bits_to_torch(dy), resid=bits_to_torch(rs) if resid else None,
+                                        quantize_out=copy)
+    rows = np.arange(M) if M <= 64 else np.sort(np.random.default_rng(H).choice(M, size=64, replace=False))
+    ref, refq = omx.rmsnorm_bwd_residual(omx.MXFP4(yq.codes[rows], yq.scales[rows]), rstd[rows], bf16_values(g),
+                                         _as_values_f32(dy[rows]), _as_values_f32(rs[rows]) if resid else None)
+    got = out.contiguous().view(torch.int16).cpu().numpy().view(np.uint16)[rows]
+    assert np.array_equal(bf16_values(got).view(np.uint32), ref.view(np.uint32)), "out"
+    if copy:
+        _assert_equal(q, refq, "out copy", rows=rows)
+    else:
+        assert q is None

@@ -261,3 +261,64 @@ def test_mx_silu_mul_quant_against_brute_force_and_closed_forms():
     # the zero block: scale byte 0 (e = -127), every code the sign bit alone
     assert hq.scales[3, 0] == 0
     assert set(onv.unpack_codes(hq.codes)[3, :32].tolist()) == {8}
+
+
+# ---------------------------------------------------------------------------
+# backward operators from an MXFP4 state (SiLU-multiply, RMSNorm + residual)
+# ---------------------------------------------------------------------------
+def _twin_states(rng, R, C):
+    """An MXFP4 tensor and an NVFP4 tensor with identical dequantized values:
+    the same codes, MXFP4 scale byte b_i on every block of row i, NVFP4 block
+    scales 1.0 (0x38) and row scale 2^(b_i - 127)."""
+    codes = rng.integers(0, 16, size=(R, C))
+    packed = (codes[:, 0::2] | (codes[:, 1::2] << 4)).astype(np.uint8)
+    b = rng.integers(118, 132, size=R)
+    mx = omx.MXFP4(packed, np.repeat(b[:, None], C // 32, axis=1).astype(np.uint8))
+    nv = onv.NVFP4(packed.copy(), np.full((R, C // 16), 0x38, np.uint8), np.ldexp(1.0, b - 127).astype(np.float32))
+    assert np.array_equal(omx.dequantize(mx), onv.dequantize(nv))
+    return mx, nv
+
+
+def test_mx_silu_mul_bwd_matches_nvfp4_path_on_equal_values():
+    """The MXFP4 backward is the NVFP4 path's pinned sequence on the
+    reconstructed values: on twin states the BF16 gradients are identical, the
+    MXFP4 copies equal the exact-rational quantization of those gradients, and
+    both lie within the float64 derivatives' bound."""
+    from oracle import backward as obwd
+    from oracle import tolerance as tol
+    rng = np.random.default_rng(161)
+    R, C = 5, 96
+    amx, anv = _twin_states(rng, R, C)
+    bmx, bnv = _twin_states(rng, R, C)
+    dh = (rng.standard_normal((R, C)) * 0.01).astype(np.float32)
+    dh = (dh.view(np.uint32) & 0xFFFF0000).view(np.float32)
+    da, db, daq, dbq = omx.silu_mul_bwd_quant(amx, bmx, dh)
+    da_nv, db_nv = obwd.silu_mul_bwd_f32(anv, bnv, dh)
+    assert np.array_equal(da.view(np.uint32), da_nv.view(np.uint32))
+    assert np.array_equal(db.view(np.uint32), db_nv.view(np.uint32))
+    for q, v in ((daq, da), (dbq, db)):
+        sb, cb = _brute_rows(v.astype(np.float64))
+        assert np.array_equal(q.scales, sb) and np.array_equal(onv.unpack_codes(q.codes), cb)
+    ref_a, ref_b, ca, cb_ = obwd.silu_mul_bwd_values(omx.dequantize(amx), omx.dequantize(bmx), dh)
+    assert tol.violations(da, ref_a, tol.grad_bound(ref_a, ca))[0] == 0
+    assert tol.violations(db, ref_b, tol.grad_bound(ref_b, cb_))[0] == 0
+
+
+def test_mx_rmsnorm_bwd_residual_matches_nvfp4_path_on_equal_values():
+    from oracle import backward as obwd
+    rng = np.random.default_rng(162)
+    R, H = 4, 128
+    ymx, ynv = _twin_states(rng, R, H)
+    rstd = rng.uniform(0.5, 2.0, R).astype(np.float32)
+    g = rng.uniform(0.9, 1.1, H).astype(np.float32)
+    g = (g.view(np.uint32) & 0xFFFF0000).view(np.float32)
+    dy = (rng.standard_normal((R, H)) * 0.01).astype(np.float32)
+    dy = (dy.view(np.uint32) & 0xFFFF0000).view(np.float32)
+    resid = (rng.standard_normal((R, H)) * 0.01).astype(np.float32)
+    resid = (resid.view(np.uint32) & 0xFFFF0000).view(np.float32)
+    for res in (None, resid):
+        out, outq = omx.rmsnorm_bwd_residual(ymx, rstd, g, dy, res)
+        out_nv, _ = obwd.rmsnorm_bwd_residual(ynv, rstd, g, dy, res)
+        assert np.array_equal(out.view(np.uint32), out_nv.view(np.uint32))
+        sb, cb = _brute_rows(out.astype(np.float64))
+        assert np.array_equal(outq.scales, sb) and np.array_equal(onv.unpack_codes(outq.codes), cb)
