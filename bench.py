@@ -952,6 +952,177 @@ def mxfp4_leg(fw, torch, synth, wl, nlayers, steps, warmup, eager=False):
                          "avg_launch_us": round(dt * 1e3 / dn, 2), "traffic": traffic}}
 
 
+class MxMlpBlock:
+    """One MLP block of the workload entirely in the MXFP4 variant: cached MXFP4
+    W_fwd / W_bwd of gate, up and down (gate and up stacked in the forward
+    layout), MXFP4 RMSNorm and SiLU-multiply quantizers, MXFP4 copies of every
+    GEMM input, backward chained through the BF16 residual gradient.  No LoRA
+    branch: the MXFP4 variant is a format comparison of the frozen path."""
+
+    def __init__(self, fw, torch, synth, wl, index=0):
+        self.fw, self.torch = fw, torch
+        P = {p.name: p for p in wl.projections}
+        M, H, I = wl.tokens, P["gate"].d_in, P["gate"].d_out
+        self.M, self.H, self.I = M, H, I
+        dev = torch.device("cuda:0")
+        off, wid = 7000 + 1000 * index, wl.wid
+        self.x = synth.activation_torch(wl, M, H, off + 1)
+        self.g = synth.uniform_torch((H,), 0.9, 1.1, wid, off + 2)
+        self.dout = synth.normal_torch((M, H), wl.dy_std, wid, off + 3)
+        wg = synth.normal_torch((I, H), wl.w_std, wid, off + 4)
+        wu = synth.normal_torch((I, H), wl.w_std, wid, off + 5)
+        wd = synth.normal_torch((H, I), wl.w_std, wid, off + 6)
+        self.w_gu = fw.mx_quantize(torch.cat([wg, wu], 0).contiguous())       # [2I x H]
+        self.w_gate_b = fw.mx_quantize(wg, transpose=True)                   # [H x I]
+        self.w_up_b = fw.mx_quantize(wu, transpose=True)
+        self.w_down, self.w_down_b = fw.mx_weight_layouts(wd)               # [H x I], [I x H]
+        del wg, wu, wd
+        mx = lambda cols: fw.empty_mxfp4(M, cols, dev)
+        bf = lambda cols: torch.empty((M, cols), dtype=torch.bfloat16, device=dev)
+        self.yq, self.rstd = mx(H), torch.empty((M,), dtype=torch.float32, device=dev)
+        self.gu, self.out = bf(2 * I), bf(H)
+        self.hq, self.gq, self.uq = mx(I), mx(I), mx(I)
+        self.doutq, self.dh = mx(H), bf(I)
+        self.dg, self.du, self.dgq, self.duq = bf(I), bf(I), mx(I), mx(I)
+        self.dy, self.dx, self.dxq = bf(H), bf(H), mx(H)
+
+    def step(self):
+        fw, I = self.fw, self.I
+        fw.mx_rmsnorm_quant(self.x, self.g, 1e-5, out=(self.yq, self.rstd))
+        fw.mx_gemm(self.yq, self.w_gu, out=self.gu)
+        fw.mx_silu_mul_quant(self.gu[:, :I], self.gu[:, I:], out=(self.hq, self.gq, self.uq))
+        fw.mx_gemm(self.hq, self.w_down, out=self.out)
+        fw.mx_quantize(self.dout, out=self.doutq)
+        fw.mx_gemm(self.doutq, self.w_down_b, out=self.dh)
+        fw.mx_silu_mul_bwd_quant(self.gq, self.uq, self.dh, out=(self.dg, self.du, self.dgq, self.duq))
+        fw.mx_gemm(self.dgq, self.w_gate_b, out=self.dy)
+        fw.mx_gemm(self.duq, self.w_up_b, out=self.dy, accumulate=True)
+        fw.mx_rmsnorm_bwd_residual(self.yq, self.rstd, self.g, self.dy, resid=self.dout, out=(self.dx, self.dxq))
+
+    def gemm_flops(self):
+        return 12.0 * self.M * self.H * self.I          # 3 forward + 3 input-gradient GEMMs of M*H*I MACs
+
+
+def mxfp4_mlp_parity(torch, blk, nrows, seed):
+    """Stage-wise oracle parity of one MXFP4 MLP block's last step on `nrows`
+    sampled token rows: each stage from the device's own inputs to it."""
+    import numpy as np
+    from oracle import mxfp4 as omx
+    from oracle import tolerance as tol
+
+    M, I = blk.M, blk.I
+    rng = np.random.default_rng(seed)
+    rows = np.sort(rng.choice(M, size=min(nrows, M), replace=False))
+    rows[-1] = M - 1
+    ridx = torch.as_tensor(rows, device="cuda")
+    checks = []
+
+    def mx(q, all_rows=False):
+        c, s = (q.codes, q.scales) if all_rows else (q.codes.index_select(0, ridx), q.scales.index_select(0, ridx))
+        return omx.MXFP4(c.cpu().numpy(), s.cpu().numpy())
+
+    def vals(t, all_rows=False):
+        t = t if all_rows else t.index_select(0, ridx)
+        b = t.contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
+        return (b.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+
+    def same_mx(name, g, o):
+        ok = np.array_equal(g.codes, o.codes) and np.array_equal(g.scales, o.scales)
+        checks.append({"stage": name, "kind": "bit-exact", "ok": bool(ok)})
+
+    def same_vals(name, got, want):
+        ok = np.array_equal(np.asarray(got, np.float32).view(np.uint32), np.asarray(want, np.float32).view(np.uint32))
+        checks.append({"stage": name, "kind": "bit-exact", "ok": bool(ok)})
+
+    def within(name, got, ref, bound):
+        n, worst = tol.violations(got, ref, bound)
+        checks.append({"stage": name, "kind": "bound", "ok": n == 0, "worst_err_over_bound": round(worst, 4),
+                       "elements": int(np.size(ref))})
+
+    x, g = vals(blk.x).astype(np.float32), vals(blk.g, True).astype(np.float32)
+    yq, rstd, _ = omx.rmsnorm_quant(x, g, 1e-5)
+    same_mx("mx_rmsnorm_quant", mx(blk.yq), yq)
+    same_vals("mx_rmsnorm rstd", blk.rstd.index_select(0, ridx).cpu().numpy(), rstd)
+    ref, rabs = omx.gemm_nt(mx(blk.yq), mx(blk.w_gu, True))
+    within("mx fwd gate/up (stacked)", vals(blk.gu), ref, tol.gemm_bound(ref, rabs))
+    gu = vals(blk.gu).astype(np.float32)
+    hq, gq, uq, _ = omx.silu_mul_quant(gu[:, :I], gu[:, I:])
+    same_mx("mx_silu_mul_quant h", mx(blk.hq), hq)
+    same_mx("mx_silu_mul_quant gate copy", mx(blk.gq), gq)
+    same_mx("mx_silu_mul_quant up copy", mx(blk.uq), uq)
+    ref, rabs = omx.gemm_nt(mx(blk.hq), mx(blk.w_down, True))
+    within("mx fwd down", vals(blk.out), ref, tol.gemm_bound(ref, rabs))
+    dv = vals(blk.dout)
+    same_mx("mx_quantize (output gradient)", mx(blk.doutq), omx.quantize(dv))
+    ref, rabs = omx.gemm_nt(mx(blk.doutq), mx(blk.w_down_b, True))
+    within("mx dgrad down", vals(blk.dh), ref, tol.gemm_bound(ref, rabs))
+    dg, du, dgq, duq = omx.silu_mul_bwd_quant(mx(blk.gq), mx(blk.uq), vals(blk.dh))
+    same_vals("mx_silu_mul_bwd dgate", vals(blk.dg).astype(np.float32), dg)
+    same_vals("mx_silu_mul_bwd dup", vals(blk.du).astype(np.float32), du)
+    same_mx("mx_silu_mul_bwd dgate copy", mx(blk.dgq), dgq)
+    same_mx("mx_silu_mul_bwd dup copy", mx(blk.duq), duq)
+    # two launches, the second accumulating onto the first's BF16 output: one
+    # extra BF16 rounding of the gate partial on top of the GEMM bound
+    rg, ag = omx.gemm_nt(mx(blk.dgq), mx(blk.w_gate_b, True))
+    ru, au = omx.gemm_nt(mx(blk.duq), mx(blk.w_up_b, True))
+    within("mx dgrad gate + up", vals(blk.dy), rg + ru, tol.gemm_bound(rg + ru, ag + au, tol.ulp_bf16(rg)))
+    out, outq = omx.rmsnorm_bwd_residual(mx(blk.yq), blk.rstd.index_select(0, ridx).cpu().numpy(),
+                                         vals(blk.g, True), vals(blk.dy), dv)
+    same_vals("mx_rmsnorm_bwd_residual", vals(blk.dx).astype(np.float32), out)
+    same_mx("mx residual-gradient copy", mx(blk.dxq), outq)
+    ok = all(c["ok"] for c in checks)
+    return {"status": "pass" if ok else "FAIL", "rows_sampled": int(len(rows)), "checks": checks}
+
+
+def mxfp4_mlp_leg(fw, torch, synth, wl, nblocks, steps, warmup, check=True, nrows=8):
+    """The MXFP4 MLP block chain (forward and input-gradient, quantizers fused)
+    at the workload's shapes over `nblocks` distinct block instances, timed as
+    HIP-graph replays; GEMM TFLOP/s of the chain, its per-launch kernel times
+    and the stage-wise parity of the last replay."""
+    blocks = [MxMlpBlock(fw, torch, synth, wl, i) for i in range(nblocks)]
+
+    def step():
+        for b in blocks:
+            b.step()
+
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        step()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        step()
+    graph.replay()
+    torch.cuda.synchronize()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    for e0, e1 in evs:
+        e0.record()
+        graph.replay()
+        e1.record()
+    torch.cuda.synchronize()
+    st = stats([e0.elapsed_time(e1) for e0, e1 in evs])
+    flops = sum(b.gemm_flops() for b in blocks)
+    res = {"workload": f"{wl.name} MLP block in MXFP4 (rmsnorm+quant, stacked gate/up, silu-mul+quant, down; "
+                       f"backward: quantize dOut, down dgrad, silu-mul bwd+quant, gate and up dgrad, "
+                       f"rmsnorm bwd+residual+quant)",
+           "blocks": nblocks, "gemm_tflops": round(flops / (st["median"] * 1e-3) / 1e12, 1),
+           "ms_per_step": round(st["median"], 4), "ms_per_step_min": round(st["min"], 4),
+           "gemm_gflop_per_step": round(flops / 1e9, 1), "timed_region": "hip graph replays"}
+    del graph
+    torch.cuda.synchronize()
+    if check:
+        res["parity"] = mxfp4_mlp_parity(torch, blocks[0], nrows, 4321 + wl.wid)
+    del blocks
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+    return res
+
+
 def recipe_leg(fw, torch, synth, wl, n_inst=4, reps=5):
     """The recipe variants at the Llama-3B shapes (M = 4096), over n_inst
     rotating instances: the Q/K/V and gate/up forward and input-gradient GEMMs
@@ -1229,6 +1400,9 @@ def main():
         progress("MXFP4 leg")
         result["mxfp4_variant"] = mxfp4_leg(fw, torch, synth, wl, max(1, args.layers), min(args.steps, 30), 3,
                                             eager=args.eager)
+        progress("MXFP4 MLP block chain")
+        result["mxfp4_mlp_block"] = mxfp4_mlp_leg(fw, torch, synth, synth.WORKLOADS[3], 2, min(args.steps, 30), 3,
+                                                  check=not args.no_cpu_baseline)
     if not legs_off:
         # measured MFMA-loop peak beside the published dense peaks (no memory traffic in the loop)
         p16, c16 = fw.mfma_probe(0)
