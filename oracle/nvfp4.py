@@ -26,6 +26,17 @@ are silent are:
 All decisions are taken with exact comparisons: ``|x| / r`` is exact in
 float64 (``r`` is a power of two), and every threshold (a midpoint times a
 scale) has at most 7 significant bits, so it too is exact in float64.
+
+Recipe variant with a conventional FP32 tensor scale (the pages leave the
+second-level scale open; this is the usual two-level reading, with every
+rounding fixed so that the result is unique): for a tensor maximum ``amax``
+(an FP32 value), the stored scale is ``S = RN32(amax / 2688)`` raised to
+2**-126 if smaller (``S = 1`` when amax is 0), the encoding multiplier is
+``R = RN32(1 / S)``, and every element's scaled magnitude is the FP32 product
+``u = RN32(|x| * R)``.  Block scale and element code then follow the rules
+above on ``u`` in place of ``|x| / r`` (``s = RNE_E4M3(max u / 6)``, code =
+``RNE_E2M1(u / s)``), and every row's stored scale is ``S``.  ``u`` is an
+FP32 number, so the decisions are again exact comparisons in float64.
 """
 
 from __future__ import annotations
@@ -152,7 +163,23 @@ def e4m3_round_up_code(t_times6: np.ndarray) -> np.ndarray:
     return np.searchsorted(6.0 * E4M3_POS, t_times6, side="left").astype(np.uint8)
 
 
-def quantize(x, transpose: bool = False, round_up: bool = False, tensor_amax=None) -> NVFP4:
+def tensor_scale_fp32(amax):
+    """(S, R) of the FP32 tensor-scale recipe for a tensor maximum ``amax``
+    (an FP32 value >= 0): S = RN32(amax / 2688), at least 2**-126, or 1 when
+    amax == 0; R = RN32(1 / S).  numpy's float32 division is IEEE division
+    (correctly rounded to nearest even)."""
+    a = np.float32(amax)
+    if not np.isfinite(a) or a < 0:
+        raise ValueError("amax must be finite and >= 0")
+    if a == 0:
+        return np.float32(1.0), np.float32(1.0)
+    s = np.float32(a / np.float32(E2M1_MAX * E4M3_MAX))
+    s = max(s, np.float32(2.0 ** -126))
+    return np.float32(s), np.float32(np.float32(1.0) / s)
+
+
+def quantize(x, transpose: bool = False, round_up: bool = False, tensor_amax=None,
+             fp32_tensor_scale: bool = False) -> NVFP4:
     """Quantize a real matrix X [R x C] (C % 16 == 0) to canonical NVFP4.
 
     With ``transpose`` the input is X^T of the given matrix: rows of the result
@@ -162,7 +189,10 @@ def quantize(x, transpose: bool = False, round_up: bool = False, tensor_amax=Non
     smallest E4M3 value >= blockmax / (6 r) instead of the nearest (then no
     element saturates); ``tensor_amax`` (a real >= max |x|, or "auto" for
     max |x|) gives every row the one power-of-two scale the row rule assigns to
-    that maximum.
+    that maximum.  With ``fp32_tensor_scale`` (and ``tensor_amax``) the
+    tensor scale is instead the FP32 value S of ``tensor_scale_fp32`` and the
+    elements are scaled by the FP32 multiplier R (module docstring); ``x``
+    must then hold FP32-representable values.
     """
     x = np.asarray(x, dtype=np.float64)
     if transpose:
@@ -171,13 +201,22 @@ def quantize(x, transpose: bool = False, round_up: bool = False, tensor_amax=Non
         raise ValueError("quantize expects [rows x cols] with cols % 16 == 0")
     R, C = x.shape
     ax = np.abs(x)
+    if fp32_tensor_scale and tensor_amax is None:
+        raise ValueError("fp32_tensor_scale needs tensor_amax")
     if tensor_amax is None:
         e = row_exponent(ax.max(axis=1) if C else np.zeros(R))
     else:
         ta = (ax.max() if ax.size else 0.0) if isinstance(tensor_amax, str) else float(tensor_amax)
         e = np.full(R, int(row_exponent(np.array(ta))), dtype=np.int64)
-    inv_r = np.ldexp(1.0, -e)[:, None]
-    xr = ax * inv_r                                           # |x| / r, exact
+    if fp32_tensor_scale:
+        ax32 = ax.astype(np.float32)
+        if not np.array_equal(ax32.astype(np.float64), ax):
+            raise ValueError("fp32_tensor_scale needs FP32-representable inputs")
+        S, Rm = tensor_scale_fp32(ta)
+        xr = (ax32 * Rm).astype(np.float64)                   # u = RN32(|x| * R), exact in float64
+    else:
+        inv_r = np.ldexp(1.0, -e)[:, None]
+        xr = ax * inv_r                                       # |x| / r, exact
     blk = xr.reshape(R, C // BLOCK, BLOCK)
     bmax = blk.max(axis=2) if C else np.zeros((R, 0))
     # compare against 6*mid (or 6*value) exactly
@@ -189,7 +228,10 @@ def quantize(x, transpose: bool = False, round_up: bool = False, tensor_amax=Non
     code = (sign << 3) | mu
     code = code.reshape(R, C)
     packed = (code[:, 0::2] | (code[:, 1::2] << 4)).astype(np.uint8)
-    rscale = np.ldexp(np.float32(1.0), e.astype(np.int32)).astype(np.float32)
+    if fp32_tensor_scale:
+        rscale = np.full(R, S, dtype=np.float32)
+    else:
+        rscale = np.ldexp(np.float32(1.0), e.astype(np.int32)).astype(np.float32)
     return NVFP4(packed, scode.reshape(R, C // BLOCK), rscale)
 
 
