@@ -1181,7 +1181,12 @@ def recipe_leg(fw, torch, synth, wl, n_inst=4, reps=5):
     amax = torch.empty((), dtype=torch.float32, device=dev)
     variants = {"default": lambda x, q: fw.quantize(x, out=q),
                 "round_up_scales": lambda x, q: fw.quantize_ex(x, round_up=True, out=q),
-                "tensor_scale_two_pass": lambda x, q: fw.quantize_ex(x, tensor_scale=True, amax=amax, out=q)}
+                "tensor_scale_two_pass": lambda x, q: fw.quantize_ex(x, tensor_scale=True, amax=amax, out=q),
+                "fp32_tensor_scale_two_pass": lambda x, q: fw.quantize_ex(x, tensor_scale=True, fp32_scale=True,
+                                                                           amax=amax, out=q),
+                "fp32_tensor_scale_supplied_amax": lambda x, q: fw.quantize_ex(x, tensor_scale=True,
+                                                                                fp32_scale=True, amax=amax,
+                                                                                compute_amax=False, out=q)}
     qb = {}
     for name, f in variants.items():
         def fn(f=f):
@@ -1193,7 +1198,48 @@ def recipe_leg(fw, torch, synth, wl, n_inst=4, reps=5):
     out["quantizer_4096x3072"] = qb
     del xs, qs
     torch.cuda.synchronize()
+    out["fp32_tensor_scale_gemm"] = fp32_scale_gemm_leg(fw, torch, synth, wl, n_inst, reps)
     return out
+
+
+def fp32_scale_gemm_leg(fw, torch, synth, wl, n_inst=4, reps=5):
+    """The stacked gate/up forward GEMM ([4096 x 3072] x [16384 x 3072]^T, LoRA
+    rank 32) on operands of the default recipe (power-of-two row scales, fused
+    term in the direct-to-LDS kernel) and of the FP32 tensor-scale recipe: the
+    plain GEMM (same kernel) and with the term (register-staged kernel,
+    PACT_GEMM_ANY_ROW_SCALES)."""
+    M, H, I, r = wl.tokens, 3072, 8192, 32
+    dev = torch.device("cuda:0")
+    inst = []
+    for i in range(n_inst):
+        off = 9500 + 100 * i
+        x = synth.activation_torch(wl, M, H, off)
+        w = synth.normal_torch((2 * I, H), wl.w_std, wl.wid, off + 1)
+        d = {"x": fw.quantize(x), "w": fw.quantize(w),
+             "x32": fw.quantize_ex(x, tensor_scale=True, fp32_scale=True),
+             "w32": fw.quantize_ex(w, tensor_scale=True, fp32_scale=True),
+             "t": synth.normal_torch((M, r), 0.3, wl.wid, off + 2),
+             "b": synth.normal_torch((2 * I, r), 0.01, wl.wid, off + 3),
+             "y": torch.empty((M, 2 * I), dtype=torch.bfloat16, device=dev)}
+        del x, w
+        inst.append(d)
+    runs = {"default_recipe_with_lora": lambda d: fw.gemm_fwd(d["x"], d["w"], lora_t=d["t"], lora_b=d["b"],
+                                                              lora_scale=LORA_SCALE, out=d["y"]),
+            "fp32_tensor_scale_no_lora": lambda d: fw.gemm_fwd(d["x32"], d["w32"], out=d["y"]),
+            "fp32_tensor_scale_with_lora": lambda d: fw.gemm_fwd(d["x32"], d["w32"], lora_t=d["t"], lora_b=d["b"],
+                                                                 lora_scale=LORA_SCALE, out=d["y"],
+                                                                 any_row_scales=True)}
+    flops = 2.0 * M * H * 2 * I
+    res = {}
+    for name, f in runs.items():
+        def fn(f=f):
+            for d in inst:
+                f(d)
+        t = timed_best(torch, fn, reps, len(inst))
+        res[name] = {"us": round(t * 1e3, 1), "tflops": round(flops / (t * 1e-3) / 1e12, 1)}
+    del inst
+    torch.cuda.synchronize()
+    return res
 
 
 def quantizer_leg(fw, torch, reps=5):

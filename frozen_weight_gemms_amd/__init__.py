@@ -89,13 +89,18 @@ def quantize(x: torch.Tensor, transpose: bool = False, out: NVFP4Tensor | None =
 QUANT_ROUND_UP_SCALES = 1
 QUANT_TENSOR_SCALE = 2
 QUANT_COMPUTE_AMAX = 4
+QUANT_TENSOR_SCALE_FP32 = 8
 
 
 def quantize_ex(x: torch.Tensor, transpose: bool = False, round_up: bool = False, tensor_scale: bool = False,
-                amax: torch.Tensor | None = None, compute_amax: bool = True, out: NVFP4Tensor | None = None):
+                amax: torch.Tensor | None = None, compute_amax: bool = True, out: NVFP4Tensor | None = None,
+                fp32_scale: bool = False):
     """NVFP4 of x (or x^T) with the recipe variants: round-up block scales and/or one
-    power-of-two scale for the whole tensor from amax (a float32 device scalar,
-    computed here by a first pass when compute_amax, else supplied)."""
+    scale for the whole tensor from amax (a float32 device scalar, computed here
+    by a first pass when compute_amax, else supplied): a power of two, or with
+    fp32_scale the conventional FP32 scale RN32(amax / 2688)."""
+    if fp32_scale and not tensor_scale:
+        raise ValueError("fp32_scale needs tensor_scale")
     _bf16(x, "x")
     if x.dim() != 2 or x.stride(1) != 1:
         raise ValueError("x must be a 2-D tensor with unit column stride")
@@ -104,6 +109,7 @@ def quantize_ex(x: torch.Tensor, transpose: bool = False, round_up: bool = False
     flags = (QUANT_ROUND_UP_SCALES if round_up else 0)
     if tensor_scale:
         flags |= QUANT_TENSOR_SCALE | (QUANT_COMPUTE_AMAX if compute_amax else 0)
+        flags |= QUANT_TENSOR_SCALE_FP32 if fp32_scale else 0
         if amax is None:
             if not compute_amax:
                 raise ValueError("a supplied amax is needed when compute_amax is False")
@@ -182,9 +188,14 @@ def silu_mul_quant(gate: torch.Tensor, up: torch.Tensor, out=None):
     return h, gq, uq
 
 
+GEMM_ANY_ROW_SCALES = 1
+
+
 def gemm_fwd(xq: NVFP4Tensor, w_fwd: NVFP4Tensor, lora_t: torch.Tensor | None = None,
-             lora_b: torch.Tensor | None = None, lora_scale: float = 1.0, out: torch.Tensor | None = None):
-    """Y = bf16(deq(X_q) deq(W_fwd)^T [+ lora_scale * T B^T])."""
+             lora_b: torch.Tensor | None = None, lora_scale: float = 1.0, out: torch.Tensor | None = None,
+             any_row_scales: bool = False):
+    """Y = bf16(deq(X_q) deq(W_fwd)^T [+ lora_scale * T B^T]).  ``any_row_scales``:
+    operands may carry non-power-of-two row scales (FP32 tensor-scale recipe)."""
     M, K = xq.rows, xq.cols
     N = w_fwd.rows
     if w_fwd.cols != K:
@@ -195,14 +206,16 @@ def gemm_fwd(xq: NVFP4Tensor, w_fwd: NVFP4Tensor, lora_t: torch.Tensor | None = 
         r = lora_t.shape[1]
         if lora_b is None or lora_b.shape != (N, r) or lora_t.shape[0] != M:
             raise ValueError("LoRA shapes: T [M x r], B [N x r]")
-    _lib.call("nvfp4_gemm_fwd", *xq.ptrs(), M, K, *w_fwd.ptrs(), N, out.data_ptr(), out.stride(0),
-              _ptr(lora_t), _ptr(lora_b), r, float(lora_scale), _stream())
+    _lib.call("nvfp4_gemm_fwd_ex", *xq.ptrs(), M, K, *w_fwd.ptrs(), N, out.data_ptr(), out.stride(0),
+              _ptr(lora_t), _ptr(lora_b), r, float(lora_scale), GEMM_ANY_ROW_SCALES if any_row_scales else 0,
+              _stream())
     return out
 
 
 def gemm_dgrad(dyq: NVFP4Tensor, w_bwd: NVFP4Tensor, out: torch.Tensor | None = None, accumulate: bool = False,
-               lora_dt: torch.Tensor | None = None, lora_a: torch.Tensor | None = None):
-    """dX = bf16([f32(dX) +] deq(dY_q) deq(W_bwd)^T [+ dT A])."""
+               lora_dt: torch.Tensor | None = None, lora_a: torch.Tensor | None = None,
+               any_row_scales: bool = False):
+    """dX = bf16([f32(dX) +] deq(dY_q) deq(W_bwd)^T [+ dT A]); ``any_row_scales`` as for gemm_fwd."""
     M, N = dyq.rows, dyq.cols
     K = w_bwd.rows
     if w_bwd.cols != N:
@@ -216,8 +229,9 @@ def gemm_dgrad(dyq: NVFP4Tensor, w_bwd: NVFP4Tensor, out: torch.Tensor | None = 
         r = lora_dt.shape[1]
         if lora_a is None or lora_a.shape != (r, K) or lora_dt.shape[0] != M:
             raise ValueError("LoRA shapes: dT [M x r], A [r x K]")
-    _lib.call("nvfp4_gemm_dgrad", *dyq.ptrs(), M, N, *w_bwd.ptrs(), K, out.data_ptr(), out.stride(0),
-              int(accumulate), _ptr(lora_dt), _ptr(lora_a), r, _stream())
+    _lib.call("nvfp4_gemm_dgrad_ex", *dyq.ptrs(), M, N, *w_bwd.ptrs(), K, out.data_ptr(), out.stride(0),
+              int(accumulate), _ptr(lora_dt), _ptr(lora_a), r, GEMM_ANY_ROW_SCALES if any_row_scales else 0,
+              _stream())
     return out
 
 

@@ -69,7 +69,7 @@ extern "C" {
 
 const char* pact_last_error(void) { return g_err; }
 
-int pact_abi_version(void) { return 10; }
+int pact_abi_version(void) { return 11; }
 
 int pact_nvfp4_sizes(int64_t rows, int64_t cols, size_t* codes_bytes, size_t* scales_bytes, size_t* rscale_bytes) {
   REQUIRE(rows >= 0 && cols >= 0, PACT_EINVAL, "negative size (rows=%lld, cols=%lld)", (long long)rows,
@@ -123,10 +123,13 @@ int nvfp4_quantize_ex(const uint16_t* x, int64_t rows, int64_t cols, int64_t ldx
   REQUIRE(rows >= 0 && cols >= 0, PACT_EINVAL, "negative size (rows=%lld, cols=%lld)", (long long)rows,
           (long long)cols);
   REQUIRE(transpose == 0 || transpose == 1, PACT_EINVAL, "transpose must be 0 or 1 (got %d)", transpose);
-  REQUIRE((flags & ~(PACT_QUANT_ROUND_UP_SCALES | PACT_QUANT_TENSOR_SCALE | PACT_QUANT_COMPUTE_AMAX)) == 0,
+  REQUIRE((flags & ~(PACT_QUANT_ROUND_UP_SCALES | PACT_QUANT_TENSOR_SCALE | PACT_QUANT_COMPUTE_AMAX |
+                     PACT_QUANT_TENSOR_SCALE_FP32)) == 0,
           PACT_EINVAL, "unknown flags 0x%x", flags);
   REQUIRE(!(flags & PACT_QUANT_COMPUTE_AMAX) || (flags & PACT_QUANT_TENSOR_SCALE), PACT_EINVAL,
           "PACT_QUANT_COMPUTE_AMAX needs PACT_QUANT_TENSOR_SCALE");
+  REQUIRE(!(flags & PACT_QUANT_TENSOR_SCALE_FP32) || (flags & PACT_QUANT_TENSOR_SCALE), PACT_EINVAL,
+          "PACT_QUANT_TENSOR_SCALE_FP32 needs PACT_QUANT_TENSOR_SCALE");
   REQUIRE(cols % 16 == 0, PACT_ESHAPE, "cols=%lld is not a multiple of 16", (long long)cols);
   const bool tensor = (flags & PACT_QUANT_TENSOR_SCALE) != 0;
   if (tensor) {
@@ -153,7 +156,9 @@ int nvfp4_quantize_ex(const uint16_t* x, int64_t rows, int64_t cols, int64_t ldx
     if (st != PACT_OK) return st;
   }
   return hip_status(pact::launch_quantize_ex(x, rows, cols, ldx, transpose,
-                                             (flags & PACT_QUANT_ROUND_UP_SCALES) ? 1 : 0, tensor ? amax : nullptr,
+                                             ((flags & PACT_QUANT_ROUND_UP_SCALES) ? 1 : 0) |
+                                                 ((flags & PACT_QUANT_TENSOR_SCALE_FP32) ? 2 : 0),
+                                             tensor ? amax : nullptr,
                                              codes, scales, rscale, s),
                     "nvfp4_quantize_ex launch");
 }
@@ -229,7 +234,17 @@ int nvfp4_gemm_fwd(const uint8_t* x_codes, const uint8_t* x_scales, const float*
                    const uint8_t* w_codes, const uint8_t* w_scales, const float* w_rscale, int64_t N, uint16_t* y,
                    int64_t ldy, const uint16_t* lora_t, const uint16_t* lora_b, int64_t lora_r, float lora_scale,
                    void* stream) {
+  return nvfp4_gemm_fwd_ex(x_codes, x_scales, x_rscale, M, K, w_codes, w_scales, w_rscale, N, y, ldy, lora_t, lora_b,
+                           lora_r, lora_scale, 0, stream);
+}
+
+int nvfp4_gemm_fwd_ex(const uint8_t* x_codes, const uint8_t* x_scales, const float* x_rscale, int64_t M, int64_t K,
+                      const uint8_t* w_codes, const uint8_t* w_scales, const float* w_rscale, int64_t N, uint16_t* y,
+                      int64_t ldy, const uint16_t* lora_t, const uint16_t* lora_b, int64_t lora_r, float lora_scale,
+                      int flags, void* stream) {
+  REQUIRE((flags & ~PACT_GEMM_ANY_ROW_SCALES) == 0, PACT_EINVAL, "unknown flags 0x%x", flags);
   pact::GemmArgs a{};
+  a.general = (flags & PACT_GEMM_ANY_ROW_SCALES) ? 1 : 0;
   a.a_codes = x_codes; a.a_scales = x_scales; a.a_rscale = x_rscale;
   a.b_codes = w_codes; a.b_scales = w_scales; a.b_rscale = w_rscale;
   a.M = M; a.N = N; a.K = K;
@@ -244,8 +259,18 @@ int nvfp4_gemm_dgrad(const uint8_t* dy_codes, const uint8_t* dy_scales, const fl
                      const uint8_t* w_codes, const uint8_t* w_scales, const float* w_rscale, int64_t K, uint16_t* dx,
                      int64_t lddx, int accumulate, const uint16_t* lora_dt, const uint16_t* lora_a, int64_t lora_r,
                      void* stream) {
+  return nvfp4_gemm_dgrad_ex(dy_codes, dy_scales, dy_rscale, M, N, w_codes, w_scales, w_rscale, K, dx, lddx,
+                             accumulate, lora_dt, lora_a, lora_r, 0, stream);
+}
+
+int nvfp4_gemm_dgrad_ex(const uint8_t* dy_codes, const uint8_t* dy_scales, const float* dy_rscale, int64_t M,
+                        int64_t N, const uint8_t* w_codes, const uint8_t* w_scales, const float* w_rscale, int64_t K,
+                        uint16_t* dx, int64_t lddx, int accumulate, const uint16_t* lora_dt, const uint16_t* lora_a,
+                        int64_t lora_r, int flags, void* stream) {
   REQUIRE(accumulate == 0 || accumulate == 1, PACT_EINVAL, "accumulate must be 0 or 1 (got %d)", accumulate);
+  REQUIRE((flags & ~PACT_GEMM_ANY_ROW_SCALES) == 0, PACT_EINVAL, "unknown flags 0x%x", flags);
   pact::GemmArgs a{};
+  a.general = (flags & PACT_GEMM_ANY_ROW_SCALES) ? 1 : 0;
   a.a_codes = dy_codes; a.a_scales = dy_scales; a.a_rscale = dy_rscale;
   a.b_codes = w_codes; a.b_scales = w_scales; a.b_rscale = w_rscale;
   a.M = M; a.N = K; a.K = N;                 // output [M x K], contraction over N
@@ -459,6 +484,9 @@ int pact_nvfp4_row_exp_max(const uint8_t* codes, const uint8_t* scales, const fl
   if (st != PACT_OK) return st;
   st = hip_status(hipStreamSynchronize(s), "row exponent read-back");
   if (st != PACT_OK) return st;
+  REQUIRE(host[0] <= 127, PACT_EUNSUPPORTED,
+          "a nonzero row has a row scale that is not a power of two: the single-layout dgrad cannot fold it into "
+          "its FP16 operand exactly");
   REQUIRE(host[0] - host[1] <= 14, PACT_EUNSUPPORTED,
           "nonzero rows span row exponents %d .. %d (more than 14 apart): the single-layout dgrad would not be "
           "exact for this weight",

@@ -351,8 +351,13 @@ struct FastCfg {
 // the same X.  The accumulator holds each segment's partial sum in units of
 // the current segment's row scales; at a segment boundary it is rescaled by
 // the power of two r_A,old r_B,old / (r_A,new r_B,new) (v_ldexp: exact in the
-// FP32 range), so the epilogue applies the last segment's scales.  Without SEG
-// every segment branch compiles away.
+// FP32 range), so the epilogue applies the last segment's scales.  Row scales
+// that are not powers of two (the FP32 tensor-scale recipe) cannot be carried
+// across segments this way: with two or more segments the epilogue checks
+// every segment's row scales of the tile and writes NaN to the tile if one of
+// them is not a power of two
+// (such operands take one nvfp4_gemm_dgrad launch per projection, with
+// accumulate, instead).  Without SEG every segment branch compiles away.
 template <int WTM, int WTN, bool SEG = false>
 __global__ __launch_bounds__(256, 1) void k_gemm_nvfp4_fast(GemmArgs p, int tiles_m, int tiles_n, SegArgs sg) {
   using C = FastCfg<WTM, WTN>;
@@ -665,9 +670,9 @@ __global__ __launch_bounds__(256, 1) void k_gemm_nvfp4_fast(GemmArgs p, int tile
   // The LoRA term is formed while those loads are in flight: acc starts as
   // (lora_scale / (rA rB)) * T U, so the epilogue's row-scale multiply turns
   // it into lora_scale * T U.  The T rows are scaled by f_m = lora_scale / rA
-  // and the U columns by 1/rB as they are loaded (1/rA and 1/rB are powers of
-  // two), so the MFMAs produce the term directly and the accumulator is never
-  // rescaled.  With a power-of-two lora_scale, T f_m is exact in BF16 (which
+  // and the U columns by 1/rB as they are loaded (exact for power-of-two row
+  // scales; see lora_factors for others), so the MFMAs produce the term
+  // directly and the accumulator is never rescaled.  With a power-of-two lora_scale, T f_m is exact in BF16 (which
   // has FP32's exponent range).  Otherwise x = fl32(T f_m) is split into three
   // BF16 values hi + mid + lo = x exactly (each residual is exact in FP32 and
   // the last has at most 8 significant bits), and the term runs three MFMA
@@ -680,8 +685,9 @@ __global__ __launch_bounds__(256, 1) void k_gemm_nvfp4_fast(GemmArgs p, int tile
     for (int j = 0; j < WTN; ++j)
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
-  // row scales are powers of two: 1/r is exact and computed on the exponent
+  // 1/r of a power of two, exact, computed on the exponent
   auto inv_pow2 = [](float v) { return __uint_as_float((254u << 23) - __float_as_uint(v)); };
+  auto is_pow2 = [](float v) { return (__float_as_uint(v) & 0x7FFFFFu) == 0u; };
   const uint32_t s_bits = __float_as_uint(p.lora_scale);
   const uint32_t s_exp = (s_bits >> 23) & 255u;
   const int npieces = ((s_bits & 0x7FFFFFu) == 0 && s_exp >= 1u && s_exp <= 254u) ? 1 : 3;
@@ -704,21 +710,33 @@ __global__ __launch_bounds__(256, 1) void k_gemm_nvfp4_fast(GemmArgs p, int tile
     o.w = pack_bf16x2(one(bf16_lo(v.w) * f), one(bf16_hi(v.w) * f));
     return __builtin_bit_cast(bf16x8_t, o);
   };
-  // T row and U column factors of this lane's fragments
+  // T row and U column factors of this lane's fragments.  A row scale of the
+  // wave's rows or columns that is not a power of two (the FP32 tensor-scale
+  // recipe) has no exact reciprocal on the exponent, and U / rB would not be
+  // exact in BF16: such a wave ("odd") writes NaN to its part of the tile
+  // (the register-staged kernel, which scales the term in FP32 after its
+  // MFMAs, serves those operands).
   float fa[WTM], fb[WTN];
+  bool odd_wave = false;                               // wave-uniform
   auto lora_factors = [&]() __attribute__((always_inline)) {
+    bool odd = false;
 #pragma unroll
     for (int i = 0; i < WTM; ++i) {
       int64_t m = m0 + wm * (BM / 2) + i * 32 + li;
       m = m < M ? m : M - 1;
-      fa[i] = p.lora_scale * inv_pow2(lra[m]);
+      const float ra = lra[m];
+      odd = odd || !is_pow2(ra);
+      fa[i] = p.lora_scale * inv_pow2(ra);
     }
 #pragma unroll
     for (int i = 0; i < WTN; ++i) {
       int64_t n = n0 + wn * (BN / 2) + i * 32 + li;
       n = n < N ? n : N - 1;
-      fb[i] = inv_pow2(lrb[n]);
+      const float rb = lrb[n];
+      odd = odd || !is_pow2(rb);
+      fb[i] = inv_pow2(rb);
     }
+    odd_wave = __ballot(odd) != 0ull;
   };
   // one rank-r term (T, U) per segment with SEG, else p's
   auto lora_term = [&](const uint16_t* lt, const uint16_t* lu, int64_t r) __attribute__((always_inline)) {
@@ -786,6 +804,8 @@ __global__ __launch_bounds__(256, 1) void k_gemm_nvfp4_fast(GemmArgs p, int tile
           uv[i] = make_uint4(w[0] | (w[1] << 16), w[2] | (w[3] << 16), w[4] | (w[5] << 16), w[6] | (w[7] << 16));
         }
       }
+      // pieces (U piece pu, T piece pt): (0, 0 .. npieces-1), or for an odd
+      // wave every pair with pu + pt <= 2 (the others are below 2^-24 of the term)
 #pragma unroll
       for (int i = 0; i < WTN; ++i) uf[i] = scaled(uv[i], fb[i], 0);
       for (int piece = 0; piece < npieces; ++piece) {
@@ -800,17 +820,19 @@ __global__ __launch_bounds__(256, 1) void k_gemm_nvfp4_fast(GemmArgs p, int tile
       }
     }
   };
+  bool any_lora = p.lora_t != nullptr;
   if constexpr (SEG) {
-    bool any = false;
-    for (int lp = 0; lp < sg.nseg; ++lp) any = any || sg.s[lp].lora_t != nullptr;
-    if (any) {
-      lora_factors();
+    any_lora = false;
+    for (int lp = 0; lp < sg.nseg; ++lp) any_lora = any_lora || sg.s[lp].lora_t != nullptr;
+  }
+  if (any_lora) {
+    lora_factors();
+    if constexpr (SEG) {
       for (int lp = 0; lp < sg.nseg; ++lp)
         if (sg.s[lp].lora_t != nullptr) lora_term(sg.s[lp].lora_t, sg.s[lp].lora_u, sg.s[lp].lora_r);
+    } else {
+      lora_term(p.lora_t, p.lora_u, p.lora_r);
     }
-  } else if (p.lora_t != nullptr) {
-    lora_factors();
-    lora_term(p.lora_t, p.lora_u, p.lora_r);
   }
   if (nk0 > 1) issue_stage(1, 1);
   if constexpr (!SEG) {
@@ -859,7 +881,20 @@ __global__ __launch_bounds__(256, 1) void k_gemm_nvfp4_fast(GemmArgs p, int tile
   // Each wave stages one 32-row slab of its tile at a time in LDS as FP32
   // (MFMA layout in, row-major out), then every lane writes 8 consecutive
   // columns of a row with one 16-byte store.
-  __syncthreads();                                     // all waves are done reading the stage buffers
+  // NaN instead of a rounded result: a wave whose LoRA term met a row scale
+  // that is not a power of two poisons its part of the tile; with two or more
+  // segments, a tile whose row scales (of any segment) are not all powers of
+  // two poisons all of it (rows past an operand's end read as 0, a
+  // power-of-two pattern)
+  float poison = odd_wave ? __uint_as_float(0x7FC00000u) : 1.0f;
+  if constexpr (SEG) {
+    uint32_t odd = 0u;
+    if (sg.nseg > 1)
+      for (int q = tid; q < sg.nseg * C::ROWS; q += 256) odd |= __float_as_uint(rsc[q]) & 0x7FFFFFu;
+    if (__syncthreads_or(odd != 0u) != 0) poison = __uint_as_float(0x7FC00000u);   // also the barrier below
+  } else {
+    __syncthreads();                                   // all waves are done reading the stage buffers
+  }
   float* epi = reinterpret_cast<float*>(smem + wave * C::EPI_WAVE);
   const float* rse = rsc + (SEG ? (sg.nseg - 1) * C::ROWS : 0);   // the last segment's row scales
   constexpr int WN = BN / 2;                            // columns of this wave's tile
@@ -870,7 +905,7 @@ __global__ __launch_bounds__(256, 1) void k_gemm_nvfp4_fast(GemmArgs p, int tile
 #pragma unroll
     for (int j = 0; j < WTN; ++j) {
       const int col = j * 32 + li;
-      const float rb = rse[BM + wn * WN + col];
+      const float rb = rse[BM + wn * WN + col] * poison;
 #pragma unroll
       for (int rr = 0; rr < 16; ++rr) {
         const int row = 8 * (rr >> 2) + 4 * h + (rr & 3);
@@ -924,8 +959,10 @@ hipError_t launch_gemm(const GemmArgs& a, hipStream_t s) {
   gemm_tile(a.M, a.N, &bm, &bn);
   const int tm = (int)((a.M + bm - 1) / bm), tn = (int)((a.N + bn - 1) / bn);
   // fast path: K a multiple of the stage length and every operand addressable
-  // with 32-bit buffer offsets
-  const bool fast = (a.K % KT2) == 0 && (uint64_t)(a.M > a.N ? a.M : a.N) * (uint64_t)(a.K / 2) < (1ull << 31);
+  // with 32-bit buffer offsets, unless the caller asks for the general one
+  // (its LoRA term takes any row scale; the fast kernel's needs powers of two)
+  const bool fast = !a.general && (a.K % KT2) == 0 &&
+                    (uint64_t)(a.M > a.N ? a.M : a.N) * (uint64_t)(a.K / 2) < (1ull << 31);
   if (fast) {
     const SegArgs none{};
     if (bm == 256 && bn == 256) k_gemm_nvfp4_fast<4, 4><<<tm * tn, 256, 0, s>>>(a, tm, tn, none);

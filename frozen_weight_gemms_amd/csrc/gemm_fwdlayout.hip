@@ -22,7 +22,8 @@
 // in FP16 while e_ref - e_n <= 14 (c s is a multiple of 2^-10 with at most 6
 // significant bits).  A row with nonzero block scales outside that window
 // (more than 2^14 below e_ref, or above it: an e_ref that is not this
-// weight's) would round or vanish in FP16; the table build flags it and the
+// weight's), or whose row scale is not a power of two, would round or vanish
+// in FP16; the table build flags it and the
 // workgroup then writes NaN to every output it owns instead of a silently
 // wrong gradient (pact_nvfp4_row_exp_max rejects such a weight up front).
 //
@@ -191,7 +192,9 @@ __global__ __launch_bounds__(256, 1) void k_gemm_dgrad_fwdlayout(FlArgs p, int t
     // for all-zero rows (excluded from e_ref), whose block scales are 0 anyway.
     // Exactness of every c s 2^-d needs 0 <= d <= 14 on rows with a nonzero scale.
     // (only for a real stage: past the last one the buffer holds stale bytes)
-    inexact_row |= (real_stage && (d > 14 || d < 0) && (raw.x | raw.y) != 0u) ? 1u : 0u;
+    // A row scale that is not a power of two (the FP32 tensor-scale recipe)
+    // cannot be folded into the table exactly at all.
+    inexact_row |= (real_stage && (d > 14 || d < 0 || (rb & 0x7FFFFFu) != 0u) && (raw.x | raw.y) != 0u) ? 1u : 0u;
     const _Float16 mult = (d >= 0 && d <= 24) ? (_Float16)__uint_as_float((uint32_t)(127 - d) << 23)
                                                : (_Float16)0.0f;
     const half2_t m2 = {mult, mult};
@@ -413,13 +416,18 @@ __global__ __launch_bounds__(256, 1) void k_gemm_dgrad_fwdlayout(FlArgs p, int t
   __syncthreads();
   const float inv_ref = __uint_as_float((uint32_t)(127 - e_ref) << 23);   // 2^-e_ref (e_ref in [-126, 127])
   if (p.lora_t != nullptr) {
-    auto inv_pow2 = [](float v) { return __uint_as_float((254u << 23) - __float_as_uint(v)); };
+    // 1/r_A: exact on the exponent for a power of two, else a rounded quotient
+    // (one FP32 rounding of the term, which the epilogue's r_A multiply undoes
+    // up to that rounding)
+    auto inv_r = [](float v) {
+      return (__float_as_uint(v) & 0x7FFFFFu) == 0u ? __uint_as_float((254u << 23) - __float_as_uint(v)) : 1.0f / v;
+    };
 #pragma unroll
     for (int i = 0; i < WTM; ++i)
 #pragma unroll
       for (int rr = 0; rr < 16; ++rr) {
         const int row = wm * (BM / 2) + i * 32 + 8 * (rr >> 2) + 4 * h + (rr & 3);
-        const float fa = inv_pow2(rsc[row]) * inv_ref;
+        const float fa = inv_r(rsc[row]) * inv_ref;
 #pragma unroll
         for (int j = 0; j < WTN; ++j) acc[i][j][rr] *= fa;
       }
@@ -525,7 +533,10 @@ __global__ __launch_bounds__(256) void k_row_exp_range(const float* __restrict__
 #pragma unroll
     for (int o = 32; o >= 1; o >>= 1) any |= (uint32_t)__shfl_xor((int)any, o, 64);
     if (any != 0) {
-      const int e = (int)((__float_as_uint(rscale[i]) >> 23) & 0xFFu) - 127;
+      const uint32_t u = __float_as_uint(rscale[i]);
+      // a row scale that is not a power of two reports the out-of-range
+      // exponent 255, which fails the caller's window check
+      const int e = (u & 0x7FFFFFu) != 0u ? 255 : (int)((u >> 23) & 0xFFu) - 127;
       hi = e > hi ? e : hi;
       lo = e < lo ? e : lo;
     }

@@ -89,6 +89,39 @@ __device__ __forceinline__ float pow2f(int e) {   // e in [-126, 127]
   return __uint_as_float((uint32_t)(e + 127) << 23);
 }
 
+// Conventional FP32 tensor scale for a tensor maximum amax (finite, >= 0):
+// stored scale S = RN32(amax / 2688), at least 2^-126 (1 for amax == 0), and
+// encoding multiplier R = RN32(1 / S).  Both quotients are taken in FP64 and
+// rounded once more to FP32; FP64 carries more than twice FP32's precision
+// plus two bits, so that second rounding of a correctly rounded quotient
+// equals the correctly rounded FP32 quotient.  A subnormal S (flushed or not)
+// is raised to 2^-126 either way.
+__device__ __forceinline__ void tensor_scale_fp32(float amax, float& S, float& R) {
+  if (amax == 0.0f) {
+    S = 1.0f;
+    R = 1.0f;
+    return;
+  }
+  const float s = fmaxf((float)((double)amax / 2688.0), 1.17549435e-38f);
+  S = s;
+  R = (float)(1.0 / (double)s);
+}
+
+// Scale pair (r, inv_r) of a row from its (or the tensor's) maximum: the
+// power of two of the row rule, or with kQuantFp32Tensor the FP32 tensor
+// scale S and multiplier R (then |x| * inv_r is the rounded product u).
+constexpr int kQuantRoundUp = 1;
+constexpr int kQuantFp32Tensor = 2;
+__device__ __forceinline__ void row_scale_pair(float amax, int qmode, float& r, float& inv_r) {
+  if (qmode & kQuantFp32Tensor) {
+    tensor_scale_fp32(amax, r, inv_r);
+  } else {
+    const int e = row_exponent(amax);
+    r = pow2f(e);
+    inv_r = pow2f(-e);
+  }
+}
+
 // RNE of t >= 0 onto the E4M3FN grid, saturating at 448 (code 0x7E).
 __device__ __forceinline__ uint32_t e4m3_encode(float t) {
   if (t >= 448.0f) return 0x7Eu;
@@ -105,7 +138,12 @@ __device__ __forceinline__ float e4m3_decode(uint32_t c) {
 // Per-block constants for quantizing one block.  The quotient |x| / (s r) is
 // formed as (|x| 2^-e) / s: the power-of-two scaling is exact, and s is a
 // normal FP32 number, so the division stays out of the FP32 subnormal range
-// (where the remainder of the correction step would not be exact).
+// (where the remainder of the correction step would not be exact).  With the
+// FP32 tensor scale, inv_r = R and |x| * inv_r is the recipe's rounded product
+// u itself; u / s is again correctly rounded, and since u has 24 significant
+// bits and every threshold (midpoint times s) at most 7, an exact quotient off
+// a threshold lies more than half an ulp from it, so the rounded quotient
+// takes the same side (a quotient below 2^-126 is far below the first one).
 struct BlockQ {
   float s;      // block scale (0 if it rounds to 0)
   float rcp;    // correctly rounded 1/s
@@ -127,7 +165,7 @@ __device__ __forceinline__ uint32_t e4m3_encode_up(float X) {
 __device__ __forceinline__ BlockQ block_setup(float bmax, float r, float inv_r, bool round_up = false) {
   (void)r;
   BlockQ q;
-  const float X = bmax * inv_r;                        // exact: r is a power of two
+  const float X = bmax * inv_r;                        // |x| / r exactly, or the largest u of the block
   q.sc = round_up ? e4m3_encode_up(X) : e4m3_encode(div6_rn(X));
   q.s = e4m3_decode(q.sc);
   q.rcp = q.s != 0.0f ? recip_rn(q.s) : 0.0f;          // s >= 2^-9: normal, with a normal reciprocal

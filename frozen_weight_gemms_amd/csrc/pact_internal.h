@@ -15,8 +15,8 @@ hipError_t launch_quantize(const uint16_t* x, int64_t rows, int64_t cols, int64_
 // round_up: block scales rounded up (non-saturating); tensor_amax (device, may be
 // null): one power-of-two scale for the whole tensor from that maximum
 hipError_t launch_quantize_ex(const uint16_t* x, int64_t rows, int64_t cols, int64_t ldx, int transpose,
-                              int round_up, const float* tensor_amax, uint8_t* codes, uint8_t* scales,
-                              float* rscale, hipStream_t s);
+                              int qmode, const float* tensor_amax, uint8_t* codes, uint8_t* scales,
+                              float* rscale, hipStream_t s);   // qmode: bit 0 round-up scales, bit 1 FP32 tensor scale
 // *amax = max |x| over x [rows x cols] (row stride ldx)
 hipError_t launch_selftest_arith(unsigned long long* counts, hipStream_t s);
 constexpr int kMfmaProbeGroups = 512;      // workgroups of the MFMA-rate probe
@@ -50,6 +50,7 @@ struct GemmArgs {
   int64_t u_stride_j, u_stride_n;
   int64_t lora_r;
   float lora_scale;
+  int general;              // 1: row scales may be any positive FP32 (register-staged kernel)
 };
 
 hipError_t launch_gemm(const GemmArgs& a, hipStream_t s);

@@ -30,7 +30,7 @@ template <int NB, int WPR>
 __global__ __launch_bounds__(kThreads) void k_quantize_rows(const uint16_t* __restrict__ x, int64_t rows,
                                                             int64_t cols, int64_t ldx, uint8_t* __restrict__ codes,
                                                             uint8_t* __restrict__ scales,
-                                                            float* __restrict__ rscale, int round_up,
+                                                            float* __restrict__ rscale, int qmode,
                                                             const float* __restrict__ tensor_amax) {
   __shared__ float red[4];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -68,8 +68,8 @@ __global__ __launch_bounds__(kThreads) void k_quantize_rows(const uint16_t* __re
     }
   }
   if (!row_ok) return;
-  const int e = row_exponent(amax);
-  const float r = pow2f(e), inv_r = pow2f(-e);
+  float r, inv_r;
+  row_scale_pair(amax, qmode, r, inv_r);
   uint8_t* crow = codes + row * (cols >> 1);
   uint8_t* srow = scales + row * (cols >> 4);
 #pragma unroll
@@ -79,7 +79,7 @@ __global__ __launch_bounds__(kThreads) void k_quantize_rows(const uint16_t* __re
       float f[16];
       unpack_bf16x8(v[i][0], f);
       unpack_bf16x8(v[i][1], f + 8);
-      quant_block16(f, bm[i], r, inv_r, crow, srow, blk, round_up != 0);
+      quant_block16(f, bm[i], r, inv_r, crow, srow, blk, (qmode & kQuantRoundUp) != 0);
     }
   }
   if (lane == 0 && part == 0) rscale[row] = r;
@@ -88,7 +88,7 @@ __global__ __launch_bounds__(kThreads) void k_quantize_rows(const uint16_t* __re
 __global__ __launch_bounds__(kThreads) void k_quantize_rows_long(const uint16_t* __restrict__ x, int64_t cols,
                                                                  int64_t ldx, uint8_t* __restrict__ codes,
                                                                  uint8_t* __restrict__ scales,
-                                                                 float* __restrict__ rscale, int round_up,
+                                                                 float* __restrict__ rscale, int qmode,
                                                                  const float* __restrict__ tensor_amax) {
   __shared__ float red[4];
   const int64_t row = blockIdx.x;
@@ -101,8 +101,8 @@ __global__ __launch_bounds__(kThreads) void k_quantize_rows_long(const uint16_t*
     lmax = fmaxf(lmax, absmax8(f));
   }
   const float amax = tensor_amax != nullptr ? *tensor_amax : block_max_256(lmax, red);
-  const int e = row_exponent(amax);
-  const float r = pow2f(e), inv_r = pow2f(-e);
+  float r, inv_r;
+  row_scale_pair(amax, qmode, r, inv_r);
   uint8_t* crow = codes + row * (cols >> 1);
   uint8_t* srow = scales + row * (cols >> 4);
   const int nround = (nchunk + kThreads - 1) / kThreads;
@@ -111,7 +111,7 @@ __global__ __launch_bounds__(kThreads) void k_quantize_rows_long(const uint16_t*
     float f[8];
     uint4 v = c < nchunk ? load16(xr + 8 * c) : make_uint4(0, 0, 0, 0);
     unpack_bf16x8(v, f);
-    quant_chunk(f, c < nchunk, r, inv_r, crow, srow, c, round_up != 0);
+    quant_chunk(f, c < nchunk, r, inv_r, crow, srow, c, (qmode & kQuantRoundUp) != 0);
   }
   if (threadIdx.x == 0) rscale[row] = r;
 }
@@ -126,7 +126,7 @@ __global__ __launch_bounds__(kThreads) void k_quantize_cols(const uint16_t* __re
                                                             int64_t cols, int64_t ldx,
                                                             uint8_t* __restrict__ codes,
                                                             uint8_t* __restrict__ scales,
-                                                            float* __restrict__ rscale, int round_up,
+                                                            float* __restrict__ rscale, int qmode,
                                                             const float* __restrict__ tensor_amax) {
   __shared__ float red[4][64];
   const int li = threadIdx.x & 63, g = threadIdx.x >> 6;
@@ -140,8 +140,8 @@ __global__ __launch_bounds__(kThreads) void k_quantize_cols(const uint16_t* __re
   __syncthreads();
   const float amax = tensor_amax != nullptr ? *tensor_amax
                                             : fmaxf(fmaxf(red[0][li], red[1][li]), fmaxf(red[2][li], red[3][li]));
-  const int e = row_exponent(amax);
-  const float r = pow2f(e), inv_r = pow2f(-e);
+  float r, inv_r;
+  row_scale_pair(amax, qmode, r, inv_r);
   for (int64_t b = g; b < nblk; b += 4) {
     float f[16];
     float m = 0.0f;
@@ -150,7 +150,7 @@ __global__ __launch_bounds__(kThreads) void k_quantize_cols(const uint16_t* __re
       f[t] = bf16_lo(x[(16 * b + t) * ldx + ic]);
       m = fmaxf(m, fabsf(f[t]));
     }
-    const BlockQ q = block_setup(m, r, inv_r, round_up != 0);
+    const BlockQ q = block_setup(m, r, inv_r, (qmode & kQuantRoundUp) != 0);
     const uint32_t w0 = encode8(f, q), w1 = encode8(f + 8, q);
     if (ok) {
       uint32_t* dst = reinterpret_cast<uint32_t*>(codes + i * (cols >> 1) + 8 * b);
@@ -549,11 +549,11 @@ hipError_t launch_tensor_absmax(const uint16_t* x, int64_t rows, int64_t cols, i
 }
 
 hipError_t launch_quantize_ex(const uint16_t* x, int64_t rows, int64_t cols, int64_t ldx, int transpose,
-                              int round_up, const float* tensor_amax, uint8_t* codes, uint8_t* scales,
+                              int qmode, const float* tensor_amax, uint8_t* codes, uint8_t* scales,
                               float* rscale, hipStream_t s) {
   if (transpose) {
     const unsigned grid = (unsigned)((rows + 63) / 64);
-    k_quantize_cols<<<grid, kThreads, 0, s>>>(x, rows, cols, ldx, codes, scales, rscale, round_up, tensor_amax);
+    k_quantize_cols<<<grid, kThreads, 0, s>>>(x, rows, cols, ldx, codes, scales, rscale, qmode, tensor_amax);
     return hipGetLastError();
   }
   // blocks per lane <= 4: one wave per row up to 4096 columns, two up to 8192, four up to 16384
@@ -562,9 +562,9 @@ hipError_t launch_quantize_ex(const uint16_t* x, int64_t rows, int64_t cols, int
   const int64_t nb = (nblk + 64 * wpr - 1) / (64 * wpr);
   const dim3 grid((unsigned)((rows + 4 / wpr - 1) / (4 / wpr)));
 #define PACT_QR(N, W) \
-  k_quantize_rows<N, W><<<grid, kThreads, 0, s>>>(x, rows, cols, ldx, codes, scales, rscale, round_up, tensor_amax)
+  k_quantize_rows<N, W><<<grid, kThreads, 0, s>>>(x, rows, cols, ldx, codes, scales, rscale, qmode, tensor_amax)
   if (nblk > 1024) k_quantize_rows_long<<<dim3((unsigned)rows), kThreads, 0, s>>>(x, cols, ldx, codes, scales, rscale,
-                                                                                  round_up, tensor_amax);
+                                                                                  qmode, tensor_amax);
   else if (wpr == 1 && nb <= 1) PACT_QR(1, 1);
   else if (wpr == 1 && nb <= 2) PACT_QR(2, 1);
   else if (wpr == 1 && nb <= 3) PACT_QR(3, 1);

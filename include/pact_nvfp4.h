@@ -131,11 +131,23 @@ int nvfp4_quantize(const uint16_t *x, int64_t rows, int64_t cols, int64_t ldx, i
  *       must be >= max |x| or elements saturate.
  *   PACT_QUANT_COMPUTE_AMAX (with PACT_QUANT_TENSOR_SCALE): a first pass over x
  *       writes max |x| to *amax (two passes over x in all).
+ *   PACT_QUANT_TENSOR_SCALE_FP32 (with PACT_QUANT_TENSOR_SCALE): the tensor
+ *       scale is the conventional FP32 one instead of a power of two: every
+ *       rscale is S = RN32(*amax / 2688) (at least 2^-126; 1 if *amax == 0),
+ *       and each element is scaled by the FP32 product u = RN32(|x| * R),
+ *       R = RN32(1 / S), before the block rules (s = RNE_E4M3(max u / 6),
+ *       code = RNE_E2M1(u / s)).  *amax must be finite.  nvfp4_gemm_fwd
+ *       and nvfp4_gemm_dgrad accept such tensors (results within the GEMM
+ *       bound), with a fused LoRA term only through their _ex forms with
+ *       PACT_GEMM_ANY_ROW_SCALES; nvfp4_gemm_dgrad_multi with two or more
+ *       segments and nvfp4_gemm_dgrad_fwd_layout need power-of-two row scales
+ *       (NaN output, and PACT_EUNSUPPORTED from pact_nvfp4_row_exp_max).
  * Other arguments and layouts as nvfp4_quantize.  Unknown flags: PACT_EINVAL.
  */
 #define PACT_QUANT_ROUND_UP_SCALES 1
 #define PACT_QUANT_TENSOR_SCALE 2
 #define PACT_QUANT_COMPUTE_AMAX 4
+#define PACT_QUANT_TENSOR_SCALE_FP32 8
 int nvfp4_quantize_ex(const uint16_t *x, int64_t rows, int64_t cols, int64_t ldx, int transpose, int flags,
                       float *amax, uint8_t *codes, uint8_t *scales, float *rscale, void *stream);
 
@@ -213,6 +225,33 @@ int nvfp4_gemm_fwd(const uint8_t *x_codes, const uint8_t *x_scales, const float 
                    void *stream);
 
 /*
+ * nvfp4_gemm_fwd_ex / nvfp4_gemm_dgrad_ex -- nvfp4_gemm_fwd / nvfp4_gemm_dgrad
+ * with flags (0: exactly the plain call).
+ *   PACT_GEMM_ANY_ROW_SCALES: the operands' row scales may be any positive
+ *     FP32 values, as the FP32 tensor-scale recipe (PACT_QUANT_TENSOR_SCALE_FP32)
+ *     writes; the launch takes the register-staged kernel, whose LoRA term is
+ *     scaled in FP32 after its BF16 MFMAs.  Without the flag the plain calls
+ *     handle such operands too unless a LoRA term is fused: the
+ *     direct-to-LDS kernel folds 1/r into the term's BF16 operands, which is
+ *     exact only for powers of two, and writes NaN (at least to every output
+ *     whose row or column scale is not a power of two) rather than a
+ *     silently rounded result.
+ * Unknown flags: PACT_EINVAL.
+ */
+#define PACT_GEMM_ANY_ROW_SCALES 1
+int nvfp4_gemm_fwd_ex(const uint8_t *x_codes, const uint8_t *x_scales, const float *x_rscale,
+                      int64_t M, int64_t K,
+                      const uint8_t *w_codes, const uint8_t *w_scales, const float *w_rscale, int64_t N,
+                      uint16_t *y, int64_t ldy,
+                      const uint16_t *lora_t, const uint16_t *lora_b, int64_t lora_r, float lora_scale,
+                      int flags, void *stream);
+int nvfp4_gemm_dgrad_ex(const uint8_t *dy_codes, const uint8_t *dy_scales, const float *dy_rscale,
+                        int64_t M, int64_t N,
+                        const uint8_t *w_codes, const uint8_t *w_scales, const float *w_rscale, int64_t K,
+                        uint16_t *dx, int64_t lddx, int accumulate,
+                        const uint16_t *lora_dt, const uint16_t *lora_a, int64_t lora_r, int flags, void *stream);
+
+/*
  * nvfp4_gemm_dgrad -- frozen-projection input gradient dX = dY W (Appendix
  * Table 7 row "Frozen projections": the input gradient is an NVFP4 GEMM over
  * the weight's cached backward copy).
@@ -246,7 +285,8 @@ int nvfp4_gemm_dgrad(const uint8_t *dy_codes, const uint8_t *dy_scales, const fl
  *   element is formed in FP16 as code * block scale * 2^(e_row - w_exp_max),
  *   exact while every nonzero row's exponent lies in [w_exp_max - 14,
  *   w_exp_max] (the weights pact_nvfp4_row_exp_max accepts).  If a nonzero row
- *   falls outside that window the launch cannot be exact: every output the
+ *   falls outside that window, or its row scale is not a power of two (the
+ *   FP32 tensor-scale recipe), the launch cannot be exact: every output the
  *   affected workgroups own is written as NaN (in practice all of dX, since
  *   every workgroup contracts over all rows) rather than a rounded gradient.
  *   N % 256 == 0 and K % 64 == 0 (else PACT_EUNSUPPORTED), operands below
@@ -273,8 +313,12 @@ int nvfp4_gemm_dgrad_fwd_layout(const uint8_t *dy_codes, const uint8_t *dy_scale
  * Each segment keeps its own row scales: the partial sum is carried from one
  * segment's row-scale units to the next by an exact power-of-two rescale
  * (exact unless two segments' row exponents differ by more than about 90,
- * where the smaller contribution can leave the FP32 range).  With nseg == 1
- * the result equals nvfp4_gemm_dgrad's bit for bit.
+ * where the smaller contribution can leave the FP32 range).  With nseg >= 2
+ * every row scale must be a power of two: operands from the FP32
+ * tensor-scale recipe (PACT_QUANT_TENSOR_SCALE_FP32) make the launch write
+ * NaN to the output tiles whose row scales it meets (use one nvfp4_gemm_dgrad
+ * per segment with accumulate for them).  With nseg == 1 the result equals
+ * nvfp4_gemm_dgrad's bit for bit.
  */
 int nvfp4_gemm_dgrad_multi(int nseg, const uint8_t *const *dy_codes, const uint8_t *const *dy_scales,
                            const float *const *dy_rscale, const int64_t *seg_n,
@@ -293,7 +337,9 @@ int nvfp4_gemm_dgrad_multi(int nseg, const uint8_t *const *dy_codes, const uint8
  * `stream` (it reads the two exponents back) and returns PACT_EUNSUPPORTED when
  * out[0] - out[1] > 14: the single-layout dgrad forms each weight element in
  * FP16 relative to 2^out[0], which is exact only within that window (the
- * exponents are still written).
+ * exponents are still written).  A nonzero row whose row scale is not a power
+ * of two counts as exponent 255 (out[0] = 255) and also gives
+ * PACT_EUNSUPPORTED.
  */
 int pact_nvfp4_row_exp_max(const uint8_t *codes, const uint8_t *scales, const float *rscale, int64_t rows,
                            int64_t cols, int *out, void *stream);
