@@ -224,6 +224,9 @@ class Layer:
         if dyq is None:
             self._ev("quant", "nvfp4_quantize", ("quant", self.M, p.d_out), lambda: fw.quantize(dy, out=P["dyq"]))
         P["dyq_used"] = dyq if dyq is not None else P["dyq"]     # the NVFP4 dY its input gradient reads
+        # one call (dT, dA, dB).  Splitting it (lora_bwd_dt before the input
+        # gradient, lora_bwd_ab on a stream of its own) shortens the chain but
+        # measured slower: the deferred kernels take CUs from the GEMM tiles.
         self._ev("lora", "lora_bwd", ("lora_bwd", self.M, p.d_in, p.d_out, self.r),
                  lambda: fw.lora_bwd(xq, P["A"], P["B"], dy, LORA_SCALE, out=(P["dT"], P["dA"], P["dB"]),
                                      workspace=P["ws"]))

@@ -353,6 +353,36 @@ def lora_bwd(xq: NVFP4Tensor, A: torch.Tensor, B: torch.Tensor, dy: torch.Tensor
     return dT, dA, dB
 
 
+def lora_bwd_dt(dy: torch.Tensor, B: torch.Tensor, scale: float, out: torch.Tensor | None = None):
+    """dT = bf16(scale dY B) alone (lora_bwd's dT, bit for bit)."""
+    _bf16(B, "B"); _dense(_bf16(dy, "dy"), "dy")
+    M, N = dy.shape
+    r = B.shape[1]
+    if B.shape != (N, r):
+        raise ValueError("shapes: dy [M x N], B [N x r]")
+    dT = out if out is not None else torch.empty((M, r), dtype=torch.bfloat16, device=dy.device)
+    _lib.call("lora_bwd_dt", dy.data_ptr(), M, N, B.data_ptr(), r, float(scale), dT.data_ptr(), _stream())
+    return dT
+
+
+def lora_bwd_ab(xq: NVFP4Tensor, A: torch.Tensor, dy: torch.Tensor, dT: torch.Tensor, scale: float, out=None,
+                workspace: torch.Tensor | None = None):
+    """(dA, dB) given lora_bwd_dt's dT (lora_bwd's dA and dB, bit for bit)."""
+    _bf16(A, "A"); _bf16(dy, "dy"); _bf16(dT, "dT")
+    r, K = A.shape
+    M, N = dy.shape
+    if K != xq.cols or xq.rows != M or dT.shape != (M, r):
+        raise ValueError("shapes: xq [M x K], A [r x K], dy [M x N], dT [M x r]")
+    dev = A.device
+    dA, dB = out if out is not None else (torch.empty((r, K), dtype=torch.bfloat16, device=dev),
+                                          torch.empty((N, r), dtype=torch.bfloat16, device=dev))
+    if workspace is None:
+        workspace = lora_bwd_workspace(M, K, N, r, dev)
+    _lib.call("lora_bwd_ab", *xq.ptrs(), M, K, A.data_ptr(), r, float(scale), dy.data_ptr(), N, dT.data_ptr(),
+              dA.data_ptr(), dB.data_ptr(), workspace.data_ptr(), workspace.numel(), _stream())
+    return dA, dB
+
+
 def lora_bwd_noalloc(xq: NVFP4Tensor, A: torch.Tensor, B: torch.Tensor, dy: torch.Tensor, scale: float, out):
     """lora_bwd into caller tensors ``out`` = (dT, dA, dB) with the library's fixed
     per-device scratch instead of a workspace (allocates nothing)."""

@@ -69,7 +69,7 @@ extern "C" {
 
 const char* pact_last_error(void) { return g_err; }
 
-int pact_abi_version(void) { return 11; }
+int pact_abi_version(void) { return 12; }
 
 int pact_nvfp4_sizes(int64_t rows, int64_t cols, size_t* codes_bytes, size_t* scales_bytes, size_t* rscale_bytes) {
   REQUIRE(rows >= 0 && cols >= 0, PACT_EINVAL, "negative size (rows=%lld, cols=%lld)", (long long)rows,
@@ -380,6 +380,45 @@ int lora_bwd(const uint8_t* x_codes, const uint8_t* x_scales, const float* x_rsc
   return hip_status(pact::launch_lora_bwd(x_codes, x_scales, x_rscale, M, K, A, B, r, scale, dy, N, dT, dA, dB,
                                           workspace, as_stream(stream)),
                     "lora_bwd launch");
+}
+
+int lora_bwd_dt(const uint16_t* dy, int64_t M, int64_t N, const uint16_t* B, int64_t r, float scale, uint16_t* dT,
+                void* stream) {
+  REQUIRE(M >= 0 && N >= 0, PACT_EINVAL, "negative size");
+  REQUIRE(N % 16 == 0, PACT_ESHAPE, "N=%lld must be a multiple of 16", (long long)N);
+  REQUIRE(r >= 1 && r <= kMaxRank, PACT_ESHAPE, "rank %lld outside [1, %lld]", (long long)r, (long long)kMaxRank);
+  if (M == 0) return ok();
+  REQUIRE_PTR(dy, "dy");
+  REQUIRE_PTR(B, "B");
+  REQUIRE_PTR(dT, "dT");
+  REQUIRE((M + 15) / 16 < 0x7FFFFFFF, PACT_EUNSUPPORTED, "M too large");
+  return hip_status(pact::launch_lora_bwd_dt(dy, M, N, B, r, scale, dT, as_stream(stream)), "lora_bwd_dt launch");
+}
+
+int lora_bwd_ab(const uint8_t* x_codes, const uint8_t* x_scales, const float* x_rscale, int64_t M, int64_t K,
+                const uint16_t* A, int64_t r, float scale, const uint16_t* dy, int64_t N, const uint16_t* dT,
+                uint16_t* dA, uint16_t* dB, void* workspace, size_t workspace_bytes, void* stream) {
+  REQUIRE(M >= 0 && K >= 0 && N >= 0, PACT_EINVAL, "negative size");
+  REQUIRE(K % 16 == 0 && N % 16 == 0, PACT_ESHAPE, "K=%lld and N=%lld must be multiples of 16", (long long)K,
+          (long long)N);
+  REQUIRE(r >= 1 && r <= kMaxRank, PACT_ESHAPE, "rank %lld outside [1, %lld]", (long long)r, (long long)kMaxRank);
+  if (M > 0) {
+    int st = check_nvfp4(x_codes, x_scales, x_rscale, "x");
+    if (st != PACT_OK) return st;
+    REQUIRE_PTR(dy, "dy");
+    REQUIRE_PTR(dT, "dT");
+  }
+  REQUIRE_PTR(A, "A");
+  REQUIRE_PTR(dA, "dA");
+  REQUIRE_PTR(dB, "dB");
+  const size_t need = pact::lora_bwd_workspace(M, K, N, r);
+  REQUIRE(workspace != nullptr, PACT_EINVAL, "workspace is NULL (needs %zu bytes)", need);
+  REQUIRE((reinterpret_cast<uintptr_t>(workspace) & 255u) == 0, PACT_EALIGN, "workspace is not 256-byte aligned");
+  REQUIRE(workspace_bytes >= need, PACT_EINVAL, "workspace has %zu bytes, needs %zu", workspace_bytes, need);
+  REQUIRE((M + 15) / 16 < 0x7FFFFFFF, PACT_EUNSUPPORTED, "M too large");
+  return hip_status(pact::launch_lora_bwd_ab(x_codes, x_scales, x_rscale, M, K, A, r, scale, dy, N, dT, dA, dB,
+                                             workspace, as_stream(stream)),
+                    "lora_bwd_ab launch");
 }
 
 int lora_bwd_noalloc(const uint8_t* x_codes, const uint8_t* x_scales, const float* x_rscale, int64_t M, int64_t K,

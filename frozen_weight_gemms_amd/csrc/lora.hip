@@ -230,9 +230,10 @@ __device__ __forceinline__ void row_reduce(const uint8_t* __restrict__ xc, const
 }
 
 // Part 0 writes T (row-major, if T != NULL) and Tt (rank-major with leading
-// dimension ldt, if Tt != NULL); part 1 writes dT and dTt.  The rank-major
-// copies get zeros in their padding columns [P, ldt), which the column kernel
-// reads.
+// dimension ldt, if Tt != NULL); part 1 writes dT and dTt; part 2 copies a
+// given dT (dT_in) into dTt.  The rank-major copies get zeros in their padding
+// columns [P, ldt), which the column kernel reads.  Block row y runs part
+// (parts >> 4y) & 15.
 template <int NT>
 __global__ __launch_bounds__(512) void k_lora_rows(const uint8_t* __restrict__ xc, const uint8_t* __restrict__ xs,
                                                    const float* __restrict__ xr, int64_t P, int64_t K,
@@ -240,15 +241,28 @@ __global__ __launch_bounds__(512) void k_lora_rows(const uint8_t* __restrict__ x
                                                    uint16_t* __restrict__ T, uint16_t* __restrict__ Tt, int64_t ldt,
                                                    const uint16_t* __restrict__ dy, int64_t N,
                                                    const uint16_t* __restrict__ B, float scale,
-                                                   uint16_t* __restrict__ dT, uint16_t* __restrict__ dTt) {
+                                                   uint16_t* __restrict__ dT, uint16_t* __restrict__ dTt,
+                                                   int parts, const uint16_t* __restrict__ dT_in) {
   constexpr int NW = 8;
   constexpr int RT = 16 * NT;
   __shared__ float red[NW][16][RT + 1];
   __shared__ __attribute__((aligned(16))) uint8_t stage[NW][RSTAGE];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int i = lane & 15, g = lane >> 4;
-  const int part = (int)blockIdx.y;
+  const int part = (parts >> (4 * (int)blockIdx.y)) & 15;
   const int64_t p0 = (int64_t)blockIdx.x * 16;
+  if (part == 2) {
+    // rank-major copy of the given dT rows p0 .. p0 + 15 (and the padding)
+    for (int q = threadIdx.x; q < 16 * r; q += 512) {
+      const int64_t pp = p0 + q / r, j = q % r;
+      if (pp < P) dTt[j * ldt + pp] = dT_in[pp * r + j];
+    }
+    if (p0 + 16 >= P && ldt > P) {
+      const int64_t pad = ldt - P;
+      for (int64_t q = threadIdx.x; q < r * pad; q += 512) dTt[(q / pad) * ldt + P + q % pad] = 0;
+    }
+    return;
+  }
 
   floatx4 acc[NT];
 #pragma unroll
@@ -586,9 +600,10 @@ size_t lora_bwd_workspace(int64_t M, int64_t K, int64_t N, int64_t r) { return l
 
 static void rows(int ntc, dim3 grid, hipStream_t s, const uint8_t* xc, const uint8_t* xs, const float* xr,
                  int64_t M, int64_t K, const uint16_t* A, int64_t r, uint16_t* T, uint16_t* Tt, int64_t ldt,
-                 const uint16_t* dy, int64_t N, const uint16_t* B, float scale, uint16_t* dT, uint16_t* dTt) {
+                 const uint16_t* dy, int64_t N, const uint16_t* B, float scale, uint16_t* dT, uint16_t* dTt,
+                 int parts = 0x10, const uint16_t* dT_in = nullptr) {
 #define PACT_ROWS(NT) \
-  k_lora_rows<NT><<<grid, 512, 0, s>>>(xc, xs, xr, M, K, A, r, T, Tt, ldt, dy, N, B, scale, dT, dTt)
+  k_lora_rows<NT><<<grid, 512, 0, s>>>(xc, xs, xr, M, K, A, r, T, Tt, ldt, dy, N, B, scale, dT, dTt, parts, dT_in)
   if (ntc <= 1) PACT_ROWS(1);
   else if (ntc <= 2) PACT_ROWS(2);
   else if (ntc <= 4) PACT_ROWS(4);
@@ -605,9 +620,32 @@ hipError_t launch_lora_down(const uint8_t* xc, const uint8_t* xs, const float* x
   return hipGetLastError();
 }
 
+hipError_t launch_lora_bwd_dt(const uint16_t* dy, int64_t M, int64_t N, const uint16_t* B, int64_t r, float scale,
+                              uint16_t* dT, hipStream_t s) {
+  if (M == 0) return hipSuccess;
+  rows(nt_class(r), dim3((unsigned)((M + 15) / 16), 1), s, nullptr, nullptr, nullptr, M, 0, nullptr, r, nullptr,
+       nullptr, 0, dy, N, B, scale, dT, nullptr, 0x1);
+  return hipGetLastError();
+}
+
 hipError_t launch_lora_bwd(const uint8_t* xc, const uint8_t* xs, const float* xr, int64_t M, int64_t K,
                            const uint16_t* A, const uint16_t* B, int64_t r, float scale, const uint16_t* dy,
                            int64_t N, uint16_t* dT, uint16_t* dA, uint16_t* dB, void* workspace, hipStream_t s) {
+  return launch_lora_bwd_impl(xc, xs, xr, M, K, A, B, r, scale, dy, N, dT, nullptr, dA, dB, workspace, s);
+}
+
+hipError_t launch_lora_bwd_ab(const uint8_t* xc, const uint8_t* xs, const float* xr, int64_t M, int64_t K,
+                              const uint16_t* A, int64_t r, float scale, const uint16_t* dy, int64_t N,
+                              const uint16_t* dT, uint16_t* dA, uint16_t* dB, void* workspace, hipStream_t s) {
+  return launch_lora_bwd_impl(xc, xs, xr, M, K, A, nullptr, r, scale, dy, N, nullptr, dT, dA, dB, workspace, s);
+}
+
+// dT_in == nullptr: the whole backward (dT from dY and B); else dT is given
+// (lora_bwd_dt's output) and only dA and dB are formed, with identical results.
+hipError_t launch_lora_bwd_impl(const uint8_t* xc, const uint8_t* xs, const float* xr, int64_t M, int64_t K,
+                                const uint16_t* A, const uint16_t* B, int64_t r, float scale, const uint16_t* dy,
+                                int64_t N, uint16_t* dT, const uint16_t* dT_in, uint16_t* dA, uint16_t* dB,
+                                void* workspace, hipStream_t s) {
   const LoraWs w = lora_ws(M, K, N, r);
   uint8_t* ws = static_cast<uint8_t*>(workspace);
   uint16_t* Tt = reinterpret_cast<uint16_t*>(ws + w.off_Tt);
@@ -622,9 +660,9 @@ hipError_t launch_lora_bwd(const uint8_t* xc, const uint8_t* xs, const float* xr
     if (K * r > 0) k_zero_u16<<<grid_for(K * r), 256, 0, s>>>(dA, K * r);
     return hipGetLastError();
   }
-  // T^T (workspace), dT and dT^T (workspace)
+  // T^T (workspace), dT and dT^T (workspace); or T^T and the copy of the given dT
   rows(ntc, dim3((unsigned)((M + 15) / 16), 2), s, xc, xs, xr, M, K, A, r, nullptr, Tt, w.ldt, dy, N, B, scale, dT,
-       dTt);
+       dTt, dT_in != nullptr ? 0x20 : 0x10, dT_in);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int64_t nblk = (int64_t)w.nstrip_b * w.nsplit_b + (int64_t)w.nstrip_a * w.nsplit_a;

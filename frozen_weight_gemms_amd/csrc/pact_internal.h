@@ -103,6 +103,17 @@ hipError_t lora_scratch_address(void** out);
 hipError_t launch_lora_bwd(const uint8_t* xc, const uint8_t* xs, const float* xr, int64_t M, int64_t K,
                            const uint16_t* A, const uint16_t* B, int64_t r, float scale, const uint16_t* dy,
                            int64_t N, uint16_t* dT, uint16_t* dA, uint16_t* dB, void* workspace, hipStream_t s);
+// dT = bf16(scale dY B) alone (the row kernel's dT part)
+hipError_t launch_lora_bwd_dt(const uint16_t* dy, int64_t M, int64_t N, const uint16_t* B, int64_t r, float scale,
+                              uint16_t* dT, hipStream_t s);
+// dA and dB given dT (lora_bwd_dt's output): the rest of launch_lora_bwd
+hipError_t launch_lora_bwd_ab(const uint8_t* xc, const uint8_t* xs, const float* xr, int64_t M, int64_t K,
+                              const uint16_t* A, int64_t r, float scale, const uint16_t* dy, int64_t N,
+                              const uint16_t* dT, uint16_t* dA, uint16_t* dB, void* workspace, hipStream_t s);
+hipError_t launch_lora_bwd_impl(const uint8_t* xc, const uint8_t* xs, const float* xr, int64_t M, int64_t K,
+                                const uint16_t* A, const uint16_t* B, int64_t r, float scale, const uint16_t* dy,
+                                int64_t N, uint16_t* dT, const uint16_t* dT_in, uint16_t* dA, uint16_t* dB,
+                                void* workspace, hipStream_t s);
 
 hipError_t launch_silu_mul_bwd(const uint8_t* gc, const uint8_t* gs, const float* gr, const uint8_t* uc,
                                const uint8_t* us, const float* ur, const uint16_t* dh, int64_t M, int64_t I,

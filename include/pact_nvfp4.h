@@ -377,6 +377,24 @@ int lora_bwd(const uint8_t *x_codes, const uint8_t *x_scales, const float *x_rsc
              void *workspace, size_t workspace_bytes, void *stream);
 
 /*
+ * lora_bwd_dt / lora_bwd_ab -- lora_bwd in two calls, so that the input
+ * gradient (which needs only dT, through nvfp4_gemm_dgrad's LoRA term) does
+ * not wait for the adapter gradients (which nothing in the step reads before
+ * the optimizer):
+ *   lora_bwd_dt: dT = bf16(s dY B) [M x r] from dY [M x N] and B [N x r];
+ *     no workspace.
+ *   lora_bwd_ab: dB and dA as lora_bwd, given that dT (T recomputed from X_q
+ *     and A); workspace as for lora_bwd (pact_lora_bwd_workspace_size).
+ * Together they write exactly lora_bwd's dT, dA and dB, bit for bit.
+ * Arguments and requirements as lora_bwd.
+ */
+int lora_bwd_dt(const uint16_t *dy, int64_t M, int64_t N, const uint16_t *B, int64_t r, float scale,
+                uint16_t *dT, void *stream);
+int lora_bwd_ab(const uint8_t *x_codes, const uint8_t *x_scales, const float *x_rscale, int64_t M, int64_t K,
+                const uint16_t *A, int64_t r, float scale, const uint16_t *dy, int64_t N, const uint16_t *dT,
+                uint16_t *dA, uint16_t *dB, void *workspace, size_t workspace_bytes, void *stream);
+
+/*
  * lora_bwd_noalloc -- lora_bwd for callers that cannot allocate device memory
  * (code under HIP graph capture, tight serving loops, harnesses that forbid
  * hipMalloc): the same operation, arguments and results as lora_bwd (bit for

@@ -57,7 +57,7 @@ def test_gemm_tile_query(lib):
 
 
 def test_abi_version(lib):
-    assert lib.pact_abi_version() == 11
+    assert lib.pact_abi_version() == 12
 
 
 def test_sizes(lib):

@@ -58,6 +58,11 @@ def test_lora_down_and_bwd(fw, M, K, N, r):
                   tol.gemm_bound(ref["dB_exact"], ref["dB_abs"], ref["dB_tslack"]), "dB")
     assert_within(torch_bf16_to_f64(dA), ref["dA_exact"],
                   tol.gemm_bound(ref["dA_exact"], ref["dA_abs"], ref["dA_tslack"]), "dA")
+    # the same backward in two calls (dT alone, then dA and dB given dT), each
+    # with its own buffers: identical bits
+    dT2 = fw.lora_bwd_dt(bits_to_torch(dy), bits_to_torch(B), s)
+    dA2, dB2 = fw.lora_bwd_ab(gx, bits_to_torch(A), bits_to_torch(dy), dT2, s)
+    assert torch.equal(dT2, dT) and torch.equal(dA2, dA) and torch.equal(dB2, dB), "split backward differs"
 
 
 # ---------------------------------------------------------------- RMSNorm
