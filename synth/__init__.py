@@ -2,13 +2,16 @@
 
 This module holds no arithmetic of the method: it only draws random numbers
 and rounds them to BF16, the precision the LoRA linear layer receives its
-activations, gradients and adapters in (PACT, "Appendix" Table 7).  Both the
+activations, gradients and adapters in (PACT, Appendix Table 7).  Both the
 CPU oracle's tests and the GPU path's tests and benchmark take their inputs
 from here, so each side sees the same tensors.
 
-Every tensor is drawn from ``numpy.random.default_rng([workload_id, tensor_id])``
-in float32 and rounded to BF16 with round-to-nearest-even.  ``N(0, s)`` means
-standard deviation ``s``.
+Test tensors are drawn from ``numpy.random.default_rng([workload_id, tensor_id])``
+in float32 and rounded to BF16 with round-to-nearest-even.  The benchmark's
+large inputs come from the ``*_torch`` functions below: the same
+distributions drawn on the device by torch's generator seeded with
+``(workload_id << 40) + tensor_id``, so multi-GB workloads need no host
+sampling.  ``N(0, s)`` means standard deviation ``s``.
 
 The workloads are the synthetic Llama-shaped projection sets: the pages use
 Llama-1B/3B models and quote Llama-3B projection dimensions in Table 1 (query
