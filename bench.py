@@ -923,12 +923,13 @@ def mxfp4_leg(fw, torch, synth, wl, nlayers, steps, warmup, eager=False):
     torch.cuda.synchronize()
     by_tile = {}
     for e0, e1, (M, N, K) in recs:
-        t = by_tile.setdefault(_lib.gemm_tile(M, N, K), [0.0, 0.0, 0])
+        t = by_tile.setdefault(_lib.gemm_tile(M, N, K), [0.0, 0.0, 0, 0.0])
         t[0] += e0.elapsed_time(e1)
         t[1] += 2.0 * M * N * K
         t[2] += 1
+        t[3] += (M + N) * K * 17 / 32 + 2.0 * M * N       # MXFP4 A and B (codes + E8M0 scales), BF16 C
     dom = max(by_tile, key=lambda k: by_tile[k][0])
-    dt, dfl, dn = by_tile[dom]
+    dt, dfl, dn, dbytes = by_tile[dom]
     ach = dfl / (dt * 1e-3) / 1e12
     flops = sum(ly.gemm_flops() for ly in layers)
     gemm_ms = sum(v[0] for v in by_tile.values()) / nsteps
@@ -952,7 +953,8 @@ def mxfp4_leg(fw, torch, synth, wl, nlayers, steps, warmup, eager=False):
             "roofline": {"kernel": kname, "bound": "mfma",
                          "achieved": round(ach, 1), "peak": PEAK["fp4_mfma_tflops"], "unit": "TFLOP/s",
                          "frac": round(ach / PEAK["fp4_mfma_tflops"], 4), "launches_per_step": dn // nsteps,
-                         "avg_launch_us": round(dt * 1e3 / dn, 2), "traffic": traffic}}
+                         "avg_launch_us": round(dt * 1e3 / dn, 2),
+                         "algorithmic_bytes_per_launch": round(dbytes / dn), "traffic": traffic}}
 
 
 class MxMlpBlock:
