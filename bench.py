@@ -18,9 +18,11 @@ output gradient of the layer below:
             rmsnorm_bwd_residual (+ the output gradient; NVFP4 copy) -> o
             q/k/v (nvfp4_quantize of the attention-backward gradients)
             rmsnorm_bwd_residual (+ the MLP-block residual gradient; NVFP4 copy)
-  per projection: lora_bwd; per input: one NVFP4 dgrad launch with the LoRA
-  input-gradient terms (q/k/v and gate/up each sum into one dX in a single
-  nvfp4_gemm_dgrad_multi launch; down and o alone)
+  per projection: lora_bwd_dt (dT); per input: one NVFP4 dgrad launch with
+  the LoRA input-gradient terms (q/k/v and gate/up each sum into one dX in a
+  single nvfp4_gemm_dgrad_multi launch; down and o alone); per layer, at the
+  end of its backward: lora_bwd_ab_batch (dA and dB of all its projections,
+  from the T that the forward's lora_down left)
 
 The metric is the NVFP4 fwd + dgrad GEMM throughput of the step:
   value = (GEMM FLOPs per step) / (median time per step)   [TFLOP/s]
@@ -67,7 +69,8 @@ sys.path.insert(0, ROOT)
 
 PEAK = {"fp16_mfma_tflops": 2500.0, "fp4_mfma_tflops": 10100.0, "hbm_gbs": 8000.0}
 LORA_SCALE = 2.0
-HEAD_START_CYCLES = 40_000_000      # spin ahead of each instrumented step (about 20 ms)
+HEAD_START_CYCLES = 40_000_000      # spin ahead of a timed launch sequence (about 20 ms)
+STEP_HEAD_START_CYCLES = 100_000_000  # spin ahead of each instrumented step (about 50 ms)
 METRIC = "NVFP4 fwd+dgrad GEMM TFLOP/s at Llama-3B shapes; % FP4 MFMA peak"
 
 
@@ -193,6 +196,8 @@ class Layer:
         self.proj["gate"]["dyq"], self.proj["up"]["dyq"] = self.daq, self.dbq
         self.record = None       # list to append (category, name, start_event, end_event, work) into
         self.streams = None      # side streams: independent branches of the step run concurrently
+        self.ab_jobs = []        # adapter-gradient problems of the backward so far
+        self.ab_plan = None      # (buffer addresses, LoraAbBatch, work) of the last batch
         self.dout = None         # the output gradient this layer received in the last step
 
     # ---- instrumented launch helper ----
@@ -224,12 +229,26 @@ class Layer:
         if dyq is None:
             self._ev("quant", "nvfp4_quantize", ("quant", self.M, p.d_out), lambda: fw.quantize(dy, out=P["dyq"]))
         P["dyq_used"] = dyq if dyq is not None else P["dyq"]     # the NVFP4 dY its input gradient reads
-        # one call (dT, dA, dB).  Splitting it (lora_bwd_dt before the input
-        # gradient, lora_bwd_ab on a stream of its own) shortens the chain but
-        # measured slower: the deferred kernels take CUs from the GEMM tiles.
-        self._ev("lora", "lora_bwd", ("lora_bwd", self.M, p.d_in, p.d_out, self.r),
-                 lambda: fw.lora_bwd(xq, P["A"], P["B"], dy, LORA_SCALE, out=(P["dT"], P["dA"], P["dB"]),
-                                     workspace=P["ws"]))
+        # dT, which the input-gradient GEMM's LoRA term needs, now; dA and dB
+        # (read by nothing else in the step) for every projection of the layer
+        # in one batched call at the end of its backward, from the T that the
+        # forward's lora_down left (X_q A^T is not recomputed).  (On a stream of
+        # their own, beside the GEMMs, the adapter gradients measured slower:
+        # they take CUs from the GEMM's one-workgroup-per-CU tiles.)
+        self._ev("lora", "lora_bwd_dt", ("lora_bwd_dt", self.M, p.d_out, self.r),
+                 lambda: fw.lora_bwd_dt(dy, P["B"], LORA_SCALE, out=P["dT"]))
+        self.ab_jobs.append((xq, P["T"], dy, P["dT"], (P["dA"], P["dB"]), P["ws"]))
+
+    def _adapter_grads(self):
+        jobs, self.ab_jobs = self.ab_jobs, []
+        # the batch's argument arrays are built once: every step passes the
+        # same buffers (checked by their addresses)
+        key = tuple(t.data_ptr() for j in jobs for t in (j[0].codes, j[1], j[2], j[3], j[4][0], j[4][1], j[5]))
+        if self.ab_plan is None or self.ab_plan[0] != key:
+            work = ("lora_ab_batch", tuple((self.M, j[0].cols, j[2].shape[1], j[1].shape[1]) for j in jobs))
+            self.ab_plan = (key, self.fw.LoraAbBatch(jobs, LORA_SCALE), work)
+        _, plan, work = self.ab_plan
+        self._ev("lora", "lora_bwd_ab_batch", work, plan.run)
 
     def _bwd_dgrad(self, name, dyq, dx):
         fw, P = self.fw, self.proj[name]
@@ -307,6 +326,7 @@ class Layer:
                  lambda: fw.rmsnorm_bwd_residual(self.y2q, self.rstd2, self.g2, self.dy2, resid=dout,
                                                  out=(self.dh2, self.dh2q)))
         if self.mlp_only:
+            self._adapter_grads()
             return self.dh2, self.dh2q
         # attention block: h2 = h1 + o(attn(q, k, v of n1)),  n1 = rmsnorm(h1); the
         # attention backward itself is not part of the path (dq, dk, dv are inputs)
@@ -318,6 +338,7 @@ class Layer:
         self._ev("bwd", "rmsnorm_bwd_residual", ("rmsbr", M, H),
                  lambda: fw.rmsnorm_bwd_residual(self.y1q, self.rstd1, self.g1, self.dy1, resid=self.dh2,
                                                  out=(self.dh1, self.dh1q)))
+        self._adapter_grads()
         return self.dh1, self.dh1q
 
     def gemm_flops(self):
@@ -343,6 +364,12 @@ def kernel_bytes(work):
     if kind == "lora_bwd":                   # X_q and dY read once, A, B read; dT, dA, dB written
         _, M, K, N, r = work
         return NV_B * M * K + 4 * M + 2 * M * N + 2 * r * K + 2 * N * r + 2 * M * r + 2 * r * K + 2 * N * r
+    if kind == "lora_bwd_dt":                # dY and B read, dT written
+        _, M, N, r = work
+        return 2 * M * N + 2 * N * r + 2 * M * r
+    if kind == "lora_ab_batch":              # per projection: X_q, T, dY, dT read once; dA, dB written
+        return sum(NV_B * M * K + 4 * M + 2 * M * N + 4 * M * r + 2 * r * K + 2 * N * r
+                   for M, K, N, r in work[1])
     _, rows, cols = work
     return BYTES_PER_ELEM[kind] * rows * cols + BYTES_PER_ROW[kind] * rows
 
@@ -466,16 +493,28 @@ def run_config(fw, torch, synth, wl, nlayers, steps, warmup, instr_steps, args, 
     # the step time comes from).  A spin kernel ahead of each step lets the
     # host enqueue the step's launches before the GPU reaches them, so an event
     # pair brackets the kernel and not the host's launch time.
+    # The pass checks that the host finished enqueueing each step before the
+    # spin ended (else the GPU waited for launches inside the event pairs).
     recs = []
     for ly in layers:
         ly.record = recs
     torch.cuda.synchronize()
+    head_start_ok = True
     for _ in range(instr_steps):
-        torch.cuda._sleep(HEAD_START_CYCLES)
+        s0, s1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        s0.record()
+        torch.cuda._sleep(STEP_HEAD_START_CYCLES)
+        s1.record()
+        h0 = time.perf_counter()
         step()
-    torch.cuda.synchronize()
+        host_ms = (time.perf_counter() - h0) * 1e3
+        torch.cuda.synchronize()
+        head_start_ok = head_start_ok and host_ms < s0.elapsed_time(s1)
     for ly in layers:
         ly.record = None
+    if not head_start_ok:
+        print(f"{wl.name}: the instrumented pass's head start was shorter than the host's enqueue time",
+              file=sys.stderr)
 
     flops = sum(ly.gemm_flops() for ly in layers)
     ms = st["median"]
@@ -561,6 +600,7 @@ def run_config(fw, torch, synth, wl, nlayers, steps, warmup, instr_steps, args, 
         "timed_region": "hip graph replays of the step" if graph is not None else "eager steps",
         "schedule_matches_one_stream": schedule_matches,
         "kernel_ms_per_step_by_category": {k: round(v / instr_steps, 4) for k, v in sorted(cat_ms.items())},
+        "instr_head_start_ok": head_start_ok,
         "bandwidth_kernels": bandwidth,
         "gemm_kernels": gemm_kernels,
         "roofline": {"kernel": kname, "bound": "mfma", "achieved": round(achieved, 1),
@@ -1415,15 +1455,18 @@ def main():
     }
     for k in ("roofline", "cpu_baseline", "parity", "frac_fp4_peak", "frac_fp16_peak", "ms_per_step_min",
               "ms_per_step_mean", "ms_per_step_wall", "timed_ms", "gemm_only_tflops", "timed_region",
-              "schedule_matches_one_stream", "kernel_ms_per_step_by_category", "bandwidth_kernels", "gemm_kernels"):
+              "schedule_matches_one_stream", "kernel_ms_per_step_by_category", "instr_head_start_ok",
+              "bandwidth_kernels", "gemm_kernels"):
         if k in head:
             result[k] = head[k]
     if isinstance(result.get("parity"), dict):
         result["parity_status"] = result["parity"]["status"]
     result["schedule"] = ("stacked q/k/v and gate/up forward GEMMs (stacked LoRA rank <= 128); one "
-                          "input-gradient launch each for q/k/v and gate/up; " +
+                          "input-gradient launch each for q/k/v and gate/up; LoRA dT per projection before its "
+                          "input gradient, every projection's dA and dB (from the forward's T) in one batched call at the end of the "
+                          "layer's backward; " +
                           ("one stream" if args.sequential else
-                           "LoRA backwards of gate/up and q/k/v on 2 side streams"))
+                           "the dT of gate/up and of q/k/v on 2 side streams"))
     if not legs_off and not args.no_configs:
         cfgs = {}
         for wid, nlay, mlp in ((1, 2, False), (3, 2, True), (4, 1, False)):

@@ -383,6 +383,53 @@ def lora_bwd_ab(xq: NVFP4Tensor, A: torch.Tensor, dy: torch.Tensor, dT: torch.Te
     return dA, dB
 
 
+class LoraAbBatch:
+    """dA and dB of several projections in three launches, from the forward's
+    T, with the call's argument arrays built once (every run() reads the
+    tensors' current contents and launches on the current stream).
+    ``problems``: list of (xq, T, dy, dT, (dA, dB), workspace) with one token
+    count; T [M x r] is the projection's lora_down output (a column slice of a
+    stacked lora_down output is accepted: rows may be strided, columns must be
+    contiguous).  run() writes each problem's dA and dB in place (lora_bwd's
+    values, bit for bit, when T = lora_down(xq, A))."""
+
+    def __init__(self, problems, scale: float):
+        import ctypes
+        n = len(problems)
+        M = problems[0][2].shape[0]
+        for xq, T, dy, dT, (dA, dB), ws in problems:
+            _bf16(T, "T"); _dense(_bf16(dy, "dy"), "dy"); _dense(_bf16(dT, "dT"), "dT")
+            _dense(_bf16(dA, "dA"), "dA"); _dense(_bf16(dB, "dB"), "dB")
+            if T.dim() != 2 or T.stride(1) != 1 or T.stride(0) < T.shape[1]:
+                raise ValueError("T must be [M x r] with contiguous columns")
+            r, K = T.shape[1], xq.cols
+            if dy.shape[0] != M or xq.rows != M or T.shape[0] != M or dT.shape != (M, r) or dA.shape != (r, K) \
+                    or dB.shape != (dy.shape[1], r):
+                raise ValueError("shapes: xq [M x K], T [M x r], dy [M x N], dT [M x r], dA [r x K], dB [N x r]")
+        arr = lambda t, f: (t * n)(*[f(p) for p in problems])
+        vp, i64 = ctypes.c_void_p, ctypes.c_int64
+        self.problems = list(problems)          # keeps the tensors alive while the plan exists
+        self.outputs = [p[4] for p in problems]
+        self._args = (n,
+                      arr(vp, lambda p: p[0].codes.data_ptr()), arr(vp, lambda p: p[0].scales.data_ptr()),
+                      arr(vp, lambda p: p[0].rscale.data_ptr()), M, arr(i64, lambda p: p[0].cols),
+                      arr(vp, lambda p: p[1].data_ptr()), arr(i64, lambda p: p[1].stride(0)),
+                      arr(i64, lambda p: p[1].shape[1]), float(scale),
+                      arr(vp, lambda p: p[2].data_ptr()), arr(i64, lambda p: p[2].shape[1]),
+                      arr(vp, lambda p: p[3].data_ptr()), arr(vp, lambda p: p[4][0].data_ptr()),
+                      arr(vp, lambda p: p[4][1].data_ptr()), arr(vp, lambda p: p[5].data_ptr()),
+                      arr(ctypes.c_size_t, lambda p: p[5].numel()))
+
+    def run(self):
+        _lib.call("lora_bwd_ab_batch", *self._args, _stream())
+        return self.outputs
+
+
+def lora_bwd_ab_batch(problems, scale: float):
+    """One run of LoraAbBatch(problems, scale): dA and dB of every problem, in place."""
+    return LoraAbBatch(problems, scale).run()
+
+
 def lora_bwd_noalloc(xq: NVFP4Tensor, A: torch.Tensor, B: torch.Tensor, dy: torch.Tensor, scale: float, out):
     """lora_bwd into caller tensors ``out`` = (dT, dA, dB) with the library's fixed
     per-device scratch instead of a workspace (allocates nothing)."""

@@ -46,6 +46,8 @@ SIGNATURES = {
     "lora_bwd_dt": ([c_vp, c_i64, c_i64, c_vp, c_i64, c_float, c_vp, c_vp], c_int),
     "lora_bwd_ab": ([c_vp, c_vp, c_vp, c_i64, c_i64, c_vp, c_i64, c_float, c_vp, c_i64, c_vp, c_vp, c_vp, c_vp,
                      ctypes.c_size_t, c_vp], c_int),
+    "lora_bwd_ab_batch": ([c_int] + [c_vp] * 3 + [c_i64, c_vp, c_vp, c_vp, c_vp, c_float] + [c_vp] * 7 + [c_vp],
+                          c_int),
     "lora_down": ([c_vp, c_vp, c_vp, c_i64, c_i64, c_vp, c_i64, c_vp, c_vp], c_int),
     "pact_lora_bwd_workspace_size": ([c_i64, c_i64, c_i64, c_i64, c_size_p], c_int),
     "lora_bwd": ([c_vp, c_vp, c_vp, c_i64, c_i64, c_vp, c_vp, c_i64, c_float, c_vp, c_i64,

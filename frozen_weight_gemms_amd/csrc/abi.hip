@@ -69,7 +69,7 @@ extern "C" {
 
 const char* pact_last_error(void) { return g_err; }
 
-int pact_abi_version(void) { return 12; }
+int pact_abi_version(void) { return 13; }
 
 int pact_nvfp4_sizes(int64_t rows, int64_t cols, size_t* codes_bytes, size_t* scales_bytes, size_t* rscale_bytes) {
   REQUIRE(rows >= 0 && cols >= 0, PACT_EINVAL, "negative size (rows=%lld, cols=%lld)", (long long)rows,
@@ -419,6 +419,47 @@ int lora_bwd_ab(const uint8_t* x_codes, const uint8_t* x_scales, const float* x_
   return hip_status(pact::launch_lora_bwd_ab(x_codes, x_scales, x_rscale, M, K, A, r, scale, dy, N, dT, dA, dB,
                                              workspace, as_stream(stream)),
                     "lora_bwd_ab launch");
+}
+
+int lora_bwd_ab_batch(int n, const uint8_t* const* x_codes, const uint8_t* const* x_scales,
+                      const float* const* x_rscale, int64_t M, const int64_t* K, const uint16_t* const* T,
+                      const int64_t* ldT, const int64_t* r, float scale, const uint16_t* const* dy,
+                      const int64_t* N, const uint16_t* const* dT, uint16_t* const* dA, uint16_t* const* dB,
+                      void* const* workspace, const size_t* workspace_bytes, void* stream) {
+  REQUIRE(n >= 1 && n <= pact::kLoraBatch, PACT_EINVAL, "n=%d outside [1, %d]", n, pact::kLoraBatch);
+  REQUIRE(x_codes && x_scales && x_rscale && K && T && ldT && r && dy && N && dT && dA && dB && workspace &&
+              workspace_bytes,
+          PACT_EINVAL, "a problem array is NULL");
+  REQUIRE(M >= 0, PACT_EINVAL, "negative size");
+  REQUIRE((M + 63) / 64 < 0x7FFFFFFF, PACT_EUNSUPPORTED, "M too large");
+  for (int i = 0; i < n; ++i) {
+    REQUIRE(K[i] >= 0 && N[i] >= 0, PACT_EINVAL, "problem %d: negative size", i);
+    REQUIRE(K[i] % 16 == 0 && N[i] % 16 == 0, PACT_ESHAPE, "problem %d: K=%lld and N=%lld must be multiples of 16",
+            i, (long long)K[i], (long long)N[i]);
+    REQUIRE(r[i] >= 1 && r[i] <= kMaxRank, PACT_ESHAPE, "problem %d: rank %lld outside [1, %lld]", i,
+            (long long)r[i], (long long)kMaxRank);
+    REQUIRE(pact::lora_same_rank_class(r[0], r[i]), PACT_EINVAL,
+            "problem %d: rank %lld is not in the rank class of problem 0's rank %lld", i, (long long)r[i],
+            (long long)r[0]);
+    REQUIRE(ldT[i] >= r[i], PACT_ESHAPE, "problem %d: ldT=%lld is below the rank %lld", i, (long long)ldT[i],
+            (long long)r[i]);
+    if (M > 0) {
+      int st = check_nvfp4(x_codes[i], x_scales[i], x_rscale[i], "x");
+      if (st != PACT_OK) return st;
+      REQUIRE(T[i] != nullptr && dy[i] != nullptr && dT[i] != nullptr, PACT_EINVAL,
+              "problem %d: T, dy or dT is NULL", i);
+    }
+    REQUIRE(dA[i] != nullptr && dB[i] != nullptr, PACT_EINVAL, "problem %d: dA or dB is NULL", i);
+    const size_t need = pact::lora_bwd_workspace(M, K[i], N[i], r[i]);
+    REQUIRE(workspace[i] != nullptr, PACT_EINVAL, "problem %d: workspace is NULL (needs %zu bytes)", i, need);
+    REQUIRE((reinterpret_cast<uintptr_t>(workspace[i]) & 255u) == 0, PACT_EALIGN,
+            "problem %d: workspace is not 256-byte aligned", i);
+    REQUIRE(workspace_bytes[i] >= need, PACT_EINVAL, "problem %d: workspace has %zu bytes, needs %zu", i,
+            workspace_bytes[i], need);
+  }
+  return hip_status(pact::launch_lora_bwd_ab_batch(n, x_codes, x_scales, x_rscale, M, K, T, ldT, r, scale, dy, N, dT,
+                                                   dA, dB, workspace, as_stream(stream)),
+                    "lora_bwd_ab_batch launch");
 }
 
 int lora_bwd_noalloc(const uint8_t* x_codes, const uint8_t* x_scales, const float* x_rscale, int64_t M, int64_t K,

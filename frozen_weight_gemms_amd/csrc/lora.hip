@@ -234,23 +234,23 @@ __device__ __forceinline__ void row_reduce(const uint8_t* __restrict__ xc, const
 // given dT (dT_in) into dTt.  The rank-major copies get zeros in their padding
 // columns [P, ldt), which the column kernel reads.  Block row y runs part
 // (parts >> 4y) & 15.
+// One workgroup of the row kernel: token rows 16 bx .. 16 bx + 15, `part`.
 template <int NT>
-__global__ __launch_bounds__(512) void k_lora_rows(const uint8_t* __restrict__ xc, const uint8_t* __restrict__ xs,
-                                                   const float* __restrict__ xr, int64_t P, int64_t K,
-                                                   const uint16_t* __restrict__ A, int64_t r,
-                                                   uint16_t* __restrict__ T, uint16_t* __restrict__ Tt, int64_t ldt,
-                                                   const uint16_t* __restrict__ dy, int64_t N,
-                                                   const uint16_t* __restrict__ B, float scale,
-                                                   uint16_t* __restrict__ dT, uint16_t* __restrict__ dTt,
-                                                   int parts, const uint16_t* __restrict__ dT_in) {
+__device__ __forceinline__ void lora_rows_block(const uint8_t* __restrict__ xc, const uint8_t* __restrict__ xs,
+                                                const float* __restrict__ xr, int64_t P, int64_t K,
+                                                const uint16_t* __restrict__ A, int64_t r,
+                                                uint16_t* __restrict__ T, uint16_t* __restrict__ Tt, int64_t ldt,
+                                                const uint16_t* __restrict__ dy, int64_t N,
+                                                const uint16_t* __restrict__ B, float scale,
+                                                uint16_t* __restrict__ dT, uint16_t* __restrict__ dTt,
+                                                const uint16_t* __restrict__ dT_in, int part, int64_t bx) {
   constexpr int NW = 8;
   constexpr int RT = 16 * NT;
   __shared__ float red[NW][16][RT + 1];
   __shared__ __attribute__((aligned(16))) uint8_t stage[NW][RSTAGE];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int i = lane & 15, g = lane >> 4;
-  const int part = (parts >> (4 * (int)blockIdx.y)) & 15;
-  const int64_t p0 = (int64_t)blockIdx.x * 16;
+  const int64_t p0 = bx * 16;
   if (part == 2) {
     // rank-major copy of the given dT rows p0 .. p0 + 15 (and the padding)
     for (int q = threadIdx.x; q < 16 * r; q += 512) {
@@ -295,6 +295,19 @@ __global__ __launch_bounds__(512) void k_lora_rows(const uint8_t* __restrict__ x
     const int64_t pad = ldt - P;
     for (int64_t q = threadIdx.x; q < r * pad; q += 512) outt[(q / pad) * ldt + P + q % pad] = 0;
   }
+}
+
+template <int NT>
+__global__ __launch_bounds__(512) void k_lora_rows(const uint8_t* __restrict__ xc, const uint8_t* __restrict__ xs,
+                                                   const float* __restrict__ xr, int64_t P, int64_t K,
+                                                   const uint16_t* __restrict__ A, int64_t r,
+                                                   uint16_t* __restrict__ T, uint16_t* __restrict__ Tt, int64_t ldt,
+                                                   const uint16_t* __restrict__ dy, int64_t N,
+                                                   const uint16_t* __restrict__ B, float scale,
+                                                   uint16_t* __restrict__ dT, uint16_t* __restrict__ dTt,
+                                                   int parts, const uint16_t* __restrict__ dT_in) {
+  lora_rows_block<NT>(xc, xs, xr, P, K, A, r, T, Tt, ldt, dy, N, B, scale, dT, dTt, dT_in,
+                      (parts >> (4 * (int)blockIdx.y)) & 15, (int64_t)blockIdx.x);
 }
 
 // ---------------------------------------------------------------------------
@@ -426,14 +439,18 @@ __device__ __forceinline__ void col_mma(const ColStep<NT, CPL>& st, floatx4 (&ac
 
 // Column kernel.  Blocks [0, nstrip_b * nsplit_b) are (strip, split) pairs of
 // dB, the rest of dA; each writes the FP32 partial of its strip and split.
+// One workgroup of the column kernel: block `blk` of the `nblk` blocks of
+// one problem's launch (blocks of different problems start at multiples of 8,
+// so block ids map to XCDs as in a launch of its own).
 template <int NT>
-__global__ __launch_bounds__(256) void k_lora_cols(const uint8_t* __restrict__ xc, const uint8_t* __restrict__ xs,
-                                                   const float* __restrict__ xr, int64_t M, int64_t K,
-                                                   const uint16_t* __restrict__ dy, int64_t N,
-                                                   const uint16_t* __restrict__ Tt, const uint16_t* __restrict__ dTt,
-                                                   int64_t ldt, int64_t r, int nstrip_b, int nsplit_b,
-                                                   int64_t rows_b, int nstrip_a, int64_t rows_a,
-                                                   float* __restrict__ part_b, float* __restrict__ part_a) {
+__device__ __forceinline__ void lora_cols_block(const uint8_t* __restrict__ xc, const uint8_t* __restrict__ xs,
+                                                const float* __restrict__ xr, int64_t M, int64_t K,
+                                                const uint16_t* __restrict__ dy, int64_t N,
+                                                const uint16_t* __restrict__ Tt, const uint16_t* __restrict__ dTt,
+                                                int64_t ldt, int64_t r, int nstrip_b, int nsplit_b,
+                                                int64_t rows_b, int nstrip_a, int64_t rows_a,
+                                                float* __restrict__ part_b, float* __restrict__ part_a, int blk,
+                                                int nblk) {
   constexpr int CPL = ColCfg<NT>::CPL;
   constexpr int SW = 16 * CPL;
   __shared__ floatx4 red[4][CPL][NT][64];
@@ -445,10 +462,10 @@ __global__ __launch_bounds__(256) void k_lora_cols(const uint8_t* __restrict__ x
   // token rows, so the cache lines of a row (codes, scales, BF16) that
   // neighbouring strips share are fetched into one L2.
   const int nb = nstrip_b * nsplit_b;
-  const bool is_b = (int)blockIdx.x < nb;
-  int bid = is_b ? (int)blockIdx.x : (int)blockIdx.x - nb;
+  const bool is_b = blk < nb;
+  int bid = is_b ? blk : blk - nb;
   const int nstrip = is_b ? nstrip_b : nstrip_a;
-  const int npart = is_b ? nb : (int)gridDim.x - nb;
+  const int npart = is_b ? nb : nblk - nb;
   if ((npart & 7) == 0 && ((is_b ? 0 : nb) & 7) == 0) bid = (bid & 7) * (npart >> 3) + (bid >> 3);
   const int strip = bid % nstrip, split = bid / nstrip;
   const int64_t rows_per_split = is_b ? rows_b : rows_a;
@@ -502,16 +519,30 @@ __global__ __launch_bounds__(256) void k_lora_cols(const uint8_t* __restrict__ x
 
 }
 
+template <int NT>
+__global__ __launch_bounds__(256) void k_lora_cols(const uint8_t* __restrict__ xc, const uint8_t* __restrict__ xs,
+                                                   const float* __restrict__ xr, int64_t M, int64_t K,
+                                                   const uint16_t* __restrict__ dy, int64_t N,
+                                                   const uint16_t* __restrict__ Tt, const uint16_t* __restrict__ dTt,
+                                                   int64_t ldt, int64_t r, int nstrip_b, int nsplit_b,
+                                                   int64_t rows_b, int nstrip_a, int64_t rows_a,
+                                                   float* __restrict__ part_b, float* __restrict__ part_a) {
+  lora_cols_block<NT>(xc, xs, xr, M, K, dy, N, Tt, dTt, ldt, r, nstrip_b, nsplit_b, rows_b, nstrip_a, rows_a, part_b,
+                      part_a, (int)blockIdx.x, (int)gridDim.x);
+}
+
 // Sum of the split partials in split order, rounded to BF16: dB [N x r]
 // (times `scale`) for the first N*r elements, then dA [r x K] (stored
 // transposed from the [K x r] partials).  A thread owns 4 consecutive elements
 // and issues the loads of 8 splits before adding them, in split order.
-__global__ __launch_bounds__(256) void k_lora_reduce(const float* __restrict__ part_b,
-                                                     const float* __restrict__ part_a, int nsplit_b, int nsplit_a,
-                                                     int64_t N, int64_t K, int64_t r, float scale,
-                                                     uint16_t* __restrict__ dB, uint16_t* __restrict__ dA) {
+// Block `blk` of `nblk` of one problem's reduce (a grid-stride loop, so every
+// output is formed by one thread in the same order whatever the grid).
+__device__ __forceinline__ void lora_reduce_block(const float* __restrict__ part_b, const float* __restrict__ part_a,
+                                                  int nsplit_b, int nsplit_a, int64_t N, int64_t K, int64_t r,
+                                                  float scale, uint16_t* __restrict__ dB, uint16_t* __restrict__ dA,
+                                                  int64_t blk, int64_t nblk) {
   const int64_t nb4 = N * r / 4, total4 = nb4 + K * r / 4;       // N * r and K * r are multiples of 16
-  for (int64_t q = (int64_t)blockIdx.x * 256 + threadIdx.x; q < total4; q += (int64_t)gridDim.x * 256) {
+  for (int64_t q = blk * 256 + threadIdx.x; q < total4; q += nblk * 256) {
     const bool is_b = q < nb4;
     const int64_t qq = is_b ? q : q - nb4;
     const int64_t stride = is_b ? N * r : K * r;
@@ -542,6 +573,89 @@ __global__ __launch_bounds__(256) void k_lora_reduce(const float* __restrict__ p
       }
     }
   }
+}
+
+__global__ __launch_bounds__(256) void k_lora_reduce(const float* __restrict__ part_b,
+                                                     const float* __restrict__ part_a, int nsplit_b, int nsplit_a,
+                                                     int64_t N, int64_t K, int64_t r, float scale,
+                                                     uint16_t* __restrict__ dB, uint16_t* __restrict__ dA) {
+  lora_reduce_block(part_b, part_a, nsplit_b, nsplit_a, N, K, r, scale, dB, dA, (int64_t)blockIdx.x,
+                    (int64_t)gridDim.x);
+}
+
+// ---------------------------------------------------------------------------
+// Batched adapter gradients: dA and dB of up to kLoraBatch problems (each with
+// its own X_q, A, dY, dT, workspace and shapes; one token count M and one
+// scale) in three launches, each problem's blocks running exactly the
+// single-problem code above, so the results are those of lora_bwd_ab.
+// ---------------------------------------------------------------------------
+struct LoraProb {
+  const uint8_t* xc;
+  const uint8_t* xs;
+  const float* xr;
+  const uint16_t* T;                     // [M x r], leading dimension ldT
+  const uint16_t* dy;
+  const uint16_t* dT;
+  uint16_t* dA;
+  uint16_t* dB;
+  uint16_t* Tt;
+  uint16_t* dTt;
+  float* pdB;
+  float* pdA;
+  int64_t K, N, r, ldT, ldt, rows_b, rows_a;
+  int nstrip_b, nsplit_b, nstrip_a, nsplit_a;
+  int cols_begin, cols_end;              // block range in the column launch (begin % 8 == 0)
+  int red_begin, red_end;                // block range in the reduce launch
+};
+struct LoraBatch {
+  LoraProb p[kLoraBatch];
+  int n;
+  int64_t M;
+  float scale;
+};
+
+// The rank-major copies the column kernel reads, of every problem of a batch:
+// Tt[j][m] = T[m][j] (T with leading dimension ldT) and dTt[j][m] = dT[m][j],
+// with zeros in the padding columns [M, ldt).  Workgroup (x, p): rows
+// 64 x .. 64 x + 63 of problem p; consecutive threads write consecutive rows.
+__global__ __launch_bounds__(256) void k_lora_tt_batch(LoraBatch b) {
+  const LoraProb& q = b.p[blockIdx.y];
+  const int64_t P = b.M, r = q.r;
+  const int64_t p0 = (int64_t)blockIdx.x * 64;
+  for (int64_t k = threadIdx.x; k < 64 * r; k += 256) {
+    const int64_t j = k >> 6, pp = p0 + (k & 63);
+    if (pp < P) {
+      q.Tt[j * q.ldt + pp] = q.T[pp * q.ldT + j];
+      q.dTt[j * q.ldt + pp] = q.dT[pp * r + j];
+    }
+  }
+  if (p0 + 64 >= P && q.ldt > P) {
+    const int64_t pad = q.ldt - P;
+    for (int64_t k = threadIdx.x; k < r * pad; k += 256) {
+      q.Tt[(k / pad) * q.ldt + P + k % pad] = 0;
+      q.dTt[(k / pad) * q.ldt + P + k % pad] = 0;
+    }
+  }
+}
+
+template <int NT>
+__global__ __launch_bounds__(256) void k_lora_cols_batch(LoraBatch b) {
+  const int g = (int)blockIdx.x;
+  int pi = 0;
+  while (pi + 1 < b.n && g >= b.p[pi + 1].cols_begin) ++pi;
+  const LoraProb& q = b.p[pi];
+  if (g >= q.cols_end) return;                        // alignment padding: the whole block leaves
+  lora_cols_block<NT>(q.xc, q.xs, q.xr, b.M, q.K, q.dy, q.N, q.Tt, q.dTt, q.ldt, q.r, q.nstrip_b, q.nsplit_b,
+                      q.rows_b, q.nstrip_a, q.rows_a, q.pdB, q.pdA, g - q.cols_begin, q.cols_end - q.cols_begin);
+}
+
+__global__ __launch_bounds__(256) void k_lora_reduce_batch(LoraBatch b) {
+  const int g = (int)blockIdx.x;
+  int pi = 0;
+  while (pi + 1 < b.n && g >= b.p[pi + 1].red_begin) ++pi;
+  const LoraProb& q = b.p[pi];
+  lora_reduce_block(q.pdB, q.pdA, q.nsplit_b, q.nsplit_a, q.N, q.K, q.r, b.scale, q.dB, q.dA,
+                    (int64_t)(g - q.red_begin), (int64_t)(q.red_end - q.red_begin));
 }
 
 __global__ __launch_bounds__(256) void k_zero_u16(uint16_t* __restrict__ p, int64_t n) {
@@ -679,6 +793,61 @@ hipError_t launch_lora_bwd_impl(const uint8_t* xc, const uint8_t* xs, const floa
   if ((e = hipGetLastError()) != hipSuccess) return e;
   const int64_t tot4 = (N + K) * r / 4;
   k_lora_reduce<<<grid_for(tot4), 256, 0, s>>>(pdB, pdA, (int)w.nsplit_b, (int)w.nsplit_a, N, K, r, scale, dB, dA);
+  return hipGetLastError();
+}
+
+bool lora_same_rank_class(int64_t r0, int64_t r1) { return nt_class(r0) == nt_class(r1); }
+
+hipError_t launch_lora_bwd_ab_batch(int n, const uint8_t* const* xc, const uint8_t* const* xs,
+                                    const float* const* xr, int64_t M, const int64_t* K,
+                                    const uint16_t* const* T, const int64_t* ldT, const int64_t* r, float scale,
+                                    const uint16_t* const* dy, const int64_t* N, const uint16_t* const* dT,
+                                    uint16_t* const* dA, uint16_t* const* dB, void* const* ws, hipStream_t s) {
+  if (n <= 0) return hipSuccess;
+  if (M == 0) {
+    for (int i = 0; i < n; ++i) {
+      if (N[i] * r[i] > 0) k_zero_u16<<<grid_for(N[i] * r[i]), 256, 0, s>>>(dB[i], N[i] * r[i]);
+      if (K[i] * r[i] > 0) k_zero_u16<<<grid_for(K[i] * r[i]), 256, 0, s>>>(dA[i], K[i] * r[i]);
+    }
+    return hipGetLastError();
+  }
+  LoraBatch b{};
+  b.n = n;
+  b.M = M;
+  b.scale = scale;
+  int cols = 0, red = 0;
+  for (int i = 0; i < n; ++i) {
+    const LoraWs w = lora_ws(M, K[i], N[i], r[i]);
+    uint8_t* base = static_cast<uint8_t*>(ws[i]);
+    LoraProb& q = b.p[i];
+    q.xc = xc[i]; q.xs = xs[i]; q.xr = xr[i]; q.T = T[i]; q.dy = dy[i]; q.dT = dT[i]; q.dA = dA[i]; q.dB = dB[i];
+    q.Tt = reinterpret_cast<uint16_t*>(base + w.off_Tt);
+    q.dTt = reinterpret_cast<uint16_t*>(base + w.off_dTt);
+    q.pdB = reinterpret_cast<float*>(base + w.off_pdB);
+    q.pdA = reinterpret_cast<float*>(base + w.off_pdA);
+    q.K = K[i]; q.N = N[i]; q.r = r[i]; q.ldT = ldT[i]; q.ldt = w.ldt; q.rows_b = w.rows_b; q.rows_a = w.rows_a;
+    q.nstrip_b = w.nstrip_b; q.nsplit_b = (int)w.nsplit_b; q.nstrip_a = w.nstrip_a; q.nsplit_a = (int)w.nsplit_a;
+    const int nblk = (int)((int64_t)w.nstrip_b * w.nsplit_b + (int64_t)w.nstrip_a * w.nsplit_a);
+    q.cols_begin = cols;
+    q.cols_end = cols + nblk;
+    cols = (q.cols_end + 7) / 8 * 8;
+    q.red_begin = red;
+    q.red_end = red + (int)grid_for((N[i] + K[i]) * r[i] / 4);
+    red = q.red_end;
+  }
+  k_lora_tt_batch<<<dim3((unsigned)((M + 63) / 64), (unsigned)n), 256, 0, s>>>(b);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  if (cols > 0) {
+    const int ntc = nt_class(r[0]);
+    if (ntc <= 1) k_lora_cols_batch<1><<<(unsigned)cols, 256, 0, s>>>(b);
+    else if (ntc <= 2) k_lora_cols_batch<2><<<(unsigned)cols, 256, 0, s>>>(b);
+    else if (ntc <= 4) k_lora_cols_batch<4><<<(unsigned)cols, 256, 0, s>>>(b);
+    else k_lora_cols_batch<8><<<(unsigned)cols, 256, 0, s>>>(b);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  k_lora_reduce_batch<<<(unsigned)red, 256, 0, s>>>(b);
   return hipGetLastError();
 }
 

@@ -98,6 +98,19 @@ size_t lora_bwd_workspace(int64_t M, int64_t K, int64_t N, int64_t r);
 // fixed per-device scratch of lora_bwd_noalloc (a device array; its address on
 // the current device is looked up once per device)
 constexpr size_t kLoraScratchBytes = (size_t)32 << 20;
+// problems per batched adapter-gradient launch (lora_bwd_ab_batch)
+constexpr int kLoraBatch = 8;
+// dA and dB of n <= kLoraBatch problems given T and dT; problem i: X_q
+// (xc[i], xs[i], xr[i]) [M x K[i]], T[i] [M x r[i]] with leading dimension
+// ldT[i], dY dy[i] [M x N[i]], dT[i] [M x r[i]], outputs dA[i], dB[i], its own
+// workspace ws[i] (at least lora_bwd_workspace(M, K[i], N[i], r[i]) bytes).
+// Every r[i] in one rank class.
+hipError_t launch_lora_bwd_ab_batch(int n, const uint8_t* const* xc, const uint8_t* const* xs,
+                                    const float* const* xr, int64_t M, const int64_t* K,
+                                    const uint16_t* const* T, const int64_t* ldT, const int64_t* r, float scale,
+                                    const uint16_t* const* dy, const int64_t* N, const uint16_t* const* dT,
+                                    uint16_t* const* dA, uint16_t* const* dB, void* const* ws, hipStream_t s);
+bool lora_same_rank_class(int64_t r0, int64_t r1);
 hipError_t lora_scratch_address(void** out);
 
 hipError_t launch_lora_bwd(const uint8_t* xc, const uint8_t* xs, const float* xr, int64_t M, int64_t K,

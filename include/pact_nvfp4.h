@@ -395,6 +395,29 @@ int lora_bwd_ab(const uint8_t *x_codes, const uint8_t *x_scales, const float *x_
                 uint16_t *dA, uint16_t *dB, void *workspace, size_t workspace_bytes, void *stream);
 
 /*
+ * lora_bwd_ab_batch -- the adapter gradients dA and dB of n (1..8) projections
+ * in three launches (for example every projection of a decoder layer once its
+ * backward has run), from the forward's T instead of a recomputed one (the
+ * LoRA branch of Appendix Table 7: dB = s dY^T T, dA = dT^T X~).  Problem i
+ * has X_q (x_codes[i], x_scales[i], x_rscale[i]) [M x K[i]], T[i] [M x r[i]]
+ * with leading dimension ldT[i] >= r[i] (lora_down's output for the
+ * projection's adapter: a column slice of a stacked lora_down's output is
+ * fine), dY dy[i] [M x N[i]], dT[i] [M x r[i]] (lora_bwd_dt's output),
+ * outputs dA[i] [r[i] x K[i]] and dB[i] [N[i] x r[i]], and its own workspace
+ * (workspace[i], workspace_bytes[i] >= pact_lora_bwd_workspace_size(M, K[i],
+ * N[i], r[i]), 256-byte aligned).  One token count M and one scale for all.
+ * Every r[i] must be in the rank class of r[0] (1-16, 17-32, 33-64 or
+ * 65-128), else PACT_EINVAL.  With T[i] = lora_down(X_q, A[i]) each
+ * problem's dA and dB equal lora_bwd's bit for bit.  The arrays are host
+ * arrays of device pointers (sizes on the host).
+ */
+int lora_bwd_ab_batch(int n, const uint8_t *const *x_codes, const uint8_t *const *x_scales,
+                      const float *const *x_rscale, int64_t M, const int64_t *K, const uint16_t *const *T,
+                      const int64_t *ldT, const int64_t *r, float scale, const uint16_t *const *dy,
+                      const int64_t *N, const uint16_t *const *dT, uint16_t *const *dA, uint16_t *const *dB,
+                      void *const *workspace, const size_t *workspace_bytes, void *stream);
+
+/*
  * lora_bwd_noalloc -- lora_bwd for callers that cannot allocate device memory
  * (code under HIP graph capture, tight serving loops, harnesses that forbid
  * hipMalloc): the same operation, arguments and results as lora_bwd (bit for

@@ -134,3 +134,62 @@ def test_silu_mul_bwd(fw, M, I):
     da, db, cda, cdb = obwd.silu_mul_bwd(aq, bq, bf16_values(dh))
     assert_within(torch_bf16_to_f64(dg), da, tol.grad_bound(da, cda), "dgate")
     assert_within(torch_bf16_to_f64(du), db, tol.grad_bound(db, cdb), "dup")
+
+
+def test_lora_bwd_ab_batch_equals_single_calls(fw):
+    """The batched adapter gradients of several projections (different K, N
+    and ranks of one class, ragged M), each from the forward's T (lora_down,
+    also a column slice of a stacked lora_down), equal each projection's
+    lora_bwd bit for bit, and ranks of different classes are refused."""
+    from frozen_weight_gemms_amd import _lib
+    M, s = 300, 0.75
+    shapes = [(256, 272, 16), (512, 128, 5), (272, 1024, 9), (1024, 256, 16), (128, 128, 1)]
+    probs, refs = [], []
+    for k, (K, N, r) in enumerate(shapes):
+        x = synth.activations_bf16((M, K), 94, 10 * k)
+        A = bits_to_torch(synth.normal_bf16((r, K), 0.01, 94, 10 * k + 1))
+        B = bits_to_torch(synth.normal_bf16((N, r), 0.01, 94, 10 * k + 2))
+        dy = bits_to_torch(synth.normal_bf16((M, N), 0.01, 94, 10 * k + 3))
+        gx = nvfp4_to_gpu(_q(x))
+        refs.append(fw.lora_bwd(gx, A, B, dy, s))
+        dT = fw.lora_bwd_dt(dy, B, s)
+        out = (torch.full((r, K), 7.0, dtype=torch.bfloat16, device="cuda"),
+               torch.full((N, r), 7.0, dtype=torch.bfloat16, device="cuda"))
+        probs.append((gx, fw.lora_down(gx, A), dy, dT, out, fw.lora_bwd_workspace(M, K, N, r), A, B))
+    # two projections over one input with their adapters stacked in one lora_down
+    gx0, A0, A1 = probs[0][0], probs[0][6], probs[3][6][:, :256]
+    Ts = fw.lora_down(gx0, torch.cat([A0, A1]).contiguous())
+    B1 = probs[3][7]
+    ref_st = fw.lora_bwd(gx0, A1.contiguous(), B1, probs[3][2], s)
+    out_st = (torch.empty((16, 256), dtype=torch.bfloat16, device="cuda"), torch.empty_like(ref_st[2]))
+    dT_st = fw.lora_bwd_dt(probs[3][2], B1, s)
+    fw.lora_bwd_ab_batch([p[:6] for p in probs] + [(gx0, Ts[:, 16:32], probs[3][2], dT_st, out_st,
+                                                   fw.lora_bwd_workspace(M, 256, 256, 16))], s)
+    for (dT_ref, dA_ref, dB_ref), p in zip(refs, probs):
+        assert torch.equal(p[3], dT_ref)
+        assert torch.equal(p[4][0], dA_ref) and torch.equal(p[4][1], dB_ref), "batched dA / dB differ"
+    assert torch.equal(Ts[:, :16], probs[0][1]), "stacked lora_down T differs from the single one"
+    assert torch.equal(out_st[0], ref_st[1]) and torch.equal(out_st[1], ref_st[2]), "stacked-T problem differs"
+    # one problem, and the Llama-3B gate shape (token splits of the big shapes)
+    fw.lora_bwd_ab_batch([probs[0][:6]], s)
+    assert torch.equal(probs[0][4][0], refs[0][1])
+    M2, K2, N2, r2 = 4096, 3072, 8192, 16
+    x = synth.activations_bf16((M2, K2), 94, 99)
+    A = bits_to_torch(synth.normal_bf16((r2, K2), 0.01, 94, 100))
+    B = bits_to_torch(synth.normal_bf16((N2, r2), 0.01, 94, 101))
+    dy = bits_to_torch(synth.normal_bf16((M2, N2), 0.01, 94, 102))
+    gx = nvfp4_to_gpu(_q(x))
+    dT, dA, dB = fw.lora_bwd(gx, A, B, dy, s)
+    out = (torch.empty_like(dA), torch.empty_like(dB))
+    fw.lora_bwd_ab_batch([(gx, fw.lora_down(gx, A), dy, dT, out, fw.lora_bwd_workspace(M2, K2, N2, r2))], s)
+    assert torch.equal(out[0], dA) and torch.equal(out[1], dB)
+    # ranks of different classes in one batch
+    bad = [probs[0][:6]]
+    gx, T, dy, dT, _, ws = probs[0][:6]
+    T32 = torch.zeros((M, 32), dtype=torch.bfloat16, device="cuda")
+    dT32 = torch.zeros((M, 32), dtype=torch.bfloat16, device="cuda")
+    bad.append((gx, T32, dy, dT32, (torch.empty((32, gx.cols), dtype=torch.bfloat16, device="cuda"),
+                                    torch.empty((dy.shape[1], 32), dtype=torch.bfloat16, device="cuda")),
+                fw.lora_bwd_workspace(M, gx.cols, dy.shape[1], 32)))
+    with pytest.raises(_lib.PactError):
+        fw.lora_bwd_ab_batch(bad, s)
