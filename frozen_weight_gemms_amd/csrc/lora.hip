@@ -107,6 +107,11 @@ __device__ __forceinline__ uint4 load_b8(const uint16_t* __restrict__ B, int64_t
   return make_uint4(w[0], w[1], w[2], w[3]);
 }
 
+// A of lora_down / the T part is loaded row-contiguously and laid out for the
+// MFMA through LDS up to 4 rank tiles (8 would spill)
+template <int NT>
+constexpr bool kRowTileA = NT <= 4;
+
 template <int NT, bool NVFP4>
 __device__ __forceinline__ void row_reduce(const uint8_t* __restrict__ xc, const uint8_t* __restrict__ xs,
                                            const uint16_t* __restrict__ lb, int64_t p0, int64_t P, int64_t R,
@@ -118,7 +123,8 @@ __device__ __forceinline__ void row_reduce(const uint8_t* __restrict__ xc, const
   for (int64_t cb = wave; cb < nchunk; cb += 8 * CH) {
     uint4 lv[CH][4];          // BF16: instruction v holds rows 4v + lane/16, elements 8 (lane % 16) + (0..7)
     uint32_t lsc[CH][2];      // NVFP4: scale bytes of row lane/4, blocks 2 (lane % 4) and + 1
-    uint4 sv[CH][NT][4];      // A: MFMA operand of sub-step u; B: rows 32v + lane/2, columns 16t + 8 (lane % 2) + (0..7)
+    uint4 sv[CH][NT][4];      // A: rows 16t + 4v + lane/16, elements 8 (lane % 16) + (0..7) (NT <= 4; else the
+                              // MFMA operand of sub-step u); B: rows 32v + lane/2, columns 16t + 8 (lane % 2) + (0..7)
 #pragma unroll
     for (int q = 0; q < CH; ++q) {
       const int64_t c = cb + 8 * q;
@@ -149,7 +155,21 @@ __device__ __forceinline__ void row_reduce(const uint8_t* __restrict__ xc, const
       }
 #pragma unroll
       for (int t = 0; t < NT; ++t) {
-        if constexpr (NVFP4) {
+        if constexpr (NVFP4 && kRowTileA<NT>) {
+          // A rows 16 t + 4 v + lane / 16, elements 8 (lane % 16) .. + 7 of the
+          // chunk: four whole rows per instruction (full cache lines); the MFMA
+          // layout is formed through the wave's LDS tile below
+#pragma unroll
+          for (int v = 0; v < 4; ++v) {
+            const int64_t j = 16 * t + 4 * v + (lane >> 4);
+            const int64_t k = c * 128 + 8 * (lane & 15);
+            const bool ok = cin && j < r && k + 8 <= R;
+            sv[q][t][v] = load_or_zero(reinterpret_cast<const uint4*>(S + j * R + k),
+                                       reinterpret_cast<const uint4*>(S), ok);
+          }
+        } else if constexpr (NVFP4) {
+          // A in the MFMA layout directly (lane (i, g): row 16 t + i, elements
+          // 32 u + 8 g .. + 7), half a cache line per row and instruction
           const int64_t j = 16 * t + i;
 #pragma unroll
           for (int u = 0; u < 4; ++u) {
@@ -195,7 +215,19 @@ __device__ __forceinline__ void row_reduce(const uint8_t* __restrict__ xc, const
 #pragma unroll
       for (int t = 0; t < NT; ++t) {
         uint4 bv[4];
-        if constexpr (NVFP4) {
+        if constexpr (NVFP4 && kRowTileA<NT>) {
+          // A tile (16 rows x 256 bytes) into the wave's LDS tile as loaded, read
+          // back as lane (i, g): row 16 t + i, elements 32 u + 8 g .. + 7
+#pragma unroll
+          for (int v = 0; v < 4; ++v)
+            *reinterpret_cast<uint4*>(stage + (4 * v + (lane >> 4)) * RL_STRIDE + 16 * (lane & 15)) = sv[q][t][v];
+          __builtin_amdgcn_s_waitcnt(0xc07f);
+          __builtin_amdgcn_wave_barrier();
+#pragma unroll
+          for (int u = 0; u < 4; ++u) bv[u] = *reinterpret_cast<const uint4*>(stage + i * RL_STRIDE + 64 * u + 16 * g);
+          __builtin_amdgcn_s_waitcnt(0xc07f);         // reads done before the tile is overwritten
+          __builtin_amdgcn_wave_barrier();
+        } else if constexpr (NVFP4) {
 #pragma unroll
           for (int u = 0; u < 4; ++u) bv[u] = sv[q][t][u];
         } else {
