@@ -70,7 +70,7 @@ sys.path.insert(0, ROOT)
 PEAK = {"fp16_mfma_tflops": 2500.0, "fp4_mfma_tflops": 10100.0, "hbm_gbs": 8000.0}
 LORA_SCALE = 2.0
 HEAD_START_CYCLES = 40_000_000      # spin ahead of a timed launch sequence (about 20 ms)
-STEP_HEAD_START_CYCLES = 100_000_000  # spin ahead of each instrumented step (about 50 ms)
+STEP_HEAD_START_CYCLES = 200_000_000  # spin ahead of each instrumented step (about 100 ms)
 METRIC = "NVFP4 fwd+dgrad GEMM TFLOP/s at Llama-3B shapes; % FP4 MFMA peak"
 
 
@@ -197,7 +197,8 @@ class Layer:
         self.record = None       # list to append (category, name, start_event, end_event, work) into
         self.streams = None      # side streams: independent branches of the step run concurrently
         self.ab_jobs = []        # adapter-gradient problems of the backward so far
-        self.ab_plan = None      # (buffer addresses, LoraAbBatch, work) of the last batch
+        self.ab_plan = {}        # batch tag -> (buffer addresses, LoraAbBatch, work)
+        self.pending = None      # list (shared by the layers) of side-stream work the next GEMM waits for
         self.dout = None         # the output gradient this layer received in the last step
 
     # ---- instrumented launch helper ----
@@ -239,20 +240,44 @@ class Layer:
                  lambda: fw.lora_bwd_dt(dy, P["B"], LORA_SCALE, out=P["dT"]))
         self.ab_jobs.append((xq, P["T"], dy, P["dT"], (P["dA"], P["dB"]), P["ws"]))
 
-    def _adapter_grads(self):
+    def _adapter_grads(self, tag):
+        """dA and dB of the projections whose dT is done (one batched call).
+        Nothing later in the step reads them, so with side streams the batch
+        runs on a stream of its own beside the next non-GEMM kernels, and the
+        next input-gradient GEMM waits for it (GEMM tiles fill every CU, so a
+        batch running beside one would delay its tiles)."""
         jobs, self.ab_jobs = self.ab_jobs, []
         # the batch's argument arrays are built once: every step passes the
         # same buffers (checked by their addresses)
         key = tuple(t.data_ptr() for j in jobs for t in (j[0].codes, j[1], j[2], j[3], j[4][0], j[4][1], j[5]))
-        if self.ab_plan is None or self.ab_plan[0] != key:
+        if tag not in self.ab_plan or self.ab_plan[tag][0] != key:
             work = ("lora_ab_batch", tuple((self.M, j[0].cols, j[2].shape[1], j[1].shape[1]) for j in jobs))
-            self.ab_plan = (key, self.fw.LoraAbBatch(jobs, LORA_SCALE), work)
-        _, plan, work = self.ab_plan
-        self._ev("lora", "lora_bwd_ab_batch", work, plan.run)
+            self.ab_plan[tag] = (key, self.fw.LoraAbBatch(jobs, LORA_SCALE), work)
+        _, plan, work = self.ab_plan[tag]
+        if self.streams is None or self.record is not None or self.pending is None:
+            self._ev("lora", "lora_bwd_ab_batch", work, plan.run)
+            return
+        torch = self.torch
+        cur, st = torch.cuda.current_stream(), self.streams[-1]
+        st.wait_stream(cur)
+        with torch.cuda.stream(st):
+            plan.run()
+        ev = torch.cuda.Event()
+        ev.record(st)
+        self.pending.append(ev)
+
+    def join(self):
+        """The current stream waits for the side-stream work started so far."""
+        if self.pending:
+            cur = self.torch.cuda.current_stream()
+            for ev in self.pending:
+                cur.wait_event(ev)
+            self.pending.clear()
 
     def _bwd_dgrad(self, name, dyq, dx):
         fw, P = self.fw, self.proj[name]
         p = P["p"]
+        self.join()
         self._ev("gemm", f"dgrad {name}", ("gemm", self.M, p.d_in, (p.d_out,), False),
                  lambda: fw.gemm_dgrad(dyq, P["wb"], out=dx, lora_dt=P["dT"], lora_a=P["A"]))
 
@@ -261,6 +286,7 @@ class Layer:
         input (each with its LoRA term dT A)."""
         fw = self.fw
         Ps = [self.proj[n] for n in names]
+        self.join()
         work = ("gemm", self.M, Ps[0]["p"].d_in, tuple(P["p"].d_out for P in Ps), False)
         self._ev("gemm", "dgrad " + "/".join(names), work,
                  lambda: fw.gemm_dgrad_multi([(P["dyq"], P["wb"]) for P in Ps], out=dx,
@@ -322,11 +348,11 @@ class Layer:
         self._branches([lambda: self._bwd_lora("gate", self.y2q, self.da, self.daq),
                         lambda: self._bwd_lora("up", self.y2q, self.db, self.dbq)])
         self._bwd_dgrad_multi(("gate", "up"), self.dy2)
+        self._adapter_grads("mlp")
         self._ev("bwd", "rmsnorm_bwd_residual", ("rmsbr", M, H),
                  lambda: fw.rmsnorm_bwd_residual(self.y2q, self.rstd2, self.g2, self.dy2, resid=dout,
                                                  out=(self.dh2, self.dh2q)))
         if self.mlp_only:
-            self._adapter_grads()
             return self.dh2, self.dh2q
         # attention block: h2 = h1 + o(attn(q, k, v of n1)),  n1 = rmsnorm(h1); the
         # attention backward itself is not part of the path (dq, dk, dv are inputs)
@@ -335,10 +361,10 @@ class Layer:
         self._branches([lambda n=n, d=d: self._bwd_lora(n, self.y1q, d)
                         for n, d in (("q", self.dq), ("k", self.dk), ("v", self.dv))])
         self._bwd_dgrad_multi(("q", "k", "v"), self.dy1)
+        self._adapter_grads("attn")
         self._ev("bwd", "rmsnorm_bwd_residual", ("rmsbr", M, H),
                  lambda: fw.rmsnorm_bwd_residual(self.y1q, self.rstd1, self.g1, self.dy1, resid=self.dh2,
                                                  out=(self.dh1, self.dh1q)))
-        self._adapter_grads()
         return self.dh1, self.dh1q
 
     def gemm_flops(self):
@@ -409,9 +435,11 @@ def stats(ms):
 def run_config(fw, torch, synth, wl, nlayers, steps, warmup, instr_steps, args, mlp_only=False, check=True):
     from frozen_weight_gemms_amd import _lib
     layers = [Layer(fw, torch, synth, wl, li, mlp_only=mlp_only) for li in range(max(1, nlayers))]
-    side_streams = None if args.sequential else [torch.cuda.Stream(), torch.cuda.Stream()]
+    side_streams = None if args.sequential else [torch.cuda.Stream(), torch.cuda.Stream(), torch.cuda.Stream()]
+    pending = []                 # side-stream work of one layer that a later GEMM (maybe the next layer's) waits for
     for ly in layers:
         ly.streams = side_streams
+        ly.pending = pending
     torch.cuda.synchronize()
     top = layers[-1]
 
@@ -424,6 +452,7 @@ def run_config(fw, torch, synth, wl, nlayers, steps, warmup, instr_steps, args, 
         d, dq = top.dOut, top.dOut_q
         for ly in reversed(layers):
             d, dq = ly.backward(d, dq)
+        top.join()
 
     for _ in range(warmup):
         step()
@@ -469,9 +498,10 @@ def run_config(fw, torch, synth, wl, nlayers, steps, warmup, instr_steps, args, 
     # bit (same kernels, same inputs; only their overlap differs)
     def snapshot():
         ts = [layers[0].dh2, layers[0].dy2, layers[-1].proj["up"]["dB"], layers[0].proj["gate"]["dA"],
-              layers[-1].proj["down"]["Y"]]
+              layers[-1].proj["down"]["Y"], layers[0].proj["down"]["dB"]]
         if not mlp_only:
-            ts += [layers[0].dh1, layers[0].dy1, layers[-1].proj["k"]["dB"], layers[0].proj["q"]["dT"]]
+            ts += [layers[0].dh1, layers[0].dy1, layers[-1].proj["k"]["dB"], layers[0].proj["q"]["dT"],
+                   layers[0].proj["o"]["dA"], layers[-1].proj["v"]["dA"]]
         return [t.clone() for t in ts]
     run()
     torch.cuda.synchronize()
