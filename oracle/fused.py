@@ -24,12 +24,19 @@ SiLU-multiply, elementwise for BF16 gate a and up b:
   sigma = 1 / (1 + E(-a)),  silu = a * sigma,  h = silu * b   (FP32)
   outputs Q(h) (the down-projection input), Q(a) and Q(b) (saved for backward)
 with E the FP32 exponential below (Cody and Waite's two-constant argument
-reduction, then the degree-7 Taylor polynomial of e^r in Horner form):
+reduction, then the degree-7 Taylor polynomial of e^r in Horner form, each
+reduction and Horner step one fused multiply-add, fma(a, b, c) = RN32(a*b + c)
+with a single rounding):
   E(x) = 0 for x < -80; +inf for x > 89; otherwise
-  n = rint(x * L2E)  (ties to even),  r = (x - n*LN2_HI) - n*LN2_LO,
-  p = C7;  p = p*r + C_k  for k = 6..0,  E = ldexp(p, n)
+  n = rint(x * L2E)  (ties to even),
+  r = fma(-n, LN2_LO, fma(-n, LN2_HI, x)),
+  p = C7;  p = fma(p, r, C_k)  for k = 6..0,  E = ldexp(p, n)
 where L2E = RN32(1/ln 2), LN2_HI = ln 2 rounded to 16 significant bits,
-LN2_LO = RN32(ln 2 - LN2_HI) and C_k = RN32(1/k!).
+LN2_LO = RN32(ln 2 - LN2_HI) and C_k = RN32(1/k!).  numpy has no FP32 fused
+multiply-add; fma32 below evaluates it exactly (the FP32 product is exact in
+float64, the float64 sum's rounding error is recovered exactly, and the one
+case where rounding twice differs from rounding once, an FP32 midpoint, is
+decided by that error).
 """
 
 from __future__ import annotations
@@ -85,6 +92,31 @@ EXP_LO = np.float32(-80.0)
 EXP_HI = np.float32(89.0)
 
 
+def fma32(a, b, c) -> np.ndarray:
+    """RN32(a*b + c) for float32 a, b, c (finite, result in the FP32 range),
+    elementwise: the fused multiply-add with a single rounding to nearest
+    even."""
+    a = np.asarray(a, dtype=np.float32)
+    b = np.asarray(b, dtype=np.float32)
+    c = np.asarray(c, dtype=np.float32)
+    p = a.astype(np.float64) * b.astype(np.float64)      # exact: 24 + 24 significant bits
+    c64 = c.astype(np.float64)
+    s = p + c64                                          # RN64(p + c)
+    bb = s - p                                           # two-sum: p + c = s + e exactly
+    e = (p - (s - bb)) + (c64 - bb)
+    r = s.astype(np.float32)                             # RN32(s)
+    # RN32(s) differs from RN32(p + c) only when s is an FP32 midpoint and e
+    # pushes the exact sum off it (a midpoint has 25 significant bits, so it
+    # is a float64 value the float64 rounding cannot cross)
+    d = s - r.astype(np.float64)
+    toward = np.where(d > 0, np.float32(np.inf), np.float32(-np.inf))
+    nb = np.nextafter(r, toward)
+    mid = (d != 0) & (np.abs(d) * 2 == np.abs(nb.astype(np.float64) - r.astype(np.float64)))
+    # at a midpoint r is the even neighbour; the exact sum lies on nb's side when e has d's sign
+    fix = mid & (e != 0) & (np.sign(e) == np.sign(d))
+    return np.where(fix, nb, r).astype(np.float32)
+
+
 def exp_f32(x) -> np.ndarray:
     """The pinned FP32 exponential E(x), elementwise on float32."""
     x = np.asarray(x, dtype=np.float32)
@@ -92,11 +124,10 @@ def exp_f32(x) -> np.ndarray:
         xc = np.clip(x, EXP_LO, EXP_HI)
         t = xc * L2E
         n = np.rint(t)
-        r = (xc - n * LN2_HI) - n * LN2_LO
-        p = COEF[7]
+        r = fma32(-n, LN2_LO, fma32(-n, LN2_HI, xc))
+        p = np.full(x.shape, COEF[7], dtype=np.float32)
         for k in range(6, -1, -1):
-            p = p * r + COEF[k]
-        p = np.asarray(p, dtype=np.float32)
+            p = fma32(p, r, COEF[k])
         out = np.ldexp(p, n.astype(np.int32)).astype(np.float32)
     out = np.where(x < EXP_LO, np.float32(0.0), out)
     out = np.where(x > EXP_HI, np.float32(np.inf), out)

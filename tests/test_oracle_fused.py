@@ -11,6 +11,7 @@ formulas against finite differences of the float64 forward.
 """
 
 import math
+from fractions import Fraction
 
 import numpy as np
 
@@ -28,12 +29,76 @@ def test_exp_constants():
         assert abs(float(fused.COEF[k]) * math.factorial(k) - 1.0) <= 2.0 ** -24
 
 
+def _rn32_exact(v: Fraction) -> float:
+    """Nearest FP32 value to the rational v (ties to even), v in the FP32 range."""
+    if v == 0:
+        return 0.0
+    a = abs(v)
+    e = a.numerator.bit_length() - a.denominator.bit_length()
+    while Fraction(2) ** e > a:
+        e -= 1
+    while Fraction(2) ** (e + 1) <= a:
+        e += 1
+    q = Fraction(2) ** (max(e, -126) - 23)            # FP32 quantum at this binade (subnormals: 2^-149)
+    m = a / q
+    mi = m.numerator // m.denominator
+    rem = m - mi
+    if rem > Fraction(1, 2) or (rem == Fraction(1, 2) and mi % 2 == 1):
+        mi += 1
+    out = float(mi * q)
+    return -out if v < 0 else out
+
+
+def _fma_exact(a, b, c) -> np.float32:
+    return np.float32(_rn32_exact(Fraction(float(a)) * Fraction(float(b)) + Fraction(float(c))))
+
+
+def test_fma32_single_rounding():
+    rng = np.random.default_rng(5)
+    a = rng.standard_normal(3000).astype(np.float32)
+    b = (rng.standard_normal(3000) * np.exp2(rng.integers(-30, 30, 3000))).astype(np.float32)
+    c = (rng.standard_normal(3000) * np.exp2(rng.integers(-40, 40, 3000))).astype(np.float32)
+    c[:500] = (-(a[:500].astype(np.float64) * b[:500]) * (1 + 2.0 ** -20)).astype(np.float32)   # cancellation
+    got = fused.fma32(a, b, c)
+    want = np.array([_fma_exact(x, y, z) for x, y, z in zip(a, b, c)], dtype=np.float32)
+    assert np.array_equal(got.view(np.uint32), want.view(np.uint32))
+    # the float64 sum lands exactly on an FP32 midpoint, the exact sum just off it:
+    # (1 + 2^-15)(1 - 2^-15) = 1 - 2^-30, and 2^24 + 3 - 2^-30 rounds down to 2^24 + 2
+    # (rounding the float64 tie to even would give 2^24 + 4); 2^24 + 1 + 2^-30 rounds up
+    u, d = np.float32(1 + 2.0 ** -15), np.float32(1 - 2.0 ** -15)
+    assert fused.fma32(u, d, np.float32(2.0 ** 24 + 2)) == np.float32(2.0 ** 24 + 2)
+    assert fused.fma32(-u, d, np.float32(2.0 ** 24 + 2)) == np.float32(2.0 ** 24 + 2)
+    assert _fma_exact(u, d, np.float32(2.0 ** 24 + 2)) == np.float32(2.0 ** 24 + 2)
+    # subnormal results, exact zeros (+0 for an exact cancellation, -0 + -0 = -0)
+    t = np.float32(2.0 ** -140)
+    assert fused.fma32(t, np.float32(1.5), t) == _fma_exact(t, np.float32(1.5), t)
+    z = fused.fma32(np.float32(3.0), np.float32(2.0), np.float32(-6.0))
+    assert z == 0.0 and not np.signbit(z)
+    assert np.signbit(fused.fma32(np.float32(-0.0), np.float32(1.0), np.float32(-0.0)))
+
+
+def test_exp_is_the_fma_sequence():
+    """E(x) at sampled x against the same reduction and Horner steps evaluated
+    with exact rational fused multiply-adds (each rounded once to FP32)."""
+    xs = np.concatenate([np.linspace(-79.5, 88.5, 97, dtype=np.float32),
+                         np.array([0.0, -0.0, 1e-8, -1e-8, 0.3466, -0.3466, 1.0, -1.0], dtype=np.float32)])
+    got = fused.exp_f32(xs)
+    for x, g in zip(xs, got):
+        n = np.float32(np.rint(np.float32(x) * fused.L2E))
+        r = _fma_exact(-n, fused.LN2_LO, _fma_exact(-n, fused.LN2_HI, x))
+        p = fused.COEF[7]
+        for k in range(6, -1, -1):
+            p = _fma_exact(p, r, fused.COEF[k])
+        want = np.float32(math.ldexp(float(p), int(n)))
+        assert np.float32(g).view(np.uint32) == want.view(np.uint32), float(x)
+
+
 def test_exp_accuracy_and_edges():
     x = np.linspace(-80, 88, 400001, dtype=np.float32)
     e = fused.exp_f32(x).astype(np.float64)
     ref = np.array([math.exp(float(v)) for v in x[::50]])
     ulp = np.array([np.spacing(np.float32(v)) for v in ref], dtype=np.float64)
-    assert np.max(np.abs(e[::50] - ref) / ulp) <= 2.0
+    assert np.max(np.abs(e[::50] - ref) / ulp) <= 1.0
     assert fused.exp_f32(np.float32(0.0)) == 1.0
     assert fused.exp_f32(np.float32(-80.5)) == 0.0
     assert np.isinf(fused.exp_f32(np.float32(89.5)))
