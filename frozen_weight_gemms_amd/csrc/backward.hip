@@ -11,8 +11,9 @@
 //                 float64), mean = fp32(S / H)
 //                 dx = rstd ((g dy) - ((y^ / g) mean))
 // Every FP32 step is one IEEE round-to-nearest operation in the order written
-// (no contraction), and E is the pinned exponential of the forward SiLU, so the
-// BF16 gradients are reproducible bit for bit.
+// (no contraction), and E is the pinned exponential of the forward SiLU (whose
+// own steps are fused multiply-adds), so the BF16 gradients are reproducible
+// bit for bit.
 //
 // The quantize-on-emit variants also write the NVFP4 copy of what they store
 // (the input of the next input-gradient GEMM): silu_mul_bwd_quant emits

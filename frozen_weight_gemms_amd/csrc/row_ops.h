@@ -54,8 +54,9 @@ __device__ __forceinline__ void two_sum(double a, double b, double& s, double& e
 
 // FP32 exponential: Cody-Waite reduction with ln 2 split in two (the high part
 // has 16 significant bits, so n * LN2_HI is exact for |n| <= 128), then the
-// degree-7 Taylor polynomial of e^r in Horner form, every step an IEEE
-// round-to-nearest operation with no contraction.
+// degree-7 Taylor polynomial of e^r in Horner form; each reduction and Horner
+// step is one fused multiply-add (a single IEEE round to nearest), the other
+// operations plain round-to-nearest ones.
 //   L2E    = RN32(1 / ln 2)          = 0x3FB8AA3B
 //   LN2_HI = ln 2 to 16 significant bits = 0x3F317200
 //   LN2_LO = RN32(ln 2 - LN2_HI)     = 0x35BFBE8E
@@ -66,15 +67,15 @@ __device__ __forceinline__ float exp_pinned(float x) {
   const float LN2_LO = __uint_as_float(0x35BFBE8Eu);
   const float xc = fminf(fmaxf(x, -80.0f), 89.0f);
   const float n = rintf(__fmul_rn(xc, L2E));
-  const float rr = __fsub_rn(__fsub_rn(xc, __fmul_rn(n, LN2_HI)), __fmul_rn(n, LN2_LO));
+  const float rr = __builtin_fmaf(-n, LN2_LO, __builtin_fmaf(-n, LN2_HI, xc));
   float p = __uint_as_float(0x39500D01u);                         // 1/7!
-  p = __fadd_rn(__fmul_rn(p, rr), __uint_as_float(0x3AB60B61u));  // 1/6!
-  p = __fadd_rn(__fmul_rn(p, rr), __uint_as_float(0x3C088889u));  // 1/5!
-  p = __fadd_rn(__fmul_rn(p, rr), __uint_as_float(0x3D2AAAABu));  // 1/4!
-  p = __fadd_rn(__fmul_rn(p, rr), __uint_as_float(0x3E2AAAABu));  // 1/3!
-  p = __fadd_rn(__fmul_rn(p, rr), 0.5f);
-  p = __fadd_rn(__fmul_rn(p, rr), 1.0f);
-  p = __fadd_rn(__fmul_rn(p, rr), 1.0f);
+  p = __builtin_fmaf(p, rr, __uint_as_float(0x3AB60B61u));        // 1/6!
+  p = __builtin_fmaf(p, rr, __uint_as_float(0x3C088889u));        // 1/5!
+  p = __builtin_fmaf(p, rr, __uint_as_float(0x3D2AAAABu));        // 1/4!
+  p = __builtin_fmaf(p, rr, __uint_as_float(0x3E2AAAABu));        // 1/3!
+  p = __builtin_fmaf(p, rr, 0.5f);
+  p = __builtin_fmaf(p, rr, 1.0f);
+  p = __builtin_fmaf(p, rr, 1.0f);
   float e = __builtin_ldexpf(p, (int)n);
   e = x < -80.0f ? 0.0f : e;
   e = x > 89.0f ? __builtin_huge_valf() : e;

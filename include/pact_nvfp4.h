@@ -183,7 +183,8 @@ int rmsnorm_quant_ex(const uint16_t *x, const uint16_t *gain, float eps, int64_t
  * up values; an NVFP4 copy of each of the two is saved for backward).  Elementwise on gate a, up b [M x I]
  * (shared leading dim ld):
  *   sigma = 1/(1 + E(-a)), h = (a * sigma) * b   (FP32; E is the library's
- *   Cody-Waite + degree-7 Taylor exponential),
+ *   Cody-Waite + degree-7 Taylor exponential, each reduction and Horner step
+ *   one fused multiply-add),
  * writes Q(h) (the down-projection input), Q(a) and Q(b).  I % 16 == 0.
  */
 int silu_mul_quant(const uint16_t *gate, const uint16_t *up, int64_t M, int64_t I, int64_t ld,
