@@ -20,9 +20,10 @@ output gradient of the layer below:
             rmsnorm_bwd_residual (+ the MLP-block residual gradient; NVFP4 copy)
   per projection: lora_bwd_dt (dT); per input: one NVFP4 dgrad launch with
   the LoRA input-gradient terms (q/k/v and gate/up each sum into one dX in a
-  single nvfp4_gemm_dgrad_multi launch; down and o alone); per layer, at the
-  end of its backward: lora_bwd_ab_batch (dA and dB of all its projections,
-  from the T that the forward's lora_down left)
+  single nvfp4_gemm_dgrad_multi launch; down and o alone); per layer two
+  lora_bwd_ab_batch calls (dA and dB of down/gate/up, then of o/q/k/v), each
+  after T = X_q A^T is recomputed from the saved NVFP4 input (one stacked
+  lora_down per input)
 
 The metric is the NVFP4 fwd + dgrad GEMM throughput of the step:
   value = (GEMM FLOPs per step) / (median time per step)   [TFLOP/s]
@@ -81,7 +82,10 @@ def parse():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--no-cpu-baseline", action="store_true",
                     help="skip the oracle leg (its timing on host cores and the parity of the timed outputs)")
-    ap.add_argument("--cpu-sample-rows", type=int, default=24, help="token rows the oracle recomputes per stage")
+    ap.add_argument("--cpu-sample-rows", type=int, default=160,
+                    help="token rows the oracle recomputes per stage for the headline step (about 10 s of oracle time)")
+    ap.add_argument("--config-sample-rows", type=int, default=24,
+                    help="token rows the oracle recomputes per stage for the other configurations")
     ap.add_argument("--eager", action="store_true", help="time eager launches instead of a captured HIP graph")
     ap.add_argument("--sequential", action="store_true",
                     help="one stream: no concurrent branches (the LoRA backwards beside each other)")
@@ -108,7 +112,7 @@ class Layer:
     block) of the workload: the projections' cached NVFP4 layouts, LoRA
     adapters, inputs and every intermediate buffer, preallocated."""
 
-    def __init__(self, fw, torch, synth, wl, index=0, mlp_only=False):
+    def __init__(self, fw, torch, synth, wl, index=0, mlp_only=False, shared_t=None):
         self.fw, self.torch, self.wl = fw, torch, wl
         self.mlp_only = mlp_only
         P = {p.name: p for p in wl.projections}
@@ -172,6 +176,12 @@ class Layer:
                 B = torch.zeros((sum(q["p"].d_out for q in Ps), r * len(Ps)), dtype=torch.bfloat16, device=dev)
             nout = wf.rows
             T = torch.empty((M, A.shape[0]), dtype=torch.bfloat16, device=dev)
+            # the backward recomputes T from X_q into a transient buffer, one per
+            # group shared by every layer (T is not state kept for the backward)
+            shared_t = {} if shared_t is None else shared_t
+            if g not in shared_t:
+                shared_t[g] = torch.empty((M, A.shape[0]), dtype=torch.bfloat16, device=dev)
+            Tb = shared_t[g]
             Y = torch.empty((M, nout), dtype=torch.bfloat16, device=dev)
             n0 = 0
             for j, q in enumerate(Ps):
@@ -180,9 +190,9 @@ class Layer:
                     B[n0:n0 + n, j * r:(j + 1) * r] = q["B"]
                     q["A"] = A[j * r:(j + 1) * r]                    # contiguous row block of the stacked A
                     q["wf"] = fw.NVFP4Tensor(wf.codes[n0:n0 + n], wf.scales[n0:n0 + n], wf.rscale[n0:n0 + n])
-                q["Y"], q["T"] = Y[:, n0:n0 + n], T[:, j * r:(j + 1) * r]
+                q["Y"], q["T"], q["Tb"] = Y[:, n0:n0 + n], T[:, j * r:(j + 1) * r], Tb[:, j * r:(j + 1) * r]
                 n0 += n
-            self.grp[g] = dict(names=names, wf=wf, A=A, B=B, T=T, Y=Y, K=K)
+            self.grp[g] = dict(names=names, wf=wf, A=A, B=B, T=T, Tb=Tb, Y=Y, K=K, xq=None)
 
         self.y2q, self.rstd2 = nv(H), torch.empty((M,), dtype=torch.float32, device=dev)
         self.hq, self.gq, self.uq = nv(I), nv(I), nv(I)
@@ -216,6 +226,7 @@ class Layer:
     def _fwd_group(self, g, xq):
         fw, G = self.fw, self.grp[g]
         M, K = self.M, G["K"]
+        G["xq"] = xq
         self._ev("lora", "lora_down", ("lora_down", M, K, G["A"].shape[0]),
                  lambda: fw.lora_down(xq, G["A"], out=G["T"]))
         self._ev("gemm", f"fwd {g}", ("gemm", M, G["wf"].rows, (K,), False),
@@ -238,14 +249,44 @@ class Layer:
         # they take CUs from the GEMM's one-workgroup-per-CU tiles.)
         self._ev("lora", "lora_bwd_dt", ("lora_bwd_dt", self.M, p.d_out, self.r),
                  lambda: fw.lora_bwd_dt(dy, P["B"], LORA_SCALE, out=P["dT"]))
-        self.ab_jobs.append((xq, P["T"], dy, P["dT"], (P["dA"], P["dB"]), P["ws"]))
+        self.ab_jobs.append((xq, P["Tb"], dy, P["dT"], (P["dA"], P["dB"]), P["ws"]))
+
+    def _side(self, fn):
+        """fn on the side stream of the adapter-gradient work (after the
+        current stream's work so far), recorded for the next join; in place
+        without side streams or while the step is instrumented."""
+        if self.streams is None or self.record is not None or self.pending is None:
+            fn()
+            return
+        torch = self.torch
+        cur, st = torch.cuda.current_stream(), self.streams[-1]
+        st.wait_stream(cur)
+        with torch.cuda.stream(st):
+            fn()
+        ev = torch.cuda.Event()
+        ev.record(st)
+        self.pending.append(ev)
+
+    def _recompute_t(self, names):
+        """T = X~ A^T of these projections' groups, recomputed from the saved
+        NVFP4 input (one stacked lora_down per input) into the transient
+        buffers: the LoRA branch keeps only the shared NVFP4 input and its
+        adapters for the backward."""
+        fw = self.fw
+        groups = [G for G in self.grp.values() if set(G["names"]) <= set(names)]
+
+        def run():
+            for G in groups:
+                self._ev("lora", "lora_down", ("lora_down", self.M, G["K"], G["A"].shape[0]),
+                         lambda G=G: fw.lora_down(G["xq"], G["A"], out=G["Tb"]))
+        self._side(run)
 
     def _adapter_grads(self, tag):
-        """dA and dB of the projections whose dT is done (one batched call).
-        Nothing later in the step reads them, so with side streams the batch
-        runs on a stream of its own beside the next non-GEMM kernels, and the
-        next input-gradient GEMM waits for it (GEMM tiles fill every CU, so a
-        batch running beside one would delay its tiles)."""
+        """dA and dB of the projections whose dT is done (one batched call,
+        from the recomputed T).  Nothing later in the step reads them, so with
+        side streams this runs on a stream of its own beside the next non-GEMM
+        kernels, and the next input-gradient GEMM waits for it (GEMM tiles fill
+        every CU, so work running beside one would delay its tiles)."""
         jobs, self.ab_jobs = self.ab_jobs, []
         # the batch's argument arrays are built once: every step passes the
         # same buffers (checked by their addresses)
@@ -254,17 +295,7 @@ class Layer:
             work = ("lora_ab_batch", tuple((self.M, j[0].cols, j[2].shape[1], j[1].shape[1]) for j in jobs))
             self.ab_plan[tag] = (key, self.fw.LoraAbBatch(jobs, LORA_SCALE), work)
         _, plan, work = self.ab_plan[tag]
-        if self.streams is None or self.record is not None or self.pending is None:
-            self._ev("lora", "lora_bwd_ab_batch", work, plan.run)
-            return
-        torch = self.torch
-        cur, st = torch.cuda.current_stream(), self.streams[-1]
-        st.wait_stream(cur)
-        with torch.cuda.stream(st):
-            plan.run()
-        ev = torch.cuda.Event()
-        ev.record(st)
-        self.pending.append(ev)
+        self._side(lambda: self._ev("lora", "lora_bwd_ab_batch", work, plan.run))
 
     def join(self):
         """The current stream waits for the side-stream work started so far."""
@@ -341,6 +372,10 @@ class Layer:
         # MLP block: out = h2 + down(silu(gate(n2)) * up(n2)),  n2 = rmsnorm(h2)
         self._bwd_lora("down", self.hq, dout, dout_q)
         self._bwd_dgrad("down", dout_q, self.dh)
+        # T of the MLP projections, beside silu_mul_bwd_quant and the gate/up dT
+        # (recomputing every projection's T there measured slower: it slows
+        # silu_mul_bwd_quant more than the later stretches gain)
+        self._recompute_t(("gate", "up", "down"))
         self._ev("bwd", "silu_mul_bwd_quant", ("silubq", M, I),
                  lambda: fw.silu_mul_bwd_quant(self.gq, self.uq, self.dh, out=(self.da, self.db, self.daq, self.dbq)))
         # the gate and up LoRA backwards run side by side; one input-gradient
@@ -358,6 +393,8 @@ class Layer:
         # attention backward itself is not part of the path (dq, dk, dv are inputs)
         self._bwd_lora("o", self.aq, self.dh2, self.dh2q)
         self._bwd_dgrad("o", self.dh2q, self.dattn)
+        # T of the attention projections, beside the q/k/v quantizations and dT
+        self._recompute_t(("q", "k", "v", "o"))
         self._branches([lambda n=n, d=d: self._bwd_lora(n, self.y1q, d)
                         for n, d in (("q", self.dq), ("k", self.dk), ("v", self.dv))])
         self._bwd_dgrad_multi(("q", "k", "v"), self.dy1)
@@ -432,9 +469,11 @@ def stats(ms):
 # ---------------------------------------------------------------------------
 # one workload: build, time, instrument, check
 # ---------------------------------------------------------------------------
-def run_config(fw, torch, synth, wl, nlayers, steps, warmup, instr_steps, args, mlp_only=False, check=True):
+def run_config(fw, torch, synth, wl, nlayers, steps, warmup, instr_steps, args, mlp_only=False, check=True,
+               sample_rows=None):
     from frozen_weight_gemms_amd import _lib
-    layers = [Layer(fw, torch, synth, wl, li, mlp_only=mlp_only) for li in range(max(1, nlayers))]
+    shared_t = {}                # transient T of the backward's recomputation, one buffer per group
+    layers = [Layer(fw, torch, synth, wl, li, mlp_only=mlp_only, shared_t=shared_t) for li in range(max(1, nlayers))]
     side_streams = None if args.sequential else [torch.cuda.Stream(), torch.cuda.Stream(), torch.cuda.Stream()]
     pending = []                 # side-stream work of one layer that a later GEMM (maybe the next layer's) waits for
     for ly in layers:
@@ -648,7 +687,7 @@ def run_config(fw, torch, synth, wl, nlayers, steps, warmup, instr_steps, args, 
     del graph, run
     torch.cuda.synchronize()
     if check:
-        res["cpu_baseline"], res["parity"] = cpu_baseline(torch, layers, wl, args.cpu_sample_rows)
+        res["cpu_baseline"], res["parity"] = cpu_baseline(torch, layers, wl, sample_rows or args.cpu_sample_rows)
     del layers
     torch.cuda.synchronize()
     torch.cuda.empty_cache()
@@ -1493,17 +1532,19 @@ def main():
         result["parity_status"] = result["parity"]["status"]
     result["schedule"] = ("stacked q/k/v and gate/up forward GEMMs (stacked LoRA rank <= 128); one "
                           "input-gradient launch each for q/k/v and gate/up; LoRA dT per projection before its "
-                          "input gradient, every projection's dA and dB (from the forward's T) in one batched call at the end of the "
-                          "layer's backward; " +
+                          "input gradient; per layer two batched dA/dB calls (down/gate/up after the gate/up "
+                          "input gradient, o/q/k/v after the q/k/v one), each after T is recomputed from the "
+                          "saved NVFP4 input by one stacked lora_down per input; " +
                           ("one stream" if args.sequential else
-                           "the dT of gate/up and of q/k/v on 2 side streams"))
+                           "the dT of gate/up and of q/k/v on 2 side streams, the dA/dB batches on a third, "
+                           "joined before the next input-gradient GEMM"))
     if not legs_off and not args.no_configs:
         cfgs = {}
         for wid, nlay, mlp in ((1, 2, False), (3, 2, True), (4, 1, False)):
             w = synth.WORKLOADS[wid]
             progress(f"config {w.name}")
             c = run_config(fw, torch, synth, w, nlay, max(10, min(args.steps, 30)), 3, 3, args, mlp_only=mlp,
-                           check=not args.no_cpu_baseline)
+                           check=not args.no_cpu_baseline, sample_rows=args.config_sample_rows)
             c["workload"] = w.name
             cfgs[w.name] = c
         result["configs"] = cfgs

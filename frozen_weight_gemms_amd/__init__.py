@@ -384,9 +384,10 @@ def lora_bwd_ab(xq: NVFP4Tensor, A: torch.Tensor, dy: torch.Tensor, dT: torch.Te
 
 
 class LoraAbBatch:
-    """dA and dB of several projections in three launches, from the forward's
-    T, with the call's argument arrays built once (every run() reads the
-    tensors' current contents and launches on the current stream).
+    """dA and dB of several projections in three launches, given T = X_q A^T
+    (lora_down's output), with the call's argument arrays built once (every
+    run() reads the tensors' current contents and launches on the current
+    stream).
     ``problems``: list of (xq, T, dy, dT, (dA, dB), workspace) with one token
     count; T [M x r] is the projection's lora_down output (a column slice of a
     stacked lora_down output is accepted: rows may be strided, columns must be

@@ -397,9 +397,12 @@ int lora_bwd_ab(const uint8_t *x_codes, const uint8_t *x_scales, const float *x_
 
 /*
  * lora_bwd_ab_batch -- the adapter gradients dA and dB of n (1..8) projections
- * in three launches (for example every projection of a decoder layer once its
- * backward has run), from the forward's T instead of a recomputed one (the
- * LoRA branch of Appendix Table 7: dB = s dY^T T, dA = dT^T X~).  Problem i
+ * in three launches (for example the projections of a decoder layer once
+ * their dT is done), given T = X~ A^T (the LoRA branch of Appendix Table 7:
+ * dB = s dY^T T, dA = dT^T X~).  T is lora_down's output: the branch keeps
+ * only the shared NVFP4 input and the adapters for the backward, so a caller
+ * recomputes it there, and one stacked lora_down serves every projection that
+ * reads the same input.  Problem i
  * has X_q (x_codes[i], x_scales[i], x_rscale[i]) [M x K[i]], T[i] [M x r[i]]
  * with leading dimension ldT[i] >= r[i] (lora_down's output for the
  * projection's adapter: a column slice of a stacked lora_down's output is

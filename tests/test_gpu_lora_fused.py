@@ -138,8 +138,8 @@ def test_silu_mul_bwd(fw, M, I):
 
 def test_lora_bwd_ab_batch_equals_single_calls(fw):
     """The batched adapter gradients of several projections (different K, N
-    and ranks of one class, ragged M), each from the forward's T (lora_down,
-    also a column slice of a stacked lora_down), equal each projection's
+    and ranks of one class, ragged M), each given T from lora_down (also a
+    column slice of a stacked lora_down), equal each projection's
     lora_bwd bit for bit, and ranks of different classes are refused."""
     from frozen_weight_gemms_amd import _lib
     M, s = 300, 0.75
