@@ -397,6 +397,10 @@ class LoraAbBatch:
     def __init__(self, problems, scale: float):
         import ctypes
         n = len(problems)
+        if n == 0:                               # the library refuses it (PACT_EINVAL) when run
+            self.problems, self.outputs = [], []
+            self._args = (0,) + (None,) * 3 + (0, None, None, None, None, float(scale)) + (None,) * 7
+            return
         M = problems[0][2].shape[0]
         for xq, T, dy, dT, (dA, dB), ws in problems:
             _bf16(T, "T"); _dense(_bf16(dy, "dy"), "dy"); _dense(_bf16(dT, "dT"), "dT")

@@ -193,3 +193,39 @@ def test_lora_bwd_ab_batch_equals_single_calls(fw):
                 fw.lora_bwd_workspace(M, gx.cols, dy.shape[1], 32)))
     with pytest.raises(_lib.PactError):
         fw.lora_bwd_ab_batch(bad, s)
+
+
+def test_lora_bwd_ab_batch_edges(fw):
+    """Empty token axis (every gradient an empty sum: zeros), the maximum of 8
+    problems in one call, and problem counts outside 1..8 refused."""
+    from frozen_weight_gemms_amd import _lib
+    s = 0.5
+    # M = 0: dA and dB are zero-filled
+    K, N, r = 256, 128, 16
+    gx = fw.empty_nvfp4(0, K, "cuda")
+    out = (torch.full((r, K), 3.0, dtype=torch.bfloat16, device="cuda"),
+           torch.full((N, r), 3.0, dtype=torch.bfloat16, device="cuda"))
+    z = lambda *sh: torch.zeros(sh, dtype=torch.bfloat16, device="cuda")
+    fw.lora_bwd_ab_batch([(gx, z(0, r), z(0, N), z(0, r), out, fw.lora_bwd_workspace(0, K, N, r))], s)
+    assert not out[0].any() and not out[1].any()
+    # 8 problems at once, each equal to its own lora_bwd
+    M = 96
+    probs, refs = [], []
+    for k in range(8):
+        K, N, r = 128 + 16 * k, 256 - 16 * k, 9 + k
+        x = synth.activations_bf16((M, K), 95, 10 * k)
+        A = bits_to_torch(synth.normal_bf16((r, K), 0.01, 95, 10 * k + 1))
+        B = bits_to_torch(synth.normal_bf16((N, r), 0.01, 95, 10 * k + 2))
+        dy = bits_to_torch(synth.normal_bf16((M, N), 0.01, 95, 10 * k + 3))
+        g = nvfp4_to_gpu(_q(x))
+        refs.append(fw.lora_bwd(g, A, B, dy, s))
+        out = (torch.empty((r, K), dtype=torch.bfloat16, device="cuda"),
+               torch.empty((N, r), dtype=torch.bfloat16, device="cuda"))
+        probs.append((g, fw.lora_down(g, A), dy, fw.lora_bwd_dt(dy, B, s), out, fw.lora_bwd_workspace(M, K, N, r)))
+    fw.lora_bwd_ab_batch(probs, s)
+    for (_, dA_ref, dB_ref), p in zip(refs, probs):
+        assert torch.equal(p[4][0], dA_ref) and torch.equal(p[4][1], dB_ref)
+    with pytest.raises(_lib.PactError):
+        fw.lora_bwd_ab_batch(probs + probs[:1], s)
+    with pytest.raises(_lib.PactError):
+        fw.lora_bwd_ab_batch([], s)
