@@ -82,7 +82,7 @@ def parse():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--no-cpu-baseline", action="store_true",
                     help="skip the oracle leg (its timing on host cores and the parity of the timed outputs)")
-    ap.add_argument("--cpu-sample-rows", type=int, default=160,
+    ap.add_argument("--cpu-sample-rows", type=int, default=1536,
                     help="token rows the oracle recomputes per stage for the headline step (about 10 s of oracle time)")
     ap.add_argument("--config-sample-rows", type=int, default=24,
                     help="token rows the oracle recomputes per stage for the other configurations")
