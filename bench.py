@@ -192,7 +192,8 @@ class Layer:
                     q["wf"] = fw.NVFP4Tensor(wf.codes[n0:n0 + n], wf.scales[n0:n0 + n], wf.rscale[n0:n0 + n])
                 q["Y"], q["T"], q["Tb"] = Y[:, n0:n0 + n], T[:, j * r:(j + 1) * r], Tb[:, j * r:(j + 1) * r]
                 n0 += n
-            self.grp[g] = dict(names=names, wf=wf, A=A, B=B, T=T, Tb=Tb, Y=Y, K=K, xq=None)
+            self.grp[g] = dict(names=names, wf=wf, A=A, B=B, T=T, Tb=Tb, Y=Y, K=K, xq=None,
+                               launches=self._launch_split(M, K, [q["p"].d_out for q in Ps]))
 
         self.y2q, self.rstd2 = nv(H), torch.empty((M,), dtype=torch.float32, device=dev)
         self.hq, self.gq, self.uq = nv(I), nv(I), nv(I)
@@ -210,6 +211,24 @@ class Layer:
         self.ab_plan = {}        # batch tag -> (buffer addresses, LoraAbBatch, work)
         self.pending = None      # list (shared by the layers) of side-stream work the next GEMM waits for
         self.dout = None         # the output gradient this layer received in the last step
+
+    @staticmethod
+    def _launch_split(M, K, widths):
+        """Row ranges of a group's stacked weight, one forward GEMM launch
+        each: the whole stack, or its first projection and the rest, whichever
+        needs fewer tile rounds on 256 CUs (tile area times rounds).  Either
+        way every output element is the same sum in the same order (the LoRA
+        term of a part is the stacked one with the other parts' zero B blocks)."""
+        from frozen_weight_gemms_amd import _lib
+
+        def cost(n):
+            bm, bn = _lib.gemm_tile(M, n, K)
+            tiles = -(-M // bm) * -(-n // bn)
+            return -(-tiles // 256) * bm * bn
+        total = sum(widths)
+        if len(widths) > 1 and cost(widths[0]) + cost(total - widths[0]) < cost(total):
+            return [(0, widths[0]), (widths[0], total)]
+        return [(0, total)]
 
     # ---- instrumented launch helper ----
     def _ev(self, cat, name, work, fn):
@@ -229,9 +248,12 @@ class Layer:
         G["xq"] = xq
         self._ev("lora", "lora_down", ("lora_down", M, K, G["A"].shape[0]),
                  lambda: fw.lora_down(xq, G["A"], out=G["T"]))
-        self._ev("gemm", f"fwd {g}", ("gemm", M, G["wf"].rows, (K,), False),
-                 lambda: fw.gemm_fwd(xq, G["wf"], lora_t=G["T"], lora_b=G["B"], lora_scale=LORA_SCALE,
-                                     out=G["Y"]))
+        wf = G["wf"]
+        for a, b in G["launches"]:
+            part = wf if (a, b) == (0, wf.rows) else fw.NVFP4Tensor(wf.codes[a:b], wf.scales[a:b], wf.rscale[a:b])
+            self._ev("gemm", f"fwd {g}", ("gemm", M, b - a, (K,), False),
+                     lambda part=part, a=a, b=b: fw.gemm_fwd(xq, part, lora_t=G["T"], lora_b=G["B"][a:b],
+                                                             lora_scale=LORA_SCALE, out=G["Y"][:, a:b]))
 
     def _bwd_lora(self, name, xq, dy, dyq=None):
         """dY's NVFP4 copy (unless a fused kernel made it) and the LoRA
