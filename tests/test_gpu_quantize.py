@@ -89,6 +89,33 @@ def test_edge_values(fw):
     _check(fw, bits, transpose=True, what="edges T")
 
 
+def test_row_exponents_across_the_range(fw):
+    """Rows whose power-of-two scales 2^e span -75 .. 110, each with exact
+    E2M1 midpoints times E4M3 scales, random values, values far below the
+    block scale, and -0: codes, scales and row scales are bit-exact against
+    the oracle at every exponent."""
+    rng = np.random.default_rng(78)
+    rows = []
+    for e in (-75, -61, -60, -59, -33, -1, 0, 1, 64, 99, 100, 101, 110):
+        p2 = np.float32(2.0 ** e)
+        s = onv.E4M3_POS[rng.integers(1, 127, size=2)]
+        mids = np.concatenate([onv.E2M1_MID, onv.E2M1_MAG, [0.0]])[:16]
+        r = np.concatenate([
+            np.concatenate([[2688.0], rng.standard_normal(15) * 300]),        # row maximum: scale exponent e
+            mids * s[0], mids * s[1],
+            np.concatenate([rng.standard_normal(8) * 2.0 ** -30, [-0.0, 0.0], rng.standard_normal(6)]),
+        ]).astype(np.float32) * p2
+        rows.append(r)
+    while len(rows) % 16:
+        rows.append(rng.standard_normal(64).astype(np.float32))
+    x = np.array(rows, dtype=np.float32)
+    bits = synth.bf16_bits(x)
+    q, ref = _check(fw, bits, what="row exponents")
+    got_e = np.log2(np.asarray(ref.rscale[:13], dtype=np.float64))
+    assert np.array_equal(got_e, [-75, -61, -60, -59, -33, -1, 0, 1, 64, 99, 100, 101, 110])
+    _check(fw, bits, transpose=True, what="row exponents T")
+
+
 def test_strided_input(fw):
     bits = synth.activations_bf16((40, 512), 91, 1)
     x = bits_to_torch(bits)[:, 128:384]
