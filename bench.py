@@ -665,9 +665,11 @@ def run_config(fw, torch, synth, wl, nlayers, steps, warmup, instr_steps, args, 
     if os.path.exists(tfile):
         try:
             tj = json.load(open(tfile))
+            ent = tj.get("kernels", {}).get(kname, {})
+            # the counters hold for these sources and this kernel's mix of shapes in the step
             if tj.get("src_hash") == src_hash("gemm.hip", "nvfp4_device.h", "lds_dma.h", "mfma_fp16.h") and \
-                    tj.get("workload") == wl.name:
-                traffic = tj.get("kernels", {}).get(kname, {}).get("bytes_per_launch")
+                    tj.get("workload") == wl.name and ent.get("algorithmic_bytes_per_launch") == round(dbytes / dcount):
+                traffic = ent.get("bytes_per_launch")
         except (ValueError, OSError):
             traffic = None
     bandwidth = {n: {"GB/s": round(b[1] / (b[0] * 1e-3) / 1e9, 1), "frac_hbm": round(b[1] / (b[0] * 1e-3) / 8e12, 3),
@@ -967,33 +969,42 @@ def copy_leg(torch, sizes):
 
 
 class MxLayer:
-    """The same layer's projections in the MXFP4 variant: cached W_fwd / W_bwd in
-    MXFP4 (quantized once, untimed) and MXFP4 GEMM inputs; a step is the 7
-    forward and 7 input-gradient GEMMs."""
+    """The same layer's projections in the MXFP4 variant, grouped like the NVFP4
+    step: the projections that read one input (q/k/v, gate/up) run as one
+    forward GEMM over their stacked weights and one input-gradient GEMM over
+    their stacked gradients and backward layouts (MXFP4 has no row scale and
+    every projection width is a multiple of the 32-element block, so stacking
+    changes no code or scale); cached W_fwd / W_bwd in MXFP4 (quantized once,
+    untimed) and MXFP4 GEMM inputs.  A step is 4 forward and 4 input-gradient
+    GEMMs (those of 7 projections)."""
 
     def __init__(self, fw, torch, synth, wl, index=0):
         self.fw, self.torch = fw, torch
         off = 5000 + 1000 * index
         M = wl.tokens
         dev = torch.device("cuda:0")
-        self.M, self.items = M, []
-        for i, p in enumerate(wl.projections):
-            w = synth.normal_torch((p.d_out, p.d_in), wl.w_std, wl.wid, off + 20 + i)
-            wf, wb = fw.mx_weight_layouts(w)
+        self.M, self.items, self.projections = M, [], list(wl.projections)
+        P = {p.name: p for p in wl.projections}
+        groups = [g for g in (("q", "k", "v"), ("o",), ("gate", "up"), ("down",)) if all(n in P for n in g)]
+        for gi, names in enumerate(groups):
+            ps = [P[n] for n in names]
+            K, N = ps[0].d_in, sum(p.d_out for p in ps)
+            w = torch.cat([synth.normal_torch((p.d_out, p.d_in), wl.w_std, wl.wid, off + 20 + wl.projections.index(p))
+                           for p in ps])
+            wf, wb = fw.mx_weight_layouts(w)                 # Q(W) [N x K] and Q(W^T) [K x N] of the stack
             del w
-            xq = fw.mx_quantize(synth.activation_torch(wl, M, p.d_in, off + 60 + i))
-            dyq = fw.mx_quantize(synth.normal_torch((M, p.d_out), wl.dy_std, wl.wid, off + 80 + i))
-            self.items.append(dict(p=p, wf=wf, wb=wb, xq=xq, dyq=dyq,
-                                   Y=torch.empty((M, p.d_out), dtype=torch.bfloat16, device=dev),
-                                   dX=torch.empty((M, p.d_in), dtype=torch.bfloat16, device=dev)))
+            xq = fw.mx_quantize(synth.activation_torch(wl, M, K, off + 60 + gi))
+            dyq = fw.mx_quantize(synth.normal_torch((M, N), wl.dy_std, wl.wid, off + 80 + gi))
+            self.items.append(dict(names=names, K=K, N=N, wf=wf, wb=wb, xq=xq, dyq=dyq,
+                                   Y=torch.empty((M, N), dtype=torch.bfloat16, device=dev),
+                                   dX=torch.empty((M, K), dtype=torch.bfloat16, device=dev)))
         self.record = None
 
     def step(self):
         fw, torch = self.fw, self.torch
         for it in self.items:
-            p = it["p"]
-            for what, a, b, out, n, k in (("fwd", it["xq"], it["wf"], it["Y"], p.d_out, p.d_in),
-                                          ("dgrad", it["dyq"], it["wb"], it["dX"], p.d_in, p.d_out)):
+            for a, b, out, n, k in ((it["xq"], it["wf"], it["Y"], it["N"], it["K"]),
+                                    (it["dyq"], it["wb"], it["dX"], it["K"], it["N"])):
                 if self.record is None:
                     fw.mx_gemm(a, b, out=out)
                 else:
@@ -1004,7 +1015,7 @@ class MxLayer:
                     self.record.append((e0, e1, (self.M, n, k)))
 
     def gemm_flops(self):
-        return sum(4 * self.M * it["p"].d_in * it["p"].d_out for it in self.items)
+        return sum(4 * self.M * p.d_in * p.d_out for p in self.projections)
 
 
 def mxfp4_leg(fw, torch, synth, wl, nlayers, steps, warmup, eager=False):
@@ -1073,14 +1084,17 @@ def mxfp4_leg(fw, torch, synth, wl, nlayers, steps, warmup, eager=False):
     if os.path.exists(tfile):
         try:
             tj = json.load(open(tfile))
-            if tj.get("src_hash") == src_hash("mxfp4.hip", "lds_dma.h") and tj.get("kernel") == kname:
+            # the counters hold for this kernel's sources and this leg's mix of shapes
+            if tj.get("src_hash") == src_hash("mxfp4.hip", "lds_dma.h") and tj.get("kernel") == kname and \
+                    tj.get("algorithmic_bytes_per_launch") == round(dbytes / dn):
                 traffic = tj.get("bytes_per_launch")
         except (ValueError, OSError):
             traffic = None
     return {"gemm_tflops": round(value, 1), "frac_fp4_peak": round(value / PEAK["fp4_mfma_tflops"], 4),
             "ms_per_step": round(ms, 4), "ms_per_step_min": round(st["min"], 4), "layers": nlayers,
             "gemm_only_tflops_events": round(flops / (gemm_ms * 1e-3) / 1e12, 1),
-            "timed_region": ("eager" if eager else "hip graph replays") + " of 14 MXFP4 GEMMs per layer",
+            "timed_region": ("eager" if eager else "hip graph replays") +
+                            " of the MXFP4 GEMMs of 7 projections per layer (q/k/v and gate/up stacked: 8 launches)",
             "roofline": {"kernel": kname, "bound": "mfma",
                          "achieved": round(ach, 1), "peak": PEAK["fp4_mfma_tflops"], "unit": "TFLOP/s",
                          "frac": round(ach / PEAK["fp4_mfma_tflops"], 4), "launches_per_step": dn // nsteps,
