@@ -102,6 +102,15 @@ def test_concatenated_qkv_forward_and_dgrad(fw):
     y_cat = fw.gemm_fwd(xq, gw_cat, lora_t=T_cat, lora_b=bits_to_torch(Bcat), lora_scale=s)
     assert torch.equal(y_cat.view(torch.int16), torch.cat(sep, dim=1).view(torch.int16)), \
         "stacked forward must equal the separate GEMMs bit for bit"
+    # the stack launched as q plus k/v (row blocks of the stacked layout, the
+    # matching rows of B_cat, column blocks of one output, the stacked T)
+    y_two = torch.empty_like(y_cat)
+    Bg = bits_to_torch(Bcat)
+    for a, b in ((0, widths[0]), (widths[0], sum(widths))):
+        part = fw.NVFP4Tensor(gw_cat.codes[a:b], gw_cat.scales[a:b], gw_cat.rscale[a:b])
+        fw.gemm_fwd(xq, part, lora_t=T_cat, lora_b=Bg[a:b], lora_scale=s, out=y_two[:, a:b])
+    assert torch.equal(y_two.view(torch.int16), y_cat.view(torch.int16)), \
+        "the stack in two launches must equal one launch bit for bit"
     # input gradient: one GEMM over the stacked contraction sum(N)
     dys = [synth.normal_bf16((M, n), 0.01, 99, 60 + i) for i, n in enumerate(widths)]
     dy_cat = np.concatenate(dys, axis=1)
