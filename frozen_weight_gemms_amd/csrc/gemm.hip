@@ -900,16 +900,29 @@ __global__ __launch_bounds__(256, 1) void k_gemm_nvfp4_fast(GemmArgs p, int tile
   constexpr int WN = BN / 2;                            // columns of this wave's tile
   constexpr int CHUNKS = WN / 8;                        // 8-column chunks per row
   const bool vec_ok = (p.ldo % 8) == 0 && ((reinterpret_cast<uintptr_t>(p.out) & 15u) == 0);
+  // The row scales a slab needs are read into registers before any of its
+  // staging writes: the compiler keeps LDS reads in order behind LDS writes
+  // to the same array, so a read per write would wait out the LDS latency
+  // once per accumulator (this lane's rows of slab i are 8g + 4h + (0..3),
+  // one aligned 16-byte read per g).
+  float rbv[WTN];
+#pragma unroll
+  for (int j = 0; j < WTN; ++j) rbv[j] = rse[BM + wn * WN + j * 32 + li] * poison;
 #pragma unroll
   for (int i = 0; i < WTM; ++i) {
+    float4 rav[4];
+#pragma unroll
+    for (int g = 0; g < 4; ++g)
+      rav[g] = *reinterpret_cast<const float4*>(rse + wm * (BM / 2) + i * 32 + 8 * g + 4 * h);
 #pragma unroll
     for (int j = 0; j < WTN; ++j) {
       const int col = j * 32 + li;
-      const float rb = rse[BM + wn * WN + col] * poison;
 #pragma unroll
       for (int rr = 0; rr < 16; ++rr) {
         const int row = 8 * (rr >> 2) + 4 * h + (rr & 3);
-        epi[row * C::EPI_LD + col] = acc[i][j][rr] * (rse[wm * (BM / 2) + i * 32 + row] * rb);
+        const float4& q = rav[rr >> 2];
+        const float ra = (rr & 3) == 0 ? q.x : (rr & 3) == 1 ? q.y : (rr & 3) == 2 ? q.z : q.w;
+        epi[row * C::EPI_LD + col] = acc[i][j][rr] * (ra * rbv[j]);
       }
     }
     __builtin_amdgcn_s_waitcnt(0xc07f);                 // lgkmcnt(0): this wave's LDS writes done
