@@ -738,86 +738,94 @@ __global__ __launch_bounds__(256, 1) void k_gemm_nvfp4_fast(GemmArgs p, int tile
     }
     odd_wave = __ballot(odd) != 0ull;
   };
-  // one rank-r term (T, U) per segment with SEG, else p's
-  auto lora_term = [&](const uint16_t* lt, const uint16_t* lu, int64_t r) __attribute__((always_inline)) {
+  // Fragments of T (rows) and U (columns) for ranks k0 .. k0 + 15.  Where a
+  // fragment is not one aligned 16-byte run, its 8 elements are gathered with
+  // clamped indices and selected afterwards (no branches), and every
+  // fragment's loads are issued before any is used, so they are in flight
+  // together.
+  auto lora_load = [&](const uint16_t* lt, const uint16_t* lu, int64_t r, int64_t k0, uint4 (&tv)[WTM],
+                       uint4 (&uv)[WTN]) __attribute__((always_inline)) {
     const bool t_vec = (r & 15) == 0;                          // T rows: 16-byte aligned runs of 8 ranks
     const bool u_vec = t_vec && p.u_stride_j == 1;             // U(j, n) = B[n][j]: same for B rows
+    if (t_vec) {
+#pragma unroll
+      for (int i = 0; i < WTM; ++i) {
+        int64_t m = m0 + wm * (BM / 2) + i * 32 + li;
+        m = m < M ? m : M - 1;
+        tv[i] = *reinterpret_cast<const uint4*>(lt + m * r + k0 + 8 * h);
+      }
+    } else {
+      uint32_t e[WTM][8];
+#pragma unroll
+      for (int i = 0; i < WTM; ++i) {
+        int64_t m = m0 + wm * (BM / 2) + i * 32 + li;
+        m = m < M ? m : M - 1;
+#pragma unroll
+        for (int t = 0; t < 8; ++t) {
+          const int64_t j = k0 + 8 * h + t;
+          e[i][t] = lt[m * r + (j < r ? j : r - 1)];
+        }
+      }
+#pragma unroll
+      for (int i = 0; i < WTM; ++i) {
+        uint32_t w[8];
+#pragma unroll
+        for (int t = 0; t < 8; ++t) w[t] = k0 + 8 * h + t < r ? e[i][t] : 0u;
+        tv[i] = make_uint4(w[0] | (w[1] << 16), w[2] | (w[3] << 16), w[4] | (w[5] << 16), w[6] | (w[7] << 16));
+      }
+    }
+    if (u_vec) {
+#pragma unroll
+      for (int i = 0; i < WTN; ++i) {
+        int64_t n = n0 + wn * (BN / 2) + i * 32 + li;
+        n = n < N ? n : N - 1;
+        uv[i] = *reinterpret_cast<const uint4*>(lu + n * p.u_stride_n + k0 + 8 * h);
+      }
+    } else {
+      uint32_t e[WTN][8];
+#pragma unroll
+      for (int i = 0; i < WTN; ++i) {
+        int64_t n = n0 + wn * (BN / 2) + i * 32 + li;
+        n = n < N ? n : N - 1;
+#pragma unroll
+        for (int t = 0; t < 8; ++t) {
+          const int64_t j = k0 + 8 * h + t;
+          e[i][t] = lu[(j < r ? j : r - 1) * p.u_stride_j + n * p.u_stride_n];
+        }
+      }
+#pragma unroll
+      for (int i = 0; i < WTN; ++i) {
+        uint32_t w[8];
+#pragma unroll
+        for (int t = 0; t < 8; ++t) w[t] = k0 + 8 * h + t < r ? e[i][t] : 0u;
+        uv[i] = make_uint4(w[0] | (w[1] << 16), w[2] | (w[3] << 16), w[4] | (w[5] << 16), w[6] | (w[7] << 16));
+      }
+    }
+  };
+  // the MFMAs of one loaded rank chunk (after lora_factors)
+  auto lora_mma = [&](const uint4 (&tv)[WTM], const uint4 (&uv)[WTN]) __attribute__((always_inline)) {
+    bf16x8_t uf[WTN];
+    // pieces (U piece pu, T piece pt): (0, 0 .. npieces-1), or for an odd
+    // wave every pair with pu + pt <= 2 (the others are below 2^-24 of the term)
+#pragma unroll
+    for (int i = 0; i < WTN; ++i) uf[i] = scaled(uv[i], fb[i], 0);
+    for (int piece = 0; piece < npieces; ++piece) {
+      bf16x8_t tf[WTM];
+#pragma unroll
+      for (int i = 0; i < WTM; ++i) tf[i] = scaled(tv[i], fa[i], piece);
+#pragma unroll
+      for (int i = 0; i < WTM; ++i)
+#pragma unroll
+        for (int j = 0; j < WTN; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tf[i], uf[j], acc[i][j], 0, 0, 0);
+    }
+  };
+  // one rank-r term (T, U), a chunk of 16 ranks at a time
+  auto lora_term = [&](const uint16_t* lt, const uint16_t* lu, int64_t r) __attribute__((always_inline)) {
     for (int64_t k0 = 0; k0 < r; k0 += 16) {
-      // Fragments of T (rows) and U (columns).  Where a fragment is not one
-      // aligned 16-byte run, its 8 elements are gathered with clamped indices
-      // and selected afterwards (no branches), and every fragment's loads are
-      // issued before any is used, so they are in flight together.
-      uint4 tv[WTM];
-      bf16x8_t uf[WTN];
-      if (t_vec) {
-#pragma unroll
-        for (int i = 0; i < WTM; ++i) {
-          int64_t m = m0 + wm * (BM / 2) + i * 32 + li;
-          m = m < M ? m : M - 1;
-          tv[i] = *reinterpret_cast<const uint4*>(lt + m * r + k0 + 8 * h);
-        }
-      } else {
-        uint32_t e[WTM][8];
-#pragma unroll
-        for (int i = 0; i < WTM; ++i) {
-          int64_t m = m0 + wm * (BM / 2) + i * 32 + li;
-          m = m < M ? m : M - 1;
-#pragma unroll
-          for (int t = 0; t < 8; ++t) {
-            const int64_t j = k0 + 8 * h + t;
-            e[i][t] = lt[m * r + (j < r ? j : r - 1)];
-          }
-        }
-#pragma unroll
-        for (int i = 0; i < WTM; ++i) {
-          uint32_t w[8];
-#pragma unroll
-          for (int t = 0; t < 8; ++t) w[t] = k0 + 8 * h + t < r ? e[i][t] : 0u;
-          tv[i] = make_uint4(w[0] | (w[1] << 16), w[2] | (w[3] << 16), w[4] | (w[5] << 16), w[6] | (w[7] << 16));
-        }
-      }
-      uint4 uv[WTN];
-      if (u_vec) {
-#pragma unroll
-        for (int i = 0; i < WTN; ++i) {
-          int64_t n = n0 + wn * (BN / 2) + i * 32 + li;
-          n = n < N ? n : N - 1;
-          uv[i] = *reinterpret_cast<const uint4*>(lu + n * p.u_stride_n + k0 + 8 * h);
-        }
-      } else {
-        uint32_t e[WTN][8];
-#pragma unroll
-        for (int i = 0; i < WTN; ++i) {
-          int64_t n = n0 + wn * (BN / 2) + i * 32 + li;
-          n = n < N ? n : N - 1;
-#pragma unroll
-          for (int t = 0; t < 8; ++t) {
-            const int64_t j = k0 + 8 * h + t;
-            e[i][t] = lu[(j < r ? j : r - 1) * p.u_stride_j + n * p.u_stride_n];
-          }
-        }
-#pragma unroll
-        for (int i = 0; i < WTN; ++i) {
-          uint32_t w[8];
-#pragma unroll
-          for (int t = 0; t < 8; ++t) w[t] = k0 + 8 * h + t < r ? e[i][t] : 0u;
-          uv[i] = make_uint4(w[0] | (w[1] << 16), w[2] | (w[3] << 16), w[4] | (w[5] << 16), w[6] | (w[7] << 16));
-        }
-      }
-      // pieces (U piece pu, T piece pt): (0, 0 .. npieces-1), or for an odd
-      // wave every pair with pu + pt <= 2 (the others are below 2^-24 of the term)
-#pragma unroll
-      for (int i = 0; i < WTN; ++i) uf[i] = scaled(uv[i], fb[i], 0);
-      for (int piece = 0; piece < npieces; ++piece) {
-        bf16x8_t tf[WTM];
-#pragma unroll
-        for (int i = 0; i < WTM; ++i) tf[i] = scaled(tv[i], fa[i], piece);
-#pragma unroll
-        for (int i = 0; i < WTM; ++i)
-#pragma unroll
-          for (int j = 0; j < WTN; ++j)
-            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tf[i], uf[j], acc[i][j], 0, 0, 0);
-      }
+      uint4 tv[WTM], uv[WTN];
+      lora_load(lt, lu, r, k0, tv, uv);
+      lora_mma(tv, uv);
     }
   };
   bool any_lora = p.lora_t != nullptr;
@@ -826,12 +834,24 @@ __global__ __launch_bounds__(256, 1) void k_gemm_nvfp4_fast(GemmArgs p, int tile
     for (int lp = 0; lp < sg.nseg; ++lp) any_lora = any_lora || sg.s[lp].lora_t != nullptr;
   }
   if (any_lora) {
-    lora_factors();
     if constexpr (SEG) {
+      lora_factors();
       for (int lp = 0; lp < sg.nseg; ++lp)
         if (sg.s[lp].lora_t != nullptr) lora_term(sg.s[lp].lora_t, sg.s[lp].lora_u, sg.s[lp].lora_r);
     } else {
-      lora_term(p.lora_t, p.lora_u, p.lora_r);
+      // the loads of the first rank chunk go out before lora_factors' row-scale
+      // loads, so both wait for memory together (a second chunk in flight as
+      // well costs a register spill in the 256 x 256 tile)
+      const int64_t r = p.lora_r;
+      uint4 tv0[WTM], uv0[WTN];
+      lora_load(p.lora_t, p.lora_u, r, 0, tv0, uv0);
+      lora_factors();
+      lora_mma(tv0, uv0);
+      for (int64_t k0 = 16; k0 < r; k0 += 16) {
+        uint4 tv[WTM], uv[WTN];
+        lora_load(p.lora_t, p.lora_u, r, k0, tv, uv);
+        lora_mma(tv, uv);
+      }
     }
   }
   if (nk0 > 1) issue_stage(1, 1);
@@ -896,6 +916,10 @@ __global__ __launch_bounds__(256, 1) void k_gemm_nvfp4_fast(GemmArgs p, int tile
     __syncthreads();                                   // all waves are done reading the stage buffers
   }
   float* epi = reinterpret_cast<float*>(smem + wave * C::EPI_WAVE);
+  // the lane half, derived afresh: kept live from the prologue, the register
+  // allocator of the 256 x 256 tile spills it and the epilogue then waits on
+  // a scratch load
+  const int he = (int)(__builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u)) >> 5);
   const float* rse = rsc + (SEG ? (sg.nseg - 1) * C::ROWS : 0);   // the last segment's row scales
   constexpr int WN = BN / 2;                            // columns of this wave's tile
   constexpr int CHUNKS = WN / 8;                        // 8-column chunks per row
@@ -908,18 +932,32 @@ __global__ __launch_bounds__(256, 1) void k_gemm_nvfp4_fast(GemmArgs p, int tile
   float rbv[WTN];
 #pragma unroll
   for (int j = 0; j < WTN; ++j) rbv[j] = rse[BM + wn * WN + j * 32 + li] * poison;
+  // A tile inside the output with 16-byte aligned rows takes the unchecked
+  // path: each lane's IT row pieces of a slab are read from LDS together and
+  // stored from one base address (the checked loop waited for every piece).
+  constexpr int IT = CHUNKS / 2;                        // 16-byte pieces per lane and slab
+  const bool full = vec_ok && m0 + BM <= M && n0 + BN <= N;
 #pragma unroll
   for (int i = 0; i < WTM; ++i) {
+    uint16_t* const slab_out = p.out + (m0 + wm * (BM / 2) + i * 32) * p.ldo + n0 + wn * WN;
+    uint4 old[IT];
+    if (full && p.accumulate) {
+#pragma unroll
+      for (int t = 0; t < IT; ++t) {
+        const int q = lane + 64 * t, row = q / CHUNKS, ch = q % CHUNKS;
+        old[t] = *reinterpret_cast<const uint4*>(slab_out + row * p.ldo + ch * 8);
+      }
+    }
     float4 rav[4];
 #pragma unroll
     for (int g = 0; g < 4; ++g)
-      rav[g] = *reinterpret_cast<const float4*>(rse + wm * (BM / 2) + i * 32 + 8 * g + 4 * h);
+      rav[g] = *reinterpret_cast<const float4*>(rse + wm * (BM / 2) + i * 32 + 8 * g + 4 * he);
 #pragma unroll
     for (int j = 0; j < WTN; ++j) {
       const int col = j * 32 + li;
 #pragma unroll
       for (int rr = 0; rr < 16; ++rr) {
-        const int row = 8 * (rr >> 2) + 4 * h + (rr & 3);
+        const int row = 8 * (rr >> 2) + 4 * he + (rr & 3);
         const float4& q = rav[rr >> 2];
         const float ra = (rr & 3) == 0 ? q.x : (rr & 3) == 1 ? q.y : (rr & 3) == 2 ? q.z : q.w;
         epi[row * C::EPI_LD + col] = acc[i][j][rr] * (ra * rbv[j]);
@@ -927,6 +965,32 @@ __global__ __launch_bounds__(256, 1) void k_gemm_nvfp4_fast(GemmArgs p, int tile
     }
     __builtin_amdgcn_s_waitcnt(0xc07f);                 // lgkmcnt(0): this wave's LDS writes done
     __builtin_amdgcn_wave_barrier();
+    if (full) {
+      float4 v[IT][2];
+#pragma unroll
+      for (int t = 0; t < IT; ++t) {
+        const int q = lane + 64 * t, row = q / CHUNKS, ch = q % CHUNKS;
+        const float4* src = reinterpret_cast<const float4*>(epi + row * C::EPI_LD + ch * 8);
+        v[t][0] = src[0];
+        v[t][1] = src[1];
+      }
+#pragma unroll
+      for (int t = 0; t < IT; ++t) {
+        const int q = lane + 64 * t, row = q / CHUNKS, ch = q % CHUNKS;
+        float4 a = v[t][0], b = v[t][1];
+        if (p.accumulate) {
+          a.x += bf16_lo(old[t].x); a.y += bf16_hi(old[t].x); a.z += bf16_lo(old[t].y); a.w += bf16_hi(old[t].y);
+          b.x += bf16_lo(old[t].z); b.y += bf16_hi(old[t].z); b.z += bf16_lo(old[t].w); b.w += bf16_hi(old[t].w);
+        }
+        uint4 o;
+        o.x = pack_bf16x2(a.x, a.y); o.y = pack_bf16x2(a.z, a.w);
+        o.z = pack_bf16x2(b.x, b.y); o.w = pack_bf16x2(b.z, b.w);
+        *reinterpret_cast<uint4*>(slab_out + row * p.ldo + ch * 8) = o;
+      }
+      __builtin_amdgcn_s_waitcnt(0xc07f);               // this slab's LDS reads done before the next slab's writes
+      __builtin_amdgcn_wave_barrier();
+      continue;
+    }
     for (int q = lane; q < 32 * CHUNKS; q += 64) {
       const int row = q / CHUNKS, ch = q % CHUNKS;
       const int64_t m = m0 + wm * (BM / 2) + i * 32 + row;
