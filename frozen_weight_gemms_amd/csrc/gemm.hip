@@ -30,6 +30,7 @@
 // Both take the same consistent permutation of K for the two operands.
 #include <type_traits>
 
+#include "epilogue.h"
 #include "lds_dma.h"
 #include "mfma_fp16.h"
 #include "pact_internal.h"
@@ -932,22 +933,12 @@ __global__ __launch_bounds__(256, 1) void k_gemm_nvfp4_fast(GemmArgs p, int tile
   float rbv[WTN];
 #pragma unroll
   for (int j = 0; j < WTN; ++j) rbv[j] = rse[BM + wn * WN + j * 32 + li] * poison;
-  // A tile inside the output with 16-byte aligned rows takes the unchecked
-  // path: each lane's IT row pieces of a slab are read from LDS together and
-  // stored from one base address (the checked loop waited for every piece).
-  constexpr int IT = CHUNKS / 2;                        // 16-byte pieces per lane and slab
+  // a tile inside the output with 16-byte aligned rows takes the unchecked
+  // slab path
   const bool full = vec_ok && m0 + BM <= M && n0 + BN <= N;
 #pragma unroll
   for (int i = 0; i < WTM; ++i) {
     uint16_t* const slab_out = p.out + (m0 + wm * (BM / 2) + i * 32) * p.ldo + n0 + wn * WN;
-    uint4 old[IT];
-    if (full && p.accumulate) {
-#pragma unroll
-      for (int t = 0; t < IT; ++t) {
-        const int q = lane + 64 * t, row = q / CHUNKS, ch = q % CHUNKS;
-        old[t] = *reinterpret_cast<const uint4*>(slab_out + row * p.ldo + ch * 8);
-      }
-    }
     float4 rav[4];
 #pragma unroll
     for (int g = 0; g < 4; ++g)
@@ -966,27 +957,7 @@ __global__ __launch_bounds__(256, 1) void k_gemm_nvfp4_fast(GemmArgs p, int tile
     __builtin_amdgcn_s_waitcnt(0xc07f);                 // lgkmcnt(0): this wave's LDS writes done
     __builtin_amdgcn_wave_barrier();
     if (full) {
-      float4 v[IT][2];
-#pragma unroll
-      for (int t = 0; t < IT; ++t) {
-        const int q = lane + 64 * t, row = q / CHUNKS, ch = q % CHUNKS;
-        const float4* src = reinterpret_cast<const float4*>(epi + row * C::EPI_LD + ch * 8);
-        v[t][0] = src[0];
-        v[t][1] = src[1];
-      }
-#pragma unroll
-      for (int t = 0; t < IT; ++t) {
-        const int q = lane + 64 * t, row = q / CHUNKS, ch = q % CHUNKS;
-        float4 a = v[t][0], b = v[t][1];
-        if (p.accumulate) {
-          a.x += bf16_lo(old[t].x); a.y += bf16_hi(old[t].x); a.z += bf16_lo(old[t].y); a.w += bf16_hi(old[t].y);
-          b.x += bf16_lo(old[t].z); b.y += bf16_hi(old[t].z); b.z += bf16_lo(old[t].w); b.w += bf16_hi(old[t].w);
-        }
-        uint4 o;
-        o.x = pack_bf16x2(a.x, a.y); o.y = pack_bf16x2(a.z, a.w);
-        o.z = pack_bf16x2(b.x, b.y); o.w = pack_bf16x2(b.z, b.w);
-        *reinterpret_cast<uint4*>(slab_out + row * p.ldo + ch * 8) = o;
-      }
+      slab_store<WN, C::EPI_LD>(epi, slab_out, p.ldo, p.accumulate, lane);
       __builtin_amdgcn_s_waitcnt(0xc07f);               // this slab's LDS reads done before the next slab's writes
       __builtin_amdgcn_wave_barrier();
       continue;

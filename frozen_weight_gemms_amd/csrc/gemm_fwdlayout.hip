@@ -33,6 +33,7 @@
 // dual-layout kernel.
 #include <type_traits>
 
+#include "epilogue.h"
 #include "lds_dma.h"
 #include "mfma_fp16.h"
 #include "pact_internal.h"
@@ -465,8 +466,10 @@ __global__ __launch_bounds__(256, 1) void k_gemm_dgrad_fwdlayout(FlArgs p, int t
     for (int rr = 0; rr < 16; ++rr)
       ra_row[i][rr >> 2][rr & 3] = rsc[wm * (BM / 2) + i * 32 + 8 * (rr >> 2) + 4 * h + (rr & 3)] * ref;
   __syncthreads();                                       // row scales read before the slabs overwrite them
+  const bool full = vec_ok && m0 + BM <= M && k0 + BN <= K;   // unchecked slab path
 #pragma unroll
   for (int i = 0; i < WTM; ++i) {
+    uint16_t* const slab_out = p.out + (m0 + wm * (BM / 2) + i * 32) * p.ldo + k0 + wn * WN;
 #pragma unroll
     for (int j = 0; j < WTN; ++j) {
       const int col = j * 32 + li;
@@ -478,6 +481,12 @@ __global__ __launch_bounds__(256, 1) void k_gemm_dgrad_fwdlayout(FlArgs p, int t
     }
     __builtin_amdgcn_s_waitcnt(0xc07f);
     __builtin_amdgcn_wave_barrier();
+    if (full) {
+      slab_store<WN, C::EPI_LD>(epi, slab_out, p.ldo, p.accumulate, lane);
+      __builtin_amdgcn_s_waitcnt(0xc07f);               // LDS reads done before the next slab's writes
+      __builtin_amdgcn_wave_barrier();
+      continue;
+    }
     for (int q = lane; q < 32 * CHUNKS; q += 64) {
       const int row = q / CHUNKS, ch = q % CHUNKS;
       const int64_t m = m0 + wm * (BM / 2) + i * 32 + row;

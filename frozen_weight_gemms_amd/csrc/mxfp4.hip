@@ -15,6 +15,7 @@
 #include <type_traits>
 #include <utility>
 
+#include "epilogue.h"
 #include "lds_dma.h"
 #include "mxfp4_device.h"
 #include "pact_internal.h"
@@ -378,8 +379,12 @@ __global__ __launch_bounds__(256, 1) void k_gemm_mxfp4(MxGemmArgs p, int tiles_m
   constexpr int WN = BN / 2;
   constexpr int CHUNKS = WN / 8;
   const bool vec_ok = (p.ldo % 8) == 0 && ((reinterpret_cast<uintptr_t>(p.out) & 15u) == 0);
+  // unchecked slab path (not in the 256 x 256 tile: there the compiler holds
+  // every accumulator in VGPRs after the loop and the path's registers spill)
+  const bool full = WTM * WTN < 16 && vec_ok && m0 + BM <= M && n0 + BN <= N;
 #pragma unroll
   for (int i = 0; i < WTM; ++i) {
+    uint16_t* const slab_out = p.out + (m0 + wm * (BM / 2) + i * 32) * p.ldo + n0 + wn * WN;
 #pragma unroll
     for (int j = 0; j < WTN; ++j) {
       const int col = j * 32 + li;
@@ -391,6 +396,12 @@ __global__ __launch_bounds__(256, 1) void k_gemm_mxfp4(MxGemmArgs p, int tiles_m
     }
     __builtin_amdgcn_s_waitcnt(0xc07f);
     __builtin_amdgcn_wave_barrier();
+    if (full) {
+      slab_store<WN, C::EPI_LD>(epi, slab_out, p.ldo, p.accumulate, lane);
+      __builtin_amdgcn_s_waitcnt(0xc07f);               // LDS reads done before the next slab's writes
+      __builtin_amdgcn_wave_barrier();
+      continue;
+    }
     for (int q = lane; q < 32 * CHUNKS; q += 64) {
       const int row = q / CHUNKS, ch = q % CHUNKS;
       const int64_t m = m0 + wm * (BM / 2) + i * 32 + row;
