@@ -667,7 +667,7 @@ def run_config(fw, torch, synth, wl, nlayers, steps, warmup, instr_steps, args, 
             tj = json.load(open(tfile))
             ent = tj.get("kernels", {}).get(kname, {})
             # the counters hold for these sources and this kernel's mix of shapes in the step
-            if tj.get("src_hash") == src_hash("gemm.hip", "nvfp4_device.h", "lds_dma.h", "mfma_fp16.h") and \
+            if tj.get("src_hash") == src_hash("gemm.hip", "nvfp4_device.h", "lds_dma.h", "mfma_fp16.h", "epilogue.h") and \
                     tj.get("workload") == wl.name and ent.get("algorithmic_bytes_per_launch") == round(dbytes / dcount):
                 traffic = ent.get("bytes_per_launch")
         except (ValueError, OSError):
@@ -1085,7 +1085,7 @@ def mxfp4_leg(fw, torch, synth, wl, nlayers, steps, warmup, eager=False):
         try:
             tj = json.load(open(tfile))
             # the counters hold for this kernel's sources and this leg's mix of shapes
-            if tj.get("src_hash") == src_hash("mxfp4.hip", "lds_dma.h") and tj.get("kernel") == kname and \
+            if tj.get("src_hash") == src_hash("mxfp4.hip", "lds_dma.h", "epilogue.h") and tj.get("kernel") == kname and \
                     tj.get("algorithmic_bytes_per_launch") == round(dbytes / dn):
                 traffic = tj.get("bytes_per_launch")
         except (ValueError, OSError):
