@@ -51,9 +51,14 @@ def test_one_segment_equals_dgrad(fw, M, N, K):
             assert torch.equal(o1.view(torch.int16), o2.view(torch.int16)), f"lora={lora is not None} acc={acc}"
 
 
+# Segments of one, two, three and four stages (256 to 1024 wide) in several
+# orders, with row scales spread across the segments.
 @pytest.mark.parametrize("widths,scales", [((512, 256, 256), (1.0, 2.0 ** -12, 2.0 ** 8)),
                                            ((256, 768), (1.0, 1.0)),
-                                           ((256, 256, 512, 256), (2.0 ** 20, 1.0, 2.0 ** -20, 4.0))])
+                                           ((256, 256, 512, 256), (2.0 ** 20, 1.0, 2.0 ** -20, 4.0)),
+                                           ((512, 512, 768), (2.0 ** -6, 1.0, 2.0 ** 10)),
+                                           ((768, 512), (4.0, 2.0 ** -16)),
+                                           ((768, 256, 1024), (1.0, 2.0 ** 12, 0.5))])
 def test_segments_against_oracle(fw, widths, scales):
     M, K, r = 160, 640, 16
     segs = [_seg(M, n, K, 40 + 3 * i, sc) for i, (n, sc) in enumerate(zip(widths, scales))]
