@@ -71,6 +71,7 @@ sys.path.insert(0, ROOT)
 PEAK = {"fp16_mfma_tflops": 2500.0, "fp4_mfma_tflops": 10100.0, "hbm_gbs": 8000.0}
 LORA_SCALE = 2.0
 HEAD_START_CYCLES = 40_000_000      # spin ahead of a timed launch sequence (about 20 ms)
+QKV_GRAD_QUANT = "branches"              # how the step quantizes dq, dk, dv (--qkv-grad-quant)
 STEP_HEAD_START_CYCLES = 200_000_000  # spin ahead of each instrumented step (about 100 ms)
 METRIC = "NVFP4 fwd+dgrad GEMM TFLOP/s at Llama-3B shapes; % FP4 MFMA peak"
 
@@ -101,6 +102,9 @@ def parse():
     ap.add_argument("--instr-steps", type=int, default=10, help="steps of the per-kernel event pass")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a 1 GiB read + 1 GiB write copy (counter calibration)")
+    ap.add_argument("--qkv-grad-quant", choices=("branches", "batched"), default="branches",
+                    help="attention gradients dq, dk, dv: quantized in each projection's branch beside its dT, "
+                         "or in one nvfp4_quantize_batch launch before the branches")
     return ap.parse_args()
 
 
@@ -151,6 +155,9 @@ class Layer:
                                      dT=torch.empty((M, r), dtype=torch.bfloat16, device=dev),
                                      dA=torch.empty((r, p.d_in), dtype=torch.bfloat16, device=dev),
                                      dB=torch.empty((p.d_out, r), dtype=torch.bfloat16, device=dev))
+        # the attention gradients' NVFP4 copies in one launch (when the step batches them)
+        self.qkv_quant = None if mlp_only else fw.QuantizeBatch(
+            [self.dq, self.dk, self.dv], [self.proj[n]["dyq"] for n in ("q", "k", "v")])
         # forward groups: the projections that read one input run as one GEMM over
         # their stacked weights (rows of Q(W) are independent, so the stacked
         # layout is the row concatenation of the separate ones) with one
@@ -417,8 +424,13 @@ class Layer:
         self._bwd_dgrad("o", self.dh2q, self.dattn)
         # T of the attention projections, beside the q/k/v quantizations and dT
         self._recompute_t(("q", "k", "v", "o"))
-        self._branches([lambda n=n, d=d: self._bwd_lora(n, self.y1q, d)
-                        for n, d in (("q", self.dq), ("k", self.dk), ("v", self.dv))])
+        if QKV_GRAD_QUANT == "batched":
+            self._ev("quant", "nvfp4_quantize_batch", ("quant", self.M, self.H + 2 * self.KV, 3), self.qkv_quant.run)
+            self._branches([lambda n=n, d=d: self._bwd_lora(n, self.y1q, d, self.proj[n]["dyq"])
+                            for n, d in (("q", self.dq), ("k", self.dk), ("v", self.dv))])
+        else:
+            self._branches([lambda n=n, d=d: self._bwd_lora(n, self.y1q, d)
+                            for n, d in (("q", self.dq), ("k", self.dk), ("v", self.dv))])
         self._bwd_dgrad_multi(("q", "k", "v"), self.dy1)
         self._adapter_grads("attn")
         self._ev("bwd", "rmsnorm_bwd_residual", ("rmsbr", M, H),
@@ -455,8 +467,8 @@ def kernel_bytes(work):
     if kind == "lora_ab_batch":              # per projection: X_q, T, dY, dT read once; dA, dB written
         return sum(NV_B * M * K + 4 * M + 2 * M * N + 4 * M * r + 2 * r * K + 2 * N * r
                    for M, K, N, r in work[1])
-    _, rows, cols = work
-    return BYTES_PER_ELEM[kind] * rows * cols + BYTES_PER_ROW[kind] * rows
+    _, rows, cols, *tensors = work           # a batched launch: the row bytes of each of its tensors
+    return BYTES_PER_ELEM[kind] * rows * cols + BYTES_PER_ROW[kind] * rows * (tensors[0] if tensors else 1)
 
 
 def gemm_bytes(M, N, segs, accumulate):
@@ -1516,7 +1528,9 @@ def single_layout_leg(fw, torch, synth, wl, n_inst=4, reps=5):
 
 # ---------------------------------------------------------------------------
 def main():
+    global QKV_GRAD_QUANT
     args = parse()
+    QKV_GRAD_QUANT = args.qkv_grad_quant
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the multi-GPU layout is "
               f"described in the design notes but not built.", file=sys.stderr)
@@ -1568,7 +1582,10 @@ def main():
         result["parity_status"] = result["parity"]["status"]
     result["schedule"] = ("stacked q/k/v and gate/up forward GEMMs (stacked LoRA rank <= 128); one "
                           "input-gradient launch each for q/k/v and gate/up; LoRA dT per projection before its "
-                          "input gradient; per layer two batched dA/dB calls (down/gate/up after the gate/up "
+                          "input gradient; dq, dk, dv quantized " +
+                          ("in one nvfp4_quantize_batch launch; " if QKV_GRAD_QUANT == "batched" else
+                           "each beside its projection's dT; ") +
+                          "per layer two batched dA/dB calls (down/gate/up after the gate/up "
                           "input gradient, o/q/k/v after the q/k/v one), each after T is recomputed from the "
                           "saved NVFP4 input by one stacked lora_down per input; " +
                           ("one stream" if args.sequential else

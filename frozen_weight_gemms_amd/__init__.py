@@ -86,6 +86,43 @@ def quantize(x: torch.Tensor, transpose: bool = False, out: NVFP4Tensor | None =
     return out
 
 
+class QuantizeBatch:
+    """nvfp4_quantize_batch: Q(x_i) of several BF16 [rows_i x cols_i] tensors in
+    one launch (each bit-identical to quantize(x_i)), with the call's argument
+    arrays built once; every run() reads the inputs' current contents and
+    writes ``outputs`` (allocated here unless given) on the current stream."""
+
+    def __init__(self, xs, outs=None):
+        import ctypes
+        n = len(xs)
+        if outs is None:
+            outs = [empty_nvfp4(x.shape[0], x.shape[1], x.device) for x in xs]
+        if len(outs) != n:
+            raise ValueError("one output per input")
+        for x, o in zip(xs, outs):
+            _bf16(x, "x")
+            if x.dim() != 2 or x.stride(1) != 1:
+                raise ValueError("x must be a 2-D tensor with unit column stride")
+            if (o.rows, o.cols) != tuple(x.shape):
+                raise ValueError("output shape differs from its input's")
+        vp, i64 = ctypes.c_void_p, ctypes.c_int64
+        arr = lambda t, vals: (t * max(n, 1))(*vals) if n else None
+        self.inputs, self.outputs = list(xs), list(outs)   # keeps the tensors alive while the plan exists
+        self._args = (n, arr(vp, [x.data_ptr() for x in xs]), arr(i64, [x.shape[0] for x in xs]),
+                      arr(i64, [x.shape[1] for x in xs]), arr(i64, [x.stride(0) for x in xs]),
+                      arr(vp, [o.codes.data_ptr() for o in outs]), arr(vp, [o.scales.data_ptr() for o in outs]),
+                      arr(vp, [o.rscale.data_ptr() for o in outs]))
+
+    def run(self):
+        _lib.call("nvfp4_quantize_batch", *self._args, _stream())
+        return self.outputs
+
+
+def quantize_batch(xs, outs=None):
+    """One run of QuantizeBatch(xs, outs): the NVFP4 outputs, in input order."""
+    return QuantizeBatch(xs, outs).run()
+
+
 QUANT_ROUND_UP_SCALES = 1
 QUANT_TENSOR_SCALE = 2
 QUANT_COMPUTE_AMAX = 4

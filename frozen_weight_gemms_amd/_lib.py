@@ -57,6 +57,7 @@ SIGNATURES = {
     "silu_mul_bwd": ([c_vp] * 7 + [c_i64, c_i64, c_vp, c_vp, c_vp], c_int),
     "rmsnorm_bwd": ([c_vp] * 6 + [c_i64, c_i64, c_vp, c_vp], c_int),
     "nvfp4_quantize_ex": ([c_vp, c_i64, c_i64, c_i64, c_int, c_int, c_vp, c_vp, c_vp, c_vp, c_vp], c_int),
+    "nvfp4_quantize_batch": ([c_int] + [c_vp] * 7 + [c_vp], c_int),
     "nvfp4_gemm_dgrad_fwd_layout": ([c_vp, c_vp, c_vp, c_i64, c_i64, c_vp, c_vp, c_vp, c_vp, c_i64, c_vp, c_i64,
                                      c_int, c_vp, c_vp, c_i64, c_vp], c_int),
     "pact_nvfp4_row_exp_max": ([c_vp, c_vp, c_vp, c_i64, c_i64, c_vp, c_vp], c_int),

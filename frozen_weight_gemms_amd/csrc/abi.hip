@@ -69,7 +69,7 @@ extern "C" {
 
 const char* pact_last_error(void) { return g_err; }
 
-int pact_abi_version(void) { return 13; }
+int pact_abi_version(void) { return 14; }
 
 int pact_nvfp4_sizes(int64_t rows, int64_t cols, size_t* codes_bytes, size_t* scales_bytes, size_t* rscale_bytes) {
   REQUIRE(rows >= 0 && cols >= 0, PACT_EINVAL, "negative size (rows=%lld, cols=%lld)", (long long)rows,
@@ -116,6 +116,35 @@ int nvfp4_quantize(const uint16_t* x, int64_t rows, int64_t cols, int64_t ldx, i
   REQUIRE(rows <= 0x7FFFFFFF, PACT_EUNSUPPORTED, "rows=%lld exceeds the grid limit", (long long)rows);
   return hip_status(pact::launch_quantize(x, rows, cols, ldx, transpose, codes, scales, rscale, as_stream(stream)),
                     "nvfp4_quantize launch");
+}
+
+int nvfp4_quantize_batch(int n, const uint16_t* const* x, const int64_t* rows, const int64_t* cols,
+                         const int64_t* ldx, uint8_t* const* codes, uint8_t* const* scales, float* const* rscale,
+                         void* stream) {
+  REQUIRE(n >= 1 && n <= pact::kQuantBatch, PACT_EINVAL, "n=%d outside [1, %d]", n, pact::kQuantBatch);
+  REQUIRE(x && rows && cols && ldx && codes && scales && rscale, PACT_EINVAL, "a problem array is NULL");
+  for (int i = 0; i < n; ++i) {
+    REQUIRE(rows[i] >= 0 && cols[i] >= 0, PACT_EINVAL, "problem %d: negative size (rows=%lld, cols=%lld)", i,
+            (long long)rows[i], (long long)cols[i]);
+    REQUIRE(cols[i] % 16 == 0, PACT_ESHAPE, "problem %d: cols=%lld is not a multiple of 16", i,
+            (long long)cols[i]);
+    if (rows[i] == 0) continue;
+    if (x[i] == nullptr) return fail(PACT_EINVAL, "problem %d: x is NULL", i);
+    if (!aligned16(x[i])) return fail(PACT_EALIGN, "problem %d: x is not 16-byte aligned", i);
+    int st = check_nvfp4(codes[i], scales[i], rscale[i], "out");
+    if (st != PACT_OK) return st;
+    REQUIRE(ldx[i] >= cols[i], PACT_ESHAPE, "problem %d: ldx=%lld < cols=%lld", i, (long long)ldx[i],
+            (long long)cols[i]);
+    REQUIRE(ldx[i] % 8 == 0, PACT_EALIGN, "problem %d: ldx=%lld is not a multiple of 8 elements", i,
+            (long long)ldx[i]);
+    REQUIRE(rows[i] <= 0x7FFFFFFF, PACT_EUNSUPPORTED, "problem %d: rows=%lld exceeds the grid limit", i,
+            (long long)rows[i]);
+  }
+  int64_t wgs = 0;
+  for (int i = 0; i < n; ++i) wgs += (rows[i] + 3) / 4;
+  REQUIRE(wgs <= 0x7FFFFFFF, PACT_EUNSUPPORTED, "%lld workgroups exceed the grid limit", (long long)wgs);
+  return hip_status(pact::launch_quantize_batch(n, x, rows, cols, ldx, codes, scales, rscale, as_stream(stream)),
+                    "nvfp4_quantize_batch launch");
 }
 
 int nvfp4_quantize_ex(const uint16_t* x, int64_t rows, int64_t cols, int64_t ldx, int transpose, int flags,

@@ -12,6 +12,23 @@ namespace pact {
 hipError_t launch_quantize(const uint16_t* x, int64_t rows, int64_t cols, int64_t ldx, int transpose,
                            uint8_t* codes, uint8_t* scales, float* rscale, hipStream_t s);
 
+// n <= kQuantBatch row-wise quantizations (default recipe) in one launch;
+// problems wider than 3072 columns get launches of their own
+constexpr int kQuantBatch = 8;
+struct QuantBatch {
+  const uint16_t* x[kQuantBatch];
+  int64_t rows[kQuantBatch], cols[kQuantBatch], ldx[kQuantBatch];
+  uint8_t* codes[kQuantBatch];
+  uint8_t* scales[kQuantBatch];
+  float* rscale[kQuantBatch];
+  int64_t wg_end[kQuantBatch];   // workgroups of problems 0 .. i
+  int nb[kQuantBatch];           // 16-element blocks per lane (1..3)
+  int n;
+};
+hipError_t launch_quantize_batch(int n, const uint16_t* const* x, const int64_t* rows, const int64_t* cols,
+                                 const int64_t* ldx, uint8_t* const* codes, uint8_t* const* scales,
+                                 float* const* rscale, hipStream_t s);
+
 // round_up: block scales rounded up (non-saturating); tensor_amax (device, may be
 // null): one power-of-two scale for the whole tensor from that maximum
 hipError_t launch_quantize_ex(const uint16_t* x, int64_t rows, int64_t cols, int64_t ldx, int transpose,

@@ -26,16 +26,16 @@ namespace pact {
 // l + 64 p + 64 WPR i (two 16-byte loads each), so every block's scale is set
 // up once by the lane that holds it; the row maximum is a wave reduction,
 // exchanged through LDS when a row spans several waves.  NB = blocks per lane.
+// Workgroup `wg` of the row quantizer over one tensor (rows 4 / WPR wg ..).
 template <int NB, int WPR>
-__global__ __launch_bounds__(kThreads) void k_quantize_rows(const uint16_t* __restrict__ x, int64_t rows,
-                                                            int64_t cols, int64_t ldx, uint8_t* __restrict__ codes,
-                                                            uint8_t* __restrict__ scales,
-                                                            float* __restrict__ rscale, int qmode,
-                                                            const float* __restrict__ tensor_amax) {
+__device__ __forceinline__ void quantize_rows_wg(const uint16_t* __restrict__ x, int64_t rows, int64_t cols,
+                                                 int64_t ldx, uint8_t* __restrict__ codes,
+                                                 uint8_t* __restrict__ scales, float* __restrict__ rscale,
+                                                 int qmode, const float* __restrict__ tensor_amax, int64_t wg) {
   __shared__ float red[4];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int part = wave % WPR;
-  const int64_t row = (int64_t)blockIdx.x * (4 / WPR) + wave / WPR;
+  const int64_t row = wg * (4 / WPR) + wave / WPR;
   const bool row_ok = row < rows;                      // uniform per wave (no early exit: barrier below)
   const int nblk = (int)(cols >> 4);
   const uint16_t* xr = x + (row_ok ? row : 0) * ldx;
@@ -83,6 +83,35 @@ __global__ __launch_bounds__(kThreads) void k_quantize_rows(const uint16_t* __re
     }
   }
   if (lane == 0 && part == 0) rscale[row] = r;
+}
+
+template <int NB, int WPR>
+__global__ __launch_bounds__(kThreads) void k_quantize_rows(const uint16_t* __restrict__ x, int64_t rows,
+                                                            int64_t cols, int64_t ldx, uint8_t* __restrict__ codes,
+                                                            uint8_t* __restrict__ scales,
+                                                            float* __restrict__ rscale, int qmode,
+                                                            const float* __restrict__ tensor_amax) {
+  quantize_rows_wg<NB, WPR>(x, rows, cols, ldx, codes, scales, rscale, qmode, tensor_amax, (int64_t)blockIdx.x);
+}
+
+// Several independent row-wise quantizations (default recipe) of at most 3072
+// columns in one launch: workgroup w belongs to the first problem whose
+// cumulative workgroup count exceeds w, and runs that problem's one-wave-per-
+// row body, so every problem's outputs equal its own launch's.  (Up to 3
+// blocks per lane: the 4-block body's registers would lower every problem's
+// occupancy.)
+__global__ __launch_bounds__(kThreads) void k_quantize_rows_batch(QuantBatch b) {
+  int i = 0;
+  while (i + 1 < b.n && (int64_t)blockIdx.x >= b.wg_end[i]) ++i;
+  const int64_t wg = (int64_t)blockIdx.x - (i > 0 ? b.wg_end[i - 1] : 0);
+  switch (b.nb[i]) {
+    case 1: quantize_rows_wg<1, 1>(b.x[i], b.rows[i], b.cols[i], b.ldx[i], b.codes[i], b.scales[i], b.rscale[i], 0,
+                                   nullptr, wg); break;
+    case 2: quantize_rows_wg<2, 1>(b.x[i], b.rows[i], b.cols[i], b.ldx[i], b.codes[i], b.scales[i], b.rscale[i], 0,
+                                   nullptr, wg); break;
+    default: quantize_rows_wg<3, 1>(b.x[i], b.rows[i], b.cols[i], b.ldx[i], b.codes[i], b.scales[i], b.rscale[i], 0,
+                                    nullptr, wg); break;
+  }
 }
 
 __global__ __launch_bounds__(kThreads) void k_quantize_rows_long(const uint16_t* __restrict__ x, int64_t cols,
@@ -580,6 +609,37 @@ hipError_t launch_quantize_ex(const uint16_t* x, int64_t rows, int64_t cols, int
 hipError_t launch_quantize(const uint16_t* x, int64_t rows, int64_t cols, int64_t ldx, int transpose,
                            uint8_t* codes, uint8_t* scales, float* rscale, hipStream_t s) {
   return launch_quantize_ex(x, rows, cols, ldx, transpose, 0, nullptr, codes, scales, rscale, s);
+}
+
+hipError_t launch_quantize_batch(int n, const uint16_t* const* x, const int64_t* rows, const int64_t* cols,
+                                 const int64_t* ldx, uint8_t* const* codes, uint8_t* const* scales,
+                                 float* const* rscale, hipStream_t s) {
+  QuantBatch b{};
+  int64_t wgs = 0;
+  for (int i = 0; i < n; ++i) {
+    if (rows[i] == 0) continue;
+    const int64_t nblk = cols[i] >> 4;
+    if (nblk > 192) {
+      // more than 3 blocks per lane: a launch of its own
+      const hipError_t e = launch_quantize(x[i], rows[i], cols[i], ldx[i], 0, codes[i], scales[i], rscale[i], s);
+      if (e != hipSuccess) return e;
+      continue;
+    }
+    const int k = b.n++;
+    b.x[k] = x[i];
+    b.rows[k] = rows[i];
+    b.cols[k] = cols[i];
+    b.ldx[k] = ldx[i];
+    b.codes[k] = codes[i];
+    b.scales[k] = scales[i];
+    b.rscale[k] = rscale[i];
+    b.nb[k] = nblk > 64 ? (int)((nblk + 63) / 64) : 1;
+    wgs += (rows[i] + 3) / 4;
+    b.wg_end[k] = wgs;
+  }
+  if (b.n == 0) return hipSuccess;
+  k_quantize_rows_batch<<<dim3((unsigned)wgs), kThreads, 0, s>>>(b);
+  return hipGetLastError();
 }
 
 hipError_t launch_rmsnorm_quant(const uint16_t* x, const uint16_t* gain, float eps, int64_t M, int64_t H,

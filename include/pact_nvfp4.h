@@ -152,6 +152,24 @@ int nvfp4_quantize_ex(const uint16_t *x, int64_t rows, int64_t cols, int64_t ldx
                       float *amax, uint8_t *codes, uint8_t *scales, float *rscale, void *stream);
 
 /*
+ * nvfp4_quantize_batch -- n (1..8) independent row-wise quantizations, as
+ * nvfp4_quantize with transpose == 0, in one launch: the several output
+ * gradients that one backward step quantizes at the same point for their
+ * NVFP4 input-gradient GEMMs (Appendix Table 7 row "Frozen projections":
+ * gradients quantized on the fly; in a decoder layer the attention gradients
+ * of q, k and v).  Problem i: x[i] [rows[i] x cols[i]] with leading dimension
+ * ldx[i] into codes[i], scales[i], rscale[i]; its outputs are bit-identical to
+ * nvfp4_quantize of that problem alone.  The pointer and size arrays are host
+ * arrays of n entries; every problem is validated as nvfp4_quantize (first
+ * failure reported, nothing launched).  Problems of at most 3072 columns share
+ * one launch; wider ones get launches of their own on the same stream.
+ * Outputs must not overlap one another or any input.
+ */
+int nvfp4_quantize_batch(int n, const uint16_t *const *x, const int64_t *rows, const int64_t *cols,
+                         const int64_t *ldx, uint8_t *const *codes, uint8_t *const *scales,
+                         float *const *rscale, void *stream);
+
+/*
  * rmsnorm_quant -- RMSNorm forward fused with NVFP4 quantization (Appendix
  * Table 7 row "RMSNorm": a BF16 row normalized in FP32; the NVFP4 result and
  * one FP32 statistic per token are saved for backward).  For each row of x [M x H] (leading dim ldx):

@@ -57,7 +57,7 @@ def test_gemm_tile_query(lib):
 
 
 def test_abi_version(lib):
-    assert lib.pact_abi_version() == 13
+    assert lib.pact_abi_version() == 14
 
 
 def test_sizes(lib):
@@ -86,6 +86,28 @@ def test_quantize_validation(lib):
     assert q(ALIGNED, 0, 32, 32, 0, None, None, None, None) == 0                    # empty: no-op
     assert lib.pact_last_error() == b""
 
+
+
+def test_quantize_batch_validation(lib):
+    """nvfp4_quantize_batch checks every problem on the host before launching anything."""
+    P, I = ctypes.c_void_p * 3, ctypes.c_int64 * 3
+    ptrs = P(ALIGNED, ALIGNED, ALIGNED)
+    rows, cols, ldx = I(4, 8, 2), I(32, 48, 16), I(32, 48, 16)
+    q = lib.nvfp4_quantize_batch
+    assert q(0, ptrs, rows, cols, ldx, ptrs, ptrs, ptrs, None) == -1                 # n outside [1, 8]
+    assert q(9, ptrs, rows, cols, ldx, ptrs, ptrs, ptrs, None) == -1
+    assert q(3, None, rows, cols, ldx, ptrs, ptrs, ptrs, None) == -1                 # NULL problem array
+    assert q(3, ptrs, rows, I(32, 40, 16), ldx, ptrs, ptrs, ptrs, None) == -2        # problem 1: cols % 16
+    assert b"problem 1" in lib.pact_last_error()
+    assert q(3, P(ALIGNED, ALIGNED, MISALIGNED), rows, cols, ldx, ptrs, ptrs, ptrs, None) == -3   # problem 2: x
+    assert b"problem 2" in lib.pact_last_error()
+    assert q(3, ptrs, rows, cols, I(32, 40, 16), ptrs, ptrs, ptrs, None) == -2       # problem 1: ldx < cols
+    assert q(3, ptrs, rows, cols, I(32, 52, 16), ptrs, ptrs, ptrs, None) == -3       # problem 1: ldx % 8
+    assert q(3, ptrs, rows, cols, ldx, ptrs, P(ALIGNED, None, ALIGNED), ptrs, None) == -1   # problem 1: scales
+    assert q(3, ptrs, I(-1, 8, 2), cols, ldx, ptrs, ptrs, ptrs, None) == -1          # negative rows
+    empty = P(None, None, None)
+    assert q(3, empty, I(0, 0, 0), cols, ldx, empty, empty, empty, None) == 0          # every problem empty: no-op
+    assert lib.pact_last_error() == b""
 
 def test_fused_validation(lib):
     assert lib.rmsnorm_quant(ALIGNED, ALIGNED, 1e-5, 4, 20000, 20000, ALIGNED, ALIGNED, ALIGNED, ALIGNED,

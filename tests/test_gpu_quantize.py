@@ -152,3 +152,55 @@ def test_full_size(fw, name, rows, cols, kind):
 def test_full_size_transposed_weight(fw):
     bits = synth.normal_bf16((3072, 8192), 0.02, 2, 505)    # W_down [N=3072 x K=8192]
     _check(fw, bits, transpose=True, what="W_bwd down [8192 x 3072]")
+
+
+def _bits_equal(a, b):
+    import torch
+    return (torch.equal(a.codes, b.codes) and torch.equal(a.scales, b.scales)
+            and torch.equal(a.rscale.view(torch.int32), b.rscale.view(torch.int32)))
+
+
+def test_quantize_batch_equals_single_calls(fw):
+    """nvfp4_quantize_batch: every problem bit-identical to its own nvfp4_quantize
+    call: the attention-gradient shapes of the Llama-3B step (one launch),
+    ragged rows, one 16-column row, a padded leading dimension, an empty
+    problem, and problems wider than 3072 columns (launches of their own)."""
+    import torch
+    wl = synth.WORKLOADS[2]
+    cases = [
+        [(4096, 3072), (4096, 1024), (4096, 1024)],
+        [(333, 3072), (1, 16), (77, 1024), (0, 512), (129, 2048)],
+        [(64, 4096), (40, 3072), (96, 8192), (33, 16384), (8, 20480)],
+    ]
+    for k, shapes in enumerate(cases):
+        xs = []
+        for i, (rows, cols) in enumerate(shapes):
+            if rows and cols:
+                x = synth.activation_torch(wl, rows, cols, 300 + 10 * k + i) * (2.0 ** (3 * i - 4))
+            else:
+                x = torch.zeros((rows, cols), dtype=torch.bfloat16, device="cuda")
+            xs.append(x)
+        if k == 1:                          # one padded leading dimension
+            big = synth.activation_torch(wl, 129, 2048 + 64, 399)
+            xs[4] = big[:, :2048]
+        got = fw.quantize_batch(xs)
+        torch.cuda.synchronize()
+        for i, (x, q) in enumerate(zip(xs, got)):
+            want = fw.quantize(x)
+            assert _bits_equal(q, want), f"case {k} problem {i} {tuple(x.shape)}"
+
+
+def test_quantize_batch_plan_reruns(fw):
+    """A QuantizeBatch plan run twice reads its inputs' current contents."""
+    import torch
+    xs = [synth.normal_torch((256, 3072), 0.02, 2, 410), synth.normal_torch((256, 1024), 0.02, 2, 411)]
+    plan = fw.QuantizeBatch(xs)
+    plan.run()
+    first = [fw.quantize(x) for x in xs]
+    assert all(_bits_equal(a, b) for a, b in zip(plan.outputs, first))
+    for x in xs:
+        x.mul_(-3.0)
+    plan.run()
+    torch.cuda.synchronize()
+    second = [fw.quantize(x) for x in xs]
+    assert all(_bits_equal(a, b) for a, b in zip(plan.outputs, second))
