@@ -382,18 +382,39 @@ __global__ __launch_bounds__(256, 1) void k_gemm_dgrad_fwdlayout(FlArgs p, int t
   // prescaled by 1 / (r_A 2^e_ref) so that the epilogue's scaling restores it
   if (p.lora_t != nullptr) {
     const int64_t r = p.lora_r;
+    // dT rows as 16-byte runs of 8 ranks where aligned; otherwise (and for A,
+    // whose 8 ranks of one column are K apart) every element is loaded from a
+    // clamped, valid index and selected afterwards.  A conditional load
+    // compiles to a branch, and the wait after each one serialized them
+    // (12 us of prologue per tile).
+    const bool t_vec = (r & 15) == 0 && (reinterpret_cast<uintptr_t>(p.lora_t) & 15u) == 0;
     for (int64_t j0 = 0; j0 < r; j0 += 16) {
       bf16x8_t tf[WTM], uf[WTN];
+      if (t_vec) {
 #pragma unroll
-      for (int i = 0; i < WTM; ++i) {
-        int64_t m = m0 + wm * (BM / 2) + i * 32 + li;
-        m = m < M ? m : M - 1;
-#pragma unroll
-        for (int t = 0; t < 8; ++t) {
-          const int64_t j = j0 + 8 * h + t;
-          tf[i][t] = bf16_of(j < r ? p.lora_t[m * r + j] : (uint16_t)0);
+        for (int i = 0; i < WTM; ++i) {
+          int64_t m = m0 + wm * (BM / 2) + i * 32 + li;
+          m = m < M ? m : M - 1;
+          tf[i] = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const uint4*>(p.lora_t + m * r + j0 + 8 * h));
         }
+      } else {
+        uint16_t e[WTM][8];
+#pragma unroll
+        for (int i = 0; i < WTM; ++i) {
+          int64_t m = m0 + wm * (BM / 2) + i * 32 + li;
+          m = m < M ? m : M - 1;
+#pragma unroll
+          for (int t = 0; t < 8; ++t) {
+            const int64_t j = j0 + 8 * h + t;
+            e[i][t] = p.lora_t[m * r + (j < r ? j : r - 1)];
+          }
+        }
+#pragma unroll
+        for (int i = 0; i < WTM; ++i)
+#pragma unroll
+          for (int t = 0; t < 8; ++t) tf[i][t] = bf16_of(j0 + 8 * h + t < r ? e[i][t] : (uint16_t)0);
       }
+      uint16_t ea[WTN][8];
 #pragma unroll
       for (int jj = 0; jj < WTN; ++jj) {
         int64_t k = k0 + wn * (BN / 2) + jj * 32 + li;
@@ -401,9 +422,13 @@ __global__ __launch_bounds__(256, 1) void k_gemm_dgrad_fwdlayout(FlArgs p, int t
 #pragma unroll
         for (int t = 0; t < 8; ++t) {
           const int64_t j = j0 + 8 * h + t;
-          uf[jj][t] = bf16_of(j < r ? p.lora_a[j * K + k] : (uint16_t)0);
+          ea[jj][t] = p.lora_a[(j < r ? j : r - 1) * K + k];
         }
       }
+#pragma unroll
+      for (int jj = 0; jj < WTN; ++jj)
+#pragma unroll
+        for (int t = 0; t < 8; ++t) uf[jj][t] = bf16_of(j0 + 8 * h + t < r ? ea[jj][t] : (uint16_t)0);
 #pragma unroll
       for (int i = 0; i < WTM; ++i)
 #pragma unroll
