@@ -108,6 +108,9 @@ __global__ __launch_bounds__(256, 1) void k_gemm_nvfp4(GemmArgs p, int tiles_m, 
     const int64_t r = p.lora_r;
     for (int64_t k0 = 0; k0 < r; k0 += 16) {
       bf16x8_t tf[WTM], uf[WTN];
+      // every element from a clamped, valid index, selected afterwards (a
+      // conditional load compiles to a branch and a wait of its own)
+      uint16_t et[WTM][8], eu[WTN][8];
 #pragma unroll
       for (int i = 0; i < WTM; ++i) {
         int64_t m = m0 + wm * (BM / 2) + i * 32 + li;
@@ -115,7 +118,7 @@ __global__ __launch_bounds__(256, 1) void k_gemm_nvfp4(GemmArgs p, int tiles_m, 
 #pragma unroll
         for (int t = 0; t < 8; ++t) {
           const int64_t j = k0 + 8 * h + t;
-          tf[i][t] = bf16_of(j < r ? p.lora_t[m * r + j] : (uint16_t)0);
+          et[i][t] = p.lora_t[m * r + (j < r ? j : r - 1)];
         }
       }
 #pragma unroll
@@ -125,9 +128,17 @@ __global__ __launch_bounds__(256, 1) void k_gemm_nvfp4(GemmArgs p, int tiles_m, 
 #pragma unroll
         for (int t = 0; t < 8; ++t) {
           const int64_t j = k0 + 8 * h + t;
-          uf[i][t] = bf16_of(j < r ? p.lora_u[j * p.u_stride_j + n * p.u_stride_n] : (uint16_t)0);
+          eu[i][t] = p.lora_u[(j < r ? j : r - 1) * p.u_stride_j + n * p.u_stride_n];
         }
       }
+#pragma unroll
+      for (int i = 0; i < WTM; ++i)
+#pragma unroll
+        for (int t = 0; t < 8; ++t) tf[i][t] = bf16_of(k0 + 8 * h + t < r ? et[i][t] : (uint16_t)0);
+#pragma unroll
+      for (int i = 0; i < WTN; ++i)
+#pragma unroll
+        for (int t = 0; t < 8; ++t) uf[i][t] = bf16_of(k0 + 8 * h + t < r ? eu[i][t] : (uint16_t)0);
 #pragma unroll
       for (int i = 0; i < WTM; ++i)
 #pragma unroll
@@ -162,7 +173,8 @@ __global__ __launch_bounds__(256, 1) void k_gemm_nvfp4(GemmArgs p, int tiles_m, 
       int64_t m = m0 + row;
       m = m < M ? m : M - 1;
       const int64_t b = (int64_t)kt * 8 + blk;
-      ga[it] = b < kb ? *reinterpret_cast<const uint2*>(p.a_codes + m * crow + b * 8) : make_uint2(0, 0);
+      ga[it] = load_or_zero(reinterpret_cast<const uint2*>(p.a_codes + m * crow + (b < kb ? b : 0) * 8),
+                            reinterpret_cast<const uint2*>(p.a_codes), b < kb);
     }
 #pragma unroll
     for (int it = 0; it < C::NCODE_B; ++it) {
@@ -171,7 +183,8 @@ __global__ __launch_bounds__(256, 1) void k_gemm_nvfp4(GemmArgs p, int tiles_m, 
       int64_t n = n0 + row;
       n = n < N ? n : N - 1;
       const int64_t b = (int64_t)kt * 8 + blk;
-      gb[it] = b < kb ? *reinterpret_cast<const uint2*>(p.b_codes + n * crow + b * 8) : make_uint2(0, 0);
+      gb[it] = load_or_zero(reinterpret_cast<const uint2*>(p.b_codes + n * crow + (b < kb ? b : 0) * 8),
+                            reinterpret_cast<const uint2*>(p.b_codes), b < kb);
     }
 #pragma unroll
     for (int it = 0; it < C::NSC; ++it) {
