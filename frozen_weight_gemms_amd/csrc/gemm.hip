@@ -967,11 +967,9 @@ __global__ __launch_bounds__(256, 1) void k_gemm_nvfp4_fast(GemmArgs p, int tile
         epi[row * C::EPI_LD + col] = acc[i][j][rr] * (ra * rbv[j]);
       }
     }
-    __builtin_amdgcn_s_waitcnt(0xc07f);                 // lgkmcnt(0): this wave's LDS writes done
-    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_wave_barrier();                    // the slab is this wave's: LDS order suffices
     if (full) {
       slab_store<WN, C::EPI_LD>(epi, slab_out, p.ldo, p.accumulate, lane);
-      __builtin_amdgcn_s_waitcnt(0xc07f);               // this slab's LDS reads done before the next slab's writes
       __builtin_amdgcn_wave_barrier();
       continue;
     }

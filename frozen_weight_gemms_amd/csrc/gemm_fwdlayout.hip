@@ -504,11 +504,9 @@ __global__ __launch_bounds__(256, 1) void k_gemm_dgrad_fwdlayout(FlArgs p, int t
         epi[row * C::EPI_LD + col] = acc[i][j][rr] * ra_row[i][rr >> 2][rr & 3];
       }
     }
-    __builtin_amdgcn_s_waitcnt(0xc07f);
-    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_wave_barrier();                    // the slab is this wave's: LDS order suffices
     if (full) {
       slab_store<WN, C::EPI_LD>(epi, slab_out, p.ldo, p.accumulate, lane);
-      __builtin_amdgcn_s_waitcnt(0xc07f);               // LDS reads done before the next slab's writes
       __builtin_amdgcn_wave_barrier();
       continue;
     }

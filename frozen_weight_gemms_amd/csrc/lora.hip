@@ -188,6 +188,9 @@ __device__ __forceinline__ void row_reduce(const uint8_t* __restrict__ xc, const
 #pragma unroll
     for (int q = 0; q < CH; ++q) {
       // stage the chunk in this wave's LDS tile, then read it back in the MFMA layout
+      // (the tile is the wave's own and a wave's LDS accesses execute in
+      // order, so a read sees the writes before it and a later write
+      // cannot overtake a read: no waits, only compiler barriers)
       if constexpr (NVFP4) {
         *reinterpret_cast<uint4*>(stage + (lane >> 2) * RQ_STRIDE + 16 * (lane & 3)) = lv[q][0];
         stage[RQ_SCALES + (lane >> 2) * 8 + 2 * (lane & 3)] = (uint8_t)lsc[q][0];
@@ -197,7 +200,6 @@ __device__ __forceinline__ void row_reduce(const uint8_t* __restrict__ xc, const
         for (int v = 0; v < 4; ++v)
           *reinterpret_cast<uint4*>(stage + (4 * v + (lane >> 4)) * RL_STRIDE + 16 * (lane & 15)) = lv[q][v];
       }
-      __builtin_amdgcn_s_waitcnt(0xc07f);             // lgkmcnt(0): this wave's tile is written
       __builtin_amdgcn_wave_barrier();
       uint4 av[4];
 #pragma unroll
@@ -210,7 +212,6 @@ __device__ __forceinline__ void row_reduce(const uint8_t* __restrict__ xc, const
           av[u] = *reinterpret_cast<const uint4*>(stage + i * RL_STRIDE + 64 * u + 16 * g);
         }
       }
-      __builtin_amdgcn_s_waitcnt(0xc07f);             // reads done before the tile is overwritten
       __builtin_amdgcn_wave_barrier();
 #pragma unroll
       for (int t = 0; t < NT; ++t) {
@@ -221,11 +222,9 @@ __device__ __forceinline__ void row_reduce(const uint8_t* __restrict__ xc, const
 #pragma unroll
           for (int v = 0; v < 4; ++v)
             *reinterpret_cast<uint4*>(stage + (4 * v + (lane >> 4)) * RL_STRIDE + 16 * (lane & 15)) = sv[q][t][v];
-          __builtin_amdgcn_s_waitcnt(0xc07f);
           __builtin_amdgcn_wave_barrier();
 #pragma unroll
           for (int u = 0; u < 4; ++u) bv[u] = *reinterpret_cast<const uint4*>(stage + i * RL_STRIDE + 64 * u + 16 * g);
-          __builtin_amdgcn_s_waitcnt(0xc07f);         // reads done before the tile is overwritten
           __builtin_amdgcn_wave_barrier();
         } else if constexpr (NVFP4) {
 #pragma unroll
@@ -235,7 +234,6 @@ __device__ __forceinline__ void row_reduce(const uint8_t* __restrict__ xc, const
 #pragma unroll
           for (int v = 0; v < 4; ++v)
             *reinterpret_cast<uint4*>(stage + (32 * v + (lane >> 1)) * 32 + 16 * (lane & 1)) = sv[q][t][v];
-          __builtin_amdgcn_s_waitcnt(0xc07f);
           __builtin_amdgcn_wave_barrier();
           const int l16 = lane & 15;
 #pragma unroll
@@ -249,7 +247,6 @@ __device__ __forceinline__ void row_reduce(const uint8_t* __restrict__ xc, const
             const uint2 lo = __builtin_bit_cast(uint2, h2[0]), hi = __builtin_bit_cast(uint2, h2[1]);
             bv[u] = make_uint4(lo.x, lo.y, hi.x, hi.y);
           }
-          __builtin_amdgcn_s_waitcnt(0xc07f);         // reads done before the tile is overwritten
           __builtin_amdgcn_wave_barrier();
         }
 #pragma unroll
