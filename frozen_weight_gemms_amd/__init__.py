@@ -162,7 +162,7 @@ def selftest_arith(device="cuda") -> list:
     """Disagreement counts of the device's arithmetic shortcuts against IEEE
     operations over their whole input ranges (pact_selftest_arith); all 0 on a
     conforming device."""
-    counts = torch.zeros((4,), dtype=torch.int64, device=device)
+    counts = torch.zeros((5,), dtype=torch.int64, device=device)
     _lib.call("pact_selftest_arith", counts.data_ptr(), _stream())
     return [int(v) for v in counts.cpu().tolist()]
 

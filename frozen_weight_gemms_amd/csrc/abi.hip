@@ -69,7 +69,7 @@ extern "C" {
 
 const char* pact_last_error(void) { return g_err; }
 
-int pact_abi_version(void) { return 14; }
+int pact_abi_version(void) { return 15; }
 
 int pact_nvfp4_sizes(int64_t rows, int64_t cols, size_t* codes_bytes, size_t* scales_bytes, size_t* rscale_bytes) {
   REQUIRE(rows >= 0 && cols >= 0, PACT_EINVAL, "negative size (rows=%lld, cols=%lld)", (long long)rows,

@@ -26,8 +26,7 @@
 
 namespace pact {
 
-__device__ __forceinline__ void silu_bwd_elem(float a, float b, float d, float& da, float& db) {
-  const float sig = sigmoid_pinned(a);
+__device__ __forceinline__ void silu_bwd_from_sig(float a, float b, float d, float sig, float& da, float& db) {
   const float t = __fmul_rn(__fmul_rn(d, b), sig);
   const float w = __fadd_rn(1.0f, __fmul_rn(a, __fsub_rn(1.0f, sig)));
   da = __fmul_rn(t, w);
@@ -35,14 +34,26 @@ __device__ __forceinline__ void silu_bwd_elem(float a, float b, float d, float& 
 }
 
 // Decode one chunk of a and b, load dh, and form the BF16 gradients (packed).
+// Every sigmoid takes recip_rn of its denominator; a chunk whose largest
+// denominator reaches 2^126 is redone with sigmoid_pinned (IEEE division
+// there), so both give the same values.
 __device__ __forceinline__ void silu_bwd_chunk(uint32_t wa, float ma, uint32_t wb, float mb, const uint4& vd,
                                                uint4& oa, uint4& ob) {
   float a[8], b[8], d[8], da[8], db[8];
   decode8_f32(wa, ma, a);
   decode8_f32(wb, mb, b);
   unpack_bf16x8(vd, d);
+  float dmax = 0.0f;
 #pragma unroll
-  for (int t = 0; t < 8; ++t) silu_bwd_elem(a[t], b[t], d[t], da[t], db[t]);
+  for (int t = 0; t < 8; ++t) {
+    const float den = sigmoid_den(a[t]);
+    dmax = fmaxf(dmax, den);
+    silu_bwd_from_sig(a[t], b[t], d[t], recip_rn(den), da[t], db[t]);
+  }
+  if (!(dmax < 0x1p126f)) {
+#pragma unroll
+    for (int t = 0; t < 8; ++t) silu_bwd_from_sig(a[t], b[t], d[t], sigmoid_pinned(a[t]), da[t], db[t]);
+  }
   oa.x = pack_bf16x2(da[0], da[1]); oa.y = pack_bf16x2(da[2], da[3]);
   oa.z = pack_bf16x2(da[4], da[5]); oa.w = pack_bf16x2(da[6], da[7]);
   ob.x = pack_bf16x2(db[0], db[1]); ob.y = pack_bf16x2(db[2], db[3]);
@@ -66,8 +77,8 @@ __global__ __launch_bounds__(256) void k_silu_mul_bwd(const uint8_t* __restrict_
   for (int64_t q = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; q < total; q += (int64_t)gridDim.x * blockDim.x) {
     const int64_t row = q / nchunk_row, c = q - row * nchunk_row;
     const int64_t e0 = row * I + 8 * c;
-    const float ma = e4m3_decode(gs[row * (I >> 4) + (c >> 1)]) * gr[row];
-    const float mb = e4m3_decode(us[row * (I >> 4) + (c >> 1)]) * ur[row];
+    const float ma = e4m3_decode_hw(gs[row * (I >> 4) + (c >> 1)]) * gr[row];
+    const float mb = e4m3_decode_hw(us[row * (I >> 4) + (c >> 1)]) * ur[row];
     uint4 oa, ob;
     silu_bwd_chunk(reinterpret_cast<const uint32_t*>(gc)[q], ma, reinterpret_cast<const uint32_t*>(uc)[q], mb,
                    load16(dh + e0), oa, ob);
@@ -112,8 +123,8 @@ __global__ __launch_bounds__(256) void k_silu_mul_bwd_quant(
   for (int i = 0; i < NCH; ++i) {
     const int c = threadIdx.x + 256 * i;
     if (c < nchunk) {
-      const float ma = MX ? e8m0_decode(sg[i]) : e4m3_decode(sg[i]) * rg;
-      const float mb = MX ? e8m0_decode(su[i]) : e4m3_decode(su[i]) * ru;
+      const float ma = MX ? e8m0_decode(sg[i]) : e4m3_decode_hw(sg[i]) * rg;
+      const float mb = MX ? e8m0_decode(su[i]) : e4m3_decode_hw(su[i]) * ru;
       silu_bwd_chunk(wg[i], ma, wu[i], mb, vdh[i], oa[i], ob[i]);
       *reinterpret_cast<uint4*>(dgate + row * I + 8 * c) = oa[i];
       *reinterpret_cast<uint4*>(dup + row * I + 8 * c) = ob[i];
@@ -196,7 +207,7 @@ __global__ __launch_bounds__(256) void k_rmsnorm_bwd(const uint8_t* __restrict__
   }
 #pragma unroll
   for (int i = 0; i < NB; ++i)
-    sm[i] = row_ok && lane + 64 * part + 64 * WPR * i < nblk ? (MX ? e8m0_decode(sb[i]) : e4m3_decode(sb[i]) * rr)
+    sm[i] = row_ok && lane + 64 * part + 64 * WPR * i < nblk ? (MX ? e8m0_decode(sb[i]) : e4m3_decode_hw(sb[i]) * rr)
                                                              : 0.0f;
 #pragma unroll
   for (int i = 0; i < NB; ++i) {

@@ -426,8 +426,7 @@ __global__ __launch_bounds__(kThreads) void k_silu_mul_quant(const uint16_t* __r
     float a[8], b[8];
     unpack_bf16x8(va[i], a);
     unpack_bf16x8(vb[i], b);
-#pragma unroll
-    for (int t = 0; t < 8; ++t) h[i][t] = silu_mul(a[t], b[t]);
+    silu_mul8(a, b, h[i]);
     ma = fmaxf(ma, absmax8(a));
     mb = fmaxf(mb, absmax8(b));
     mh = fmaxf(mh, absmax8(h[i]));
@@ -486,6 +485,8 @@ __global__ __launch_bounds__(kThreads) void k_silu_mul_quant(const uint16_t* __r
 //   1: div6_rn(x) == x/6                x in [6 * 2^-126, FLT_MAX] (normal quotient)
 //   2: sigmoid_pinned(a) == 1/(1 + E(-a)), IEEE division   every non-NaN a
 //   3: f32_to_bf16_rne(x) == integer RNE of the bit pattern  every non-NaN x
+//   4: e4m3_encode_hw(t) == e4m3_encode(t)   every t in [0, 448]; and
+//      e4m3_decode_hw(c) == e4m3_decode(c)   every code c in [0, 0x7E]
 // --------------------------------------------------------------------------
 __global__ __launch_bounds__(kThreads) void k_selftest_arith(int which, uint64_t lo, uint64_t hi,
                                                              unsigned long long* __restrict__ count) {
@@ -502,9 +503,12 @@ __global__ __launch_bounds__(kThreads) void k_selftest_arith(int which, uint64_t
     } else if (which == 2) {
       const float ref = __fdiv_rn(1.0f, __fadd_rn(1.0f, exp_pinned(-x)));
       ok = __float_as_uint(sigmoid_pinned(x)) == __float_as_uint(ref);
-    } else {
+    } else if (which == 3) {
       const uint32_t b = __float_as_uint(x);
       ok = f32_to_bf16_rne(x) == ((b + 0x7FFFu + ((b >> 16) & 1u)) >> 16);
+    } else {
+      ok = e4m3_encode_hw(x) == e4m3_encode(x);
+      if (u <= 0x7Eu) ok = ok && __float_as_uint(e4m3_decode_hw((uint32_t)u)) == __float_as_uint(e4m3_decode((uint32_t)u));
     }
     bad += ok ? 0ull : 1ull;
   }
@@ -512,15 +516,15 @@ __global__ __launch_bounds__(kThreads) void k_selftest_arith(int which, uint64_t
   if ((threadIdx.x & 63) == 0 && bad != 0) atomicAdd(count + which, bad);
 }
 
-__global__ void k_zero_u64x4(unsigned long long* p) {
-  if (threadIdx.x < 4) p[threadIdx.x] = 0ull;
+__global__ void k_zero_u64x5(unsigned long long* p) {
+  if (threadIdx.x < 5) p[threadIdx.x] = 0ull;
 }
 
 hipError_t launch_selftest_arith(unsigned long long* counts, hipStream_t s) {
-  k_zero_u64x4<<<1, 64, 0, s>>>(counts);
-  const uint64_t lo[4] = {0x00800000ull, 0x01C00000ull, 0ull, 0ull};
-  const uint64_t hi[4] = {0x7E7FFFFFull, 0x7F7FFFFFull, 0xFFFFFFFFull, 0xFFFFFFFFull};
-  for (int w = 0; w < 4; ++w) k_selftest_arith<<<8192, kThreads, 0, s>>>(w, lo[w], hi[w], counts);
+  k_zero_u64x5<<<1, 64, 0, s>>>(counts);
+  const uint64_t lo[5] = {0x00800000ull, 0x01C00000ull, 0ull, 0ull, 0ull};
+  const uint64_t hi[5] = {0x7E7FFFFFull, 0x7F7FFFFFull, 0xFFFFFFFFull, 0xFFFFFFFFull, 0x43E00000ull};   // 448
+  for (int w = 0; w < 5; ++w) k_selftest_arith<<<8192, kThreads, 0, s>>>(w, lo[w], hi[w], counts);
   return hipGetLastError();
 }
 

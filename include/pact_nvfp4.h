@@ -64,7 +64,7 @@ int pact_abi_version(void);
 /*
  * pact_selftest_arith -- device self-test of the arithmetic shortcuts inside
  * the kernels, each checked against the IEEE operation it stands for over
- * every input bit pattern of its range.  counts: device array of 4 unsigned
+ * every input bit pattern of its range.  counts: device array of 5 unsigned
  * 64-bit integers (caller-owned), set to the number of disagreements of
  *   [0] the correctly rounded reciprocal (hardware estimate + one FMA
  *       correction), d in [2^-126, 2^126);
@@ -74,9 +74,12 @@ int pact_abi_version(void);
  *   [2] the SiLU sigmoid 1/(1 + E(-a)) with that reciprocal (IEEE division
  *       past 1 + E >= 2^126), every non-NaN a;
  *   [3] the hardware float -> BF16 conversion against integer round to
- *       nearest even on the bit pattern, every non-NaN x.
- * All four are 0 on a conforming device.  Asynchronous on `stream`; about
- * 1.3e10 evaluations (well under a second on one GPU).
+ *       nearest even on the bit pattern, every non-NaN x;
+ *   [4] the hardware FP8 conversions used for block scales in the row
+ *       kernels against the software E4M3FN encoder (round to nearest even,
+ *       every t in [0, 448]) and decoder (every code 0 .. 0x7E).
+ * All five are 0 on a conforming device.  Asynchronous on `stream`; about
+ * 1.4e10 evaluations (well under a second on one GPU).
  */
 int pact_selftest_arith(unsigned long long *counts, void *stream);
 

@@ -57,7 +57,7 @@ def test_gemm_tile_query(lib):
 
 
 def test_abi_version(lib):
-    assert lib.pact_abi_version() == 14
+    assert lib.pact_abi_version() == 15
 
 
 def test_sizes(lib):
