@@ -26,7 +26,11 @@
 
 namespace pact {
 
-__device__ __forceinline__ void silu_bwd_from_sig(float a, float b, float d, float sig, float& da, float& db) {
+// The sigmoid per element, its rare IEEE division behind a branch: a chunk
+// test on the largest denominator (as in the forward SiLU) measured slower
+// here, where keeping the chunk's inputs for the redo costs occupancy.
+__device__ __forceinline__ void silu_bwd_elem(float a, float b, float d, float& da, float& db) {
+  const float sig = sigmoid_pinned(a);
   const float t = __fmul_rn(__fmul_rn(d, b), sig);
   const float w = __fadd_rn(1.0f, __fmul_rn(a, __fsub_rn(1.0f, sig)));
   da = __fmul_rn(t, w);
@@ -34,26 +38,14 @@ __device__ __forceinline__ void silu_bwd_from_sig(float a, float b, float d, flo
 }
 
 // Decode one chunk of a and b, load dh, and form the BF16 gradients (packed).
-// Every sigmoid takes recip_rn of its denominator; a chunk whose largest
-// denominator reaches 2^126 is redone with sigmoid_pinned (IEEE division
-// there), so both give the same values.
 __device__ __forceinline__ void silu_bwd_chunk(uint32_t wa, float ma, uint32_t wb, float mb, const uint4& vd,
                                                uint4& oa, uint4& ob) {
   float a[8], b[8], d[8], da[8], db[8];
   decode8_f32(wa, ma, a);
   decode8_f32(wb, mb, b);
   unpack_bf16x8(vd, d);
-  float dmax = 0.0f;
 #pragma unroll
-  for (int t = 0; t < 8; ++t) {
-    const float den = sigmoid_den(a[t]);
-    dmax = fmaxf(dmax, den);
-    silu_bwd_from_sig(a[t], b[t], d[t], recip_rn(den), da[t], db[t]);
-  }
-  if (!(dmax < 0x1p126f)) {
-#pragma unroll
-    for (int t = 0; t < 8; ++t) silu_bwd_from_sig(a[t], b[t], d[t], sigmoid_pinned(a[t]), da[t], db[t]);
-  }
+  for (int t = 0; t < 8; ++t) silu_bwd_elem(a[t], b[t], d[t], da[t], db[t]);
   oa.x = pack_bf16x2(da[0], da[1]); oa.y = pack_bf16x2(da[2], da[3]);
   oa.z = pack_bf16x2(da[4], da[5]); oa.w = pack_bf16x2(da[6], da[7]);
   ob.x = pack_bf16x2(db[0], db[1]); ob.y = pack_bf16x2(db[2], db[3]);
