@@ -134,10 +134,10 @@ __device__ __forceinline__ float sigmoid_den(float a) {
 
 // sigma(a) = 1 / (1 + E(-a)) in the pinned FP32 sequence (0 when E overflows),
 // the division correctly rounded: recip_rn while 1 + E < 2^126, IEEE division
-// beyond (a < -87, where the reciprocal is subnormal or 0).  The chunk
-// kernels take recip_rn(d) for all elements, track the largest d (never NaN:
-// 1 <= d <= +inf) and redo a chunk with this function when it reaches 2^126,
-// so the per-element division branch is not in their common path.
+// beyond (a < -87, where the reciprocal is subnormal or 0).  The forward
+// SiLU kernel takes recip_rn(d) for all elements, tracks the largest d (never
+// NaN: 1 <= d <= +inf) and redoes a chunk with this function when it reaches
+// 2^126, so the per-element division branch is not in its common path.
 __device__ __forceinline__ float sigmoid_pinned(float a) {
   const float d = sigmoid_den(a);
   float sig;
