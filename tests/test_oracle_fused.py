@@ -106,6 +106,23 @@ def test_exp_accuracy_and_edges():
     assert np.all(np.diff(fused.exp_f32(np.linspace(-5, 5, 10001, dtype=np.float32))) >= 0)
 
 
+def test_exp_range_selects_do_not_reach_the_sigmoid():
+    """The sigmoid's denominator 1 + E(-a) is the same with or without E's two
+    range selects: at the lower clamp E(-80) is about 2^-115, too small to move
+    1 + E off 1 in FP32, and at the upper clamp the polynomial times 2^128
+    already overflows to +inf.  (The GPU kernels form the denominator without
+    the selects and rely on exactly these two facts.)"""
+    lo = fused.exp_f32(np.float32(-80.0))
+    assert 0.0 < float(lo) < 2.0 ** -110
+    assert np.float32(1.0) + lo == np.float32(1.0)
+    assert np.isinf(fused.exp_f32(np.float32(89.0)))
+    # below and above the clamps the selects' values give the same denominators
+    for x in (-80.25, -100.0, -1e30):
+        assert np.float32(1.0) + fused.exp_f32(np.float32(x)) == np.float32(1.0) + lo
+    for x in (89.25, 100.0, 1e30):
+        assert np.isinf(fused.exp_f32(np.float32(x)))
+
+
 def test_silu_closed_forms():
     a = np.array([0.0, -0.0, 1.0, -1.0, 100.0, -100.0, 3.0], dtype=np.float32)
     s = fused.silu_f32(a)
